@@ -1,0 +1,113 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the oracle side.
+
+This module only draws random numbers into arrays of the workloads' shapes
+and distributions; it holds none of the summation method's arithmetic and
+imports neither the oracle nor the HIP path.  numpy ``Generator(PCG64(seed))``
+everywhere, so a seed names the same bytes on every machine with the same
+numpy version.
+
+Workloads (the pages measure on video fixtures that are not available; these
+synthetic inputs stand in for them with the same sizes and the structure that
+matters to the method):
+
+* ``uniform(n, seed)`` -- n fp64 terms uniform in [0, 1).
+* ``tie_heavy(n, seed)`` -- d = 1 - q with q = k * 2^-53, k uniform in
+  [2^52, 2^53), so d is a multiple of 2^-53 in (0, 0.5]; 10 % of the terms are
+  exactly 0.  Research-1433 Findings 3 describes this term shape (every second
+  such term ties while the running sum is in [1, 2)).
+* ``signed_terms(n, seed)`` -- 90 % Beta(20, 2), 10 % uniform in [-1, 0.2]:
+  signed SSIM-like terms whose running sum needs prefix bounds.
+* ``frame_pair(h, w, seed)`` -- uint8 ref uniform in 0..255 and
+  dis = clamp(rint(ref + N(0, 8)), 0, 255).
+* ``pyramid(seed)`` -- 6 scales of a 3840x2160 frame (each side halved with
+  (s + 1) // 2), 3 channels, 6 sums each: sums 0-2 tie-heavy, sums 3-5
+  |N(0, 0.05)|; an independent stream per (scale, channel, sum).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+FRAME_W, FRAME_H = 3840, 2160
+FRAME_N = FRAME_W * FRAME_H            # 8,294,400 terms (66,355,200 bytes)
+HALF_W, HALF_H = 1920, 1080
+HALF_N = HALF_W * HALF_H               # 2,073,600 terms
+
+
+def rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def uniform(n: int = 4096, seed: int = 0) -> np.ndarray:
+    return rng(seed).random(n)
+
+
+def tie_heavy(n: int = FRAME_N, seed: int = 0, zero_frac: float = 0.1) -> np.ndarray:
+    g = rng(seed)
+    k = g.integers(2 ** 52, 2 ** 53, n, dtype=np.int64)
+    q = k.astype(np.float64) * 2.0 ** -53      # exact: k < 2^53
+    d = 1.0 - q                                 # exact: q in [0.5, 1)
+    d[g.random(n) < zero_frac] = 0.0
+    return d
+
+
+def signed_terms(n: int = HALF_N, seed: int = 0) -> np.ndarray:
+    g = rng(seed)
+    m = g.random(n) < 0.9
+    pos = g.beta(20.0, 2.0, n)
+    neg = g.uniform(-1.0, 0.2, n)
+    return np.where(m, pos, neg)
+
+
+def half_normal(n: int, seed: int = 0, sigma: float = 0.05) -> np.ndarray:
+    return np.abs(rng(seed).normal(0.0, sigma, n))
+
+
+def frame_pair(h: int = FRAME_H, w: int = FRAME_W, seed: int = 0, sigma: float = 8.0):
+    g = rng(seed)
+    ref = g.integers(0, 256, (h, w), dtype=np.uint8)
+    noise = g.normal(0.0, sigma, (h, w))
+    dis = np.clip(np.rint(ref.astype(np.float64) + noise), 0, 255).astype(np.uint8)
+    return ref, dis
+
+
+def pyramid_shapes(w: int = FRAME_W, h: int = FRAME_H, scales: int = 6):
+    """(width, height) per scale; each side halved as (s + 1) // 2 while both
+    sides stay >= 8, at most ``scales`` scales."""
+    out = []
+    for _ in range(scales):
+        if w < 8 or h < 8:
+            break
+        out.append((w, h))
+        w, h = (w + 1) // 2, (h + 1) // 2
+    return out
+
+
+def pyramid(seed: int = 0, w: int = FRAME_W, h: int = FRAME_H, scales: int = 6,
+            channels: int = 3, sums: int = 6):
+    """List of ``scales * channels * sums`` fp64 arrays (scale-major order)."""
+    out = []
+    ss = np.random.SeedSequence(seed)
+    children = ss.spawn(len(pyramid_shapes(w, h, scales)) * channels * sums)
+    i = 0
+    for (sw, sh) in pyramid_shapes(w, h, scales):
+        n = sw * sh
+        for _c in range(channels):
+            for j in range(sums):
+                g = np.random.Generator(np.random.PCG64(children[i]))
+                i += 1
+                if j < sums // 2:
+                    k = g.integers(2 ** 52, 2 ** 53, n, dtype=np.int64)
+                    d = 1.0 - k.astype(np.float64) * 2.0 ** -53
+                    d[g.random(n) < 0.1] = 0.0
+                    out.append(d)
+                else:
+                    out.append(np.abs(g.normal(0.0, 0.05, n)))
+    return out
+
+
+def tie_suite(n: int = 4096, seed: int = 0) -> np.ndarray:
+    """Terms k * 2^-53 with k in [0, 7]: started from 1.0 the running sum
+    stays in [1, 2) and every term with odd k is a tie at that scale."""
+    k = rng(seed).integers(0, 8, n)
+    return k.astype(np.float64) * 2.0 ** -53
