@@ -1,0 +1,134 @@
+// The C ABI of libexseq.so: argument checks, workspace carving, launches.
+// Declarations and their contracts are in include/exseq.h.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "exseq.h"
+#include "exseq_internal.h"
+
+using namespace exseq;
+
+namespace {
+
+bool aligned8(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0u; }
+
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+const char *exseq_version(void) { return "exseq 0.1 (gfx950)"; }
+
+const char *exseq_strerror(int code)
+{
+    switch (code) {
+    case EXSEQ_OK:
+        return "ok";
+    case EXSEQ_EINVAL:
+        return "invalid argument (null pointer, misalignment or bad size)";
+    case EXSEQ_EWORKSPACE:
+        return "workspace too small";
+    case EXSEQ_EHIP:
+        return "HIP runtime error at launch";
+    default:
+        return "unknown exseq error";
+    }
+}
+
+size_t exact_seq_sum_f64_workspace_size(size_t n) { return n ? sum_layout(n).total : 256; }
+
+int exact_seq_sum_f64(const double *x, size_t n, double init, double *out, void *ws,
+                      size_t ws_bytes, exseq_stream_t stream, uint32_t flags,
+                      exseq_stats *stats)
+{
+    if (!out || !aligned8(out) || (n && (!x || !aligned8(x))))
+        return EXSEQ_EINVAL;
+    if (n && !ws)
+        return EXSEQ_EINVAL;
+    if (n && ws_bytes < exact_seq_sum_f64_workspace_size(n))
+        return EXSEQ_EWORKSPACE;
+    if (n > ((size_t)1 << 40))
+        return EXSEQ_EINVAL;
+    return launch_exact_sum(x, n, init, out, ws, reinterpret_cast<hipStream_t>(stream), flags,
+                            stats);
+}
+
+size_t exact_seq_sum_f64_batch_workspace_size(const size_t *ns, size_t count)
+{
+    size_t mx = 256;
+    for (size_t k = 0; ns && k < count; k++) {
+        size_t b = exact_seq_sum_f64_workspace_size(ns[k]);
+        mx = b > mx ? b : mx;
+    }
+    return round256(mx);
+}
+
+int exact_seq_sum_f64_batch(const double *const *xs, const size_t *ns, const double *inits,
+                            size_t count, double *outs, void *ws, size_t ws_bytes,
+                            exseq_stream_t stream, uint32_t flags, exseq_stats *stats)
+{
+    if (count == 0)
+        return EXSEQ_OK;
+    if (!xs || !ns || !outs || !aligned8(outs))
+        return EXSEQ_EINVAL;
+    for (size_t k = 0; k < count; k++) {
+        if (ns[k] && (!xs[k] || !aligned8(xs[k])))
+            return EXSEQ_EINVAL;
+        if (ns[k] > ((size_t)1 << 40))
+            return EXSEQ_EINVAL;
+    }
+    if (!ws || ws_bytes < exact_seq_sum_f64_batch_workspace_size(ns, count))
+        return ws ? EXSEQ_EWORKSPACE : EXSEQ_EINVAL;
+    for (size_t k = 0; k < count; k++) {
+        int rc = launch_exact_sum(xs[k], ns[k], inits ? inits[k] : 0.0, outs + k, ws,
+                                  reinterpret_cast<hipStream_t>(stream), flags,
+                                  stats ? stats + k : nullptr);
+        if (rc != EXSEQ_OK)
+            return rc;
+    }
+    return EXSEQ_OK;
+}
+
+size_t ssim_term_and_sum_workspace_size(int width, int height)
+{
+    if (width < 1 || height < 1)
+        return 256;
+    return ssim_layout(width, height).total;
+}
+
+int ssim_term_and_sum(const uint8_t *ref, const uint8_t *dis, int width, int height,
+                      ptrdiff_t stride, int radius, double c1, double c2, double *out_sum,
+                      int64_t *out_weight_sum, double *out_terms, void *ws, size_t ws_bytes,
+                      exseq_stream_t stream, uint32_t flags, exseq_stats *stats)
+{
+    if (!ref || !dis || !out_sum || !aligned8(out_sum) || width < 1 || height < 1 ||
+        stride < width || radius < 0 || radius > 15)
+        return EXSEQ_EINVAL;
+    if ((size_t)width * (size_t)height > ((size_t)1 << 34))
+        return EXSEQ_EINVAL;
+    if ((out_weight_sum && !aligned8(out_weight_sum)) || (out_terms && !aligned8(out_terms)))
+        return EXSEQ_EINVAL;
+    if (!ws)
+        return EXSEQ_EINVAL;
+    if (ws_bytes < ssim_term_and_sum_workspace_size(width, height))
+        return EXSEQ_EWORKSPACE;
+    return launch_ssim_sum(ref, dis, width, height, stride, radius, c1, c2, out_sum,
+                           out_weight_sum, out_terms, ws, reinterpret_cast<hipStream_t>(stream),
+                           flags, stats);
+}
+
+size_t tree_sum_f64_workspace_size(size_t n) { return n ? sum_layout(n).total : 256; }
+
+int tree_sum_f64(const double *x, size_t n, double *out, void *ws, size_t ws_bytes,
+                 exseq_stream_t stream)
+{
+    if (!out || !aligned8(out) || (n && (!x || !aligned8(x))))
+        return EXSEQ_EINVAL;
+    if (n && (!ws || ws_bytes < tree_sum_f64_workspace_size(n)))
+        return ws ? EXSEQ_EWORKSPACE : EXSEQ_EINVAL;
+    return launch_tree_sum(x, n, out, ws, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,182 @@
+/*
+ * exseq -- bit-exact sequential fp64 sums on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libexseq.so.  Every result equals, bit for bit, the CPU loop
+ *
+ *     double s = init; for (i = 0; i < n; i++) s += x[i];
+ *
+ * in IEEE-754 binary64 with round to nearest, ties to even (Research-1433
+ * "Forming the CPU's sequential double sums on a GPU, bit for bit", Question
+ * and Findings 1; Research-1424 "integer_ssim_cuda and the CPU's frame sum",
+ * Findings 1 and 3).  The terms stay on the device and are not added on one
+ * thread: inside one binade the running sum is an integer count of units,
+ * each term an increment pair formed from its own bits (ties to even make it
+ * a pair), runs compose in order, prefix bounds prove a run stayed in its
+ * binade, and chunks that leave it are added term by term from the exact sum.
+ *
+ * Conventions for every call below:
+ *  - Data pointers (`x`, `xs[k]`, `ref`, `dis`, `out*`, `ws`, `stats`) are
+ *    DEVICE pointers on the current HIP device; `ns`, `xs` (the array of
+ *    pointers itself) and `shapes` are HOST arrays.  The caller owns every
+ *    buffer; the library allocates nothing and never frees.
+ *  - Every call is stream-ordered and non-blocking on `stream` (0 = the null
+ *    stream): no host synchronisation, no device-to-host copy.  A return of
+ *    EXSEQ_OK means the work was enqueued; the result appears in device
+ *    memory when the stream reaches it.
+ *  - `ws` is a caller-provided device workspace of at least the size the
+ *    matching *_workspace_size() call returns.  Its contents need no
+ *    initialisation and are clobbered.  Calls that share a workspace must
+ *    be ordered (same stream); calls on different streams need different
+ *    workspaces.
+ *  - Terms are fp64 in native (little-endian) layout, contiguous, 8-byte
+ *    aligned.  n == 0 is valid and writes `init`.
+ *  - Non-finite terms are allowed: the result is what the loop gives (NaN
+ *    payloads are not specified); `stats->flags` then has EXSEQ_STAT_NONFINITE.
+ *  - Return value: EXSEQ_OK (0) or a negative EXSEQ_E* code.  Argument errors
+ *    are found before anything is enqueued; EXSEQ_EHIP reports a launch
+ *    error from the HIP runtime.
+ */
+#ifndef EXSEQ_H
+#define EXSEQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *exseq_stream_t; /* a hipStream_t */
+
+enum {
+    EXSEQ_OK = 0,
+    EXSEQ_EINVAL = -1,     /* null pointer with work to do, misalignment, bad size */
+    EXSEQ_EWORKSPACE = -2, /* ws_bytes below the required size */
+    EXSEQ_EHIP = -3        /* the HIP runtime rejected a launch */
+};
+
+/* Plan modes (low 4 bits of `flags`).  The plan names the binade each chunk's
+ * increments are formed for.  It is an approximation and can never change a
+ * result, only how many chunks are added term by term (Research-1433
+ * Findings 5).  The overrides exist to test that statement.
+ *   AUTO          binade of the prefix of the chunks' tree sums (default)
+ *   ALL_FALLBACK  no chunk gets a fast path: every chunk term by term
+ *   PLUS_ONE      one binade too high on every chunk
+ *   MINUS_ONE     one binade too low on every chunk
+ *   FIXED         every chunk planned for the key in bits 8..19 of `flags`
+ *                 (sign bit << 11 | biased exponent; 1023 is [1, 2)) */
+#define EXSEQ_PLAN_AUTO 0u
+#define EXSEQ_PLAN_ALL_FALLBACK 1u
+#define EXSEQ_PLAN_PLUS_ONE 2u
+#define EXSEQ_PLAN_MINUS_ONE 3u
+#define EXSEQ_PLAN_FIXED 4u
+#define EXSEQ_PLAN_MASK 0xFu
+#define EXSEQ_PLAN_FIXED_KEY(key) (EXSEQ_PLAN_FIXED | (((uint32_t)(key) & 0xFFFu) << 8))
+
+/* Device-side statistics of one sum (written when the walk finishes). */
+typedef struct exseq_stats {
+    uint64_t chunks;          /* chunks walked */
+    uint64_t fast_chunks;     /* chunks applied from their increment pairs */
+    uint64_t fallback_chunks; /* chunks added term by term */
+    uint64_t fallback_terms;  /* terms added one by one */
+    int64_t first_fallback;   /* index of the first fallback chunk, -1 if none */
+    uint32_t flags;           /* EXSEQ_STAT_* */
+    uint32_t plan_misses;     /* chunks whose planned binade was not the exact one */
+} exseq_stats;
+
+#define EXSEQ_STAT_NONFINITE 1u
+
+/* Terms per chunk: the unit of descriptors and of the term-by-term fallback. */
+#define EXSEQ_CHUNK_TERMS 1024
+
+/* ---------------------------------------------------------------------------
+ * exact_seq_sum_f64
+ *   out[0] = ((init + x[0]) + x[1]) + ... + x[n-1], in fp64 RNE, bit exact.
+ *   x: n device doubles.  out: one device double.  stats: nullable device
+ *   pointer.  flags: EXSEQ_PLAN_* (0 for production use).
+ *   Research-1433 Findings 2-6 (method and layout); Research-1424 Findings 3.
+ * ------------------------------------------------------------------------- */
+size_t exact_seq_sum_f64_workspace_size(size_t n);
+int exact_seq_sum_f64(const double *x, size_t n, double init, double *out,
+                      void *ws, size_t ws_bytes, exseq_stream_t stream,
+                      uint32_t flags, exseq_stats *stats);
+
+/* ---------------------------------------------------------------------------
+ * exact_seq_sum_f64_batch
+ *   count independent sums: outs[k] = the loop over xs[k][0 .. ns[k]) started
+ *   at inits[k] (inits: host array, or NULL for +0.0 everywhere).  One launch
+ *   sequence covers every sum (the per-scale sums of a frame pyramid; ADR-1391
+ *   "The CUDA ssimulacra2 twin is device-resident", Decision step 2-3).
+ *   xs, ns, inits: HOST arrays of length count (xs holds device pointers).
+ *   outs: count device doubles.  stats: nullable device array of count.
+ * ------------------------------------------------------------------------- */
+size_t exact_seq_sum_f64_batch_workspace_size(const size_t *ns, size_t count);
+int exact_seq_sum_f64_batch(const double *const *xs, const size_t *ns,
+                            const double *inits, size_t count, double *outs,
+                            void *ws, size_t ws_bytes, exseq_stream_t stream,
+                            uint32_t flags, exseq_stats *stats);
+
+/* ---------------------------------------------------------------------------
+ * ssim_term_and_sum
+ *   Fused integer-SSIM frame sum.  For every pixel (i, j) of two 8-bit planes
+ *   (row-major, `stride` bytes between rows) the edge-truncated
+ *   (2r+1) x (2r+1) window gives int64 sums x, y, x2, y2, xy and the pixel
+ *   count w; the fp64 term
+ *     w*(2*mxy + c1)*(c2 + 2*(xy*w - mxy))
+ *       / ((mx2 + my2 + c1)*(x2*w - mx2 + y2*w - my2 + c2)),
+ *   mx2 = x*x, my2 = y*y, mxy = x*y in fp64, evaluated left to right with no
+ *   contraction (Research-1424 Findings 1; ADR-1443 "integer_ssim_sycl
+ *   computes the CPU's fp64 term in 64-bit integers and adds in the CPU's
+ *   order", Context and Decision), is added into one double in raster order
+ *   starting from +0.0.  out_sum: one device double.  out_weight_sum:
+ *   nullable device int64, the sum of w over the frame.  out_terms: nullable
+ *   device plane of width*height doubles receiving every term (debugging).
+ *   width, height >= 1; stride >= width; 0 <= radius <= 15.
+ * ------------------------------------------------------------------------- */
+size_t ssim_term_and_sum_workspace_size(int width, int height);
+int ssim_term_and_sum(const uint8_t *ref, const uint8_t *dis, int width,
+                      int height, ptrdiff_t stride, int radius, double c1,
+                      double c2, double *out_sum, int64_t *out_weight_sum,
+                      double *out_terms, void *ws, size_t ws_bytes,
+                      exseq_stream_t stream, uint32_t flags, exseq_stats *stats);
+
+/* ---------------------------------------------------------------------------
+ * tree_sum_f64
+ *   Deterministic fixed-shape tree sum of x (NOT the loop's bits): chunks of
+ *   1024 terms reduced in a fixed tree, then the chunk sums in a fixed tree.
+ *   Its result depends only on n and the values, and is reported beside the
+ *   exact sum to show the gap a tree leaves (ADR-1391 Decision, Numerics).
+ *   out: one device double.
+ * ------------------------------------------------------------------------- */
+size_t tree_sum_f64_workspace_size(size_t n);
+int tree_sum_f64(const double *x, size_t n, double *out, void *ws,
+                 size_t ws_bytes, exseq_stream_t stream);
+
+/* Text for an EXSEQ_* return code (static storage). */
+const char *exseq_strerror(int code);
+
+/* Library version string (static storage). */
+const char *exseq_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Host model of the method (test infrastructure; runs on the CPU, no GPU).
+ *   The same rules as the kernels, walked chunk by chunk on the host, with
+ *   the plan overrides and four deliberate mutations of the rules that the
+ *   method's own tests must catch (Research-1433 Findings 1 "Tests": always
+ *   round a tie up, drop the binade check, drop the upper bound check,
+ *   ignore the parity when composing).  x: HOST array.  chunk_terms >= 1.
+ *   stats: nullable HOST pointer.  Returns the sum.
+ * ------------------------------------------------------------------------- */
+#define EXSEQ_MUT_TIE_UP 1u
+#define EXSEQ_MUT_NO_BINADE_CHECK 2u
+#define EXSEQ_MUT_NO_UPPER_CHECK 4u
+#define EXSEQ_MUT_IGNORE_PARITY 8u
+double exseq_model_seq_sum_f64(const double *x, size_t n, double init,
+                               size_t chunk_terms, uint32_t flags,
+                               uint32_t mutations, exseq_stats *stats);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXSEQ_H */

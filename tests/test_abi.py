@@ -1,0 +1,54 @@
+"""The C-ABI library loads and exports every symbol include/exseq.h declares;
+argument checks reject bad calls before anything reaches a GPU (CPU only)."""
+
+import ctypes
+import os
+
+import bit_exact_sequential_amd as ex
+
+
+def test_library_exports_every_declared_function():
+    L = ex.lib()
+    names = ex.declared_functions()
+    assert "exact_seq_sum_f64" in names and "ssim_term_and_sum" in names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_strerror_and_version():
+    L = ex.lib()
+    for code in (0, -1, -2, -3, -99):
+        assert L.exseq_strerror(code)
+    assert b"gfx950" in L.exseq_version()
+
+
+def test_workspace_sizes():
+    L = ex.lib()
+    assert L.exact_seq_sum_f64_workspace_size(0) >= 0
+    w = L.exact_seq_sum_f64_workspace_size(8294400)
+    assert 8100 * 32 <= w < 8294400            # descriptors, far below the terms
+    assert L.tree_sum_f64_workspace_size(1000) > 0
+    assert L.ssim_term_and_sum_workspace_size(3840, 2160) > 0
+    ns = (ctypes.c_size_t * 3)(10, 100000, 0)
+    assert L.exact_seq_sum_f64_batch_workspace_size(ns, 3) >= L.exact_seq_sum_f64_workspace_size(100000)
+
+
+def test_argument_errors_return_before_any_launch():
+    L = ex.lib()
+    # null terms with n > 0
+    assert L.exact_seq_sum_f64(None, 10, 0.0, 8, 64, 1 << 20, None, 0, None) == ex.EXSEQ_EINVAL
+    # misaligned output
+    assert L.exact_seq_sum_f64(64, 10, 0.0, 9, 64, 1 << 20, None, 0, None) == ex.EXSEQ_EINVAL
+    # workspace too small
+    assert L.exact_seq_sum_f64(64, 100000, 0.0, 8, 64, 16, None, 0, None) == ex.EXSEQ_EWORKSPACE
+    # bad geometry
+    assert L.ssim_term_and_sum(64, 64, 0, 5, 5, 3, 1.0, 1.0, 8, None, None, 64, 1 << 20, None,
+                               0, None) == ex.EXSEQ_EINVAL
+    assert L.ssim_term_and_sum(64, 64, 5, 5, 4, 3, 1.0, 1.0, 8, None, None, 64, 1 << 20, None,
+                               0, None) == ex.EXSEQ_EINVAL
+    assert L.tree_sum_f64(None, 5, 8, 64, 1 << 20, None) == ex.EXSEQ_EINVAL
+
+
+def test_built_for_gfx950():
+    data = open(ex.LIB_PATH, "rb").read()
+    assert b"gfx950" in data

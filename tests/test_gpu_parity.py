@@ -1,0 +1,227 @@
+"""GPU parity: every sum from the HIP path equals the oracle bit for bit
+(tolerance 0 ULP), through the C ABI.  Inputs are seeded; both sides see the
+same bytes."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs as si
+import bit_exact_sequential_amd as ex
+from tests import suites
+from tests.gpu_util import same, say, to_dev, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+PLANS = [ex.PLAN_AUTO, ex.PLAN_ALL_FALLBACK, ex.PLAN_PLUS_ONE, ex.PLAN_MINUS_ONE,
+         ex.plan_fixed(1023)]
+
+
+@pytest.fixture(autouse=True)
+def _name(request):
+    say("start", request.node.nodeid)
+    yield
+
+
+def gpu_sum(torch, x, init=0.0, flags=0, stats=False):
+    xd = to_dev(torch, x)
+    r = ex.exact_seq_sum(xd, init, flags=flags, stats=stats)
+    if stats:
+        out, st = r
+        return float(out.cpu()[0]), st
+    return float(r.cpu()[0])
+
+
+@pytest.mark.parametrize("case", suites.edge_suite(), ids=lambda c: c[0])
+def test_edge_cases(case):
+    torch = torch_cuda()
+    name, x, init = case
+    want = oracle.seq_sum(x, init)
+    for plan in (ex.PLAN_AUTO, ex.PLAN_ALL_FALLBACK, ex.PLAN_PLUS_ONE):
+        got = gpu_sum(torch, x, init, plan)
+        assert same(got, want), (name, plan, got, want)
+
+
+@pytest.mark.parametrize("n", suites.ragged_sizes())
+def test_ragged_sizes(n):
+    torch = torch_cuda()
+    for x in (si.tie_heavy(n, n), si.signed_terms(n, n + 1)):
+        got = gpu_sum(torch, x)
+        assert same(got, oracle.seq_sum(x)), n
+
+
+@pytest.mark.parametrize("case", suites.workload_suite(small=True), ids=lambda c: c[0])
+def test_workloads_every_plan(case):
+    """Research-1433 Findings 5: the plan cannot change a result."""
+    torch = torch_cuda()
+    name, x, init = case
+    want = oracle.seq_sum(x, init)
+    for plan in PLANS:
+        got = gpu_sum(torch, x, init, plan)
+        assert same(got, want), (name, plan, got, want)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3, 4])
+def test_full_size_workloads(seed):
+    """The frame-size tie-heavy sum (8,294,400 terms), the 1920x1080 signed
+    sum and the 4096-term uniform sum, five seeds each, at full size."""
+    torch = torch_cuda()
+    for name, x in (("uniform", si.uniform(4096, seed)),
+                    ("tie_heavy", si.tie_heavy(si.FRAME_N, seed)),
+                    ("signed", si.signed_terms(si.HALF_N, seed))):
+        got, st = gpu_sum(torch, x, stats=True)
+        want = oracle.seq_sum(x)
+        say(name, seed, st)
+        assert same(got, want), (name, seed, got, want)
+
+
+def test_full_size_stats_ranges():
+    """Fallback counts in the range the method predicts: the first chunk and
+    about one per binade crossed (Research-1433 Findings 4)."""
+    torch = torch_cuda()
+    x = si.tie_heavy(si.FRAME_N, 0)
+    _, st = gpu_sum(torch, x, stats=True)
+    assert st["chunks"] == 8100
+    assert 1 <= st["fallback_chunks"] <= 40, st
+    assert st["fast_chunks"] + st["fallback_chunks"] == 8100
+    assert st["flags"] == 0
+
+
+def test_tie_fast_path_suite():
+    """init = 1 and terms k * 2^-53: the sum stays in [1, 2) and every odd k
+    is a tie on the fast path."""
+    torch = torch_cuda()
+    for seed in range(3):
+        x = si.tie_suite(1 << 20, seed)
+        got, st = gpu_sum(torch, x, 1.0, stats=True)
+        assert same(got, oracle.seq_sum(x, 1.0))
+        assert st["fallback_chunks"] == 0, st
+
+
+def test_exhaustive_short_sequences():
+    torch = torch_cuda()
+    cases = suites.exhaustive_short(8)
+    for i, (x, init) in enumerate(cases):
+        got = gpu_sum(torch, x, init)
+        assert same(got, oracle.seq_sum(x, init)), (i, x, init)
+
+
+def test_resume_with_init():
+    torch = torch_cuda()
+    x = si.signed_terms(300_000, 5)
+    whole = oracle.seq_sum(x)
+    for k in (0, 1, 1024, 150_001, 300_000):
+        head = oracle.seq_sum(x[:k])
+        assert same(gpu_sum(torch, x[k:], head), whole), k
+
+
+def test_unaligned_terms():
+    """Terms at an 8-byte but not 16-byte aligned address take the scalar
+    load path."""
+    torch = torch_cuda()
+    x = si.tie_heavy(100_001, 3)
+    xd = to_dev(torch, np.concatenate([[0.0], x]))[1:]
+    assert xd.data_ptr() % 16 == 8
+    got = float(ex.exact_seq_sum(xd).cpu()[0])
+    assert same(got, oracle.seq_sum(x))
+
+
+def test_repeat_determinism():
+    torch = torch_cuda()
+    x = to_dev(torch, si.signed_terms(si.HALF_N, 7))
+    first = float(ex.exact_seq_sum(x).cpu()[0])
+    outs = torch.empty(50, dtype=torch.float64, device="cuda")
+    for i in range(50):
+        ex.exact_seq_sum(x, out=outs[i:i + 1])
+    assert all(same(v, first) for v in outs.cpu().tolist())
+
+
+def test_tree_sum_gap_and_determinism():
+    """The fixed tree is deterministic and within the standard error bound
+    of a depth-d tree (d * 2^-53 * sum|x|); its gap to the exact sum is what
+    the exact path removes."""
+    torch = torch_cuda()
+    x = si.tie_heavy(si.FRAME_N, 1)
+    xd = to_dev(torch, x)
+    t1 = float(ex.tree_sum(xd).cpu()[0])
+    t2 = float(ex.tree_sum(xd).cpu()[0])
+    assert same(t1, t2)
+    exact = math.fsum(x)
+    depth = 2 + 6 + 2 + 3 + 10 + 1
+    assert abs(t1 - exact) <= depth * 2.0 ** -53 * float(np.abs(x).sum()) * 1.01
+    seq = oracle.seq_sum(x)
+    say("tree", t1, "seq", seq, "gap", t1 - seq)
+
+
+def test_batch_matches_single_sums():
+    torch = torch_cuda()
+    arrays = [si.tie_heavy(n, n) for n in (0, 1, 1000, 4097, 65_536, 300_001)]
+    inits = [0.0, 1.0, -2.0, 0.5, 0.0, 3.0]
+    xs = [to_dev(torch, a) for a in arrays]
+    out = ex.exact_seq_sum_batch(xs, inits).cpu().tolist()
+    for a, i, o in zip(arrays, inits, out):
+        assert same(o, oracle.seq_sum(a, i))
+
+
+def test_pyramid_batch_full():
+    """108 sums of the 6-scale pyramid of a 3840x2160 frame."""
+    torch = torch_cuda()
+    arrays = si.pyramid(0)
+    assert len(arrays) == 108
+    xs = [to_dev(torch, a) for a in arrays]
+    out = ex.exact_seq_sum_batch(xs).cpu().tolist()
+    want = oracle.seq_sum_many(arrays)
+    for k, (o, w) in enumerate(zip(out, want)):
+        assert same(o, w), k
+
+
+SIZES = [(1, 1), (2, 2), (3, 4), (5, 7), (9, 9), (16, 16), (33, 17), (65, 63), (182, 322),
+         (8, 8), (17, 9), (31, 33), (323, 577), (48, 64), (47, 65)]
+
+
+@pytest.mark.parametrize("hw", SIZES, ids=lambda s: "%dx%d" % s)
+def test_ssim_small_frames(hw):
+    """Frame sizes from the pages' random-size lists; every term and the sum
+    equal the oracle's."""
+    torch = torch_cuda()
+    h, w = hw
+    ref, dis = si.frame_pair(h, w, h * 1000 + w)
+    s, wsum, terms = oracle.ssim_frame_sum(ref, dis, 3, want_terms=True)
+    r = torch.from_numpy(ref).cuda()
+    d = torch.from_numpy(dis).cuda()
+    gs, gw, gt = ex.ssim_term_and_sum(r, d, 3, want_terms=True)
+    assert np.array_equal(gt.cpu().numpy().view(np.uint64), terms.view(np.uint64))
+    assert same(float(gs.cpu()[0]), s)
+    assert int(gw.cpu()[0]) == wsum
+
+
+def test_ssim_full_frame():
+    torch = torch_cuda()
+    ref, dis = si.frame_pair(si.FRAME_H, si.FRAME_W, 0)
+    s, wsum, _ = oracle.ssim_frame_sum(ref, dis, 3)
+    r = torch.from_numpy(ref).cuda()
+    d = torch.from_numpy(dis).cuda()
+    gs, gw, _, st = ex.ssim_term_and_sum(r, d, 3, stats=True)
+    say("ssim full", st)
+    assert same(float(gs.cpu()[0]), s)
+    assert int(gw.cpu()[0]) == wsum
+
+
+def test_ssim_term_divide_against_host():
+    """The device divide and term equal the host's on many random windows,
+    including wide int64 moments where products round (stride > width)."""
+    torch = torch_cuda()
+    for radius in (0, 1, 3, 5):
+        ref, dis = si.frame_pair(37, 53, 40 + radius)
+        s, wsum, terms = oracle.ssim_frame_sum(ref, dis, radius, want_terms=True)
+        big_r = np.zeros((37, 64), np.uint8)
+        big_d = np.zeros((37, 64), np.uint8)
+        big_r[:, :53] = ref
+        big_d[:, :53] = dis
+        r = torch.from_numpy(big_r).cuda()[:, :53]
+        d = torch.from_numpy(big_d).cuda()[:, :53]
+        gs, gw, gt = ex.ssim_term_and_sum(r, d, radius, want_terms=True)
+        assert np.array_equal(gt.cpu().numpy().view(np.uint64), terms.view(np.uint64)), radius
+        assert same(float(gs.cpu()[0]), s)
