@@ -69,6 +69,11 @@ def lib():
     if not os.path.exists(LIB_PATH):
         raise ExseqError("libexseq.so is not built: run "
                          "`python -m bit_exact_sequential_amd.build`")
+    # torch's ROCm wheel carries its own HIP runtime under the same soname as
+    # /opt/rocm's.  Loading torch first makes libexseq.so bind to that one
+    # runtime, so torch's streams and events are valid handles for the
+    # library; loading the library first would map a second runtime.
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     sz, vp, u32, i32 = ctypes.c_size_t, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int
     L.exact_seq_sum_f64_workspace_size.restype = sz
@@ -95,11 +100,29 @@ def lib():
     L.exseq_strerror.argtypes = [i32]
     L.exseq_version.restype = ctypes.c_char_p
     L.exseq_version.argtypes = []
+    L.exseq_profile_kernel_count.restype = i32
+    L.exseq_profile_kernel_count.argtypes = []
+    L.exseq_profile_kernel_name.restype = ctypes.c_char_p
+    L.exseq_profile_kernel_name.argtypes = [i32]
+    L.exact_seq_sum_f64_profiled.restype = i32
+    L.exact_seq_sum_f64_profiled.argtypes = [vp, sz, ctypes.c_double, vp, vp, sz, vp, u32, vp,
+                                             ctypes.POINTER(vp), i32]
     L.exseq_model_seq_sum_f64.restype = ctypes.c_double
     L.exseq_model_seq_sum_f64.argtypes = [vp, sz, ctypes.c_double, sz, u32, u32,
                                           ctypes.POINTER(Stats)]
     _lib = L
     return L
+
+
+def hip_runtimes_mapped():
+    """Paths of every libamdhip64 mapped into this process (expect one)."""
+    paths = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) >= 6 and "libamdhip64" in parts[-1]:
+                paths.add(parts[-1])
+    return sorted(paths)
 
 
 def declared_functions(header: str = HEADER):

@@ -55,6 +55,27 @@ int exact_seq_sum_f64(const double *x, size_t n, double init, double *out, void 
                             stats);
 }
 
+int exseq_profile_kernel_count(void) { return kPathKernelCount; }
+
+const char *exseq_profile_kernel_name(int i)
+{
+    return (i >= 0 && i < kPathKernelCount) ? kPathKernels[i] : "";
+}
+
+int exact_seq_sum_f64_profiled(const double *x, size_t n, double init, double *out, void *ws,
+                               size_t ws_bytes, exseq_stream_t stream, uint32_t flags,
+                               exseq_stats *stats, void *const *events, int n_events)
+{
+    if (!out || !aligned8(out) || (n && (!x || !aligned8(x))) || n == 0)
+        return EXSEQ_EINVAL;
+    if (!ws || ws_bytes < exact_seq_sum_f64_workspace_size(n))
+        return ws ? EXSEQ_EWORKSPACE : EXSEQ_EINVAL;
+    if (n_events < 0 || (n_events && !events))
+        return EXSEQ_EINVAL;
+    return launch_exact_sum(x, n, init, out, ws, reinterpret_cast<hipStream_t>(stream), flags,
+                            stats, events, n_events);
+}
+
 size_t exact_seq_sum_f64_batch_workspace_size(const size_t *ns, size_t count)
 {
     size_t mx = 256;

@@ -37,7 +37,10 @@ struct SumLayout {
 
 SumLayout sum_layout(size_t n);
 int launch_exact_sum(const double *x, size_t n, double init, double *out, void *ws,
-                     hipStream_t stream, uint32_t flags, exseq_stats *stats);
+                     hipStream_t stream, uint32_t flags, exseq_stats *stats,
+                     void *const *events = nullptr, int n_events = 0);
+extern const char *const kPathKernels[];
+extern const int kPathKernelCount;
 int launch_tree_sum(const double *x, size_t n, double *out, void *ws, hipStream_t stream);
 
 struct SsimLayout {

@@ -448,9 +448,19 @@ SumLayout sum_layout(size_t n)
     return L;
 }
 
+const char *const kPathKernels[] = {"chunk_tsum_kernel", "plan_kernel", "chunk_desc_kernel",
+                                     "walk_kernel"};
+const int kPathKernelCount = 4;
+
 int launch_exact_sum(const double *x, size_t n, double init, double *out, void *ws,
-                     hipStream_t stream, uint32_t flags, exseq_stats *stats)
+                     hipStream_t stream, uint32_t flags, exseq_stats *stats,
+                     void *const *events, int n_events)
 {
+    // events[2i] / events[2i+1] bracket kernel i when profiling.
+    auto mark = [&](int i) {
+        if (events && i < n_events && events[i])
+            hipEventRecord(static_cast<hipEvent_t>(events[i]), stream);
+    };
     if (n == 0) {
         hipLaunchKernelGGL(write_value_kernel, dim3(1), dim3(1), 0, stream, out, init);
         if (stats)
@@ -462,14 +472,22 @@ int launch_exact_sum(const double *x, size_t n, double init, double *out, void *
     double *tsum = reinterpret_cast<double *>(w + L.tsum_off);
     uint32_t *key = reinterpret_cast<uint32_t *>(w + L.key_off);
     DescRec *desc = reinterpret_cast<DescRec *>(w + L.desc_off);
+    mark(0);
     hipLaunchKernelGGL(chunk_tsum_kernel, dim3((unsigned)L.nch), dim3(kChunkThreads), 0,
                        stream, x, n, tsum);
+    mark(1);
+    mark(2);
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, tsum, L.nch,
                        init, flags, key);
+    mark(3);
+    mark(4);
     hipLaunchKernelGGL(chunk_desc_kernel, dim3((unsigned)L.nch), dim3(kChunkThreads), 0,
                        stream, x, n, key, desc);
+    mark(5);
+    mark(6);
     hipLaunchKernelGGL(walk_kernel, dim3(1), dim3(kWalkThreads), 0, stream, x, n, init,
                        desc, L.nch, out, stats);
+    mark(7);
     return hipGetLastError() == hipSuccess ? EXSEQ_OK : EXSEQ_EHIP;
 }
 

@@ -152,6 +152,22 @@ size_t tree_sum_f64_workspace_size(size_t n);
 int tree_sum_f64(const double *x, size_t n, double *out, void *ws,
                  size_t ws_bytes, exseq_stream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Profiling of the exact-sum path (used by the benchmark for per-kernel
+ * device time).  exseq_profile_kernel_count() kernels run, in order, for
+ * every n > 0; exseq_profile_kernel_name(i) names kernel i (static storage;
+ * "" out of range).  exact_seq_sum_f64_profiled() is exact_seq_sum_f64 (n > 0)
+ * that also records events[2i] just before and events[2i+1] just after
+ * kernel i on `stream`; `events` is a HOST array of n_events hipEvent_t
+ * handles created by the caller (NULL entries are skipped).
+ * ------------------------------------------------------------------------- */
+int exseq_profile_kernel_count(void);
+const char *exseq_profile_kernel_name(int i);
+int exact_seq_sum_f64_profiled(const double *x, size_t n, double init, double *out,
+                               void *ws, size_t ws_bytes, exseq_stream_t stream,
+                               uint32_t flags, exseq_stats *stats,
+                               void *const *events, int n_events);
+
 /* Text for an EXSEQ_* return code (static storage). */
 const char *exseq_strerror(int code);
 

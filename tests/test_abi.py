@@ -52,3 +52,11 @@ def test_argument_errors_return_before_any_launch():
 def test_built_for_gfx950():
     data = open(ex.LIB_PATH, "rb").read()
     assert b"gfx950" in data
+
+
+def test_single_hip_runtime():
+    """torch and libexseq.so share one HIP runtime (stream handles are valid
+    across them)."""
+    ex.lib()
+    maps = ex.hip_runtimes_mapped()
+    assert len(maps) == 1, maps
