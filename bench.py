@@ -172,7 +172,8 @@ def main():
         "plan_kernel": nch * 8 + nch * 4,
         "chunk_desc_kernel": n * TERM_BYTES + nch * 4 + nch * DESC_BYTES,
         "walk_kernel": nch * DESC_BYTES,
-        "chunk_pass_kernel": n * TERM_BYTES + nch * DESC_BYTES,
+        "chunk_pass_kernel": n * TERM_BYTES + nch * (DESC_BYTES + 8),
+        "tile_kernel": n * TERM_BYTES + nch * (3 * 8 + 4) + (nch // 4) * 8,
     }
     ab = alg_bytes.get(dominant, n * TERM_BYTES)
     achieved = ab / (avg_ms[dominant] * 1e-3) / 1e9

@@ -37,7 +37,9 @@ const char *exseq_strerror(int code)
     }
 }
 
-size_t exact_seq_sum_f64_workspace_size(size_t n) { return n ? sum_layout(n).total : 256; }
+size_t chunks_of(size_t n) { return (n + kChunk - 1) / kChunk; }
+
+size_t exact_seq_sum_f64_workspace_size(size_t n) { return sum_ws_bytes(padded_chunks(n)); }
 
 int exact_seq_sum_f64(const double *x, size_t n, double init, double *out, void *ws,
                       size_t ws_bytes, exseq_stream_t stream, uint32_t flags,
@@ -49,7 +51,7 @@ int exact_seq_sum_f64(const double *x, size_t n, double init, double *out, void 
         return EXSEQ_EINVAL;
     if (n && ws_bytes < exact_seq_sum_f64_workspace_size(n))
         return EXSEQ_EWORKSPACE;
-    if (n > ((size_t)1 << 40))
+    if (chunks_of(n) > 0xFFFFFFFFull)
         return EXSEQ_EINVAL;
     return launch_exact_sum(x, n, init, out, ws, reinterpret_cast<hipStream_t>(stream), flags,
                             stats);
@@ -76,14 +78,18 @@ int exact_seq_sum_f64_profiled(const double *x, size_t n, double init, double *o
                             stats, events, n_events);
 }
 
+// Sums go to the kernels in groups of kMaxBatch; the groups run one after
+// the other on the stream and reuse one workspace region.
 size_t exact_seq_sum_f64_batch_workspace_size(const size_t *ns, size_t count)
 {
-    size_t mx = 256;
-    for (size_t k = 0; ns && k < count; k++) {
-        size_t b = exact_seq_sum_f64_workspace_size(ns[k]);
-        mx = b > mx ? b : mx;
+    size_t mx = 0;
+    for (size_t g = 0; ns && g < count; g += kMaxBatch) {
+        size_t chunks = 0;
+        for (size_t k = g; k < count && k < g + kMaxBatch; k++)
+            chunks += padded_chunks(ns[k]);
+        mx = chunks > mx ? chunks : mx;
     }
-    return round256(mx);
+    return round256(sum_ws_bytes(mx));
 }
 
 int exact_seq_sum_f64_batch(const double *const *xs, const size_t *ns, const double *inits,
@@ -97,15 +103,28 @@ int exact_seq_sum_f64_batch(const double *const *xs, const size_t *ns, const dou
     for (size_t k = 0; k < count; k++) {
         if (ns[k] && (!xs[k] || !aligned8(xs[k])))
             return EXSEQ_EINVAL;
-        if (ns[k] > ((size_t)1 << 40))
+        if (chunks_of(ns[k]) > 0xFFFFFFFFull)
             return EXSEQ_EINVAL;
     }
     if (!ws || ws_bytes < exact_seq_sum_f64_batch_workspace_size(ns, count))
         return ws ? EXSEQ_EWORKSPACE : EXSEQ_EINVAL;
-    for (size_t k = 0; k < count; k++) {
-        int rc = launch_exact_sum(xs[k], ns[k], inits ? inits[k] : 0.0, outs + k, ws,
-                                  reinterpret_cast<hipStream_t>(stream), flags,
-                                  stats ? stats + k : nullptr);
+    for (size_t g = 0; g < count; g += kMaxBatch) {
+        BatchArgs a{};
+        a.count = (int)(count - g < (size_t)kMaxBatch ? count - g : (size_t)kMaxBatch);
+        a.flags = flags;
+        uint64_t chunks = 0;
+        for (int k = 0; k < a.count; k++) {
+            a.x[k] = xs[g + k];
+            a.n[k] = ns[g + k];
+            a.init[k] = inits ? inits[g + k] : 0.0;
+            a.chunk_base[k] = (uint32_t)chunks;
+            chunks += padded_chunks(ns[g + k]);
+        }
+        if (chunks > 0xFFFFFFFFull)
+            return EXSEQ_EINVAL;
+        a.chunk_base[a.count] = (uint32_t)chunks;
+        int rc = launch_batch(a, ws, outs + g, reinterpret_cast<hipStream_t>(stream),
+                              stats ? stats + g : nullptr);
         if (rc != EXSEQ_OK)
             return rc;
     }
@@ -140,7 +159,7 @@ int ssim_term_and_sum(const uint8_t *ref, const uint8_t *dis, int width, int hei
                            flags, stats);
 }
 
-size_t tree_sum_f64_workspace_size(size_t n) { return n ? sum_layout(n).total : 256; }
+size_t tree_sum_f64_workspace_size(size_t n) { return round256(chunks_of(n) * sizeof(double)) + 256; }
 
 int tree_sum_f64(const double *x, size_t n, double *out, void *ws, size_t ws_bytes,
                  exseq_stream_t stream)

@@ -13,9 +13,22 @@ namespace exseq {
 constexpr int kChunk = EXSEQ_CHUNK_TERMS;  // terms per chunk
 constexpr int kChunkThreads = 256;         // 4 waves x 64 lanes x 4 terms
 constexpr int kPlanThreads = 1024;
-constexpr int kWalkThreads = 256;
+constexpr int kWalkThreads = 256;          // one walk workgroup: 4 waves x 4 items
+constexpr int kMaxBatch = 64;              // sums per launch (kernel arguments)
 
 static_assert(kChunk == kChunkThreads * 4, "a lane holds 4 consecutive terms");
+
+// Chunks per workgroup of the chunk pass (a tile); each sum's chunk range is
+// padded to a multiple of the largest tile.  Bits 4..5 of `flags` choose the
+// tile (0 = default 4, 1, 2 or 3 = 4 chunks), a tuning knob.
+constexpr int kTileMax = 4;
+constexpr uint32_t kTileShift = 4;
+
+inline size_t padded_chunks(size_t n)
+{
+    const size_t c = (n + kChunk - 1) / kChunk;
+    return (c + kTileMax - 1) / kTileMax * kTileMax;
+}
 
 // One chunk's descriptor (32 bytes): the increment for an even start count
 // (the odd one differs by -1, 0 or +1, kept in meta), the prefix bounds, and
@@ -29,13 +42,36 @@ struct alignas(16) DescRec {
 };
 static_assert(sizeof(DescRec) == 32, "descriptor is 32 bytes");
 
-struct SumLayout {
-    size_t nch;
-    size_t tsum_off, key_off, desc_off;
-    size_t total;
+// Up to kMaxBatch independent sums, passed to the kernels by value.  Sum k
+// owns the global chunks [chunk_base[k], chunk_base[k + 1]) (its chunks,
+// padded to a multiple of kTileMax).
+struct BatchArgs {
+    int count;
+    uint32_t flags;
+    uint32_t epoch;  // tags this launch's look-back status words
+    uint32_t pad_;
+    const double *x[kMaxBatch];
+    uint64_t n[kMaxBatch];
+    double init[kMaxBatch];
+    uint32_t chunk_base[kMaxBatch + 1];
 };
 
-SumLayout sum_layout(size_t n);
+// Descriptors live in four arrays (structure of arrays, so that the walk
+// reads what it needs with coalesced loads): r0, lo, hi (int64) and meta =
+// key | (r1 - r0 + 1) << 12 | flags.  For a chunk with kFlagExact, lo holds
+// the bits of the exact running sum after it instead.
+struct DescArrays {
+    int64_t *r0;
+    int64_t *lo;
+    int64_t *hi;
+    uint32_t *meta;
+};
+
+// Workspace of a launch over `total_chunks` chunks: status words, then the
+// descriptor arrays.
+size_t sum_ws_bytes(size_t total_chunks);
+int launch_batch(const BatchArgs &a, void *ws, double *outs, hipStream_t stream,
+                 exseq_stats *stats, void *const *events = nullptr, int n_events = 0);
 int launch_exact_sum(const double *x, size_t n, double init, double *out, void *ws,
                      hipStream_t stream, uint32_t flags, exseq_stats *stats,
                      void *const *events = nullptr, int n_events = 0);

@@ -88,7 +88,7 @@ SsimLayout ssim_layout(int width, int height)
     const size_t n = (size_t)width * (size_t)height;
     L.plane_off = 0;
     L.sum_off = (n * sizeof(double) + 255) & ~(size_t)255;
-    L.total = L.sum_off + sum_layout(n).total;
+    L.total = L.sum_off + sum_ws_bytes(padded_chunks(n));
     return L;
 }
 

@@ -97,7 +97,9 @@ def test_tie_fast_path_suite():
         x = si.tie_suite(1 << 20, seed)
         got, st = gpu_sum(torch, x, 1.0, stats=True)
         assert same(got, oracle.seq_sum(x, 1.0))
-        assert st["fallback_chunks"] == 0, st
+        # only the first chunk, added in order from init by its tile
+        assert st["fallback_chunks"] <= 1, st
+        assert st["fast_chunks"] + st["fallback_chunks"] == st["chunks"], st
 
 
 def test_exhaustive_short_sequences():
