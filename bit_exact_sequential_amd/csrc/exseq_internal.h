@@ -48,8 +48,8 @@ static_assert(sizeof(DescRec) == 32, "descriptor is 32 bytes");
 struct BatchArgs {
     int count;
     uint32_t flags;
-    uint32_t epoch;  // tags this launch's look-back status words
-    uint32_t pad_;
+    uint32_t epoch;      // tags this launch's look-back status words
+    uint32_t rec_slots;  // crossing records this launch may allocate
     const double *x[kMaxBatch];
     uint64_t n[kMaxBatch];
     double init[kMaxBatch];
@@ -67,8 +67,16 @@ struct DescArrays {
     uint32_t *meta;
 };
 
-// Workspace of a launch over `total_chunks` chunks: status words, then the
-// descriptor arrays.
+// Crossing records: a counter of allocated slots (reset by the walk for the
+// next launch; any value is safe, slots past the limit are simply not made)
+// and the slots, 2 x 1024 packed prefix pairs each.
+struct RecArea {
+    uint32_t *counter;
+    int64_t *data;
+};
+
+// Workspace of a launch over `total_chunks` chunks: record counter, status
+// words, the descriptor arrays, the crossing records.
 size_t sum_ws_bytes(size_t total_chunks);
 int launch_batch(const BatchArgs &a, void *ws, double *outs, hipStream_t stream,
                  exseq_stats *stats, void *const *events = nullptr, int n_events = 0);

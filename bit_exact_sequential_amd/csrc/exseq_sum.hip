@@ -292,6 +292,72 @@ __device__ __forceinline__ void store_desc(const DescArrays &d, size_t c, uint32
                 (cross ? kFlagCross : 0u);
 }
 
+// ---------------------------------------------------------------------------
+// Crossing records.  For a chunk whose plan expects the running sum to cross
+// into the next binade, the tile also stores, for every term position, the
+// increment pair of the prefix ending there under the planned binade and
+// under the next one (packed as r0 << 2 | (r1 - r0 + 1)).  Given the exact
+// start count, the walk then finds the term that crosses, adds it with one
+// fp64 add, and takes the rest of the chunk from the second prefix.
+// Records exist only for chunks with no negative scaled term and nothing bad
+// under either binade.
+// ---------------------------------------------------------------------------
+constexpr int64_t kRecMax = (int64_t)1 << 56;  // larger prefixes are clamped (never apply)
+
+__device__ __forceinline__ int64_t rec_pack(Pair p)
+{
+    const int64_t r0 = p.r0 < kRecMax ? p.r0 : kRecMax;
+    return (r0 << 2) | (p.r1 - p.r0 + 1);
+}
+__device__ __forceinline__ Pair rec_unpack(int64_t v)
+{
+    const int64_t r0 = v >> 2;
+    return Pair{r0, r0 + (v & 3) - 1};
+}
+
+// Inclusive prefix pairs of the workgroup's 1024 terms under `key`, written
+// to out[0 .. 1023]; returns (uniformly) whether any term was bad or
+// negative under that key.  One barrier.
+__device__ __forceinline__ bool record_prefix(const Four &f, uint32_t key, int64_t *out,
+                                              Pair *lds_wtot, bool *lds_flag)
+{
+    const int scale = 1075 - (int)(key & 0x7FFu);
+    const bool sgn = (key >> 11) & 1u;
+    Pair acc[4];
+    bool bad = false;
+    Pair a = pair_identity();
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        if (i < f.cnt) {
+            const TermInc ti = term_inc(f.v[i], scale, sgn);
+            bad |= ti.bad || ti.neg;
+            a = compose(a, Pair{ti.r0, ti.r1});
+        }
+        acc[i] = a;
+    }
+    const Pair inc = wave_incl_scan_pair(a);
+    const bool wbad = __ballot(bad) != 0;
+    const int lane = lane_id(), wave = wave_id();
+    if (lane == 63)
+        lds_wtot[wave] = inc;
+    if (lane == 0)
+        lds_flag[wave] = wbad;
+    __syncthreads();
+    Pair pre = pair_identity();
+    bool any = false;
+#pragma unroll
+    for (int w = 0; w < kChunkThreads / 64; w++) {
+        if (w < wave)
+            pre = compose(pre, lds_wtot[w]);
+        any |= lds_flag[w];
+    }
+    pre = compose(pre, wave_shift_pair(inc));
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        out[threadIdx.x * 4 + i] = rec_pack(compose(pre, acc[i]));
+    return any;
+}
+
 // acc + t[lo] + t[lo+1] + ... + t[hi-1], one add at a time in that order (the
 // loop itself), on one lane.  The LDS reads go out eight at a time so that
 // only the chain of adds is serial.
@@ -331,13 +397,16 @@ __device__ __forceinline__ int find_sum(const BatchArgs &a, uint32_t g)
 template <int CPB>
 __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a,
                                                              uint64_t *__restrict__ status,
-                                                             DescArrays d)
+                                                             DescArrays d, RecArea rec)
 {
     constexpr int kW = kChunkThreads / 64;
     __shared__ double lds_t[CPB][kW];
     __shared__ WaveRun lds_runs[CPB][kW];
     __shared__ double lds_p;
     __shared__ double lds_terms[kChunk];
+    __shared__ Pair lds_wtot[2][kW];
+    __shared__ bool lds_flag[2][kW];
+    __shared__ int lds_slot;
     const uint32_t g0 = blockIdx.x * CPB;  // first global chunk of the tile
     const int s = find_sum(a, g0);
     const double *__restrict__ x = a.x[s];
@@ -390,12 +459,13 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a,
             store_relaxed_u64(st0 + tl, st_pack(a.epoch, kStIncl, P + Ttile));
     }
 
-    uint32_t key[CPB];
+    uint32_t key[CPB], key2[CPB];
     bool cross[CPB];
 #pragma unroll
     for (int k = 0; k < CPB; k++) {
         key[k] = plan_key(P, a.flags);
-        cross[k] = key_of(P + T[k]) != key_of(P);
+        key2[k] = key_of(P + T[k]);
+        cross[k] = key2[k] != key_of(P);
         P += T[k];
     }
 #pragma unroll
@@ -428,6 +498,31 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a,
                     cc = cross[j];
                 }
             store_desc(d, (size_t)(g0 + k), kk, join_waves(lds_runs[k]), cc);
+        }
+    }
+
+    // crossing records (see record_prefix)
+#pragma unroll
+    for (int k = 0; k < CPB; k++) {
+        if (!cross[k] || c0 + k >= nch || c0 + k == 0 || !key_has_fast_path(key[k]) ||
+            !key_has_fast_path(key2[k]) || ((key[k] ^ key2[k]) & 0x800u) ||
+            (join_waves(lds_runs[k]).flags & (kFlagNeg | kFlagBad | kFlagNonFinite)))
+            continue;
+        if (threadIdx.x == 0)
+            lds_slot = (int)atomicAdd(rec.counter, 1u);
+        __syncthreads();
+        const int slot = lds_slot;
+        __syncthreads();  // every lane has read the slot before it is reused
+        if (slot < 0 || slot >= (int)a.rec_slots)
+            continue;
+        int64_t *r = rec.data + (size_t)slot * 2 * kChunk;
+        const bool bad1 = record_prefix(f[k], key[k], r, lds_wtot[0], lds_flag[0]);
+        const bool bad2 = record_prefix(f[k], key2[k], r + kChunk, lds_wtot[1], lds_flag[1]);
+        if (threadIdx.x == 0 && !bad1 && !bad2) {
+            const size_t c = (size_t)(g0 + k);
+            d.lo[c] = (int64_t)key2[k];
+            d.hi[c] = slot;
+            d.meta[c] |= kFlagRecord;
         }
     }
 
@@ -472,13 +567,16 @@ struct Cand {
     int ok2;        // chunk applies after renormalising (1), misplanned (2)
     double s_at;    // exact sum at the item (or after the item's plain add)
     double s_next;  // exact sum after the chunk when ok2 == 1
-    Pair ex_after;  // window prefix through the chunk
+    Pair ex_after;  // window prefix through the chunk (a record's second prefix)
+    int rec;        // the chunk's crossing record, or -1
+    uint32_t key, key2;  // the chunk's planned binade and the record's next one
 };
 
 struct WalkLds {
     Pair tot[2][kWaves];   // per-wave totals of a scan (double-buffered)
     Cand cand[2][kWaves];  // per-wave candidates (double-buffered)
     double endv[2];        // a round's end state, from the lane holding the last item
+    Pair lastp[2];         // a record's last second-binade prefix
     int flag[2][kWaves];
     double terms[kChunk];  // a chunk's terms, for the one-lane path
 };
@@ -561,14 +659,16 @@ __device__ __forceinline__ Cand block_first(bool has, const Cand &mine, WalkLds 
         sh.cand[buf][wave] = mine;
     }
     __syncthreads();
-    Cand best = sh.cand[buf][0];
+    int bw = 0, bi = sh.cand[buf][0].idx;
 #pragma unroll
     for (int k = 1; k < kWaves; k++) {
-        const Cand c = sh.cand[buf][k];
-        if (c.idx < best.idx)
-            best = c;
+        const int i = sh.cand[buf][k].idx;
+        if (i < bi) {
+            bi = i;
+            bw = k;
+        }
     }
-    return best;
+    return sh.cand[buf][bw];
 }
 
 __device__ __forceinline__ Cand cand_none()
@@ -579,12 +679,14 @@ __device__ __forceinline__ Cand cand_none()
     c.s_at = 0.0;
     c.s_next = 0.0;
     c.ex_after = pair_identity();
+    c.rec = -1;
+    c.key = c.key2 = 0u;
     return c;
 }
 
 // Exact resolution of one chunk from the exact running sum S.
 __device__ double resolve_chunk(const double *__restrict__ x, size_t n, size_t c, double S,
-                                WalkLds &sh, int &buf)
+                                int pos, WalkLds &sh, int &buf)
 {
     const int t = threadIdx.x;
     const size_t b = c * kChunk;
@@ -596,7 +698,6 @@ __device__ double resolve_chunk(const double *__restrict__ x, size_t n, size_t c
         xv[k] = f.v[k];
         sh.terms[kPer * t + k] = xv[k];  // visible after the next barrier
     }
-    int pos = 0;
     int shorts = 0;
     while (pos < len) {
         const uint64_t sb = dbits(S);
@@ -745,7 +846,121 @@ __device__ double resolve_chunk(const double *__restrict__ x, size_t n, size_t c
     return S;
 }
 
+// A crossing chunk from its record, given the exact sum S at its start (in
+// the chunk's planned binade).  One barrier.  Returns done with the sum
+// after the chunk, or not done with the state after the crossing term and
+// the position to continue term by term from.
+struct RecOut {
+    bool done;
+    double S;
+    int pos;
+};
+
+// This lane's share of a record chunk: its terms and packed prefixes (loaded
+// ahead of need, so that the resolve does not wait for memory).
+struct RecPre {
+    Four f;
+    int64_t pe[kPer], pe2[kPer], prev;
+    int len;
+};
+
+__device__ __forceinline__ RecPre rec_load(const double *__restrict__ x, size_t n, size_t c,
+                                           const int64_t *__restrict__ rec)
+{
+    RecPre r;
+    const int t = threadIdx.x;
+    const size_t b = c * kChunk;
+    r.len = (int)(n - b < (size_t)kChunk ? n - b : (size_t)kChunk);
+    r.f = load_four(x, n, b + (size_t)kPer * t, false);
+#pragma unroll
+    for (int k = 0; k < kPer; k++) {
+        const int i = kPer * t + k;
+        r.pe[k] = i < r.len ? rec[i] : 1;
+        r.pe2[k] = i < r.len ? rec[kChunk + i] : 1;
+    }
+    r.prev = t > 0 && kPer * t - 1 < r.len ? rec[kPer * t - 1] : 1;  // 1: packed identity
+    return r;
+}
+
+__device__ RecOut resolve_with_record(const RecPre &R, double S, uint32_t key2, WalkLds &sh,
+                                      int &buf)
+{
+    const int t = threadIdx.x;
+    const int len = R.len;
+    const Four &f = R.f;
+    const uint32_t key = key_of(S);
+    const int64_t m = count_of(S);
+    int64_t pe[kPer], pe2[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; k++) {
+        pe[k] = R.pe[k];
+        pe2[k] = R.pe2[k];
+    }
+    const int64_t prev = R.prev;
+    int64_t cnt[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; k++)
+        cnt[k] = m + pair_at(rec_unpack(pe[k]), m);
+    Cand mine = cand_none();
+    int firstk = -1;
+#pragma unroll
+    for (int k = kPer - 1; k >= 0; k--) {
+        const int i = kPer * t + k;
+        if (i < len && (cnt[k] < kCountLo + 1 || cnt[k] > kCountHi - 1))
+            firstk = k;
+    }
+    if (firstk >= 0) {
+        int64_t cb = m + pair_at(rec_unpack(prev), m);
+        double xf = f.v[0];
+        int64_t p2 = pe2[0];
+#pragma unroll
+        for (int k = 1; k < kPer; k++)
+            if (k == firstk) {
+                cb = cnt[k - 1];
+                xf = f.v[k];
+                p2 = pe2[k];
+            }
+        const int i = kPer * t + firstk;
+        mine.idx = i;
+        mine.s_at = ((i == 0) ? S : assemble(key, cb)) + xf;  // the one plain add
+        mine.ex_after = rec_unpack(p2);
+    }
+    if ((len - 1) / kPer == t) {
+        const int kl = (len - 1) - kPer * t;
+#pragma unroll
+        for (int k = 0; k < kPer; k++)
+            if (k == kl) {
+                sh.endv[buf] = assemble(key, cnt[k]);
+                sh.lastp[buf] = rec_unpack(pe2[k]);
+            }
+    }
+    const Cand fr = block_first(firstk >= 0, mine, sh, buf);
+    const double endv = sh.endv[buf];
+    const Pair lastp = sh.lastp[buf];
+    buf ^= 1;
+    if (fr.idx == kNone)
+        return RecOut{true, endv, len};
+    const double s2 = fr.s_at;
+    if (fr.idx == len - 1)
+        return RecOut{true, s2, len};
+    const uint32_t k2 = key_of(s2);
+    const int64_t m2 = count_of(s2);
+    const Pair at = fr.ex_after;
+    int p = -1;
+    if ((at.r0 & 1) == (m2 & 1))
+        p = 0;
+    else if (((1 + at.r1) & 1) == (m2 & 1))
+        p = 1;
+    if (k2 != key2 || !key_has_fast_path(k2) || p < 0)
+        return RecOut{false, s2, fr.idx + 1};
+    const int64_t cnt_end = m2 + ((p ? lastp.r1 : lastp.r0) - (p ? at.r1 : at.r0));
+    if (cnt_end > kCountHi)
+        return RecOut{false, s2, fr.idx + 1};  // a second crossing
+    return RecOut{true, assemble(k2, cnt_end), len};
+}
+
 __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, DescArrays dall,
+                                                            RecArea rec,
                                                             double *__restrict__ outs,
                                                             exseq_stats *__restrict__ stats)
 {
@@ -800,6 +1015,7 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, DescArr
             nmeta[k] = i < nch ? dmeta[i] : kFlagBad;
         }
         uint32_t dkey[kPer], dfl[kPer];
+        bool drec[kPer];
         Pair mine[kPer];
         bool lane_tie = false, lane_nf = false, lane_clean = true;
         int64_t lane_sum = 0;
@@ -809,6 +1025,7 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, DescArr
             const bool have = kPer * t + k < cnt;
             dkey[k] = have ? (meta[k] & kKeyMask) : 0u;
             dfl[k] = have ? (meta[k] & (kFlagNeg | kFlagBad | kFlagNonFinite)) : kFlagBad;
+            drec[k] = have && (meta[k] & kFlagRecord) != 0;
             const int64_t d1 = (int64_t)((meta[k] >> kDrShift) & 3u) - 1;
             mine[k] = have ? Pair{r0[k], r0[k] + d1} : pair_identity();
             if (have) {
@@ -837,7 +1054,7 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, DescArr
 #pragma unroll
         for (int k = 0; k < kPer; k++) {
             dlo[k] = dhi[k] = 0;
-            if (dfl[k] & kFlagNeg) {
+            if ((dfl[k] & kFlagNeg) || drec[k]) {
                 dlo[k] = dlo_a[base + kPer * t + k];
                 dhi[k] = dhi_a[base + kPer * t + k];
             }
@@ -897,6 +1114,7 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, DescArr
             int fk = -1;
             int64_t fmt = 0, flo = 0, fhi = 0;
             uint32_t fkey = 0, ffl = 0;
+            bool frec = false;
             Pair fmine = pair_identity(), fex = pair_identity();
 #pragma unroll
             for (int k = kPer - 1; k >= 0; k--) {
@@ -914,6 +1132,7 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, DescArr
                         ffl = dfl[k];
                         fmine = mine[k];
                         fex = ex[k];
+                        frec = drec[k];
                     }
                 }
             }
@@ -931,6 +1150,11 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, DescArr
                 mc.s_at = sat;
                 mc.s_next = ok2 ? assemble(k2, m2 + pair_at(fmine, m2)) : 0.0;
                 mc.ex_after = compose(fex, fmine);
+                mc.key = fkey;
+                if (frec) {
+                    mc.rec = (int)fhi;
+                    mc.key2 = (uint32_t)flo;
+                }
             }
             // the lane holding the window's last chunk reports the end state
             const int lastk = (cnt - 1) - kPer * t;
@@ -959,7 +1183,13 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, DescArr
             } else {
                 misses += fc.ok2 == 2;
                 const size_t c = base + (size_t)fc.idx;
-                S = resolve_chunk(x, n, c, fc.s_at, sh, buf);
+                if (fc.rec >= 0 && key_of(fc.s_at) == fc.key) {
+                    const RecPre R = rec_load(x, n, c, rec.data + (size_t)fc.rec * 2 * kChunk);
+                    const RecOut r = resolve_with_record(R, fc.s_at, fc.key2, sh, buf);
+                    S = r.done ? r.S : resolve_chunk(x, n, c, r.S, r.pos, sh, buf);
+                } else {
+                    S = resolve_chunk(x, n, c, fc.s_at, 0, sh, buf);
+                }
                 n_fb++;
                 fb_terms += (n - c * kChunk < (size_t)kChunk) ? n - c * kChunk : (size_t)kChunk;
                 if (first_fb < 0)
@@ -969,6 +1199,9 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, DescArr
         }
     }
     if (t == 0) {
+        // the next launch (after this one, in stream order) numbers records from 0
+        if (s == 0)
+            *rec.counter = 0u;
         outs[s] = S;
         if (stats) {
             exseq_stats st;
@@ -1028,6 +1261,7 @@ uint32_t next_epoch()
 struct WsParts {
     uint64_t *status;
     DescArrays d;
+    RecArea rec;
 };
 
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -1036,6 +1270,8 @@ WsParts carve(void *ws, size_t total)
 {
     char *w = static_cast<char *>(ws);
     WsParts p;
+    p.rec.counter = reinterpret_cast<uint32_t *>(w);
+    w += 256;
     p.status = reinterpret_cast<uint64_t *>(w);
     w += round256(total * sizeof(uint64_t));
     p.d.r0 = reinterpret_cast<int64_t *>(w);
@@ -1045,6 +1281,8 @@ WsParts carve(void *ws, size_t total)
     p.d.hi = reinterpret_cast<int64_t *>(w);
     w += round256(total * sizeof(int64_t));
     p.d.meta = reinterpret_cast<uint32_t *>(w);
+    w += round256(total * sizeof(uint32_t));
+    p.rec.data = reinterpret_cast<int64_t *>(w);
     return p;
 }
 }  // namespace
@@ -1052,10 +1290,19 @@ WsParts carve(void *ws, size_t total)
 const char *const kPathKernels[] = {"tile_kernel", "walk_kernel"};
 const int kPathKernelCount = 2;
 
+// Records a launch may make: about one per binade a sum crosses is needed;
+// one slot per 8 chunks (16 to 512) leaves room for mis-planned ones.
+size_t rec_slots(size_t total_chunks)
+{
+    const size_t s = total_chunks / 8;
+    return s < 16 ? 16 : (s > 512 ? 512 : s);
+}
+
 size_t sum_ws_bytes(size_t total_chunks)
 {
-    return 4 * round256(total_chunks * sizeof(int64_t)) + round256(total_chunks * sizeof(uint32_t)) +
-           256;
+    return 256 + 4 * round256(total_chunks * sizeof(int64_t)) +
+           round256(total_chunks * sizeof(uint32_t)) +
+           rec_slots(total_chunks) * 2 * kChunk * sizeof(int64_t) + 256;
 }
 
 template <int CPB>
@@ -1065,7 +1312,7 @@ static void launch_tiles(const BatchArgs &args, uint32_t total, const WsParts &p
     const unsigned tiles = total / CPB;
     if (tiles)
         hipLaunchKernelGGL(tile_kernel<CPB>, dim3(tiles), dim3(kChunkThreads), 0, stream, args,
-                           p.status, p.d);
+                           p.status, p.d, p.rec);
 }
 
 int launch_batch(const BatchArgs &a, void *ws, double *outs, hipStream_t stream,
@@ -1079,6 +1326,7 @@ int launch_batch(const BatchArgs &a, void *ws, double *outs, hipStream_t stream,
     const WsParts p = carve(ws, total);
     BatchArgs args = a;
     args.epoch = next_epoch();
+    args.rec_slots = (uint32_t)rec_slots(total);
     const uint32_t tile = (a.flags >> kTileShift) & 3u;  // 0: default
     mark(0);
     if (tile == 1)
@@ -1090,7 +1338,7 @@ int launch_batch(const BatchArgs &a, void *ws, double *outs, hipStream_t stream,
     mark(1);
     mark(2);
     hipLaunchKernelGGL(walk_kernel, dim3((unsigned)a.count), dim3(kWalkThreads), 0, stream, args,
-                       p.d, outs, stats);
+                       p.d, p.rec, outs, stats);
     mark(3);
     return hipGetLastError() == hipSuccess ? EXSEQ_OK : EXSEQ_EHIP;
 }

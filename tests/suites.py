@@ -47,6 +47,15 @@ def edge_suite():
         ("start_nan", si.uniform(2000, 14), math.nan),
         ("start_inf", si.uniform(2000, 15), -math.inf),
         ("max_finite", np.full(1500, 1e307), 1.7e308),
+        # the running sum doubles every ~700 terms: crossings in the middle of
+        # chunks, sometimes two in one chunk
+        ("geometric_growth", 2.0 ** (np.arange(20000) / 700.0) * si.uniform(20000, 16), 0.0),
+        # exactly 256 per chunk from 256: every crossing lands on a chunk's
+        # last term
+        ("crossing_on_last_term", np.full(16384, 0.25), 256.0),
+        # a chunk whose sum is three times the running sum (two crossings)
+        ("triple_jump", np.concatenate([np.full(4096, 0.5), np.full(1024, 6.0),
+                                        np.full(4096, 0.5)]), 0.0),
     ]
     return out
 
