@@ -33,6 +33,15 @@ def plan_fixed(key: int) -> int:
     return PLAN_FIXED | ((key & 0xFFF) << 8)
 
 
+WALK_ONLY = 1 << 6
+CHAIN_CUT = 1 << 7
+
+
+def tile_flag(chunks_per_tile: int) -> int:
+    """Flags that choose the chunks per tile of the single pass (1, 2 or 4)."""
+    return {1: 1, 2: 2, 4: 3}[chunks_per_tile] << 4
+
+
 MUT_TIE_UP = 1
 MUT_NO_BINADE_CHECK = 2
 MUT_NO_UPPER_CHECK = 4

@@ -30,26 +30,14 @@ inline size_t padded_chunks(size_t n)
     return (c + kTileMax - 1) / kTileMax * kTileMax;
 }
 
-// One chunk's descriptor (32 bytes): the increment for an even start count
-// (the odd one differs by -1, 0 or +1, kept in meta), the prefix bounds, and
-// meta = plan key | (r1 - r0 + 1) << 12 | flags.
-struct alignas(16) DescRec {
-    int64_t r0;
-    int64_t lo;
-    int64_t hi;
-    uint32_t meta;
-    uint32_t aux;
-};
-static_assert(sizeof(DescRec) == 32, "descriptor is 32 bytes");
-
 // Up to kMaxBatch independent sums, passed to the kernels by value.  Sum k
 // owns the global chunks [chunk_base[k], chunk_base[k + 1]) (its chunks,
 // padded to a multiple of kTileMax).
 struct BatchArgs {
     int count;
     uint32_t flags;
-    uint32_t epoch;      // tags this launch's look-back status words
-    uint32_t rec_slots;  // crossing records this launch may allocate
+    uint32_t epoch;  // tags this launch's look-back status words
+    uint32_t tile;   // chunks per tile (1, 2 or 4)
     const double *x[kMaxBatch];
     uint64_t n[kMaxBatch];
     double init[kMaxBatch];
@@ -67,16 +55,17 @@ struct DescArrays {
     uint32_t *meta;
 };
 
-// Crossing records: a counter of allocated slots (reset by the walk for the
-// next launch; any value is safe, slots past the limit are simply not made)
-// and the slots, 2 x 1024 packed prefix pairs each.
-struct RecArea {
-    uint32_t *counter;
-    int64_t *data;
+// The exact chain between the tiles of a sum (zeroed before every launch;
+// a published word is never zero): per tile, four words describing it
+// (agg: meta, r0, lo, hi of the composition of its chunks, or "irregular")
+// and the exact running sum after it (incl, irregular tiles only).
+struct ChainArea {
+    uint64_t *agg;
+    uint64_t *incl;
 };
 
-// Workspace of a launch over `total_chunks` chunks: record counter, status
-// words, the descriptor arrays, the crossing records.
+// Workspace of a launch over `total_chunks` chunks: plan status words, the
+// descriptor arrays, the chain words.
 size_t sum_ws_bytes(size_t total_chunks);
 int launch_batch(const BatchArgs &a, void *ws, double *outs, hipStream_t stream,
                  exseq_stats *stats, void *const *events = nullptr, int n_events = 0);

@@ -57,7 +57,7 @@ constexpr uint32_t kFlagBad = 1u << 15;  // some term had |y| >= 2^51 or was NaN
 constexpr uint32_t kFlagNonFinite = 1u << 16;  // some term was +-inf or NaN
 constexpr uint32_t kFlagCross = 1u << 17;      // the plan expects a binade crossing
 constexpr uint32_t kFlagExact = 1u << 18;      // the exact sum after the chunk is known
-constexpr uint32_t kFlagRecord = 1u << 19;     // a crossing record exists (slot in hi)
+constexpr uint32_t kFlagResolved = 1u << 19;   // the chunk was added term by term
 
 EXSEQ_HD uint64_t dbits(double x) { return __builtin_bit_cast(uint64_t, x); }
 EXSEQ_HD double bitsd(uint64_t b) { return __builtin_bit_cast(double, b); }

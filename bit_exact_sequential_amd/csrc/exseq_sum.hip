@@ -5,6 +5,7 @@
 // frame sum", Findings 3).  A chunk is 1024 consecutive terms, held by 256
 // lanes (4 waves of 64) with 4 consecutive terms per lane.
 //
+//  chain_clear_kernel: zeroes the chain words of the launch's tiles.
 //  tile_kernel (one workgroup per tile of CPB consecutive chunks of one sum;
 //  every tile of every sum of a batch in one launch; reads each term once):
 //    1. load the tile's terms (16-byte non-temporal loads), fixed-tree fp64
@@ -15,26 +16,37 @@
 //       is that of the prefix before it;
 //    3. every term's increment pair under its chunk's planned binade,
 //       composed in order (lane, ordered wave scan, waves in order) into the
-//       chunk's descriptor: the pair, prefix bounds, flags;
-//    4. the tile holding a sum's first chunk knows its exact start state
-//       (init): one lane adds its terms in order and records the exact sum
-//       after it, off the walk's critical path.
+//       chunk's run: the pair, prefix bounds, flags;
+//    4. the exact chain.  A tile whose chunks all share one planned binade
+//       and stay clear of its edges (with a margin for the plan's error) is
+//       regular: it publishes the composition of its runs and is done.  Any
+//       other tile (a sum's first and last tile among them) waits for the
+//       exact sum after the nearest irregular tile before it, applies the
+//       composed runs of the regular tiles in between (checked against the
+//       binade), adds its own chunks in order -- a run where it applies, term
+//       by term from the exact sum where it does not -- and publishes the
+//       exact sum after itself.  The last tile's value is the result.
 //  walk_kernel (one workgroup of 256 lanes per sum, after the tiles):
-//    5. follows the chunks in order with the exact running sum, a window of
-//       1024 chunks at a time.  A clean window (every chunk in the running
-//       sum's binade, no tie, nothing negative or bad) is applied from the
-//       sum of its increments; otherwise one scan gives every chunk's start
-//       count, every chunk is checked at its exact start, and the first one
-//       that fails is added term by term from the exact sum;
+//    5. takes the last tile's exact sum.  Where the chain could not finish
+//       (a wait that timed out, a composed run that did not apply), it
+//       resumes from the last exact sum the chain published and follows the
+//       remaining chunks in order, a window of 1024 chunks at a time: a
+//       clean window (every chunk in the running sum's binade, no tie,
+//       nothing negative or bad) is applied from the sum of its increments;
+//       otherwise one scan gives every chunk's start count, every chunk is
+//       checked at its exact start, and the first one that fails is added
+//       term by term from the exact sum;
 //    6. term by term means: every lane forms its terms' increments in the
 //       current binade, a workgroup scan gives every prefix count, the first
 //       term that leaves the binade is added with one fp64 add, and the next
 //       round starts after it; when rounds keep resolving only a few terms,
 //       one lane adds the rest in order.
 //
-// The look-back waits are bounded: a workgroup that waits too long gives up
-// its plan (no fast path for its chunks).  A plan never changes a result,
-// only how much is added term by term.
+// Every wait is bounded: a plan wait that times out gives up the tile's
+// plan (no fast path for its chunks), a chain wait that times out reports
+// failure to the tiles after it and leaves the rest to the walk.  Neither a
+// plan nor the chain ever changes a result, only where and how much is added
+// term by term.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -54,6 +66,32 @@ struct Four {
     double v[4];
     int cnt;  // how many of the four exist (0..4)
 };
+
+// A value the compiler must treat as opaque.  Picking one of several
+// register values by a run-time index (unrolled selects) is otherwise turned
+// back into an indexed load from a stack copy, i.e. scratch memory.
+__device__ __forceinline__ double opaque(double x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
+}
+__device__ __forceinline__ int64_t opaque(int64_t x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
+}
+__device__ __forceinline__ uint32_t opaque(uint32_t x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
+}
+__device__ __forceinline__ Four opaque(Four f)
+{
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        f.v[i] = opaque(f.v[i]);
+    return f;
+}
 
 typedef double v2f64 __attribute__((ext_vector_type(2)));
 
@@ -272,11 +310,10 @@ __device__ __forceinline__ WaveRun join_waves(const WaveRun *w)
     return r;
 }
 
-__device__ __forceinline__ void store_desc(const DescArrays &d, size_t c, uint32_t key, WaveRun r,
-                                           bool cross)
+// A run whose increment exceeds the width of a binade can never apply;
+// clearing it keeps every sum of runs far from int64 overflow.
+__device__ __forceinline__ WaveRun clamp_run(WaveRun r)
 {
-    // A run whose increment exceeds the width of a binade can never apply;
-    // clearing it keeps every sum of descriptors far from int64 overflow.
     const int64_t lim = kCountLo + 1;
     if (r.p.r0 > lim || r.p.r0 < -lim || r.p.r1 > lim || r.p.r1 < -lim || r.hi > lim ||
         r.lo < -lim) {
@@ -284,94 +321,57 @@ __device__ __forceinline__ void store_desc(const DescArrays &d, size_t c, uint32
         r.p = Pair{0, 0};
         r.lo = r.hi = 0;
     }
+    return r;
+}
+
+// r must be clamped.
+__device__ __forceinline__ void store_desc(const DescArrays &d, size_t c, uint32_t key,
+                                           const WaveRun &r, uint32_t extra)
+{
     const int64_t dr = r.p.r1 - r.p.r0;  // -1, 0 or +1: the run's map is monotone
     d.r0[c] = r.p.r0;
     d.lo[c] = r.lo;
     d.hi[c] = r.hi;
-    d.meta[c] = (key & kKeyMask) | ((uint32_t)(dr + 1) << kDrShift) | r.flags |
-                (cross ? kFlagCross : 0u);
-}
-
-// ---------------------------------------------------------------------------
-// Crossing records.  For a chunk whose plan expects the running sum to cross
-// into the next binade, the tile also stores, for every term position, the
-// increment pair of the prefix ending there under the planned binade and
-// under the next one (packed as r0 << 2 | (r1 - r0 + 1)).  Given the exact
-// start count, the walk then finds the term that crosses, adds it with one
-// fp64 add, and takes the rest of the chunk from the second prefix.
-// Records exist only for chunks with no negative scaled term and nothing bad
-// under either binade.
-// ---------------------------------------------------------------------------
-constexpr int64_t kRecMax = (int64_t)1 << 56;  // larger prefixes are clamped (never apply)
-
-__device__ __forceinline__ int64_t rec_pack(Pair p)
-{
-    const int64_t r0 = p.r0 < kRecMax ? p.r0 : kRecMax;
-    return (r0 << 2) | (p.r1 - p.r0 + 1);
-}
-__device__ __forceinline__ Pair rec_unpack(int64_t v)
-{
-    const int64_t r0 = v >> 2;
-    return Pair{r0, r0 + (v & 3) - 1};
-}
-
-// Inclusive prefix pairs of the workgroup's 1024 terms under `key`, written
-// to out[0 .. 1023]; returns (uniformly) whether any term was bad or
-// negative under that key.  One barrier.
-__device__ __forceinline__ bool record_prefix(const Four &f, uint32_t key, int64_t *out,
-                                              Pair *lds_wtot, bool *lds_flag)
-{
-    const int scale = 1075 - (int)(key & 0x7FFu);
-    const bool sgn = (key >> 11) & 1u;
-    Pair acc[4];
-    bool bad = false;
-    Pair a = pair_identity();
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        if (i < f.cnt) {
-            const TermInc ti = term_inc(f.v[i], scale, sgn);
-            bad |= ti.bad || ti.neg;
-            a = compose(a, Pair{ti.r0, ti.r1});
-        }
-        acc[i] = a;
-    }
-    const Pair inc = wave_incl_scan_pair(a);
-    const bool wbad = __ballot(bad) != 0;
-    const int lane = lane_id(), wave = wave_id();
-    if (lane == 63)
-        lds_wtot[wave] = inc;
-    if (lane == 0)
-        lds_flag[wave] = wbad;
-    __syncthreads();
-    Pair pre = pair_identity();
-    bool any = false;
-#pragma unroll
-    for (int w = 0; w < kChunkThreads / 64; w++) {
-        if (w < wave)
-            pre = compose(pre, lds_wtot[w]);
-        any |= lds_flag[w];
-    }
-    pre = compose(pre, wave_shift_pair(inc));
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-        out[threadIdx.x * 4 + i] = rec_pack(compose(pre, acc[i]));
-    return any;
+    d.meta[c] = (key & kKeyMask) | ((uint32_t)(dr + 1) << kDrShift) | r.flags | extra;
 }
 
 // acc + t[lo] + t[lo+1] + ... + t[hi-1], one add at a time in that order (the
-// loop itself), on one lane.  The LDS reads go out eight at a time so that
-// only the chain of adds is serial.
+// loop itself), on one lane.  Two banks of eight terms alternate: the LDS
+// reads of one bank go out while the other bank is added, so that only the
+// chain of dependent adds (about 13 cycles each) is serial.
 __device__ __forceinline__ double add_in_order(double acc, const double *t, int lo, int hi)
 {
     int i = lo;
-    for (; i + 8 <= hi; i += 8) {
-        double v[8];
+    if (hi - i >= 16) {
+        double a[8], b[8];
 #pragma unroll
         for (int j = 0; j < 8; j++)
-            v[j] = t[i + j];
+            a[j] = t[i + j];
 #pragma unroll
         for (int j = 0; j < 8; j++)
-            acc = acc + v[j];
+            b[j] = t[i + 8 + j];
+        i += 16;
+        while (hi - i >= 16) {
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                acc = acc + a[j];
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                a[j] = t[i + j];
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                acc = acc + b[j];
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                b[j] = t[i + 8 + j];
+            i += 16;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            acc = acc + a[j];
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            acc = acc + b[j];
     }
     for (; i < hi; i++)
         acc = acc + t[i];
@@ -379,176 +379,9 @@ __device__ __forceinline__ double add_in_order(double acc, const double *t, int 
 }
 
 // ---------------------------------------------------------------------------
-// tile_kernel
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int find_sum(const BatchArgs &a, uint32_t g)
-{
-    int lo = 0, hi = a.count - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (a.chunk_base[mid] <= g)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    return lo;
-}
-
-template <int CPB>
-__global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a,
-                                                             uint64_t *__restrict__ status,
-                                                             DescArrays d, RecArea rec)
-{
-    constexpr int kW = kChunkThreads / 64;
-    __shared__ double lds_t[CPB][kW];
-    __shared__ WaveRun lds_runs[CPB][kW];
-    __shared__ double lds_p;
-    __shared__ double lds_terms[kChunk];
-    __shared__ Pair lds_wtot[2][kW];
-    __shared__ bool lds_flag[2][kW];
-    __shared__ int lds_slot;
-    const uint32_t g0 = blockIdx.x * CPB;  // first global chunk of the tile
-    const int s = find_sum(a, g0);
-    const double *__restrict__ x = a.x[s];
-    const size_t n = a.n[s];
-    const uint32_t c0 = g0 - a.chunk_base[s];  // first local chunk
-    const double init = a.init[s];
-    const uint32_t mode = a.flags & EXSEQ_PLAN_MASK;
-    const int lane = lane_id(), wave = wave_id();
-    const uint32_t nch = (uint32_t)((n + kChunk - 1) / kChunk);
-
-    Four f[CPB];
-#pragma unroll
-    for (int k = 0; k < CPB; k++)
-        f[k] = load_four(x, n, (size_t)(c0 + k) * kChunk + (size_t)threadIdx.x * 4, true);
-#pragma unroll
-    for (int k = 0; k < CPB; k++) {
-        const double ws = wave_sum_f64((f[k].v[0] + f[k].v[1]) + (f[k].v[2] + f[k].v[3]));
-        if (lane == 0)
-            lds_t[k][wave] = ws;
-    }
-    __syncthreads();
-    double T[CPB];
-    double Ttile = 0.0;
-#pragma unroll
-    for (int k = 0; k < CPB; k++) {
-        T[k] = (lds_t[k][0] + lds_t[k][1]) + (lds_t[k][2] + lds_t[k][3]);
-        Ttile += T[k];
-    }
-
-    double P;
-    if (mode == EXSEQ_PLAN_ALL_FALLBACK || mode == EXSEQ_PLAN_FIXED) {
-        P = 0.0;  // these modes do not look at the prefix
-    } else {
-        const uint32_t tl = c0 / CPB;  // tile index within the sum
-        uint64_t *st0 = status + a.chunk_base[s] / CPB;
-        if (tl == 0) {
-            P = init;
-        } else {
-            if (threadIdx.x == 0)
-                store_relaxed_u64(st0 + tl, st_pack(a.epoch, kStAgg, Ttile));
-            if (wave == 0) {
-                const double p = lookback(st0, tl, init, a.epoch);
-                if (lane == 0)
-                    lds_p = p;
-            }
-            __syncthreads();
-            P = lds_p;
-        }
-        if (threadIdx.x == 0)
-            store_relaxed_u64(st0 + tl, st_pack(a.epoch, kStIncl, P + Ttile));
-    }
-
-    uint32_t key[CPB], key2[CPB];
-    bool cross[CPB];
-#pragma unroll
-    for (int k = 0; k < CPB; k++) {
-        key[k] = plan_key(P, a.flags);
-        key2[k] = key_of(P + T[k]);
-        cross[k] = key2[k] != key_of(P);
-        P += T[k];
-    }
-#pragma unroll
-    for (int k = 0; k < CPB; k++) {
-        WaveRun w;
-        if (key_has_fast_path(key[k])) {
-            w = wave_run(f[k], key[k]);
-        } else {
-            bool nf = false;
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                nf |= i < f[k].cnt && is_nonfinite(f[k].v[i]);
-            w.p = pair_identity();
-            w.lo = w.hi = 0;
-            w.flags = __ballot(nf) ? kFlagNonFinite : 0u;
-        }
-        if (lane == 0)
-            lds_runs[k][wave] = w;
-    }
-    __syncthreads();
-    if ((int)threadIdx.x < CPB) {
-        const int k = threadIdx.x;
-        if (c0 + k < nch) {
-            uint32_t kk = 0;
-            bool cc = false;
-#pragma unroll
-            for (int j = 0; j < CPB; j++)
-                if (j == k) {
-                    kk = key[j];
-                    cc = cross[j];
-                }
-            store_desc(d, (size_t)(g0 + k), kk, join_waves(lds_runs[k]), cc);
-        }
-    }
-
-    // crossing records (see record_prefix)
-#pragma unroll
-    for (int k = 0; k < CPB; k++) {
-        if (!cross[k] || c0 + k >= nch || c0 + k == 0 || !key_has_fast_path(key[k]) ||
-            !key_has_fast_path(key2[k]) || ((key[k] ^ key2[k]) & 0x800u) ||
-            (join_waves(lds_runs[k]).flags & (kFlagNeg | kFlagBad | kFlagNonFinite)))
-            continue;
-        if (threadIdx.x == 0)
-            lds_slot = (int)atomicAdd(rec.counter, 1u);
-        __syncthreads();
-        const int slot = lds_slot;
-        __syncthreads();  // every lane has read the slot before it is reused
-        if (slot < 0 || slot >= (int)a.rec_slots)
-            continue;
-        int64_t *r = rec.data + (size_t)slot * 2 * kChunk;
-        const bool bad1 = record_prefix(f[k], key[k], r, lds_wtot[0], lds_flag[0]);
-        const bool bad2 = record_prefix(f[k], key2[k], r + kChunk, lds_wtot[1], lds_flag[1]);
-        if (threadIdx.x == 0 && !bad1 && !bad2) {
-            const size_t c = (size_t)(g0 + k);
-            d.lo[c] = (int64_t)key2[k];
-            d.hi[c] = slot;
-            d.meta[c] |= kFlagRecord;
-        }
-    }
-
-    // A sum's first chunk starts from init exactly.  There the running sum
-    // is small next to the terms and crosses many binades, which is the
-    // worst case of the walk's rounds, so its tile adds it in order on one
-    // lane (about 10 ns a term, hidden under the stream of the other tiles)
-    // and records the exact sum after it.
-    if (c0 == 0) {
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-            lds_terms[threadIdx.x * 4 + i] = f[0].v[i];
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            const int len = (int)(n < (size_t)kChunk ? n : (size_t)kChunk);
-            d.lo[g0] = (int64_t)dbits(add_in_order(init, lds_terms, 0, len));
-            d.meta[g0] |= kFlagExact;
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// The walk: one workgroup of 256 lanes per sum; lane t holds 4 consecutive
-// items (the chunks of a window of 1024, or the 1024 terms of a chunk being
-// resolved).
+// Workgroup building blocks of the chain and the walk: 256 lanes, lane t
+// holds 4 consecutive items (the chunks of a window of 1024, or the 1024
+// terms of a chunk being resolved).
 // ---------------------------------------------------------------------------
 constexpr int kPer = 4;
 constexpr int kWaves = kWalkThreads / 64;
@@ -559,6 +392,7 @@ constexpr int kNone = 0x7FFFFFFF;
 constexpr int kShortRound = 128;
 
 static_assert(kWindow == kChunk, "a window of chunks and a chunk of terms share the layout");
+static_assert(kWalkThreads == kChunkThreads, "the tiles and the walk share the resolve");
 
 // One wave's candidate for "the first item that needs attention", with what
 // the owning lane computed for it.
@@ -567,16 +401,13 @@ struct Cand {
     int ok2;        // chunk applies after renormalising (1), misplanned (2)
     double s_at;    // exact sum at the item (or after the item's plain add)
     double s_next;  // exact sum after the chunk when ok2 == 1
-    Pair ex_after;  // window prefix through the chunk (a record's second prefix)
-    int rec;        // the chunk's crossing record, or -1
-    uint32_t key, key2;  // the chunk's planned binade and the record's next one
+    Pair ex_after;  // window prefix through the chunk
 };
 
 struct WalkLds {
     Pair tot[2][kWaves];   // per-wave totals of a scan (double-buffered)
     Cand cand[2][kWaves];  // per-wave candidates (double-buffered)
     double endv[2];        // a round's end state, from the lane holding the last item
-    Pair lastp[2];         // a record's last second-binade prefix
     int flag[2][kWaves];
     double terms[kChunk];  // a chunk's terms, for the one-lane path
 };
@@ -679,26 +510,26 @@ __device__ __forceinline__ Cand cand_none()
     c.s_at = 0.0;
     c.s_next = 0.0;
     c.ex_after = pair_identity();
-    c.rec = -1;
-    c.key = c.key2 = 0u;
     return c;
 }
 
-// Exact resolution of one chunk from the exact running sum S.
-__device__ double resolve_chunk(const double *__restrict__ x, size_t n, size_t c, double S,
-                                int pos, WalkLds &sh, int &buf)
+// Exact resolution of the len terms of a chunk (lane t holds terms 4t ..
+// 4t+3 in f) from the exact running sum S before term pos.
+__device__ __forceinline__ double resolve_terms(const Four &f, int len, double S, int pos, WalkLds &sh, int &buf)
 {
     const int t = threadIdx.x;
-    const size_t b = c * kChunk;
-    const int len = (int)(n - b < (size_t)kChunk ? n - b : (size_t)kChunk);
-    const Four f = load_four(x, n, b + (size_t)kPer * t, false);
     double xv[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; k++) {
         xv[k] = f.v[k];
         sh.terms[kPer * t + k] = xv[k];  // visible after the next barrier
     }
+    // A round costs about as much as 300 one-lane adds.  Rounds pay where a
+    // binade holds more terms than that; after a crossing (or the first
+    // non-zero term) that leaves |S| below 512 times the term just added, the
+    // next binades are short and the rest goes through one lane in order.
     int shorts = 0;
+    bool small = false;
     while (pos < len) {
         const uint64_t sb = dbits(S);
         const uint32_t E = (uint32_t)(sb >> 52) & 0x7FFu;
@@ -731,6 +562,7 @@ __device__ double resolve_chunk(const double *__restrict__ x, size_t n, size_t c
                 break;
             S = fz.s_at;
             pos = fz.idx + 1;
+            small = true;  // S is now one term
             continue;
         }
         if (E == 0x7FFu) {
@@ -751,7 +583,7 @@ __device__ double resolve_chunk(const double *__restrict__ x, size_t n, size_t c
             }
             break;
         }
-        if (E == 0u || shorts >= 2) {
+        if (E == 0u || small || shorts >= 2) {
             // subnormal S, or the binade keeps changing: the remaining terms
             // one by one on lane 0, in order
             __syncthreads();
@@ -811,16 +643,17 @@ __device__ double resolve_chunk(const double *__restrict__ x, size_t n, size_t c
         Cand mine = cand_none();
         if (firstk >= 0) {
             int64_t cb = cnt0;
-            double xf = xv[0];
+            double xf = opaque(xv[0]);
 #pragma unroll
             for (int k = 1; k < kPer; k++)
                 if (k == firstk) {
-                    cb = cnt[k - 1];
-                    xf = xv[k];
+                    cb = opaque(cnt[k - 1]);
+                    xf = opaque(xv[k]);
                 }
             const int i = kPer * t + firstk;
             mine.idx = i;
             mine.s_at = ((i == pos) ? S : assemble(key, cb)) + xf;  // the one plain add
+            mine.s_next = xf;
         }
         // the lane holding the last term reports the round's end state
         if ((len - 1) / kPer == t) {
@@ -840,111 +673,390 @@ __device__ double resolve_chunk(const double *__restrict__ x, size_t n, size_t c
             break;
         }
         shorts += (fr.idx + 1 - pos) < kShortRound;
+        small = fabs(fr.s_at) < 512.0 * fabs(fr.s_next);
         S = fr.s_at;
         pos = fr.idx + 1;
     }
     return S;
 }
 
-// A crossing chunk from its record, given the exact sum S at its start (in
-// the chunk's planned binade).  One barrier.  Returns done with the sum
-// after the chunk, or not done with the state after the crossing term and
-// the position to continue term by term from.
-struct RecOut {
-    bool done;
-    double S;
-    int pos;
-};
-
-// This lane's share of a record chunk: its terms and packed prefixes (loaded
-// ahead of need, so that the resolve does not wait for memory).
-struct RecPre {
-    Four f;
-    int64_t pe[kPer], pe2[kPer], prev;
-    int len;
-};
-
-__device__ __forceinline__ RecPre rec_load(const double *__restrict__ x, size_t n, size_t c,
-                                           const int64_t *__restrict__ rec)
+// The same for chunk c of a sum, its terms read again from memory.
+__device__ double resolve_chunk(const double *__restrict__ x, size_t n, size_t c, double S,
+                                int pos, WalkLds &sh, int &buf)
 {
-    RecPre r;
-    const int t = threadIdx.x;
     const size_t b = c * kChunk;
-    r.len = (int)(n - b < (size_t)kChunk ? n - b : (size_t)kChunk);
-    r.f = load_four(x, n, b + (size_t)kPer * t, false);
-#pragma unroll
-    for (int k = 0; k < kPer; k++) {
-        const int i = kPer * t + k;
-        r.pe[k] = i < r.len ? rec[i] : 1;
-        r.pe2[k] = i < r.len ? rec[kChunk + i] : 1;
+    const int len = (int)(n - b < (size_t)kChunk ? n - b : (size_t)kChunk);
+    const Four f = load_four(x, n, b + (size_t)kPer * threadIdx.x, false);
+    return resolve_terms(f, len, S, pos, sh, buf);
+}
+
+// ---------------------------------------------------------------------------
+// The exact chain between the tiles of a sum.
+//
+// Chain words start at zero (chain_clear_kernel runs before the tiles) and a
+// published word is never zero, so a word is there exactly when it is not
+// zero.  Each word is self-contained and written once with a relaxed
+// agent-scope atomic store, so no other memory has to be ordered with it.
+//   agg[4 t + 0]: kAggPresent | kAggRegular (regular tiles) | the descriptor
+//                 meta bits of the tile's composed run (key, r1 - r0, flags)
+//   agg[4 t + 1..3]: r0, lo, hi of that run, each xor kIntTag (regular only)
+//   incl[t]:      bits of the exact sum after tile t, xor kInclXor, or
+//                 kInclFailed (irregular tiles only)
+// A published sum is never the NaN whose bits are kInclXor or kInclXor ^ 1:
+// NaNs are published as the default quiet NaN.
+// ---------------------------------------------------------------------------
+constexpr uint64_t kAggPresent = 1ULL << 63;
+constexpr uint64_t kAggRegular = 1ULL << 62;
+constexpr uint64_t kIntTag = 1ULL << 62;  // v ^ kIntTag != 0 for |v| < 2^61
+constexpr uint64_t kInclXor = 0xFFF8000000000001ULL;
+constexpr uint64_t kInclFailed = 1;
+constexpr uint64_t kQuietNaN = 0x7FF8000000000000ULL;
+
+__device__ __forceinline__ uint64_t enc_i64(int64_t v) { return (uint64_t)v ^ kIntTag; }
+__device__ __forceinline__ int64_t dec_i64(uint64_t w) { return (int64_t)(w ^ kIntTag); }
+__device__ __forceinline__ uint64_t enc_sum(double s)
+{
+    return (s == s ? dbits(s) : kQuietNaN) ^ kInclXor;
+}
+
+// A composed run over many tiles: the components stay bounded (a run that
+// large never applies, so it is only marked bad).
+__device__ __forceinline__ Run run_compose_sat(const Run &a, const Run &b)
+{
+    Run c = run_compose(a, b);
+    const int64_t lim = (int64_t)1 << 56;
+    if (c.p.r0 > lim || c.p.r0 < -lim || c.p.r1 > lim || c.p.r1 < -lim || c.lo < -lim ||
+        c.hi > lim) {
+        c.flags |= kFlagBad;
+        c.p = Pair{0, 0};
+        c.lo = c.hi = 0;
     }
-    r.prev = t > 0 && kPer * t - 1 < r.len ? rec[kPer * t - 1] : 1;  // 1: packed identity
+    return c;
+}
+
+template <int Ctrl, int RowMask = 0xF>
+__device__ __forceinline__ Run dpp_run(const Run &v)
+{
+    Run r;
+    r.p = dpp_pair<Ctrl, RowMask>(v.p);
+    r.lo = dpp_i64<Ctrl, RowMask>(v.lo, 0);
+    r.hi = dpp_i64<Ctrl, RowMask>(v.hi, 0);
+    r.flags = dpp_u32<Ctrl, RowMask>(v.flags, 0u);
     return r;
 }
 
-__device__ RecOut resolve_with_record(const RecPre &R, double S, uint32_t key2, WalkLds &sh,
-                                      int &buf)
+// Composition of the wave's runs with the HIGHER lanes first (lane 63's run,
+// then lane 62's, ..., then lane 0's), complete in lane 63: the same ordered
+// scan as wave_incl_scan_pair with the operands swapped.
+__device__ __forceinline__ Run wave_reduce_run_rev(Run v)
+{
+    v = run_compose_sat(v, dpp_run<kDppRowShr1>(v));
+    v = run_compose_sat(v, dpp_run<kDppRowShr2>(v));
+    v = run_compose_sat(v, dpp_run<kDppRowShr4>(v));
+    v = run_compose_sat(v, dpp_run<kDppRowShr8>(v));
+    v = run_compose_sat(v, dpp_run<kDppRowBcast15, 0xA>(v));
+    v = run_compose_sat(v, dpp_run<kDppRowBcast31, 0xC>(v));
+    return v;
+}
+
+struct ChainLds {
+    Run wrun[2][kWaves];
+    uint32_t key0;
+    uint64_t incl;
+};
+
+// The exact sum before tile tl of a sum (whose tile 0 is tile tb of the
+// launch), for all lanes: the nearest irregular tile before tl is found by
+// looking back 256 tiles at a time, the regular tiles in between are
+// composed in order (they must all be planned for one binade), and the
+// irregular tile's exact sum is awaited and the composition applied to it.
+// ok = false if that cannot be done: a word that never shows up, a failed
+// predecessor, a change of binade between regular tiles or a composed run
+// that does not apply.
+__device__ __forceinline__ double chain_in(const ChainArea &ch, uint32_t tb, uint32_t tl, WalkLds &sh,
+                           ChainLds &cl, int &buf, bool &ok)
+{
+    const int t = threadIdx.x, lane = lane_id(), wave = wave_id();
+    Run acc = run_identity();  // the tiles after the irregular one, in order
+    uint32_t key0 = 0u;
+    int64_t xp = -1;
+    ok = false;
+    for (int64_t j0 = (int64_t)tl - 1; j0 >= 0; j0 -= kChunkThreads) {
+        const int64_t j = j0 - t;  // this lane's tile
+        const uint64_t *p = ch.agg + 4 * ((size_t)tb + (size_t)(j < 0 ? 0 : j));
+        uint64_t w0 = 0;
+        bool miss = false;
+        if (j >= 0) {
+            w0 = load_relaxed_u64(p);
+            for (int spin = 0; w0 == 0; spin++) {
+                if (spin > kSpinLimit) {
+                    miss = true;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+                w0 = load_relaxed_u64(p);
+            }
+        }
+        // the nearest irregular tile in this group: the lowest such lane
+        const bool irr = j >= 0 && !miss && !(w0 & kAggRegular);
+        const uint64_t bi = __ballot(irr), bm = __ballot(miss);
+        if (lane == 0)
+            sh.flag[buf][wave] = (bi ? (int)__builtin_ctzll(bi) + 64 * wave : kChunkThreads) |
+                                 (bm ? 0x10000 : 0);
+        if (t == 0 && j0 == (int64_t)tl - 1)
+            cl.key0 = (uint32_t)(w0 & kKeyMask);
+        __syncthreads();
+        int first = kChunkThreads;
+        bool anymiss = false;
+#pragma unroll
+        for (int k = 0; k < kWaves; k++) {
+            const int v = sh.flag[buf][k];
+            first = (v & 0xFFFF) < first ? (v & 0xFFFF) : first;
+            anymiss |= (v >> 16) != 0;
+        }
+        key0 = cl.key0;
+        buf ^= 1;
+        if (anymiss)
+            return 0.0;
+        // the regular tiles before it (lanes below `first`), composed with
+        // the earlier tiles first
+        Run r = run_identity();
+        bool miss2 = false;
+        if (t < first && j >= 0) {
+            uint64_t w1 = load_relaxed_u64(p + 1);
+            uint64_t w2 = load_relaxed_u64(p + 2);
+            uint64_t w3 = load_relaxed_u64(p + 3);
+            for (int spin = 0; w1 == 0 || w2 == 0 || w3 == 0; spin++) {
+                if (spin > kSpinLimit) {
+                    miss2 = true;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+                if (w1 == 0)
+                    w1 = load_relaxed_u64(p + 1);
+                if (w2 == 0)
+                    w2 = load_relaxed_u64(p + 2);
+                if (w3 == 0)
+                    w3 = load_relaxed_u64(p + 3);
+            }
+            if (!miss2) {
+                r.p.r0 = dec_i64(w1);
+                r.p.r1 = r.p.r0 + (int64_t)((w0 >> kDrShift) & 3u) - 1;
+                r.lo = dec_i64(w2);
+                r.hi = dec_i64(w3);
+                r.flags = (uint32_t)w0 & (kFlagNeg | kFlagBad | kFlagNonFinite);
+            }
+            miss2 |= ((uint32_t)w0 & kKeyMask) != key0;
+        }
+        r = wave_reduce_run_rev(r);
+        const uint64_t bm2 = __ballot(miss2);
+        if (lane == 63)
+            cl.wrun[buf][wave] = r;
+        if (lane == 0)
+            sh.flag[buf][wave] = bm2 != 0;
+        __syncthreads();
+        Run R = cl.wrun[buf][kWaves - 1];
+        bool anymiss2 = sh.flag[buf][kWaves - 1] != 0;
+#pragma unroll
+        for (int k = kWaves - 2; k >= 0; k--) {
+            R = run_compose_sat(R, cl.wrun[buf][k]);
+            anymiss2 |= sh.flag[buf][k] != 0;
+        }
+        buf ^= 1;
+        if (anymiss2)
+            return 0.0;
+        acc = run_compose_sat(R, acc);
+        if (first < kChunkThreads) {
+            xp = j0 - first;
+            break;
+        }
+    }
+    if (xp < 0)
+        return 0.0;  // no irregular tile before (the first tile always is one)
+    if (t == 0) {
+        const uint64_t *p = ch.incl + tb + (size_t)xp;
+        uint64_t w = load_relaxed_u64(p);
+        for (int spin = 0; w == 0 && spin <= kSpinLimit; spin++) {
+            __builtin_amdgcn_s_sleep(2);
+            w = load_relaxed_u64(p);
+        }
+        cl.incl = w;
+    }
+    __syncthreads();
+    const uint64_t w = cl.incl;
+    if (w <= kInclFailed)
+        return 0.0;
+    const double S = bitsd(w ^ kInclXor);
+    if (xp == (int64_t)tl - 1) {
+        ok = true;  // nothing in between
+        return S;
+    }
+    const uint32_t ks = key_of(S);
+    const int64_t m = count_of(S);
+    if (ks != key0 || !key_has_fast_path(ks) || !run_applies(m, acc.p, acc.lo, acc.hi, acc.flags))
+        return 0.0;
+    ok = true;
+    return assemble(ks, m + pair_at(acc.p, m));
+}
+
+// ---------------------------------------------------------------------------
+// Crossing records in registers.  For a chunk whose plan expects the running
+// sum to cross from its binade into the next one up, an irregular tile forms,
+// before it waits for the chain, the increment pair of every prefix of the
+// chunk under the planned binade and under the next one (each lane: its four
+// terms' inclusive prefixes, packed as r0 << 2 | (r1 - r0 + 1), and the
+// prefix before its first term).  Given the exact start state, the crossing
+// term is then found with one workgroup step and added with one fp64 add,
+// and the rest of the chunk is taken from the second binade's prefixes.
+// Records are made only for chunks with no negative scaled term and nothing
+// bad under either binade.
+// ---------------------------------------------------------------------------
+constexpr int64_t kRecMax = (int64_t)1 << 56;  // larger prefixes are clamped (never apply)
+
+__device__ __forceinline__ int64_t rec_pack(Pair p)
+{
+    const int64_t r0 = p.r0 < kRecMax ? p.r0 : kRecMax;
+    return (r0 << 2) | (p.r1 - p.r0 + 1);
+}
+__device__ __forceinline__ Pair rec_unpack(int64_t v)
+{
+    const int64_t r0 = v >> 2;
+    return Pair{r0, r0 + (v & 3) - 1};
+}
+
+// A tile's record, in LDS.
+struct RecLds {
+    int64_t pe[kChunk];   // inclusive prefix under the planned binade at every term
+    int64_t pe2[kChunk];  // the same under the next binade
+    Pair last2;           // the whole chunk under the next binade
+};
+
+// The lane's inclusive prefixes under `key` (acc) and whether any term was
+// negative or bad under it.
+__device__ __forceinline__ bool lane_prefixes(const Four &f, uint32_t key, Pair *acc)
+{
+    const int scale = 1075 - (int)(key & 0x7FFu);
+    const bool sgn = (key >> 11) & 1u;
+    bool bad = false;
+    Pair a = pair_identity();
+#pragma unroll
+    for (int i = 0; i < kPer; i++) {
+        if (i < f.cnt) {
+            const TermInc ti = term_inc(f.v[i], scale, sgn);
+            bad |= ti.bad || ti.neg;
+            a = compose(a, Pair{ti.r0, ti.r1});
+        }
+        acc[i] = a;
+    }
+    return bad;
+}
+
+// Ordered exclusive workgroup scan and the workgroup's total; one barrier.
+__device__ __forceinline__ Pair block_scan_total(Pair v, WalkLds &sh, int buf, Pair &total)
+{
+    const int lane = lane_id(), wave = wave_id();
+    const Pair inc = wave_incl_scan_pair(v);
+    if (lane == 63)
+        sh.tot[buf][wave] = inc;
+    __syncthreads();
+    Pair pre = pair_identity();
+    total = pair_identity();
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) {
+        if (w < wave)
+            pre = compose(pre, sh.tot[buf][w]);
+        total = compose(total, sh.tot[buf][w]);
+    }
+    return compose(pre, wave_shift_pair(inc));
+}
+
+// Builds the record of a chunk (terms f, planned key, next key key2); false
+// (uniformly) if the chunk cannot have one.  Three barriers.
+__device__ __forceinline__ bool record_build(const Four &f, uint32_t key, uint32_t key2,
+                                             WalkLds &sh, int &buf, RecLds &r)
+{
+    Pair acc[kPer], acc2[kPer], tot, tot2;
+    const int t = threadIdx.x;
+    const bool bad1 = lane_prefixes(f, key, acc);
+    const bool bad2 = lane_prefixes(f, key2, acc2);
+    const Pair pre = block_scan_total(acc[kPer - 1], sh, buf, tot);
+    buf ^= 1;
+    const Pair pre2 = block_scan_total(acc2[kPer - 1], sh, buf, tot2);
+    buf ^= 1;
+#pragma unroll
+    for (int i = 0; i < kPer; i++) {
+        r.pe[kPer * t + i] = rec_pack(compose(pre, acc[i]));
+        r.pe2[kPer * t + i] = rec_pack(compose(pre2, acc2[i]));
+    }
+    if (t == 0)
+        r.last2 = tot2;
+    const bool bad = block_any(bad1 || bad2, sh, buf);  // its barrier publishes r
+    buf ^= 1;
+    return !bad;
+}
+
+// Resolves a record chunk of len terms from the exact sum S before it.
+// Returns true with S the sum after the chunk, or false with S the exact sum
+// after term pos - 1 (the rest goes term by term).  One barrier.
+__device__ __forceinline__ bool record_resolve(const RecLds &r, const Four &f, int len,
+                                               uint32_t key, uint32_t key2, double &S, int &pos,
+                                               WalkLds &sh, int &buf)
 {
     const int t = threadIdx.x;
-    const int len = R.len;
-    const Four &f = R.f;
-    const uint32_t key = key_of(S);
+    const uint32_t ks = key_of(S);
     const int64_t m = count_of(S);
-    int64_t pe[kPer], pe2[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; k++) {
-        pe[k] = R.pe[k];
-        pe2[k] = R.pe2[k];
+    if (ks == key2) {
+        // the crossing came before the chunk: all of it in the second binade
+        const int64_t e = m + pair_at(r.last2, m);
+        if (e <= kCountHi) {
+            S = assemble(ks, e);
+            return true;
+        }
+        pos = 0;
+        return false;
     }
-    const int64_t prev = R.prev;
     int64_t cnt[kPer];
 #pragma unroll
-    for (int k = 0; k < kPer; k++)
-        cnt[k] = m + pair_at(rec_unpack(pe[k]), m);
+    for (int i = 0; i < kPer; i++)
+        cnt[i] = m + pair_at(rec_unpack(r.pe[kPer * t + i]), m);
     Cand mine = cand_none();
     int firstk = -1;
 #pragma unroll
-    for (int k = kPer - 1; k >= 0; k--) {
-        const int i = kPer * t + k;
-        if (i < len && (cnt[k] < kCountLo + 1 || cnt[k] > kCountHi - 1))
-            firstk = k;
-    }
+    for (int i = kPer - 1; i >= 0; i--)
+        if (kPer * t + i < len && cnt[i] > kCountHi - 1)
+            firstk = i;
     if (firstk >= 0) {
-        int64_t cb = m + pair_at(rec_unpack(prev), m);
-        double xf = f.v[0];
-        int64_t p2 = pe2[0];
+        const int i = kPer * t + firstk;
+        const int64_t cb = (i == 0) ? m : m + pair_at(rec_unpack(r.pe[i - 1]), m);
+        double xf = opaque(f.v[0]);
 #pragma unroll
         for (int k = 1; k < kPer; k++)
-            if (k == firstk) {
-                cb = cnt[k - 1];
-                xf = f.v[k];
-                p2 = pe2[k];
-            }
-        const int i = kPer * t + firstk;
+            if (k == firstk)
+                xf = opaque(f.v[k]);
         mine.idx = i;
         mine.s_at = ((i == 0) ? S : assemble(key, cb)) + xf;  // the one plain add
-        mine.ex_after = rec_unpack(p2);
+        mine.ex_after = rec_unpack(r.pe2[i]);
     }
     if ((len - 1) / kPer == t) {
         const int kl = (len - 1) - kPer * t;
 #pragma unroll
-        for (int k = 0; k < kPer; k++)
-            if (k == kl) {
-                sh.endv[buf] = assemble(key, cnt[k]);
-                sh.lastp[buf] = rec_unpack(pe2[k]);
-            }
+        for (int i = 0; i < kPer; i++)
+            if (i == kl)
+                sh.endv[buf] = assemble(key, cnt[i]);
     }
     const Cand fr = block_first(firstk >= 0, mine, sh, buf);
     const double endv = sh.endv[buf];
-    const Pair lastp = sh.lastp[buf];
     buf ^= 1;
-    if (fr.idx == kNone)
-        return RecOut{true, endv, len};
-    const double s2 = fr.s_at;
-    if (fr.idx == len - 1)
-        return RecOut{true, s2, len};
-    const uint32_t k2 = key_of(s2);
-    const int64_t m2 = count_of(s2);
+    if (fr.idx == kNone) {
+        S = endv;
+        return true;
+    }
+    S = fr.s_at;
+    pos = fr.idx + 1;
+    if (pos == len)
+        return true;
+    const uint32_t k2 = key_of(S);
+    const int64_t m2 = count_of(S);
     const Pair at = fr.ex_after;
     int p = -1;
     if ((at.r0 & 1) == (m2 & 1))
@@ -952,19 +1064,351 @@ __device__ RecOut resolve_with_record(const RecPre &R, double S, uint32_t key2, 
     else if (((1 + at.r1) & 1) == (m2 & 1))
         p = 1;
     if (k2 != key2 || !key_has_fast_path(k2) || p < 0)
-        return RecOut{false, s2, fr.idx + 1};
-    const int64_t cnt_end = m2 + ((p ? lastp.r1 : lastp.r0) - (p ? at.r1 : at.r0));
-    if (cnt_end > kCountHi)
-        return RecOut{false, s2, fr.idx + 1};  // a second crossing
-    return RecOut{true, assemble(k2, cnt_end), len};
+        return false;
+    const int64_t e = m2 + ((p ? r.last2.r1 : r.last2.r0) - (p ? at.r1 : at.r0));
+    if (e > kCountHi)
+        return false;  // a second crossing
+    S = assemble(k2, e);
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// tile_kernel
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int find_sum(const BatchArgs &a, uint32_t g)
+{
+    int lo = 0, hi = a.count - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.chunk_base[mid] <= g)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+__host__ __device__ __forceinline__ bool chain_on(uint32_t flags)
+{
+    return (flags & EXSEQ_PLAN_MASK) != EXSEQ_PLAN_ALL_FALLBACK && !(flags & EXSEQ_WALK_ONLY);
+}
+
+// How close (in counts of the binade) a chunk's planned start or end may come
+// to an edge of its planned binade before the tile stops trusting the plan
+// there.  The planned prefix and the exact running sum add the same terms in
+// different orders; for non-negative terms each is within n * 2^-53 of the
+// real sum (relative), so up to 2^23 terms (a 3840x2160 frame) they differ by
+// less than 2^-29 of the sum: 2^24 counts of its binade.  Beyond that, or
+// under cancellation, the margin is a heuristic; it only decides which chunks
+// are added term by term, never a result.
+constexpr int64_t kPlanMargin = (int64_t)1 << 24;
+
+template <int CPB>
+__global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a,
+                                                             uint64_t *__restrict__ status,
+                                                             DescArrays d, ChainArea ch)
+{
+    constexpr int kW = kChunkThreads / 64;
+    __shared__ double lds_t[CPB][kW];
+    __shared__ WaveRun lds_runs[CPB][kW];
+    __shared__ double lds_p;
+    __shared__ WalkLds sh;
+    __shared__ ChainLds cl;
+    __shared__ RecLds srec;
+    __shared__ Run lds_grp[2];
+    __shared__ uint32_t lds_gkey[2];
+    const uint32_t g0 = blockIdx.x * CPB;  // first global chunk of the tile
+    const int s = find_sum(a, g0);
+    const double *__restrict__ x = a.x[s];
+    const size_t n = a.n[s];
+    const uint32_t c0 = g0 - a.chunk_base[s];  // first local chunk
+    const double init = a.init[s];
+    const uint32_t mode = a.flags & EXSEQ_PLAN_MASK;
+    const int lane = lane_id(), wave = wave_id();
+    const uint32_t nch = (uint32_t)((n + kChunk - 1) / kChunk);
+    if (c0 >= nch)
+        return;  // padding after the sum's last chunk
+    // A sum's first tile starts the exact chain: its waves go first in the
+    // instruction arbitration of their SIMDs, ahead of streaming tiles.
+    if (c0 == 0 && chain_on(a.flags))
+        __builtin_amdgcn_s_setprio(3);
+
+    Four f[CPB];
+#pragma unroll
+    for (int k = 0; k < CPB; k++)
+        f[k] = load_four(x, n, (size_t)(c0 + k) * kChunk + (size_t)threadIdx.x * 4, true);
+#pragma unroll
+    for (int k = 0; k < CPB; k++) {
+        const double ws = wave_sum_f64((f[k].v[0] + f[k].v[1]) + (f[k].v[2] + f[k].v[3]));
+        if (lane == 0)
+            lds_t[k][wave] = ws;
+    }
+    __syncthreads();
+    double T[CPB];
+    double Ttile = 0.0;
+#pragma unroll
+    for (int k = 0; k < CPB; k++) {
+        T[k] = (lds_t[k][0] + lds_t[k][1]) + (lds_t[k][2] + lds_t[k][3]);
+        Ttile += T[k];
+    }
+
+    const uint32_t tl = c0 / CPB;  // tile index within the sum
+    double P;
+    if (mode == EXSEQ_PLAN_ALL_FALLBACK || mode == EXSEQ_PLAN_FIXED) {
+        P = 0.0;  // these modes do not look at the prefix
+    } else {
+        uint64_t *st0 = status + a.chunk_base[s] / CPB;
+        if (tl == 0) {
+            P = init;
+        } else {
+            if (threadIdx.x == 0)
+                store_relaxed_u64(st0 + tl, st_pack(a.epoch, kStAgg, Ttile));
+            if (wave == 0) {
+                const double p = lookback(st0, tl, init, a.epoch);
+                if (lane == 0)
+                    lds_p = p;
+            }
+            __syncthreads();
+            P = lds_p;
+        }
+        if (threadIdx.x == 0)
+            store_relaxed_u64(st0 + tl, st_pack(a.epoch, kStIncl, P + Ttile));
+    }
+
+    uint32_t key[CPB];
+    double Pk[CPB];
+    bool cross[CPB];
+#pragma unroll
+    for (int k = 0; k < CPB; k++) {
+        Pk[k] = P;
+        key[k] = plan_key(P, a.flags);
+        cross[k] = key_of(P + T[k]) != key_of(P);
+        P += T[k];
+    }
+#pragma unroll
+    for (int k = 0; k < CPB; k++) {
+        WaveRun w;
+        if (key_has_fast_path(key[k])) {
+            w = wave_run(f[k], key[k]);
+        } else {
+            bool nf = false;
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                nf |= i < f[k].cnt && is_nonfinite(f[k].v[i]);
+            w.p = pair_identity();
+            w.lo = w.hi = 0;
+            w.flags = __ballot(nf) ? kFlagNonFinite : 0u;
+        }
+        if (lane == 0)
+            lds_runs[k][wave] = w;
+    }
+    __syncthreads();
+    // A chunk's run is joined from LDS where it is needed (chunk_run), so
+    // that the runs do not hold registers through the chain.
+    auto chunk_run = [&](int k) { return clamp_run(join_waves(lds_runs[k])); };
+    uint32_t rflags[CPB];
+#pragma unroll
+    for (int k = 0; k < CPB; k++) {
+        const WaveRun r = chunk_run(k);
+        rflags[k] = r.flags;
+        // near an edge of the planned binade: the plan is not trusted there
+        if (key_has_fast_path(key[k]) && key[k] == key_of(Pk[k])) {
+            const int64_t m = count_of(Pk[k]);
+            bool near = m < kCountLo + kPlanMargin;
+            if (r.flags & kFlagNeg)
+                near |= m + r.lo - kPlanMargin < kCountLo + 1 ||
+                        m + r.hi + kPlanMargin > kCountHi - 1;
+            else
+                near |= m + r.hi + kPlanMargin > kCountHi;
+            cross[k] |= near;
+        }
+    }
+
+    // descriptors for the walk (regular tiles and those that fail);
+    // resolved: bit k for chunks added term by term
+    auto store_descs = [&](uint32_t resolved) {
+        if ((int)threadIdx.x < CPB) {
+            const int k = threadIdx.x;
+            if (c0 + k < nch) {
+                uint32_t kk = opaque(key[0] | (cross[0] ? 0x80000000u : 0u));
+#pragma unroll
+                for (int j = 1; j < CPB; j++)
+                    if (j == k)
+                        kk = opaque(key[j] | (cross[j] ? 0x80000000u : 0u));
+                const bool cc = (kk >> 31) != 0;
+                kk &= kKeyMask;
+                store_desc(d, (size_t)(g0 + k), kk, chunk_run(k),
+                           (cc ? kFlagCross : 0u) | (((resolved >> k) & 1u) ? kFlagResolved : 0u));
+            }
+        }
+    };
+
+    if (!chain_on(a.flags)) {
+        store_descs(0u);
+        // A sum's first chunk starts from init exactly.  There the running
+        // sum is small next to the terms and crosses many binades, the worst
+        // case of the walk's rounds, so its tile adds it in order and records
+        // the exact sum after it.
+        if (c0 == 0) {
+            const int len = (int)(n < (size_t)kChunk ? n : (size_t)kChunk);
+            int buf = 0;
+            const double e = resolve_terms(f[0], len, init, 0, sh, buf);
+            if (threadIdx.x == 0) {
+                d.lo[g0] = (int64_t)dbits(e);
+                d.meta[g0] |= kFlagExact;
+            }
+        }
+        return;
+    }
+
+    // ---- the exact chain ----------------------------------------------------
+    const uint32_t tb = a.chunk_base[s] / CPB;  // the sum's first tile in the launch
+    uint64_t *agg = ch.agg + 4 * (size_t)(tb + tl);
+    bool regular = c0 != 0 && c0 + CPB < nch;
+#pragma unroll
+    for (int k = 0; k < CPB; k++)
+        regular &= key_has_fast_path(key[k]) && key[k] == key[0] && !cross[k] &&
+                   !(rflags[k] & (kFlagBad | kFlagNonFinite));
+    if (regular) {
+        store_descs(0u);
+        Run tr = run_identity();
+#pragma unroll
+        for (int k = 0; k < CPB; k++) {
+            const WaveRun r = chunk_run(k);
+            tr = run_compose_sat(tr, Run{r.p, r.lo, r.hi, r.flags});
+        }
+        if (threadIdx.x == 0) {
+            const int64_t dr = tr.p.r1 - tr.p.r0;
+            store_relaxed_u64(agg + 1, enc_i64(tr.p.r0));
+            store_relaxed_u64(agg + 2, enc_i64(tr.lo));
+            store_relaxed_u64(agg + 3, enc_i64(tr.hi));
+            store_relaxed_u64(agg + 0, kAggPresent | kAggRegular | (uint64_t)(key[0] & kKeyMask) |
+                                           ((uint64_t)(dr + 1) << kDrShift) |
+                                           (uint64_t)(tr.flags & kFlagNeg));
+        }
+        return;
+    }
+    if (threadIdx.x == 0)
+        store_relaxed_u64(agg, kAggPresent);
+    // from here on this tile is on the chain's critical path
+    __builtin_amdgcn_s_setprio(3);
+    int buf = 0;
+    // The record of the first chunk expected to cross into the next binade
+    // up.  Per-chunk values are picked by unrolled selects throughout: an
+    // array indexed by a run-time chunk number would live in scratch memory.
+    int rk = -1;
+#pragma unroll
+    for (int k = CPB - 1; k >= 0; k--)
+        if (c0 + k < nch && cross[k] && key_has_fast_path(key[k]) && !(key[k] & 0x800u) &&
+            key_has_fast_path(key[k] + 1u) &&
+            !(rflags[k] & (kFlagNeg | kFlagBad | kFlagNonFinite)))
+            rk = k;
+    if (rk >= 0) {
+        Four fr = opaque(f[0]);
+        uint32_t kr = opaque(key[0]);
+#pragma unroll
+        for (int j = 1; j < CPB; j++)
+            if (j == rk) {
+                fr = opaque(f[j]);
+                kr = opaque(key[j]);
+            }
+        if (!record_build(fr, kr, kr + 1u, sh, buf, srec))
+            rk = -1;
+    }
+    // The chunks before the record chunk (group 0) and after it (group 1),
+    // each composed into one run if its chunks share one planned binade and
+    // none is bad: one step each on the critical path instead of one per
+    // chunk.
+    const int nk = (int)(nch - c0 < (uint32_t)CPB ? nch - c0 : (uint32_t)CPB);
+    const int g0e = rk >= 0 ? rk : nk;      // group 0: chunks [0, g0e)
+    const int g1b = rk >= 0 ? rk + 1 : nk;  // group 1: chunks [g1b, nk)
+    if (threadIdx.x < 2) {
+        const int gb = threadIdx.x == 0 ? 0 : g1b, ge = threadIdx.x == 0 ? g0e : nk;
+        Run r = run_identity();
+        uint32_t gk = 0u;
+        bool same = gb < ge;
+#pragma unroll
+        for (int k = 0; k < CPB; k++) {
+            if (k >= gb && k < ge) {
+                const WaveRun w = chunk_run(k);
+                r = run_compose_sat(r, Run{w.p, w.lo, w.hi, w.flags});
+                if (k == gb)
+                    gk = key[k];
+                same &= key[k] == gk && key_has_fast_path(key[k]);
+            }
+        }
+        if (!same || (r.flags & (kFlagBad | kFlagNonFinite)))
+            gk = 0u;
+        lds_grp[threadIdx.x] = r;
+        lds_gkey[threadIdx.x] = gk;
+    }
+    __syncthreads();
+    bool ok = true;
+    double S = init;
+    if ((a.flags & EXSEQ_CHAIN_CUT) && tl >= ((nch + CPB - 1) / CPB) / 2 && tl > 0)
+        ok = false;
+    else if (c0 != 0)
+        S = chain_in(ch, tb, tl, sh, cl, buf, ok);
+    if (!ok) {
+        store_descs(0u);
+        if (threadIdx.x == 0)
+            store_relaxed_u64(ch.incl + tb + tl, kInclFailed);
+        return;
+    }
+    uint32_t resolved = 0u;
+#pragma unroll 1
+    for (int k = 0; k < nk; k++) {
+        const int gi = k == 0 && g0e > 1 ? 0 : (k == g1b && nk - g1b > 1 ? 1 : -1);
+        if (gi >= 0) {
+            const uint32_t gk = lds_gkey[gi];
+            const Run g = lds_grp[gi];
+            const uint32_t ks = key_of(S);
+            const int64_t m = count_of(S);
+            if (gk != 0u && ks == gk && run_applies(m, g.p, g.lo, g.hi, g.flags)) {
+                S = assemble(ks, m + pair_at(g.p, m));
+                k = gi == 0 ? g0e - 1 : nk - 1;
+                continue;
+            }
+        }
+        Four fk = opaque(f[0]);
+        uint32_t kk = opaque(key[0]);
+#pragma unroll
+        for (int j = 1; j < CPB; j++)
+            if (j == k) {
+                fk = opaque(f[j]);
+                kk = opaque(key[j]);
+            }
+        const WaveRun rn = chunk_run(k);
+        const uint32_t ks = key_of(S);
+        const int64_t m = count_of(S);
+        if (key_has_fast_path(ks) && ks == kk && run_applies(m, rn.p, rn.lo, rn.hi, rn.flags)) {
+            S = assemble(ks, m + pair_at(rn.p, m));
+        } else {
+            const size_t b = (size_t)(c0 + k) * kChunk;
+            const int len = (int)(n - b < (size_t)kChunk ? n - b : (size_t)kChunk);
+            int pos = 0;
+            const bool done = k == rk && (ks == kk || ks == kk + 1u) &&
+                              record_resolve(srec, fk, len, kk, kk + 1u, S, pos, sh, buf);
+            if (!done)
+                S = resolve_terms(fk, len, S, pos, sh, buf);
+            resolved |= 1u << k;
+        }
+    }
+    store_descs(resolved);
+    if (threadIdx.x == 0)
+        store_relaxed_u64(ch.incl + tb + tl, enc_sum(S));
 }
 
 __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, DescArrays dall,
-                                                            RecArea rec,
+                                                            ChainArea ch,
                                                             double *__restrict__ outs,
                                                             exseq_stats *__restrict__ stats)
 {
     __shared__ WalkLds sh;
+    __shared__ unsigned long long st_fb, st_terms;
+    __shared__ long long st_first;
+    __shared__ unsigned st_nf;
+    __shared__ long long st_best[kWaves];
     const int s = blockIdx.x;
     const double *__restrict__ x = a.x[s];
     const size_t n = a.n[s];
@@ -981,10 +1425,73 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, DescArr
     bool nonfinite = false;
     int buf = 0;
 
-    // The first tile left the exact sum after the first chunk.
     double S = a.init[s];
     size_t start = 0;
-    if (nch && (dmeta[0] & kFlagExact)) {
+    if (nch && chain_on(a.flags)) {
+        // The chain's exact sum after the last tile, or else the last exact
+        // sum it published (the chain fails at one tile and at every
+        // irregular tile after it, so that is where it stopped).
+        const size_t tile = a.tile;
+        const size_t tb = cb / tile;
+        const int64_t tlast = (int64_t)((nch - 1) / tile);
+        int64_t best = -1;
+        if (ch.incl[tb + (size_t)tlast] > kInclFailed) {
+            best = tlast;
+        } else {
+            for (int64_t j = t; j <= tlast; j += kWalkThreads)
+                if (ch.incl[tb + (size_t)j] > kInclFailed)
+                    best = j;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {
+                const long long o = __shfl_xor((long long)best, off);
+                best = o > best ? o : best;
+            }
+            if (lane_id() == 0)
+                st_best[wave_id()] = best;
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < kWaves; k++)
+                best = st_best[k] > best ? st_best[k] : best;
+        }
+        if (best >= 0) {
+            S = bitsd(ch.incl[tb + (size_t)best] ^ kInclXor);
+            start = (size_t)(best + 1) * tile;
+            start = start < nch ? start : nch;
+        }
+        if (stats && start > 0) {
+            // what the tiles did before that point
+            if (t == 0) {
+                st_fb = 0;
+                st_terms = 0;
+                st_first = 0x7FFFFFFFFFFFFFFFLL;
+                st_nf = 0;
+            }
+            __syncthreads();
+            unsigned long long my_fb = 0, my_terms = 0;
+            long long my_first = 0x7FFFFFFFFFFFFFFFLL;
+            unsigned my_nf = 0;
+            for (size_t j = t; j < start; j += kWalkThreads) {
+                const uint32_t mt = dmeta[j];
+                my_nf |= mt & kFlagNonFinite;
+                if (mt & kFlagResolved) {
+                    my_fb++;
+                    my_terms += n - j * kChunk < (size_t)kChunk ? n - j * kChunk : (size_t)kChunk;
+                    my_first = (long long)j < my_first ? (long long)j : my_first;
+                }
+            }
+            atomicAdd(&st_fb, my_fb);
+            atomicAdd(&st_terms, my_terms);
+            atomicMin(&st_first, my_first);
+            atomicOr(&st_nf, my_nf);
+            __syncthreads();
+            n_fb = st_fb;
+            fb_terms = st_terms;
+            first_fb = st_first == 0x7FFFFFFFFFFFFFFFLL ? -1 : (int64_t)st_first;
+            nonfinite |= st_nf != 0;
+            n_fast = start - n_fb;
+        }
+    } else if (nch && (dmeta[0] & kFlagExact)) {
+        // the first tile left the exact sum after the first chunk
         S = bitsd((uint64_t)dlo_a[0]);
         nonfinite |= (dmeta[0] & kFlagNonFinite) != 0;
         start = 1;
@@ -1015,7 +1522,6 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, DescArr
             nmeta[k] = i < nch ? dmeta[i] : kFlagBad;
         }
         uint32_t dkey[kPer], dfl[kPer];
-        bool drec[kPer];
         Pair mine[kPer];
         bool lane_tie = false, lane_nf = false, lane_clean = true;
         int64_t lane_sum = 0;
@@ -1025,7 +1531,6 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, DescArr
             const bool have = kPer * t + k < cnt;
             dkey[k] = have ? (meta[k] & kKeyMask) : 0u;
             dfl[k] = have ? (meta[k] & (kFlagNeg | kFlagBad | kFlagNonFinite)) : kFlagBad;
-            drec[k] = have && (meta[k] & kFlagRecord) != 0;
             const int64_t d1 = (int64_t)((meta[k] >> kDrShift) & 3u) - 1;
             mine[k] = have ? Pair{r0[k], r0[k] + d1} : pair_identity();
             if (have) {
@@ -1054,7 +1559,7 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, DescArr
 #pragma unroll
         for (int k = 0; k < kPer; k++) {
             dlo[k] = dhi[k] = 0;
-            if ((dfl[k] & kFlagNeg) || drec[k]) {
+            if (dfl[k] & kFlagNeg) {
                 dlo[k] = dlo_a[base + kPer * t + k];
                 dhi[k] = dhi_a[base + kPer * t + k];
             }
@@ -1114,7 +1619,6 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, DescArr
             int fk = -1;
             int64_t fmt = 0, flo = 0, fhi = 0;
             uint32_t fkey = 0, ffl = 0;
-            bool frec = false;
             Pair fmine = pair_identity(), fex = pair_identity();
 #pragma unroll
             for (int k = kPer - 1; k >= 0; k--) {
@@ -1132,7 +1636,6 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, DescArr
                         ffl = dfl[k];
                         fmine = mine[k];
                         fex = ex[k];
-                        frec = drec[k];
                     }
                 }
             }
@@ -1150,11 +1653,6 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, DescArr
                 mc.s_at = sat;
                 mc.s_next = ok2 ? assemble(k2, m2 + pair_at(fmine, m2)) : 0.0;
                 mc.ex_after = compose(fex, fmine);
-                mc.key = fkey;
-                if (frec) {
-                    mc.rec = (int)fhi;
-                    mc.key2 = (uint32_t)flo;
-                }
             }
             // the lane holding the window's last chunk reports the end state
             const int lastk = (cnt - 1) - kPer * t;
@@ -1183,13 +1681,7 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, DescArr
             } else {
                 misses += fc.ok2 == 2;
                 const size_t c = base + (size_t)fc.idx;
-                if (fc.rec >= 0 && key_of(fc.s_at) == fc.key) {
-                    const RecPre R = rec_load(x, n, c, rec.data + (size_t)fc.rec * 2 * kChunk);
-                    const RecOut r = resolve_with_record(R, fc.s_at, fc.key2, sh, buf);
-                    S = r.done ? r.S : resolve_chunk(x, n, c, r.S, r.pos, sh, buf);
-                } else {
-                    S = resolve_chunk(x, n, c, fc.s_at, 0, sh, buf);
-                }
+                S = resolve_chunk(x, n, c, fc.s_at, 0, sh, buf);
                 n_fb++;
                 fb_terms += (n - c * kChunk < (size_t)kChunk) ? n - c * kChunk : (size_t)kChunk;
                 if (first_fb < 0)
@@ -1199,9 +1691,6 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, DescArr
         }
     }
     if (t == 0) {
-        // the next launch (after this one, in stream order) numbers records from 0
-        if (s == 0)
-            *rec.counter = 0u;
         outs[s] = S;
         if (stats) {
             exseq_stats st;
@@ -1241,6 +1730,19 @@ __global__ __launch_bounds__(kPlanThreads) void tree_total_kernel(
 
 __global__ void write_value_kernel(double *out, double v) { out[0] = v; }
 
+// Zeroes the chain words of `tiles` tiles before a launch's tiles run.
+__global__ __launch_bounds__(256) void chain_clear_kernel(ChainArea ch, uint32_t tiles)
+{
+    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+    if (i < tiles) {
+        ch.agg[4 * (size_t)i + 0] = 0;
+        ch.agg[4 * (size_t)i + 1] = 0;
+        ch.agg[4 * (size_t)i + 2] = 0;
+        ch.agg[4 * (size_t)i + 3] = 0;
+        ch.incl[i] = 0;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Host-side launch sequences.
 // ---------------------------------------------------------------------------
@@ -1261,7 +1763,7 @@ uint32_t next_epoch()
 struct WsParts {
     uint64_t *status;
     DescArrays d;
-    RecArea rec;
+    ChainArea ch;
 };
 
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -1270,8 +1772,6 @@ WsParts carve(void *ws, size_t total)
 {
     char *w = static_cast<char *>(ws);
     WsParts p;
-    p.rec.counter = reinterpret_cast<uint32_t *>(w);
-    w += 256;
     p.status = reinterpret_cast<uint64_t *>(w);
     w += round256(total * sizeof(uint64_t));
     p.d.r0 = reinterpret_cast<int64_t *>(w);
@@ -1282,27 +1782,24 @@ WsParts carve(void *ws, size_t total)
     w += round256(total * sizeof(int64_t));
     p.d.meta = reinterpret_cast<uint32_t *>(w);
     w += round256(total * sizeof(uint32_t));
-    p.rec.data = reinterpret_cast<int64_t *>(w);
+    p.ch.agg = reinterpret_cast<uint64_t *>(w);
+    w += round256(4 * total * sizeof(uint64_t));
+    p.ch.incl = reinterpret_cast<uint64_t *>(w);
     return p;
 }
 }  // namespace
 
-const char *const kPathKernels[] = {"tile_kernel", "walk_kernel"};
-const int kPathKernelCount = 2;
+const char *const kPathKernels[] = {"chain_clear_kernel", "tile_kernel", "walk_kernel"};
+const int kPathKernelCount = 3;
 
-// Records a launch may make: about one per binade a sum crosses is needed;
-// one slot per 8 chunks (16 to 512) leaves room for mis-planned ones.
-size_t rec_slots(size_t total_chunks)
-{
-    const size_t s = total_chunks / 8;
-    return s < 16 ? 16 : (s > 512 ? 512 : s);
-}
-
+// Per chunk (a tile is at least one chunk): the plan status word, the four
+// descriptor arrays, the chain words.
 size_t sum_ws_bytes(size_t total_chunks)
 {
-    return 256 + 4 * round256(total_chunks * sizeof(int64_t)) +
+    return 4 * round256(total_chunks * sizeof(int64_t)) +
            round256(total_chunks * sizeof(uint32_t)) +
-           rec_slots(total_chunks) * 2 * kChunk * sizeof(int64_t) + 256;
+           round256(4 * total_chunks * sizeof(uint64_t)) +
+           round256(total_chunks * sizeof(uint64_t));
 }
 
 template <int CPB>
@@ -1312,7 +1809,7 @@ static void launch_tiles(const BatchArgs &args, uint32_t total, const WsParts &p
     const unsigned tiles = total / CPB;
     if (tiles)
         hipLaunchKernelGGL(tile_kernel<CPB>, dim3(tiles), dim3(kChunkThreads), 0, stream, args,
-                           p.status, p.d, p.rec);
+                           p.status, p.d, p.ch);
 }
 
 int launch_batch(const BatchArgs &a, void *ws, double *outs, hipStream_t stream,
@@ -1326,20 +1823,26 @@ int launch_batch(const BatchArgs &a, void *ws, double *outs, hipStream_t stream,
     const WsParts p = carve(ws, total);
     BatchArgs args = a;
     args.epoch = next_epoch();
-    args.rec_slots = (uint32_t)rec_slots(total);
-    const uint32_t tile = (a.flags >> kTileShift) & 3u;  // 0: default
+    const uint32_t sel = (a.flags >> kTileShift) & 3u;  // 0: default
+    args.tile = sel == 1 ? 1u : (sel == 2 ? 2u : 4u);
+    const uint32_t tiles = total / args.tile;
     mark(0);
-    if (tile == 1)
+    if (chain_on(a.flags) && tiles)
+        hipLaunchKernelGGL(chain_clear_kernel, dim3((tiles + 255) / 256), dim3(256), 0, stream,
+                           p.ch, tiles);
+    mark(1);
+    mark(2);
+    if (args.tile == 1)
         launch_tiles<1>(args, total, p, stream);
-    else if (tile == 2)
+    else if (args.tile == 2)
         launch_tiles<2>(args, total, p, stream);
     else
         launch_tiles<4>(args, total, p, stream);
-    mark(1);
-    mark(2);
-    hipLaunchKernelGGL(walk_kernel, dim3((unsigned)a.count), dim3(kWalkThreads), 0, stream, args,
-                       p.d, p.rec, outs, stats);
     mark(3);
+    mark(4);
+    hipLaunchKernelGGL(walk_kernel, dim3((unsigned)a.count), dim3(kWalkThreads), 0, stream, args,
+                       p.d, p.ch, outs, stats);
+    mark(5);
     return hipGetLastError() == hipSuccess ? EXSEQ_OK : EXSEQ_EHIP;
 }
 

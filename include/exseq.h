@@ -73,6 +73,19 @@ enum {
 #define EXSEQ_PLAN_MASK 0xFu
 #define EXSEQ_PLAN_FIXED_KEY(key) (EXSEQ_PLAN_FIXED | (((uint32_t)(key) & 0xFFFu) << 8))
 
+/* Further bits of `flags` (testing and tuning; 0 for production use).
+ *   bits 4..5     chunks per tile of the single pass: 0 (default) or 3 = 4,
+ *                 1 = 1, 2 = 2
+ *   WALK_ONLY     the tiles only plan and describe; the ordered walk after
+ *                 them follows every chunk (no exact chain between tiles)
+ *   CHAIN_CUT     the exact chain stops half way through every sum (the tiles
+ *                 of the second half report failure), so that the walk must
+ *                 resume from the last exact value the chain published
+ * ALL_FALLBACK implies WALK_ONLY. */
+#define EXSEQ_TILE_SHIFT 4
+#define EXSEQ_WALK_ONLY (1u << 6)
+#define EXSEQ_CHAIN_CUT (1u << 7)
+
 /* Device-side statistics of one sum (written when the walk finishes). */
 typedef struct exseq_stats {
     uint64_t chunks;          /* chunks walked */

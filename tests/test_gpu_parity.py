@@ -63,6 +63,36 @@ def test_workloads_every_plan(case):
         assert same(got, want), (name, plan, got, want)
 
 
+CHAIN_VARIANTS = [0, ex.WALK_ONLY, ex.CHAIN_CUT, ex.tile_flag(1), ex.tile_flag(2),
+                  ex.tile_flag(1) | ex.CHAIN_CUT, ex.tile_flag(2) | ex.CHAIN_CUT]
+
+
+@pytest.mark.parametrize("case", suites.workload_suite(small=True), ids=lambda c: c[0])
+def test_workloads_chain_variants(case):
+    """The exact chain between tiles, the walk alone, and the walk resuming
+    from the chain's last exact value give the same bits at every tile size."""
+    torch = torch_cuda()
+    name, x, init = case
+    want = oracle.seq_sum(x, init)
+    for fl in CHAIN_VARIANTS:
+        got, st = gpu_sum(torch, x, init, fl, stats=True)
+        assert same(got, want), (name, fl, got, want)
+        assert st["fast_chunks"] + st["fallback_chunks"] == st["chunks"], (name, fl, st)
+
+
+def test_full_size_chain_cut():
+    """The frame-size sum with the chain stopped half way: the walk resumes
+    from the last exact value published before the cut."""
+    torch = torch_cuda()
+    for name, x in (("tie_heavy", si.tie_heavy(si.FRAME_N, 11)),
+                    ("signed", si.signed_terms(si.HALF_N, 12))):
+        want = oracle.seq_sum(x)
+        for fl in (ex.CHAIN_CUT, ex.WALK_ONLY):
+            got, st = gpu_sum(torch, x, 0.0, fl, stats=True)
+            say(name, fl, st)
+            assert same(got, want), (name, fl, got, want)
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2, 3, 4])
 def test_full_size_workloads(seed):
     """The frame-size tie-heavy sum (8,294,400 terms), the 1920x1080 signed
