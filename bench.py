@@ -33,7 +33,6 @@ if ROOT not in sys.path:
 METRIC = "fp64 terms/sec (GB/s, % HBM roofline) for bit-exact seq sum @3840x2160"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published peak
 TERM_BYTES = 8
-DESC_BYTES = 32                 # one chunk descriptor
 CHUNK = 1024
 
 
@@ -165,15 +164,14 @@ def main():
     avg_ms = {nm: statistics.fmean(v) for nm, v in per_kernel.items()}
     dominant = max(avg_ms, key=avg_ms.get)
 
-    # algorithmic bytes per launch of each kernel (terms read once, chunk
-    # sums/keys/descriptors written and read)
+    # algorithmic bytes per launch of each kernel: the terms read once; per
+    # chunk a 28-byte descriptor written; per tile of 4 chunks a plan status
+    # word and 40 bytes of chain words written and read
+    tiles = (nch + 3) // 4
     alg_bytes = {
-        "chunk_tsum_kernel": n * TERM_BYTES + nch * 8,
-        "plan_kernel": nch * 8 + nch * 4,
-        "chunk_desc_kernel": n * TERM_BYTES + nch * 4 + nch * DESC_BYTES,
-        "walk_kernel": nch * DESC_BYTES,
-        "chunk_pass_kernel": n * TERM_BYTES + nch * (DESC_BYTES + 8),
-        "tile_kernel": n * TERM_BYTES + nch * (3 * 8 + 4) + (nch // 4) * 8,
+        "chain_clear_kernel": tiles * 40,
+        "tile_kernel": n * TERM_BYTES + nch * 28 + tiles * (8 + 40),
+        "walk_kernel": tiles * 8 + 8,
     }
     ab = alg_bytes.get(dominant, n * TERM_BYTES)
     achieved = ab / (avg_ms[dominant] * 1e-3) / 1e9
