@@ -765,48 +765,82 @@ struct ChainLds {
     uint64_t incl;
 };
 
-// The exact sum before tile tl of a sum (whose tile 0 is tile tb of the
-// launch), for all lanes: the nearest irregular tile before tl is found by
-// looking back 256 tiles at a time, the regular tiles in between are
-// composed in order (they must all be planned for one binade), and the
-// irregular tile's exact sum is awaited and the composition applied to it.
-// ok = false if that cannot be done: a word that never shows up, a failed
-// predecessor, a change of binade between regular tiles or a composed run
-// that does not apply.
-__device__ __forceinline__ double chain_in(const ChainArea &ch, uint32_t tb, uint32_t tl, WalkLds &sh,
-                           ChainLds &cl, int &buf, bool &ok)
+// Looks back from tile tl of a sum (whose tile 0 is tile tb of the launch)
+// for the nearest irregular tile xp, 1024 tiles at a time (4 per lane, all
+// their words requested at once), and composes the regular tiles in between
+// in order into acc (they must all be planned for one binade, key0).
+// Returns kBackOk, kBackBad (xp found, but the regular tiles in between
+// changed binade) or kBackLost (a word never showed up).
+constexpr int kBackOk = 0, kBackBad = 1, kBackLost = 2;
+constexpr int kBackPer = 4;  // tiles per lane per round
+
+__device__ __forceinline__ int chain_back(const ChainArea &ch, uint32_t tb, uint32_t tl,
+                                          WalkLds &sh, ChainLds &cl, int &buf, Run &acc,
+                                          uint32_t &key0, int64_t &xp)
 {
+    constexpr int kRound = kBackPer * kChunkThreads;
     const int t = threadIdx.x, lane = lane_id(), wave = wave_id();
-    Run acc = run_identity();  // the tiles after the irregular one, in order
-    uint32_t key0 = 0u;
-    int64_t xp = -1;
-    ok = false;
-    for (int64_t j0 = (int64_t)tl - 1; j0 >= 0; j0 -= kChunkThreads) {
-        const int64_t j = j0 - t;  // this lane's tile
-        const uint64_t *p = ch.agg + 4 * ((size_t)tb + (size_t)(j < 0 ? 0 : j));
-        uint64_t w0 = 0;
-        bool miss = false;
-        if (j >= 0) {
-            w0 = load_relaxed_u64(p);
-            for (int spin = 0; w0 == 0; spin++) {
-                if (spin > kSpinLimit) {
-                    miss = true;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(2);
-                w0 = load_relaxed_u64(p);
-            }
+    acc = run_identity();  // the tiles after the irregular one, in order
+    key0 = 0u;
+    xp = -1;
+    bool keys_ok = true;
+    for (int64_t j0 = (int64_t)tl - 1; j0 >= 0; j0 -= kRound) {
+        // lane t holds tiles j0 - 4t - i, i = 0..3 (i = 0 the latest)
+        uint64_t w[kBackPer][4];
+#pragma unroll
+        for (int i = 0; i < kBackPer; i++) {
+            const int64_t j = j0 - kBackPer * t - i;
+            const uint64_t *p = ch.agg + 4 * ((size_t)tb + (size_t)(j < 0 ? 0 : j));
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+                w[i][q] = j >= 0 ? load_relaxed_u64(p + q) : 0;
         }
-        // the nearest irregular tile in this group: the lowest such lane
-        const bool irr = j >= 0 && !miss && !(w0 & kAggRegular);
-        const uint64_t bi = __ballot(irr), bm = __ballot(miss);
-        if (lane == 0)
-            sh.flag[buf][wave] = (bi ? (int)__builtin_ctzll(bi) + 64 * wave : kChunkThreads) |
-                                 (bm ? 0x10000 : 0);
+        bool miss = false;
+        for (int spin = 0;; spin++) {
+            bool need = false;
+#pragma unroll
+            for (int i = 0; i < kBackPer; i++) {
+                const int64_t j = j0 - kBackPer * t - i;
+                const uint64_t *p = ch.agg + 4 * ((size_t)tb + (size_t)(j < 0 ? 0 : j));
+                if (j < 0)
+                    continue;
+                if (w[i][0] == 0) {
+                    need = true;
+                    w[i][0] = load_relaxed_u64(p);
+                } else if (w[i][0] & kAggRegular) {
+#pragma unroll
+                    for (int q = 1; q < 4; q++)
+                        if (w[i][q] == 0) {
+                            need = true;
+                            w[i][q] = load_relaxed_u64(p + q);
+                        }
+                }
+            }
+            if (!need)
+                break;
+            if (spin > kSpinLimit) {
+                miss = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        // the nearest irregular tile: the smallest local index 4t + i
+        int mine = kRound;
+#pragma unroll
+        for (int i = kBackPer - 1; i >= 0; i--)
+            if (j0 - kBackPer * t - i >= 0 && !(w[i][0] & kAggRegular))
+                mine = kBackPer * t + i;
+        const uint64_t bi = __ballot(mine < kRound), bm = __ballot(miss);
+        if (lane == 0) {
+            int wf = kRound;
+            if (bi)
+                wf = __builtin_amdgcn_readlane(mine, (int)__builtin_ctzll(bi));
+            sh.flag[buf][wave] = wf | (bm ? 0x10000 : 0);
+        }
         if (t == 0 && j0 == (int64_t)tl - 1)
-            cl.key0 = (uint32_t)(w0 & kKeyMask);
+            cl.key0 = (uint32_t)(w[0][0] & kKeyMask);
         __syncthreads();
-        int first = kChunkThreads;
+        int first = kRound;
         bool anymiss = false;
 #pragma unroll
         for (int k = 0; k < kWaves; k++) {
@@ -817,99 +851,61 @@ __device__ __forceinline__ double chain_in(const ChainArea &ch, uint32_t tb, uin
         key0 = cl.key0;
         buf ^= 1;
         if (anymiss)
-            return 0.0;
-        // the regular tiles before it (lanes below `first`), composed with
-        // the earlier tiles first
+            return kBackLost;
+        // the regular tiles after it, the earlier ones first
         Run r = run_identity();
-        bool miss2 = false;
-        if (t < first && j >= 0) {
-            uint64_t w1 = load_relaxed_u64(p + 1);
-            uint64_t w2 = load_relaxed_u64(p + 2);
-            uint64_t w3 = load_relaxed_u64(p + 3);
-            for (int spin = 0; w1 == 0 || w2 == 0 || w3 == 0; spin++) {
-                if (spin > kSpinLimit) {
-                    miss2 = true;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(2);
-                if (w1 == 0)
-                    w1 = load_relaxed_u64(p + 1);
-                if (w2 == 0)
-                    w2 = load_relaxed_u64(p + 2);
-                if (w3 == 0)
-                    w3 = load_relaxed_u64(p + 3);
+        bool bad = false;
+#pragma unroll
+        for (int i = kBackPer - 1; i >= 0; i--) {
+            if (j0 - kBackPer * t - i >= 0 && kBackPer * t + i < first) {
+                const int64_t r0 = dec_i64(w[i][1]);
+                const Run ti{Pair{r0, r0 + (int64_t)((w[i][0] >> kDrShift) & 3u) - 1},
+                             dec_i64(w[i][2]), dec_i64(w[i][3]),
+                             (uint32_t)w[i][0] & (kFlagNeg | kFlagBad | kFlagNonFinite)};
+                r = run_compose_sat(r, ti);
+                bad |= ((uint32_t)w[i][0] & kKeyMask) != key0;
             }
-            if (!miss2) {
-                r.p.r0 = dec_i64(w1);
-                r.p.r1 = r.p.r0 + (int64_t)((w0 >> kDrShift) & 3u) - 1;
-                r.lo = dec_i64(w2);
-                r.hi = dec_i64(w3);
-                r.flags = (uint32_t)w0 & (kFlagNeg | kFlagBad | kFlagNonFinite);
-            }
-            miss2 |= ((uint32_t)w0 & kKeyMask) != key0;
         }
         r = wave_reduce_run_rev(r);
-        const uint64_t bm2 = __ballot(miss2);
+        const uint64_t bb = __ballot(bad);
         if (lane == 63)
             cl.wrun[buf][wave] = r;
         if (lane == 0)
-            sh.flag[buf][wave] = bm2 != 0;
+            sh.flag[buf][wave] = bb != 0;
         __syncthreads();
         Run R = cl.wrun[buf][kWaves - 1];
-        bool anymiss2 = sh.flag[buf][kWaves - 1] != 0;
+        bool anybad = sh.flag[buf][kWaves - 1] != 0;
 #pragma unroll
         for (int k = kWaves - 2; k >= 0; k--) {
             R = run_compose_sat(R, cl.wrun[buf][k]);
-            anymiss2 |= sh.flag[buf][k] != 0;
+            anybad |= sh.flag[buf][k] != 0;
         }
         buf ^= 1;
-        if (anymiss2)
-            return 0.0;
+        keys_ok &= !anybad;
         acc = run_compose_sat(R, acc);
-        if (first < kChunkThreads) {
+        if (first < kRound) {
             xp = j0 - first;
             break;
         }
     }
     if (xp < 0)
-        return 0.0;  // no irregular tile before (the first tile always is one)
-    if (t == 0) {
-        const uint64_t *p = ch.incl + tb + (size_t)xp;
-        uint64_t w = load_relaxed_u64(p);
-        for (int spin = 0; w == 0 && spin <= kSpinLimit; spin++) {
-            __builtin_amdgcn_s_sleep(2);
-            w = load_relaxed_u64(p);
-        }
-        cl.incl = w;
-    }
-    __syncthreads();
-    const uint64_t w = cl.incl;
-    if (w <= kInclFailed)
-        return 0.0;
-    const double S = bitsd(w ^ kInclXor);
-    if (xp == (int64_t)tl - 1) {
-        ok = true;  // nothing in between
-        return S;
-    }
-    const uint32_t ks = key_of(S);
-    const int64_t m = count_of(S);
-    if (ks != key0 || !key_has_fast_path(ks) || !run_applies(m, acc.p, acc.lo, acc.hi, acc.flags))
-        return 0.0;
-    ok = true;
-    return assemble(ks, m + pair_at(acc.p, m));
+        return kBackLost;  // no irregular tile before (the first tile always is one)
+    return keys_ok ? kBackOk : kBackBad;
 }
 
 // ---------------------------------------------------------------------------
-// Crossing records in registers.  For a chunk whose plan expects the running
-// sum to cross from its binade into the next one up, an irregular tile forms,
-// before it waits for the chain, the increment pair of every prefix of the
-// chunk under the planned binade and under the next one (each lane: its four
-// terms' inclusive prefixes, packed as r0 << 2 | (r1 - r0 + 1), and the
-// prefix before its first term).  Given the exact start state, the crossing
-// term is then found with one workgroup step and added with one fp64 add,
-// and the rest of the chunk is taken from the second binade's prefixes.
-// Records are made only for chunks with no negative scaled term and nothing
-// bad under either binade.
+// Crossings, located by the tile.  For a chunk whose plan expects the running
+// sum to cross from its binade into the next one up, the tile forms the
+// increment pair of every prefix of the chunk under both binades and finds,
+// from the planned start count, the term that crosses.  It publishes only
+// that term and the prefixes around it (pairs packed as r0 << 2 |
+// (r1 - r0 + 1)).  Given the exact start count m, the walk checks in O(1)
+// that the crossing is still at that term -- the count before it below 2^53,
+// the count through it at least 2^53; the plan is off by far fewer counts
+// than one term moves the count, so it nearly always is -- adds the term
+// with one fp64 add and takes the rest of the chunk from the second binade's
+// prefixes.  Only chunks with no negative scaled term and nothing bad under
+// either binade get a crossing.
 // ---------------------------------------------------------------------------
 constexpr int64_t kRecMax = (int64_t)1 << 56;  // larger prefixes are clamped (never apply)
 
@@ -923,13 +919,6 @@ __device__ __forceinline__ Pair rec_unpack(int64_t v)
     const int64_t r0 = v >> 2;
     return Pair{r0, r0 + (v & 3) - 1};
 }
-
-// A tile's record, in LDS.
-struct RecLds {
-    int64_t pe[kChunk];   // inclusive prefix under the planned binade at every term
-    int64_t pe2[kChunk];  // the same under the next binade
-    Pair last2;           // the whole chunk under the next binade
-};
 
 // The lane's inclusive prefixes under `key` (acc) and whether any term was
 // negative or bad under it.
@@ -970,106 +959,270 @@ __device__ __forceinline__ Pair block_scan_total(Pair v, WalkLds &sh, int buf, P
     return compose(pre, wave_shift_pair(inc));
 }
 
-// Builds the record of a chunk (terms f, planned key, next key key2); false
-// (uniformly) if the chunk cannot have one.  Three barriers.
-__device__ __forceinline__ bool record_build(const Four &f, uint32_t key, uint32_t key2,
-                                             WalkLds &sh, int &buf, RecLds &r)
+// A crossing as published: the crossing term's index j, the packed prefix
+// pairs through j - 1 and through j under the planned binade, through j
+// under the next one, the whole chunk under the next one, and the term.
+constexpr int kCrossWords = 6;
+struct CrossCand {
+    int j;
+    int64_t pj1, pj, p2j;
+    double xj;
+};
+struct CrossLds {
+    CrossCand c[kWaves];
+    int bad[kWaves];
+};
+
+// Locates the crossing of a chunk (terms f, len of them, planned binade
+// key, planned start count m_est); false (uniformly) if the chunk has none
+// from m_est or cannot have one.  On success out[] holds the published
+// words in every lane.  Three barriers.
+__device__ __forceinline__ bool crossing_find(const Four &f, int len, uint32_t key, int64_t m_est,
+                                              WalkLds &sh, CrossLds &xl, int &buf, uint64_t *out)
 {
+    const int t = threadIdx.x, lane = lane_id(), wave = wave_id();
     Pair acc[kPer], acc2[kPer], tot, tot2;
-    const int t = threadIdx.x;
     const bool bad1 = lane_prefixes(f, key, acc);
-    const bool bad2 = lane_prefixes(f, key2, acc2);
+    const bool bad2 = lane_prefixes(f, key + 1u, acc2);
     const Pair pre = block_scan_total(acc[kPer - 1], sh, buf, tot);
     buf ^= 1;
     const Pair pre2 = block_scan_total(acc2[kPer - 1], sh, buf, tot2);
     buf ^= 1;
-#pragma unroll
-    for (int i = 0; i < kPer; i++) {
-        r.pe[kPer * t + i] = rec_pack(compose(pre, acc[i]));
-        r.pe2[kPer * t + i] = rec_pack(compose(pre2, acc2[i]));
-    }
-    if (t == 0)
-        r.last2 = tot2;
-    const bool bad = block_any(bad1 || bad2, sh, buf);  // its barrier publishes r
-    buf ^= 1;
-    return !bad;
-}
-
-// Resolves a record chunk of len terms from the exact sum S before it.
-// Returns true with S the sum after the chunk, or false with S the exact sum
-// after term pos - 1 (the rest goes term by term).  One barrier.
-__device__ __forceinline__ bool record_resolve(const RecLds &r, const Four &f, int len,
-                                               uint32_t key, uint32_t key2, double &S, int &pos,
-                                               WalkLds &sh, int &buf)
-{
-    const int t = threadIdx.x;
-    const uint32_t ks = key_of(S);
-    const int64_t m = count_of(S);
-    if (ks == key2) {
-        // the crossing came before the chunk: all of it in the second binade
-        const int64_t e = m + pair_at(r.last2, m);
-        if (e <= kCountHi) {
-            S = assemble(ks, e);
-            return true;
-        }
-        pos = 0;
-        return false;
-    }
-    int64_t cnt[kPer];
-#pragma unroll
-    for (int i = 0; i < kPer; i++)
-        cnt[i] = m + pair_at(rec_unpack(r.pe[kPer * t + i]), m);
-    Cand mine = cand_none();
+    // the first term whose count from m_est reaches 2^53 (counts only grow)
     int firstk = -1;
 #pragma unroll
-    for (int i = kPer - 1; i >= 0; i--)
-        if (kPer * t + i < len && cnt[i] > kCountHi - 1)
+    for (int i = kPer - 1; i >= 0; i--) {
+        const Pair pe = compose(pre, acc[i]);
+        if (kPer * t + i < len && m_est + pair_at(pe, m_est) >= kCountHi)
             firstk = i;
-    if (firstk >= 0) {
-        const int i = kPer * t + firstk;
-        const int64_t cb = (i == 0) ? m : m + pair_at(rec_unpack(r.pe[i - 1]), m);
-        double xf = opaque(f.v[0]);
+    }
+    const uint64_t b = __ballot(firstk >= 0), bb = __ballot(bad1 || bad2);
+    if (lane == (b ? (int)__builtin_ctzll(b) : 0)) {
+        CrossCand c;
+        c.j = kNone;
+        c.pj1 = c.pj = c.p2j = 0;
+        c.xj = 0.0;
+        if (b) {
+            Pair before = pre, at = acc[0], at2 = acc2[0];
+            double x = opaque(f.v[0]);
 #pragma unroll
-        for (int k = 1; k < kPer; k++)
-            if (k == firstk)
-                xf = opaque(f.v[k]);
-        mine.idx = i;
-        mine.s_at = ((i == 0) ? S : assemble(key, cb)) + xf;  // the one plain add
-        mine.ex_after = rec_unpack(r.pe2[i]);
+            for (int i = 1; i < kPer; i++)
+                if (i == firstk) {
+                    before = Pair{opaque(acc[i - 1].r0), opaque(acc[i - 1].r1)};
+                    at = Pair{opaque(acc[i].r0), opaque(acc[i].r1)};
+                    at2 = Pair{opaque(acc2[i].r0), opaque(acc2[i].r1)};
+                    x = opaque(f.v[i]);
+                }
+            c.j = kPer * t + firstk;
+            c.pj1 = rec_pack(firstk == 0 ? pre : compose(pre, before));
+            c.pj = rec_pack(compose(pre, at));
+            c.p2j = rec_pack(compose(pre2, at2));
+            c.xj = x;
+        }
+        xl.c[wave] = c;
+        xl.bad[wave] = bb != 0;
     }
-    if ((len - 1) / kPer == t) {
-        const int kl = (len - 1) - kPer * t;
+    __syncthreads();
+    int bw = 0;
+    bool bad = xl.bad[0] != 0;
 #pragma unroll
-        for (int i = 0; i < kPer; i++)
-            if (i == kl)
-                sh.endv[buf] = assemble(key, cnt[i]);
+    for (int k = 1; k < kWaves; k++) {
+        bad |= xl.bad[k] != 0;
+        if (xl.c[k].j < xl.c[bw].j)
+            bw = k;
     }
-    const Cand fr = block_first(firstk >= 0, mine, sh, buf);
-    const double endv = sh.endv[buf];
-    buf ^= 1;
-    if (fr.idx == kNone) {
-        S = endv;
-        return true;
+    const CrossCand c = xl.c[bw];
+    if (bad || c.j == kNone)
+        return false;
+    out[0] = enc_i64(c.j);
+    out[1] = enc_i64(c.pj1);
+    out[2] = enc_i64(c.pj);
+    out[3] = enc_i64(c.p2j);
+    out[4] = enc_i64(rec_pack(tot2));
+    out[5] = dbits(c.xj) ^ kInclXor;  // a crossing term is finite: never kInclXor
+    return true;
+}
+
+// The walk's side: from the exact sum S before a chunk (len terms, planned
+// binade key) with a published crossing w[0..5].  Returns 1 with S the sum
+// after the chunk, 2 with S the exact sum after the crossing term and pos
+// the next term (the rest term by term), or 0 if the crossing does not hold
+// for this S (the whole chunk term by term).
+__device__ __forceinline__ int crossing_apply(const uint64_t *w, int len, uint32_t key, double &S,
+                                              int &pos)
+{
+    const uint32_t ks = key_of(S);
+    const int64_t m = count_of(S);
+    const Pair last2 = rec_unpack(dec_i64(w[4]));
+    if (ks == key + 1u) {
+        // the crossing came before the chunk: all of it in the next binade
+        const int64_t e = m + pair_at(last2, m);
+        if (e > kCountHi)
+            return 0;
+        S = assemble(ks, e);
+        return 1;
     }
-    S = fr.s_at;
-    pos = fr.idx + 1;
+    if (ks != key)
+        return 0;
+    const int j = (int)dec_i64(w[0]);
+    const int64_t cb = j == 0 ? m : m + pair_at(rec_unpack(dec_i64(w[1])), m);
+    const int64_t cj = m + pair_at(rec_unpack(dec_i64(w[2])), m);
+    if (j >= len || cb > kCountHi - 1 || cj < kCountHi)
+        return 0;  // the crossing is elsewhere for this start
+    const double sb = j == 0 ? S : assemble(key, cb);
+    S = sb + bitsd(w[5] ^ kInclXor);  // the one plain add
+    pos = j + 1;
     if (pos == len)
-        return true;
+        return 1;
     const uint32_t k2 = key_of(S);
     const int64_t m2 = count_of(S);
-    const Pair at = fr.ex_after;
+    const Pair at = rec_unpack(dec_i64(w[3]));
     int p = -1;
     if ((at.r0 & 1) == (m2 & 1))
         p = 0;
     else if (((1 + at.r1) & 1) == (m2 & 1))
         p = 1;
-    if (k2 != key2 || !key_has_fast_path(k2) || p < 0)
-        return false;
-    const int64_t e = m2 + ((p ? r.last2.r1 : r.last2.r0) - (p ? at.r1 : at.r0));
+    if (k2 != key + 1u || !key_has_fast_path(k2) || p < 0)
+        return 2;
+    const int64_t e = m2 + ((p ? last2.r1 : last2.r0) - (p ? at.r1 : at.r0));
     if (e > kCountHi)
-        return false;  // a second crossing
+        return 2;  // a second crossing
     S = assemble(k2, e);
-    return true;
+    return 1;
+}
+
+// ---------------------------------------------------------------------------
+// The walk of the chain.  Irregular tiles do not wait for each other.  Each
+// one writes a block of words into the slot of the nearest irregular tile
+// before it (the sum's first tile: into the sum's head slot): its own index,
+// the composed run of the regular tiles in between (R), and its chunks'
+// runs, each with the crossing record slot it filled, if any.  One workgroup
+// per sum (the first blocks of the tile launch, so resident from the start)
+// follows these blocks: one round trip to memory gives the next irregular
+// tile and all it needs, apart from records.  It adds the sum's first chunk
+// from init before anything is published, then for each irregular tile
+// applies R and each chunk's run, its record or its terms one by one, and
+// writes the exact sum after the tile to incl, while the tiles behind it
+// still stream.
+// ---------------------------------------------------------------------------
+constexpr int kIrrTile = 4;    // 1 + index of the tile the block describes
+constexpr int kIrrInfo = 5;    // present | chunks
+constexpr int kIrrChunk = 6;   // chunk k at 6 + 10k: meta, r0, lo, hi, crossing[6]
+constexpr int kIrrPer = 4 + kCrossWords;
+constexpr int kIrrWords = kIrrChunk + kIrrPer * kTileMax;
+constexpr uint64_t kIrrEmpty = 1ULL << 61;   // R: no regular tile in between
+constexpr uint64_t kIrrFailed = 1ULL << 60;  // R: the look-back failed
+constexpr uint64_t kIrrCross = 1ULL << 40;   // chunk meta: a crossing is published
+static_assert(kIrrWords <= kChunkThreads, "one lane per word");
+
+// The walk stops (and the walk kernel resumes) where a wait times out.
+__device__ __forceinline__ uint64_t spin_load(const uint64_t *p)
+{
+    uint64_t w = load_relaxed_u64(p);
+    for (int spin = 0; w == 0 && spin <= kSpinLimit; spin++) {
+        __builtin_amdgcn_s_sleep(2);
+        w = load_relaxed_u64(p);
+    }
+    return w;
+}
+
+struct WalkOut {
+    uint64_t fb, terms;
+    int64_t first;
+};
+
+__device__ __forceinline__ void chain_walk(const BatchArgs &a, int s, const ChainArea &ch,
+                                           WalkLds &sh, uint64_t *words)
+{
+    __builtin_amdgcn_s_setprio(3);  // the walk is the critical path
+    const int t = threadIdx.x;
+    const double *__restrict__ x = a.x[s];
+    const size_t n = a.n[s];
+    const size_t nch = (n + kChunk - 1) / kChunk;
+    const uint32_t cpb = a.tile;
+    const size_t tb = a.chunk_base[s] / cpb;
+    const int nw = kIrrChunk + kIrrPer * (int)cpb;
+    WalkOut wo{0, 0, -1};
+    int buf = 0;
+    if (nch == 0)
+        return;
+    const uint32_t tlast = (uint32_t)((nch - 1) / cpb);
+    // the head block's words go out first, then the first chunk is added
+    uint64_t pre = t < nw ? load_relaxed_u64(ch.irr + (size_t)kIrrWords * tb + t) : 0;
+    double S = resolve_chunk(x, n, 0, a.init[s], 0, sh, buf);
+    wo.fb = 1;
+    wo.terms = n < (size_t)kChunk ? n : (size_t)kChunk;
+    wo.first = 0;
+    int64_t cur = -1;  // the last irregular tile walked
+    while (true) {
+        // the block in the slot of tile cur (cur = -1: the head slot)
+        const uint64_t *blk = ch.irr + (size_t)kIrrWords * (tb + (size_t)(cur + 1));
+        __syncthreads();  // words[] of the previous tile are read
+        if (t < nw)
+            words[t] = pre != 0 ? pre : spin_load(blk + t);
+        __syncthreads();
+        const uint64_t xw = words[kIrrTile], info = words[kIrrInfo], rm = words[0];
+        if (!(info & kAggPresent) || !(rm & kAggPresent) || (rm & kIrrFailed) || xw == 0 ||
+            (int64_t)xw - 1 <= cur || xw - 1 > tlast)
+            break;
+        const uint32_t X = (uint32_t)(xw - 1);
+        // the next block, if already there (not waited for)
+        pre = t < nw && X != tlast ? load_relaxed_u64(ch.irr + (size_t)kIrrWords * (tb + X + 1) + t)
+                                   : 0;
+        // R: the regular tiles since tile cur
+        if (!(rm & kIrrEmpty)) {
+            const uint32_t rkey = (uint32_t)rm & kKeyMask;
+            const int64_t r0 = dec_i64(words[1]);
+            const Pair p{r0, r0 + (int64_t)((rm >> kDrShift) & 3u) - 1};
+            const uint32_t ks = key_of(S);
+            const int64_t m = count_of(S);
+            if (ks != rkey || !key_has_fast_path(ks) ||
+                !run_applies(m, p, dec_i64(words[2]), dec_i64(words[3]),
+                             (uint32_t)rm & (kFlagNeg | kFlagBad | kFlagNonFinite)))
+                break;
+            S = assemble(ks, m + pair_at(p, m));
+        }
+        const int nk = (int)(info & 15u);
+        const size_t cX = (size_t)X * cpb;  // first local chunk of X
+        for (int k = X == 0 ? 1 : 0; k < nk; k++) {
+            const uint64_t *cw = words + kIrrChunk + kIrrPer * k;
+            const uint64_t cm = cw[0];
+            const uint32_t kk = (uint32_t)cm & kKeyMask;
+            const uint32_t fl = (uint32_t)cm & (kFlagNeg | kFlagBad | kFlagNonFinite);
+            const int64_t r0 = dec_i64(cw[1]);
+            const Pair p{r0, r0 + (int64_t)((cm >> kDrShift) & 3u) - 1};
+            const uint32_t ks = key_of(S);
+            const int64_t m = count_of(S);
+            if (key_has_fast_path(ks) && ks == kk &&
+                run_applies(m, p, dec_i64(cw[2]), dec_i64(cw[3]), fl)) {
+                S = assemble(ks, m + pair_at(p, m));
+                continue;
+            }
+            const size_t c = cX + (size_t)k;
+            const int len = (int)(n - c * kChunk < (size_t)kChunk ? n - c * kChunk : (size_t)kChunk);
+            int pos = 0;
+            const int xr = (cm & kIrrCross) ? crossing_apply(cw + 4, len, kk, S, pos) : 0;
+            if (xr != 1) {
+                const Four f = load_four(x, n, c * kChunk + (size_t)kPer * t, false);
+                S = resolve_terms(f, len, S, xr == 2 ? pos : 0, sh, buf);
+            }
+            wo.fb++;
+            wo.terms += (uint64_t)len;
+            if (wo.first < 0)
+                wo.first = (int64_t)c;
+        }
+        if (t == 0)
+            ch.incl[tb + X] = enc_sum(S);
+        cur = X;
+        if (X == tlast)
+            break;
+    }
+    if (t == 0) {
+        ch.wstat[4 * s + 0] = wo.fb;
+        ch.wstat[4 * s + 1] = wo.terms;
+        ch.wstat[4 * s + 2] = (uint64_t)(wo.first + 1);
+        ch.wstat[4 * s + 3] = 1;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1095,13 +1248,15 @@ __host__ __device__ __forceinline__ bool chain_on(uint32_t flags)
 
 // How close (in counts of the binade) a chunk's planned start or end may come
 // to an edge of its planned binade before the tile stops trusting the plan
-// there.  The planned prefix and the exact running sum add the same terms in
-// different orders; for non-negative terms each is within n * 2^-53 of the
-// real sum (relative), so up to 2^23 terms (a 3840x2160 frame) they differ by
-// less than 2^-29 of the sum: 2^24 counts of its binade.  Beyond that, or
-// under cancellation, the margin is a heuristic; it only decides which chunks
-// are added term by term, never a result.
-constexpr int64_t kPlanMargin = (int64_t)1 << 24;
+// there: 4096 + 64 sqrt(terms up to the chunk's end).  The planned prefix and
+// the exact running sum add the same terms in different orders; each add
+// rounds by at most half a count, and rounding errors of either sum grow like
+// a random walk, so this is far beyond their usual distance.  The margin only
+// decides which chunks the chain adds term by term, never a result.
+__device__ __forceinline__ int64_t plan_margin(uint32_t chunks_to_end)
+{
+    return 4096 + (int64_t)(64.0 * __builtin_sqrt((double)chunks_to_end * (double)kChunk));
+}
 
 template <int CPB>
 __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a,
@@ -1114,10 +1269,16 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a,
     __shared__ double lds_p;
     __shared__ WalkLds sh;
     __shared__ ChainLds cl;
-    __shared__ RecLds srec;
-    __shared__ Run lds_grp[2];
-    __shared__ uint32_t lds_gkey[2];
-    const uint32_t g0 = blockIdx.x * CPB;  // first global chunk of the tile
+    __shared__ CrossLds xl;
+    __shared__ uint64_t lds_x[CPB][kCrossWords];
+    __shared__ uint64_t lds_words[kIrrWords + 1];
+    // With the chain on, the first a.count blocks walk it, one per sum.
+    const uint32_t nwalk = chain_on(a.flags) ? (uint32_t)a.count : 0u;
+    if (blockIdx.x < nwalk) {
+        chain_walk(a, (int)blockIdx.x, ch, sh, lds_words);
+        return;
+    }
+    const uint32_t g0 = (blockIdx.x - nwalk) * CPB;  // first global chunk of the tile
     const int s = find_sum(a, g0);
     const double *__restrict__ x = a.x[s];
     const size_t n = a.n[s];
@@ -1128,7 +1289,7 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a,
     const uint32_t nch = (uint32_t)((n + kChunk - 1) / kChunk);
     if (c0 >= nch)
         return;  // padding after the sum's last chunk
-    // A sum's first tile starts the exact chain: its waves go first in the
+    // A sum's first tile heads the exact chain: its waves go first in the
     // instruction arbitration of their SIMDs, ahead of streaming tiles.
     if (c0 == 0 && chain_on(a.flags))
         __builtin_amdgcn_s_setprio(3);
@@ -1214,12 +1375,12 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a,
         // near an edge of the planned binade: the plan is not trusted there
         if (key_has_fast_path(key[k]) && key[k] == key_of(Pk[k])) {
             const int64_t m = count_of(Pk[k]);
-            bool near = m < kCountLo + kPlanMargin;
+            const int64_t mg = plan_margin(c0 + k + 1);
+            bool near = m < kCountLo + mg;
             if (r.flags & kFlagNeg)
-                near |= m + r.lo - kPlanMargin < kCountLo + 1 ||
-                        m + r.hi + kPlanMargin > kCountHi - 1;
+                near |= m + r.lo - mg < kCountLo + 1 || m + r.hi + mg > kCountHi - 1;
             else
-                near |= m + r.hi + kPlanMargin > kCountHi;
+                near |= m + r.hi + mg > kCountHi;
             cross[k] |= near;
         }
     }
@@ -1290,113 +1451,109 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a,
     }
     if (threadIdx.x == 0)
         store_relaxed_u64(agg, kAggPresent);
-    // from here on this tile is on the chain's critical path
-    __builtin_amdgcn_s_setprio(3);
     int buf = 0;
-    // The record of the first chunk expected to cross into the next binade
-    // up.  Per-chunk values are picked by unrolled selects throughout: an
-    // array indexed by a run-time chunk number would live in scratch memory.
-    int rk = -1;
-#pragma unroll
-    for (int k = CPB - 1; k >= 0; k--)
-        if (c0 + k < nch && cross[k] && key_has_fast_path(key[k]) && !(key[k] & 0x800u) &&
-            key_has_fast_path(key[k] + 1u) &&
-            !(rflags[k] & (kFlagNeg | kFlagBad | kFlagNonFinite)))
-            rk = k;
-    if (rk >= 0) {
-        Four fr = opaque(f[0]);
-        uint32_t kr = opaque(key[0]);
-#pragma unroll
-        for (int j = 1; j < CPB; j++)
-            if (j == rk) {
-                fr = opaque(f[j]);
-                kr = opaque(key[j]);
-            }
-        if (!record_build(fr, kr, kr + 1u, sh, buf, srec))
-            rk = -1;
-    }
-    // The chunks before the record chunk (group 0) and after it (group 1),
-    // each composed into one run if its chunks share one planned binade and
-    // none is bad: one step each on the critical path instead of one per
-    // chunk.
+    // Crossings: every chunk expected to cross into the next binade up, with
+    // a plan for its binade, gets one located.  Per-chunk values are picked
+    // by unrolled selects: an array indexed by a run-time chunk number would
+    // live in scratch memory.
     const int nk = (int)(nch - c0 < (uint32_t)CPB ? nch - c0 : (uint32_t)CPB);
-    const int g0e = rk >= 0 ? rk : nk;      // group 0: chunks [0, g0e)
-    const int g1b = rk >= 0 ? rk + 1 : nk;  // group 1: chunks [g1b, nk)
-    if (threadIdx.x < 2) {
-        const int gb = threadIdx.x == 0 ? 0 : g1b, ge = threadIdx.x == 0 ? g0e : nk;
-        Run r = run_identity();
-        uint32_t gk = 0u;
-        bool same = gb < ge;
+    uint32_t want = 0u;
 #pragma unroll
-        for (int k = 0; k < CPB; k++) {
-            if (k >= gb && k < ge) {
-                const WaveRun w = chunk_run(k);
-                r = run_compose_sat(r, Run{w.p, w.lo, w.hi, w.flags});
-                if (k == gb)
-                    gk = key[k];
-                same &= key[k] == gk && key_has_fast_path(key[k]);
-            }
-        }
-        if (!same || (r.flags & (kFlagBad | kFlagNonFinite)))
-            gk = 0u;
-        lds_grp[threadIdx.x] = r;
-        lds_gkey[threadIdx.x] = gk;
-    }
-    __syncthreads();
-    bool ok = true;
-    double S = init;
-    if ((a.flags & EXSEQ_CHAIN_CUT) && tl >= ((nch + CPB - 1) / CPB) / 2 && tl > 0)
-        ok = false;
-    else if (c0 != 0)
-        S = chain_in(ch, tb, tl, sh, cl, buf, ok);
-    if (!ok) {
-        store_descs(0u);
-        if (threadIdx.x == 0)
-            store_relaxed_u64(ch.incl + tb + tl, kInclFailed);
-        return;
-    }
-    uint32_t resolved = 0u;
+    for (int k = 0; k < CPB; k++)
+        if (k < nk && !(c0 == 0 && k == 0) && cross[k] && key_has_fast_path(key[k]) &&
+            key[k] == key_of(Pk[k]) && !(key[k] & 0x800u) && key_has_fast_path(key[k] + 1u) &&
+            !(rflags[k] & (kFlagNeg | kFlagBad | kFlagNonFinite)))
+            want |= 1u << k;
+    uint32_t found = 0u;
 #pragma unroll 1
-    for (int k = 0; k < nk; k++) {
-        const int gi = k == 0 && g0e > 1 ? 0 : (k == g1b && nk - g1b > 1 ? 1 : -1);
-        if (gi >= 0) {
-            const uint32_t gk = lds_gkey[gi];
-            const Run g = lds_grp[gi];
-            const uint32_t ks = key_of(S);
-            const int64_t m = count_of(S);
-            if (gk != 0u && ks == gk && run_applies(m, g.p, g.lo, g.hi, g.flags)) {
-                S = assemble(ks, m + pair_at(g.p, m));
-                k = gi == 0 ? g0e - 1 : nk - 1;
-                continue;
-            }
-        }
-        Four fk = opaque(f[0]);
-        uint32_t kk = opaque(key[0]);
+    for (int k = 0; k < CPB; k++) {
+        if (!((want >> k) & 1u))
+            continue;
+        uint32_t kr = opaque(key[0]);
+        double pr = opaque(Pk[0]);
 #pragma unroll
         for (int j = 1; j < CPB; j++)
             if (j == k) {
-                fk = opaque(f[j]);
-                kk = opaque(key[j]);
+                kr = opaque(key[j]);
+                pr = opaque(Pk[j]);
             }
-        const WaveRun rn = chunk_run(k);
-        const uint32_t ks = key_of(S);
-        const int64_t m = count_of(S);
-        if (key_has_fast_path(ks) && ks == kk && run_applies(m, rn.p, rn.lo, rn.hi, rn.flags)) {
-            S = assemble(ks, m + pair_at(rn.p, m));
-        } else {
-            const size_t b = (size_t)(c0 + k) * kChunk;
-            const int len = (int)(n - b < (size_t)kChunk ? n - b : (size_t)kChunk);
-            int pos = 0;
-            const bool done = k == rk && (ks == kk || ks == kk + 1u) &&
-                              record_resolve(srec, fk, len, kk, kk + 1u, S, pos, sh, buf);
-            if (!done)
-                S = resolve_terms(fk, len, S, pos, sh, buf);
-            resolved |= 1u << k;
+        // the terms again (from cache, most likely): irregular tiles are few,
+        // and not keeping every chunk's terms in registers this far keeps
+        // the register count of all tiles down
+        const size_t b = (size_t)(c0 + k) * kChunk;
+        const int len = (int)(n - b < (size_t)kChunk ? n - b : (size_t)kChunk);
+        const Four fr = load_four(x, n, b + (size_t)kPer * threadIdx.x, false);
+        uint64_t w[kCrossWords];
+        if (crossing_find(fr, len, kr, count_of(pr), sh, xl, buf, w)) {
+            found |= 1u << k;
+            if (threadIdx.x == 0) {
+#pragma unroll
+                for (int i = 0; i < kCrossWords; i++)
+                    lds_x[k][i] = w[i];
+            }
         }
     }
-    store_descs(resolved);
-    if (threadIdx.x == 0)
-        store_relaxed_u64(ch.incl + tb + tl, enc_sum(S));
+    __syncthreads();  // lds_x is complete
+
+    // The composed run of the regular tiles back to the nearest irregular
+    // one, then the block for the walk, written into that tile's slot (the
+    // sum's first tile: into the head slot).
+    Run acc = run_identity();
+    uint32_t key0 = 0u;
+    int64_t xp = -1;
+    int st = c0 != 0 ? chain_back(ch, tb, tl, sh, cl, buf, acc, key0, xp) : kBackOk;
+    if ((a.flags & EXSEQ_CHAIN_CUT) && tl >= ((nch + CPB - 1) / CPB) / 2 && st == kBackOk && tl > 0)
+        st = kBackBad;  // a test hook: the walk of the chain stops here
+    if (st != kBackLost) {
+        uint64_t *blk = ch.irr + (size_t)kIrrWords * (tb + (size_t)(xp + 1));
+        if ((int)threadIdx.x < CPB) {
+            const int k = threadIdx.x;
+            uint64_t *cw = blk + kIrrChunk + kIrrPer * k;
+            const bool hx = (found >> k) & 1u;
+#pragma unroll
+            for (int i = 0; i < kCrossWords; i++)
+                store_relaxed_u64(cw + 4 + i, hx ? lds_x[k][i] : enc_i64(0));
+            if (k < nk) {
+                uint32_t kk = opaque(key[0]);
+#pragma unroll
+                for (int j = 1; j < CPB; j++)
+                    if (j == k)
+                        kk = opaque(key[j]);
+                const WaveRun r = chunk_run(k);
+                store_relaxed_u64(cw + 1, enc_i64(r.p.r0));
+                store_relaxed_u64(cw + 2, enc_i64(r.lo));
+                store_relaxed_u64(cw + 3, enc_i64(r.hi));
+                store_relaxed_u64(cw, kAggPresent | (uint64_t)(kk & kKeyMask) |
+                                          ((uint64_t)(r.p.r1 - r.p.r0 + 1) << kDrShift) |
+                                          (uint64_t)(r.flags & (kFlagNeg | kFlagBad | kFlagNonFinite)) |
+                                          (hx ? kIrrCross : 0ULL));
+            } else {
+                store_relaxed_u64(cw + 1, enc_i64(0));
+                store_relaxed_u64(cw + 2, enc_i64(0));
+                store_relaxed_u64(cw + 3, enc_i64(0));
+                store_relaxed_u64(cw, kAggPresent);
+            }
+        }
+        if (threadIdx.x == 0) {
+            uint64_t rm = kAggPresent;
+            if (st != kBackOk)
+                rm |= kIrrFailed;
+            else if (xp == (int64_t)tl - 1)
+                rm |= kIrrEmpty;
+            else
+                rm |= (uint64_t)(key0 & kKeyMask) |
+                      ((uint64_t)(acc.p.r1 - acc.p.r0 + 1) << kDrShift) |
+                      (uint64_t)(acc.flags & (kFlagNeg | kFlagBad | kFlagNonFinite));
+            store_relaxed_u64(blk + 1, enc_i64(acc.p.r0));
+            store_relaxed_u64(blk + 2, enc_i64(acc.lo));
+            store_relaxed_u64(blk + 3, enc_i64(acc.hi));
+            store_relaxed_u64(blk + kIrrTile, (uint64_t)tl + 1);
+            store_relaxed_u64(blk + kIrrInfo, kAggPresent | (uint64_t)nk);
+            store_relaxed_u64(blk + 0, rm);
+        }
+    }
+    store_descs(0u);
+
 }
 
 __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, DescArrays dall,
@@ -1488,6 +1645,15 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, DescArr
             fb_terms = st_terms;
             first_fb = st_first == 0x7FFFFFFFFFFFFFFFLL ? -1 : (int64_t)st_first;
             nonfinite |= st_nf != 0;
+            if (ch.wstat[4 * s + 3]) {
+                // what the walk of the chain added term by term (after the
+                // first tile, which marks its own descriptors)
+                n_fb += ch.wstat[4 * s + 0];
+                fb_terms += ch.wstat[4 * s + 1];
+                const int64_t wf = (int64_t)ch.wstat[4 * s + 2] - 1;
+                if (wf >= 0 && (first_fb < 0 || wf < first_fb))
+                    first_fb = wf;
+            }
             n_fast = start - n_fb;
         }
     } else if (nch && (dmeta[0] & kFlagExact)) {
@@ -1730,17 +1896,23 @@ __global__ __launch_bounds__(kPlanThreads) void tree_total_kernel(
 
 __global__ void write_value_kernel(double *out, double v) { out[0] = v; }
 
-// Zeroes the chain words of `tiles` tiles before a launch's tiles run.
+// Zeroes the chain words of `tiles` tiles (and the launch's record counter
+// and walk statistics) before a launch's tiles run.
 __global__ __launch_bounds__(256) void chain_clear_kernel(ChainArea ch, uint32_t tiles)
 {
     const uint32_t i = blockIdx.x * 256u + threadIdx.x;
     if (i < tiles) {
-        ch.agg[4 * (size_t)i + 0] = 0;
-        ch.agg[4 * (size_t)i + 1] = 0;
-        ch.agg[4 * (size_t)i + 2] = 0;
-        ch.agg[4 * (size_t)i + 3] = 0;
+#pragma unroll
+        for (int k = 0; k < 4; k++)
+            ch.agg[4 * (size_t)i + k] = 0;
         ch.incl[i] = 0;
+#pragma unroll
+        for (int k = 0; k < kIrrWords; k++)
+            ch.irr[(size_t)kIrrWords * i + k] = 0;
     }
+    if (blockIdx.x == 0)
+        for (int k = threadIdx.x; k < 4 * kMaxBatch; k += 256)
+            ch.wstat[k] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -1766,6 +1938,7 @@ struct WsParts {
     ChainArea ch;
 };
 
+
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 WsParts carve(void *ws, size_t total)
@@ -1785,6 +1958,10 @@ WsParts carve(void *ws, size_t total)
     p.ch.agg = reinterpret_cast<uint64_t *>(w);
     w += round256(4 * total * sizeof(uint64_t));
     p.ch.incl = reinterpret_cast<uint64_t *>(w);
+    w += round256(total * sizeof(uint64_t));
+    p.ch.irr = reinterpret_cast<uint64_t *>(w);
+    w += round256((size_t)kIrrWords * total * sizeof(uint64_t));
+    p.ch.wstat = reinterpret_cast<uint64_t *>(w);
     return p;
 }
 }  // namespace
@@ -1799,7 +1976,9 @@ size_t sum_ws_bytes(size_t total_chunks)
     return 4 * round256(total_chunks * sizeof(int64_t)) +
            round256(total_chunks * sizeof(uint32_t)) +
            round256(4 * total_chunks * sizeof(uint64_t)) +
-           round256(total_chunks * sizeof(uint64_t));
+           round256(total_chunks * sizeof(uint64_t)) +
+           round256((size_t)kIrrWords * total_chunks * sizeof(uint64_t)) +
+           round256(4 * kMaxBatch * sizeof(uint64_t));
 }
 
 template <int CPB>
@@ -1807,9 +1986,10 @@ static void launch_tiles(const BatchArgs &args, uint32_t total, const WsParts &p
                          hipStream_t stream)
 {
     const unsigned tiles = total / CPB;
+    const unsigned walkers = chain_on(args.flags) ? (unsigned)args.count : 0u;
     if (tiles)
-        hipLaunchKernelGGL(tile_kernel<CPB>, dim3(tiles), dim3(kChunkThreads), 0, stream, args,
-                           p.status, p.d, p.ch);
+        hipLaunchKernelGGL(tile_kernel<CPB>, dim3(walkers + tiles), dim3(kChunkThreads), 0, stream,
+                           args, p.status, p.d, p.ch);
 }
 
 int launch_batch(const BatchArgs &a, void *ws, double *outs, hipStream_t stream,
