@@ -42,6 +42,11 @@ struct BatchArgs {
     uint64_t n[kMaxBatch];
     double init[kMaxBatch];
     uint32_t chunk_base[kMaxBatch + 1];
+    // Dispatch order of the tiles with the exact chain: each sum's last tile
+    // first (last_tile: its index in the launch, ~0u for an empty sum), then
+    // the others in order (rest_base: prefix count of them per sum).
+    uint32_t last_tile[kMaxBatch];
+    uint32_t rest_base[kMaxBatch + 1];
 };
 
 // Descriptors live in four arrays (structure of arrays, so that the walk

@@ -294,6 +294,63 @@ __device__ __forceinline__ WaveRun wave_run(const Four &f, uint32_t key)
     return w;
 }
 
+// The runs of CPB chunks at once (one wave's part of each, as wave_run).
+// Where no term of the wave ties and none is negative under its chunk's key
+// -- nearly always -- the CPB order-free integer sums are taken together so
+// that their reduction chains overlap; otherwise chunk by chunk.
+template <int CPB>
+__device__ __forceinline__ void wave_runs(const Four *f, const uint32_t *key,
+                                          WaveRun (*lds)[kChunkThreads / 64])
+{
+    int64_t v[CPB];
+    uint32_t fl[CPB];
+    bool easy = true;
+#pragma unroll
+    for (int k = 0; k < CPB; k++) {
+        const int scale = 1075 - (int)(key[k] & 0x7FFu);
+        const bool sgn = (key[k] >> 11) & 1u;
+        bool neg = false, bad = false, nonfin = false, tie = false;
+        int64_t sum = 0;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            if (i < f[k].cnt) {
+                const TermInc ti = term_inc(f[k].v[i], scale, sgn);
+                sum += ti.r0;
+                neg |= ti.neg;
+                bad |= ti.bad;
+                nonfin |= is_nonfinite(f[k].v[i]);
+                tie |= ti.r0 != ti.r1;
+            }
+        }
+        v[k] = sum;
+        const bool wtie = __ballot(tie) != 0;
+        const bool wneg = __ballot(neg) != 0;
+        fl[k] = (wneg ? kFlagNeg : 0u) | (__ballot(bad) ? kFlagBad : 0u) |
+                (__ballot(nonfin) ? kFlagNonFinite : 0u);
+        easy &= !wtie && !wneg;
+    }
+    if (easy) {
+        wave_sum_i64_n<CPB>(v);
+        if (lane_id() == 0) {
+#pragma unroll
+            for (int k = 0; k < CPB; k++) {
+                WaveRun w;
+                w.p = Pair{v[k], v[k]};
+                w.lo = w.hi = 0;
+                w.flags = fl[k];
+                lds[k][wave_id()] = w;
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int k = 0; k < CPB; k++) {
+        const WaveRun w = wave_run(f[k], key[k]);
+        if (lane_id() == 0)
+            lds[k][wave_id()] = w;
+    }
+}
+
 // The four waves' parts composed in order.
 __device__ __forceinline__ WaveRun join_waves(const WaveRun *w)
 {
@@ -1093,19 +1150,19 @@ __device__ __forceinline__ int crossing_apply(const uint64_t *w, int len, uint32
 
 // ---------------------------------------------------------------------------
 // The walk of the chain.  Irregular tiles do not wait for each other.  Each
-// one writes a block of words into the slot of the nearest irregular tile
-// before it (the sum's first tile: into the sum's head slot): its own index,
-// the composed run of the regular tiles in between (R), and its chunks'
-// runs, each with the crossing record slot it filled, if any.  One workgroup
-// per sum (the first blocks of the tile launch, so resident from the start)
-// follows these blocks: one round trip to memory gives the next irregular
-// tile and all it needs, apart from records.  It adds the sum's first chunk
-// from init before anything is published, then for each irregular tile
-// applies R and each chunk's run, its record or its terms one by one, and
-// writes the exact sum after the tile to incl, while the tiles behind it
-// still stream.
+// one writes a block of words at its own index: the index of the nearest
+// irregular tile before it, the composed run of the regular tiles in between
+// (R), and its chunks' runs, each with its located crossing, if any.  One
+// workgroup per sum (the first blocks of the tile launch, so resident from
+// the start) walks the chain: it adds the sum's first chunk from init before
+// anything is published; then, a window of 1024 tiles at a time, one round
+// trip to memory tells it which tiles are irregular (the first word of every
+// tile's agg words), and one more brings the blocks of up to five of them.
+// For each irregular tile in order it applies R, then each chunk's run, its
+// crossing or its terms one by one, and writes the exact sum after the tile
+// to incl, while the tiles behind it still stream.
 // ---------------------------------------------------------------------------
-constexpr int kIrrTile = 4;    // 1 + index of the tile the block describes
+constexpr int kIrrTile = 4;    // 2 + index of the irregular tile before (1: none)
 constexpr int kIrrInfo = 5;    // present | chunks
 constexpr int kIrrChunk = 6;   // chunk k at 6 + 10k: meta, r0, lo, hi, crossing[6]
 constexpr int kIrrPer = 4 + kCrossWords;
@@ -1131,11 +1188,29 @@ struct WalkOut {
     int64_t first;
 };
 
+constexpr int kWalkBatch = kChunkThreads / kIrrWords;  // blocks per round trip
+
+// A value known to be the same in every lane, moved to scalar registers so
+// that the walk's bookkeeping on it runs on the scalar unit.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+struct WalkLdsX {
+    uint64_t words[kWalkBatch][kIrrWords];
+    int queue[kBackPer * kChunkThreads];  // irregular tiles found, in order
+    int cnt[kWaves];
+    int unk[kWaves];
+};
+
 __device__ __forceinline__ void chain_walk(const BatchArgs &a, int s, const ChainArea &ch,
-                                           WalkLds &sh, uint64_t *words)
+                                           WalkLds &sh, WalkLdsX &wl)
 {
     __builtin_amdgcn_s_setprio(3);  // the walk is the critical path
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, lane = lane_id(), wave = wave_id();
     const double *__restrict__ x = a.x[s];
     const size_t n = a.n[s];
     const size_t nch = (n + kChunk - 1) / kChunk;
@@ -1146,76 +1221,147 @@ __device__ __forceinline__ void chain_walk(const BatchArgs &a, int s, const Chai
     int buf = 0;
     if (nch == 0)
         return;
-    const uint32_t tlast = (uint32_t)((nch - 1) / cpb);
-    // the head block's words go out first, then the first chunk is added
-    uint64_t pre = t < nw ? load_relaxed_u64(ch.irr + (size_t)kIrrWords * tb + t) : 0;
+    const int64_t tlast = (int64_t)((nch - 1) / cpb);
     double S = resolve_chunk(x, n, 0, a.init[s], 0, sh, buf);
     wo.fb = 1;
     wo.terms = n < (size_t)kChunk ? n : (size_t)kChunk;
     wo.first = 0;
-    int64_t cur = -1;  // the last irregular tile walked
-    while (true) {
-        // the block in the slot of tile cur (cur = -1: the head slot)
-        const uint64_t *blk = ch.irr + (size_t)kIrrWords * (tb + (size_t)(cur + 1));
-        __syncthreads();  // words[] of the previous tile are read
-        if (t < nw)
-            words[t] = pre != 0 ? pre : spin_load(blk + t);
+    int64_t cur = -1;   // the last irregular tile walked
+    int64_t scan = 0;   // tiles before this one are known to be regular or queued
+    bool ok = true;
+    for (int idle = 0; ok && cur != tlast && idle <= kSpinLimit;) {
+        // ---- which tiles of the next window are irregular
+        uint64_t m[kBackPer];
+#pragma unroll
+        for (int i = 0; i < kBackPer; i++) {
+            const int64_t j = scan + kBackPer * t + i;
+            m[i] = j <= tlast ? load_relaxed_u64(ch.agg + 4 * ((size_t)tb + (size_t)j)) : kAggPresent;
+        }
+        int unk = kBackPer * kChunkThreads, cnt = 0;
+#pragma unroll
+        for (int i = kBackPer - 1; i >= 0; i--) {
+            const int64_t j = scan + kBackPer * t + i;
+            if (j <= tlast && m[i] == 0)
+                unk = kBackPer * t + i;
+        }
+        // the window ends at the first tile not yet published
+        const uint64_t bu = __ballot(unk < kBackPer * kChunkThreads);
+        if (lane == 0)
+            wl.unk[wave] = bu ? __builtin_amdgcn_readlane(unk, (int)__builtin_ctzll(bu))
+                              : kBackPer * kChunkThreads;
         __syncthreads();
-        const uint64_t xw = words[kIrrTile], info = words[kIrrInfo], rm = words[0];
-        if (!(info & kAggPresent) || !(rm & kAggPresent) || (rm & kIrrFailed) || xw == 0 ||
-            (int64_t)xw - 1 <= cur || xw - 1 > tlast)
-            break;
-        const uint32_t X = (uint32_t)(xw - 1);
-        // the next block, if already there (not waited for)
-        pre = t < nw && X != tlast ? load_relaxed_u64(ch.irr + (size_t)kIrrWords * (tb + X + 1) + t)
-                                   : 0;
-        // R: the regular tiles since tile cur
-        if (!(rm & kIrrEmpty)) {
-            const uint32_t rkey = (uint32_t)rm & kKeyMask;
-            const int64_t r0 = dec_i64(words[1]);
-            const Pair p{r0, r0 + (int64_t)((rm >> kDrShift) & 3u) - 1};
-            const uint32_t ks = key_of(S);
-            const int64_t m = count_of(S);
-            if (ks != rkey || !key_has_fast_path(ks) ||
-                !run_applies(m, p, dec_i64(words[2]), dec_i64(words[3]),
-                             (uint32_t)rm & (kFlagNeg | kFlagBad | kFlagNonFinite)))
-                break;
-            S = assemble(ks, m + pair_at(p, m));
+        int end = kBackPer * kChunkThreads;
+#pragma unroll
+        for (int k = 0; k < kWaves; k++)
+            end = wl.unk[k] < end ? wl.unk[k] : end;
+        // the irregular tiles before it, in order, into the queue
+#pragma unroll
+        for (int i = 0; i < kBackPer; i++) {
+            const int64_t j = scan + kBackPer * t + i;
+            cnt += j <= tlast && kBackPer * t + i < end && !(m[i] & kAggRegular);
         }
-        const int nk = (int)(info & 15u);
-        const size_t cX = (size_t)X * cpb;  // first local chunk of X
-        for (int k = X == 0 ? 1 : 0; k < nk; k++) {
-            const uint64_t *cw = words + kIrrChunk + kIrrPer * k;
-            const uint64_t cm = cw[0];
-            const uint32_t kk = (uint32_t)cm & kKeyMask;
-            const uint32_t fl = (uint32_t)cm & (kFlagNeg | kFlagBad | kFlagNonFinite);
-            const int64_t r0 = dec_i64(cw[1]);
-            const Pair p{r0, r0 + (int64_t)((cm >> kDrShift) & 3u) - 1};
-            const uint32_t ks = key_of(S);
-            const int64_t m = count_of(S);
-            if (key_has_fast_path(ks) && ks == kk &&
-                run_applies(m, p, dec_i64(cw[2]), dec_i64(cw[3]), fl)) {
-                S = assemble(ks, m + pair_at(p, m));
-                continue;
-            }
-            const size_t c = cX + (size_t)k;
-            const int len = (int)(n - c * kChunk < (size_t)kChunk ? n - c * kChunk : (size_t)kChunk);
-            int pos = 0;
-            const int xr = (cm & kIrrCross) ? crossing_apply(cw + 4, len, kk, S, pos) : 0;
-            if (xr != 1) {
-                const Four f = load_four(x, n, c * kChunk + (size_t)kPer * t, false);
-                S = resolve_terms(f, len, S, xr == 2 ? pos : 0, sh, buf);
-            }
-            wo.fb++;
-            wo.terms += (uint64_t)len;
-            if (wo.first < 0)
-                wo.first = (int64_t)c;
+        const int64_t incl = wave_incl_scan_i64(cnt);
+        if (lane == 63)
+            wl.cnt[wave] = (int)incl;
+        __syncthreads();
+        int before = 0, total = 0;
+#pragma unroll
+        for (int k = 0; k < kWaves; k++) {
+            before += k < wave ? wl.cnt[k] : 0;
+            total += wl.cnt[k];
         }
-        if (t == 0)
-            ch.incl[tb + X] = enc_sum(S);
-        cur = X;
-        if (X == tlast)
-            break;
+        int qi = before + (int)incl - cnt;
+#pragma unroll
+        for (int i = 0; i < kBackPer; i++) {
+            const int64_t j = scan + kBackPer * t + i;
+            if (j <= tlast && kBackPer * t + i < end && !(m[i] & kAggRegular))
+                wl.queue[qi++] = (int)j;
+        }
+        __syncthreads();
+        scan += end;
+        if (total == 0) {
+            idle++;
+            __builtin_amdgcn_s_sleep(2);
+            continue;
+        }
+        idle = 0;
+        // ---- their blocks, kWalkBatch per round trip
+        for (int q0 = 0; ok && q0 < total; q0 += kWalkBatch) {
+            const int qb = t / kIrrWords, qw = t % kIrrWords;
+            const int nq = total - q0 < kWalkBatch ? total - q0 : kWalkBatch;
+            if (qb < nq && qw < nw)
+                wl.words[qb][qw] = spin_load(ch.irr + (size_t)kIrrWords * (tb + (size_t)wl.queue[q0 + qb]) + qw);
+            __syncthreads();
+            for (int q = 0; q < nq; q++) {
+                const uint64_t *words = wl.words[q];
+                const int64_t X = wl.queue[q0 + q];
+                // the head words at once (one LDS latency, not one per word)
+                uint64_t hw[kIrrChunk];
+#pragma unroll
+                for (int i = 0; i < kIrrChunk; i++)
+                    hw[i] = uniform_u64(words[i]);
+                S = bitsd(uniform_u64(dbits(S)));
+                const uint64_t xw = hw[kIrrTile], info = hw[kIrrInfo], rm = hw[0];
+                if (!(info & kAggPresent) || !(rm & kAggPresent) || (rm & kIrrFailed) ||
+                    (int64_t)xw - 2 != cur) {
+                    ok = false;
+                    break;
+                }
+                // R: the regular tiles since tile cur
+                if (!(rm & kIrrEmpty)) {
+                    const uint32_t rkey = (uint32_t)rm & kKeyMask;
+                    const int64_t r0 = dec_i64(hw[1]);
+                    const Pair p{r0, r0 + (int64_t)((rm >> kDrShift) & 3u) - 1};
+                    const uint32_t ks = key_of(S);
+                    const int64_t mm = count_of(S);
+                    if (ks != rkey || !key_has_fast_path(ks) ||
+                        !run_applies(mm, p, dec_i64(hw[2]), dec_i64(hw[3]),
+                                     (uint32_t)rm & (kFlagNeg | kFlagBad | kFlagNonFinite))) {
+                        ok = false;
+                        break;
+                    }
+                    S = assemble(ks, mm + pair_at(p, mm));
+                }
+                const int nk = (int)(info & 15u);
+                const size_t cX = (size_t)X * cpb;  // first local chunk of X
+                for (int k = X == 0 ? 1 : 0; k < nk; k++) {
+                    uint64_t cw[kIrrPer];  // the chunk's words at once
+#pragma unroll
+                    for (int i = 0; i < kIrrPer; i++)
+                        cw[i] = uniform_u64(words[kIrrChunk + kIrrPer * k + i]);
+                    const uint64_t cm = cw[0];
+                    const uint32_t kk = (uint32_t)cm & kKeyMask;
+                    const uint32_t fl = (uint32_t)cm & (kFlagNeg | kFlagBad | kFlagNonFinite);
+                    const int64_t r0 = dec_i64(cw[1]);
+                    const Pair p{r0, r0 + (int64_t)((cm >> kDrShift) & 3u) - 1};
+                    const uint32_t ks = key_of(S);
+                    const int64_t mm = count_of(S);
+                    if (key_has_fast_path(ks) && ks == kk &&
+                        run_applies(mm, p, dec_i64(cw[2]), dec_i64(cw[3]), fl)) {
+                        S = assemble(ks, mm + pair_at(p, mm));
+                        continue;
+                    }
+                    const size_t c = cX + (size_t)k;
+                    const int len =
+                        (int)(n - c * kChunk < (size_t)kChunk ? n - c * kChunk : (size_t)kChunk);
+                    int pos = 0;
+                    const int xr = (cm & kIrrCross) ? crossing_apply(cw + 4, len, kk, S, pos) : 0;
+                    if (xr != 1) {
+                        const Four f = load_four(x, n, c * kChunk + (size_t)kPer * t, false);
+                        S = resolve_terms(f, len, S, xr == 2 ? pos : 0, sh, buf);
+                    }
+                    S = bitsd(uniform_u64(dbits(S)));
+                    wo.fb++;
+                    wo.terms += (uint64_t)len;
+                    if (wo.first < 0)
+                        wo.first = (int64_t)c;
+                }
+                if (t == 0)
+                    ch.incl[tb + (size_t)X] = enc_sum(S);
+                cur = X;
+            }
+            __syncthreads();  // wl.words is read
+        }
     }
     if (t == 0) {
         ch.wstat[4 * s + 0] = wo.fb;
@@ -1266,19 +1412,45 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a,
     constexpr int kW = kChunkThreads / 64;
     __shared__ double lds_t[CPB][kW];
     __shared__ WaveRun lds_runs[CPB][kW];
+    __shared__ WaveRun lds_join[CPB];
+    __shared__ bool lds_cross[CPB];
     __shared__ double lds_p;
     __shared__ WalkLds sh;
     __shared__ ChainLds cl;
     __shared__ CrossLds xl;
     __shared__ uint64_t lds_x[CPB][kCrossWords];
-    __shared__ uint64_t lds_words[kIrrWords + 1];
+    __shared__ WalkLdsX wl;
     // With the chain on, the first a.count blocks walk it, one per sum.
     const uint32_t nwalk = chain_on(a.flags) ? (uint32_t)a.count : 0u;
     if (blockIdx.x < nwalk) {
-        chain_walk(a, (int)blockIdx.x, ch, sh, lds_words);
+        chain_walk(a, (int)blockIdx.x, ch, sh, wl);
         return;
     }
-    const uint32_t g0 = (blockIdx.x - nwalk) * CPB;  // first global chunk of the tile
+    // With the chain on, each sum's last tile goes right after the walks:
+    // the walk ends with it, and started early it has waited for the tiles
+    // before it by the time they are done.  Nothing waits on it but the walk.
+    uint32_t gt = blockIdx.x - nwalk;  // this block's tile
+    if (nwalk) {
+        if (gt < (uint32_t)a.count) {
+            gt = a.last_tile[gt];
+            if (gt == ~0u)
+                return;
+        } else {
+            const uint32_t r = gt - (uint32_t)a.count;
+            int lo = 0, hi = a.count - 1;  // the first sum with rest_base[s + 1] > r
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (a.rest_base[mid + 1] > r)
+                    hi = mid;
+                else
+                    lo = mid + 1;
+            }
+            const uint32_t first = a.chunk_base[lo] / CPB;
+            const uint32_t q = r - a.rest_base[lo];
+            gt = first + (q < a.last_tile[lo] - first ? q : q + 1);
+        }
+    }
+    const uint32_t g0 = gt * CPB;  // first global chunk of the tile
     const int s = find_sum(a, g0);
     const double *__restrict__ x = a.x[s];
     const size_t n = a.n[s];
@@ -1298,11 +1470,17 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a,
 #pragma unroll
     for (int k = 0; k < CPB; k++)
         f[k] = load_four(x, n, (size_t)(c0 + k) * kChunk + (size_t)threadIdx.x * 4, true);
+    {
+        double ws[CPB];
 #pragma unroll
-    for (int k = 0; k < CPB; k++) {
-        const double ws = wave_sum_f64((f[k].v[0] + f[k].v[1]) + (f[k].v[2] + f[k].v[3]));
-        if (lane == 0)
-            lds_t[k][wave] = ws;
+        for (int k = 0; k < CPB; k++)
+            ws[k] = (f[k].v[0] + f[k].v[1]) + (f[k].v[2] + f[k].v[3]);
+        wave_sum_f64_n<CPB>(ws);
+        if (lane == 0) {
+#pragma unroll
+            for (int k = 0; k < CPB; k++)
+                lds_t[k][wave] = ws[k];
+        }
     }
     __syncthreads();
     double T[CPB];
@@ -1346,66 +1524,78 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a,
         cross[k] = key_of(P + T[k]) != key_of(P);
         P += T[k];
     }
+    {
+        bool allfast = true;
 #pragma unroll
-    for (int k = 0; k < CPB; k++) {
-        WaveRun w;
-        if (key_has_fast_path(key[k])) {
-            w = wave_run(f[k], key[k]);
+        for (int k = 0; k < CPB; k++)
+            allfast &= key_has_fast_path(key[k]);
+        if (allfast) {
+            wave_runs<CPB>(f, key, lds_runs);
         } else {
-            bool nf = false;
 #pragma unroll
-            for (int i = 0; i < 4; i++)
-                nf |= i < f[k].cnt && is_nonfinite(f[k].v[i]);
-            w.p = pair_identity();
-            w.lo = w.hi = 0;
-            w.flags = __ballot(nf) ? kFlagNonFinite : 0u;
+            for (int k = 0; k < CPB; k++) {
+                WaveRun w;
+                if (key_has_fast_path(key[k])) {
+                    w = wave_run(f[k], key[k]);
+                } else {
+                    bool nf = false;
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        nf |= i < f[k].cnt && is_nonfinite(f[k].v[i]);
+                    w.p = pair_identity();
+                    w.lo = w.hi = 0;
+                    w.flags = __ballot(nf) ? kFlagNonFinite : 0u;
+                }
+                if (lane == 0)
+                    lds_runs[k][wave] = w;
+            }
         }
-        if (lane == 0)
-            lds_runs[k][wave] = w;
     }
     __syncthreads();
-    // A chunk's run is joined from LDS where it is needed (chunk_run), so
-    // that the runs do not hold registers through the chain.
-    auto chunk_run = [&](int k) { return clamp_run(join_waves(lds_runs[k])); };
-    uint32_t rflags[CPB];
+    // Each chunk's run is joined, clamped and checked against the edges of
+    // its binade once, by one lane (lane k for chunk k), which also stores
+    // the chunk's descriptor for the walk; the rest of the tile reads the
+    // result from LDS.  (Work that is the same for every lane costs as much
+    // in one wave as in all of them.)
+    if ((int)threadIdx.x < CPB) {
+        const int k = threadIdx.x;
+        uint32_t kk = opaque(key[0]);
+        double pk = opaque(Pk[0]);
+        bool cc = cross[0];
 #pragma unroll
-    for (int k = 0; k < CPB; k++) {
-        const WaveRun r = chunk_run(k);
-        rflags[k] = r.flags;
+        for (int j = 1; j < CPB; j++)
+            if (j == k) {
+                kk = opaque(key[j]);
+                pk = opaque(Pk[j]);
+                cc = cross[j];
+            }
+        const WaveRun r = clamp_run(join_waves(lds_runs[k]));
         // near an edge of the planned binade: the plan is not trusted there
-        if (key_has_fast_path(key[k]) && key[k] == key_of(Pk[k])) {
-            const int64_t m = count_of(Pk[k]);
+        if (key_has_fast_path(kk) && kk == key_of(pk)) {
+            const int64_t m = count_of(pk);
             const int64_t mg = plan_margin(c0 + k + 1);
             bool near = m < kCountLo + mg;
             if (r.flags & kFlagNeg)
                 near |= m + r.lo - mg < kCountLo + 1 || m + r.hi + mg > kCountHi - 1;
             else
                 near |= m + r.hi + mg > kCountHi;
-            cross[k] |= near;
+            cc |= near;
         }
+        lds_join[k] = r;
+        lds_cross[k] = cc;
+        if (c0 + k < nch)
+            store_desc(d, (size_t)(g0 + k), kk, r, cc ? kFlagCross : 0u);
+    }
+    __syncthreads();
+    auto chunk_run = [&](int k) { return lds_join[k]; };
+    uint32_t rflags[CPB];
+#pragma unroll
+    for (int k = 0; k < CPB; k++) {
+        rflags[k] = lds_join[k].flags;
+        cross[k] = lds_cross[k];
     }
 
-    // descriptors for the walk (regular tiles and those that fail);
-    // resolved: bit k for chunks added term by term
-    auto store_descs = [&](uint32_t resolved) {
-        if ((int)threadIdx.x < CPB) {
-            const int k = threadIdx.x;
-            if (c0 + k < nch) {
-                uint32_t kk = opaque(key[0] | (cross[0] ? 0x80000000u : 0u));
-#pragma unroll
-                for (int j = 1; j < CPB; j++)
-                    if (j == k)
-                        kk = opaque(key[j] | (cross[j] ? 0x80000000u : 0u));
-                const bool cc = (kk >> 31) != 0;
-                kk &= kKeyMask;
-                store_desc(d, (size_t)(g0 + k), kk, chunk_run(k),
-                           (cc ? kFlagCross : 0u) | (((resolved >> k) & 1u) ? kFlagResolved : 0u));
-            }
-        }
-    };
-
     if (!chain_on(a.flags)) {
-        store_descs(0u);
         // A sum's first chunk starts from init exactly.  There the running
         // sum is small next to the terms and crosses many binades, the worst
         // case of the walk's rounds, so its tile adds it in order and records
@@ -1431,14 +1621,13 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a,
         regular &= key_has_fast_path(key[k]) && key[k] == key[0] && !cross[k] &&
                    !(rflags[k] & (kFlagBad | kFlagNonFinite));
     if (regular) {
-        store_descs(0u);
-        Run tr = run_identity();
-#pragma unroll
-        for (int k = 0; k < CPB; k++) {
-            const WaveRun r = chunk_run(k);
-            tr = run_compose_sat(tr, Run{r.p, r.lo, r.hi, r.flags});
-        }
         if (threadIdx.x == 0) {
+            Run tr = run_identity();
+#pragma unroll
+            for (int k = 0; k < CPB; k++) {
+                const WaveRun r = chunk_run(k);
+                tr = run_compose_sat(tr, Run{r.p, r.lo, r.hi, r.flags});
+            }
             const int64_t dr = tr.p.r1 - tr.p.r0;
             store_relaxed_u64(agg + 1, enc_i64(tr.p.r0));
             store_relaxed_u64(agg + 2, enc_i64(tr.lo));
@@ -1504,8 +1693,8 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a,
     int st = c0 != 0 ? chain_back(ch, tb, tl, sh, cl, buf, acc, key0, xp) : kBackOk;
     if ((a.flags & EXSEQ_CHAIN_CUT) && tl >= ((nch + CPB - 1) / CPB) / 2 && st == kBackOk && tl > 0)
         st = kBackBad;  // a test hook: the walk of the chain stops here
-    if (st != kBackLost) {
-        uint64_t *blk = ch.irr + (size_t)kIrrWords * (tb + (size_t)(xp + 1));
+    {
+        uint64_t *blk = ch.irr + (size_t)kIrrWords * (tb + tl);
         if ((int)threadIdx.x < CPB) {
             const int k = threadIdx.x;
             uint64_t *cw = blk + kIrrChunk + kIrrPer * k;
@@ -1547,13 +1736,11 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a,
             store_relaxed_u64(blk + 1, enc_i64(acc.p.r0));
             store_relaxed_u64(blk + 2, enc_i64(acc.lo));
             store_relaxed_u64(blk + 3, enc_i64(acc.hi));
-            store_relaxed_u64(blk + kIrrTile, (uint64_t)tl + 1);
+            store_relaxed_u64(blk + kIrrTile, (uint64_t)(xp + 2));
             store_relaxed_u64(blk + kIrrInfo, kAggPresent | (uint64_t)nk);
             store_relaxed_u64(blk + 0, rm);
         }
     }
-    store_descs(0u);
-
 }
 
 __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, DescArrays dall,
@@ -1986,10 +2173,12 @@ static void launch_tiles(const BatchArgs &args, uint32_t total, const WsParts &p
                          hipStream_t stream)
 {
     const unsigned tiles = total / CPB;
-    const unsigned walkers = chain_on(args.flags) ? (unsigned)args.count : 0u;
+    const bool chain = chain_on(args.flags);
+    const unsigned blocks =
+        chain ? (unsigned)args.count * 2u + args.rest_base[args.count] : tiles;
     if (tiles)
-        hipLaunchKernelGGL(tile_kernel<CPB>, dim3(walkers + tiles), dim3(kChunkThreads), 0, stream,
-                           args, p.status, p.d, p.ch);
+        hipLaunchKernelGGL(tile_kernel<CPB>, dim3(blocks), dim3(kChunkThreads), 0, stream, args,
+                           p.status, p.d, p.ch);
 }
 
 int launch_batch(const BatchArgs &a, void *ws, double *outs, hipStream_t stream,
@@ -2006,6 +2195,13 @@ int launch_batch(const BatchArgs &a, void *ws, double *outs, hipStream_t stream,
     const uint32_t sel = (a.flags >> kTileShift) & 3u;  // 0: default
     args.tile = sel == 1 ? 1u : (sel == 2 ? 2u : 4u);
     const uint32_t tiles = total / args.tile;
+    args.rest_base[0] = 0;
+    for (int k = 0; k < a.count; k++) {
+        const uint32_t nch = (uint32_t)((a.n[k] + kChunk - 1) / kChunk);
+        const uint32_t tk = (a.chunk_base[k + 1] - a.chunk_base[k]) / args.tile;
+        args.last_tile[k] = nch ? a.chunk_base[k] / args.tile + (nch - 1) / args.tile : ~0u;
+        args.rest_base[k + 1] = args.rest_base[k] + (nch ? tk - 1 : tk);
+    }
     mark(0);
     if (chain_on(a.flags) && tiles)
         hipLaunchKernelGGL(chain_clear_kernel, dim3((tiles + 255) / 256), dim3(256), 0, stream,

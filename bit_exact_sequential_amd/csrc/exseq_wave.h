@@ -117,6 +117,61 @@ __device__ __forceinline__ double wave_sum_f64(double v)
     return readlane_f64(v, 63);
 }
 
+// N independent wave sums, each step taken for all N before the next so
+// that the N dependency chains overlap.  Each sum has the same fixed order
+// as the single-value version.
+template <int N>
+__device__ __forceinline__ void wave_sum_i64_n(int64_t *v)
+{
+#pragma unroll
+    for (int k = 0; k < N; k++)
+        v[k] += dpp_i64<kDppRowShr1>(v[k], 0);
+#pragma unroll
+    for (int k = 0; k < N; k++)
+        v[k] += dpp_i64<kDppRowShr2>(v[k], 0);
+#pragma unroll
+    for (int k = 0; k < N; k++)
+        v[k] += dpp_i64<kDppRowShr4>(v[k], 0);
+#pragma unroll
+    for (int k = 0; k < N; k++)
+        v[k] += dpp_i64<kDppRowShr8>(v[k], 0);
+#pragma unroll
+    for (int k = 0; k < N; k++)
+        v[k] += dpp_i64<kDppRowBcast15, 0xA>(v[k], 0);
+#pragma unroll
+    for (int k = 0; k < N; k++)
+        v[k] += dpp_i64<kDppRowBcast31, 0xC>(v[k], 0);
+#pragma unroll
+    for (int k = 0; k < N; k++)
+        v[k] = readlane_i64(v[k], 63);
+}
+
+template <int N>
+__device__ __forceinline__ void wave_sum_f64_n(double *v)
+{
+#pragma unroll
+    for (int k = 0; k < N; k++)
+        v[k] += dpp_f64<kDppRowShr1>(v[k], 0.0);
+#pragma unroll
+    for (int k = 0; k < N; k++)
+        v[k] += dpp_f64<kDppRowShr2>(v[k], 0.0);
+#pragma unroll
+    for (int k = 0; k < N; k++)
+        v[k] += dpp_f64<kDppRowShr4>(v[k], 0.0);
+#pragma unroll
+    for (int k = 0; k < N; k++)
+        v[k] += dpp_f64<kDppRowShr8>(v[k], 0.0);
+#pragma unroll
+    for (int k = 0; k < N; k++)
+        v[k] += dpp_f64<kDppRowBcast15, 0xA>(v[k], 0.0);
+#pragma unroll
+    for (int k = 0; k < N; k++)
+        v[k] += dpp_f64<kDppRowBcast31, 0xC>(v[k], 0.0);
+#pragma unroll
+    for (int k = 0; k < N; k++)
+        v[k] = readlane_f64(v[k], 63);
+}
+
 // Ordered composition of the wave's pairs (lane 0 first), in every lane.
 __device__ __forceinline__ Pair wave_reduce_pair(Pair v)
 {
