@@ -146,7 +146,7 @@ int ssim_term_and_sum(const uint8_t *ref, const uint8_t *dis, int width, int hei
     if (!ref || !dis || !out_sum || !aligned8(out_sum) || width < 1 || height < 1 ||
         stride < width || radius < 0 || radius > 15)
         return EXSEQ_EINVAL;
-    if ((size_t)width * (size_t)height > ((size_t)1 << 34))
+    if ((size_t)width * (size_t)height >= ((size_t)1 << 31))
         return EXSEQ_EINVAL;
     if ((out_weight_sum && !aligned8(out_weight_sum)) || (out_terms && !aligned8(out_terms)))
         return EXSEQ_EINVAL;

@@ -30,6 +30,24 @@ inline size_t padded_chunks(size_t n)
     return (c + kTileMax - 1) / kTileMax * kTileMax;
 }
 
+// A lane's four consecutive terms of a chunk (cnt of them exist).
+struct Four {
+    double v[4];
+    int cnt;
+};
+
+// The fused integer-SSIM term source: two 8-bit planes, the window radius
+// and the stabilisers; out_terms (nullable) receives every term.
+struct SsimParams {
+    const uint8_t *ref;
+    const uint8_t *dis;
+    int width, height;
+    ptrdiff_t stride;
+    int radius;
+    double c1, c2;
+    double *out_terms;
+};
+
 // Up to kMaxBatch independent sums, passed to the kernels by value.  Sum k
 // owns the global chunks [chunk_base[k], chunk_base[k + 1]) (its chunks,
 // padded to a multiple of kTileMax).
@@ -93,5 +111,8 @@ int launch_ssim_sum(const uint8_t *ref, const uint8_t *dis, int width, int heigh
                     ptrdiff_t stride, int radius, double c1, double c2, double *out_sum,
                     int64_t *out_weight_sum, double *out_terms, void *ws, hipStream_t stream,
                     uint32_t flags, exseq_stats *stats);
+// The exact sum of the fused term source (exseq_sum.hip).
+int launch_ssim_exact(const SsimParams &sp, double *out, void *ws, hipStream_t stream,
+                      uint32_t flags, exseq_stats *stats);
 
 }  // namespace exseq

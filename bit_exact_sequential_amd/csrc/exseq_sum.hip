@@ -55,6 +55,7 @@
 #include "exseq.h"
 #include "exseq_internal.h"
 #include "exseq_rules.h"
+#include "exseq_ssim_dev.h"
 #include "exseq_wave.h"
 
 namespace exseq {
@@ -62,11 +63,6 @@ namespace exseq {
 // ---------------------------------------------------------------------------
 // Loads: lane l of a chunk takes terms 4l .. 4l+3; past n a term is absent.
 // ---------------------------------------------------------------------------
-struct Four {
-    double v[4];
-    int cnt;  // how many of the four exist (0..4)
-};
-
 // A value the compiler must treat as opaque.  Picking one of several
 // register values by a run-time index (unrolled selects) is otherwise turned
 // back into an indexed load from a stack copy, i.e. scratch memory.
@@ -129,6 +125,18 @@ __device__ __forceinline__ Four load_four(const double *__restrict__ x, size_t n
     }
     return f;
 }
+
+// Term sources of the exact sum.  chunk() gives lane t its terms 4t .. 4t+3
+// of chunk c of sum s; it is called by every lane of the workgroup with the
+// same chunk.  keep() hands the terms to the caller where it asked for them.
+struct PlainTerms {
+    static constexpr int kLdsInts = 1;
+    __device__ __forceinline__ Four chunk(const BatchArgs &a, int s, size_t c, int *) const
+    {
+        return load_four(a.x[s], a.n[s], c * kChunk + 4 * (size_t)threadIdx.x, true);
+    }
+    __device__ __forceinline__ void keep(size_t, const Four &) const {}
+};
 
 // Fixed-shape tree sum of a chunk: ((v0+v1)+(v2+v3)) per lane, the wave in a
 // fixed order, then the four waves as ((w0+w1)+(w2+w3)).
@@ -737,13 +745,16 @@ __device__ __forceinline__ double resolve_terms(const Four &f, int len, double S
     return S;
 }
 
-// The same for chunk c of a sum, its terms read again from memory.
-__device__ double resolve_chunk(const double *__restrict__ x, size_t n, size_t c, double S,
-                                int pos, WalkLds &sh, int &buf)
+// The same for chunk c of sum s, its terms formed again by the source.
+template <class Src>
+__device__ __forceinline__ double resolve_chunk(const Src &src, const BatchArgs &a, int s,
+                                                size_t c, double S, int pos, WalkLds &sh,
+                                                int &buf, int *lds_src)
 {
+    const size_t n = a.n[s];
     const size_t b = c * kChunk;
     const int len = (int)(n - b < (size_t)kChunk ? n - b : (size_t)kChunk);
-    const Four f = load_four(x, n, b + (size_t)kPer * threadIdx.x, false);
+    const Four f = src.chunk(a, s, c, lds_src);
     return resolve_terms(f, len, S, pos, sh, buf);
 }
 
@@ -1206,12 +1217,13 @@ struct WalkLdsX {
     int unk[kWaves];
 };
 
-__device__ __forceinline__ void chain_walk(const BatchArgs &a, int s, const ChainArea &ch,
-                                           WalkLds &sh, WalkLdsX &wl)
+template <class Src>
+__device__ __forceinline__ void chain_walk(const Src &src, const BatchArgs &a, int s,
+                                           const ChainArea &ch, WalkLds &sh, WalkLdsX &wl,
+                                           int *lds_src)
 {
     __builtin_amdgcn_s_setprio(3);  // the walk is the critical path
     const int t = threadIdx.x, lane = lane_id(), wave = wave_id();
-    const double *__restrict__ x = a.x[s];
     const size_t n = a.n[s];
     const size_t nch = (n + kChunk - 1) / kChunk;
     const uint32_t cpb = a.tile;
@@ -1222,7 +1234,7 @@ __device__ __forceinline__ void chain_walk(const BatchArgs &a, int s, const Chai
     if (nch == 0)
         return;
     const int64_t tlast = (int64_t)((nch - 1) / cpb);
-    double S = resolve_chunk(x, n, 0, a.init[s], 0, sh, buf);
+    double S = resolve_chunk(src, a, s, 0, a.init[s], 0, sh, buf, lds_src);
     wo.fb = 1;
     wo.terms = n < (size_t)kChunk ? n : (size_t)kChunk;
     wo.first = 0;
@@ -1346,10 +1358,8 @@ __device__ __forceinline__ void chain_walk(const BatchArgs &a, int s, const Chai
                         (int)(n - c * kChunk < (size_t)kChunk ? n - c * kChunk : (size_t)kChunk);
                     int pos = 0;
                     const int xr = (cm & kIrrCross) ? crossing_apply(cw + 4, len, kk, S, pos) : 0;
-                    if (xr != 1) {
-                        const Four f = load_four(x, n, c * kChunk + (size_t)kPer * t, false);
-                        S = resolve_terms(f, len, S, xr == 2 ? pos : 0, sh, buf);
-                    }
+                    if (xr != 1)
+                        S = resolve_chunk(src, a, s, c, S, xr == 2 ? pos : 0, sh, buf, lds_src);
                     S = bitsd(uniform_u64(dbits(S)));
                     wo.fb++;
                     wo.terms += (uint64_t)len;
@@ -1404,8 +1414,8 @@ __device__ __forceinline__ int64_t plan_margin(uint32_t chunks_to_end)
     return 4096 + (int64_t)(64.0 * __builtin_sqrt((double)chunks_to_end * (double)kChunk));
 }
 
-template <int CPB>
-__global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a,
+template <int CPB, class Src>
+__global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src src,
                                                              uint64_t *__restrict__ status,
                                                              DescArrays d, ChainArea ch)
 {
@@ -1420,10 +1430,11 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a,
     __shared__ CrossLds xl;
     __shared__ uint64_t lds_x[CPB][kCrossWords];
     __shared__ WalkLdsX wl;
+    __shared__ int lds_src[Src::kLdsInts];
     // With the chain on, the first a.count blocks walk it, one per sum.
     const uint32_t nwalk = chain_on(a.flags) ? (uint32_t)a.count : 0u;
     if (blockIdx.x < nwalk) {
-        chain_walk(a, (int)blockIdx.x, ch, sh, wl);
+        chain_walk(src, a, (int)blockIdx.x, ch, sh, wl, lds_src);
         return;
     }
     // With the chain on, each sum's last tile goes right after the walks:
@@ -1452,7 +1463,6 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a,
     }
     const uint32_t g0 = gt * CPB;  // first global chunk of the tile
     const int s = find_sum(a, g0);
-    const double *__restrict__ x = a.x[s];
     const size_t n = a.n[s];
     const uint32_t c0 = g0 - a.chunk_base[s];  // first local chunk
     const double init = a.init[s];
@@ -1468,8 +1478,10 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a,
 
     Four f[CPB];
 #pragma unroll
-    for (int k = 0; k < CPB; k++)
-        f[k] = load_four(x, n, (size_t)(c0 + k) * kChunk + (size_t)threadIdx.x * 4, true);
+    for (int k = 0; k < CPB; k++) {
+        f[k] = src.chunk(a, s, c0 + k, lds_src);
+        src.keep(c0 + k, f[k]);
+    }
     {
         double ws[CPB];
 #pragma unroll
@@ -1671,7 +1683,7 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a,
         // the register count of all tiles down
         const size_t b = (size_t)(c0 + k) * kChunk;
         const int len = (int)(n - b < (size_t)kChunk ? n - b : (size_t)kChunk);
-        const Four fr = load_four(x, n, b + (size_t)kPer * threadIdx.x, false);
+        const Four fr = src.chunk(a, s, c0 + k, lds_src);
         uint64_t w[kCrossWords];
         if (crossing_find(fr, len, kr, count_of(pr), sh, xl, buf, w)) {
             found |= 1u << k;
@@ -1743,18 +1755,19 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a,
     }
 }
 
-__global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, DescArrays dall,
+template <class Src>
+__global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, Src src, DescArrays dall,
                                                             ChainArea ch,
                                                             double *__restrict__ outs,
                                                             exseq_stats *__restrict__ stats)
 {
     __shared__ WalkLds sh;
+    __shared__ int lds_src[Src::kLdsInts];
     __shared__ unsigned long long st_fb, st_terms;
     __shared__ long long st_first;
     __shared__ unsigned st_nf;
     __shared__ long long st_best[kWaves];
     const int s = blockIdx.x;
-    const double *__restrict__ x = a.x[s];
     const size_t n = a.n[s];
     const size_t nch = (n + kChunk - 1) / kChunk;
     const size_t cb = a.chunk_base[s];
@@ -2034,7 +2047,7 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, DescArr
             } else {
                 misses += fc.ok2 == 2;
                 const size_t c = base + (size_t)fc.idx;
-                S = resolve_chunk(x, n, c, fc.s_at, 0, sh, buf);
+                S = resolve_chunk(src, a, s, c, fc.s_at, 0, sh, buf, lds_src);
                 n_fb++;
                 fb_terms += (n - c * kChunk < (size_t)kChunk) ? n - c * kChunk : (size_t)kChunk;
                 if (first_fb < 0)
@@ -2168,8 +2181,8 @@ size_t sum_ws_bytes(size_t total_chunks)
            round256(4 * kMaxBatch * sizeof(uint64_t));
 }
 
-template <int CPB>
-static void launch_tiles(const BatchArgs &args, uint32_t total, const WsParts &p,
+template <int CPB, class Src>
+static void launch_tiles(const BatchArgs &args, const Src &src, uint32_t total, const WsParts &p,
                          hipStream_t stream)
 {
     const unsigned tiles = total / CPB;
@@ -2177,12 +2190,14 @@ static void launch_tiles(const BatchArgs &args, uint32_t total, const WsParts &p
     const unsigned blocks =
         chain ? (unsigned)args.count * 2u + args.rest_base[args.count] : tiles;
     if (tiles)
-        hipLaunchKernelGGL(tile_kernel<CPB>, dim3(blocks), dim3(kChunkThreads), 0, stream, args,
-                           p.status, p.d, p.ch);
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(tile_kernel<CPB, Src>), dim3(blocks),
+                           dim3(kChunkThreads), 0, stream, args, src, p.status, p.d, p.ch);
 }
 
-int launch_batch(const BatchArgs &a, void *ws, double *outs, hipStream_t stream,
-                 exseq_stats *stats, void *const *events, int n_events)
+template <class Src>
+static int launch_batch_src(const BatchArgs &a, const Src &src, void *ws, double *outs,
+                            hipStream_t stream, exseq_stats *stats, void *const *events,
+                            int n_events)
 {
     auto mark = [&](int i) {
         if (events && i < n_events && events[i])
@@ -2209,17 +2224,38 @@ int launch_batch(const BatchArgs &a, void *ws, double *outs, hipStream_t stream,
     mark(1);
     mark(2);
     if (args.tile == 1)
-        launch_tiles<1>(args, total, p, stream);
+        launch_tiles<1>(args, src, total, p, stream);
     else if (args.tile == 2)
-        launch_tiles<2>(args, total, p, stream);
+        launch_tiles<2>(args, src, total, p, stream);
     else
-        launch_tiles<4>(args, total, p, stream);
+        launch_tiles<4>(args, src, total, p, stream);
     mark(3);
     mark(4);
-    hipLaunchKernelGGL(walk_kernel, dim3((unsigned)a.count), dim3(kWalkThreads), 0, stream, args,
-                       p.d, p.ch, outs, stats);
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(walk_kernel<Src>), dim3((unsigned)a.count),
+                       dim3(kWalkThreads), 0, stream, args, src, p.d, p.ch, outs, stats);
     mark(5);
     return hipGetLastError() == hipSuccess ? EXSEQ_OK : EXSEQ_EHIP;
+}
+
+int launch_batch(const BatchArgs &a, void *ws, double *outs, hipStream_t stream,
+                 exseq_stats *stats, void *const *events, int n_events)
+{
+    return launch_batch_src(a, PlainTerms{}, ws, outs, stream, stats, events, n_events);
+}
+
+int launch_ssim_exact(const SsimParams &sp, double *out, void *ws, hipStream_t stream,
+                      uint32_t flags, exseq_stats *stats)
+{
+    const size_t n = (size_t)sp.width * (size_t)sp.height;
+    BatchArgs a{};
+    a.count = 1;
+    a.flags = flags;
+    a.x[0] = nullptr;
+    a.n[0] = n;
+    a.init[0] = 0.0;
+    a.chunk_base[0] = 0;
+    a.chunk_base[1] = (uint32_t)padded_chunks(n);
+    return launch_batch_src(a, SsimTerms{sp}, ws, out, stream, stats, nullptr, 0);
 }
 
 int launch_exact_sum(const double *x, size_t n, double init, double *out, void *ws,

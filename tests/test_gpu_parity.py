@@ -241,6 +241,29 @@ def test_ssim_full_frame():
     assert int(gw.cpu()[0]) == wsum
 
 
+@pytest.mark.parametrize("flags", [ex.WALK_ONLY, ex.CHAIN_CUT, ex.PLAN_ALL_FALLBACK,
+                                   ex.tile_flag(1), ex.tile_flag(2) | ex.CHAIN_CUT])
+def test_ssim_fused_paths(flags):
+    """The fused term source under every walk: the terms the tiles form and
+    the ones the walk forms again for chunks it adds term by term give the
+    oracle's sum (radius 5, a frame whose rows are not a multiple of a
+    chunk, plane rows padded)."""
+    torch = torch_cuda()
+    h, w = 211, 373
+    ref, dis = si.frame_pair(h, w, 77)
+    s, wsum, _ = oracle.ssim_frame_sum(ref, dis, 5)
+    big_r = np.zeros((h, 400), np.uint8)
+    big_d = np.zeros((h, 400), np.uint8)
+    big_r[:, :w] = ref
+    big_d[:, :w] = dis
+    r = torch.from_numpy(big_r).cuda()[:, :w]
+    d = torch.from_numpy(big_d).cuda()[:, :w]
+    gs, gw, _, st = ex.ssim_term_and_sum(r, d, 5, flags=flags, stats=True)
+    assert same(float(gs.cpu()[0]), s), flags
+    assert int(gw.cpu()[0]) == wsum
+    assert st["fast_chunks"] + st["fallback_chunks"] == st["chunks"]
+
+
 def test_ssim_term_divide_against_host():
     """The device divide and term equal the host's on many random windows,
     including wide int64 moments where products round (stride > width)."""
