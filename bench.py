@@ -11,8 +11,10 @@ used in rotation so that every step reads its terms from HBM.
 
 Prints ONE JSON line with the whole-job throughput (terms/s), the roofline
 of the dominant kernel (per-kernel device time measured live with HIP events
-recorded by the library around each kernel), and the oracle timed on the
-host as the CPU baseline.
+recorded by the library around each kernel), the oracle timed on the host as
+the CPU baseline, and the device time of the other workloads (the uniform
+4096-term sum, the signed 1920x1080 sum, the fused SSIM frame and the
+108-sum pyramid batch) under "other_configs".
 """
 
 from __future__ import annotations
@@ -46,6 +48,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bound on the oracle timing (cpu_baseline)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing the other configurations")
     ap.add_argument("--copy-ref", action="store_true",
                     help="also run plain copies of known size (PMC scale reference)")
     return ap.parse_args()
@@ -81,6 +85,69 @@ class Hip:
 
     def destroy(self, e):
         self.L.hipEventDestroy(e)
+
+
+def time_configs(ex, si, torch, dev, seed, reps=30):
+    """Device time per call of the other workloads (torch events on the
+    library's stream, after a warm-up call).  Sizes: the uniform 4096-term
+    sum, the signed 1920x1080 sum, the fused SSIM sum of two 3840x2160
+    planes (radius 3), and the 108-sum pyramid batch (6 scales x 3 channels x
+    6 sums, 199,018,080 terms)."""
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    res = {}
+    x1 = torch.from_numpy(si.uniform(4096, seed)).to(dev)
+    o1 = torch.empty(1, dtype=torch.float64, device=dev)
+    w1 = ex.workspace(ex.lib().exact_seq_sum_f64_workspace_size(4096), dev)
+    ms = timed(lambda: ex.exact_seq_sum(x1, out=o1, ws=w1), reps)
+    res["uniform_4096"] = {"us_per_sum": ms * 1e3, "terms_per_s": 4096 / (ms * 1e-3)}
+
+    n3 = si.HALF_N
+    x3 = [torch.from_numpy(si.signed_terms(n3, seed + b)).to(dev) for b in range(4)]
+    o3 = torch.empty(1, dtype=torch.float64, device=dev)
+    w3 = ex.workspace(ex.lib().exact_seq_sum_f64_workspace_size(n3), dev)
+    k = [0]
+
+    def sig():
+        ex.exact_seq_sum(x3[k[0] % 4], out=o3, ws=w3)
+        k[0] += 1
+    ms = timed(sig, reps)
+    res["signed_1920x1080"] = {"us_per_sum": ms * 1e3, "terms_per_s": n3 / (ms * 1e-3),
+                               "gbs": n3 * 8 / (ms * 1e-3) / 1e9,
+                               "buffers_rotated": 4}
+
+    ref, dis = si.frame_pair(si.FRAME_H, si.FRAME_W, seed)
+    r4 = torch.from_numpy(ref).to(dev)
+    d4 = torch.from_numpy(dis).to(dev)
+    w4 = ex.workspace(ex.lib().ssim_term_and_sum_workspace_size(si.FRAME_W, si.FRAME_H), dev)
+    ms = timed(lambda: ex.ssim_term_and_sum(r4, d4, 3, ws=w4), reps)
+    res["fused_ssim_3840x2160"] = {"us_per_frame": ms * 1e3,
+                                   "pixels_per_s": si.FRAME_N / (ms * 1e-3),
+                                   "plane_gbs": 2 * si.FRAME_N / (ms * 1e-3) / 1e9}
+
+    xs = [torch.from_numpy(a).to(dev) for a in si.pyramid(seed)]
+    total = sum(int(x.numel()) for x in xs)
+    ns = [int(x.numel()) for x in xs]
+    import ctypes
+    nsa = (ctypes.c_size_t * len(ns))(*ns)
+    w5 = ex.workspace(ex.lib().exact_seq_sum_f64_batch_workspace_size(nsa, len(ns)), dev)
+    o5 = torch.empty(len(xs), dtype=torch.float64, device=dev)
+    ms = timed(lambda: ex.exact_seq_sum_batch(xs, out=o5, ws=w5), max(3, reps // 3))
+    res["pyramid_batch_108"] = {"us_per_batch": ms * 1e3, "sums": len(xs), "terms": total,
+                                "terms_per_s": total / (ms * 1e-3),
+                                "gbs": total * 8 / (ms * 1e-3) / 1e9}
+    del xs
+    return res
 
 
 def main():
@@ -202,6 +269,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    # ---- the other configurations (throughput only; parity is in the tests)
+    others = {} if args.no_configs else time_configs(ex, si, torch, dev, args.seed)
+
     # ---- cpu_baseline: the oracle on the host, bounded ----------------------
     cpu = None
     parity = None
@@ -258,6 +328,7 @@ def main():
         "tree_sum": {"ms_per_step": tree_ms, "value": tree0, "exact": exact0,
                      "gap": tree0 - exact0},
         "host_wall_ms_per_step": wall * 1e3 / args.steps,
+        "other_configs": others,
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,
     }
