@@ -80,15 +80,11 @@ struct DescArrays {
 
 // The exact chain between the tiles of a sum (zeroed before every launch;
 // a published word is never zero).  Per tile: four words describing it (agg:
-// meta, r0, lo, hi of the composition of its chunks, or "irregular"), the
-// exact running sum after it (incl, irregular tiles only) and, for an
-// irregular tile, the words the walk of the chain needs (irr); wstat holds
-// per sum what the walk of the chain added term by term.
+// meta, r0, lo, hi of the composition of its chunks, or "irregular") and the
+// exact running sum after it (incl, irregular tiles only).
 struct ChainArea {
     uint64_t *agg;
     uint64_t *incl;
-    uint64_t *irr;
-    uint64_t *wstat;
 };
 
 // Workspace of a launch over `total_chunks` chunks: plan status words, the

@@ -303,50 +303,53 @@ __device__ __forceinline__ WaveRun wave_run(const Four &f, uint32_t key)
 }
 
 // The runs of CPB chunks at once (one wave's part of each, as wave_run).
-// Where no term of the wave ties and none is negative under its chunk's key
-// -- nearly always -- the CPB order-free integer sums are taken together so
-// that their reduction chains overlap; otherwise chunk by chunk.
+// Where no term of the wave ties and every scaled term is in [0, 2^51) --
+// nearly always -- the CPB order-free integer sums are taken together so
+// that their reduction chains overlap; otherwise chunk by chunk.  Missing
+// terms are +0.0 (the sources pad with it), which changes no run.
 template <int CPB>
 __device__ __forceinline__ void wave_runs(const Four *f, const uint32_t *key,
                                           WaveRun (*lds)[kChunkThreads / 64])
 {
-    int64_t v[CPB];
-    uint32_t fl[CPB];
+    uint64_t v[CPB];
     bool easy = true;
 #pragma unroll
     for (int k = 0; k < CPB; k++) {
         const int scale = 1075 - (int)(key[k] & 0x7FFu);
-        const bool sgn = (key[k] >> 11) & 1u;
-        bool neg = false, bad = false, nonfin = false, tie = false;
-        int64_t sum = 0;
+        const uint32_t flip = (key[k] & 0x800u) ? 0x80000000u : 0u;  // mirror a negative plan
+        bool odd = false;
+        uint64_t sum = 0;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            if (i < f[k].cnt) {
-                const TermInc ti = term_inc(f[k].v[i], scale, sgn);
-                sum += ti.r0;
-                neg |= ti.neg;
-                bad |= ti.bad;
-                nonfin |= is_nonfinite(f[k].v[i]);
-                tie |= ti.r0 != ti.r1;
-            }
+            double y = ldexp(f[k].v[i], scale);
+            y = bitsd(dbits(y) ^ ((uint64_t)flip << 32));
+            const double a0 = kMagic0 + y;
+            const double a1 = kMagic1 + y;
+            // 0 <= y < 2^51 as one unsigned compare of the bit patterns
+            // (a negative y, -0.0 and NaN have larger patterns)
+            odd |= dbits(y) >= (uint64_t)dbits(kHugeY);
+            // a tie: the two starts round to counts that differ by other
+            // than one (both sums lie in [2^52, 2^53), so the low words do)
+            odd |= (uint32_t)dbits(a1) - (uint32_t)dbits(a0) != 1u;
+            sum += dbits(a0);
         }
-        v[k] = sum;
-        const bool wtie = __ballot(tie) != 0;
-        const bool wneg = __ballot(neg) != 0;
-        fl[k] = (wneg ? kFlagNeg : 0u) | (__ballot(bad) ? kFlagBad : 0u) |
-                (__ballot(nonfin) ? kFlagNonFinite : 0u);
-        easy &= !wtie && !wneg;
+        v[k] = sum - 4 * (uint64_t)kMagic0Bits;
+        easy &= __ballot(odd) == 0;
     }
     if (easy) {
-        wave_sum_i64_n<CPB>(v);
+        int64_t w[CPB];
+#pragma unroll
+        for (int k = 0; k < CPB; k++)
+            w[k] = (int64_t)v[k];
+        wave_sum_i64_n<CPB>(w);
         if (lane_id() == 0) {
 #pragma unroll
             for (int k = 0; k < CPB; k++) {
-                WaveRun w;
-                w.p = Pair{v[k], v[k]};
-                w.lo = w.hi = 0;
-                w.flags = fl[k];
-                lds[k][wave_id()] = w;
+                WaveRun r;
+                r.p = Pair{w[k], w[k]};
+                r.lo = r.hi = 0;
+                r.flags = 0u;
+                lds[k][wave_id()] = r;
             }
         }
         return;
@@ -964,23 +967,23 @@ __device__ __forceinline__ int chain_back(const ChainArea &ch, uint32_t tb, uint
 // ---------------------------------------------------------------------------
 // Crossings, located by the tile.  For a chunk whose plan expects the running
 // sum to cross from its binade into the next one up, the tile forms the
-// increment pair of every prefix of the chunk under both binades and finds,
-// from the planned start count, the term that crosses.  It publishes only
-// that term and the prefixes around it (pairs packed as r0 << 2 |
-// (r1 - r0 + 1)).  Given the exact start count m, the walk checks in O(1)
-// that the crossing is still at that term -- the count before it below 2^53,
-// the count through it at least 2^53; the plan is off by far fewer counts
-// than one term moves the count, so it nearly always is -- adds the term
-// with one fp64 add and takes the rest of the chunk from the second binade's
-// prefixes.  Only chunks with no negative scaled term and nothing bad under
-// either binade get a crossing.
+// increment pair of every prefix of the chunk under the planned binade and
+// finds, from the planned start count, the term that crosses.  It publishes
+// that term, the prefix pairs just before it and through it, and under the
+// next binade the pair of the terms after it and of the whole chunk (pairs
+// packed as r0 << 2 | (r1 - r0 + 1)).  Given the exact start count m, the
+// chain checks in O(1) that the crossing is still at that term -- the count
+// before it below 2^53, the count through it at least 2^53; the plan is off
+// by far fewer counts than one term moves the count, so it nearly always is
+// -- adds the term with one fp64 add and applies the pair of the rest from
+// the count the add gave (Research-1433 Findings 4: non-negative increments
+// keep every intermediate count below the final one, so the final count
+// alone shows that no second crossing happened).  Only chunks with no
+// negative scaled term and nothing bad under either binade get a crossing.
 // ---------------------------------------------------------------------------
-constexpr int64_t kRecMax = (int64_t)1 << 56;  // larger prefixes are clamped (never apply)
-
 __device__ __forceinline__ int64_t rec_pack(Pair p)
 {
-    const int64_t r0 = p.r0 < kRecMax ? p.r0 : kRecMax;
-    return (r0 << 2) | (p.r1 - p.r0 + 1);
+    return p.r0 * 4 + (p.r1 - p.r0 + 1);
 }
 __device__ __forceinline__ Pair rec_unpack(int64_t v)
 {
@@ -1028,17 +1031,19 @@ __device__ __forceinline__ Pair block_scan_total(Pair v, WalkLds &sh, int buf, P
 }
 
 // A crossing as published: the crossing term's index j, the packed prefix
-// pairs through j - 1 and through j under the planned binade, through j
-// under the next one, the whole chunk under the next one, and the term.
+// pairs through j - 1 and through j under the planned binade, the packed
+// pairs of the terms after j and of the whole chunk under the next one, and
+// the term.
 constexpr int kCrossWords = 6;
 struct CrossCand {
     int j;
-    int64_t pj1, pj, p2j;
+    int64_t pj1, pj;
     double xj;
 };
 struct CrossLds {
     CrossCand c[kWaves];
     int bad[kWaves];
+    Pair tot2[kWaves], suf2[kWaves];
 };
 
 // Locates the crossing of a chunk (terms f, len of them, planned binade
@@ -1049,12 +1054,9 @@ __device__ __forceinline__ bool crossing_find(const Four &f, int len, uint32_t k
                                               WalkLds &sh, CrossLds &xl, int &buf, uint64_t *out)
 {
     const int t = threadIdx.x, lane = lane_id(), wave = wave_id();
-    Pair acc[kPer], acc2[kPer], tot, tot2;
+    Pair acc[kPer], tot;
     const bool bad1 = lane_prefixes(f, key, acc);
-    const bool bad2 = lane_prefixes(f, key + 1u, acc2);
     const Pair pre = block_scan_total(acc[kPer - 1], sh, buf, tot);
-    buf ^= 1;
-    const Pair pre2 = block_scan_total(acc2[kPer - 1], sh, buf, tot2);
     buf ^= 1;
     // the first term whose count from m_est reaches 2^53 (counts only grow)
     int firstk = -1;
@@ -1064,27 +1066,25 @@ __device__ __forceinline__ bool crossing_find(const Four &f, int len, uint32_t k
         if (kPer * t + i < len && m_est + pair_at(pe, m_est) >= kCountHi)
             firstk = i;
     }
-    const uint64_t b = __ballot(firstk >= 0), bb = __ballot(bad1 || bad2);
+    const uint64_t b = __ballot(firstk >= 0), bb = __ballot(bad1);
     if (lane == (b ? (int)__builtin_ctzll(b) : 0)) {
         CrossCand c;
         c.j = kNone;
-        c.pj1 = c.pj = c.p2j = 0;
+        c.pj1 = c.pj = 0;
         c.xj = 0.0;
         if (b) {
-            Pair before = pre, at = acc[0], at2 = acc2[0];
+            Pair before = pre, at = acc[0];
             double x = opaque(f.v[0]);
 #pragma unroll
             for (int i = 1; i < kPer; i++)
                 if (i == firstk) {
                     before = Pair{opaque(acc[i - 1].r0), opaque(acc[i - 1].r1)};
                     at = Pair{opaque(acc[i].r0), opaque(acc[i].r1)};
-                    at2 = Pair{opaque(acc2[i].r0), opaque(acc2[i].r1)};
                     x = opaque(f.v[i]);
                 }
             c.j = kPer * t + firstk;
             c.pj1 = rec_pack(firstk == 0 ? pre : compose(pre, before));
             c.pj = rec_pack(compose(pre, at));
-            c.p2j = rec_pack(compose(pre2, at2));
             c.xj = x;
         }
         xl.c[wave] = c;
@@ -1102,35 +1102,71 @@ __device__ __forceinline__ bool crossing_find(const Four &f, int len, uint32_t k
     const CrossCand c = xl.c[bw];
     if (bad || c.j == kNone)
         return false;
+    // Under the next binade: the whole chunk, and the terms after j.
+    const uint32_t key2 = key + 1u;
+    const int scale2 = 1075 - (int)(key2 & 0x7FFu);
+    const bool sgn2 = (key2 >> 11) & 1u;
+    bool bad2 = false;
+    Pair whole = pair_identity(), suf = pair_identity();
+#pragma unroll
+    for (int i = 0; i < kPer; i++) {
+        if (i < f.cnt) {
+            const TermInc ti = term_inc(f.v[i], scale2, sgn2);
+            bad2 |= ti.bad || ti.neg;
+            const Pair q{ti.r0, ti.r1};
+            whole = compose(whole, q);
+            if (kPer * t + i > c.j)
+                suf = compose(suf, q);
+        }
+    }
+    whole = wave_reduce_pair(whole);
+    suf = wave_reduce_pair(suf);
+    const uint64_t bb2 = __ballot(bad2);
+    if (lane == 0) {
+        xl.tot2[wave] = whole;
+        xl.suf2[wave] = suf;
+        xl.bad[wave] = bb2 != 0;
+    }
+    __syncthreads();
+    Pair tot2 = pair_identity(), suf2 = pair_identity();
+#pragma unroll
+    for (int k = 0; k < kWaves; k++) {
+        bad2 |= xl.bad[k] != 0;
+        tot2 = compose(tot2, xl.tot2[k]);
+        suf2 = compose(suf2, xl.suf2[k]);
+    }
+    if (bad2)
+        return false;
     out[0] = enc_i64(c.j);
     out[1] = enc_i64(c.pj1);
     out[2] = enc_i64(c.pj);
-    out[3] = enc_i64(c.p2j);
+    out[3] = enc_i64(rec_pack(suf2));
     out[4] = enc_i64(rec_pack(tot2));
     out[5] = dbits(c.xj) ^ kInclXor;  // a crossing term is finite: never kInclXor
     return true;
 }
 
-// The walk's side: from the exact sum S before a chunk (len terms, planned
-// binade key) with a published crossing w[0..5].  Returns 1 with S the sum
+// The chain's side: from the exact sum S before a chunk (len terms, planned
+// binade key) with a located crossing w[0..5].  Returns 1 with S the sum
 // after the chunk, 2 with S the exact sum after the crossing term and pos
 // the next term (the rest term by term), or 0 if the crossing does not hold
-// for this S (the whole chunk term by term).
+// for this S (the whole chunk term by term).  The pairs w[3] and w[4] may
+// also take in runs that follow the chunk in the next binade: every success
+// applies one of them.
 __device__ __forceinline__ int crossing_apply(const uint64_t *w, int len, uint32_t key, double &S,
                                               int &pos)
 {
     const uint32_t ks = key_of(S);
     const int64_t m = count_of(S);
-    const Pair last2 = rec_unpack(dec_i64(w[4]));
     if (ks == key + 1u) {
         // the crossing came before the chunk: all of it in the next binade
-        const int64_t e = m + pair_at(last2, m);
-        if (e > kCountHi)
+        const int64_t e = m + pair_at(rec_unpack(dec_i64(w[4])), m);
+        if (!key_has_fast_path(ks) || e > kCountHi)
             return 0;
         S = assemble(ks, e);
         return 1;
     }
-    if (ks != key)
+    if (ks != key || !key_has_fast_path(ks))
         return 0;
     const int j = (int)dec_i64(w[0]);
     const int64_t cb = j == 0 ? m : m + pair_at(rec_unpack(dec_i64(w[1])), m);
@@ -1140,245 +1176,15 @@ __device__ __forceinline__ int crossing_apply(const uint64_t *w, int len, uint32
     const double sb = j == 0 ? S : assemble(key, cb);
     S = sb + bitsd(w[5] ^ kInclXor);  // the one plain add
     pos = j + 1;
-    if (pos == len)
-        return 1;
     const uint32_t k2 = key_of(S);
     const int64_t m2 = count_of(S);
-    const Pair at = rec_unpack(dec_i64(w[3]));
-    int p = -1;
-    if ((at.r0 & 1) == (m2 & 1))
-        p = 0;
-    else if (((1 + at.r1) & 1) == (m2 & 1))
-        p = 1;
-    if (k2 != key + 1u || !key_has_fast_path(k2) || p < 0)
+    if (k2 != key + 1u || !key_has_fast_path(k2))
         return 2;
-    const int64_t e = m2 + ((p ? last2.r1 : last2.r0) - (p ? at.r1 : at.r0));
+    const int64_t e = m2 + pair_at(rec_unpack(dec_i64(w[3])), m2);
     if (e > kCountHi)
         return 2;  // a second crossing
     S = assemble(k2, e);
     return 1;
-}
-
-// ---------------------------------------------------------------------------
-// The walk of the chain.  Irregular tiles do not wait for each other.  Each
-// one writes a block of words at its own index: the index of the nearest
-// irregular tile before it, the composed run of the regular tiles in between
-// (R), and its chunks' runs, each with its located crossing, if any.  One
-// workgroup per sum (the first blocks of the tile launch, so resident from
-// the start) walks the chain: it adds the sum's first chunk from init before
-// anything is published; then, a window of 1024 tiles at a time, one round
-// trip to memory tells it which tiles are irregular (the first word of every
-// tile's agg words), and one more brings the blocks of up to five of them.
-// For each irregular tile in order it applies R, then each chunk's run, its
-// crossing or its terms one by one, and writes the exact sum after the tile
-// to incl, while the tiles behind it still stream.
-// ---------------------------------------------------------------------------
-constexpr int kIrrTile = 4;    // 2 + index of the irregular tile before (1: none)
-constexpr int kIrrInfo = 5;    // present | chunks
-constexpr int kIrrChunk = 6;   // chunk k at 6 + 10k: meta, r0, lo, hi, crossing[6]
-constexpr int kIrrPer = 4 + kCrossWords;
-constexpr int kIrrWords = kIrrChunk + kIrrPer * kTileMax;
-constexpr uint64_t kIrrEmpty = 1ULL << 61;   // R: no regular tile in between
-constexpr uint64_t kIrrFailed = 1ULL << 60;  // R: the look-back failed
-constexpr uint64_t kIrrCross = 1ULL << 40;   // chunk meta: a crossing is published
-static_assert(kIrrWords <= kChunkThreads, "one lane per word");
-
-// The walk stops (and the walk kernel resumes) where a wait times out.
-__device__ __forceinline__ uint64_t spin_load(const uint64_t *p)
-{
-    uint64_t w = load_relaxed_u64(p);
-    for (int spin = 0; w == 0 && spin <= kSpinLimit; spin++) {
-        __builtin_amdgcn_s_sleep(2);
-        w = load_relaxed_u64(p);
-    }
-    return w;
-}
-
-struct WalkOut {
-    uint64_t fb, terms;
-    int64_t first;
-};
-
-constexpr int kWalkBatch = kChunkThreads / kIrrWords;  // blocks per round trip
-
-// A value known to be the same in every lane, moved to scalar registers so
-// that the walk's bookkeeping on it runs on the scalar unit.
-__device__ __forceinline__ uint64_t uniform_u64(uint64_t v)
-{
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
-    return ((uint64_t)hi << 32) | lo;
-}
-
-struct WalkLdsX {
-    uint64_t words[kWalkBatch][kIrrWords];
-    int queue[kBackPer * kChunkThreads];  // irregular tiles found, in order
-    int cnt[kWaves];
-    int unk[kWaves];
-};
-
-template <class Src>
-__device__ __forceinline__ void chain_walk(const Src &src, const BatchArgs &a, int s,
-                                           const ChainArea &ch, WalkLds &sh, WalkLdsX &wl,
-                                           int *lds_src)
-{
-    __builtin_amdgcn_s_setprio(3);  // the walk is the critical path
-    const int t = threadIdx.x, lane = lane_id(), wave = wave_id();
-    const size_t n = a.n[s];
-    const size_t nch = (n + kChunk - 1) / kChunk;
-    const uint32_t cpb = a.tile;
-    const size_t tb = a.chunk_base[s] / cpb;
-    const int nw = kIrrChunk + kIrrPer * (int)cpb;
-    WalkOut wo{0, 0, -1};
-    int buf = 0;
-    if (nch == 0)
-        return;
-    const int64_t tlast = (int64_t)((nch - 1) / cpb);
-    double S = resolve_chunk(src, a, s, 0, a.init[s], 0, sh, buf, lds_src);
-    wo.fb = 1;
-    wo.terms = n < (size_t)kChunk ? n : (size_t)kChunk;
-    wo.first = 0;
-    int64_t cur = -1;   // the last irregular tile walked
-    int64_t scan = 0;   // tiles before this one are known to be regular or queued
-    bool ok = true;
-    for (int idle = 0; ok && cur != tlast && idle <= kSpinLimit;) {
-        // ---- which tiles of the next window are irregular
-        uint64_t m[kBackPer];
-#pragma unroll
-        for (int i = 0; i < kBackPer; i++) {
-            const int64_t j = scan + kBackPer * t + i;
-            m[i] = j <= tlast ? load_relaxed_u64(ch.agg + 4 * ((size_t)tb + (size_t)j)) : kAggPresent;
-        }
-        int unk = kBackPer * kChunkThreads, cnt = 0;
-#pragma unroll
-        for (int i = kBackPer - 1; i >= 0; i--) {
-            const int64_t j = scan + kBackPer * t + i;
-            if (j <= tlast && m[i] == 0)
-                unk = kBackPer * t + i;
-        }
-        // the window ends at the first tile not yet published
-        const uint64_t bu = __ballot(unk < kBackPer * kChunkThreads);
-        if (lane == 0)
-            wl.unk[wave] = bu ? __builtin_amdgcn_readlane(unk, (int)__builtin_ctzll(bu))
-                              : kBackPer * kChunkThreads;
-        __syncthreads();
-        int end = kBackPer * kChunkThreads;
-#pragma unroll
-        for (int k = 0; k < kWaves; k++)
-            end = wl.unk[k] < end ? wl.unk[k] : end;
-        // the irregular tiles before it, in order, into the queue
-#pragma unroll
-        for (int i = 0; i < kBackPer; i++) {
-            const int64_t j = scan + kBackPer * t + i;
-            cnt += j <= tlast && kBackPer * t + i < end && !(m[i] & kAggRegular);
-        }
-        const int64_t incl = wave_incl_scan_i64(cnt);
-        if (lane == 63)
-            wl.cnt[wave] = (int)incl;
-        __syncthreads();
-        int before = 0, total = 0;
-#pragma unroll
-        for (int k = 0; k < kWaves; k++) {
-            before += k < wave ? wl.cnt[k] : 0;
-            total += wl.cnt[k];
-        }
-        int qi = before + (int)incl - cnt;
-#pragma unroll
-        for (int i = 0; i < kBackPer; i++) {
-            const int64_t j = scan + kBackPer * t + i;
-            if (j <= tlast && kBackPer * t + i < end && !(m[i] & kAggRegular))
-                wl.queue[qi++] = (int)j;
-        }
-        __syncthreads();
-        scan += end;
-        if (total == 0) {
-            idle++;
-            __builtin_amdgcn_s_sleep(2);
-            continue;
-        }
-        idle = 0;
-        // ---- their blocks, kWalkBatch per round trip
-        for (int q0 = 0; ok && q0 < total; q0 += kWalkBatch) {
-            const int qb = t / kIrrWords, qw = t % kIrrWords;
-            const int nq = total - q0 < kWalkBatch ? total - q0 : kWalkBatch;
-            if (qb < nq && qw < nw)
-                wl.words[qb][qw] = spin_load(ch.irr + (size_t)kIrrWords * (tb + (size_t)wl.queue[q0 + qb]) + qw);
-            __syncthreads();
-            for (int q = 0; q < nq; q++) {
-                const uint64_t *words = wl.words[q];
-                const int64_t X = wl.queue[q0 + q];
-                // the head words at once (one LDS latency, not one per word)
-                uint64_t hw[kIrrChunk];
-#pragma unroll
-                for (int i = 0; i < kIrrChunk; i++)
-                    hw[i] = uniform_u64(words[i]);
-                S = bitsd(uniform_u64(dbits(S)));
-                const uint64_t xw = hw[kIrrTile], info = hw[kIrrInfo], rm = hw[0];
-                if (!(info & kAggPresent) || !(rm & kAggPresent) || (rm & kIrrFailed) ||
-                    (int64_t)xw - 2 != cur) {
-                    ok = false;
-                    break;
-                }
-                // R: the regular tiles since tile cur
-                if (!(rm & kIrrEmpty)) {
-                    const uint32_t rkey = (uint32_t)rm & kKeyMask;
-                    const int64_t r0 = dec_i64(hw[1]);
-                    const Pair p{r0, r0 + (int64_t)((rm >> kDrShift) & 3u) - 1};
-                    const uint32_t ks = key_of(S);
-                    const int64_t mm = count_of(S);
-                    if (ks != rkey || !key_has_fast_path(ks) ||
-                        !run_applies(mm, p, dec_i64(hw[2]), dec_i64(hw[3]),
-                                     (uint32_t)rm & (kFlagNeg | kFlagBad | kFlagNonFinite))) {
-                        ok = false;
-                        break;
-                    }
-                    S = assemble(ks, mm + pair_at(p, mm));
-                }
-                const int nk = (int)(info & 15u);
-                const size_t cX = (size_t)X * cpb;  // first local chunk of X
-                for (int k = X == 0 ? 1 : 0; k < nk; k++) {
-                    uint64_t cw[kIrrPer];  // the chunk's words at once
-#pragma unroll
-                    for (int i = 0; i < kIrrPer; i++)
-                        cw[i] = uniform_u64(words[kIrrChunk + kIrrPer * k + i]);
-                    const uint64_t cm = cw[0];
-                    const uint32_t kk = (uint32_t)cm & kKeyMask;
-                    const uint32_t fl = (uint32_t)cm & (kFlagNeg | kFlagBad | kFlagNonFinite);
-                    const int64_t r0 = dec_i64(cw[1]);
-                    const Pair p{r0, r0 + (int64_t)((cm >> kDrShift) & 3u) - 1};
-                    const uint32_t ks = key_of(S);
-                    const int64_t mm = count_of(S);
-                    if (key_has_fast_path(ks) && ks == kk &&
-                        run_applies(mm, p, dec_i64(cw[2]), dec_i64(cw[3]), fl)) {
-                        S = assemble(ks, mm + pair_at(p, mm));
-                        continue;
-                    }
-                    const size_t c = cX + (size_t)k;
-                    const int len =
-                        (int)(n - c * kChunk < (size_t)kChunk ? n - c * kChunk : (size_t)kChunk);
-                    int pos = 0;
-                    const int xr = (cm & kIrrCross) ? crossing_apply(cw + 4, len, kk, S, pos) : 0;
-                    if (xr != 1)
-                        S = resolve_chunk(src, a, s, c, S, xr == 2 ? pos : 0, sh, buf, lds_src);
-                    S = bitsd(uniform_u64(dbits(S)));
-                    wo.fb++;
-                    wo.terms += (uint64_t)len;
-                    if (wo.first < 0)
-                        wo.first = (int64_t)c;
-                }
-                if (t == 0)
-                    ch.incl[tb + (size_t)X] = enc_sum(S);
-                cur = X;
-            }
-            __syncthreads();  // wl.words is read
-        }
-    }
-    if (t == 0) {
-        ch.wstat[4 * s + 0] = wo.fb;
-        ch.wstat[4 * s + 1] = wo.terms;
-        ch.wstat[4 * s + 2] = (uint64_t)(wo.first + 1);
-        ch.wstat[4 * s + 3] = 1;
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1414,34 +1220,49 @@ __device__ __forceinline__ int64_t plan_margin(uint32_t chunks_to_end)
     return 4096 + (int64_t)(64.0 * __builtin_sqrt((double)chunks_to_end * (double)kChunk));
 }
 
+// A value known to be the same in every lane, moved to scalar registers so
+// that the chain's arithmetic on it runs on the scalar unit.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+constexpr int kIrrPer = 4 + kCrossWords;       // bank words per chunk
+constexpr uint64_t kIrrCross = 1ULL << 40;     // bank meta: a crossing is located
+static_assert(4 + kIrrPer * kTileMax <= 64, "the bank fits one wave");
+
+// What the waves of a tile hand each other.
+template <int CPB>
+struct TileLds {
+    double wsum[CPB][kWaves];    // per-wave fixed-tree chunk sums
+    WaveRun wrun[CPB][kWaves];   // per-wave parts of the chunk runs
+    WaveRun join[CPB];           // the chunk runs
+    double pk[CPB];              // planned prefix before each chunk
+    uint32_t key[CPB];           // planned binade of each chunk (0: none)
+    uint32_t cross[CPB];         // the plan does not keep the chunk in its binade
+    uint64_t xw[CPB][kCrossWords];  // located crossings
+    uint64_t word;               // a word read by one lane for all
+};
+
+// One workgroup per tile of CPB consecutive chunks of one sum.  With the
+// chain on, each sum's last tile comes first (blocks 0 .. count-1): started
+// early, it has composed the tiles before it by the time they are done, and
+// nothing waits on it.  The other tiles follow in order.
 template <int CPB, class Src>
 __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src src,
                                                              uint64_t *__restrict__ status,
                                                              DescArrays d, ChainArea ch)
 {
-    constexpr int kW = kChunkThreads / 64;
-    __shared__ double lds_t[CPB][kW];
-    __shared__ WaveRun lds_runs[CPB][kW];
-    __shared__ WaveRun lds_join[CPB];
-    __shared__ bool lds_cross[CPB];
-    __shared__ double lds_p;
+    __shared__ TileLds<CPB> L;
     __shared__ WalkLds sh;
     __shared__ ChainLds cl;
     __shared__ CrossLds xl;
-    __shared__ uint64_t lds_x[CPB][kCrossWords];
-    __shared__ WalkLdsX wl;
     __shared__ int lds_src[Src::kLdsInts];
-    // With the chain on, the first a.count blocks walk it, one per sum.
-    const uint32_t nwalk = chain_on(a.flags) ? (uint32_t)a.count : 0u;
-    if (blockIdx.x < nwalk) {
-        chain_walk(src, a, (int)blockIdx.x, ch, sh, wl, lds_src);
-        return;
-    }
-    // With the chain on, each sum's last tile goes right after the walks:
-    // the walk ends with it, and started early it has waited for the tiles
-    // before it by the time they are done.  Nothing waits on it but the walk.
-    uint32_t gt = blockIdx.x - nwalk;  // this block's tile
-    if (nwalk) {
+    const bool chain = chain_on(a.flags);
+    uint32_t gt = blockIdx.x;  // this block's tile
+    if (chain) {
         if (gt < (uint32_t)a.count) {
             gt = a.last_tile[gt];
             if (gt == ~0u)
@@ -1465,17 +1286,19 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
     const int s = find_sum(a, g0);
     const size_t n = a.n[s];
     const uint32_t c0 = g0 - a.chunk_base[s];  // first local chunk
-    const double init = a.init[s];
-    const uint32_t mode = a.flags & EXSEQ_PLAN_MASK;
-    const int lane = lane_id(), wave = wave_id();
     const uint32_t nch = (uint32_t)((n + kChunk - 1) / kChunk);
     if (c0 >= nch)
         return;  // padding after the sum's last chunk
+    const uint32_t mode = a.flags & EXSEQ_PLAN_MASK;
+    const int t = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const uint32_t tl = c0 / CPB;               // tile index within the sum
+    const uint32_t tb = a.chunk_base[s] / CPB;  // the sum's first tile in the launch
     // A sum's first tile heads the exact chain: its waves go first in the
     // instruction arbitration of their SIMDs, ahead of streaming tiles.
-    if (c0 == 0 && chain_on(a.flags))
+    if (c0 == 0 && chain)
         __builtin_amdgcn_s_setprio(3);
 
+    // ---- the terms, and the fixed-tree sum of each chunk
     Four f[CPB];
 #pragma unroll
     for (int k = 0; k < CPB; k++) {
@@ -1491,101 +1314,92 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
         if (lane == 0) {
 #pragma unroll
             for (int k = 0; k < CPB; k++)
-                lds_t[k][wave] = ws[k];
+                L.wsum[k][wave] = ws[k];
         }
     }
     __syncthreads();
-    double T[CPB];
-    double Ttile = 0.0;
-#pragma unroll
-    for (int k = 0; k < CPB; k++) {
-        T[k] = (lds_t[k][0] + lds_t[k][1]) + (lds_t[k][2] + lds_t[k][3]);
-        Ttile += T[k];
-    }
 
-    const uint32_t tl = c0 / CPB;  // tile index within the sum
-    double P;
-    if (mode == EXSEQ_PLAN_ALL_FALLBACK || mode == EXSEQ_PLAN_FIXED) {
-        P = 0.0;  // these modes do not look at the prefix
-    } else {
-        uint64_t *st0 = status + a.chunk_base[s] / CPB;
-        if (tl == 0) {
-            P = init;
-        } else {
-            if (threadIdx.x == 0)
-                store_relaxed_u64(st0 + tl, st_pack(a.epoch, kStAgg, Ttile));
-            if (wave == 0) {
-                const double p = lookback(st0, tl, init, a.epoch);
-                if (lane == 0)
-                    lds_p = p;
-            }
-            __syncthreads();
-            P = lds_p;
+    // ---- the plan (wave 0): the prefix before the tile by look-back, then
+    // lane k < CPB plans chunk k
+    if (wave == 0) {
+        double T[CPB];
+        double Ttile = 0.0;
+#pragma unroll
+        for (int k = 0; k < CPB; k++) {
+            T[k] = (L.wsum[k][0] + L.wsum[k][1]) + (L.wsum[k][2] + L.wsum[k][3]);
+            Ttile += T[k];
         }
-        if (threadIdx.x == 0)
-            store_relaxed_u64(st0 + tl, st_pack(a.epoch, kStIncl, P + Ttile));
+        double P = 0.0;  // the fallback and fixed-binade modes do not look at it
+        if (mode != EXSEQ_PLAN_ALL_FALLBACK && mode != EXSEQ_PLAN_FIXED) {
+            uint64_t *st0 = status + tb;
+            if (tl == 0) {
+                P = a.init[s];
+            } else {
+                if (lane == 0)
+                    store_relaxed_u64(st0 + tl, st_pack(a.epoch, kStAgg, Ttile));
+                P = lookback(st0, tl, a.init[s], a.epoch);
+            }
+            if (lane == 0)
+                store_relaxed_u64(st0 + tl, st_pack(a.epoch, kStIncl, P + Ttile));
+        }
+        if (lane < CPB) {
+            double pk = P, tk = T[0];
+#pragma unroll
+            for (int k = 0; k < CPB - 1; k++) {
+                if (k < lane)
+                    pk += T[k];
+                if (k + 1 == lane)
+                    tk = T[k + 1];
+            }
+            L.pk[lane] = pk;
+            L.key[lane] = plan_key(pk, a.flags);
+            L.cross[lane] = key_of(pk + tk) != key_of(pk);
+        }
     }
+    __syncthreads();
 
+    // ---- every chunk's run under its planned binade
     uint32_t key[CPB];
-    double Pk[CPB];
-    bool cross[CPB];
+    bool allfast = true;
 #pragma unroll
     for (int k = 0; k < CPB; k++) {
-        Pk[k] = P;
-        key[k] = plan_key(P, a.flags);
-        cross[k] = key_of(P + T[k]) != key_of(P);
-        P += T[k];
+        key[k] = L.key[k];
+        allfast &= key_has_fast_path(key[k]);
     }
-    {
-        bool allfast = true;
+    if (allfast) {
+        wave_runs<CPB>(f, key, L.wrun);
+    } else {
 #pragma unroll
-        for (int k = 0; k < CPB; k++)
-            allfast &= key_has_fast_path(key[k]);
-        if (allfast) {
-            wave_runs<CPB>(f, key, lds_runs);
-        } else {
+        for (int k = 0; k < CPB; k++) {
+            WaveRun w;
+            if (key_has_fast_path(key[k])) {
+                w = wave_run(f[k], key[k]);
+            } else {
+                bool nf = false;
 #pragma unroll
-            for (int k = 0; k < CPB; k++) {
-                WaveRun w;
-                if (key_has_fast_path(key[k])) {
-                    w = wave_run(f[k], key[k]);
-                } else {
-                    bool nf = false;
-#pragma unroll
-                    for (int i = 0; i < 4; i++)
-                        nf |= i < f[k].cnt && is_nonfinite(f[k].v[i]);
-                    w.p = pair_identity();
-                    w.lo = w.hi = 0;
-                    w.flags = __ballot(nf) ? kFlagNonFinite : 0u;
-                }
-                if (lane == 0)
-                    lds_runs[k][wave] = w;
+                for (int i = 0; i < 4; i++)
+                    nf |= is_nonfinite(f[k].v[i]);
+                w.p = pair_identity();
+                w.lo = w.hi = 0;
+                w.flags = __ballot(nf) ? kFlagNonFinite : 0u;
             }
+            if (lane == 0)
+                L.wrun[k][wave] = w;
         }
     }
     __syncthreads();
     // Each chunk's run is joined, clamped and checked against the edges of
-    // its binade once, by one lane (lane k for chunk k), which also stores
-    // the chunk's descriptor for the walk; the rest of the tile reads the
-    // result from LDS.  (Work that is the same for every lane costs as much
-    // in one wave as in all of them.)
-    if ((int)threadIdx.x < CPB) {
-        const int k = threadIdx.x;
-        uint32_t kk = opaque(key[0]);
-        double pk = opaque(Pk[0]);
-        bool cc = cross[0];
-#pragma unroll
-        for (int j = 1; j < CPB; j++)
-            if (j == k) {
-                kk = opaque(key[j]);
-                pk = opaque(Pk[j]);
-                cc = cross[j];
-            }
-        const WaveRun r = clamp_run(join_waves(lds_runs[k]));
+    // its binade once, by lane k for chunk k, which also stores the chunk's
+    // descriptor; the rest of the tile reads the result from LDS.
+    if (t < CPB) {
+        const uint32_t kk = L.key[t];
+        const double pk = L.pk[t];
+        bool cc = L.cross[t] != 0;
+        const WaveRun r = clamp_run(join_waves(L.wrun[t]));
         // near an edge of the planned binade: the plan is not trusted there
         if (key_has_fast_path(kk) && kk == key_of(pk)) {
             const int64_t m = count_of(pk);
-            const int64_t mg = plan_margin(c0 + k + 1);
+            const int64_t mg = plan_margin(c0 + t + 1);
             bool near = m < kCountLo + mg;
             if (r.flags & kFlagNeg)
                 near |= m + r.lo - mg < kCountLo + 1 || m + r.hi + mg > kCountHi - 1;
@@ -1593,21 +1407,14 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
                 near |= m + r.hi + mg > kCountHi;
             cc |= near;
         }
-        lds_join[k] = r;
-        lds_cross[k] = cc;
-        if (c0 + k < nch)
-            store_desc(d, (size_t)(g0 + k), kk, r, cc ? kFlagCross : 0u);
+        L.join[t] = r;
+        L.cross[t] = cc;
+        if (c0 + t < nch)
+            store_desc(d, (size_t)(g0 + t), kk, r, cc ? kFlagCross : 0u);
     }
     __syncthreads();
-    auto chunk_run = [&](int k) { return lds_join[k]; };
-    uint32_t rflags[CPB];
-#pragma unroll
-    for (int k = 0; k < CPB; k++) {
-        rflags[k] = lds_join[k].flags;
-        cross[k] = lds_cross[k];
-    }
 
-    if (!chain_on(a.flags)) {
+    if (!chain) {
         // A sum's first chunk starts from init exactly.  There the running
         // sum is small next to the terms and crosses many binades, the worst
         // case of the walk's rounds, so its tile adds it in order and records
@@ -1615,8 +1422,8 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
         if (c0 == 0) {
             const int len = (int)(n < (size_t)kChunk ? n : (size_t)kChunk);
             int buf = 0;
-            const double e = resolve_terms(f[0], len, init, 0, sh, buf);
-            if (threadIdx.x == 0) {
+            const double e = resolve_terms(f[0], len, a.init[s], 0, sh, buf);
+            if (t == 0) {
                 d.lo[g0] = (int64_t)dbits(e);
                 d.meta[g0] |= kFlagExact;
             }
@@ -1625,19 +1432,18 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
     }
 
     // ---- the exact chain ----------------------------------------------------
-    const uint32_t tb = a.chunk_base[s] / CPB;  // the sum's first tile in the launch
     uint64_t *agg = ch.agg + 4 * (size_t)(tb + tl);
     bool regular = c0 != 0 && c0 + CPB < nch;
 #pragma unroll
     for (int k = 0; k < CPB; k++)
-        regular &= key_has_fast_path(key[k]) && key[k] == key[0] && !cross[k] &&
-                   !(rflags[k] & (kFlagBad | kFlagNonFinite));
+        regular &= key_has_fast_path(key[k]) && key[k] == key[0] && !L.cross[k] &&
+                   !(L.join[k].flags & (kFlagBad | kFlagNonFinite));
     if (regular) {
-        if (threadIdx.x == 0) {
+        if (t == 0) {
             Run tr = run_identity();
 #pragma unroll
             for (int k = 0; k < CPB; k++) {
-                const WaveRun r = chunk_run(k);
+                const WaveRun r = L.join[k];
                 tr = run_compose_sat(tr, Run{r.p, r.lo, r.hi, r.flags});
             }
             const int64_t dr = tr.p.r1 - tr.p.r0;
@@ -1650,108 +1456,249 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
         }
         return;
     }
-    if (threadIdx.x == 0)
+    // An irregular tile: located crossings, the composed run of the regular
+    // tiles back to the nearest irregular one, that tile's exact sum, then
+    // this tile's chunks in order from it.
+    if (t == 0)
         store_relaxed_u64(agg, kAggPresent);
+    // The chain is the critical path: this tile's waves go first in the
+    // instruction arbitration of their SIMDs, ahead of streaming tiles.
+    __builtin_amdgcn_s_setprio(3);
     int buf = 0;
-    // Crossings: every chunk expected to cross into the next binade up, with
-    // a plan for its binade, gets one located.  Per-chunk values are picked
-    // by unrolled selects: an array indexed by a run-time chunk number would
-    // live in scratch memory.
     const int nk = (int)(nch - c0 < (uint32_t)CPB ? nch - c0 : (uint32_t)CPB);
+    // Crossings: every chunk expected to cross into the next binade up, with
+    // a plan for its binade and no negative or non-finite term, gets one
+    // located.  (A run clamped for spanning more than its binade is no
+    // obstacle: the crossing's own checks cover each binade.)
     uint32_t want = 0u;
 #pragma unroll
-    for (int k = 0; k < CPB; k++)
-        if (k < nk && !(c0 == 0 && k == 0) && cross[k] && key_has_fast_path(key[k]) &&
-            key[k] == key_of(Pk[k]) && !(key[k] & 0x800u) && key_has_fast_path(key[k] + 1u) &&
-            !(rflags[k] & (kFlagNeg | kFlagBad | kFlagNonFinite)))
+    for (int k = 0; k < CPB; k++) {
+        const uint32_t fl = L.join[k].flags;
+        if (k < nk && !(c0 == 0 && k == 0) && L.cross[k] && key_has_fast_path(key[k]) &&
+            key[k] == key_of(L.pk[k]) && !(key[k] & 0x800u) && key_has_fast_path(key[k] + 1u) &&
+            !(fl & (kFlagNeg | kFlagNonFinite)))
             want |= 1u << k;
+    }
     uint32_t found = 0u;
 #pragma unroll 1
     for (int k = 0; k < CPB; k++) {
         if (!((want >> k) & 1u))
             continue;
-        uint32_t kr = opaque(key[0]);
-        double pr = opaque(Pk[0]);
-#pragma unroll
-        for (int j = 1; j < CPB; j++)
-            if (j == k) {
-                kr = opaque(key[j]);
-                pr = opaque(Pk[j]);
-            }
         // the terms again (from cache, most likely): irregular tiles are few,
         // and not keeping every chunk's terms in registers this far keeps
         // the register count of all tiles down
+        const Four fr = src.chunk(a, s, c0 + k, lds_src);
         const size_t b = (size_t)(c0 + k) * kChunk;
         const int len = (int)(n - b < (size_t)kChunk ? n - b : (size_t)kChunk);
-        const Four fr = src.chunk(a, s, c0 + k, lds_src);
         uint64_t w[kCrossWords];
-        if (crossing_find(fr, len, kr, count_of(pr), sh, xl, buf, w)) {
+        if (crossing_find(fr, len, L.key[k], count_of(L.pk[k]), sh, xl, buf, w)) {
             found |= 1u << k;
-            if (threadIdx.x == 0) {
+            if (t == 0) {
 #pragma unroll
                 for (int i = 0; i < kCrossWords; i++)
-                    lds_x[k][i] = w[i];
+                    L.xw[k][i] = w[i];
             }
         }
     }
-    __syncthreads();  // lds_x is complete
 
-    // The composed run of the regular tiles back to the nearest irregular
-    // one, then the block for the walk, written into that tile's slot (the
-    // sum's first tile: into the head slot).
-    Run acc = run_identity();
-    uint32_t key0 = 0u;
-    int64_t xp = -1;
-    int st = c0 != 0 ? chain_back(ch, tb, tl, sh, cl, buf, acc, key0, xp) : kBackOk;
-    if ((a.flags & EXSEQ_CHAIN_CUT) && tl >= ((nch + CPB - 1) / CPB) / 2 && st == kBackOk && tl > 0)
-        st = kBackBad;  // a test hook: the walk of the chain stops here
+    __syncthreads();  // L.xw is complete
+    // Everything the chain applies, one 64-bit word per lane (the bank):
+    // lane 4 + 10k + i holds word i of chunk k -- meta (key, r1 - r0 + 1,
+    // flags, crossing located), r0, lo, hi, then the crossing's words -- so
+    // that from the exact sum on every step reads its operands with
+    // readlane straight into scalar registers, with no LDS round trip.
+    uint64_t bank = 0;
     {
-        uint64_t *blk = ch.irr + (size_t)kIrrWords * (tb + tl);
-        if ((int)threadIdx.x < CPB) {
-            const int k = threadIdx.x;
-            uint64_t *cw = blk + kIrrChunk + kIrrPer * k;
-            const bool hx = (found >> k) & 1u;
+        const int k = (lane - 4) / kIrrPer, i = (lane - 4) - kIrrPer * ((lane - 4) / kIrrPer);
+        if (lane >= 4 && k < CPB) {
+            const WaveRun r = L.join[k];
+            if (i == 0)
+                bank = (uint64_t)(L.key[k] & kKeyMask) |
+                       ((uint64_t)(r.p.r1 - r.p.r0 + 1) << kDrShift) |
+                       (uint64_t)(r.flags & (kFlagNeg | kFlagBad | kFlagNonFinite)) |
+                       (((found >> k) & 1u) ? kIrrCross : 0ULL);
+            else if (i == 1)
+                bank = (uint64_t)r.p.r0;
+            else if (i == 2)
+                bank = (uint64_t)r.lo;
+            else if (i == 3)
+                bank = (uint64_t)r.hi;
+            else
+                bank = L.xw[k][i - 4];
+        }
+    }
+
+    // The exact sum before the tile.
+    double S = a.init[s];
+    bool ok = true;
+    bool done = false;  // the tile's chunks are applied too
+    if (c0 != 0) {
+        Run acc = run_identity();
+        uint32_t key0 = 0u;
+        int64_t xp = -1;
+        int st = chain_back(ch, tb, tl, sh, cl, buf, acc, key0, xp);
+        if ((a.flags & EXSEQ_CHAIN_CUT) && tl >= ((nch + CPB - 1) / CPB) / 2 && st == kBackOk)
+            st = kBackBad;  // a test hook: the chain stops here
+        ok = st == kBackOk;
+        // R, the regular tiles since tile xp, as scalars
+        const bool rnone = xp == (int64_t)tl - 1;
+        const Run R{Pair{readlane_i64(acc.p.r0, 0), readlane_i64(acc.p.r1, 0)},
+                    readlane_i64(acc.lo, 0), readlane_i64(acc.hi, 0),
+                    (uint32_t)__builtin_amdgcn_readfirstlane(
+                        (int)(acc.flags & (kFlagNeg | kFlagBad | kFlagNonFinite)))};
+        const uint32_t rkey = (uint32_t)__builtin_amdgcn_readfirstlane((int)key0);
+        // While the exact sum is on its way: the whole tile as few steps as
+        // its shape allows -- R and the chunks before the located crossing
+        // (all in one binade) composed into one run A, then the crossing,
+        // whose rest-of-chunk pair takes in the chunks after it (all in the
+        // next binade, none negative).  Any other shape, or any step that
+        // does not hold for the exact sum, goes chunk by chunk below.
+        bool fast = ok;
+        Run A = R;
+        uint32_t akey = rnone ? 0u : rkey;
+        int kx = nk;  // the crossing chunk (nk: none)
+        uint64_t xw[kCrossWords];
+#pragma unroll
+        for (int i = 0; i < kCrossWords; i++)
+            xw[i] = 0;
+        for (int k = 0; fast && k < nk; k++) {
+            const int base = 4 + kIrrPer * k;
+            const uint64_t cm = (uint64_t)readlane_i64((int64_t)bank, base);
+            const uint32_t kk = (uint32_t)cm & kKeyMask;
+            if (cm & kIrrCross) {
+                kx = k;
+                break;
+            }
+            const int64_t r0 = readlane_i64((int64_t)bank, base + 1);
+            const Run rk{Pair{r0, r0 + (int64_t)((cm >> kDrShift) & 3u) - 1},
+                         readlane_i64((int64_t)bank, base + 2), readlane_i64((int64_t)bank, base + 3),
+                         (uint32_t)cm & (kFlagNeg | kFlagBad | kFlagNonFinite)};
+            fast = key_has_fast_path(kk) && !(rk.flags & (kFlagBad | kFlagNonFinite)) &&
+                   (akey == 0u || akey == kk);
+            A = run_compose_sat(A, rk);
+            akey = kk;
+        }
+        uint32_t xkey = 0u;
+        if (fast && kx < nk) {
+            const int base = 4 + kIrrPer * kx;
+            xkey = (uint32_t)readlane_i64((int64_t)bank, base) & kKeyMask;
 #pragma unroll
             for (int i = 0; i < kCrossWords; i++)
-                store_relaxed_u64(cw + 4 + i, hx ? lds_x[k][i] : enc_i64(0));
-            if (k < nk) {
-                uint32_t kk = opaque(key[0]);
-#pragma unroll
-                for (int j = 1; j < CPB; j++)
-                    if (j == k)
-                        kk = opaque(key[j]);
-                const WaveRun r = chunk_run(k);
-                store_relaxed_u64(cw + 1, enc_i64(r.p.r0));
-                store_relaxed_u64(cw + 2, enc_i64(r.lo));
-                store_relaxed_u64(cw + 3, enc_i64(r.hi));
-                store_relaxed_u64(cw, kAggPresent | (uint64_t)(kk & kKeyMask) |
-                                          ((uint64_t)(r.p.r1 - r.p.r0 + 1) << kDrShift) |
-                                          (uint64_t)(r.flags & (kFlagNeg | kFlagBad | kFlagNonFinite)) |
-                                          (hx ? kIrrCross : 0ULL));
-            } else {
-                store_relaxed_u64(cw + 1, enc_i64(0));
-                store_relaxed_u64(cw + 2, enc_i64(0));
-                store_relaxed_u64(cw + 3, enc_i64(0));
-                store_relaxed_u64(cw, kAggPresent);
+                xw[i] = (uint64_t)readlane_i64((int64_t)bank, base + 4 + i);
+            fast = akey == 0u || akey == xkey;
+            Pair suf = rec_unpack(dec_i64(xw[3])), whole = rec_unpack(dec_i64(xw[4]));
+            for (int k = kx + 1; fast && k < nk; k++) {
+                const int b2 = 4 + kIrrPer * k;
+                const uint64_t cm = (uint64_t)readlane_i64((int64_t)bank, b2);
+                const int64_t r0 = readlane_i64((int64_t)bank, b2 + 1);
+                fast = ((uint32_t)cm & kKeyMask) == xkey + 1u && !(cm & kIrrCross) &&
+                       !((uint32_t)cm & (kFlagNeg | kFlagBad | kFlagNonFinite));
+                const Pair q{r0, r0 + (int64_t)((cm >> kDrShift) & 3u) - 1};
+                suf = compose(suf, q);
+                whole = compose(whole, q);
+            }
+            const int64_t lim = (int64_t)1 << 56;
+            fast = fast && suf.r0 < lim && suf.r1 < lim && whole.r0 < lim && whole.r1 < lim;
+            xw[3] = enc_i64(rec_pack(suf));
+            xw[4] = enc_i64(rec_pack(whole));
+        }
+        if (ok) {
+            if (t == 0) {
+                const uint64_t *p = ch.incl + tb + (size_t)xp;
+                uint64_t w = load_relaxed_u64(p);
+                for (int spin = 0; w == 0 && spin <= kSpinLimit; spin++) {
+                    __builtin_amdgcn_s_sleep(1);
+                    w = load_relaxed_u64(p);
+                }
+                L.word = w;
+            }
+            __syncthreads();
+            const uint64_t w = uniform_u64(L.word);
+            ok = w > kInclFailed;  // 0: the wait timed out
+            if (ok)
+                S = bitsd(w ^ kInclXor);
+            if (ok && fast) {
+                double T = S;
+                bool good = true;
+                if (akey != 0u) {
+                    const uint32_t ks = key_of(T);
+                    const int64_t mm = count_of(T);
+                    good = ks == akey && key_has_fast_path(ks) &&
+                           run_applies(mm, A.p, A.lo, A.hi, A.flags);
+                    if (good)
+                        T = assemble(ks, mm + pair_at(A.p, mm));
+                }
+                if (good && kx < nk) {
+                    const size_t b = (size_t)(c0 + kx) * kChunk;
+                    const int len = (int)(n - b < (size_t)kChunk ? n - b : (size_t)kChunk);
+                    int pos = 0;
+                    good = crossing_apply(xw, len, xkey, T, pos) == 1;
+                    T = bitsd(uniform_u64(dbits(T)));
+                }
+                if (good) {
+                    S = T;
+                    done = true;
+                }
+            }
+            if (ok && !done && !rnone) {
+                const uint32_t ks = key_of(S);
+                const int64_t mm = count_of(S);
+                ok = ks == rkey && key_has_fast_path(ks) &&
+                     run_applies(mm, R.p, R.lo, R.hi, R.flags);
+                if (ok)
+                    S = assemble(ks, mm + pair_at(R.p, mm));
             }
         }
-        if (threadIdx.x == 0) {
-            uint64_t rm = kAggPresent;
-            if (st != kBackOk)
-                rm |= kIrrFailed;
-            else if (xp == (int64_t)tl - 1)
-                rm |= kIrrEmpty;
-            else
-                rm |= (uint64_t)(key0 & kKeyMask) |
-                      ((uint64_t)(acc.p.r1 - acc.p.r0 + 1) << kDrShift) |
-                      (uint64_t)(acc.flags & (kFlagNeg | kFlagBad | kFlagNonFinite));
-            store_relaxed_u64(blk + 1, enc_i64(acc.p.r0));
-            store_relaxed_u64(blk + 2, enc_i64(acc.lo));
-            store_relaxed_u64(blk + 3, enc_i64(acc.hi));
-            store_relaxed_u64(blk + kIrrTile, (uint64_t)(xp + 2));
-            store_relaxed_u64(blk + kIrrInfo, kAggPresent | (uint64_t)nk);
-            store_relaxed_u64(blk + 0, rm);
+    }
+    // This tile's chunks in order: each chunk's run where it applies from
+    // the exact sum, else its crossing, else term by term.
+    uint32_t resolved = 0u;
+    if (ok && !done) {
+#pragma unroll 1
+        for (int k = 0; k < nk; k++) {
+            const size_t b = (size_t)(c0 + k) * kChunk;
+            const int len = (int)(n - b < (size_t)kChunk ? n - b : (size_t)kChunk);
+            int pos = 0;
+            if (!(c0 == 0 && k == 0)) {
+                const int base = 4 + kIrrPer * k;
+                const uint64_t cm = (uint64_t)readlane_i64((int64_t)bank, base);
+                const uint32_t kk = (uint32_t)cm & kKeyMask;
+                const int64_t r0 = readlane_i64((int64_t)bank, base + 1);
+                const Pair rp{r0, r0 + (int64_t)((cm >> kDrShift) & 3u) - 1};
+                const uint32_t ks = key_of(S);
+                const int64_t mm = count_of(S);
+                if (key_has_fast_path(ks) && ks == kk &&
+                    run_applies(mm, rp, readlane_i64((int64_t)bank, base + 2),
+                                readlane_i64((int64_t)bank, base + 3),
+                                (uint32_t)cm & (kFlagNeg | kFlagBad | kFlagNonFinite))) {
+                    S = assemble(ks, mm + pair_at(rp, mm));
+                    continue;
+                }
+                int xr = 0;
+                if (cm & kIrrCross) {
+                    uint64_t xw[kCrossWords];
+#pragma unroll
+                    for (int i = 0; i < kCrossWords; i++)
+                        xw[i] = (uint64_t)readlane_i64((int64_t)bank, base + 4 + i);
+                    xr = crossing_apply(xw, len, kk, S, pos);
+                    S = bitsd(uniform_u64(dbits(S)));
+                }
+                if (xr == 1)
+                    continue;
+                if (xr == 0)
+                    pos = 0;
+            }
+            S = resolve_terms(src.chunk(a, s, c0 + k, lds_src), len, S, pos, sh, buf);
+            S = bitsd(uniform_u64(dbits(S)));
+            resolved |= 1u << k;
         }
+    }
+    if (t == 0) {
+        store_relaxed_u64(ch.incl + tb + tl, ok ? enc_sum(S) : kInclFailed);
+#pragma unroll
+        for (int k = 0; k < CPB; k++)
+            if ((resolved >> k) & 1u)
+                d.meta[g0 + k] |= kFlagResolved;
     }
 }
 
@@ -1845,15 +1792,6 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, Src src
             fb_terms = st_terms;
             first_fb = st_first == 0x7FFFFFFFFFFFFFFFLL ? -1 : (int64_t)st_first;
             nonfinite |= st_nf != 0;
-            if (ch.wstat[4 * s + 3]) {
-                // what the walk of the chain added term by term (after the
-                // first tile, which marks its own descriptors)
-                n_fb += ch.wstat[4 * s + 0];
-                fb_terms += ch.wstat[4 * s + 1];
-                const int64_t wf = (int64_t)ch.wstat[4 * s + 2] - 1;
-                if (wf >= 0 && (first_fb < 0 || wf < first_fb))
-                    first_fb = wf;
-            }
             n_fast = start - n_fb;
         }
     } else if (nch && (dmeta[0] & kFlagExact)) {
@@ -2096,8 +2034,7 @@ __global__ __launch_bounds__(kPlanThreads) void tree_total_kernel(
 
 __global__ void write_value_kernel(double *out, double v) { out[0] = v; }
 
-// Zeroes the chain words of `tiles` tiles (and the launch's record counter
-// and walk statistics) before a launch's tiles run.
+// Zeroes the chain words of `tiles` tiles before a launch's tiles run.
 __global__ __launch_bounds__(256) void chain_clear_kernel(ChainArea ch, uint32_t tiles)
 {
     const uint32_t i = blockIdx.x * 256u + threadIdx.x;
@@ -2106,13 +2043,7 @@ __global__ __launch_bounds__(256) void chain_clear_kernel(ChainArea ch, uint32_t
         for (int k = 0; k < 4; k++)
             ch.agg[4 * (size_t)i + k] = 0;
         ch.incl[i] = 0;
-#pragma unroll
-        for (int k = 0; k < kIrrWords; k++)
-            ch.irr[(size_t)kIrrWords * i + k] = 0;
     }
-    if (blockIdx.x == 0)
-        for (int k = threadIdx.x; k < 4 * kMaxBatch; k += 256)
-            ch.wstat[k] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -2158,10 +2089,6 @@ WsParts carve(void *ws, size_t total)
     p.ch.agg = reinterpret_cast<uint64_t *>(w);
     w += round256(4 * total * sizeof(uint64_t));
     p.ch.incl = reinterpret_cast<uint64_t *>(w);
-    w += round256(total * sizeof(uint64_t));
-    p.ch.irr = reinterpret_cast<uint64_t *>(w);
-    w += round256((size_t)kIrrWords * total * sizeof(uint64_t));
-    p.ch.wstat = reinterpret_cast<uint64_t *>(w);
     return p;
 }
 }  // namespace
@@ -2176,9 +2103,7 @@ size_t sum_ws_bytes(size_t total_chunks)
     return 4 * round256(total_chunks * sizeof(int64_t)) +
            round256(total_chunks * sizeof(uint32_t)) +
            round256(4 * total_chunks * sizeof(uint64_t)) +
-           round256(total_chunks * sizeof(uint64_t)) +
-           round256((size_t)kIrrWords * total_chunks * sizeof(uint64_t)) +
-           round256(4 * kMaxBatch * sizeof(uint64_t));
+           round256(total_chunks * sizeof(uint64_t));
 }
 
 template <int CPB, class Src>
@@ -2187,8 +2112,7 @@ static void launch_tiles(const BatchArgs &args, const Src &src, uint32_t total, 
 {
     const unsigned tiles = total / CPB;
     const bool chain = chain_on(args.flags);
-    const unsigned blocks =
-        chain ? (unsigned)args.count * 2u + args.rest_base[args.count] : tiles;
+    const unsigned blocks = chain ? (unsigned)args.count + args.rest_base[args.count] : tiles;
     if (tiles)
         hipLaunchKernelGGL(HIP_KERNEL_NAME(tile_kernel<CPB, Src>), dim3(blocks),
                            dim3(kChunkThreads), 0, stream, args, src, p.status, p.d, p.ch);
