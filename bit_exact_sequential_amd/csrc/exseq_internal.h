@@ -81,10 +81,12 @@ struct DescArrays {
 // The exact chain between the tiles of a sum (zeroed before every launch;
 // a published word is never zero).  Per tile: four words describing it (agg:
 // meta, r0, lo, hi of the composition of its chunks, or "irregular") and the
-// exact running sum after it (incl, irregular tiles only).
+// exact running sum after it (incl, irregular tiles only); per sum, the exact
+// sum after its first chunk (head).
 struct ChainArea {
     uint64_t *agg;
     uint64_t *incl;
+    uint64_t *head;  // per sum: the exact sum after its first chunk
 };
 
 // Workspace of a launch over `total_chunks` chunks: plan status words, the

@@ -124,9 +124,8 @@ EXSEQ_HD Pair compose(Pair a, Pair b)
 
 EXSEQ_HD int64_t pair_at(Pair p, int64_t m) { return (m & 1) ? p.r1 : p.r0; }
 
-// A chunk's descriptor.  lo/hi bound every prefix of the run for either start
-// parity: lo = sum of min(r0, r1, 0), hi = sum of max(r0, r1, 0) over its
-// terms (sound because each term's increment lies between its r0 and r1).
+// A chunk's descriptor.  lo/hi bound the increment of every prefix of the
+// run, for either start parity (lo <= 0 <= hi: the empty prefix counts).
 struct Run {
     Pair p;
     int64_t lo, hi;
@@ -148,12 +147,18 @@ EXSEQ_HD Run run_of_term(const TermInc& t, bool nonfinite)
     return r;
 }
 
+// a then b.  A prefix of the composition is a prefix of a, or all of a
+// (r0 or r1 of a, by the start parity) followed by a prefix of b, so the
+// bounds compose as a minimum and a maximum (sound for either start parity
+// and for any grouping of the terms).
 EXSEQ_HD Run run_compose(const Run& a, const Run& b)
 {
     Run c;
     c.p = compose(a.p, b.p);
-    c.lo = a.lo + b.lo;
-    c.hi = a.hi + b.hi;
+    const int64_t amin = a.p.r0 < a.p.r1 ? a.p.r0 : a.p.r1;
+    const int64_t amax = a.p.r0 < a.p.r1 ? a.p.r1 : a.p.r0;
+    c.lo = a.lo < amin + b.lo ? a.lo : amin + b.lo;
+    c.hi = a.hi > amax + b.hi ? a.hi : amax + b.hi;
     c.flags = a.flags | b.flags;
     return c;
 }

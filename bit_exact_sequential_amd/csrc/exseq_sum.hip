@@ -236,6 +236,49 @@ __device__ double lookback(const uint64_t *st0, uint32_t c, double init, uint32_
     }
 }
 
+// A composed run over many tiles: the components stay bounded (a run that
+// large never applies, so it is only marked bad).
+__device__ __forceinline__ Run run_compose_sat(const Run &a, const Run &b)
+{
+    Run c = run_compose(a, b);
+    const int64_t lim = (int64_t)1 << 56;
+    if (c.p.r0 > lim || c.p.r0 < -lim || c.p.r1 > lim || c.p.r1 < -lim || c.lo < -lim ||
+        c.hi > lim) {
+        c.flags |= kFlagBad;
+        c.p = Pair{0, 0};
+        c.lo = c.hi = 0;
+    }
+    return c;
+}
+
+template <int Ctrl, int RowMask = 0xF>
+__device__ __forceinline__ Run dpp_run(const Run &v)
+{
+    Run r;
+    r.p = dpp_pair<Ctrl, RowMask>(v.p);
+    r.lo = dpp_i64<Ctrl, RowMask>(v.lo, 0);
+    r.hi = dpp_i64<Ctrl, RowMask>(v.hi, 0);
+    r.flags = dpp_u32<Ctrl, RowMask>(v.flags, 0u);
+    return r;
+}
+
+// Ordered composition of the wave's runs (lane 0 first), in every lane.
+__device__ __forceinline__ Run wave_reduce_run(Run v)
+{
+    v = run_compose_sat(dpp_run<kDppRowShr1>(v), v);
+    v = run_compose_sat(dpp_run<kDppRowShr2>(v), v);
+    v = run_compose_sat(dpp_run<kDppRowShr4>(v), v);
+    v = run_compose_sat(dpp_run<kDppRowShr8>(v), v);
+    v = run_compose_sat(dpp_run<kDppRowBcast15, 0xA>(v), v);
+    v = run_compose_sat(dpp_run<kDppRowBcast31, 0xC>(v), v);
+    Run r;
+    r.p = readlane_pair(v.p, 63);
+    r.lo = readlane_i64(v.lo, 63);
+    r.hi = readlane_i64(v.hi, 63);
+    r.flags = (uint32_t)__builtin_amdgcn_readlane((int)v.flags, 63);
+    return r;
+}
+
 // ---------------------------------------------------------------------------
 // A chunk's run under a key
 // ---------------------------------------------------------------------------
@@ -287,16 +330,18 @@ __device__ __forceinline__ WaveRun wave_run(const Four &f, uint32_t key)
     w.lo = 0;
     w.hi = 0;
     if (wneg) {
-        int64_t lo = 0, hi = 0;
+        // the bounds of every prefix: the lane's terms composed in order,
+        // then the lanes in order
+        Run v = run_identity();
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int64_t mn = r0[i] < r1[i] ? r0[i] : r1[i];
             const int64_t mx = r0[i] < r1[i] ? r1[i] : r0[i];
-            lo += mn < 0 ? mn : 0;
-            hi += mx > 0 ? mx : 0;
+            v = run_compose(v, Run{Pair{r0[i], r1[i]}, mn < 0 ? mn : 0, mx > 0 ? mx : 0, 0u});
         }
-        w.lo = wave_sum_i64(lo);
-        w.hi = wave_sum_i64(hi);
+        v = wave_reduce_run(v);
+        w.lo = v.lo;
+        w.hi = v.hi;
     }
     w.flags = (wneg ? kFlagNeg : 0u) | (wbad ? kFlagBad : 0u) | (wnf ? kFlagNonFinite : 0u);
     return w;
@@ -368,10 +413,12 @@ __device__ __forceinline__ WaveRun join_waves(const WaveRun *w)
     WaveRun r = w[0];
 #pragma unroll
     for (int k = 1; k < kChunkThreads / 64; k++) {
-        r.p = compose(r.p, w[k].p);
-        r.lo += w[k].lo;
-        r.hi += w[k].hi;
-        r.flags |= w[k].flags;
+        const Run c = run_compose(Run{r.p, r.lo, r.hi, r.flags},
+                                  Run{w[k].p, w[k].lo, w[k].hi, w[k].flags});
+        r.p = c.p;
+        r.lo = c.lo;
+        r.hi = c.hi;
+        r.flags = c.flags;
     }
     if (!(r.flags & kFlagNeg))
         r.hi = r.p.r0 > r.p.r1 ? r.p.r0 : r.p.r1;
@@ -788,32 +835,6 @@ __device__ __forceinline__ int64_t dec_i64(uint64_t w) { return (int64_t)(w ^ kI
 __device__ __forceinline__ uint64_t enc_sum(double s)
 {
     return (s == s ? dbits(s) : kQuietNaN) ^ kInclXor;
-}
-
-// A composed run over many tiles: the components stay bounded (a run that
-// large never applies, so it is only marked bad).
-__device__ __forceinline__ Run run_compose_sat(const Run &a, const Run &b)
-{
-    Run c = run_compose(a, b);
-    const int64_t lim = (int64_t)1 << 56;
-    if (c.p.r0 > lim || c.p.r0 < -lim || c.p.r1 > lim || c.p.r1 < -lim || c.lo < -lim ||
-        c.hi > lim) {
-        c.flags |= kFlagBad;
-        c.p = Pair{0, 0};
-        c.lo = c.hi = 0;
-    }
-    return c;
-}
-
-template <int Ctrl, int RowMask = 0xF>
-__device__ __forceinline__ Run dpp_run(const Run &v)
-{
-    Run r;
-    r.p = dpp_pair<Ctrl, RowMask>(v.p);
-    r.lo = dpp_i64<Ctrl, RowMask>(v.lo, 0);
-    r.hi = dpp_i64<Ctrl, RowMask>(v.hi, 0);
-    r.flags = dpp_u32<Ctrl, RowMask>(v.flags, 0u);
-    return r;
 }
 
 // Composition of the wave's runs with the HIGHER lanes first (lane 63's run,
@@ -1233,6 +1254,24 @@ constexpr int kIrrPer = 4 + kCrossWords;       // bank words per chunk
 constexpr uint64_t kIrrCross = 1ULL << 40;     // bank meta: a crossing is located
 static_assert(4 + kIrrPer * kTileMax <= 64, "the bank fits one wave");
 
+// The head of a sum's chain: its first chunk added to init term by term,
+// published as the exact sum after that chunk.
+template <class Src>
+__device__ __forceinline__ void chain_head(const Src &src, const BatchArgs &a, int s,
+                                           const ChainArea &ch, const DescArrays &d, WalkLds &sh,
+                                           int *lds_src)
+{
+    const size_t n = a.n[s];
+    if (n == 0)
+        return;
+    __builtin_amdgcn_s_setprio(3);  // the chain starts here
+    const int len = (int)(n < (size_t)kChunk ? n : (size_t)kChunk);
+    int buf = 0;
+    const double S = resolve_terms(src.chunk(a, s, 0, lds_src), len, a.init[s], 0, sh, buf);
+    if (threadIdx.x == 0)
+        store_relaxed_u64(ch.head + s, enc_sum(S));
+}
+
 // What the waves of a tile hand each other.
 template <int CPB>
 struct TileLds {
@@ -1249,7 +1288,11 @@ struct TileLds {
 // One workgroup per tile of CPB consecutive chunks of one sum.  With the
 // chain on, each sum's last tile comes first (blocks 0 .. count-1): started
 // early, it has composed the tiles before it by the time they are done, and
-// nothing waits on it.  The other tiles follow in order.
+// nothing waits on it.  Then one head block per sum (count .. 2 count - 1)
+// adds the sum's first chunk to init term by term -- there the running sum
+// is small next to the terms and crosses binade after binade, the slowest
+// part of any chain -- while the tiles stream.  The other tiles follow in
+// order.
 template <int CPB, class Src>
 __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src src,
                                                              uint64_t *__restrict__ status,
@@ -1267,8 +1310,11 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
             gt = a.last_tile[gt];
             if (gt == ~0u)
                 return;
+        } else if (gt < 2u * (uint32_t)a.count) {
+            chain_head(src, a, (int)(gt - (uint32_t)a.count), ch, d, sh, lds_src);
+            return;
         } else {
-            const uint32_t r = gt - (uint32_t)a.count;
+            const uint32_t r = gt - 2u * (uint32_t)a.count;
             int lo = 0, hi = a.count - 1;  // the first sum with rest_base[s + 1] > r
             while (lo < hi) {
                 const int mid = (lo + hi) >> 1;
@@ -1528,20 +1574,26 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
         }
     }
 
-    // The exact sum before the tile.
+    // The exact sum before the tile's first chunk that it adds itself: after
+    // the nearest irregular tile before it and the regular tiles in between
+    // (R), or, in a sum's first tile, after the first chunk (the head's).
     double S = a.init[s];
     bool ok = true;
     bool done = false;  // the tile's chunks are applied too
-    if (c0 != 0) {
+    const int kfirst = c0 == 0 ? 1 : 0;
+    {
         Run acc = run_identity();
         uint32_t key0 = 0u;
         int64_t xp = -1;
-        int st = chain_back(ch, tb, tl, sh, cl, buf, acc, key0, xp);
-        if ((a.flags & EXSEQ_CHAIN_CUT) && tl >= ((nch + CPB - 1) / CPB) / 2 && st == kBackOk)
-            st = kBackBad;  // a test hook: the chain stops here
+        int st = kBackOk;
+        if (c0 != 0) {
+            st = chain_back(ch, tb, tl, sh, cl, buf, acc, key0, xp);
+            if ((a.flags & EXSEQ_CHAIN_CUT) && tl >= ((nch + CPB - 1) / CPB) / 2 && st == kBackOk)
+                st = kBackBad;  // a test hook: the chain stops here
+        }
         ok = st == kBackOk;
-        // R, the regular tiles since tile xp, as scalars
-        const bool rnone = xp == (int64_t)tl - 1;
+        // R as scalars
+        const bool rnone = c0 == 0 || xp == (int64_t)tl - 1;
         const Run R{Pair{readlane_i64(acc.p.r0, 0), readlane_i64(acc.p.r1, 0)},
                     readlane_i64(acc.lo, 0), readlane_i64(acc.hi, 0),
                     (uint32_t)__builtin_amdgcn_readfirstlane(
@@ -1561,7 +1613,7 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
 #pragma unroll
         for (int i = 0; i < kCrossWords; i++)
             xw[i] = 0;
-        for (int k = 0; fast && k < nk; k++) {
+        for (int k = kfirst; fast && k < nk; k++) {
             const int base = 4 + kIrrPer * k;
             const uint64_t cm = (uint64_t)readlane_i64((int64_t)bank, base);
             const uint32_t kk = (uint32_t)cm & kKeyMask;
@@ -1604,7 +1656,7 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
         }
         if (ok) {
             if (t == 0) {
-                const uint64_t *p = ch.incl + tb + (size_t)xp;
+                const uint64_t *p = c0 == 0 ? ch.head + s : ch.incl + tb + (size_t)xp;
                 uint64_t w = load_relaxed_u64(p);
                 for (int spin = 0; w == 0 && spin <= kSpinLimit; spin++) {
                     __builtin_amdgcn_s_sleep(1);
@@ -1652,14 +1704,14 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
     }
     // This tile's chunks in order: each chunk's run where it applies from
     // the exact sum, else its crossing, else term by term.
-    uint32_t resolved = 0u;
+    uint32_t resolved = c0 == 0 ? 1u : 0u;  // the head adds the first chunk term by term
     if (ok && !done) {
 #pragma unroll 1
-        for (int k = 0; k < nk; k++) {
+        for (int k = kfirst; k < nk; k++) {
             const size_t b = (size_t)(c0 + k) * kChunk;
             const int len = (int)(n - b < (size_t)kChunk ? n - b : (size_t)kChunk);
             int pos = 0;
-            if (!(c0 == 0 && k == 0)) {
+            {
                 const int base = 4 + kIrrPer * k;
                 const uint64_t cm = (uint64_t)readlane_i64((int64_t)bank, base);
                 const uint32_t kk = (uint32_t)cm & kKeyMask;
@@ -2044,6 +2096,8 @@ __global__ __launch_bounds__(256) void chain_clear_kernel(ChainArea ch, uint32_t
             ch.agg[4 * (size_t)i + k] = 0;
         ch.incl[i] = 0;
     }
+    if (i < (uint32_t)kMaxBatch)
+        ch.head[i] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -2089,6 +2143,8 @@ WsParts carve(void *ws, size_t total)
     p.ch.agg = reinterpret_cast<uint64_t *>(w);
     w += round256(4 * total * sizeof(uint64_t));
     p.ch.incl = reinterpret_cast<uint64_t *>(w);
+    w += round256(total * sizeof(uint64_t));
+    p.ch.head = reinterpret_cast<uint64_t *>(w);
     return p;
 }
 }  // namespace
@@ -2103,7 +2159,8 @@ size_t sum_ws_bytes(size_t total_chunks)
     return 4 * round256(total_chunks * sizeof(int64_t)) +
            round256(total_chunks * sizeof(uint32_t)) +
            round256(4 * total_chunks * sizeof(uint64_t)) +
-           round256(total_chunks * sizeof(uint64_t));
+           round256(total_chunks * sizeof(uint64_t)) +
+           round256(kMaxBatch * sizeof(uint64_t));
 }
 
 template <int CPB, class Src>
@@ -2112,7 +2169,7 @@ static void launch_tiles(const BatchArgs &args, const Src &src, uint32_t total, 
 {
     const unsigned tiles = total / CPB;
     const bool chain = chain_on(args.flags);
-    const unsigned blocks = chain ? (unsigned)args.count + args.rest_base[args.count] : tiles;
+    const unsigned blocks = chain ? 2u * (unsigned)args.count + args.rest_base[args.count] : tiles;
     if (tiles)
         hipLaunchKernelGGL(HIP_KERNEL_NAME(tile_kernel<CPB, Src>), dim3(blocks),
                            dim3(kChunkThreads), 0, stream, args, src, p.status, p.d, p.ch);
@@ -2143,8 +2200,9 @@ static int launch_batch_src(const BatchArgs &a, const Src &src, void *ws, double
     }
     mark(0);
     if (chain_on(a.flags) && tiles)
-        hipLaunchKernelGGL(chain_clear_kernel, dim3((tiles + 255) / 256), dim3(256), 0, stream,
-                           p.ch, tiles);
+        hipLaunchKernelGGL(chain_clear_kernel,
+                           dim3((unsigned)((tiles > (uint32_t)kMaxBatch ? tiles : (uint32_t)kMaxBatch) + 255) / 256),
+                           dim3(256), 0, stream, p.ch, tiles);
     mark(1);
     mark(2);
     if (args.tile == 1)
