@@ -6,8 +6,10 @@
 // lanes (4 waves of 64) with 4 consecutive terms per lane.
 //
 //  chain_clear_kernel: zeroes the chain words of the launch's tiles.
-//  tile_kernel (one workgroup per tile of CPB consecutive chunks of one sum;
-//  every tile of every sum of a batch in one launch; reads each term once):
+//  tile_kernel (one launch for every tile of every sum of a batch; reads
+//  each term once).  Blocks: each sum's last tile, each sum's head (its
+//  first chunk added to init term by term), then the other tiles in order,
+//  one workgroup per tile of CPB consecutive chunks of one sum:
 //    1. load the tile's terms (16-byte non-temporal loads), fixed-tree fp64
 //       sum of every chunk;
 //    2. the plan: publish the tile's sum, find the prefix of the chunk sums
@@ -20,12 +22,14 @@
 //    4. the exact chain.  A tile whose chunks all share one planned binade
 //       and stay clear of its edges (with a margin for the plan's error) is
 //       regular: it publishes the composition of its runs and is done.  Any
-//       other tile (a sum's first and last tile among them) waits for the
-//       exact sum after the nearest irregular tile before it, applies the
-//       composed runs of the regular tiles in between (checked against the
-//       binade), adds its own chunks in order -- a run where it applies, term
-//       by term from the exact sum where it does not -- and publishes the
-//       exact sum after itself.  The last tile's value is the result.
+//       other tile (a sum's first and last tile among them) locates the
+//       crossing of every chunk planned to cross into the next binade,
+//       composes the regular tiles back to the nearest irregular one,
+//       waits for that tile's exact sum (the first tile: the head's),
+//       applies the composed runs and its own chunks in order -- a run where
+//       it applies, a crossing where it holds, term by term from the exact
+//       sum where neither does -- and publishes the exact sum after itself.
+//       The last tile's value is the result.
 //  walk_kernel (one workgroup of 256 lanes per sum, after the tiles):
 //    5. takes the last tile's exact sum.  Where the chain could not finish
 //       (a wait that timed out, a composed run that did not apply), it

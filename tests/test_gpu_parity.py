@@ -108,15 +108,24 @@ def test_full_size_workloads(seed):
 
 
 def test_full_size_stats_ranges():
-    """Fallback counts in the range the method predicts: the first chunk and
-    about one per binade crossed (Research-1433 Findings 4)."""
+    """Fallback counts in the range the method predicts (Research-1433
+    Findings 4): the tie-heavy frame adds only its first chunk term by term
+    (every binade crossing after it is located and applied in O(1)); the
+    signed frame also adds each chunk that crosses a binade (no crossing is
+    located under a negative term), about one per doubling of the sum."""
     torch = torch_cuda()
     x = si.tie_heavy(si.FRAME_N, 0)
     _, st = gpu_sum(torch, x, stats=True)
     assert st["chunks"] == 8100
-    assert 1 <= st["fallback_chunks"] <= 40, st
+    assert 1 <= st["fallback_chunks"] <= 3, st
+    assert st["first_fallback"] == 0, st
     assert st["fast_chunks"] + st["fallback_chunks"] == 8100
     assert st["flags"] == 0
+    y = si.signed_terms(si.HALF_N, 0)
+    _, st = gpu_sum(torch, y, stats=True)
+    assert st["chunks"] == 2025
+    assert 1 <= st["fallback_chunks"] <= 24, st
+    assert st["fast_chunks"] + st["fallback_chunks"] == 2025
 
 
 def test_tie_fast_path_suite():
