@@ -1659,17 +1659,16 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
             xw[4] = enc_i64(rec_pack(whole));
         }
         if (ok) {
-            if (t == 0) {
+            // every wave polls on its own (no barrier between the word
+            // arriving and the steps that use it)
+            uint64_t w = 0;
+            if (lane == 0) {
                 const uint64_t *p = c0 == 0 ? ch.head + s : ch.incl + tb + (size_t)xp;
-                uint64_t w = load_relaxed_u64(p);
-                for (int spin = 0; w == 0 && spin <= kSpinLimit; spin++) {
-                    __builtin_amdgcn_s_sleep(1);
+                w = load_relaxed_u64(p);
+                for (int spin = 0; w == 0 && spin <= kSpinLimit; spin++)
                     w = load_relaxed_u64(p);
-                }
-                L.word = w;
             }
-            __syncthreads();
-            const uint64_t w = uniform_u64(L.word);
+            w = uniform_u64(w);
             ok = w > kInclFailed;  // 0: the wait timed out
             if (ok)
                 S = bitsd(w ^ kInclXor);
