@@ -1055,11 +1055,14 @@ __device__ __forceinline__ Pair block_scan_total(Pair v, WalkLds &sh, int buf, P
     return compose(pre, wave_shift_pair(inc));
 }
 
-// A crossing as published: the crossing term's index j, the packed prefix
-// pairs through j - 1 and through j under the planned binade, the packed
-// pairs of the terms after j and of the whole chunk under the next one, and
-// the term.
-constexpr int kCrossWords = 6;
+// A crossing as published (kCrossWords words): the crossing term's index j;
+// under the planned binade the packed prefix pairs through j - 1 and
+// through j, and bounds of every prefix before j; under the next binade the
+// packed pair of the terms after j and of the whole chunk, and bounds of
+// every prefix of the terms after j; the term itself.
+constexpr int kCrossWords = 10;
+constexpr int kXj = 0, kXpj1 = 1, kXpj = 2, kXsuf = 3, kXwhole = 4, kXterm = 5, kXpreLo = 6,
+              kXpreHi = 7, kXsufLo = 8, kXsufHi = 9;
 struct CrossCand {
     int j;
     int64_t pj1, pj;
@@ -1068,7 +1071,9 @@ struct CrossCand {
 struct CrossLds {
     CrossCand c[kWaves];
     int bad[kWaves];
-    Pair tot2[kWaves], suf2[kWaves];
+    Run suf2[kWaves];
+    Pair tot2[kWaves];
+    int64_t plo[kWaves], phi[kWaves];
 };
 
 // Locates the crossing of a chunk (terms f, len of them, planned binade
@@ -1079,11 +1084,25 @@ __device__ __forceinline__ bool crossing_find(const Four &f, int len, uint32_t k
                                               WalkLds &sh, CrossLds &xl, int &buf, uint64_t *out)
 {
     const int t = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const int scale = 1075 - (int)(key & 0x7FFu);
+    const bool sgn = (key >> 11) & 1u;
     Pair acc[kPer], tot;
-    const bool bad1 = lane_prefixes(f, key, acc);
+    bool bad1 = false;
+    {
+        Pair a = pair_identity();
+#pragma unroll
+        for (int i = 0; i < kPer; i++) {
+            if (i < f.cnt) {
+                const TermInc ti = term_inc(f.v[i], scale, sgn);
+                bad1 |= ti.bad;
+                a = compose(a, Pair{ti.r0, ti.r1});
+            }
+            acc[i] = a;
+        }
+    }
     const Pair pre = block_scan_total(acc[kPer - 1], sh, buf, tot);
     buf ^= 1;
-    // the first term whose count from m_est reaches 2^53 (counts only grow)
+    // the first term whose count from m_est reaches 2^53
     int firstk = -1;
 #pragma unroll
     for (int i = kPer - 1; i >= 0; i--) {
@@ -1127,88 +1146,124 @@ __device__ __forceinline__ bool crossing_find(const Four &f, int len, uint32_t k
     const CrossCand c = xl.c[bw];
     if (bad || c.j == kNone)
         return false;
-    // Under the next binade: the whole chunk, and the terms after j.
+    // Bounds of every prefix before j under the planned binade (either start
+    // parity: the smaller and the larger component of each prefix pair).
+    int64_t plo = 0, phi = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; i++) {
+        if (kPer * t + i < c.j) {
+            const Pair pe = compose(pre, acc[i]);
+            const int64_t mn = pe.r0 < pe.r1 ? pe.r0 : pe.r1;
+            const int64_t mx = pe.r0 < pe.r1 ? pe.r1 : pe.r0;
+            plo = mn < plo ? mn : plo;
+            phi = mx > phi ? mx : phi;
+        }
+    }
+    // Under the next binade: the whole chunk, and the terms after j as a run
+    // with its prefix bounds.
     const uint32_t key2 = key + 1u;
     const int scale2 = 1075 - (int)(key2 & 0x7FFu);
     const bool sgn2 = (key2 >> 11) & 1u;
     bool bad2 = false;
-    Pair whole = pair_identity(), suf = pair_identity();
+    Pair whole = pair_identity();
+    Run suf = run_identity();
 #pragma unroll
     for (int i = 0; i < kPer; i++) {
         if (i < f.cnt) {
             const TermInc ti = term_inc(f.v[i], scale2, sgn2);
-            bad2 |= ti.bad || ti.neg;
+            bad2 |= ti.bad;
             const Pair q{ti.r0, ti.r1};
             whole = compose(whole, q);
-            if (kPer * t + i > c.j)
-                suf = compose(suf, q);
+            if (kPer * t + i > c.j) {
+                const int64_t mn = ti.r0 < ti.r1 ? ti.r0 : ti.r1;
+                const int64_t mx = ti.r0 < ti.r1 ? ti.r1 : ti.r0;
+                suf = run_compose(suf, Run{q, mn < 0 ? mn : 0, mx > 0 ? mx : 0, 0u});
+            }
         }
     }
     whole = wave_reduce_pair(whole);
-    suf = wave_reduce_pair(suf);
+    suf = wave_reduce_run(suf);
+    plo = wave_min_i64(plo);
+    phi = wave_max_i64(phi);
     const uint64_t bb2 = __ballot(bad2);
     if (lane == 0) {
         xl.tot2[wave] = whole;
         xl.suf2[wave] = suf;
+        xl.plo[wave] = plo;
+        xl.phi[wave] = phi;
         xl.bad[wave] = bb2 != 0;
     }
     __syncthreads();
-    Pair tot2 = pair_identity(), suf2 = pair_identity();
+    Pair tot2 = pair_identity();
+    Run suf2 = run_identity();
 #pragma unroll
     for (int k = 0; k < kWaves; k++) {
         bad2 |= xl.bad[k] != 0;
         tot2 = compose(tot2, xl.tot2[k]);
-        suf2 = compose(suf2, xl.suf2[k]);
+        suf2 = run_compose_sat(suf2, xl.suf2[k]);
+        plo = xl.plo[k] < plo ? xl.plo[k] : plo;
+        phi = xl.phi[k] > phi ? xl.phi[k] : phi;
     }
-    if (bad2)
+    if (bad2 || (suf2.flags & kFlagBad))
         return false;
-    out[0] = enc_i64(c.j);
-    out[1] = enc_i64(c.pj1);
-    out[2] = enc_i64(c.pj);
-    out[3] = enc_i64(rec_pack(suf2));
-    out[4] = enc_i64(rec_pack(tot2));
-    out[5] = dbits(c.xj) ^ kInclXor;  // a crossing term is finite: never kInclXor
+    out[kXj] = enc_i64(c.j);
+    out[kXpj1] = enc_i64(c.pj1);
+    out[kXpj] = enc_i64(c.pj);
+    out[kXsuf] = enc_i64(rec_pack(suf2.p));
+    out[kXwhole] = enc_i64(rec_pack(tot2));
+    out[kXterm] = dbits(c.xj) ^ kInclXor;  // a crossing term is finite: never kInclXor
+    out[kXpreLo] = enc_i64(plo);
+    out[kXpreHi] = enc_i64(phi);
+    out[kXsufLo] = enc_i64(suf2.lo);
+    out[kXsufHi] = enc_i64(suf2.hi);
     return true;
 }
 
 // The chain's side: from the exact sum S before a chunk (len terms, planned
-// binade key) with a located crossing w[0..5].  Returns 1 with S the sum
-// after the chunk, 2 with S the exact sum after the crossing term and pos
-// the next term (the rest term by term), or 0 if the crossing does not hold
-// for this S (the whole chunk term by term).  The pairs w[3] and w[4] may
-// also take in runs that follow the chunk in the next binade: every success
-// applies one of them.
-__device__ __forceinline__ int crossing_apply(const uint64_t *w, int len, uint32_t key, double &S,
-                                              int &pos)
+// binade key, descriptor flags fl) with a located crossing w[].  Returns 1
+// with S the sum after the chunk, 2 with S the exact sum after the crossing
+// term and pos the next term (the rest term by term), or 0 if the crossing
+// does not hold for this S (the whole chunk term by term).  For a chunk with
+// a negative scaled term every prefix is checked against the binade it is
+// in, through the published bounds (Research-1424 Findings 3).  The pairs
+// w[kXsuf] and w[kXwhole] of a chunk without one may also take in runs that
+// follow the chunk in the next binade: every success applies one of them.
+__device__ __forceinline__ int crossing_apply(const uint64_t *w, int len, uint32_t key, uint32_t fl,
+                                              double &S, int &pos)
 {
+    const bool neg = (fl & kFlagNeg) != 0;
     const uint32_t ks = key_of(S);
     const int64_t m = count_of(S);
     if (ks == key + 1u) {
         // the crossing came before the chunk: all of it in the next binade
-        const int64_t e = m + pair_at(rec_unpack(dec_i64(w[4])), m);
-        if (!key_has_fast_path(ks) || e > kCountHi)
+        if (neg || !key_has_fast_path(ks))
+            return 0;
+        const int64_t e = m + pair_at(rec_unpack(dec_i64(w[kXwhole])), m);
+        if (e > kCountHi)
             return 0;
         S = assemble(ks, e);
         return 1;
     }
     if (ks != key || !key_has_fast_path(ks))
         return 0;
-    const int j = (int)dec_i64(w[0]);
-    const int64_t cb = j == 0 ? m : m + pair_at(rec_unpack(dec_i64(w[1])), m);
-    const int64_t cj = m + pair_at(rec_unpack(dec_i64(w[2])), m);
+    const int j = (int)dec_i64(w[kXj]);
+    const int64_t cb = j == 0 ? m : m + pair_at(rec_unpack(dec_i64(w[kXpj1])), m);
+    const int64_t cj = m + pair_at(rec_unpack(dec_i64(w[kXpj])), m);
     if (j >= len || cb > kCountHi - 1 || cj < kCountHi)
         return 0;  // the crossing is elsewhere for this start
+    if (neg && (m + dec_i64(w[kXpreLo]) < kCountLo + 1 || m + dec_i64(w[kXpreHi]) > kCountHi - 1))
+        return 0;  // some prefix before it leaves the binade
     const double sb = j == 0 ? S : assemble(key, cb);
-    S = sb + bitsd(w[5] ^ kInclXor);  // the one plain add
+    S = sb + bitsd(w[kXterm] ^ kInclXor);  // the one plain add
     pos = j + 1;
     const uint32_t k2 = key_of(S);
     const int64_t m2 = count_of(S);
     if (k2 != key + 1u || !key_has_fast_path(k2))
         return 2;
-    const int64_t e = m2 + pair_at(rec_unpack(dec_i64(w[3])), m2);
-    if (e > kCountHi)
+    const Pair sp = rec_unpack(dec_i64(w[kXsuf]));
+    if (!run_applies(m2, sp, dec_i64(w[kXsufLo]), dec_i64(w[kXsufHi]), neg ? kFlagNeg : 0u))
         return 2;  // a second crossing
-    S = assemble(k2, e);
+    S = assemble(k2, m2 + pair_at(sp, m2));
     return 1;
 }
 
@@ -1526,7 +1581,7 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
         const uint32_t fl = L.join[k].flags;
         if (k < nk && !(c0 == 0 && k == 0) && L.cross[k] && key_has_fast_path(key[k]) &&
             key[k] == key_of(L.pk[k]) && !(key[k] & 0x800u) && key_has_fast_path(key[k] + 1u) &&
-            !(fl & (kFlagNeg | kFlagNonFinite)))
+            !(fl & kFlagNonFinite))
             want |= 1u << k;
     }
     uint32_t found = 0u;
@@ -1637,12 +1692,14 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
         uint32_t xkey = 0u;
         if (fast && kx < nk) {
             const int base = 4 + kIrrPer * kx;
-            xkey = (uint32_t)readlane_i64((int64_t)bank, base) & kKeyMask;
+            const uint64_t xm = (uint64_t)readlane_i64((int64_t)bank, base);
+            xkey = (uint32_t)xm & kKeyMask;
 #pragma unroll
             for (int i = 0; i < kCrossWords; i++)
                 xw[i] = (uint64_t)readlane_i64((int64_t)bank, base + 4 + i);
-            fast = akey == 0u || akey == xkey;
-            Pair suf = rec_unpack(dec_i64(xw[3])), whole = rec_unpack(dec_i64(xw[4]));
+            // (a crossing chunk with a negative term goes chunk by chunk)
+            fast = (akey == 0u || akey == xkey) && !((uint32_t)xm & kFlagNeg);
+            Pair suf = rec_unpack(dec_i64(xw[kXsuf])), whole = rec_unpack(dec_i64(xw[kXwhole]));
             for (int k = kx + 1; fast && k < nk; k++) {
                 const int b2 = 4 + kIrrPer * k;
                 const uint64_t cm = (uint64_t)readlane_i64((int64_t)bank, b2);
@@ -1655,8 +1712,8 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
             }
             const int64_t lim = (int64_t)1 << 56;
             fast = fast && suf.r0 < lim && suf.r1 < lim && whole.r0 < lim && whole.r1 < lim;
-            xw[3] = enc_i64(rec_pack(suf));
-            xw[4] = enc_i64(rec_pack(whole));
+            xw[kXsuf] = enc_i64(rec_pack(suf));
+            xw[kXwhole] = enc_i64(rec_pack(whole));
         }
         if (ok) {
             // every wave polls on its own (no barrier between the word
@@ -1687,7 +1744,7 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
                     const size_t b = (size_t)(c0 + kx) * kChunk;
                     const int len = (int)(n - b < (size_t)kChunk ? n - b : (size_t)kChunk);
                     int pos = 0;
-                    good = crossing_apply(xw, len, xkey, T, pos) == 1;
+                    good = crossing_apply(xw, len, xkey, 0u, T, pos) == 1;
                     T = bitsd(uniform_u64(dbits(T)));
                 }
                 if (good) {
@@ -1735,7 +1792,7 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
 #pragma unroll
                     for (int i = 0; i < kCrossWords; i++)
                         xw[i] = (uint64_t)readlane_i64((int64_t)bank, base + 4 + i);
-                    xr = crossing_apply(xw, len, kk, S, pos);
+                    xr = crossing_apply(xw, len, kk, (uint32_t)cm, S, pos);
                     S = bitsd(uniform_u64(dbits(S)));
                 }
                 if (xr == 1)

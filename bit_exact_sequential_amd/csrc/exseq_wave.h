@@ -172,6 +172,42 @@ __device__ __forceinline__ void wave_sum_f64_n(double *v)
         v[k] = readlane_f64(v[k], 63);
 }
 
+// Minimum and maximum over the wave, in every lane.
+__device__ __forceinline__ int64_t wave_min_i64(int64_t v)
+{
+    int64_t o;
+    o = dpp_i64<kDppRowShr1>(v, v);
+    v = o < v ? o : v;
+    o = dpp_i64<kDppRowShr2>(v, v);
+    v = o < v ? o : v;
+    o = dpp_i64<kDppRowShr4>(v, v);
+    v = o < v ? o : v;
+    o = dpp_i64<kDppRowShr8>(v, v);
+    v = o < v ? o : v;
+    o = dpp_i64<kDppRowBcast15, 0xA>(v, v);
+    v = o < v ? o : v;
+    o = dpp_i64<kDppRowBcast31, 0xC>(v, v);
+    v = o < v ? o : v;
+    return readlane_i64(v, 63);
+}
+__device__ __forceinline__ int64_t wave_max_i64(int64_t v)
+{
+    int64_t o;
+    o = dpp_i64<kDppRowShr1>(v, v);
+    v = o > v ? o : v;
+    o = dpp_i64<kDppRowShr2>(v, v);
+    v = o > v ? o : v;
+    o = dpp_i64<kDppRowShr4>(v, v);
+    v = o > v ? o : v;
+    o = dpp_i64<kDppRowShr8>(v, v);
+    v = o > v ? o : v;
+    o = dpp_i64<kDppRowBcast15, 0xA>(v, v);
+    v = o > v ? o : v;
+    o = dpp_i64<kDppRowBcast31, 0xC>(v, v);
+    v = o > v ? o : v;
+    return readlane_i64(v, 63);
+}
+
 // Ordered composition of the wave's pairs (lane 0 first), in every lane.
 __device__ __forceinline__ Pair wave_reduce_pair(Pair v)
 {
