@@ -334,18 +334,27 @@ __device__ __forceinline__ WaveRun wave_run(const Four &f, uint32_t key)
     w.lo = 0;
     w.hi = 0;
     if (wneg) {
-        // the bounds of every prefix: the lane's terms composed in order,
-        // then the lanes in order
-        Run v = run_identity();
+        // Bounds of every prefix: the smallest and largest prefix of the
+        // even-start increments (a scan over the wave), widened by the
+        // number of ties -- along either start parity each term adds its r0
+        // or its r1, which differ by one exactly where the term ties.
+        int64_t a = 0, mn = 0, mx = 0, nt = 0;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            const int64_t mn = r0[i] < r1[i] ? r0[i] : r1[i];
-            const int64_t mx = r0[i] < r1[i] ? r1[i] : r0[i];
-            v = run_compose(v, Run{Pair{r0[i], r1[i]}, mn < 0 ? mn : 0, mx > 0 ? mx : 0, 0u});
+            a += r0[i];
+            mn = a < mn ? a : mn;
+            mx = a > mx ? a : mx;
+            nt += r0[i] != r1[i];
         }
-        v = wave_reduce_run(v);
-        w.lo = v.lo;
-        w.hi = v.hi;
+        const int64_t excl = wave_incl_scan_i64(a) - a;
+        int64_t lo = wave_min_i64(excl + mn), hi = wave_max_i64(excl + mx);
+        if (wtie) {
+            const int64_t ties = wave_sum_i64(nt);
+            lo -= ties;
+            hi += ties;
+        }
+        w.lo = lo < 0 ? lo : 0;
+        w.hi = hi > 0 ? hi : 0;
     }
     w.flags = (wneg ? kFlagNeg : 0u) | (wbad ? kFlagBad : 0u) | (wnf ? kFlagNonFinite : 0u);
     return w;
