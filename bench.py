@@ -36,6 +36,41 @@ METRIC = "fp64 terms/sec (GB/s, % HBM roofline) for bit-exact seq sum @3840x2160
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published peak
 TERM_BYTES = 8
 CHUNK = 1024
+PROFILE = os.path.join(ROOT, "profiles", "exact_sum_tie_heavy_3840x2160.md")
+TRAFFIC_TAG = "traffic record:"
+
+
+def source_digest():
+    """sha256 over the kernel sources (csrc/*.hip, csrc/*.h, sorted by name)."""
+    import hashlib
+    d = os.path.join(ROOT, "bit_exact_sequential_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel, digest):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 summary.
+
+    The summary holds one line `traffic record: {json}` with the kernel
+    sources' digest at the time the FETCH_SIZE and WRITE_SIZE passes ran and
+    the scaled bytes per dispatch. The figure is returned only when that
+    digest equals the sources' digest now (else None: the kernel changed
+    since the counters were taken)."""
+    try:
+        with open(PROFILE) as fh:
+            for ln in fh:
+                if ln.startswith(TRAFFIC_TAG):
+                    rec = json.loads(ln[len(TRAFFIC_TAG):])
+                    if rec.get("kernel") == kernel and rec.get("source_sha256") == digest:
+                        return rec["fetch_bytes"] + rec["write_bytes"]
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
 
 
 def parse():
@@ -297,6 +332,7 @@ def main():
         parity = bool(oracle_bits == res[0])
         assert parity, "bench result differs from the oracle"
 
+    digest = source_digest()
     line = {
         "metric": METRIC,
         "value": terms_per_s,
@@ -320,7 +356,9 @@ def main():
         "hbm_frac_end_to_end": gbs / HBM_PEAK_GBS,
         "roofline": {
             "bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+            "traffic": recorded_traffic(dominant, digest),
+            "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled)",
             "avg_kernel_us": avg_ms[dominant] * 1e3,
             "algorithmic_bytes_per_launch": ab,
         },
@@ -331,6 +369,7 @@ def main():
         "other_configs": others,
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,
+        "source_sha256": digest,
     }
     print(json.dumps(line), flush=True)
 
