@@ -207,11 +207,16 @@ __device__ __forceinline__ uint64_t st_flag(uint64_t w, uint32_t epoch)
 
 // Decoupled look-back (one wave): init plus every tile sum before tile c of
 // this sum.  Returns NaN if a predecessor never shows up (no plan then).
+// The wave waits on the nearest 64 predecessors; once they are all there
+// and none is inclusive, it reads up to kLbDeep further windows in one round
+// trip (the tiles before them have usually published by then).  Windows are
+// summed nearest first, one wave sum each, whichever round trip read them.
+constexpr int kLbDeep = 8;
 __device__ double lookback(const uint64_t *st0, uint32_t c, double init, uint32_t epoch)
 {
     const int lane = lane_id();
     double acc = 0.0;
-    int64_t j = (int64_t)c - 1;
+    int64_t j = (int64_t)c - 1;  // the nearest predecessor not summed yet
     int spins = 0;
     while (true) {
         const int64_t idx = j - lane;
@@ -231,12 +236,38 @@ __device__ double lookback(const uint64_t *st0, uint32_t c, double init, uint32_
             __builtin_amdgcn_s_sleep(2);
             continue;
         }
-        const uint64_t incl = __ballot(fl == kStIncl);
-        const int stop = incl ? __builtin_ctzll(incl) : 64;
+        uint64_t incl = __ballot(fl == kStIncl);
+        int stop = incl ? __builtin_ctzll(incl) : 64;
         acc += wave_sum_f64(lane <= stop ? v : 0.0);
         if (incl)
             return acc;
         j -= 64;
+        // the windows further back, all in one round trip
+        uint64_t w[kLbDeep];
+#pragma unroll
+        for (int k = 0; k < kLbDeep; k++) {
+            const int64_t ik = j - 64 * k - lane;
+            w[k] = ik >= 0 ? load_relaxed_u64(st0 + ik) : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < kLbDeep; k++) {
+            const int64_t ik = j - lane;
+            if (ik >= 0) {
+                fl = st_flag(w[k], epoch);
+                v = st_value(w[k]);
+            } else {
+                fl = kStIncl;
+                v = (ik == -1) ? init : 0.0;
+            }
+            if (__ballot(fl == 0))
+                break;  // wait on this window
+            incl = __ballot(fl == kStIncl);
+            stop = incl ? __builtin_ctzll(incl) : 64;
+            acc += wave_sum_f64(lane <= stop ? v : 0.0);
+            if (incl)
+                return acc;
+            j -= 64;
+        }
     }
 }
 
