@@ -495,44 +495,78 @@ __device__ __forceinline__ void store_desc(const DescArrays &d, size_t c, uint32
 }
 
 // acc + t[lo] + t[lo+1] + ... + t[hi-1], one add at a time in that order (the
-// loop itself), on one lane.  Two banks of eight terms alternate: the LDS
-// reads of one bank go out while the other bank is added, so that only the
-// chain of dependent adds (about 13 cycles each) is serial.
+// loop itself), on one lane.  16-byte LDS reads, three batches of kB pairs
+// in flight: a batch's reads have the adds of the two batches before it to
+// arrive in (a dependent fp64 add takes a few cycles, an LDS read far more),
+// so that mostly the chain of dependent adds is serial.
 __device__ __forceinline__ double add_in_order(double acc, const double *t, int lo, int hi)
 {
+    constexpr int kB = 4;
     int i = lo;
-    if (hi - i >= 16) {
-        double a[8], b[8];
+    if ((i & 1) && i < hi)
+        acc = acc + t[i++];
+    const v2f64 *p = reinterpret_cast<const v2f64 *>(t + i);
+    const int nv = (hi - i) >> 1;
+    int v = 0;
+    if (nv >= 3 * kB) {
+        v2f64 a[kB], b[kB], c[kB];
 #pragma unroll
-        for (int j = 0; j < 8; j++)
-            a[j] = t[i + j];
+        for (int j = 0; j < kB; j++) {
+            a[j] = p[j];
+            b[j] = p[kB + j];
+            c[j] = p[2 * kB + j];
+        }
+        v = 3 * kB;
+        while (nv - v >= 3 * kB) {
 #pragma unroll
-        for (int j = 0; j < 8; j++)
-            b[j] = t[i + 8 + j];
-        i += 16;
-        while (hi - i >= 16) {
+            for (int j = 0; j < kB; j++) {
+                acc = acc + a[j].x;
+                acc = acc + a[j].y;
+            }
 #pragma unroll
-            for (int j = 0; j < 8; j++)
-                acc = acc + a[j];
+            for (int j = 0; j < kB; j++)
+                a[j] = p[v + j];
 #pragma unroll
-            for (int j = 0; j < 8; j++)
-                a[j] = t[i + j];
+            for (int j = 0; j < kB; j++) {
+                acc = acc + b[j].x;
+                acc = acc + b[j].y;
+            }
 #pragma unroll
-            for (int j = 0; j < 8; j++)
-                acc = acc + b[j];
+            for (int j = 0; j < kB; j++)
+                b[j] = p[v + kB + j];
 #pragma unroll
-            for (int j = 0; j < 8; j++)
-                b[j] = t[i + 8 + j];
-            i += 16;
+            for (int j = 0; j < kB; j++) {
+                acc = acc + c[j].x;
+                acc = acc + c[j].y;
+            }
+#pragma unroll
+            for (int j = 0; j < kB; j++)
+                c[j] = p[v + 2 * kB + j];
+            v += 3 * kB;
         }
 #pragma unroll
-        for (int j = 0; j < 8; j++)
-            acc = acc + a[j];
+        for (int j = 0; j < kB; j++) {
+            acc = acc + a[j].x;
+            acc = acc + a[j].y;
+        }
 #pragma unroll
-        for (int j = 0; j < 8; j++)
-            acc = acc + b[j];
+        for (int j = 0; j < kB; j++) {
+            acc = acc + b[j].x;
+            acc = acc + b[j].y;
+        }
+#pragma unroll
+        for (int j = 0; j < kB; j++) {
+            acc = acc + c[j].x;
+            acc = acc + c[j].y;
+        }
     }
-    for (; i < hi; i++)
+    for (; v < nv; v++) {
+        const v2f64 q = p[v];
+        acc = acc + q.x;
+        acc = acc + q.y;
+    }
+    i += 2 * nv;
+    if (i < hi)
         acc = acc + t[i];
     return acc;
 }
@@ -940,9 +974,13 @@ __device__ __forceinline__ int chain_back(const ChainArea &ch, uint32_t tb, uint
                 const uint64_t *p = ch.agg + 4 * ((size_t)tb + (size_t)(j < 0 ? 0 : j));
                 if (j < 0)
                     continue;
+                // the meta word is written last: until it is there, all
+                // four are read again (one round trip once they arrive)
                 if (w[i][0] == 0) {
                     need = true;
-                    w[i][0] = load_relaxed_u64(p);
+#pragma unroll
+                    for (int q = 0; q < 4; q++)
+                        w[i][q] = load_relaxed_u64(p + q);
                 } else if (w[i][0] & kAggRegular) {
 #pragma unroll
                     for (int q = 1; q < 4; q++)
