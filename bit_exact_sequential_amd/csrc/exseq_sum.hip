@@ -1026,9 +1026,12 @@ __device__ __forceinline__ int chain_back(const ChainArea &ch, uint32_t tb, uint
         buf ^= 1;
         if (anymiss)
             return kBackLost;
-        // the regular tiles after it, the earlier ones first
+        // the regular tiles after it, the earlier ones first; a wave whose
+        // tiles all have a tie-free run without a negative term (nearly
+        // always) composes them as one integer sum
         Run r = run_identity();
-        bool bad = false;
+        bool bad = false, plain = true;
+        int64_t tot = 0;
 #pragma unroll
         for (int i = kBackPer - 1; i >= 0; i--) {
             if (j0 - kBackPer * t - i >= 0 && kBackPer * t + i < first) {
@@ -1036,11 +1039,20 @@ __device__ __forceinline__ int chain_back(const ChainArea &ch, uint32_t tb, uint
                 const Run ti{Pair{r0, r0 + (int64_t)((w[i][0] >> kDrShift) & 3u) - 1},
                              dec_i64(w[i][2]), dec_i64(w[i][3]),
                              (uint32_t)w[i][0] & (kFlagNeg | kFlagBad | kFlagNonFinite)};
+                plain &= ti.p.r1 == r0 && ti.flags == 0u && r0 >= 0;
+                tot += r0;
                 r = run_compose_sat(r, ti);
                 bad |= ((uint32_t)w[i][0] & kKeyMask) != key0;
             }
         }
-        r = wave_reduce_run_rev(r);
+        if (__ballot(!plain) == 0) {
+            tot = wave_sum_i64(tot);
+            r = Run{Pair{tot, tot}, 0, tot, 0u};
+            if (tot > ((int64_t)1 << 56))
+                r = Run{Pair{0, 0}, 0, 0, kFlagBad};
+        } else {
+            r = wave_reduce_run_rev(r);
+        }
         const uint64_t bb = __ballot(bad);
         if (lane == 63)
             cl.wrun[buf][wave] = r;
