@@ -1590,7 +1590,18 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
         const uint32_t kk = L.key[t];
         const double pk = L.pk[t];
         bool cc = L.cross[t] != 0;
-        const WaveRun r = clamp_run(join_waves(L.wrun[t]));
+        // the waves' parts in order; parts that are all tie-free and
+        // without a negative term (nearly always) just add up
+        bool plain = true;
+        int64_t sum = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; w++) {
+            const WaveRun &q = L.wrun[t][w];
+            plain &= q.p.r0 == q.p.r1 && q.flags == 0u && q.p.r0 >= 0;
+            sum += q.p.r0;
+        }
+        const WaveRun r =
+            clamp_run(plain ? WaveRun{Pair{sum, sum}, 0, sum, 0u} : join_waves(L.wrun[t]));
         // near an edge of the planned binade: the plan is not trusted there
         if (key_has_fast_path(kk) && kk == key_of(pk)) {
             const int64_t m = count_of(pk);
@@ -1635,11 +1646,24 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
                    !(L.join[k].flags & (kFlagBad | kFlagNonFinite));
     if (regular) {
         if (t == 0) {
-            Run tr = run_identity();
+            // the chunks' runs in order (plain ones add up)
+            bool plain = true;
+            int64_t sum = 0;
 #pragma unroll
             for (int k = 0; k < CPB; k++) {
-                const WaveRun r = L.join[k];
-                tr = run_compose_sat(tr, Run{r.p, r.lo, r.hi, r.flags});
+                const WaveRun &q = L.join[k];
+                plain &= q.p.r0 == q.p.r1 && q.flags == 0u && q.p.r0 >= 0;
+                sum += q.p.r0;
+            }
+            Run tr = run_identity();
+            if (plain) {
+                tr = Run{Pair{sum, sum}, 0, sum, 0u};
+            } else {
+#pragma unroll
+                for (int k = 0; k < CPB; k++) {
+                    const WaveRun r = L.join[k];
+                    tr = run_compose_sat(tr, Run{r.p, r.lo, r.hi, r.flags});
+                }
             }
             const int64_t dr = tr.p.r1 - tr.p.r0;
             store_relaxed_u64(agg + 1, enc_i64(tr.p.r0));
