@@ -48,7 +48,9 @@ __device__ __forceinline__ double ssim_term_dev(int64_t x, int64_t y, int64_t x2
 //      row (edge-truncated), into LDS;
 //   2. for every pixel, the sums of its row's window from those column sums
 //      (the window's columns of a pixel's row are raster positions within r
-//      of it, on the same row), and the term.
+//      of it, on the same row), and the term.  The window sums are exact
+//      integers, so sliding them along a row (adding the column that enters,
+//      subtracting the one that leaves) gives the same sums in any order.
 struct SsimTerms {
     SsimParams p;
     static constexpr int kMaxRadius = 15;
@@ -64,53 +66,179 @@ struct SsimTerms {
         const int plast = (p0 + 1024 < n ? p0 + 1024 : n) - 1;
         const int q0 = p0 - r;
         const int nq = plast + r - q0 + 1;
+        // Rows at least as wide as the span: the span crosses at most one row
+        // end, so one division per chunk gives every position's row and column
+        // (q0 may be negative, in the row before the first).
+        const bool wide = w >= kSpan;
+        const int iq0 = q0 >= 0 ? q0 / w : -1;
+        const int jq0 = q0 - iq0 * w;
+        // Column sums with 4-byte loads: rows a multiple of four pixels wide
+        // in planes whose rows and bases are 4-byte aligned put every group
+        // of four raster positions 4m .. 4m + 3 on one row, in one word per
+        // plane row; each lane loads its group's window rows at once.
+        const bool quad = wide && (w & 3) == 0 && (p.stride & 3) == 0 &&
+                          (((uintptr_t)p.ref | (uintptr_t)p.dis) & 3u) == 0;
         __syncthreads();  // earlier reads of lds are done
-        for (int k = t; k < nq; k += 256) {
-            const int q = q0 + k;
-            int sx = 0, sy = 0, sxx = 0, syy = 0, sxy = 0;
-            if (q >= 0 && q < n) {
-                const int i = q / w, j = q - (q / w) * w;
-                const int a0 = i - r < 0 ? 0 : i - r;
-                const int a1 = i + r >= h ? h - 1 : i + r;
-                for (int row = a0; row <= a1; row++) {
-                    const int x = p.ref[(ptrdiff_t)row * p.stride + j];
-                    const int y = p.dis[(ptrdiff_t)row * p.stride + j];
-                    sx += x;
-                    sy += y;
-                    sxx += x * x;
-                    syy += y * y;
-                    sxy += x * y;
+        if (quad) {
+            const int m0 = (q0 >= 0 ? q0 : q0 - 3) / 4;  // floor(q0 / 4)
+            const int m1 = (q0 + nq - 1) / 4;
+            for (int m = m0 + t; m <= m1; m += 256) {
+                const int q = 4 * m;  // first position of the group
+                int acc[5][4];
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    acc[0][e] = acc[1][e] = acc[2][e] = acc[3][e] = acc[4][e] = 0;
+                if (q >= 0 && q < n) {
+                    // (the first group may start up to 3 positions before q0)
+                    int i = iq0;
+                    int j = jq0 + (q - q0);
+                    if (j < 0) {
+                        j += w;
+                        i--;
+                    } else if (j >= w) {
+                        j -= w;
+                        i++;
+                    }
+                    const int a0 = i - r < 0 ? 0 : i - r;
+                    const int a1 = i + r >= h ? h - 1 : i + r;
+                    const uint32_t *pr = reinterpret_cast<const uint32_t *>(p.ref + (ptrdiff_t)a0 * p.stride + j);
+                    const uint32_t *pd = reinterpret_cast<const uint32_t *>(p.dis + (ptrdiff_t)a0 * p.stride + j);
+                    const ptrdiff_t sw = p.stride / 4;
+                    for (int row0 = a0; row0 <= a1; row0 += 4) {
+                        uint32_t vr[4], vd[4];
+#pragma unroll
+                        for (int u = 0; u < 4; u++) {
+                            const bool in = row0 + u <= a1;
+                            vr[u] = in ? pr[(ptrdiff_t)(row0 - a0 + u) * sw] : 0u;
+                            vd[u] = in ? pd[(ptrdiff_t)(row0 - a0 + u) * sw] : 0u;
+                        }
+#pragma unroll
+                        for (int u = 0; u < 4; u++) {
+#pragma unroll
+                            for (int e = 0; e < 4; e++) {
+                                const int x = (int)((vr[u] >> (8 * e)) & 0xFFu);
+                                const int y = (int)((vd[u] >> (8 * e)) & 0xFFu);
+                                acc[0][e] += x;
+                                acc[1][e] += y;
+                                acc[2][e] += x * x;
+                                acc[3][e] += y * y;
+                                acc[4][e] += x * y;
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int k = q + e - q0;
+                    if (k >= 0 && k < nq) {
+                        lds[k] = acc[0][e];
+                        lds[kSpan + k] = acc[1][e];
+                        lds[2 * kSpan + k] = acc[2][e];
+                        lds[3 * kSpan + k] = acc[3][e];
+                        lds[4 * kSpan + k] = acc[4][e];
+                    }
                 }
             }
-            lds[k] = sx;
-            lds[kSpan + k] = sy;
-            lds[2 * kSpan + k] = sxx;
-            lds[3 * kSpan + k] = syy;
-            lds[4 * kSpan + k] = sxy;
+        } else {
+            for (int k = t; k < nq; k += 256) {
+                const int q = q0 + k;
+                int sx = 0, sy = 0, sxx = 0, syy = 0, sxy = 0;
+                if (q >= 0 && q < n) {
+                    int i, j;
+                    if (wide) {
+                        i = iq0;
+                        j = jq0 + k;
+                        if (j >= w) {
+                            j -= w;
+                            i++;
+                        }
+                    } else {
+                        i = q / w;
+                        j = q - i * w;
+                    }
+                    const int a0 = i - r < 0 ? 0 : i - r;
+                    const int a1 = i + r >= h ? h - 1 : i + r;
+                    const uint8_t *pr = p.ref + (ptrdiff_t)a0 * p.stride + j;
+                    const uint8_t *pd = p.dis + (ptrdiff_t)a0 * p.stride + j;
+                    for (int row = a0; row <= a1; row++) {
+                        const int x = *pr;
+                        const int y = *pd;
+                        sx += x;
+                        sy += y;
+                        sxx += x * x;
+                        syy += y * y;
+                        sxy += x * y;
+                        pr += p.stride;
+                        pd += p.stride;
+                    }
+                }
+                lds[k] = sx;
+                lds[kSpan + k] = sy;
+                lds[2 * kSpan + k] = sxx;
+                lds[3 * kSpan + k] = syy;
+                lds[4 * kSpan + k] = sxy;
+            }
         }
         __syncthreads();
         Four f;
         const int first = p0 + 4 * t;
         f.cnt = first < n ? (n - first < 4 ? n - first : 4) : 0;
+        // The window sums of a lane's four pixels: the first from the column
+        // sums of its window, each next one on the same row by adding the
+        // column entering the window and taking out the one leaving it.
+        int sx = 0, sy = 0, sxx = 0, syy = 0, sxy = 0;
+        int pj = -2;  // column of the previous pixel (-2: none)
 #pragma unroll
         for (int u = 0; u < 4; u++) {
             const int pix = first + u;
             double v = 0.0;
             if (u < f.cnt) {
-                const int i = pix / w, j = pix - (pix / w) * w;
+                const int k = pix - q0;
+                int i, j;
+                if (wide) {
+                    i = iq0;
+                    j = jq0 + k;
+                    if (j >= w) {
+                        j -= w;
+                        i++;
+                    }
+                } else {
+                    i = pix / w;
+                    j = pix - i * w;
+                }
                 const int a0 = i - r < 0 ? 0 : i - r;
                 const int a1 = i + r >= h ? h - 1 : i + r;
                 const int b0 = j - r < 0 ? 0 : j - r;
                 const int b1 = j + r >= w ? w - 1 : j + r;
-                int sx = 0, sy = 0, sxx = 0, syy = 0, sxy = 0;
-                for (int jj = b0; jj <= b1; jj++) {
-                    const int k = pix - q0 + (jj - j);
-                    sx += lds[k];
-                    sy += lds[kSpan + k];
-                    sxx += lds[2 * kSpan + k];
-                    syy += lds[3 * kSpan + k];
-                    sxy += lds[4 * kSpan + k];
+                if (j == pj + 1) {
+                    if (j + r <= w - 1) {
+                        const int ka = k + r;
+                        sx += lds[ka];
+                        sy += lds[kSpan + ka];
+                        sxx += lds[2 * kSpan + ka];
+                        syy += lds[3 * kSpan + ka];
+                        sxy += lds[4 * kSpan + ka];
+                    }
+                    if (j - r - 1 >= 0) {
+                        const int kd = k - r - 1;
+                        sx -= lds[kd];
+                        sy -= lds[kSpan + kd];
+                        sxx -= lds[2 * kSpan + kd];
+                        syy -= lds[3 * kSpan + kd];
+                        sxy -= lds[4 * kSpan + kd];
+                    }
+                } else {
+                    sx = sy = sxx = syy = sxy = 0;
+                    for (int jj = b0; jj <= b1; jj++) {
+                        const int kk = k + (jj - j);
+                        sx += lds[kk];
+                        sy += lds[kSpan + kk];
+                        sxx += lds[2 * kSpan + kk];
+                        syy += lds[3 * kSpan + kk];
+                        sxy += lds[4 * kSpan + kk];
+                    }
                 }
+                pj = j;
                 const int64_t wc = (int64_t)(a1 - a0 + 1) * (int64_t)(b1 - b0 + 1);
                 v = ssim_term_dev(sx, sy, sxx, syy, sxy, wc, p.c1, p.c2);
             }

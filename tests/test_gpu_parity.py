@@ -238,6 +238,29 @@ def test_ssim_small_frames(hw):
     assert int(gw.cpu()[0]) == wsum
 
 
+@pytest.mark.parametrize("hwsr", [(40, 1088, 1088, 3), (33, 1100, 1100, 5), (21, 1057, 1057, 3),
+                                  (19, 1088, 1096, 15), (9, 2048, 2052, 0), (64, 1280, 1280, 1)],
+                         ids=lambda v: "%dx%d_s%d_r%d" % v)
+def test_ssim_wide_rows(hwsr):
+    """Rows at least as wide as a chunk's span (the producer's one-division
+    row tracking; 4-byte plane loads where rows and strides are multiples of
+    four): every term and the sum equal the oracle's, padded strides too."""
+    torch = torch_cuda()
+    h, w, stride, radius = hwsr
+    ref, dis = si.frame_pair(h, w, h * 7 + w)
+    s, wsum, terms = oracle.ssim_frame_sum(ref, dis, radius, want_terms=True)
+    big_r = np.zeros((h, stride), np.uint8)
+    big_d = np.zeros((h, stride), np.uint8)
+    big_r[:, :w] = ref
+    big_d[:, :w] = dis
+    r = torch.from_numpy(big_r).cuda()[:, :w]
+    d = torch.from_numpy(big_d).cuda()[:, :w]
+    gs, gw, gt = ex.ssim_term_and_sum(r, d, radius, want_terms=True)
+    assert np.array_equal(gt.cpu().numpy().view(np.uint64), terms.view(np.uint64))
+    assert same(float(gs.cpu()[0]), s)
+    assert int(gw.cpu()[0]) == wsum
+
+
 def test_ssim_full_frame():
     torch = torch_cuda()
     ref, dis = si.frame_pair(si.FRAME_H, si.FRAME_W, 0)
