@@ -1777,9 +1777,10 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
         // While the exact sum is on its way: the whole tile as few steps as
         // its shape allows -- R and the chunks before the located crossing
         // (all in one binade) composed into one run A, then the crossing,
-        // whose rest-of-chunk pair takes in the chunks after it (all in the
-        // next binade, none negative).  Any other shape, or any step that
-        // does not hold for the exact sum, goes chunk by chunk below.
+        // whose rest-of-chunk run takes in the chunks after it (all in the
+        // next binade; under negative terms with its prefix bounds).  Any
+        // other shape, or any step that does not hold for the exact sum,
+        // goes chunk by chunk below.
         bool fast = ok;
         Run A = R;
         uint32_t akey = rnone ? 0u : rkey;
@@ -1806,6 +1807,7 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
             akey = kk;
         }
         uint32_t xkey = 0u;
+        uint32_t xfl = 0u;  // kFlagNeg: a negative term in the crossing or after it
         if (fast && kx < nk) {
             const int base = 4 + kIrrPer * kx;
             const uint64_t xm = (uint64_t)readlane_i64((int64_t)bank, base);
@@ -1813,22 +1815,32 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
 #pragma unroll
             for (int i = 0; i < kCrossWords; i++)
                 xw[i] = (uint64_t)readlane_i64((int64_t)bank, base + 4 + i);
-            // (a crossing chunk with a negative term goes chunk by chunk)
-            fast = (akey == 0u || akey == xkey) && !((uint32_t)xm & kFlagNeg);
-            Pair suf = rec_unpack(dec_i64(xw[kXsuf])), whole = rec_unpack(dec_i64(xw[kXwhole]));
+            xfl = (uint32_t)xm & kFlagNeg;
+            fast = akey == 0u || akey == xkey;
+            // the chunks after the crossing (all in the next binade) folded
+            // into its rest-of-chunk run, bounds and all, so that a negative
+            // term anywhere is checked as the crossing's own are
+            Run suf{rec_unpack(dec_i64(xw[kXsuf])), dec_i64(xw[kXsufLo]), dec_i64(xw[kXsufHi]), xfl};
+            Pair whole = rec_unpack(dec_i64(xw[kXwhole]));
             for (int k = kx + 1; fast && k < nk; k++) {
                 const int b2 = 4 + kIrrPer * k;
                 const uint64_t cm = (uint64_t)readlane_i64((int64_t)bank, b2);
                 const int64_t r0 = readlane_i64((int64_t)bank, b2 + 1);
                 fast = ((uint32_t)cm & kKeyMask) == xkey + 1u && !(cm & kIrrCross) &&
-                       !((uint32_t)cm & (kFlagNeg | kFlagBad | kFlagNonFinite));
-                const Pair q{r0, r0 + (int64_t)((cm >> kDrShift) & 3u) - 1};
-                suf = compose(suf, q);
-                whole = compose(whole, q);
+                       !((uint32_t)cm & (kFlagBad | kFlagNonFinite));
+                const Run q{Pair{r0, r0 + (int64_t)((cm >> kDrShift) & 3u) - 1},
+                            readlane_i64((int64_t)bank, b2 + 2), readlane_i64((int64_t)bank, b2 + 3),
+                            (uint32_t)cm & kFlagNeg};
+                suf = run_compose_sat(suf, q);
+                whole = compose(whole, q.p);
+                xfl |= (uint32_t)cm & kFlagNeg;
             }
             const int64_t lim = (int64_t)1 << 56;
-            fast = fast && suf.r0 < lim && suf.r1 < lim && whole.r0 < lim && whole.r1 < lim;
-            xw[kXsuf] = enc_i64(rec_pack(suf));
+            fast = fast && !(suf.flags & kFlagBad) && whole.r0 < lim && whole.r1 < lim &&
+                   whole.r0 > -lim && whole.r1 > -lim;
+            xw[kXsuf] = enc_i64(rec_pack(suf.p));
+            xw[kXsufLo] = enc_i64(suf.lo);
+            xw[kXsufHi] = enc_i64(suf.hi);
             xw[kXwhole] = enc_i64(rec_pack(whole));
         }
         if (ok) {
@@ -1860,7 +1872,7 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
                     const size_t b = (size_t)(c0 + kx) * kChunk;
                     const int len = (int)(n - b < (size_t)kChunk ? n - b : (size_t)kChunk);
                     int pos = 0;
-                    good = crossing_apply(xw, len, xkey, 0u, T, pos) == 1;
+                    good = crossing_apply(xw, len, xkey, xfl, T, pos) == 1;
                     T = bitsd(uniform_u64(dbits(T)));
                 }
                 if (good) {
