@@ -14,7 +14,9 @@ of the dominant kernel (per-kernel device time measured live with HIP events
 recorded by the library around each kernel), the oracle timed on the host as
 the CPU baseline, and the device time of the other workloads (the uniform
 4096-term sum, the signed 1920x1080 sum, the fused SSIM frame and the
-108-sum pyramid batch) under "other_configs".
+108-sum pyramid batch) under "other_configs", and the same six frames as a
+video whose every call keeps its plan for the next (EXSEQ_PLAN_REUSE) under
+"video_plan_reuse".
 """
 
 from __future__ import annotations
@@ -246,6 +248,35 @@ def main():
     for i in range(total):
         assert res[i] == res[i % args.buffers], "nondeterministic result"
 
+    # ---- the same frames as a video: each call keeps its plan for the next
+    # (EXSEQ_PLAN_REUSE); results must be the plain calls' bits
+    ws_v = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    outs_v = torch.empty(total, dtype=torch.float64, device=dev)
+    reuse = ex.PLAN_REUSE
+
+    def vstep(i):
+        rc = f(xp[i % args.buffers], n, 0.0, outs_v.data_ptr() + 8 * i, ws_v.data_ptr(), ws_bytes,
+               sh, reuse, None)
+        if rc:
+            raise RuntimeError(L.exseq_strerror(rc))
+    for i in range(args.warmup):
+        vstep(i)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.warmup, total):
+        vstep(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_video = t0.elapsed_time(t1) / args.steps
+    res_v = outs_v.cpu().numpy().view(np.uint64)
+    video = {"us_per_frame": ms_video * 1e3, "terms_per_s": n / (ms_video * 1e-3),
+             "gbs": n * TERM_BYTES / (ms_video * 1e-3) / 1e9,
+             "frames_rotated": args.buffers,
+             "same_bits_as_plain_calls": bool((res_v == res).all()),
+             "note": "each call takes its tiles' binades from the plan the previous call "
+                     "(a different frame) kept in the workspace"}
+    assert video["same_bits_as_plain_calls"], "plan reuse changed a result"
+
     # ---- per-kernel device time, live, with HIP events ---------------------
     nk = L.exseq_profile_kernel_count()
     names = [L.exseq_profile_kernel_name(k).decode() for k in range(nk)]
@@ -366,6 +397,7 @@ def main():
         "tree_sum": {"ms_per_step": tree_ms, "value": tree0, "exact": exact0,
                      "gap": tree0 - exact0},
         "host_wall_ms_per_step": wall * 1e3 / args.steps,
+        "video_plan_reuse": video,
         "other_configs": others,
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,

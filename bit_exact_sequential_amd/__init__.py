@@ -35,6 +35,7 @@ def plan_fixed(key: int) -> int:
 
 WALK_ONLY = 1 << 6
 CHAIN_CUT = 1 << 7
+PLAN_REUSE = 1 << 20
 
 
 def tile_flag(chunks_per_tile: int) -> int:

@@ -65,6 +65,10 @@ struct BatchArgs {
     // the others in order (rest_base: prefix count of them per sum).
     uint32_t last_tile[kMaxBatch];
     uint32_t rest_base[kMaxBatch + 1];
+    // With EXSEQ_PLAN_REUSE: the tag of this launch's shape, which the plan
+    // left in the workspace by an earlier launch must carry to be used (0:
+    // no reuse, and no plan is written).
+    uint64_t plan_sig;
 };
 
 // Descriptors live in four arrays (structure of arrays, so that the walk
@@ -87,6 +91,11 @@ struct ChainArea {
     uint64_t *agg;
     uint64_t *incl;
     uint64_t *head;  // per sum: the exact sum after its first chunk
+    // The plan kept for the next launch (EXSEQ_PLAN_REUSE): per sum the tag
+    // of the launch that wrote it, and the planned prefix before every tile
+    // of kTileMax chunks (index: the tile's first chunk in the launch / kTileMax).
+    uint64_t *plan_hdr;
+    double *plan;
 };
 
 // Workspace of a launch over `total_chunks` chunks: plan status words, the

@@ -54,6 +54,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstring>
 #include <stdint.h>
 
 #include "exseq.h"
@@ -1390,6 +1391,26 @@ __device__ __forceinline__ int64_t plan_margin(uint32_t chunks_to_end)
     return 4096 + (int64_t)(64.0 * __builtin_sqrt((double)chunks_to_end * (double)kChunk));
 }
 
+// The binade a kept plan gives a tile (EXSEQ_PLAN_REUSE): pa and pb are the
+// previous launch's planned prefixes before and after the tile.  Both,
+// widened by 1/64 of their magnitude on either side, must lie in one binade
+// with a fast path; 0 otherwise.  The widening absorbs how far the prefixes of
+// consecutive frames drift apart; a plan that is still wrong costs term by
+// term adds where the chain's checks fail, never a wrong result.
+__device__ __forceinline__ uint32_t reuse_key(double pa, double pb)
+{
+    const bool neg = pa < 0.0;
+    if (!(pa != 0.0 && pb != 0.0 && (pb < 0.0) == neg))
+        return 0u;  // a zero, a NaN, or a sign change
+    const double a = fabs(pa), b = fabs(pb);
+    const double lo = (a < b ? a : b) * (1.0 - 1.0 / 64.0);
+    const double hi = (a < b ? b : a) * (1.0 + 1.0 / 64.0);
+    if (!(hi < __builtin_inf()))
+        return 0u;
+    const uint32_t k = key_of(neg ? -lo : lo);
+    return k == key_of(neg ? -hi : hi) && key_has_fast_path(k) ? k : 0u;
+}
+
 // A value known to be the same in every lane, moved to scalar registers so
 // that the chain's arithmetic on it runs on the scalar unit.
 __device__ __forceinline__ uint64_t uniform_u64(uint64_t v)
@@ -1432,6 +1453,7 @@ struct TileLds {
     uint32_t cross[CPB];         // the plan does not keep the chunk in its binade
     uint64_t xw[CPB][kCrossWords];  // located crossings
     uint64_t word;               // a word read by one lane for all
+    uint32_t reused;             // the tile took its binade from a kept plan
 };
 
 // One workgroup per tile of CPB consecutive chunks of one sum.  With the
@@ -1492,6 +1514,16 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
     // instruction arbitration of their SIMDs, ahead of streaming tiles.
     if (c0 == 0 && chain)
         __builtin_amdgcn_s_setprio(3);
+    // A kept plan (EXSEQ_PLAN_REUSE) for a tile between the sum's first and
+    // last: its tag and the prefixes around the tile, read with the terms.
+    const bool try_reuse = CPB == kTileMax && a.plan_sig != 0 && tl != 0 && c0 + CPB < nch;
+    uint64_t phdr = 0;
+    double pa = 0.0, pb = 0.0;
+    if (try_reuse && wave == 0) {
+        phdr = ch.plan_hdr[s];
+        pa = ch.plan[gt];
+        pb = ch.plan[gt + 1];
+    }
 
     // ---- the terms, and the fixed-tree sum of each chunk
     Four f[CPB];
@@ -1525,18 +1557,25 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
             Ttile += T[k];
         }
         double P = 0.0;  // the fallback and fixed-binade modes do not look at it
+        uint32_t rkey = 0u;  // the binade a kept plan gives every chunk (0: none)
         if (mode != EXSEQ_PLAN_ALL_FALLBACK && mode != EXSEQ_PLAN_FIXED) {
             uint64_t *st0 = status + tb;
+            if (try_reuse && phdr == a.plan_sig)
+                rkey = reuse_key(pa, pb);
             if (tl == 0) {
                 P = a.init[s];
             } else {
                 if (lane == 0)
                     store_relaxed_u64(st0 + tl, st_pack(a.epoch, kStAgg, Ttile));
-                P = lookback(st0, tl, a.init[s], a.epoch);
+                // with a kept binade, the tiles after this one look back past
+                // it to the nearest inclusive prefix
+                P = rkey ? pa : lookback(st0, tl, a.init[s], a.epoch);
             }
-            if (lane == 0)
+            if (lane == 0 && !rkey)
                 store_relaxed_u64(st0 + tl, st_pack(a.epoch, kStIncl, P + Ttile));
         }
+        if (lane == 0)
+            L.reused = rkey;
         if (lane < CPB) {
             double pk = P, tk = T[0];
 #pragma unroll
@@ -1547,8 +1586,8 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
                     tk = T[k + 1];
             }
             L.pk[lane] = pk;
-            L.key[lane] = plan_key(pk, a.flags);
-            L.cross[lane] = key_of(pk + tk) != key_of(pk);
+            L.key[lane] = rkey ? rkey : plan_key(pk, a.flags);
+            L.cross[lane] = !rkey && key_of(pk + tk) != key_of(pk);
         }
     }
     __syncthreads();
@@ -1695,7 +1734,7 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
 #pragma unroll
     for (int k = 0; k < CPB; k++) {
         const uint32_t fl = L.join[k].flags;
-        if (k < nk && c0 != 0 && L.cross[k] && key_has_fast_path(key[k]) &&
+        if (k < nk && c0 != 0 && !L.reused && L.cross[k] && key_has_fast_path(key[k]) &&
             key[k] == key_of(L.pk[k]) && !(key[k] & 0x800u) && key_has_fast_path(key[k] + 1u) &&
             !(fl & kFlagNonFinite))
             want |= 1u << k;
@@ -1942,9 +1981,95 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
     }
 }
 
+// The plan kept for the next launch (EXSEQ_PLAN_REUSE): the planned prefix
+// before every tile of sum s, from this launch's status words -- the
+// inclusive prefix where a tile published one, else the previous prefix plus
+// the tile's own sum -- then the launch's tag.  Lane t takes a contiguous
+// run of tiles; the runs' (restart, sum) pairs are scanned across the
+// workgroup in order.
+struct PlanLds {
+    double v[kWaves];
+    int r[kWaves];
+};
+constexpr int kPlanGroup = 8;  // status words a lane holds at once
+__device__ void keep_plan(const BatchArgs &a, const uint64_t *status, const ChainArea &ch, int s,
+                          PlanLds &pl)
+{
+    const int t = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const size_t n = a.n[s];
+    const uint32_t nt = (uint32_t)((n + kChunk * kTileMax - 1) / (kChunk * kTileMax));
+    const uint32_t tb = a.chunk_base[s] / kTileMax;
+    const uint32_t per = (nt + kWalkThreads - 1) / kWalkThreads;
+    const uint32_t j0 = (uint32_t)t * per < nt ? (uint32_t)t * per : nt;
+    const uint32_t j1 = j0 + per < nt ? j0 + per : nt;
+    // this lane's run: r set if it holds an inclusive prefix (v is then the
+    // prefix after the run), else v adds to the prefix before it; the status
+    // words are read kPlanGroup at a time, all in flight together
+    int r = 0;
+    double v = 0.0;
+    for (uint32_t g = j0; g < j1; g += kPlanGroup) {
+        uint64_t w[kPlanGroup];
+#pragma unroll
+        for (int i = 0; i < kPlanGroup; i++)
+            w[i] = g + i < j1 ? status[tb + g + i] : 0;
+#pragma unroll
+        for (int i = 0; i < kPlanGroup; i++) {
+            const uint64_t fl = st_flag(w[i], a.epoch);
+            if (fl == kStIncl) {
+                r = 1;
+                v = st_value(w[i]);
+            } else if (fl == kStAgg) {
+                v += st_value(w[i]);
+            }
+        }
+    }
+    // inclusive scan in order: (r1, v1) then (r2, v2) is r2 ? (1, v2) : (r1, v1 + v2)
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double vu = __shfl_up(v, off);
+        const int ru = __shfl_up(r, off);
+        if (lane >= off && !r) {
+            r = ru;
+            v += vu;
+        }
+    }
+    if (lane == 63) {
+        pl.v[wave] = v;
+        pl.r[wave] = r;
+    }
+    __syncthreads();
+    double P = a.init[s];  // the prefix before this wave: init, then the waves before
+    for (int k = 0; k < wave; k++)
+        P = pl.r[k] ? pl.v[k] : P + pl.v[k];
+    const double vu = __shfl_up(v, 1);
+    const int ru = __shfl_up(r, 1);
+    if (lane > 0)
+        P = ru ? vu : P + vu;
+    for (uint32_t g = j0; g < j1; g += kPlanGroup) {
+        uint64_t w[kPlanGroup];
+#pragma unroll
+        for (int i = 0; i < kPlanGroup; i++)
+            w[i] = g + i < j1 ? status[tb + g + i] : 0;
+#pragma unroll
+        for (int i = 0; i < kPlanGroup; i++) {
+            if (g + i < j1)
+                ch.plan[tb + g + i] = P;
+            const uint64_t fl = st_flag(w[i], a.epoch);
+            if (fl == kStIncl)
+                P = st_value(w[i]);
+            else if (fl == kStAgg)
+                P += st_value(w[i]);
+        }
+    }
+    __syncthreads();
+    if (t == 0)
+        ch.plan_hdr[s] = a.plan_sig;
+}
+
 template <class Src>
 __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, Src src, DescArrays dall,
                                                             ChainArea ch,
+                                                            const uint64_t *__restrict__ status,
                                                             double *__restrict__ outs,
                                                             exseq_stats *__restrict__ stats)
 {
@@ -1954,7 +2079,10 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, Src src
     __shared__ long long st_first;
     __shared__ unsigned st_nf;
     __shared__ long long st_best[kWaves];
+    __shared__ PlanLds pl;
     const int s = blockIdx.x;
+    if (a.plan_sig != 0)
+        keep_plan(a, status, ch, s, pl);
     const size_t n = a.n[s];
     const size_t nch = (n + kChunk - 1) / kChunk;
     const size_t cb = a.chunk_base[s];
@@ -2311,6 +2439,26 @@ struct WsParts {
     ChainArea ch;
 };
 
+// The tag of a launch's shape for a kept plan: every sum's length, init and
+// first chunk, mixed by splitmix64 steps; never 0.
+uint64_t plan_tag(const BatchArgs &a)
+{
+    auto mix = [](uint64_t h, uint64_t v) {
+        uint64_t z = h ^ (v + 0x9E3779B97F4A7C15ULL + (h << 6) + (h >> 2));
+        z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+        z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+        return z ^ (z >> 31);
+    };
+    uint64_t h = mix(0x6578736571706C6EULL, (uint64_t)a.count);
+    for (int k = 0; k < a.count; k++) {
+        uint64_t ib;
+        std::memcpy(&ib, &a.init[k], sizeof ib);
+        h = mix(mix(mix(h, a.n[k]), ib), a.chunk_base[k]);
+    }
+    h = mix(h, a.chunk_base[a.count]);
+    return h ? h : 1;
+}
+
 
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
@@ -2333,6 +2481,10 @@ WsParts carve(void *ws, size_t total)
     p.ch.incl = reinterpret_cast<uint64_t *>(w);
     w += round256(total * sizeof(uint64_t));
     p.ch.head = reinterpret_cast<uint64_t *>(w);
+    w += round256(kMaxBatch * sizeof(uint64_t));
+    p.ch.plan_hdr = reinterpret_cast<uint64_t *>(w);
+    w += round256(kMaxBatch * sizeof(uint64_t));
+    p.ch.plan = reinterpret_cast<double *>(w);
     return p;
 }
 }  // namespace
@@ -2341,14 +2493,16 @@ const char *const kPathKernels[] = {"chain_clear_kernel", "tile_kernel", "walk_k
 const int kPathKernelCount = 3;
 
 // Per chunk (a tile is at least one chunk): the plan status word, the four
-// descriptor arrays, the chain words.
+// descriptor arrays, the chain words; per sum a head word and a kept-plan
+// tag; per tile of kTileMax chunks a kept planned prefix.
 size_t sum_ws_bytes(size_t total_chunks)
 {
     return 4 * round256(total_chunks * sizeof(int64_t)) +
            round256(total_chunks * sizeof(uint32_t)) +
            round256(4 * total_chunks * sizeof(uint64_t)) +
            round256(total_chunks * sizeof(uint64_t)) +
-           round256(kMaxBatch * sizeof(uint64_t));
+           2 * round256(kMaxBatch * sizeof(uint64_t)) +
+           round256((total_chunks / kTileMax + 1) * sizeof(double));
 }
 
 template <int CPB, class Src>
@@ -2379,6 +2533,10 @@ static int launch_batch_src(const BatchArgs &a, const Src &src, void *ws, double
     const uint32_t sel = (a.flags >> kTileShift) & 3u;  // 0: default
     args.tile = sel == 1 ? 1u : (sel == 2 ? 2u : 4u);
     const uint32_t tiles = total / args.tile;
+    args.plan_sig = (a.flags & EXSEQ_PLAN_REUSE) && (a.flags & EXSEQ_PLAN_MASK) == EXSEQ_PLAN_AUTO &&
+                            chain_on(a.flags) && args.tile == (uint32_t)kTileMax && tiles
+                        ? plan_tag(a)
+                        : 0;
     args.rest_base[0] = 0;
     for (int k = 0; k < a.count; k++) {
         const uint32_t nch = (uint32_t)((a.n[k] + kChunk - 1) / kChunk);
@@ -2402,7 +2560,7 @@ static int launch_batch_src(const BatchArgs &a, const Src &src, void *ws, double
     mark(3);
     mark(4);
     hipLaunchKernelGGL(HIP_KERNEL_NAME(walk_kernel<Src>), dim3((unsigned)a.count),
-                       dim3(kWalkThreads), 0, stream, args, src, p.d, p.ch, outs, stats);
+                       dim3(kWalkThreads), 0, stream, args, src, p.d, p.ch, p.status, outs, stats);
     mark(5);
     return hipGetLastError() == hipSuccess ? EXSEQ_OK : EXSEQ_EHIP;
 }

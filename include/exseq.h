@@ -25,9 +25,10 @@
  *    memory when the stream reaches it.
  *  - `ws` is a caller-provided device workspace of at least the size the
  *    matching *_workspace_size() call returns.  Its contents need no
- *    initialisation and are clobbered.  Calls that share a workspace must
- *    be ordered (same stream); calls on different streams need different
- *    workspaces.
+ *    initialisation and are clobbered (with EXSEQ_PLAN_REUSE a call leaves a
+ *    plan in it for the next call; see there).  Calls that share a workspace
+ *    must be ordered (same stream); calls on different streams need
+ *    different workspaces.
  *  - Terms are fp64 in native (little-endian) layout, contiguous, 8-byte
  *    aligned.  n == 0 is valid and writes `init`.
  *  - Non-finite terms are allowed: the result is what the loop gives (NaN
@@ -85,6 +86,30 @@ enum {
 #define EXSEQ_TILE_SHIFT 4
 #define EXSEQ_WALK_ONLY (1u << 6)
 #define EXSEQ_CHAIN_CUT (1u << 7)
+
+/* EXSEQ_PLAN_REUSE (with EXSEQ_PLAN_AUTO and the default tile): the plan of
+ * the previous call on the same workspace stands in for this call's where it
+ * leaves no doubt (Research-1433 "Forming the CPU's sequential double sums
+ * on a GPU, bit for bit", Open questions, first throughput candidate: keep a
+ * frame's plan for the next frame of a video, form the increments under it
+ * in the pass that forms the tree sums, and plan again only where the plan
+ * may have changed).
+ *   - Every call with the flag writes, after its sums, the planned prefix
+ *     before each tile of 4096 terms into the workspace, tagged with the
+ *     call's shape (count, every n and init, the chunk layout).
+ *   - A later call with the flag and the same shape on the same workspace
+ *     reads it.  A tile whose prefix range there, widened by 1/64 of its
+ *     magnitude on both sides, stays inside one binade takes that binade
+ *     for all its chunks and does not wait for the look-back over the tiles
+ *     before it.  Other tiles, a sum's first and last tile, and every tile
+ *     of a call without a matching tagged plan plan as without the flag.
+ *   - Results do not depend on the flag or on the stored plan (Research-1433
+ *     Findings 5: a plan only decides which chunks go term by term).  A
+ *     frame unlike the one before it (a scene cut) is still exact, and may
+ *     be slower: chunks whose reused binade is wrong go term by term.
+ * The flag is ignored with other plan modes, WALK_ONLY or a tile size other
+ * than the default. */
+#define EXSEQ_PLAN_REUSE (1u << 20)
 
 /* Device-side statistics of one sum (written when the walk finishes). */
 typedef struct exseq_stats {
