@@ -96,6 +96,9 @@ struct ChainArea {
     // of kTileMax chunks (index: the tile's first chunk in the launch / kTileMax).
     uint64_t *plan_hdr;
     double *plan;
+    // Per tile: the irregular tile's O(1) step from the exact sum before it
+    // (16 words, each nonzero once written), for the tiles after it.
+    uint64_t *rec;
 };
 
 // Workspace of a launch over `total_chunks` chunks: plan status words, the

@@ -1424,6 +1424,155 @@ constexpr int kIrrPer = 4 + kCrossWords;       // bank words per chunk
 constexpr uint64_t kIrrCross = 1ULL << 40;     // bank meta: a crossing is located
 static_assert(4 + kIrrPer * kTileMax <= 64, "the bank fits one wave");
 
+// One irregular tile's O(1) step from the exact sum S before it: the run A
+// (the regular tiles since the irregular tile before it, then its chunks
+// before the crossing; binade akey, none if 0), then the crossing (w, in a
+// chunk of len terms, binade xkey, kFlagNeg in xfl), whose rest-of-chunk run
+// takes in the chunks after it.  False, with S unchanged, where a check fails
+// for this S; the tile then adds chunk by chunk.
+__device__ __forceinline__ bool tile_step(uint32_t akey, const Run &A, bool hasx,
+                                          const uint64_t *w, int len, uint32_t xkey, uint32_t xfl,
+                                          double &S)
+{
+    double T = S;
+    if (akey != 0u) {
+        const uint32_t ks = key_of(T);
+        const int64_t mm = count_of(T);
+        if (!(ks == akey && key_has_fast_path(ks) && run_applies(mm, A.p, A.lo, A.hi, A.flags)))
+            return false;
+        T = assemble(ks, mm + pair_at(A.p, mm));
+    }
+    if (hasx) {
+        int pos = 0;
+        const bool good = crossing_apply(w, len, xkey, xfl, T, pos) == 1;
+        T = bitsd(uniform_u64(dbits(T)));
+        if (!good)
+            return false;
+    }
+    S = T;
+    return true;
+}
+
+// A published step (kRecWords words per tile, all nonzero once written):
+//   0: kRecPresent | akey | xkey << 12 | has crossing << 24 |
+//      A's flags >> 14 << 32 | crossing kFlagNeg << 35 | (r1 - r0 + 1) << 36
+//   1..3: A's r0, lo, hi;  4: the irregular tile before it;  5: the crossing
+//   chunk's length;  6..15: the crossing's words  (integers xor kIntTag)
+constexpr int kRecWords = 16;
+constexpr uint64_t kRecPresent = 1ULL << 63;
+constexpr int kCatch = 4;  // records a wave holds while it waits (16 lanes each)
+
+// The word of the record a lane i < kRecWords of the publishing wave writes.
+__device__ __forceinline__ uint64_t rec_word(int i, uint32_t akey, const Run &A, bool hasx,
+                                             const uint64_t *w, int len, uint32_t xkey,
+                                             uint32_t xfl, int64_t xp)
+{
+    uint64_t v = enc_i64(0);
+    if (i == 0)
+        v = kRecPresent | (uint64_t)(akey & kKeyMask) | ((uint64_t)(xkey & kKeyMask) << 12) |
+            ((uint64_t)hasx << 24) |
+            ((uint64_t)((A.flags >> 14) & 7u) << 32) | ((uint64_t)((xfl & kFlagNeg) != 0) << 35) |
+            ((uint64_t)(A.p.r1 - A.p.r0 + 1) << 36);
+    else if (i == 1)
+        v = enc_i64(A.p.r0);
+    else if (i == 2)
+        v = enc_i64(A.lo);
+    else if (i == 3)
+        v = enc_i64(A.hi);
+    else if (i == 4)
+        v = enc_i64(xp);
+    else if (i == 5)
+        v = enc_i64(len);
+#pragma unroll
+    for (int k = 0; k < kCrossWords; k++)
+        if (i == 6 + k && hasx)
+            v = w[k];
+    return v;
+}
+
+// The step of the record held in lanes 16 d .. 16 d + 15 of rw, from S.
+__device__ __forceinline__ bool rec_step(uint64_t rw, int d, double &S)
+{
+    const int b = 16 * d;
+    const uint64_t m = (uint64_t)readlane_i64((int64_t)rw, b);
+    const int64_t r0 = dec_i64((uint64_t)readlane_i64((int64_t)rw, b + 1));
+    const Run A{Pair{r0, r0 + (int64_t)((m >> 36) & 3u) - 1},
+                dec_i64((uint64_t)readlane_i64((int64_t)rw, b + 2)),
+                dec_i64((uint64_t)readlane_i64((int64_t)rw, b + 3)),
+                (uint32_t)((m >> 32) & 7u) << 14};
+    const bool hasx = (m >> 24) & 1u;
+    uint64_t w[kCrossWords];
+#pragma unroll
+    for (int k = 0; k < kCrossWords; k++)
+        w[k] = (uint64_t)readlane_i64((int64_t)rw, b + 6 + k);
+    const int len = (int)dec_i64((uint64_t)readlane_i64((int64_t)rw, b + 5));
+    return tile_step((uint32_t)m & kKeyMask, A, hasx, w, len, (uint32_t)(m >> 12) & kKeyMask,
+                     ((m >> 35) & 1u) ? kFlagNeg : 0u, S);
+}
+
+// The exact sum after irregular tile xp of a sum (whose first tile is tile tb
+// of the launch), as its published word (0: the wait timed out; kInclFailed:
+// the chain failed there).  The wave waits on xp's word and, at the same
+// time, collects the records of xp, of the irregular tile before it, and so
+// on (kCatch of them), polling the words of all of them: when an earlier one
+// arrives first, the records take the sum forward to xp in O(1) steps each,
+// so that a run of short links in the chain costs one wait (Research-1433
+// Findings 6: the walk composes in order; any exact route gives the same
+// bits).  The sums formed on the way are published for the tiles waiting on
+// them (when `publish`; the same value a tile computes for itself).
+__device__ __forceinline__ uint64_t catch_up(const ChainArea &ch, uint32_t tb, int64_t xp, bool publish)
+{
+    const int lane = lane_id();
+    int64_t cl = lane == 0 ? xp : 0;  // lane d < known: c_d (c_0 = xp)
+    int known = 1;
+    bool chase = true;
+    uint64_t rw = 0;  // lanes 16 d .. 16 d + 15: the record of c_d
+    for (int spin = 0; spin <= kSpinLimit; spin++) {
+        const int slot = known - 1;  // the record chased: c_slot's
+        const bool want_rec = chase && slot < kCatch;
+        const int64_t cs = readlane_i64(cl, slot);
+        uint64_t wi = 0, wr = 0;
+        if (lane < known)
+            wi = load_relaxed_u64(ch.incl + tb + (size_t)cl);
+        if (want_rec && (lane >> 4) == slot)
+            wr = load_relaxed_u64(ch.rec + kRecWords * ((size_t)tb + (size_t)cs) + (lane & 15));
+        const uint64_t w0 = (uint64_t)readlane_i64((int64_t)wi, 0);
+        if (w0 != 0)
+            return w0;  // xp's own word (or its failure)
+        const uint64_t bi = __ballot(wi > kInclFailed);
+        if (bi) {
+            // the nearest member with a word: forward through the records
+            int d = (int)__builtin_ctzll(bi);
+            double T = bitsd((uint64_t)readlane_i64((int64_t)wi, d) ^ kInclXor);
+            while (d > 0 && rec_step(rw, d - 1, T)) {
+                d--;
+                if (publish && lane == 0)
+                    store_relaxed_u64(ch.incl + tb + (size_t)readlane_i64(cl, d), enc_sum(T));
+            }
+            if (d == 0)
+                return enc_sum(T);
+            // c_{d-1}'s step does not hold from this sum: wait on the
+            // members from c_{d-1} on only
+            known = d;
+            chase = false;
+            continue;
+        }
+        if (want_rec) {
+            const uint64_t mask = 0xFFFFULL << (16 * slot);
+            if ((__ballot(wr != 0) & mask) == mask) {
+                if ((lane >> 4) == slot)
+                    rw = wr;
+                const int64_t nx = dec_i64((uint64_t)readlane_i64((int64_t)wr, 16 * slot + 4));
+                if (lane == known)
+                    cl = nx;
+                known++;
+            }
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return 0;
+}
+
 // The head of a sum's chain: its first chunk added to init term by term,
 // published as the exact sum after that chunk.
 template <class Src>
@@ -1882,43 +2031,37 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
             xw[kXsufHi] = enc_i64(suf.hi);
             xw[kXwhole] = enc_i64(rec_pack(whole));
         }
+        const int xlen = kx < nk ? (int)(n - (size_t)(c0 + kx) * kChunk < (size_t)kChunk
+                                             ? n - (size_t)(c0 + kx) * kChunk
+                                             : (size_t)kChunk)
+                                 : 0;
+        // the tile's step, for the tiles after it that catch up through it
+        if (ok && fast && c0 != 0 && wave == 0 && lane < kRecWords)
+            store_relaxed_u64(ch.rec + kRecWords * (size_t)(tb + tl) + lane,
+                              rec_word(lane, akey, A, kx < nk, xw, xlen, xkey, xfl, xp));
         if (ok) {
-            // every wave polls on its own (no barrier between the word
+            // every wave waits on its own (no barrier between the word
             // arriving and the steps that use it)
             uint64_t w = 0;
-            if (lane == 0) {
-                const uint64_t *p = c0 == 0 ? ch.head + s : ch.incl + tb + (size_t)xp;
-                w = load_relaxed_u64(p);
-                for (int spin = 0; w == 0 && spin <= kSpinLimit; spin++)
+            if (c0 == 0) {
+                if (lane == 0) {
+                    const uint64_t *p = ch.head + s;
                     w = load_relaxed_u64(p);
+                    for (int spin = 0; w == 0 && spin <= kSpinLimit; spin++)
+                        w = load_relaxed_u64(p);
+                }
+                w = uniform_u64(w);
+            } else {
+                // one wave waits and catches up (its loop is not cheap, and
+                // more waves of it would take issue slots from the streaming
+                // tiles on the same compute unit); the rest wait at a barrier
+                w = uniform_u64(catch_up(ch, tb, xp, wave == 0));
             }
-            w = uniform_u64(w);
             ok = w > kInclFailed;  // 0: the wait timed out
             if (ok)
                 S = bitsd(w ^ kInclXor);
-            if (ok && fast) {
-                double T = S;
-                bool good = true;
-                if (akey != 0u) {
-                    const uint32_t ks = key_of(T);
-                    const int64_t mm = count_of(T);
-                    good = ks == akey && key_has_fast_path(ks) &&
-                           run_applies(mm, A.p, A.lo, A.hi, A.flags);
-                    if (good)
-                        T = assemble(ks, mm + pair_at(A.p, mm));
-                }
-                if (good && kx < nk) {
-                    const size_t b = (size_t)(c0 + kx) * kChunk;
-                    const int len = (int)(n - b < (size_t)kChunk ? n - b : (size_t)kChunk);
-                    int pos = 0;
-                    good = crossing_apply(xw, len, xkey, xfl, T, pos) == 1;
-                    T = bitsd(uniform_u64(dbits(T)));
-                }
-                if (good) {
-                    S = T;
-                    done = true;
-                }
-            }
+            if (ok && fast && tile_step(akey, A, kx < nk, xw, xlen, xkey, xfl, S))
+                done = true;
             if (ok && !done && !rnone) {
                 const uint32_t ks = key_of(S);
                 const int64_t mm = count_of(S);
@@ -2405,14 +2548,16 @@ __global__ void write_value_kernel(double *out, double v) { out[0] = v; }
 // Zeroes the chain words of `tiles` tiles before a launch's tiles run.
 __global__ __launch_bounds__(256) void chain_clear_kernel(ChainArea ch, uint32_t tiles)
 {
-    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
-    if (i < tiles) {
-#pragma unroll
-        for (int k = 0; k < 4; k++)
-            ch.agg[4 * (size_t)i + k] = 0;
+    // consecutive lanes on consecutive words
+    const size_t i = (size_t)blockIdx.x * 256u + threadIdx.x;
+    const size_t stride = (size_t)gridDim.x * 256u;
+    for (size_t k = i; k < 4 * (size_t)tiles; k += stride)
+        ch.agg[k] = 0;
+    for (size_t k = i; k < (size_t)kRecWords * tiles; k += stride)
+        ch.rec[k] = 0;
+    if (i < tiles)
         ch.incl[i] = 0;
-    }
-    if (i < (uint32_t)kMaxBatch)
+    if (i < (size_t)kMaxBatch)
         ch.head[i] = 0;
 }
 
@@ -2485,6 +2630,8 @@ WsParts carve(void *ws, size_t total)
     p.ch.plan_hdr = reinterpret_cast<uint64_t *>(w);
     w += round256(kMaxBatch * sizeof(uint64_t));
     p.ch.plan = reinterpret_cast<double *>(w);
+    w += round256((total / kTileMax + 1) * sizeof(double));
+    p.ch.rec = reinterpret_cast<uint64_t *>(w);
     return p;
 }
 }  // namespace
@@ -2502,7 +2649,8 @@ size_t sum_ws_bytes(size_t total_chunks)
            round256(4 * total_chunks * sizeof(uint64_t)) +
            round256(total_chunks * sizeof(uint64_t)) +
            2 * round256(kMaxBatch * sizeof(uint64_t)) +
-           round256((total_chunks / kTileMax + 1) * sizeof(double));
+           round256((total_chunks / kTileMax + 1) * sizeof(double)) +
+           round256(kRecWords * total_chunks * sizeof(uint64_t));
 }
 
 template <int CPB, class Src>
@@ -2547,7 +2695,7 @@ static int launch_batch_src(const BatchArgs &a, const Src &src, void *ws, double
     mark(0);
     if (chain_on(a.flags) && tiles)
         hipLaunchKernelGGL(chain_clear_kernel,
-                           dim3((unsigned)((tiles > (uint32_t)kMaxBatch ? tiles : (uint32_t)kMaxBatch) + 255) / 256),
+                           dim3((unsigned)((4 * tiles > (uint32_t)kMaxBatch ? 4 * tiles : (uint32_t)kMaxBatch) + 255) / 256),
                            dim3(256), 0, stream, p.ch, tiles);
     mark(1);
     mark(2);
