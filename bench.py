@@ -249,33 +249,36 @@ def main():
         assert res[i] == res[i % args.buffers], "nondeterministic result"
 
     # ---- the same frames as a video: each call keeps its plan for the next
-    # (EXSEQ_PLAN_REUSE); results must be the plain calls' bits
-    ws_v = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    outs_v = torch.empty(total, dtype=torch.float64, device=dev)
-    reuse = ex.PLAN_REUSE
+    # (EXSEQ_PLAN_REUSE); results must be the plain calls' bits (skipped with
+    # --no-configs, so that the profiled program runs plain calls only)
+    video = None
+    if not args.no_configs:
+        ws_v = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        outs_v = torch.empty(total, dtype=torch.float64, device=dev)
+        reuse = ex.PLAN_REUSE
 
-    def vstep(i):
-        rc = f(xp[i % args.buffers], n, 0.0, outs_v.data_ptr() + 8 * i, ws_v.data_ptr(), ws_bytes,
-               sh, reuse, None)
-        if rc:
-            raise RuntimeError(L.exseq_strerror(rc))
-    for i in range(args.warmup):
-        vstep(i)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(args.warmup, total):
-        vstep(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_video = t0.elapsed_time(t1) / args.steps
-    res_v = outs_v.cpu().numpy().view(np.uint64)
-    video = {"us_per_frame": ms_video * 1e3, "terms_per_s": n / (ms_video * 1e-3),
-             "gbs": n * TERM_BYTES / (ms_video * 1e-3) / 1e9,
-             "frames_rotated": args.buffers,
-             "same_bits_as_plain_calls": bool((res_v == res).all()),
-             "note": "each call takes its tiles' binades from the plan the previous call "
-                     "(a different frame) kept in the workspace"}
-    assert video["same_bits_as_plain_calls"], "plan reuse changed a result"
+        def vstep(i):
+            rc = f(xp[i % args.buffers], n, 0.0, outs_v.data_ptr() + 8 * i, ws_v.data_ptr(), ws_bytes,
+                   sh, reuse, None)
+            if rc:
+                raise RuntimeError(L.exseq_strerror(rc))
+        for i in range(args.warmup):
+            vstep(i)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for i in range(args.warmup, total):
+            vstep(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms_video = t0.elapsed_time(t1) / args.steps
+        res_v = outs_v.cpu().numpy().view(np.uint64)
+        video = {"us_per_frame": ms_video * 1e3, "terms_per_s": n / (ms_video * 1e-3),
+                 "gbs": n * TERM_BYTES / (ms_video * 1e-3) / 1e9,
+                 "frames_rotated": args.buffers,
+                 "same_bits_as_plain_calls": bool((res_v == res).all()),
+                 "note": "each call takes its tiles' binades from the plan the previous call "
+                         "(a different frame) kept in the workspace"}
+        assert video["same_bits_as_plain_calls"], "plan reuse changed a result"
 
     # ---- per-kernel device time, live, with HIP events ---------------------
     nk = L.exseq_profile_kernel_count()
