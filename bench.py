@@ -128,8 +128,9 @@ def time_configs(ex, si, torch, dev, seed, reps=30):
     """Device time per call of the other workloads (torch events on the
     library's stream, after a warm-up call).  Sizes: the uniform 4096-term
     sum, the signed 1920x1080 sum, the fused SSIM sum of two 3840x2160
-    planes (radius 3), and the 108-sum pyramid batch (6 scales x 3 channels x
-    6 sums, 199,018,080 terms)."""
+    planes (radius 3), the four interleaved sums of a 3840x2160 LCS plane
+    (l*c*s, l, c, s per window) with their float means, and the 108-sum
+    pyramid batch (6 scales x 3 channels x 6 sums, 199,018,080 terms)."""
     def timed(fn, n):
         fn()
         torch.cuda.synchronize()
@@ -171,6 +172,15 @@ def time_configs(ex, si, torch, dev, seed, reps=30):
     res["fused_ssim_3840x2160"] = {"us_per_frame": ms * 1e3,
                                    "pixels_per_s": si.FRAME_N / (ms * 1e-3),
                                    "plane_gbs": 2 * si.FRAME_N / (ms * 1e-3) / 1e9}
+
+    x6 = torch.from_numpy(si.lcs_records(si.FRAME_N, seed)).to(dev)
+    o6 = torch.empty(4, dtype=torch.float64, device=dev)
+    w6 = ex.workspace(ex.lib().exact_seq_sum_f64_interleaved_workspace_size(si.FRAME_N, 4), dev)
+    ms = timed(lambda: ex.exact_seq_sum_interleaved(x6, 4, out=o6, ws=w6), reps)
+    res["lcs_interleaved_3840x2160"] = {"us_per_frame": ms * 1e3, "sums": 4,
+                                        "terms_per_s": 4 * si.FRAME_N / (ms * 1e-3),
+                                        "gbs": 32 * si.FRAME_N / (ms * 1e-3) / 1e9}
+    del x6
 
     xs = [torch.from_numpy(a).to(dev) for a in si.pyramid(seed)]
     total = sum(int(x.numel()) for x in xs)

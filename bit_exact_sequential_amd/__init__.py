@@ -96,6 +96,11 @@ def lib():
     L.exact_seq_sum_f64_batch.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(sz),
                                           ctypes.POINTER(ctypes.c_double), sz, vp, vp, sz,
                                           vp, u32, vp]
+    L.exact_seq_sum_f64_interleaved_workspace_size.restype = sz
+    L.exact_seq_sum_f64_interleaved_workspace_size.argtypes = [sz, i32]
+    L.exact_seq_sum_f64_interleaved.restype = i32
+    L.exact_seq_sum_f64_interleaved.argtypes = [vp, sz, i32, ctypes.POINTER(ctypes.c_double), vp,
+                                                vp, vp, sz, vp, u32, vp]
     L.ssim_term_and_sum_workspace_size.restype = sz
     L.ssim_term_and_sum_workspace_size.argtypes = [i32, i32]
     L.ssim_term_and_sum.restype = i32
@@ -202,6 +207,41 @@ def exact_seq_sum(x, init: float = 0.0, *, flags: int = 0, out=None, ws=None,
     if stats:
         return out, _read_stats(st)
     return out
+
+
+def exact_seq_sum_interleaved(x, k: int, inits=None, *, means: bool = True, flags: int = 0,
+                              out=None, ws=None, stats: bool = False, stream=None):
+    """k independent in-order sums over records of k doubles (``x``: device
+    float64, ``k * windows`` values, record-major) and, with ``means``, each
+    sum's float mean ``(float)(sum / windows)``.
+
+    Returns (sums tensor[k] f64, means tensor[k] f32 or None[, stats list])."""
+    torch = _torch()
+    _check_device_f64(x)
+    n = x.numel()
+    if k < 1 or n % k:
+        raise ExseqError("x must hold k * windows doubles")
+    windows = n // k
+    L = lib()
+    dev = x.device
+    if out is None:
+        out = torch.empty(k, dtype=torch.float64, device=dev)
+    mt = torch.empty(k, dtype=torch.float32, device=dev) if means else None
+    ini = None
+    if inits is not None:
+        ini = (ctypes.c_double * k)(*[float(v) for v in inits])
+    need = L.exact_seq_sum_f64_interleaved_workspace_size(windows, k)
+    if ws is None:
+        ws = workspace(need, dev)
+    st = torch.empty(STATS_BYTES * k, dtype=torch.uint8, device=dev) if stats else None
+    rc = L.exact_seq_sum_f64_interleaved(x.data_ptr() if n else None, windows, k, ini,
+                                         out.data_ptr(), mt.data_ptr() if mt is not None else None,
+                                         ws.data_ptr(), ws.numel(), _stream_handle(stream, dev),
+                                         int(flags), st.data_ptr() if st is not None else None)
+    _check(rc, "exact_seq_sum_f64_interleaved")
+    if stats:
+        return out, mt, _read_stats_many(st, k)
+    return out, mt
 
 
 def _read_stats(st):

@@ -131,6 +131,29 @@ int exact_seq_sum_f64_batch(const double *const *xs, const size_t *ns, const dou
     return EXSEQ_OK;
 }
 
+size_t exact_seq_sum_f64_interleaved_workspace_size(size_t windows, int k)
+{
+    if (k < 1 || k > EXSEQ_INTERLEAVE_MAX)
+        return 256;
+    return sum_ws_bytes((size_t)k * padded_chunks(windows));
+}
+
+int exact_seq_sum_f64_interleaved(const double *x, size_t windows, int k, const double *inits,
+                                  double *outs, float *means, void *ws, size_t ws_bytes,
+                                  exseq_stream_t stream, uint32_t flags, exseq_stats *stats)
+{
+    if (k < 1 || k > EXSEQ_INTERLEAVE_MAX || !outs || !aligned8(outs) ||
+        (means && (reinterpret_cast<uintptr_t>(means) & 3u)) ||
+        (windows && (!x || !aligned8(x))))
+        return EXSEQ_EINVAL;
+    if ((uint64_t)k * padded_chunks(windows) > 0xFFFFFFFFull)
+        return EXSEQ_EINVAL;
+    if (!ws || ws_bytes < exact_seq_sum_f64_interleaved_workspace_size(windows, k))
+        return ws ? EXSEQ_EWORKSPACE : EXSEQ_EINVAL;
+    return launch_interleaved(x, windows, k, inits, outs, means, ws,
+                              reinterpret_cast<hipStream_t>(stream), flags, stats);
+}
+
 size_t ssim_term_and_sum_workspace_size(int width, int height)
 {
     if (width < 1 || height < 1)

@@ -69,6 +69,12 @@ struct BatchArgs {
     // left in the workspace by an earlier launch must carry to be used (0:
     // no reuse, and no plan is written).
     uint64_t plan_sig;
+    // Sums of one length over interleaved terms (sum s reads every k-th
+    // double from x[s]): the tiles of all sums for one range of terms are
+    // dispatched together, on one XCD, so that they share cache lines.
+    uint32_t interleave;
+    // Nullable: means[s] = (float)(sum / n[s]) is written with the sum.
+    float *means;
 };
 
 // Descriptors live in four arrays (structure of arrays, so that the walk
@@ -106,6 +112,9 @@ struct ChainArea {
 size_t sum_ws_bytes(size_t total_chunks);
 int launch_batch(const BatchArgs &a, void *ws, double *outs, hipStream_t stream,
                  exseq_stats *stats, void *const *events = nullptr, int n_events = 0);
+int launch_interleaved(const double *x, size_t windows, int k, const double *inits, double *outs,
+                       float *means, void *ws, hipStream_t stream, uint32_t flags,
+                       exseq_stats *stats);
 int launch_exact_sum(const double *x, size_t n, double init, double *out, void *ws,
                      hipStream_t stream, uint32_t flags, exseq_stats *stats,
                      void *const *events = nullptr, int n_events = 0);

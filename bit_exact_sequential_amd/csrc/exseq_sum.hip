@@ -143,6 +143,29 @@ struct PlainTerms {
     __device__ __forceinline__ void keep(size_t, const Four &) const {}
 };
 
+// Every k-th double from x[s]: one field of records of k doubles, such as the
+// four doubles per window (l*c*s, l, c, s) of an SSIM pass that keeps the
+// factors (ADR-1464 "float_ssim_cuda adds its frame sums in the CPU's raster
+// order, on the host", Decision).  Cached loads: the k sums' tiles of one
+// range run together and read the same lines.
+struct StridedTerms {
+    static constexpr int kLdsInts = 1;
+    uint32_t k;
+    __device__ __forceinline__ Four chunk(const BatchArgs &a, int s, size_t c, int *) const
+    {
+        const size_t n = a.n[s];
+        const size_t first = c * kChunk + 4 * (size_t)threadIdx.x;
+        const double *__restrict__ x = a.x[s] + first * k;
+        Four f;
+        f.cnt = first < n ? (int)(n - first < 4 ? n - first : 4) : 0;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            f.v[i] = i < f.cnt ? x[(size_t)i * k] : 0.0;
+        return f;
+    }
+    __device__ __forceinline__ void keep(size_t, const Four &) const {}
+};
+
 // Fixed-shape tree sum of a chunk: ((v0+v1)+(v2+v3)) per lane, the wave in a
 // fixed order, then the four waves as ((w0+w1)+(w2+w3)).
 __device__ __forceinline__ double chunk_tree(const Four &f, double *lds4)
@@ -1635,16 +1658,30 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
             return;
         } else {
             const uint32_t r = gt - 2u * (uint32_t)a.count;
-            int lo = 0, hi = a.count - 1;  // the first sum with rest_base[s + 1] > r
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (a.rest_base[mid + 1] > r)
-                    hi = mid;
-                else
-                    lo = mid + 1;
+            int lo = 0;
+            uint32_t q;
+            if (a.interleave) {
+                // sums of one length: groups of 8 tiles of every sum in
+                // turn, so that tile q of each sum lands on the same XCD
+                // (blocks go round robin over the 8) close in time
+                const uint32_t per = a.rest_base[1];  // other tiles per sum
+                const uint32_t g = 8u * (uint32_t)a.count;
+                const uint32_t Q = r / g, rem = r - Q * g, full = per / 8u;
+                const uint32_t G = Q < full ? 8u : per - 8u * full;
+                lo = (int)(rem / G);
+                q = 8u * Q + rem % G;
+            } else {
+                int hi = a.count - 1;  // the first sum with rest_base[s + 1] > r
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (a.rest_base[mid + 1] > r)
+                        hi = mid;
+                    else
+                        lo = mid + 1;
+                }
+                q = r - a.rest_base[lo];
             }
             const uint32_t first = a.chunk_base[lo] / CPB;
-            const uint32_t q = r - a.rest_base[lo];
             gt = first + (q < a.last_tile[lo] - first ? q : q + 1);
         }
     }
@@ -2507,6 +2544,8 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, Src src
     }
     if (t == 0) {
         outs[s] = S;
+        if (a.means)
+            a.means[s] = (float)(S / (double)n);  // ADR-1464: (float)(sum / windows)
         if (stats) {
             exseq_stats st;
             st.chunks = nch;
@@ -2732,6 +2771,26 @@ int launch_ssim_exact(const SsimParams &sp, double *out, void *ws, hipStream_t s
     a.chunk_base[0] = 0;
     a.chunk_base[1] = (uint32_t)padded_chunks(n);
     return launch_batch_src(a, SsimTerms{sp}, ws, out, stream, stats, nullptr, 0);
+}
+
+int launch_interleaved(const double *x, size_t windows, int k, const double *inits, double *outs,
+                       float *means, void *ws, hipStream_t stream, uint32_t flags,
+                       exseq_stats *stats)
+{
+    BatchArgs a{};
+    a.count = k;
+    a.flags = flags;
+    a.interleave = 1;
+    a.means = means;
+    const uint32_t per = (uint32_t)padded_chunks(windows);
+    for (int j = 0; j < k; j++) {
+        a.x[j] = x ? x + j : nullptr;
+        a.n[j] = windows;
+        a.init[j] = inits ? inits[j] : 0.0;
+        a.chunk_base[j] = (uint32_t)j * per;
+    }
+    a.chunk_base[k] = (uint32_t)k * per;
+    return launch_batch_src(a, StridedTerms{(uint32_t)k}, ws, outs, stream, stats, nullptr, 0);
 }
 
 int launch_exact_sum(const double *x, size_t n, double init, double *out, void *ws,

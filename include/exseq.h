@@ -15,8 +15,8 @@
  * binade, and chunks that leave it are added term by term from the exact sum.
  *
  * Conventions for every call below:
- *  - Data pointers (`x`, `xs[k]`, `ref`, `dis`, `out*`, `ws`, `stats`) are
- *    DEVICE pointers on the current HIP device; `ns`, `xs` (the array of
+ *  - Data pointers (`x`, `xs[k]`, `ref`, `dis`, `out*`, `means`, `ws`, `stats`) are
+ *    DEVICE pointers on the current HIP device; `ns`, `inits`, `xs` (the array of
  *    pointers itself) and `shapes` are HOST arrays.  The caller owns every
  *    buffer; the library allocates nothing and never frees.
  *  - Every call is stream-ordered and non-blocking on `stream` (0 = the null
@@ -153,6 +153,29 @@ int exact_seq_sum_f64_batch(const double *const *xs, const size_t *ns,
                             const double *inits, size_t count, double *outs,
                             void *ws, size_t ws_bytes, exseq_stream_t stream,
                             uint32_t flags, exseq_stats *stats);
+
+/* ---------------------------------------------------------------------------
+ * exact_seq_sum_f64_interleaved
+ *   k independent sums over records of k doubles: for j < k,
+ *   outs[j] = ((inits[j] + x[j]) + x[j + k]) + ... + x[j + (windows-1) k],
+ *   each in fp64 RNE, bit exact, and, if `means` is not NULL,
+ *   means[j] = (float)(outs[j] / (double)windows) (IEEE division, then
+ *   round to nearest float).  ADR-1464 "float_ssim_cuda adds its frame sums
+ *   in the CPU's raster order, on the host", Context and Decision: a window
+ *   keeps four doubles (l*c*s, l, c, s), the four sums are independent, each
+ *   in index order, and the score is the float of the mean.
+ *   x: k * windows device doubles, record-major (record w holds x[w k] ..
+ *   x[w k + k - 1]).  inits: HOST array of k, or NULL for +0.0.  outs: k
+ *   device doubles.  means: nullable, k device floats (4-byte aligned).
+ *   stats: nullable device array of k.  1 <= k <= EXSEQ_INTERLEAVE_MAX.
+ *   windows == 0 writes inits (and their means, init / 0.0).
+ * ------------------------------------------------------------------------- */
+#define EXSEQ_INTERLEAVE_MAX 8
+size_t exact_seq_sum_f64_interleaved_workspace_size(size_t windows, int k);
+int exact_seq_sum_f64_interleaved(const double *x, size_t windows, int k,
+                                  const double *inits, double *outs, float *means,
+                                  void *ws, size_t ws_bytes, exseq_stream_t stream,
+                                  uint32_t flags, exseq_stats *stats);
 
 /* ---------------------------------------------------------------------------
  * ssim_term_and_sum

@@ -18,6 +18,10 @@ documentation the method comes from):
   the CPU's fp64 term in 64-bit integers and adds in the CPU's order",
   Context).  Plain C in ``ssim_ref.c``.
 * :func:`seq_sum_many` -- many independent loops (the pyramid batch).
+* :func:`seq_sum_interleaved` -- k loops over records of k doubles, one
+  accumulator per field, and each sum's float mean ``(float)(sum / windows)``
+  (ADR-1464 "float_ssim_cuda adds its frame sums in the CPU's raster order,
+  on the host", Context and Decision).  Plain C in ``seq_sum.c``.
 
 Every function is pinned by ``tests/test_oracle_pins.py`` against values that
 the pages and mathematics fix (closed forms, exact rational brute force, the
@@ -74,6 +78,9 @@ def load(path: str | None = None):
     lib.oracle_seq_sum_f64_many.restype = None
     lib.oracle_seq_sum_f64_many.argtypes = [dp, i64p, i64p, ctypes.c_int64,
                                             dp, dp]
+    lib.oracle_seq_sum_f64_interleaved.restype = None
+    lib.oracle_seq_sum_f64_interleaved.argtypes = [dp, ctypes.c_size_t, ctypes.c_int64, dp, dp,
+                                                   ctypes.POINTER(ctypes.c_float)]
     lib.oracle_box_moments.restype = None
     lib.oracle_box_moments.argtypes = [u8p, u8p, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_ssize_t, ctypes.c_int,
@@ -125,6 +132,21 @@ def seq_sum_many(arrays, inits=None, lib=None) -> np.ndarray:
     lib.oracle_seq_sum_f64_many(_dptr(flat), _i64ptr(offs), _i64ptr(ns),
                                 len(arrays), _dptr(ini), _dptr(out))
     return out
+
+
+def seq_sum_interleaved(x, k: int, inits=None, lib=None):
+    """k in-order sums over records of k doubles (``x`` flat, record-major,
+    ``k * windows`` values) and their float means -> (float64[k], float32[k])."""
+    lib = lib or load()
+    a = np.ascontiguousarray(x, dtype=np.float64).reshape(-1)
+    assert a.size % k == 0
+    windows = a.size // k
+    ini = np.zeros(k) if inits is None else np.ascontiguousarray(inits, dtype=np.float64)
+    out = np.zeros(k, dtype=np.float64)
+    means = np.zeros(k, dtype=np.float32)
+    lib.oracle_seq_sum_f64_interleaved(_dptr(a), windows, k, _dptr(ini), _dptr(out),
+                                       means.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+    return out, means
 
 
 def box_moments(ref, dis, radius: int = 3, lib=None):

@@ -37,3 +37,21 @@ void oracle_seq_sum_f64_many(const double *x, const int64_t *offsets,
     for (int64_t k = 0; k < count; k++)
         out[k] = oracle_seq_sum_f64(x + offsets[k], (size_t)ns[k], inits[k]);
 }
+
+/* k interleaved loops over records of k doubles, and the float mean of each
+ * (ADR-1464 "float_ssim_cuda adds its frame sums in the CPU's raster order,
+ * on the host", Context and Decision): one accumulator per field, started at
+ * inits[j]; the records are read in index order and each field is added into
+ * its own accumulator, so every accumulator sees its terms in index order;
+ * the mean is the double quotient by the record count rounded to float. */
+void oracle_seq_sum_f64_interleaved(const double *x, size_t windows, int64_t k,
+                                    const double *inits, double *out, float *means)
+{
+    for (int64_t j = 0; j < k; j++)
+        out[j] = inits[j];
+    for (size_t w = 0; w < windows; w++)
+        for (int64_t j = 0; j < k; j++)
+            out[j] += x[w * (size_t)k + (size_t)j];
+    for (int64_t j = 0; j < k; j++)
+        means[j] = (float)(out[j] / (double)windows);
+}

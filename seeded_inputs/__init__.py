@@ -111,3 +111,20 @@ def tie_suite(n: int = 4096, seed: int = 0) -> np.ndarray:
     stays in [1, 2) and every term with odd k is a tie at that scale."""
     k = rng(seed).integers(0, 8, n)
     return k.astype(np.float64) * 2.0 ** -53
+
+
+def lcs_records(windows: int = FRAME_N, seed: int = 0) -> np.ndarray:
+    """Records of four doubles per window, (l*c*s, l, c, s), shaped like an
+    SSIM pass that keeps the factors: l = 1 - |N(0, 0.02)|,
+    c = 1 - |N(0, 0.1)|, s = 1 - |N(0, 0.3)| clipped to [-1, 1], and their
+    fp64 product (l * c) * s.  Returned flat, record-major (4 * windows)."""
+    r = rng(seed)
+    l = 1.0 - np.abs(r.normal(0.0, 0.02, windows))
+    c = 1.0 - np.abs(r.normal(0.0, 0.1, windows))
+    s = np.clip(1.0 - np.abs(r.normal(0.0, 0.3, windows)), -1.0, 1.0)
+    rec = np.empty((windows, 4), dtype=np.float64)
+    rec[:, 0] = (l * c) * s
+    rec[:, 1] = l
+    rec[:, 2] = c
+    rec[:, 3] = s
+    return rec.reshape(-1)
