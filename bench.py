@@ -164,6 +164,16 @@ def time_configs(ex, si, torch, dev, seed, reps=30):
                                "gbs": n3 * 8 / (ms * 1e-3) / 1e9,
                                "buffers_rotated": 4}
 
+    x7 = torch.from_numpy(-si.tie_heavy(si.FRAME_N, seed)).to(dev)
+    o7 = torch.empty(1, dtype=torch.float64, device=dev)
+    w7 = ex.workspace(ex.lib().exact_seq_sum_f64_workspace_size(si.FRAME_N), dev)
+    ms = timed(lambda: ex.exact_seq_sum(x7, out=o7, ws=w7), reps)
+    res["negated_tie_heavy_3840x2160"] = {"us_per_sum": ms * 1e3,
+                                          "terms_per_s": si.FRAME_N / (ms * 1e-3),
+                                          "note": "the frame's terms negated: a negative "
+                                                  "running sum crossing negative binades"}
+    del x7
+
     ref, dis = si.frame_pair(si.FRAME_H, si.FRAME_W, seed)
     r4 = torch.from_numpy(ref).to(dev)
     d4 = torch.from_numpy(dis).to(dev)

@@ -1910,18 +1910,21 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
     __builtin_amdgcn_s_setprio(3);
     int buf = 0;
     const int nk = (int)(nch - c0 < (uint32_t)CPB ? nch - c0 : (uint32_t)CPB);
-    // Crossings: every chunk expected to cross into the next binade up, with
-    // a plan for its binade and no non-finite term, gets one located --
-    // except in a sum's first tile, which has the exact sum before its
-    // chunks early (the head's) and adds such chunks by the rounds of the
+    // Crossings: every chunk expected to cross into the next binade up in
+    // magnitude, with a plan for its binade and no non-finite term, gets one
+    // located -- except in a sum's first tile, which has the exact sum before
+    // its chunks early (the head's) and adds such chunks by the rounds of the
     // resolve instead.  (A run clamped for spanning more than its binade is
-    // no obstacle: the crossing's own checks cover each binade.)
+    // no obstacle: the crossing's own checks cover each binade.)  A negative
+    // running sum is the mirror image: round to nearest even is symmetric in
+    // sign, the plan's sign bit mirrors every term (term_inc), and key + 1 is
+    // the next binade of the same sign.
     uint32_t want = 0u;
 #pragma unroll
     for (int k = 0; k < CPB; k++) {
         const uint32_t fl = L.join[k].flags;
         if (k < nk && c0 != 0 && !L.reused && L.cross[k] && key_has_fast_path(key[k]) &&
-            key[k] == key_of(L.pk[k]) && !(key[k] & 0x800u) && key_has_fast_path(key[k] + 1u) &&
+            key[k] == key_of(L.pk[k]) && key_has_fast_path(key[k] + 1u) &&
             !(fl & kFlagNonFinite))
             want |= 1u << k;
     }
