@@ -46,6 +46,8 @@ struct SsimParams {
     int radius;
     double c1, c2;
     double *out_terms;
+    int64_t *out_weight_sum;  // nullable: written with the sum
+    int64_t weight_sum;
 };
 
 // Up to kMaxBatch independent sums, passed to the kernels by value.  Sum k

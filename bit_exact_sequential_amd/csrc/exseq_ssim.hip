@@ -13,7 +13,6 @@
 
 namespace exseq {
 
-__global__ void write_i64_kernel(int64_t *out, int64_t v) { out[0] = v; }
 
 static int64_t line_sum(int len, int radius)
 {
@@ -41,13 +40,10 @@ int launch_ssim_sum(const uint8_t *ref, const uint8_t *dis, int width, int heigh
                     int64_t *out_weight_sum, double *out_terms, void *ws, hipStream_t stream,
                     uint32_t flags, exseq_stats *stats)
 {
-    if (out_weight_sum) {
-        const int64_t wsum = line_sum(height, radius) * line_sum(width, radius);
-        hipLaunchKernelGGL(write_i64_kernel, dim3(1), dim3(1), 0, stream, out_weight_sum, wsum);
-        if (hipGetLastError() != hipSuccess)
-            return EXSEQ_EHIP;
-    }
     SsimParams sp;
+    // the frame's weight sum, a product of line sums, written by the walk
+    sp.out_weight_sum = out_weight_sum;
+    sp.weight_sum = line_sum(height, radius) * line_sum(width, radius);
     sp.ref = ref;
     sp.dis = dis;
     sp.width = width;

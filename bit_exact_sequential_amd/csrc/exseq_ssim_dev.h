@@ -247,6 +247,13 @@ struct SsimTerms {
         return f;
     }
 
+    // Beside the sum: the frame's weight sum, if asked for.
+    __device__ __forceinline__ void done() const
+    {
+        if (p.out_weight_sum)
+            *p.out_weight_sum = p.weight_sum;
+    }
+
     // The terms of chunk c, also written to the caller's plane if asked for.
     __device__ __forceinline__ void keep(size_t c, const Four &f) const
     {

@@ -141,6 +141,7 @@ struct PlainTerms {
         return load_four(a.x[s], a.n[s], c * kChunk + 4 * (size_t)threadIdx.x, true);
     }
     __device__ __forceinline__ void keep(size_t, const Four &) const {}
+    __device__ __forceinline__ void done() const {}
 };
 
 // Every k-th double from x[s]: one field of records of k doubles, such as the
@@ -164,6 +165,7 @@ struct StridedTerms {
         return f;
     }
     __device__ __forceinline__ void keep(size_t, const Four &) const {}
+    __device__ __forceinline__ void done() const {}
 };
 
 // Fixed-shape tree sum of a chunk: ((v0+v1)+(v2+v3)) per lane, the wave in a
@@ -2547,6 +2549,7 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, Src src
     }
     if (t == 0) {
         outs[s] = S;
+        src.done();  // what the source writes beside the sum
         if (a.means)
             a.means[s] = (float)(S / (double)n);  // ADR-1464: (float)(sum / windows)
         if (stats) {
