@@ -51,6 +51,20 @@ __device__ __forceinline__ double ssim_term_dev(int64_t x, int64_t y, int64_t x2
 //      of it, on the same row), and the term.  The window sums are exact
 //      integers, so sliding them along a row (adding the column that enters,
 //      subtracting the one that leaves) gives the same sums in any order.
+// Four words w[u] of four bytes b(u, e) -> t[e] holding b(0, e) .. b(3, e)
+// (byte e of every word, in word order), by byte permutes.
+__device__ __forceinline__ void transpose4(const uint32_t *w, uint32_t *t)
+{
+    const uint32_t lo01 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);  // b00 b10 b01 b11
+    const uint32_t hi01 = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);  // b02 b12 b03 b13
+    const uint32_t lo23 = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
+    t[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+    t[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+    t[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+    t[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+}
+
 struct SsimTerms {
     SsimParams p;
     static constexpr int kMaxRadius = 15;
@@ -84,10 +98,10 @@ struct SsimTerms {
             const int m1 = (q0 + nq - 1) / 4;
             for (int m = m0 + t; m <= m1; m += 256) {
                 const int q = 4 * m;  // first position of the group
-                int acc[5][4];
+                uint32_t acc[5][4];
 #pragma unroll
                 for (int e = 0; e < 4; e++)
-                    acc[0][e] = acc[1][e] = acc[2][e] = acc[3][e] = acc[4][e] = 0;
+                    acc[0][e] = acc[1][e] = acc[2][e] = acc[3][e] = acc[4][e] = 0u;
                 if (q >= 0 && q < n) {
                     // (the first group may start up to 3 positions before q0)
                     int i = iq0;
@@ -112,18 +126,20 @@ struct SsimTerms {
                             vr[u] = in ? pr[(ptrdiff_t)(row0 - a0 + u) * sw] : 0u;
                             vd[u] = in ? pd[(ptrdiff_t)(row0 - a0 + u) * sw] : 0u;
                         }
+                        // each position's four row bytes in one word (a
+                        // 4 x 4 byte transpose), then its moments by 4-way
+                        // byte dot products: every sum is an exact integer
+                        // below 961 * 255^2 < 2^32, in any order
+                        uint32_t tx[4], ty[4];
+                        transpose4(vr, tx);
+                        transpose4(vd, ty);
 #pragma unroll
-                        for (int u = 0; u < 4; u++) {
-#pragma unroll
-                            for (int e = 0; e < 4; e++) {
-                                const int x = (int)((vr[u] >> (8 * e)) & 0xFFu);
-                                const int y = (int)((vd[u] >> (8 * e)) & 0xFFu);
-                                acc[0][e] += x;
-                                acc[1][e] += y;
-                                acc[2][e] += x * x;
-                                acc[3][e] += y * y;
-                                acc[4][e] += x * y;
-                            }
+                        for (int e = 0; e < 4; e++) {
+                            acc[0][e] = __builtin_amdgcn_udot4(tx[e], 0x01010101u, acc[0][e], false);
+                            acc[1][e] = __builtin_amdgcn_udot4(ty[e], 0x01010101u, acc[1][e], false);
+                            acc[2][e] = __builtin_amdgcn_udot4(tx[e], tx[e], acc[2][e], false);
+                            acc[3][e] = __builtin_amdgcn_udot4(ty[e], ty[e], acc[3][e], false);
+                            acc[4][e] = __builtin_amdgcn_udot4(tx[e], ty[e], acc[4][e], false);
                         }
                     }
                 }
@@ -131,11 +147,11 @@ struct SsimTerms {
                 for (int e = 0; e < 4; e++) {
                     const int k = q + e - q0;
                     if (k >= 0 && k < nq) {
-                        lds[k] = acc[0][e];
-                        lds[kSpan + k] = acc[1][e];
-                        lds[2 * kSpan + k] = acc[2][e];
-                        lds[3 * kSpan + k] = acc[3][e];
-                        lds[4 * kSpan + k] = acc[4][e];
+                        lds[k] = (int)acc[0][e];
+                        lds[kSpan + k] = (int)acc[1][e];
+                        lds[2 * kSpan + k] = (int)acc[2][e];
+                        lds[3 * kSpan + k] = (int)acc[3][e];
+                        lds[4 * kSpan + k] = (int)acc[4][e];
                     }
                 }
             }
