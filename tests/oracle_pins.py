@@ -26,7 +26,12 @@ Sources of truth (none of them is the oracle itself):
 * for the window moments: a summed-area table (a second integer method);
 * for the weight sum: the product of the two line sums (ADR-1443
   "integer_ssim_sycl computes the CPU's fp64 term ...", Decision, the weight
-  is not a plane).
+  is not a plane);
+* for the interleaved sums and their float means (ADR-1464 "float_ssim_cuda
+  adds its frame sums in the CPU's raster order, on the host", Decision):
+  the integer IEEE model per field, the exact quotient rounded to binary64
+  and then to binary32 with Python integers, and float roundings that are
+  IEEE facts (midpoints, 1/3, division by zero).
 """
 
 from __future__ import annotations
@@ -403,7 +408,70 @@ def pin_frame_sum(lib, shapes=((1, 1), (2, 2), (3, 4), (5, 7), (9, 9), (16, 16),
             assert abs(Fraction(terms[i, j]) - want_t) <= abs(want_t) * Fraction(64 * 2.0 ** -52)
 
 
+def f32_round(q):
+    """A rational rounded to the nearest binary32, ties to even (Python
+    integers only; subnormals included, overflow to infinity)."""
+    q = Fraction(q)
+    if q == 0:
+        return 0.0
+    sign = -1.0 if q < 0 else 1.0
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, -126)
+    ulp = Fraction(2) ** (e - 23)
+    m, r = divmod(a, ulp)
+    m = int(m)
+    if r > ulp / 2 or (r == ulp / 2 and m % 2 == 1):
+        m += 1
+    v = m * ulp
+    if v >= Fraction(2) ** 128:
+        return sign * math.inf
+    return sign * float(v)
+
+
+def pin_interleaved_brute_force(lib):
+    """k loops over records of k doubles (one accumulator per field, each in
+    index order) and their float means, against the integer IEEE model per
+    field and the exact quotient rounded twice (to binary64, then to
+    binary32) -- an evaluation that shares nothing with the C loop.
+    Tie-heavy fields make any other order of adds, or a swap of fields, give
+    other bits."""
+    cases = [(1, 1), (3, 2), (17, 4), (64, 3), (200, 8), (1000, 4)]
+    for windows, k in cases:
+        x = np.empty(windows * k)
+        for j in range(k):
+            if j % 2 == 0:
+                x[j::k] = si.tie_suite(windows, 11 * j + windows)
+            else:
+                x[j::k] = si.uniform(windows, 7 * j + windows) * (j + 1)
+        x[0] = 1.0
+        inits = np.array([0.0, 1.0, -0.5, 2.0, 0.0, 1.0, 0.25, 3.0][:k])
+        sums, means = oracle.seq_sum_interleaved(x, k, inits, lib=lib)
+        for j in range(k):
+            want = ieee.seq_sum(list(x[j::k]), float(inits[j]))
+            assert same(sums[j], want), (windows, k, j)
+            q = ieee.round_fraction(Fraction(want) / windows)
+            assert struct.pack("<f", float(means[j])) == struct.pack("<f", f32_round(q)), \
+                (windows, k, j)
+
+
+def pin_interleaved_mean_textbook(lib):
+    """Means whose float is an IEEE fact: 1 + 2^-24 is the midpoint of 1 and
+    1 + 2^-23 and rounds to the even 1; 1 + 3 * 2^-24 rounds up to the even
+    1 + 2^-22; 1/3 is 0x3EAAAAAB; x / 0 is NaN for x = 0 and inf for x > 0."""
+    _, means = oracle.seq_sum_interleaved([1 + 2.0 ** -24, 1 + 3 * 2.0 ** -24, -1.0], 3, lib=lib)
+    assert list(means) == [1.0, 1 + 2.0 ** -22, -1.0]
+    sums, means = oracle.seq_sum_interleaved([0.5, 0.25, 0.25], 1, lib=lib)
+    assert sums[0] == 1.0
+    assert struct.pack(">f", float(means[0])).hex() == "3eaaaaab"
+    _, means = oracle.seq_sum_interleaved(np.zeros(0), 2, [0.0, 1.0], lib=lib)
+    assert math.isnan(float(means[0])) and float(means[1]) == math.inf
+
+
 LOOP_PINS = (pin_closed_forms, pin_binade_identity, pin_cpython_reduce,
              pin_seq_sum_many, pin_exhaustive_short)
 TERM_PINS = (pin_box_moments, pin_term_textbook, pin_term_identical_windows,
              pin_term_per_operation, pin_frame_sum)
+INTERLEAVE_PINS = (pin_interleaved_brute_force, pin_interleaved_mean_textbook)

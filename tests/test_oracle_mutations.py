@@ -2,7 +2,8 @@
 at least one pin to catch it.  This shows the pins constrain every part of the
 oracle: the loop's bounds, sign, start value, precision and order; the term's
 operands, signs, constants and rounding; the moments' window and products;
-the frame sum's raster order."""
+the frame sum's raster order; the interleaved sums' fields, start values,
+record count and the float mean's rounding."""
 
 import os
 import shutil
@@ -42,6 +43,21 @@ TERM_MUTANTS = {
     "untruncated_weight": ("mw[k] = sw;", "mw[k] = (2 * radius + 1) * (2 * radius + 1);"),
     "column_order_sum": ("double s = 0.0;\n    int64_t ws = 0;\n    for (int i = 0; i < height; i++) {",
                          "double s = 0.0;\n    int64_t ws = 0;\n    for (int i = height - 1; i >= 0; i--) {"),
+}
+
+
+INTERLEAVE_MUTANTS = {
+    "swapped_fields": ("out[j] += x[w * (size_t)k + (size_t)j];",
+                       "out[j] += x[w * (size_t)k + (size_t)(k - 1 - j)];"),
+    "float_division": ("means[j] = (float)(out[j] / (double)windows);",
+                       "means[j] = (float)out[j] / (float)windows;"),
+    "ignore_init": ("out[j] = inits[j];", "out[j] = 0.0;"),
+    "drop_last_record": ("for (size_t w = 0; w < windows; w++)",
+                         "for (size_t w = 0; w + 1 < windows; w++)"),
+    "float_terms": ("out[j] += x[w * (size_t)k + (size_t)j];",
+                    "out[j] += (float)x[w * (size_t)k + (size_t)j];"),
+    "mean_by_k": ("means[j] = (float)(out[j] / (double)windows);",
+                  "means[j] = (float)(out[j] / (double)(windows * (size_t)k));"),
 }
 
 
@@ -97,3 +113,10 @@ def test_contracted_build_is_caught(tmp_path):
     lib = _build_mutant(tmp_path, "ssim_ref.c", ("double w_d", "double w_d"),
                         extra_flags=("-ffp-contract=fast", "-mfma", "-O3"))
     assert _caught(lib, (P.pin_term_per_operation,)), "contraction not detected"
+
+
+@pytest.mark.parametrize("name", sorted(INTERLEAVE_MUTANTS))
+def test_interleave_mutant_is_caught(tmp_path, name):
+    lib = _build_mutant(tmp_path, "seq_sum.c", INTERLEAVE_MUTANTS[name])
+    caught = _caught(lib, P.INTERLEAVE_PINS)
+    assert caught, "mutant %s passed every interleave pin" % name

@@ -125,64 +125,10 @@ def test_cpython_reduce_full_size(lib):
         assert P.same(oracle.seq_sum(x, lib=lib), want)
 
 
-def _f32_round(q):
-    """A rational rounded to the nearest binary32, ties to even (Python
-    integers only; subnormals included, overflow to infinity)."""
-    from fractions import Fraction
-    q = Fraction(q)
-    if q == 0:
-        return 0.0
-    sign = -1.0 if q < 0 else 1.0
-    a = abs(q)
-    e = a.numerator.bit_length() - a.denominator.bit_length()
-    if Fraction(2) ** e > a:
-        e -= 1
-    e = max(e, -126)
-    ulp = Fraction(2) ** (e - 23)
-    m, r = divmod(a, ulp)
-    m = int(m)
-    if r > ulp / 2 or (r == ulp / 2 and m % 2 == 1):
-        m += 1
-    v = m * ulp
-    if v >= Fraction(2) ** 128:
-        return sign * math.inf
-    return sign * float(v)
-
 
 def test_interleaved_brute_force(lib):
-    """k loops over records of k doubles (ADR-1464 Decision: one accumulator
-    per field, each in index order) and their float means, against the
-    integer IEEE model per field and the exact quotient rounded twice (to
-    binary64, then to binary32) -- an evaluation that shares nothing with
-    the C loop.  Tie-heavy fields make any other order of adds, or a swap of
-    fields, give other bits."""
-    from fractions import Fraction
-    cases = [(1, 1), (3, 2), (17, 4), (64, 3), (200, 8), (1000, 4)]
-    for windows, k in cases:
-        x = np.empty(windows * k)
-        for j in range(k):
-            if j % 2 == 0:
-                x[j::k] = si.tie_suite(windows, 11 * j + windows)
-            else:
-                x[j::k] = si.uniform(windows, 7 * j + windows) * (j + 1)
-        x[0] = 1.0
-        inits = np.array([0.0, 1.0, -0.5, 2.0, 0.0, 1.0, 0.25, 3.0][:k])
-        sums, means = oracle.seq_sum_interleaved(x, k, inits, lib=lib)
-        for j in range(k):
-            want = ieee.seq_sum(list(x[j::k]), float(inits[j]))
-            assert struct.pack("<d", sums[j]) == struct.pack("<d", want), (windows, k, j)
-            q = ieee.round_fraction(Fraction(want) / windows)
-            assert struct.pack("<f", float(means[j])) == struct.pack("<f", _f32_round(q)), (windows, k, j)
+    P.pin_interleaved_brute_force(lib)
 
 
 def test_interleaved_mean_textbook(lib):
-    """Means whose float is an IEEE fact: 1 + 2^-24 is the midpoint of 1 and
-    1 + 2^-23 and rounds to the even 1; 1 + 3 * 2^-24 rounds up to the even
-    1 + 2^-22; 1/3 is 0x3EAAAAAB; x / 0 is NaN for x = 0 and inf for x > 0."""
-    sums, means = oracle.seq_sum_interleaved([1 + 2.0 ** -24, 1 + 3 * 2.0 ** -24, -1.0], 3, lib=lib)
-    assert list(means) == [1.0, 1 + 2.0 ** -22, -1.0]
-    sums, means = oracle.seq_sum_interleaved([0.5, 0.25, 0.25], 1, lib=lib)
-    assert sums[0] == 1.0
-    assert struct.pack(">f", float(means[0])).hex() == "3eaaaaab"
-    sums, means = oracle.seq_sum_interleaved(np.zeros(0), 2, [0.0, 1.0], lib=lib)
-    assert math.isnan(float(means[0])) and float(means[1]) == math.inf
+    P.pin_interleaved_mean_textbook(lib)
