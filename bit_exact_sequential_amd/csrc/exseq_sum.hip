@@ -1197,7 +1197,8 @@ struct CrossLds {
 // from m_est or cannot have one.  On success out[] holds the published
 // words in every lane.  Three barriers.
 __device__ __forceinline__ bool crossing_find(const Four &f, int len, uint32_t key, int64_t m_est,
-                                              WalkLds &sh, CrossLds &xl, int &buf, uint64_t *out)
+                                              bool down, WalkLds &sh, CrossLds &xl, int &buf,
+                                              uint64_t *out)
 {
     const int t = threadIdx.x, lane = lane_id(), wave = wave_id();
     const int scale = 1075 - (int)(key & 0x7FFu);
@@ -1218,12 +1219,14 @@ __device__ __forceinline__ bool crossing_find(const Four &f, int len, uint32_t k
     }
     const Pair pre = block_scan_total(acc[kPer - 1], sh, buf, tot);
     buf ^= 1;
-    // the first term whose count from m_est reaches 2^53
+    // the first term whose count from m_est reaches 2^53 (or, downwards,
+    // falls below 2^52)
     int firstk = -1;
 #pragma unroll
     for (int i = kPer - 1; i >= 0; i--) {
         const Pair pe = compose(pre, acc[i]);
-        if (kPer * t + i < len && m_est + pair_at(pe, m_est) >= kCountHi)
+        const int64_t ce = m_est + pair_at(pe, m_est);
+        if (kPer * t + i < len && (down ? ce < kCountLo : ce >= kCountHi))
             firstk = i;
     }
     const uint64_t b = __ballot(firstk >= 0), bb = __ballot(bad1);
@@ -1275,9 +1278,9 @@ __device__ __forceinline__ bool crossing_find(const Four &f, int len, uint32_t k
             phi = mx > phi ? mx : phi;
         }
     }
-    // Under the next binade: the whole chunk, and the terms after j as a run
-    // with its prefix bounds.
-    const uint32_t key2 = key + 1u;
+    // Under the next binade (up, or down): the whole chunk, and the terms
+    // after j as a run with its prefix bounds.
+    const uint32_t key2 = down ? key - 1u : key + 1u;
     const int scale2 = 1075 - (int)(key2 & 0x7FFu);
     const bool sgn2 = (key2 >> 11) & 1u;
     bool bad2 = false;
@@ -1345,12 +1348,14 @@ __device__ __forceinline__ bool crossing_find(const Four &f, int len, uint32_t k
 // w[kXsuf] and w[kXwhole] of a chunk without one may also take in runs that
 // follow the chunk in the next binade: every success applies one of them.
 __device__ __forceinline__ int crossing_apply(const uint64_t *w, int len, uint32_t key, uint32_t fl,
-                                              double &S, int &pos)
+                                              bool down, double &S, int &pos)
 {
-    const bool neg = (fl & kFlagNeg) != 0;
+    // a downward crossing has falling counts: every bound is checked
+    const bool neg = (fl & kFlagNeg) != 0 || down;
+    const uint32_t key2 = down ? key - 1u : key + 1u;
     const uint32_t ks = key_of(S);
     const int64_t m = count_of(S);
-    if (ks == key + 1u) {
+    if (ks == key2) {
         // the crossing came before the chunk: all of it in the next binade
         if (neg || !key_has_fast_path(ks))
             return 0;
@@ -1365,7 +1370,7 @@ __device__ __forceinline__ int crossing_apply(const uint64_t *w, int len, uint32
     const int j = (int)dec_i64(w[kXj]);
     const int64_t cb = j == 0 ? m : m + pair_at(rec_unpack(dec_i64(w[kXpj1])), m);
     const int64_t cj = m + pair_at(rec_unpack(dec_i64(w[kXpj])), m);
-    if (j >= len || cb > kCountHi - 1 || cj < kCountHi)
+    if (j >= len || (down ? cb < kCountLo || cj >= kCountLo : cb > kCountHi - 1 || cj < kCountHi))
         return 0;  // the crossing is elsewhere for this start
     if (neg && (m + dec_i64(w[kXpreLo]) < kCountLo + 1 || m + dec_i64(w[kXpreHi]) > kCountHi - 1))
         return 0;  // some prefix before it leaves the binade
@@ -1374,7 +1379,7 @@ __device__ __forceinline__ int crossing_apply(const uint64_t *w, int len, uint32
     pos = j + 1;
     const uint32_t k2 = key_of(S);
     const int64_t m2 = count_of(S);
-    if (k2 != key + 1u || !key_has_fast_path(k2))
+    if (k2 != key2 || !key_has_fast_path(k2))
         return 2;
     const Pair sp = rec_unpack(dec_i64(w[kXsuf]));
     if (!run_applies(m2, sp, dec_i64(w[kXsufLo]), dec_i64(w[kXsufHi]), neg ? kFlagNeg : 0u))
@@ -1447,17 +1452,19 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t v)
 
 constexpr int kIrrPer = 4 + kCrossWords;       // bank words per chunk
 constexpr uint64_t kIrrCross = 1ULL << 40;     // bank meta: a crossing is located
+constexpr uint64_t kIrrDown = 1ULL << 41;      // ... into the binade below
 static_assert(4 + kIrrPer * kTileMax <= 64, "the bank fits one wave");
 
 // One irregular tile's O(1) step from the exact sum S before it: the run A
 // (the regular tiles since the irregular tile before it, then its chunks
 // before the crossing; binade akey, none if 0), then the crossing (w, in a
-// chunk of len terms, binade xkey, kFlagNeg in xfl), whose rest-of-chunk run
-// takes in the chunks after it.  False, with S unchanged, where a check fails
-// for this S; the tile then adds chunk by chunk.
+// chunk of len terms, binade xkey, kFlagNeg in xfl, into the binade above or,
+// with xdown, below), whose rest-of-chunk run takes in the chunks after it.
+// False, with S unchanged, where a check fails for this S; the tile then adds
+// chunk by chunk.
 __device__ __forceinline__ bool tile_step(uint32_t akey, const Run &A, bool hasx,
                                           const uint64_t *w, int len, uint32_t xkey, uint32_t xfl,
-                                          double &S)
+                                          bool xdown, double &S)
 {
     double T = S;
     if (akey != 0u) {
@@ -1469,7 +1476,7 @@ __device__ __forceinline__ bool tile_step(uint32_t akey, const Run &A, bool hasx
     }
     if (hasx) {
         int pos = 0;
-        const bool good = crossing_apply(w, len, xkey, xfl, T, pos) == 1;
+        const bool good = crossing_apply(w, len, xkey, xfl, xdown, T, pos) == 1;
         T = bitsd(uniform_u64(dbits(T)));
         if (!good)
             return false;
@@ -1480,7 +1487,8 @@ __device__ __forceinline__ bool tile_step(uint32_t akey, const Run &A, bool hasx
 
 // A published step (kRecWords words per tile, all nonzero once written):
 //   0: kRecPresent | akey | xkey << 12 | has crossing << 24 |
-//      A's flags >> 14 << 32 | crossing kFlagNeg << 35 | (r1 - r0 + 1) << 36
+//      A's flags >> 14 << 32 | crossing kFlagNeg << 35 | (r1 - r0 + 1) << 36 |
+//      crossing downwards << 38
 //   1..3: A's r0, lo, hi;  4: the irregular tile before it;  5: the crossing
 //   chunk's length;  6..15: the crossing's words  (integers xor kIntTag)
 constexpr int kRecWords = 16;
@@ -1490,14 +1498,14 @@ constexpr int kCatch = 4;  // records a wave holds while it waits (16 lanes each
 // The word of the record a lane i < kRecWords of the publishing wave writes.
 __device__ __forceinline__ uint64_t rec_word(int i, uint32_t akey, const Run &A, bool hasx,
                                              const uint64_t *w, int len, uint32_t xkey,
-                                             uint32_t xfl, int64_t xp)
+                                             uint32_t xfl, bool xdown, int64_t xp)
 {
     uint64_t v = enc_i64(0);
     if (i == 0)
         v = kRecPresent | (uint64_t)(akey & kKeyMask) | ((uint64_t)(xkey & kKeyMask) << 12) |
             ((uint64_t)hasx << 24) |
             ((uint64_t)((A.flags >> 14) & 7u) << 32) | ((uint64_t)((xfl & kFlagNeg) != 0) << 35) |
-            ((uint64_t)(A.p.r1 - A.p.r0 + 1) << 36);
+            ((uint64_t)(A.p.r1 - A.p.r0 + 1) << 36) | ((uint64_t)xdown << 38);
     else if (i == 1)
         v = enc_i64(A.p.r0);
     else if (i == 2)
@@ -1532,7 +1540,7 @@ __device__ __forceinline__ bool rec_step(uint64_t rw, int d, double &S)
         w[k] = (uint64_t)readlane_i64((int64_t)rw, b + 6 + k);
     const int len = (int)dec_i64((uint64_t)readlane_i64((int64_t)rw, b + 5));
     return tile_step((uint32_t)m & kKeyMask, A, hasx, w, len, (uint32_t)(m >> 12) & kKeyMask,
-                     ((m >> 35) & 1u) ? kFlagNeg : 0u, S);
+                     ((m >> 35) & 1u) ? kFlagNeg : 0u, ((m >> 38) & 1u) != 0, S);
 }
 
 // The exact sum after irregular tile xp of a sum (whose first tile is tile tb
@@ -1625,6 +1633,7 @@ struct TileLds {
     double pk[CPB];              // planned prefix before each chunk
     uint32_t key[CPB];           // planned binade of each chunk (0: none)
     uint32_t cross[CPB];         // the plan does not keep the chunk in its binade
+    uint32_t down[CPB];          // ... and takes it into the binade below (same sign)
     uint64_t xw[CPB][kCrossWords];  // located crossings
     uint64_t word;               // a word read by one lane for all
     uint32_t reused;             // the tile took its binade from a kept plan
@@ -1776,6 +1785,8 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
             L.pk[lane] = pk;
             L.key[lane] = rkey ? rkey : plan_key(pk, a.flags);
             L.cross[lane] = !rkey && key_of(pk + tk) != key_of(pk);
+            L.down[lane] = ((key_of(pk + tk) ^ key_of(pk)) & 0x800u) == 0u &&
+                           (key_of(pk + tk) & 0x7FFu) < (key_of(pk) & 0x7FFu);
         }
     }
     __syncthreads();
@@ -1926,7 +1937,8 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
     for (int k = 0; k < CPB; k++) {
         const uint32_t fl = L.join[k].flags;
         if (k < nk && c0 != 0 && !L.reused && L.cross[k] && key_has_fast_path(key[k]) &&
-            key[k] == key_of(L.pk[k]) && key_has_fast_path(key[k] + 1u) &&
+            key[k] == key_of(L.pk[k]) &&
+            key_has_fast_path(L.down[k] ? key[k] - 1u : key[k] + 1u) &&
             !(fl & kFlagNonFinite))
             want |= 1u << k;
     }
@@ -1942,7 +1954,7 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
         const size_t b = (size_t)(c0 + k) * kChunk;
         const int len = (int)(n - b < (size_t)kChunk ? n - b : (size_t)kChunk);
         uint64_t w[kCrossWords];
-        if (crossing_find(fr, len, L.key[k], count_of(L.pk[k]), sh, xl, buf, w)) {
+        if (crossing_find(fr, len, L.key[k], count_of(L.pk[k]), L.down[k] != 0u, sh, xl, buf, w)) {
             found |= 1u << k;
             if (t == 0) {
 #pragma unroll
@@ -1967,7 +1979,8 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
                 bank = (uint64_t)(L.key[k] & kKeyMask) |
                        ((uint64_t)(r.p.r1 - r.p.r0 + 1) << kDrShift) |
                        (uint64_t)(r.flags & (kFlagNeg | kFlagBad | kFlagNonFinite)) |
-                       (((found >> k) & 1u) ? kIrrCross : 0ULL);
+                       (((found >> k) & 1u) ? kIrrCross : 0ULL) |
+                       (((found >> k) & 1u) && L.down[k] ? kIrrDown : 0ULL);
             else if (i == 1)
                 bank = (uint64_t)r.p.r0;
             else if (i == 2)
@@ -2038,6 +2051,7 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
         }
         uint32_t xkey = 0u;
         uint32_t xfl = 0u;  // kFlagNeg: a negative term in the crossing or after it
+        bool xdown = false;  // the crossing goes into the binade below
         if (fast && kx < nk) {
             const int base = 4 + kIrrPer * kx;
             const uint64_t xm = (uint64_t)readlane_i64((int64_t)bank, base);
@@ -2046,6 +2060,7 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
             for (int i = 0; i < kCrossWords; i++)
                 xw[i] = (uint64_t)readlane_i64((int64_t)bank, base + 4 + i);
             xfl = (uint32_t)xm & kFlagNeg;
+            xdown = (xm & kIrrDown) != 0;
             fast = akey == 0u || akey == xkey;
             // the chunks after the crossing (all in the next binade) folded
             // into its rest-of-chunk run, bounds and all, so that a negative
@@ -2056,7 +2071,8 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
                 const int b2 = 4 + kIrrPer * k;
                 const uint64_t cm = (uint64_t)readlane_i64((int64_t)bank, b2);
                 const int64_t r0 = readlane_i64((int64_t)bank, b2 + 1);
-                fast = ((uint32_t)cm & kKeyMask) == xkey + 1u && !(cm & kIrrCross) &&
+                fast = ((uint32_t)cm & kKeyMask) == (xdown ? xkey - 1u : xkey + 1u) &&
+                       !(cm & kIrrCross) &&
                        !((uint32_t)cm & (kFlagBad | kFlagNonFinite));
                 const Run q{Pair{r0, r0 + (int64_t)((cm >> kDrShift) & 3u) - 1},
                             readlane_i64((int64_t)bank, b2 + 2), readlane_i64((int64_t)bank, b2 + 3),
@@ -2080,7 +2096,7 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
         // the tile's step, for the tiles after it that catch up through it
         if (ok && fast && c0 != 0 && wave == 0 && lane < kRecWords)
             store_relaxed_u64(ch.rec + kRecWords * (size_t)(tb + tl) + lane,
-                              rec_word(lane, akey, A, kx < nk, xw, xlen, xkey, xfl, xp));
+                              rec_word(lane, akey, A, kx < nk, xw, xlen, xkey, xfl, xdown, xp));
         if (ok) {
             // every wave waits on its own (no barrier between the word
             // arriving and the steps that use it)
@@ -2102,7 +2118,7 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
             ok = w > kInclFailed;  // 0: the wait timed out
             if (ok)
                 S = bitsd(w ^ kInclXor);
-            if (ok && fast && tile_step(akey, A, kx < nk, xw, xlen, xkey, xfl, S))
+            if (ok && fast && tile_step(akey, A, kx < nk, xw, xlen, xkey, xfl, xdown, S))
                 done = true;
             if (ok && !done && !rnone) {
                 const uint32_t ks = key_of(S);
@@ -2144,7 +2160,7 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
 #pragma unroll
                     for (int i = 0; i < kCrossWords; i++)
                         xw[i] = (uint64_t)readlane_i64((int64_t)bank, base + 4 + i);
-                    xr = crossing_apply(xw, len, kk, (uint32_t)cm, S, pos);
+                    xr = crossing_apply(xw, len, kk, (uint32_t)cm, (cm & kIrrDown) != 0, S, pos);
                     S = bitsd(uniform_u64(dbits(S)));
                 }
                 if (xr == 1)
