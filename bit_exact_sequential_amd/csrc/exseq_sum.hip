@@ -428,11 +428,12 @@ __device__ __forceinline__ void wave_runs(const Four *f, const uint32_t *key,
 {
     uint64_t v[CPB];
     bool easy = true;
+    uint32_t negs = 0u;  // chunk k's increments are all <= 0 (bit k)
 #pragma unroll
     for (int k = 0; k < CPB; k++) {
         const int scale = 1075 - (int)(key[k] & 0x7FFu);
         const uint32_t flip = (key[k] & 0x800u) ? 0x80000000u : 0u;  // mirror a negative plan
-        bool odd = false;
+        bool tie = false, notpos = false, notneg = false;
         uint64_t sum = 0;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
@@ -441,15 +442,21 @@ __device__ __forceinline__ void wave_runs(const Four *f, const uint32_t *key,
             const double a0 = kMagic0 + y;
             const double a1 = kMagic1 + y;
             // 0 <= y < 2^51 as one unsigned compare of the bit patterns
-            // (a negative y, -0.0 and NaN have larger patterns)
-            odd |= dbits(y) >= (uint64_t)dbits(kHugeY);
+            // (a negative y, -0.0 and NaN have larger patterns), and the
+            // same for -y
+            notpos |= dbits(y) >= (uint64_t)dbits(kHugeY);
+            notneg |= dbits(-y) >= (uint64_t)dbits(kHugeY);
             // a tie: the two starts round to counts that differ by other
             // than one (both sums lie in [2^52, 2^53), so the low words do)
-            odd |= (uint32_t)dbits(a1) - (uint32_t)dbits(a0) != 1u;
+            tie |= (uint32_t)dbits(a1) - (uint32_t)dbits(a0) != 1u;
             sum += dbits(a0);
         }
         v[k] = sum - 4 * (uint64_t)kMagic0Bits;
-        easy &= __ballot(odd) == 0;
+        // tie-free, and every increment of one sign: a monotone run, whose
+        // prefixes lie between 0 and its total (no scan for the bounds)
+        const bool pos = __ballot(notpos) == 0, neg = __ballot(notneg) == 0;
+        easy &= __ballot(tie) == 0 && (pos || neg);
+        negs |= (!pos && neg) ? 1u << k : 0u;
     }
     if (easy) {
         int64_t w[CPB];
@@ -462,8 +469,10 @@ __device__ __forceinline__ void wave_runs(const Four *f, const uint32_t *key,
             for (int k = 0; k < CPB; k++) {
                 WaveRun r;
                 r.p = Pair{w[k], w[k]};
-                r.lo = r.hi = 0;
-                r.flags = 0u;
+                const bool n = (negs >> k) & 1u;
+                r.lo = n && w[k] < 0 ? w[k] : 0;
+                r.hi = 0;
+                r.flags = n ? kFlagNeg : 0u;
                 lds[k][wave_id()] = r;
             }
         }
@@ -955,6 +964,18 @@ __device__ __forceinline__ Run wave_reduce_run_rev(Run v)
     return v;
 }
 
+// Runs that compose by a plain sum of their increments: tie-free and
+// monotone, every one non-decreasing (no flag, the bounds unused) or every
+// one non-increasing (kFlagNeg, bounds (total, 0)).
+__device__ __forceinline__ bool rising_run(const Pair &p, uint32_t flags)
+{
+    return p.r0 == p.r1 && flags == 0u && p.r0 >= 0;
+}
+__device__ __forceinline__ bool falling_run(const Pair &p, int64_t lo, int64_t hi, uint32_t flags)
+{
+    return p.r0 == p.r1 && flags == kFlagNeg && p.r0 <= 0 && lo == p.r0 && hi == 0;
+}
+
 struct ChainLds {
     Run wrun[2][kWaves];
     uint32_t key0;
@@ -1056,7 +1077,7 @@ __device__ __forceinline__ int chain_back(const ChainArea &ch, uint32_t tb, uint
         // tiles all have a tie-free run without a negative term (nearly
         // always) composes them as one integer sum
         Run r = run_identity();
-        bool bad = false, plain = true;
+        bool bad = false, plain = true, fall = true;
         int64_t tot = 0;
 #pragma unroll
         for (int i = kBackPer - 1; i >= 0; i--) {
@@ -1065,7 +1086,8 @@ __device__ __forceinline__ int chain_back(const ChainArea &ch, uint32_t tb, uint
                 const Run ti{Pair{r0, r0 + (int64_t)((w[i][0] >> kDrShift) & 3u) - 1},
                              dec_i64(w[i][2]), dec_i64(w[i][3]),
                              (uint32_t)w[i][0] & (kFlagNeg | kFlagBad | kFlagNonFinite)};
-                plain &= ti.p.r1 == r0 && ti.flags == 0u && r0 >= 0;
+                plain &= rising_run(ti.p, ti.flags);
+                fall &= falling_run(ti.p, ti.lo, ti.hi, ti.flags);
                 tot += r0;
                 r = run_compose_sat(r, ti);
                 bad |= ((uint32_t)w[i][0] & kKeyMask) != key0;
@@ -1075,6 +1097,11 @@ __device__ __forceinline__ int chain_back(const ChainArea &ch, uint32_t tb, uint
             tot = wave_sum_i64(tot);
             r = Run{Pair{tot, tot}, 0, tot, 0u};
             if (tot > ((int64_t)1 << 56))
+                r = Run{Pair{0, 0}, 0, 0, kFlagBad};
+        } else if (__ballot(!fall) == 0) {
+            tot = wave_sum_i64(tot);
+            r = Run{Pair{tot, tot}, tot, 0, kFlagNeg};
+            if (tot < -((int64_t)1 << 56))
                 r = Run{Pair{0, 0}, 0, 0, kFlagBad};
         } else {
             r = wave_reduce_run_rev(r);
@@ -1830,16 +1857,18 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
         bool cc = L.cross[t] != 0;
         // the waves' parts in order; parts that are all tie-free and
         // without a negative term (nearly always) just add up
-        bool plain = true;
+        bool plain = true, fall = true;
         int64_t sum = 0;
 #pragma unroll
         for (int w = 0; w < kWaves; w++) {
             const WaveRun &q = L.wrun[t][w];
-            plain &= q.p.r0 == q.p.r1 && q.flags == 0u && q.p.r0 >= 0;
+            plain &= rising_run(q.p, q.flags);
+            fall &= falling_run(q.p, q.lo, q.hi, q.flags);
             sum += q.p.r0;
         }
         const WaveRun r =
-            clamp_run(plain ? WaveRun{Pair{sum, sum}, 0, sum, 0u} : join_waves(L.wrun[t]));
+            clamp_run(plain ? WaveRun{Pair{sum, sum}, 0, sum, 0u}
+                            : fall ? WaveRun{Pair{sum, sum}, sum, 0, kFlagNeg} : join_waves(L.wrun[t]));
         // near an edge of the planned binade: the plan is not trusted there
         if (key_has_fast_path(kk) && kk == key_of(pk)) {
             const int64_t m = count_of(pk);
@@ -1885,17 +1914,20 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
     if (regular) {
         if (t == 0) {
             // the chunks' runs in order (plain ones add up)
-            bool plain = true;
+            bool plain = true, fall = true;
             int64_t sum = 0;
 #pragma unroll
             for (int k = 0; k < CPB; k++) {
                 const WaveRun &q = L.join[k];
-                plain &= q.p.r0 == q.p.r1 && q.flags == 0u && q.p.r0 >= 0;
+                plain &= rising_run(q.p, q.flags);
+                fall &= falling_run(q.p, q.lo, q.hi, q.flags);
                 sum += q.p.r0;
             }
             Run tr = run_identity();
             if (plain) {
                 tr = Run{Pair{sum, sum}, 0, sum, 0u};
+            } else if (fall) {
+                tr = Run{Pair{sum, sum}, sum, 0, kFlagNeg};
             } else {
 #pragma unroll
                 for (int k = 0; k < CPB; k++) {
