@@ -15,7 +15,9 @@
 //    2. the plan: publish the tile's sum, find the prefix of the chunk sums
 //       before the tile by a decoupled look-back over the predecessors'
 //       status words, publish the inclusive prefix; a chunk's planned binade
-//       is that of the prefix before it;
+//       is that of the prefix before it (or, with a plan kept from the
+//       previous call and far from a binade edge, that plan's binade, with
+//       no look-back);
 //    3. every term's increment pair under its chunk's planned binade,
 //       composed in order (lane, ordered wave scan, waves in order) into the
 //       chunk's run: the pair, prefix bounds, flags;
@@ -23,13 +25,15 @@
 //       and stay clear of its edges (with a margin for the plan's error) is
 //       regular: it publishes the composition of its runs and is done.  Any
 //       other tile (a sum's first and last tile among them) locates the
-//       crossing of every chunk planned to cross into the next binade,
-//       composes the regular tiles back to the nearest irregular one,
-//       waits for that tile's exact sum (the first tile: the head's),
-//       applies the composed runs and its own chunks in order -- a run where
-//       it applies, a crossing where it holds, term by term from the exact
-//       sum where neither does -- and publishes the exact sum after itself.
-//       The last tile's value is the result.
+//       crossing of every chunk planned to cross into the next binade up or
+//       down, composes the regular tiles back to the nearest irregular one,
+//       publishes its own O(1) step as a record, waits for that tile's exact
+//       sum (the first tile: the head's) or catches up to it through the
+//       records of the irregular tiles before, applies the composed runs and
+//       its own chunks in order -- a run where it applies, a crossing where
+//       it holds, term by term from the exact sum where neither does -- and
+//       publishes the exact sum after itself.  The last tile's value is the
+//       result.
 //  walk_kernel (one workgroup of 256 lanes per sum, after the tiles):
 //    5. takes the last tile's exact sum.  Where the chain could not finish
 //       (a wait that timed out, a composed run that did not apply), it
@@ -44,7 +48,9 @@
 //       current binade, a workgroup scan gives every prefix count, the first
 //       term that leaves the binade is added with one fp64 add, and the next
 //       round starts after it; when rounds keep resolving only a few terms,
-//       one lane adds the rest in order.
+//       one lane adds the rest in order;
+//    7. writes each sum (and the float means of interleaved sums, the SSIM
+//       weight sum) and, when asked, keeps the plan for the next call.
 //
 // Every wait is bounded: a plan wait that times out gives up the tile's
 // plan (no fast path for its chunks), a chain wait that times out reports
