@@ -2777,8 +2777,18 @@ static int launch_batch_src(const BatchArgs &a, const Src &src, void *ws, double
     const WsParts p = carve(ws, total);
     BatchArgs args = a;
     args.epoch = next_epoch();
-    const uint32_t sel = (a.flags >> kTileShift) & 3u;  // 0: default
-    args.tile = sel == 1 ? 1u : (sel == 2 ? 2u : 4u);
+    // Chunks per tile.  By default as many as keep the launch's tiles within
+    // about two generations of workgroups in flight (1024 tiles each on 256
+    // compute units): fewer chunks per tile mean shorter residency and more
+    // tiles streaming at once, until a third generation costs more than
+    // that saves.  A sum of at most two tiles of kTileMax chunks keeps them
+    // (more tiles would only add links to its chain), and a kept plan is
+    // kept per tile of kTileMax chunks.
+    const uint32_t sel = (a.flags >> kTileShift) & 3u;  // 0: by size
+    if (sel == 0 && !(a.flags & EXSEQ_PLAN_REUSE))
+        args.tile = total <= 2u * kTileMax ? 4u : total <= 2048u ? 1u : total <= 4096u ? 2u : 4u;
+    else
+        args.tile = sel == 1 ? 1u : (sel == 2 ? 2u : 4u);
     const uint32_t tiles = total / args.tile;
     args.plan_sig = (a.flags & EXSEQ_PLAN_REUSE) && (a.flags & EXSEQ_PLAN_MASK) == EXSEQ_PLAN_AUTO &&
                             chain_on(a.flags) && args.tile == (uint32_t)kTileMax && tiles

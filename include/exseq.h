@@ -75,8 +75,10 @@ enum {
 #define EXSEQ_PLAN_FIXED_KEY(key) (EXSEQ_PLAN_FIXED | (((uint32_t)(key) & 0xFFFu) << 8))
 
 /* Further bits of `flags` (testing and tuning; 0 for production use).
- *   bits 4..5     chunks per tile of the single pass: 0 (default) or 3 = 4,
- *                 1 = 1, 2 = 2
+ *   bits 4..5     chunks per tile of the single pass: 0 (default) = by the
+ *                 launch's chunk count (4 up to 8 chunks, 1 up to 2048, 2 up
+ *                 to 4096, else 4; always 4 with EXSEQ_PLAN_REUSE), 1 = 1,
+ *                 2 = 2, 3 = 4
  *   WALK_ONLY     the tiles only plan and describe; the ordered walk after
  *                 them follows every chunk (no exact chain between tiles)
  *   CHAIN_CUT     the exact chain stops half way through every sum (the tiles
