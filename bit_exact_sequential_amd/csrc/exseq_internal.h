@@ -77,6 +77,8 @@ struct BatchArgs {
     uint32_t interleave;
     // Nullable: means[s] = (float)(sum / n[s]) is written with the sum.
     float *means;
+    // A launch of at most a few chunks: the walk alone adds them in order.
+    uint32_t tiny;
 };
 
 // Descriptors live in four arrays (structure of arrays, so that the walk

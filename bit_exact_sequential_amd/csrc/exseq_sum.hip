@@ -2338,7 +2338,28 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, Src src
 
     double S = a.init[s];
     size_t start = 0;
-    if (nch && chain_on(a.flags)) {
+    if (a.tiny) {
+        // A launch of a few chunks (no tiles ran): every chunk term by term
+        // from init, in order.  Three dependent launches would cost more than
+        // the adds.
+        for (size_t c = 0; c < nch; c++) {
+            const size_t b = c * kChunk;
+            const int len = (int)(n - b < (size_t)kChunk ? n - b : (size_t)kChunk);
+            const Four f = src.chunk(a, s, c, lds_src);
+            src.keep(c, f);
+            bool nf = false;
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                nf |= i < f.cnt && is_nonfinite(f.v[i]);
+            nonfinite |= __syncthreads_or(nf) != 0;
+            S = resolve_terms(f, len, S, 0, sh, buf);
+            S = bitsd(uniform_u64(dbits(S)));
+            n_fb++;
+            fb_terms += (uint64_t)len;
+            first_fb = 0;
+        }
+        start = nch;
+    } else if (nch && chain_on(a.flags)) {
         // The chain's exact sum after the last tile, or else the last exact
         // sum it published (the chain fails at one tile and at every
         // irregular tile after it, so that is where it stopped).
@@ -2800,6 +2821,14 @@ static int launch_batch_src(const BatchArgs &a, const Src &src, void *ws, double
         const uint32_t tk = (a.chunk_base[k + 1] - a.chunk_base[k]) / args.tile;
         args.last_tile[k] = nch ? a.chunk_base[k] / args.tile + (nch - 1) / args.tile : ~0u;
         args.rest_base[k + 1] = args.rest_base[k] + (nch ? tk - 1 : tk);
+    }
+    // A launch of at most two tiles of kTileMax chunks, with default flags
+    // and no per-kernel events: the walk kernel alone adds every chunk.
+    args.tiny = total <= 2u * kTileMax && a.flags == 0u && !(events && n_events) ? 1u : 0u;
+    if (args.tiny) {
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(walk_kernel<Src>), dim3((unsigned)a.count),
+                           dim3(kWalkThreads), 0, stream, args, src, p.d, p.ch, p.status, outs, stats);
+        return hipGetLastError() == hipSuccess ? EXSEQ_OK : EXSEQ_EHIP;
     }
     mark(0);
     if (chain_on(a.flags) && tiles)
