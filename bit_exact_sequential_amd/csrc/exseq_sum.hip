@@ -5,13 +5,19 @@
 // frame sum", Findings 3).  A chunk is 1024 consecutive terms, held by 256
 // lanes (4 waves of 64) with 4 consecutive terms per lane.
 //
-//  chain_clear_kernel: zeroes the chain words of the launch's tiles.
+//  A launch of at most 8 chunks runs walk_kernel alone (every chunk term by
+//  term from init, in order).  Otherwise:
+//  chain_clear_kernel: zeroes the chain words and step records of the
+//  launch's tiles.
 //  tile_kernel (one launch for every tile of every sum of a batch; reads
 //  each term once).  Blocks: each sum's last tile, each sum's head (its
-//  first chunk added to init term by term), then the other tiles in order,
-//  one workgroup per tile of CPB consecutive chunks of one sum:
-//    1. load the tile's terms (16-byte non-temporal loads), fixed-tree fp64
-//       sum of every chunk;
+//  first chunk added to init term by term), then the other tiles in order
+//  (the tiles of interleaved sums for one range together), one workgroup
+//  per tile of CPB consecutive chunks of one sum (1, 2 or 4, by the
+//  launch's size):
+//    1. load the tile's terms (contiguous: 16-byte non-temporal loads;
+//       interleaved: every k-th double; SSIM: formed from the two planes),
+//       fixed-tree fp64 sum of every chunk;
 //    2. the plan: publish the tile's sum, find the prefix of the chunk sums
 //       before the tile by a decoupled look-back over the predecessors'
 //       status words, publish the inclusive prefix; a chunk's planned binade
