@@ -312,3 +312,19 @@ def test_ssim_term_divide_against_host():
         gs, gw, gt = ex.ssim_term_and_sum(r, d, radius, want_terms=True)
         assert np.array_equal(gt.cpu().numpy().view(np.uint64), terms.view(np.uint64)), radius
         assert same(float(gs.cpu()[0]), s)
+
+
+@pytest.mark.parametrize("n", [1, 1023, 1024, 5000, 8192])
+def test_one_launch_small_sums(n):
+    """Sums of at most 8 chunks run as one launch that adds every chunk in
+    order: exact, every chunk counted as added term by term, and the same
+    bits as with the three-launch path (forced by an explicit tile size)."""
+    torch = torch_cuda()
+    x = si.tie_heavy(n, n)
+    got, st = gpu_sum(torch, x, 0.5, stats=True)
+    assert same(got, oracle.seq_sum(x, 0.5))
+    nch = (n + 1023) // 1024
+    assert st["chunks"] == nch and st["fallback_chunks"] == nch and st["fast_chunks"] == 0, st
+    assert st["fallback_terms"] == n and st["first_fallback"] == 0, st
+    got4 = gpu_sum(torch, x, 0.5, flags=3 << 4)
+    assert same(got4, got)
