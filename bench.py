@@ -13,10 +13,11 @@ Prints ONE JSON line with the whole-job throughput (terms/s), the roofline
 of the dominant kernel (per-kernel device time measured live with HIP events
 recorded by the library around each kernel), the oracle timed on the host as
 the CPU baseline, and the device time of the other workloads (the uniform
-4096-term sum, the signed 1920x1080 sum, the fused SSIM frame and the
-108-sum pyramid batch) under "other_configs", and the same six frames as a
-video whose every call keeps its plan for the next (EXSEQ_PLAN_REUSE) under
-"video_plan_reuse".
+4096-term sum, the signed 1920x1080 sum, the negated frame, the fused SSIM
+frame, the four interleaved LCS sums and the 108-sum pyramid batch, alone and
+with two pyramids in turn keeping their plans) under "other_configs", and the
+same six frames as a video whose every call keeps its plan for the next
+(EXSEQ_PLAN_REUSE) under "video_plan_reuse".
 """
 
 from __future__ import annotations
@@ -143,6 +144,7 @@ def time_configs(ex, si, torch, dev, seed, reps=30):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n
 
+    import numpy as np
     res = {}
     x1 = torch.from_numpy(si.uniform(4096, seed)).to(dev)
     o1 = torch.empty(1, dtype=torch.float64, device=dev)
@@ -203,7 +205,27 @@ def time_configs(ex, si, torch, dev, seed, reps=30):
     res["pyramid_batch_108"] = {"us_per_batch": ms * 1e3, "sums": len(xs), "terms": total,
                                 "terms_per_s": total / (ms * 1e-3),
                                 "gbs": total * 8 / (ms * 1e-3) / 1e9}
-    del xs
+    # the same batch as a video: two pyramids (frames) in turn, each call
+    # keeping its plan for the next (EXSEQ_PLAN_REUSE); same bits required
+    ref_bits = o5.cpu().numpy().view(np.uint64).copy()
+    xs2 = [torch.from_numpy(a).to(dev) for a in si.pyramid(seed + 1)]
+    w8 = ex.workspace(ex.lib().exact_seq_sum_f64_batch_workspace_size(nsa, len(ns)), dev)
+    o8 = torch.empty(len(xs), dtype=torch.float64, device=dev)
+    k8 = [0]
+
+    def vid():
+        ex.exact_seq_sum_batch(xs if k8[0] % 2 == 0 else xs2, out=o8, ws=w8, flags=ex.PLAN_REUSE)
+        k8[0] += 1
+    n8 = max(4, reps // 3) // 2 * 2
+    ms = timed(vid, n8)
+    ex.exact_seq_sum_batch(xs, out=o8, ws=w8, flags=ex.PLAN_REUSE)
+    same = bool((o8.cpu().numpy().view(np.uint64) == ref_bits).all())
+    assert same, "plan reuse changed a pyramid result"
+    res["pyramid_batch_108_plan_reuse"] = {"us_per_batch": ms * 1e3, "terms_per_s": total / (ms * 1e-3),
+                                           "gbs": total * 8 / (ms * 1e-3) / 1e9,
+                                           "same_bits_as_plain_calls": same,
+                                           "note": "two pyramids in turn; each call keeps its plan for the next"}
+    del xs, xs2
     return res
 
 
