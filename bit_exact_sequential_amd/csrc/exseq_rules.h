@@ -147,18 +147,31 @@ EXSEQ_HD Run run_of_term(const TermInc& t, bool nonfinite)
     return r;
 }
 
+// The largest prefix of a run.  A run without a negative term rises
+// monotonically along either start parity, so its largest prefix is its
+// larger total; producers of such runs may leave hi at 0 and rely on this.
+EXSEQ_HD int64_t run_top(const Run& r)
+{
+    if (r.flags & kFlagNeg)
+        return r.hi;
+    const int64_t t = r.p.r0 < r.p.r1 ? r.p.r1 : r.p.r0;
+    return t > r.hi ? t : r.hi;
+}
+
 // a then b.  A prefix of the composition is a prefix of a, or all of a
 // (r0 or r1 of a, by the start parity) followed by a prefix of b, so the
 // bounds compose as a minimum and a maximum (sound for either start parity
-// and for any grouping of the terms).
+// and for any grouping of the terms).  A rising part's largest prefix is
+// taken as its total, so that a rise after a negative term is bounded too.
 EXSEQ_HD Run run_compose(const Run& a, const Run& b)
 {
     Run c;
     c.p = compose(a.p, b.p);
     const int64_t amin = a.p.r0 < a.p.r1 ? a.p.r0 : a.p.r1;
     const int64_t amax = a.p.r0 < a.p.r1 ? a.p.r1 : a.p.r0;
+    const int64_t ahi = run_top(a), bhi = run_top(b);
     c.lo = a.lo < amin + b.lo ? a.lo : amin + b.lo;
-    c.hi = a.hi > amax + b.hi ? a.hi : amax + b.hi;
+    c.hi = ahi > amax + bhi ? ahi : amax + bhi;
     c.flags = a.flags | b.flags;
     return c;
 }

@@ -60,11 +60,22 @@ def test_lcs_full_size():
 
 
 @pytest.mark.parametrize("flags", [ex.PLAN_ALL_FALLBACK, ex.PLAN_PLUS_ONE, ex.PLAN_MINUS_ONE,
-                                   ex.WALK_ONLY, 1 << 4, 2 << 4, ex.CHAIN_CUT])
+                                   ex.WALK_ONLY, 1 << 4, 2 << 4, 3 << 4, ex.CHAIN_CUT])
 def test_plan_and_chain_variants(flags):
     torch = torch_cuda()
     x = records(300_000, 4, 5)
     check(torch, x, 4, [1.0, 0.0, -1.0, 2.0], flags=flags)
+
+
+@pytest.mark.parametrize("windows", [32773, 200001, 518400])
+@pytest.mark.parametrize("flags", [0, 1 << 4, 2 << 4, 3 << 4, (3 << 4) | ex.WALK_ONLY,
+                                   (3 << 4) | ex.CHAIN_CUT])
+def test_lcs_tile_sizes(windows, flags):
+    """The l*c*s field rises through binades with a rare negative term: a
+    chunk whose negative term lies in an earlier wave than its upward
+    crossing must not pass as staying in its binade, for every tile size."""
+    torch = torch_cuda()
+    check(torch, si.lcs_records(windows, 0), 4, flags=flags)
 
 
 def test_plan_reuse_sequence_and_no_means():

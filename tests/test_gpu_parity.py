@@ -328,3 +328,17 @@ def test_one_launch_small_sums(n):
     assert st["fallback_terms"] == n and st["first_fallback"] == 0, st
     got4 = gpu_sum(torch, x, 0.5, flags=3 << 4)
     assert same(got4, got)
+
+
+@pytest.mark.parametrize("flags", [1 << 4, 2 << 4, 3 << 4, (3 << 4) | ex.WALK_ONLY, ex.WALK_ONLY])
+def test_rise_after_negative_term(flags):
+    """A rising sum whose chunk holds a negative term in one wave and its
+    upward binade crossing in a later, rising wave (the l*c*s products,
+    whose prefixes of 3 chunks show it): the chunk's largest prefix counts
+    the later wave's rise, so the chunk is never applied as staying in its
+    binade.  Every prefix length, every tile size, with and without the chain."""
+    torch = torch_cuda()
+    f = np.ascontiguousarray(si.lcs_records(518400, 0)[0::4])
+    for n in (3072, 4096, 5000, 40960, 518400):
+        x = f[:n]
+        assert same(gpu_sum(torch, x, 0.0, flags=flags), oracle.seq_sum(x)), (n, flags)
