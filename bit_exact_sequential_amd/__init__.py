@@ -168,6 +168,31 @@ def _stream_handle(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _side_stream(stream, device):
+    """The caller's stream when it is not the device's current one, else None."""
+    torch = _torch()
+    if stream is None or stream == torch.cuda.current_stream(device):
+        return None
+    return stream
+
+
+def _keep_for(stream, device, *tensors):
+    """Tensors allocated here on the current stream but written by kernels on
+    another stream: tell the caching allocator, so that their memory is not
+    handed out again before that stream has finished with it."""
+    s = _side_stream(stream, device)
+    if s is not None:
+        for t in tensors:
+            if t is not None:
+                t.record_stream(s)
+
+
+def _sync_for_stats(stream, device):
+    s = _side_stream(stream, device)
+    if s is not None:
+        s.synchronize()
+
+
 def _check_device_f64(x):
     torch = _torch()
     if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
@@ -194,9 +219,11 @@ def exact_seq_sum(x, init: float = 0.0, *, flags: int = 0, out=None, ws=None,
     L = lib()
     n = x.numel()
     dev = x.device
+    new_out = out is None
     if out is None:
         out = torch.empty(1, dtype=torch.float64, device=dev)
     need = L.exact_seq_sum_f64_workspace_size(n)
+    new_ws = ws is None
     if ws is None:
         ws = workspace(need, dev)
     st = torch.empty(STATS_BYTES, dtype=torch.uint8, device=dev) if stats else None
@@ -204,7 +231,9 @@ def exact_seq_sum(x, init: float = 0.0, *, flags: int = 0, out=None, ws=None,
                              ws.data_ptr(), ws.numel(), _stream_handle(stream, dev),
                              int(flags), st.data_ptr() if st is not None else None)
     _check(rc, "exact_seq_sum_f64")
+    _keep_for(stream, dev, out if new_out else None, ws if new_ws else None, st)
     if stats:
+        _sync_for_stats(stream, dev)
         return out, _read_stats(st)
     return out
 
@@ -224,6 +253,7 @@ def exact_seq_sum_interleaved(x, k: int, inits=None, *, means: bool = True, flag
     windows = n // k
     L = lib()
     dev = x.device
+    new_out = out is None
     if out is None:
         out = torch.empty(k, dtype=torch.float64, device=dev)
     mt = torch.empty(k, dtype=torch.float32, device=dev) if means else None
@@ -231,6 +261,7 @@ def exact_seq_sum_interleaved(x, k: int, inits=None, *, means: bool = True, flag
     if inits is not None:
         ini = (ctypes.c_double * k)(*[float(v) for v in inits])
     need = L.exact_seq_sum_f64_interleaved_workspace_size(windows, k)
+    new_ws = ws is None
     if ws is None:
         ws = workspace(need, dev)
     st = torch.empty(STATS_BYTES * k, dtype=torch.uint8, device=dev) if stats else None
@@ -239,7 +270,9 @@ def exact_seq_sum_interleaved(x, k: int, inits=None, *, means: bool = True, flag
                                          ws.data_ptr(), ws.numel(), _stream_handle(stream, dev),
                                          int(flags), st.data_ptr() if st is not None else None)
     _check(rc, "exact_seq_sum_f64_interleaved")
+    _keep_for(stream, dev, out if new_out else None, mt, ws if new_ws else None, st)
     if stats:
+        _sync_for_stats(stream, dev)
         return out, mt, _read_stats_many(st, k)
     return out, mt
 
@@ -269,9 +302,11 @@ def exact_seq_sum_batch(xs, inits=None, *, flags: int = 0, out=None, ws=None,
     ini = None
     if inits is not None:
         ini = (ctypes.c_double * max(count, 1))(*[float(v) for v in inits])
+    new_out = out is None
     if out is None:
         out = torch.empty(max(count, 1), dtype=torch.float64, device=dev)
     need = L.exact_seq_sum_f64_batch_workspace_size(ns, count)
+    new_ws = ws is None
     if ws is None:
         ws = workspace(need, dev)
     st = torch.empty(STATS_BYTES * max(count, 1), dtype=torch.uint8, device=dev) if stats else None
@@ -279,7 +314,9 @@ def exact_seq_sum_batch(xs, inits=None, *, flags: int = 0, out=None, ws=None,
                                    ws.numel(), _stream_handle(stream, dev), int(flags),
                                    st.data_ptr() if st is not None else None)
     _check(rc, "exact_seq_sum_f64_batch")
+    _keep_for(stream, dev, out if new_out else None, ws if new_ws else None, st)
     if stats:
+        _sync_for_stats(stream, dev)
         return out[:count], _read_stats_many(st, count)
     return out[:count]
 
@@ -309,6 +346,7 @@ def ssim_term_and_sum(ref, dis, radius: int = 3, c1: float = None, c2: float = N
     wsum = torch.empty(1, dtype=torch.int64, device=dev)
     terms = torch.empty((h, w), dtype=torch.float64, device=dev) if want_terms else None
     need = L.ssim_term_and_sum_workspace_size(w, h)
+    new_ws = ws is None
     if ws is None:
         ws = workspace(need, dev)
     st = torch.empty(STATS_BYTES, dtype=torch.uint8, device=dev) if stats else None
@@ -318,7 +356,9 @@ def ssim_term_and_sum(ref, dis, radius: int = 3, c1: float = None, c2: float = N
                              ws.numel(), _stream_handle(stream, dev), int(flags),
                              st.data_ptr() if st is not None else None)
     _check(rc, "ssim_term_and_sum")
+    _keep_for(stream, dev, out, wsum, terms, ws if new_ws else None, st)
     if stats:
+        _sync_for_stats(stream, dev)
         return out, wsum, terms, _read_stats(st)
     return out, wsum, terms
 
@@ -329,13 +369,16 @@ def tree_sum(x, *, out=None, ws=None, stream=None):
     _check_device_f64(x)
     L = lib()
     n = x.numel()
+    new_out = out is None
     if out is None:
         out = torch.empty(1, dtype=torch.float64, device=x.device)
+    new_ws = ws is None
     if ws is None:
         ws = workspace(L.tree_sum_f64_workspace_size(n), x.device)
     rc = L.tree_sum_f64(x.data_ptr() if n else None, n, out.data_ptr(), ws.data_ptr(),
                         ws.numel(), _stream_handle(stream, x.device))
     _check(rc, "tree_sum_f64")
+    _keep_for(stream, x.device, out if new_out else None, ws if new_ws else None)
     return out
 
 

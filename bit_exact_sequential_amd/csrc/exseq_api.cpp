@@ -158,7 +158,7 @@ size_t ssim_term_and_sum_workspace_size(int width, int height)
 {
     if (width < 1 || height < 1)
         return 256;
-    return ssim_layout(width, height).total;
+    return ssim_ws_bytes(width, height);
 }
 
 int ssim_term_and_sum(const uint8_t *ref, const uint8_t *dis, int width, int height,

@@ -1,8 +1,9 @@
-// Host model of the exact sequential sum: the kernels' rules (exseq_rules.h)
-// walked chunk by chunk on the CPU.  It is test infrastructure for the rules
-// themselves (the "fake device" of Research-1433 Findings 1 "Tests": the
-// whole pipeline in the kernels' layout against the loop, on several kinds of
-// input and of plan, plus mutations of the rules that must be caught).  The
+// Host model of the exact sequential sum: the rules of exseq_rules.h applied
+// chunk by chunk on the CPU, each chunk's run composed term by term (a left
+// fold), with the plan overrides and the four rule mutations of Research-1433
+// "Forming the CPU's sequential double sums on a GPU, bit for bit", Findings
+// "Tests".  It checks the rules themselves, not the kernels' grouping of the
+// terms into lanes, waves and tiles (the composition twin replays that).  The
 // GPU entry points never call it.
 #include <algorithm>
 #include <cstring>

@@ -6,11 +6,12 @@
 // GPU, bit for bit", Findings 2-4; Research-1424 "integer_ssim_cuda and the
 // CPU's frame sum", Findings 3):
 //
-//  * While the running sum S stays in one binade [2^e, 2^(e+1)) it is m*u
-//    with u = 2^(e-52) and an integer count m in [2^52, 2^53).  Adding a term
-//    x gives (m + r)*u where r is x/u rounded to an integer, as long as the
-//    result stays in the binade.  Integer adds associate, so runs of terms
-//    can be formed in parallel.
+//  * Within one binade [2^e, 2^(e+1)) every double is an integer multiple
+//    of the binade's unit u = 2^(e-52), with a multiplier (the count)
+//    between 2^52 and 2^53.  So while the running sum stays inside the
+//    binade, adding a term moves the count by that term measured in units
+//    and rounded to a whole number; the sum is an integer sum of those
+//    increments, and integer sums may be grouped in any way.
 //  * A term exactly half way between two counts rounds to the even count, so
 //    r depends on the parity of m: every term, and every run, is a pair of
 //    increments (start count even, start count odd).  Two runs compose by

@@ -25,14 +25,9 @@ static int64_t line_sum(int len, int radius)
     return s;
 }
 
-SsimLayout ssim_layout(int width, int height)
+size_t ssim_ws_bytes(int width, int height)
 {
-    SsimLayout L;
-    const size_t n = (size_t)width * (size_t)height;
-    L.plane_off = 0;
-    L.sum_off = 0;
-    L.total = sum_ws_bytes(padded_chunks(n));
-    return L;
+    return sum_ws_bytes(padded_chunks((size_t)width * (size_t)height));
 }
 
 int launch_ssim_sum(const uint8_t *ref, const uint8_t *dis, int width, int height,

@@ -1,8 +1,8 @@
 """The method's rules, walked by the host model, against the oracle (CPU).
 
 Research-1433 "Forming the CPU's sequential double sums on a GPU, bit for
-bit", Findings 1 ("Tests"): the whole pipeline in the kernels' layout against
-the loop on several kinds of input and several kinds of plan, and mutations of
+bit", Findings "Tests": the method run chunk by chunk on the host and
+compared with the loop for several input kinds and plans, and mutations of
 the rules (tie always up, no binade check, no upper bound check, parity
 ignored when composing) that must each make it fail.  Findings 5: a plan
 cannot change a result, only cost term-by-term chunks."""
