@@ -347,6 +347,10 @@ def main():
     # word and 40 bytes of chain words written and read
     tiles = (nch + 3) // 4
     alg_bytes = {
+        # the single pass: the terms read once, a 28-byte descriptor per
+        # chunk written, per tile a plan word and a 32-byte record written
+        # and the record read back by the finisher
+        "pass_kernel": n * TERM_BYTES + nch * 28 + tiles * (8 + 32 + 32),
         "chain_clear_kernel": tiles * 40,
         "tile_kernel": n * TERM_BYTES + nch * 28 + tiles * (8 + 40),
         "walk_kernel": tiles * 8 + 8,

@@ -36,6 +36,8 @@ def plan_fixed(key: int) -> int:
 WALK_ONLY = 1 << 6
 CHAIN_CUT = 1 << 7
 PLAN_REUSE = 1 << 20
+CHAIN_PATH = 1 << 21
+PASS_PATH = 1 << 22
 
 
 def tile_flag(chunks_per_tile: int) -> int:

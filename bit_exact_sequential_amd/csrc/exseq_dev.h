@@ -89,8 +89,22 @@ __device__ __forceinline__ Four load_four(const double *__restrict__ x, size_t n
 // Term sources of the exact sum.  chunk() gives lane t its terms 4t .. 4t+3
 // of chunk c of sum s; it is called by every lane of the workgroup with the
 // same chunk.  keep() hands the terms to the caller where it asked for them.
+// One sum's terms as the single pass sees them: its pointer, length and
+// start, and where its chunks begin in the launch.
+struct SumView {
+    const double *x;
+    size_t n;
+    double init;
+    uint32_t cb;   // the sum's first chunk in the launch
+    uint32_t nch;  // its chunks
+};
+
 struct PlainTerms {
     static constexpr int kLdsInts = 1;
+    __device__ __forceinline__ Four chunk_v(const SumView &v, size_t c, int *) const
+    {
+        return load_four(v.x, v.n, c * kChunk + 4 * (size_t)threadIdx.x, true);
+    }
     __device__ __forceinline__ Four chunk(const BatchArgs &a, int s, size_t c, int *) const
     {
         return load_four(a.x[s], a.n[s], c * kChunk + 4 * (size_t)threadIdx.x, true);
@@ -136,16 +150,6 @@ __device__ __forceinline__ double chunk_tree(const Four &f, double *lds4)
     return t;
 }
 
-__global__ __launch_bounds__(kChunkThreads) void chunk_tsum_kernel(
-    const double *__restrict__ x, size_t n, double *__restrict__ tsum)
-{
-    __shared__ double lds4[4];
-    const size_t c = blockIdx.x;
-    const Four f = load_four(x, n, c * kChunk + (size_t)threadIdx.x * 4, true);
-    const double t = chunk_tree(f, lds4);
-    if (threadIdx.x == 0)
-        tsum[c] = t;
-}
 
 // ---------------------------------------------------------------------------
 // The plan
@@ -587,18 +591,24 @@ struct Cand {
     Pair ex_after;  // window prefix through the chunk
 };
 
-struct WalkLds {
+// Scan and candidate scratch of the workgroup building blocks (double-
+// buffered by `buf`).
+struct WalkCore {
     Pair tot[2][kWaves];   // per-wave totals of a scan (double-buffered)
     Cand cand[2][kWaves];  // per-wave candidates (double-buffered)
     double endv[2];        // a round's end state, from the lane holding the last item
     int flag[2][kWaves];
-    double terms[kChunk];  // a chunk's terms, for the one-lane path
+};
+
+// The same with a chunk's terms, for the one-lane path of the resolution.
+struct WalkLds : WalkCore {
+    double terms[kChunk];
 };
 
 // Exclusive workgroup scan of the lanes' pairs; one barrier.  Waves without
 // a tie scan plain integers (the pair is (v, v)).  `buf` alternates between
 // calls so that a call's writes never race with the previous call's reads.
-__device__ __forceinline__ Pair block_excl_scan(Pair v, bool lane_tie, WalkLds &sh, int buf)
+__device__ __forceinline__ Pair block_excl_scan(Pair v, bool lane_tie, WalkCore &sh, int buf)
 {
     const int lane = lane_id(), wave = wave_id();
     Pair inc;
@@ -620,7 +630,7 @@ __device__ __forceinline__ Pair block_excl_scan(Pair v, bool lane_tie, WalkLds &
 }
 
 // Workgroup OR; one barrier.
-__device__ __forceinline__ bool block_any(bool p, WalkLds &sh, int buf)
+__device__ __forceinline__ bool block_any(bool p, WalkCore &sh, int buf)
 {
     const bool w = __ballot(p) != 0;
     if (lane_id() == 0)
@@ -639,7 +649,7 @@ struct CleanSum {
     bool clean, nonfinite;
     int64_t sum;
 };
-__device__ __forceinline__ CleanSum block_clean_sum(bool clean, bool nf, int64_t v, WalkLds &sh,
+__device__ __forceinline__ CleanSum block_clean_sum(bool clean, bool nf, int64_t v, WalkCore &sh,
                                                     int buf)
 {
     const bool wclean = __ballot(!clean) == 0;
@@ -662,7 +672,7 @@ __device__ __forceinline__ CleanSum block_clean_sum(bool clean, bool nf, int64_t
 
 // Publish each wave's lowest-lane candidate; the smallest over the workgroup
 // (idx = kNone if none).  One barrier.
-__device__ __forceinline__ Cand block_first(bool has, const Cand &mine, WalkLds &sh, int buf)
+__device__ __forceinline__ Cand block_first(bool has, const Cand &mine, WalkCore &sh, int buf)
 {
     const uint64_t b = __ballot(has);
     const int lane = lane_id(), wave = wave_id();
@@ -698,14 +708,15 @@ __device__ __forceinline__ Cand cand_none()
 
 // Exact resolution of the len terms of a chunk (lane t holds terms 4t ..
 // 4t+3 in f) from the exact running sum S before term pos.
-__device__ __forceinline__ double resolve_terms(const Four &f, int len, double S, int pos, WalkLds &sh, int &buf)
+__device__ __forceinline__ double resolve_terms(const Four &f, int len, double S, int pos,
+                                                WalkCore &sh, double *terms, int &buf)
 {
     const int t = threadIdx.x;
     double xv[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; k++) {
         xv[k] = f.v[k];
-        sh.terms[kPer * t + k] = xv[k];  // visible after the next barrier
+        terms[kPer * t + k] = xv[k];  // visible after the next barrier
     }
     // A round costs about as much as 300 one-lane adds.  Rounds pay where a
     // binade holds more terms than that; after a crossing (or the first
@@ -773,7 +784,7 @@ __device__ __forceinline__ double resolve_terms(const Four &f, int len, double S
             Cand mine = cand_none();
             if (t == 0) {
                 mine.idx = 0;
-                mine.s_at = add_in_order(S, sh.terms, pos, len);
+                mine.s_at = add_in_order(S, terms, pos, len);
             }
             const Cand fs = block_first(t == 0, mine, sh, buf);
             buf ^= 1;
@@ -861,6 +872,12 @@ __device__ __forceinline__ double resolve_terms(const Four &f, int len, double S
         pos = fr.idx + 1;
     }
     return S;
+}
+
+__device__ __forceinline__ double resolve_terms(const Four &f, int len, double S, int pos, WalkLds &sh,
+                                                int &buf)
+{
+    return resolve_terms(f, len, S, pos, sh, sh.terms, buf);
 }
 
 // The same for chunk c of sum s, its terms formed again by the source.
@@ -1135,7 +1152,7 @@ __device__ __forceinline__ bool lane_prefixes(const Four &f, uint32_t key, Pair 
 }
 
 // Ordered exclusive workgroup scan and the workgroup's total; one barrier.
-__device__ __forceinline__ Pair block_scan_total(Pair v, WalkLds &sh, int buf, Pair &total)
+__device__ __forceinline__ Pair block_scan_total(Pair v, WalkCore &sh, int buf, Pair &total)
 {
     const int lane = lane_id(), wave = wave_id();
     const Pair inc = wave_incl_scan_pair(v);
@@ -1179,7 +1196,7 @@ struct CrossLds {
 // from m_est or cannot have one.  On success out[] holds the published
 // words in every lane.  Three barriers.
 __device__ __forceinline__ bool crossing_find(const Four &f, int len, uint32_t key, int64_t m_est,
-                                              bool down, WalkLds &sh, CrossLds &xl, int &buf,
+                                              bool down, WalkCore &sh, CrossLds &xl, int &buf,
                                               uint64_t *out)
 {
     const int t = threadIdx.x, lane = lane_id(), wave = wave_id();

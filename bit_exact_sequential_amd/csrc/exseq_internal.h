@@ -122,6 +122,12 @@ int launch_interleaved(const double *x, size_t windows, int k, const double *ini
 int launch_exact_sum(const double *x, size_t n, double init, double *out, void *ws,
                      hipStream_t stream, uint32_t flags, exseq_stats *stats,
                      void *const *events = nullptr, int n_events = 0);
+// The single pass (exseq_pass.hip): whether a launch can take it, its
+// workspace, and its launch (one kernel; events[0] and events[1] around it).
+bool pass_eligible(const BatchArgs &a);
+size_t pass_ws_bytes(size_t total_chunks, size_t sums);
+int launch_pass(const BatchArgs &a, void *ws, double *outs, hipStream_t stream,
+                exseq_stats *stats, void *const *events, int n_events);
 extern const char *const kPathKernels[];
 extern const int kPathKernelCount;
 int launch_tree_sum(const double *x, size_t n, double *out, void *ws, hipStream_t stream);

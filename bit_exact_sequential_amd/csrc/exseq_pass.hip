@@ -1,0 +1,1771 @@
+// The single pass of the exact sequential sum: one launch per call.
+//
+// Research-1433 "Forming the CPU's sequential double sums on a GPU, bit for
+// bit" (Findings 2-6, Open questions) describes four kernels: chunk tree
+// sums, a one-lane plan, the increment pairs, and a one-lane walk over the
+// chunks.  Here all of it is one launch.  A sum of n terms is cut into
+// chunks of 1024 and into tiles: the sum's first tile is its first four
+// chunks, every later tile eight.  Each sum gets, in this order of
+// dispatch, three kinds of workgroup:
+//
+//  * the head: the first tile from init, exactly.  It publishes the tile's
+//    inclusive plan prefix at once, adds the first chunk to init term by
+//    term (there the running sum crosses binade after binade), then each
+//    further chunk by its run under the exact sum's binade where that run
+//    applies, else term by term, and publishes the exact sum after the tile.
+//  * the finisher: it takes the head's exact sum and then follows the tiles'
+//    records in order, a window of 256 tiles at a time as they appear: the
+//    regular tiles between irregular ones are composed with one segmented
+//    scan (Research-1433 Open questions: compose runs that share a binade so
+//    that the walk steps over many chunks at once), and the segments and the
+//    irregular tiles' steps are applied in order from the exact sum.  A
+//    segment or a step that does not hold for the exact sum is walked chunk
+//    by chunk from its descriptors, and a chunk that fails there is added
+//    term by term (Research-1433 Findings 4-5: a plan only decides where that
+//    happens).  It writes the result and the statistics.
+//  * one workgroup per later tile:
+//     1. its 8192 terms requested at once: the first four chunks into
+//        registers (16-byte non-temporal loads), the last four straight into
+//        LDS (16-byte global-to-LDS loads), so that a frame's tiles are all
+//        in flight together; the fixed-tree sum of every chunk;
+//     2. the plan: the approximate prefix before the tile by a two-level
+//        look-back, polled by two waves at once -- the tile words of its group
+//        of 64 tiles, and the group words before that group.  Every tile
+//        publishes its sum at once and its inclusive prefix when known; the
+//        last tile of a group publishes the group's sum, then its inclusive
+//        prefix;
+//     3. every term's increment pair under its chunk's planned binade,
+//        composed in order into each chunk's run (pair, prefix bounds,
+//        flags), half a tile at a time; the descriptors are stored;
+//     4. a tile that stays inside one planned binade away from its edges is
+//        regular and publishes its composed run.  Any other tile locates the
+//        crossing of every chunk planned to cross a binade edge (the term at
+//        which the running sum leaves its binade, from the planned start
+//        count) and publishes its O(1) step: the run before the crossing, the
+//        crossing term, and the run after it in the next binade.  Nothing
+//        waits for an exact sum.
+//
+// Cross-workgroup words carry a tag of the launch (45 bits, never zero and
+// never reused within a process), so no word needs clearing between launches
+// and stale words never match.  Plan words are self-contained.  Every word
+// another workgroup reads is written and read with device-coherent
+// (agent-scope) accesses, and a record's data words are acknowledged before
+// its tagged first word is written.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <chrono>
+#include <cstring>
+#include <stdint.h>
+
+#include "exseq.h"
+#include "exseq_dev.h"
+#include "exseq_internal.h"
+#include "exseq_rules.h"
+#include "exseq_wave.h"
+
+namespace exseq {
+
+constexpr int kHalf = 4;             // chunks per half tile (one Four each in registers)
+constexpr int kTileCh = 8;           // chunks of every tile after a sum's first
+constexpr int kHeadCh = 4;           // chunks of a sum's first tile
+constexpr uint32_t kGroup = 64;      // tiles per look-back group
+constexpr int kFinLane = 4;          // tiles per lane in a finisher window
+constexpr int kFinTiles = kFinLane * kChunkThreads;  // tiles per finisher window
+constexpr int kEvCap = 128;          // events a finisher window holds
+constexpr int kStepCap = 16;         // step records a finisher window holds
+constexpr int kOpCap = 128;          // walk ops a finisher window holds
+constexpr int kTagShift = 19;
+// An irregular tile's step (kStepWords words): word 0 holds A's key (12
+// bits), whether A is present (bit 12), the number of crossings (bits
+// 13..14), A's neg and bad flags (bits 15..16) and r1 - r0 + 1 (bits
+// 17..18); words 1..3 A's r0, lo, hi; then per crossing j a word with its
+// chunk's key (12 bits), direction (bit 12: down), negative-term flag (bit
+// 13) and length (bits 16..26), and the crossing's kCrossWords words.
+constexpr int kMaxCross = 2;
+constexpr int kXrecW = 1 + kCrossWords;
+constexpr int kStepWords = 4 + kMaxCross * kXrecW;
+constexpr uint32_t kKindReg = 1, kKindStep = 2, kKindSlow = 3;
+constexpr uint32_t kKindLost = 4;    // finisher only: the record never came
+
+static_assert(kHeadCh == kTileMax, "a sum's first tile is one padding unit of chunks");
+
+// Tiles of a sum of nch chunks, and the first chunk of tile i.
+__host__ __device__ __forceinline__ uint32_t tiles_of(uint32_t nch)
+{
+    return nch == 0 ? 0u : nch <= (uint32_t)kHeadCh ? 1u : 1u + (nch - kHeadCh + kTileCh - 1) / kTileCh;
+}
+__host__ __device__ __forceinline__ uint32_t tile_c0(uint32_t i)
+{
+    return i == 0 ? 0u : (uint32_t)kHeadCh + (uint32_t)kTileCh * (i - 1);
+}
+
+// First word of a tile record: tag | kind | flags (neg, bad, non-finite at
+// their descriptor positions) | r1 - r0 + 1 | key.
+__device__ __forceinline__ uint64_t rec_w0(uint64_t tag, uint32_t kind, uint32_t flags, int64_t dr,
+                                           uint32_t key)
+{
+    return (tag << kTagShift) | ((uint64_t)kind << 17) |
+           (uint64_t)(flags & (kFlagNeg | kFlagBad | kFlagNonFinite)) |
+           ((uint64_t)(dr + 1) << kDrShift) | (uint64_t)(key & kKeyMask);
+}
+
+// Workspace of a pass launch (see pass_carve).
+struct PassWs {
+    uint64_t *st;    // per tile: plan status word
+    uint64_t *gst;   // per group: plan status word
+    DescArrays d;    // per chunk: descriptor
+    uint64_t *trec;  // per tile: 4 words (w0, r0, lo, hi)
+    uint64_t *xrec;  // per tile: kStepWords words (an irregular tile's step)
+    uint64_t *hrec;  // per sum: 2 words (w0, exact sum after the first tile)
+};
+
+struct PassArgs {
+    BatchArgs b;
+    uint32_t block_base[kMaxBatch + 1];  // first workgroup of each sum
+    uint32_t tile_base[kMaxBatch + 1];   // first tile of each sum
+    uint32_t group_base[kMaxBatch + 1];  // first look-back group of each sum
+    uint64_t tag;                        // this launch's record tag (45 bits, nonzero)
+    double *outs;
+    exseq_stats *stats;
+};
+
+// ---------------------------------------------------------------------------
+// LDS
+// ---------------------------------------------------------------------------
+struct PassTileLds {
+    double wsum[kTileCh][kWaves];
+    WaveRun wrun[kHalf][kWaves];
+    WaveRun join[kTileCh];
+    double pk[kTileCh];
+    uint32_t key[kTileCh];
+    uint32_t cross[kTileCh];
+    uint32_t down[kTileCh];
+    uint64_t xw[kTileCh][kCrossWords];
+    uint64_t rec[kStepWords];
+    double lb1, lb2;
+    int lb_found, lb_ok1, lb_ok2;
+    volatile int lb_stop;
+};
+
+// What a finisher window keeps per event.
+struct FinEv {
+    int64_t r0, lo, hi;
+    uint32_t meta;  // key | (r1 - r0 + 1) << 12 | flags | kind << 20
+    int32_t tile;   // the event's tile in the window (a segment's last tile)
+    int32_t start;  // a segment's first tile in the window
+    int32_t slot;   // a step's record slot
+};
+
+// The finisher composes the regular tiles of a segment with two segmented
+// scans (see segp_op and segb_op): their values carry whether they start a
+// segment (head) and that segment's first tile (start).
+struct SegPair {
+    Pair p;
+    int32_t start;
+    int32_t head;
+};
+struct SegBound {
+    int64_t lo, hi;
+    uint32_t flags;
+    int32_t head;
+};
+
+// What the walks over descriptors added (the fallback), for the statistics.
+struct FinTally {
+    unsigned long long fast, fb, terms;
+    long long first;
+    unsigned misses, nonfinite;
+};
+
+// The finisher's ordered walk runs a list of ops compiled from the window's
+// events, one lane per event, before the walk starts: REG applies a run in
+// the binade it names (S's count m must lie in [L, H(m's parity)], then m
+// grows by r(parity)), CROSS adds a located crossing term with one fp64 add
+// after checking that the crossing is where the tile found it for this S,
+// FAIL stands for a tile whose records give no O(1) step.  An event (a
+// regular segment, or an irregular tile's step: run A, then per crossing a
+// CROSS and the REG of the rest in the next binade) is one to five ops;
+// where one fails, the event's chunks are walked from the sum before it.
+constexpr int kOpWords = 9;
+constexpr uint32_t kOpReg = 1, kOpCross = 2, kOpFail = 3;
+// word 0: kind | key << 2 | first << 14 | last << 15 | down << 16 |
+// j0 << 17 | nodesc << 18 | ops after this one in its event << 19
+// REG: L, H0, H1, r0, r1.  CROSS: L of the prefix check, the pairs before
+// and through the crossing term (r0, r1 each), H of the prefix check, the
+// term's bits.  Word 8: the event's chunks, c_lo | c_hi << 32.  Words 1,
+// 2 + parity and 4 + parity are read for either kind.
+constexpr uint32_t kOpFirst = 1u << 14, kOpLast = 1u << 15, kOpDown = 1u << 16, kOpJ0 = 1u << 17,
+                   kOpNoDesc = 1u << 18;
+constexpr int kOpRestShift = 19;
+
+struct FinLds {
+    uint32_t kk[kFinTiles];  // per tile of the window: kind << 16 | key
+    FinEv ev[kEvCap];
+    uint64_t rec[kStepCap][kStepWords];
+    uint64_t ops[kOpCap][kOpWords];
+    int32_t ne_cut, nops;
+    struct {
+        uint64_t sbits;
+        int32_t i;
+        uint32_t fast, fb_lo, fb_hi, fb_desc;
+    } wk;  // where wave 0's walk stopped
+    SegPair wp[kWaves];
+    SegBound wb[kWaves];
+    int32_t cnt[kWaves];
+    int32_t steps[kWaves];
+    uint32_t nf[kWaves];
+    FinTally tally;
+};
+
+// The workgroup's 32 KB of role-dependent LDS: a tile's last four chunks, the
+// head's chunk terms, or the finisher's window and chunk terms.
+constexpr int kUnionDoubles = kHalf * kChunk;
+constexpr int kFinTermsOff = (int)((sizeof(FinLds) + 15) / 16 * 2);  // in doubles
+static_assert(kFinTermsOff + kChunk <= kUnionDoubles, "the finisher's LDS fits the union");
+
+// ---------------------------------------------------------------------------
+// Device-coherent words
+// ---------------------------------------------------------------------------
+// A record's data words are acknowledged before its tagged first word is
+// written: each storing wave waits for its stores to complete (a
+// workgroup-scope release, which is only that wait), then the workgroup
+// meets at a barrier, then one lane writes the tagged word.
+__device__ __forceinline__ void stores_complete()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+}
+__device__ __forceinline__ uint32_t load_relaxed_u32(const uint32_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_relaxed_u32(uint32_t *p, uint32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int64_t load_relaxed_i64(const int64_t *p)
+{
+    return (int64_t)load_relaxed_u64(reinterpret_cast<const uint64_t *>(p));
+}
+
+// A chunk's descriptor (as store_desc), with device-coherent stores.
+__device__ __forceinline__ void store_desc_coherent(const DescArrays &d, size_t c, uint32_t key,
+                                                    const WaveRun &r, uint32_t extra)
+{
+    const int64_t dr = r.p.r1 - r.p.r0;
+    store_relaxed_u64(reinterpret_cast<uint64_t *>(d.r0 + c), (uint64_t)r.p.r0);
+    store_relaxed_u64(reinterpret_cast<uint64_t *>(d.lo + c), (uint64_t)r.lo);
+    store_relaxed_u64(reinterpret_cast<uint64_t *>(d.hi + c), (uint64_t)r.hi);
+    store_relaxed_u32(d.meta + c,
+                      (key & kKeyMask) | ((uint32_t)(dr + 1) << kDrShift) | r.flags | extra);
+}
+
+__device__ __forceinline__ uint32_t chunks_of_n(size_t n) { return (uint32_t)((n + kChunk - 1) / kChunk); }
+__device__ __forceinline__ int chunk_len(size_t n, size_t c)
+{
+    const size_t b = c * kChunk;
+    return (int)(n - b < (size_t)kChunk ? n - b : (size_t)kChunk);
+}
+
+// ---------------------------------------------------------------------------
+// A tile's last four chunks in LDS.  Lane l of wave w keeps terms 4l, 4l+1 of
+// slot k at stage[k*1024 + w*256 + 2l] and terms 4l+2, 4l+3 at 128 doubles
+// further (the layout of a 16-byte global-to-LDS load: lane l's 16 bytes at
+// 16 l from the wave's base).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double *stage_at(double *stage, int k, int half)
+{
+    return stage + k * kChunk + wave_id() * 256 + half * 128;
+}
+
+// Requests lane t's terms of chunk c into slot k: directly into LDS where
+// the chunk's terms all exist and are 16-byte aligned, else through
+// registers (missing terms are +0.0).
+__device__ __forceinline__ void stage_chunk(double *stage, int k, const SumView &v, size_t c, bool direct)
+{
+    const size_t first = c * kChunk + 4 * (size_t)threadIdx.x;
+    const int lane = lane_id();
+    if (direct) {
+        const double *p = v.x + first;
+        __builtin_amdgcn_global_load_lds((const void *)p,
+                                         (__attribute__((address_space(3))) void *)stage_at(stage, k, 0),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)(p + 2),
+                                         (__attribute__((address_space(3))) void *)stage_at(stage, k, 1),
+                                         16, 0, 0);
+    } else {
+        const Four f = load_four(v.x, v.n, first, true);
+        double *a = stage_at(stage, k, 0) + 2 * lane;
+        double *b = stage_at(stage, k, 1) + 2 * lane;
+        a[0] = f.v[0];
+        a[1] = f.v[1];
+        b[0] = f.v[2];
+        b[1] = f.v[3];
+    }
+}
+
+// Lane t's four terms of chunk c from slot k.
+__device__ __forceinline__ Four staged_chunk(double *stage, int k, size_t n, size_t c)
+{
+    const int lane = lane_id();
+    const double *a = stage_at(stage, k, 0) + 2 * lane;
+    const double *b = stage_at(stage, k, 1) + 2 * lane;
+    Four f;
+    f.v[0] = a[0];
+    f.v[1] = a[1];
+    f.v[2] = b[0];
+    f.v[3] = b[1];
+    const size_t first = c * kChunk + 4 * (size_t)threadIdx.x;
+    f.cnt = first < n ? (int)(n - first < 4 ? n - first : 4) : 0;
+    return f;
+}
+
+// ---------------------------------------------------------------------------
+// The plan: two-level look-back
+// ---------------------------------------------------------------------------
+// Level 1 (one wave): the p tile words before this tile in its group (at
+// st).  Returns whether an inclusive prefix was among them; val is that
+// prefix plus the sums of the tiles after it, else the sum of all p tiles.
+// False in ok on a timeout.
+__device__ __forceinline__ bool lb_level1(const uint64_t *st, int p, uint32_t epoch, double &val,
+                                          bool &ok)
+{
+    const int lane = lane_id();
+    ok = true;
+    val = 0.0;
+    if (p == 0)
+        return false;
+    const uint64_t need = (p >= 64) ? ~0ULL : ((1ULL << p) - 1);
+    for (int spin = 0;; spin++) {
+        const uint64_t w = lane < p ? load_relaxed_u64(st + lane) : 0;
+        const uint64_t fl = lane < p ? st_flag(w, epoch) : 0;
+        const uint64_t present = __ballot(fl != 0) & need;
+        const uint64_t incl = __ballot(fl == kStIncl) & need;
+        if (incl) {
+            const int j = 63 - __builtin_clzll(incl);
+            const uint64_t above = need & ~((j == 63) ? ~0ULL : ((2ULL << j) - 1));
+            if ((present & above) == above) {
+                val = wave_sum_f64(lane >= j && lane < p ? st_value(w) : 0.0);
+                return true;
+            }
+        }
+        if (present == need) {
+            val = wave_sum_f64(lane < p ? st_value(w) : 0.0);
+            return false;
+        }
+        if (spin >= kSpinLimit) {
+            ok = false;
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// Level 2 (one wave): the prefix before group lg from the group words before
+// it (decoupled look-back: the nearest inclusive prefix plus the group sums
+// after it).  Gives up when `stop` is set (level 1 found an inclusive
+// prefix) or on a timeout (ok false).
+__device__ __forceinline__ double lb_level2(const uint64_t *gst, uint32_t lg, uint32_t epoch,
+                                            volatile int *stop, bool &ok)
+{
+    const int lane = lane_id();
+    ok = true;
+    double acc = 0.0;
+    int64_t j = (int64_t)lg - 1;
+    for (int spin = 0;; spin++) {
+        if (*stop)
+            return 0.0;
+        const int64_t idx = j - lane;
+        uint64_t fl;
+        double v;
+        if (idx >= 0) {
+            const uint64_t w = load_relaxed_u64(gst + idx);
+            fl = st_flag(w, epoch);
+            v = st_value(w);
+        } else {
+            fl = kStIncl;  // before the sum's first group: nothing
+            v = 0.0;
+        }
+        const uint64_t missing = __ballot(fl == 0);
+        const uint64_t incl = __ballot(fl == kStIncl);
+        const int first_missing = missing ? __builtin_ctzll(missing) : 64;
+        const int first_incl = incl ? __builtin_ctzll(incl) : 64;
+        if (first_incl < first_missing) {
+            acc += wave_sum_f64(lane <= first_incl ? v : 0.0);
+            return acc;
+        }
+        if (!missing) {
+            acc += wave_sum_f64(v);
+            j -= 64;
+            continue;
+        }
+        if (spin >= kSpinLimit) {
+            ok = false;
+            return 0.0;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Building blocks of the head and the finisher
+// ---------------------------------------------------------------------------
+// Chunk f's run under `key` (all 256 lanes; the same result everywhere).
+__device__ __forceinline__ WaveRun block_run(const Four &f, uint32_t key, WaveRun *part)
+{
+    const WaveRun w = wave_run(f, key);
+    if (lane_id() == 0)
+        part[wave_id()] = w;
+    __syncthreads();
+    const WaveRun r = clamp_run(join_waves(part));
+    __syncthreads();
+    return r;
+}
+
+// The finisher composes the regular tiles of a segment with two segmented
+// scans instead of one of whole runs, which needs far fewer registers.
+// First the pairs (the parity-dependent increments), ordered; then the
+// prefix bounds, which compose as a prefix minimum and maximum: a segment's
+// lowest prefix is the least over its tiles of (the smaller component of
+// the pair before the tile + the tile's lowest prefix), its highest the
+// greatest of (the larger component + the tile's largest prefix), exactly as
+// run_compose folds them one at a time.
+
+__device__ __forceinline__ SegPair segp_op(const SegPair &l, const SegPair &r)
+{
+    if (r.head)
+        return r;
+    return SegPair{compose(l.p, r.p), l.start, l.head};
+}
+__device__ __forceinline__ SegBound segb_op(const SegBound &l, const SegBound &r)
+{
+    if (r.head)
+        return r;
+    return SegBound{l.lo < r.lo ? l.lo : r.lo, l.hi > r.hi ? l.hi : r.hi, l.flags | r.flags, l.head};
+}
+
+template <int Ctrl, int RowMask = 0xF>
+__device__ __forceinline__ SegPair dpp_segp(const SegPair &v)
+{
+    return SegPair{dpp_pair<Ctrl, RowMask>(v.p),
+                   (int32_t)dpp_u32<Ctrl, RowMask>((uint32_t)v.start, 0xFFFFFFFFu),
+                   (int32_t)dpp_u32<Ctrl, RowMask>((uint32_t)v.head, 0u)};
+}
+template <int Ctrl, int RowMask = 0xF>
+__device__ __forceinline__ SegBound dpp_segb(const SegBound &v)
+{
+    // lanes without a source take the identity: no bound (0 is inside every
+    // segment's range already, since the empty prefix counts)
+    return SegBound{dpp_i64<Ctrl, RowMask>(v.lo, 0), dpp_i64<Ctrl, RowMask>(v.hi, 0),
+                    dpp_u32<Ctrl, RowMask>(v.flags, 0u),
+                    (int32_t)dpp_u32<Ctrl, RowMask>((uint32_t)v.head, 0u)};
+}
+
+// Exclusive ordered segmented scans over the workgroup's lanes (one barrier
+// each): lane t gets the composition of lanes 0 .. t-1.
+__device__ __forceinline__ SegPair block_excl_segp(const SegPair &v, FinLds &F)
+{
+    const int lane = lane_id(), wave = wave_id();
+    SegPair inc = v;
+    inc = segp_op(dpp_segp<kDppRowShr1>(inc), inc);
+    inc = segp_op(dpp_segp<kDppRowShr2>(inc), inc);
+    inc = segp_op(dpp_segp<kDppRowShr4>(inc), inc);
+    inc = segp_op(dpp_segp<kDppRowShr8>(inc), inc);
+    inc = segp_op(dpp_segp<kDppRowBcast15, 0xA>(inc), inc);
+    inc = segp_op(dpp_segp<kDppRowBcast31, 0xC>(inc), inc);
+    if (lane == 63)
+        F.wp[wave] = inc;
+    const SegPair before = dpp_segp<kDppWaveShr1>(inc);  // lane 0: the identity
+    __syncthreads();
+    SegPair carry{pair_identity(), -1, 0};
+    for (int k = 0; k < kWaves; k++)
+        if (k < wave)
+            carry = segp_op(carry, F.wp[k]);
+    return segp_op(carry, before);
+}
+__device__ __forceinline__ SegBound block_excl_segb(const SegBound &v, FinLds &F)
+{
+    const int lane = lane_id(), wave = wave_id();
+    SegBound inc = v;
+    inc = segb_op(dpp_segb<kDppRowShr1>(inc), inc);
+    inc = segb_op(dpp_segb<kDppRowShr2>(inc), inc);
+    inc = segb_op(dpp_segb<kDppRowShr4>(inc), inc);
+    inc = segb_op(dpp_segb<kDppRowShr8>(inc), inc);
+    inc = segb_op(dpp_segb<kDppRowBcast15, 0xA>(inc), inc);
+    inc = segb_op(dpp_segb<kDppRowBcast31, 0xC>(inc), inc);
+    if (lane == 63)
+        F.wb[wave] = inc;
+    const SegBound before = dpp_segb<kDppWaveShr1>(inc);
+    __syncthreads();
+    SegBound carry{0, 0, 0u, 0};
+    for (int k = 0; k < kWaves; k++)
+        if (k < wave)
+            carry = segb_op(carry, F.wb[k]);
+    return segb_op(carry, before);
+}
+
+// The finisher's fallback: the ordered walk over the descriptors of chunks
+// [c_lo, c_hi) of the sum from the exact sum S before c_lo, one chunk per
+// lane, 256 at a time.  A scan of the pairs from the first chunk not yet
+// applied gives every chunk's start count in the running sum's binade,
+// every chunk is checked there, the first that fails is applied in the next
+// binade if the runs before it ended exactly on 2^(e+1), else added term by
+// term from the exact sum, and the next scan starts after it.  With
+// use_desc false (a record or the head's sum never came) every chunk is added
+// term by term.  Counts go to `tally` (lane 0).  Inlined: as a call, every
+// value of the finisher live across it would be spilled to scratch memory and
+// reloaded in the event loop.
+template <class Src>
+__device__ __forceinline__ double walk_lean(const Src &src, const SumView v, const DescArrays d,
+                                         uint32_t c_lo, uint32_t c_hi, double S, WalkCore &sh,
+                                         double *terms, int *lds_src, bool use_desc,
+                                         FinTally &tally)
+{
+    const int t = threadIdx.x;
+    const size_t n = v.n;
+    const size_t cb = v.cb;
+    int buf = 0;
+    uint64_t n_fast = 0, n_fb = 0, fb_terms = 0;
+    uint32_t misses = 0;
+    int64_t first = -1;
+    bool nonfinite = false;
+    __syncthreads();  // the caller's last reads of the scratch are done
+    for (uint32_t base = c_lo; base < c_hi; base += kChunkThreads) {
+        const int cnt = (int)(c_hi - base < (uint32_t)kChunkThreads ? c_hi - base : (uint32_t)kChunkThreads);
+        Pair mine = pair_identity();
+        int64_t dlo = 0, dhi = 0;
+        uint32_t dkey = 0u, dfl = kFlagBad;
+        if (t < cnt && use_desc) {
+            const size_t c = cb + base + (size_t)t;
+            const uint32_t mt = load_relaxed_u32(d.meta + c);
+            const int64_t r0 = load_relaxed_i64(d.r0 + c);
+            mine = Pair{r0, r0 + (int64_t)((mt >> kDrShift) & 3u) - 1};
+            dkey = mt & kKeyMask;
+            dfl = mt & (kFlagNeg | kFlagBad | kFlagNonFinite);
+            if (dfl & kFlagNeg) {
+                dlo = load_relaxed_i64(d.lo + c);
+                dhi = load_relaxed_i64(d.hi + c);
+            }
+        }
+        nonfinite |= __syncthreads_or(t < cnt && (dfl & kFlagNonFinite)) != 0;
+        int cur = 0;
+        while (cur < cnt) {
+            const bool in = t >= cur && t < cnt;
+            const Pair pv = in ? mine : pair_identity();
+            const Pair X = block_excl_scan(pv, in && mine.r0 != mine.r1, sh, buf);
+            buf ^= 1;
+            const uint32_t ks = key_of(S);
+            const bool fs = key_has_fast_path(ks);
+            const int64_t m = count_of(S);
+            const int64_t mt = m + pair_at(X, m);
+            const bool ok = fs && dkey == ks && mt >= kCountLo && mt < kCountHi &&
+                            run_applies(mt, mine, dlo, dhi, dfl);
+            Cand mc = cand_none();
+            if (in && !ok) {
+                mc.idx = t;
+                mc.s_at = t == cur ? S : assemble(ks, mt);
+            }
+            if (t == cnt - 1)
+                sh.endv[buf] = ok ? assemble(ks, mt + pair_at(mine, mt)) : 0.0;
+            const Cand fc = block_first(in && !ok, mc, sh, buf);
+            const double endv = sh.endv[buf];
+            buf ^= 1;
+            if (fc.idx == kNone) {
+                n_fast += (uint64_t)(cnt - cur);
+                S = bitsd(uniform_u64(dbits(endv)));
+                break;
+            }
+            const int f = __builtin_amdgcn_readfirstlane(fc.idx);
+            n_fast += (uint64_t)(f - cur);
+            const double sat = bitsd(uniform_u64(dbits(fc.s_at)));
+            const size_t c = cb + base + (size_t)f;
+            const uint32_t fmt = use_desc ? load_relaxed_u32(d.meta + c) : kFlagBad;
+            const int64_t fr0 = use_desc ? load_relaxed_i64(d.r0 + c) : 0;
+            const Pair fp{fr0, fr0 + (int64_t)((fmt >> kDrShift) & 3u) - 1};
+            const uint32_t ffl = fmt & (kFlagNeg | kFlagBad | kFlagNonFinite);
+            const int64_t flo = use_desc && (ffl & kFlagNeg) ? load_relaxed_i64(d.lo + c) : 0;
+            const int64_t fhi = use_desc && (ffl & kFlagNeg) ? load_relaxed_i64(d.hi + c) : 0;
+            const uint32_t k2 = key_of(sat);
+            const int64_t m2 = count_of(sat);
+            if (key_has_fast_path(k2) && (fmt & kKeyMask) == k2 && run_applies(m2, fp, flo, fhi, ffl)) {
+                S = assemble(k2, m2 + pair_at(fp, m2));
+                n_fast++;
+            } else {
+                misses += (fmt & kKeyMask) != k2;
+                const uint32_t cc = base + (uint32_t)f;
+                const Four fr = src.chunk_v(v, cc, lds_src);
+                if (!use_desc) {
+                    bool nf = false;
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        nf |= i < fr.cnt && is_nonfinite(fr.v[i]);
+                    nonfinite |= __syncthreads_or(nf) != 0;
+                }
+                S = resolve_terms(fr, chunk_len(n, cc), sat, 0, sh, terms, buf);
+                S = bitsd(uniform_u64(dbits(S)));
+                n_fb++;
+                fb_terms += (uint64_t)chunk_len(n, cc);
+                if (first < 0)
+                    first = (int64_t)cc;
+            }
+            cur = f + 1;
+        }
+    }
+    __syncthreads();
+    if (t == 0) {
+        tally.fast += n_fast;
+        tally.fb += n_fb;
+        tally.terms += fb_terms;
+        if (tally.first < 0 && first >= 0)
+            tally.first = first;
+        tally.misses += misses;
+        tally.nonfinite |= nonfinite ? 1u : 0u;
+    }
+    __syncthreads();
+    return S;
+}
+
+// ---------------------------------------------------------------------------
+// The head: a sum's first tile (its first four chunks) from init, exactly.
+// A sum without terms is its init.
+// ---------------------------------------------------------------------------
+template <class Src>
+__device__ __forceinline__ void head_block(const PassArgs &pa, const Src &src, const PassWs &w,
+                                           int s, PassTileLds &L, WalkCore &sc, double *terms,
+                                           int *lds_src)
+{
+    const BatchArgs &a = pa.b;
+    const int t = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const size_t n = a.n[s];
+    exseq_stats *stats = pa.stats ? pa.stats + s : nullptr;
+    if (n == 0) {
+        if (t == 0) {
+            pa.outs[s] = a.init[s];
+            if (stats) {
+                exseq_stats st;
+                st.chunks = st.fast_chunks = st.fallback_chunks = st.fallback_terms = 0;
+                st.first_fallback = -1;
+                st.flags = 0u;
+                st.plan_misses = 0u;
+                stats[0] = st;
+            }
+        }
+        return;
+    }
+    const uint32_t nch = chunks_of_n(n);
+    const uint32_t nt = tiles_of(nch);
+    const int nk = (int)(nch < (uint32_t)kHeadCh ? nch : (uint32_t)kHeadCh);
+    const SumView v{a.x[s], n, a.init[s], a.chunk_base[s], nch};
+    Four f[kHeadCh];
+#pragma unroll
+    for (int k = 0; k < kHeadCh; k++)
+        f[k] = src.chunk_v(v, (size_t)k, lds_src);
+    bool nf = false;
+#pragma unroll
+    for (int k = 0; k < kHeadCh; k++)
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            nf |= i < f[k].cnt && is_nonfinite(f[k].v[i]);
+    // the tile's inclusive plan prefix (the same fixed tree as every tile's)
+    if (nt > 1 && (a.flags & EXSEQ_PLAN_MASK) != EXSEQ_PLAN_FIXED) {
+        double ws[kHeadCh];
+#pragma unroll
+        for (int k = 0; k < kHeadCh; k++)
+            ws[k] = (f[k].v[0] + f[k].v[1]) + (f[k].v[2] + f[k].v[3]);
+        wave_sum_f64_n<kHeadCh>(ws);
+        if (lane == 0) {
+#pragma unroll
+            for (int k = 0; k < kHeadCh; k++)
+                L.wsum[k][wave] = ws[k];
+        }
+        __syncthreads();
+        if (t == 0) {
+            double Ttile = 0.0;
+#pragma unroll
+            for (int k = 0; k < kHeadCh; k++)
+                Ttile += (L.wsum[k][0] + L.wsum[k][1]) + (L.wsum[k][2] + L.wsum[k][3]);
+            store_relaxed_u64(w.st + pa.tile_base[s], st_pack(a.epoch, kStIncl, a.init[s] + Ttile));
+        }
+    }
+    nf = __syncthreads_or(nf) != 0;
+    int buf = 0;
+    double S = a.init[s];
+    uint32_t resolved = 0u;
+#pragma unroll 1
+    for (int k = 0; k < nk; k++) {
+        // chunk k's terms, by unrolled selects (no indexed register array)
+        Four fk = f[0];
+#pragma unroll
+        for (int j = 1; j < kHeadCh; j++)
+            if (j == k)
+                fk = opaque(f[j]);
+        const uint32_t ks = key_of(S);
+        bool applied = false;
+        if (k > 0 && key_has_fast_path(ks)) {
+            const WaveRun r = block_run(fk, ks, &L.wrun[0][0]);
+            const int64_t m = count_of(S);
+            if (run_applies(m, r.p, r.lo, r.hi, r.flags)) {
+                S = assemble(ks, m + pair_at(r.p, m));
+                applied = true;
+            }
+        }
+        if (!applied) {
+            S = resolve_terms(fk, chunk_len(n, (size_t)k), S, 0, sc, terms, buf);
+            S = bitsd(uniform_u64(dbits(S)));
+            resolved |= 1u << k;
+        }
+    }
+    if (t != 0)
+        return;
+    if (nt == 1) {
+        pa.outs[s] = S;
+        if (stats) {
+            exseq_stats st;
+            st.chunks = nch;
+            st.fallback_chunks = (uint64_t)__builtin_popcount(resolved);
+            st.fast_chunks = nch - st.fallback_chunks;
+            uint64_t ft = 0;
+            for (int k = 0; k < nk; k++)
+                if ((resolved >> k) & 1u)
+                    ft += (uint64_t)chunk_len(n, (size_t)k);
+            st.fallback_terms = ft;
+            st.first_fallback = 0;
+            st.flags = nf ? EXSEQ_STAT_NONFINITE : 0u;
+            st.plan_misses = 0u;
+            stats[0] = st;
+        }
+        return;
+    }
+    uint64_t *hrec = w.hrec + 2 * (size_t)s;
+    store_relaxed_u64(hrec + 1, dbits(S));
+    stores_complete();
+    store_relaxed_u64(hrec, (pa.tag << kTagShift) | (nf ? 16u : 0u) | (uint64_t)resolved);
+}
+
+// Writes a REG op for a run (pair p, prefix bounds lo/hi, flags) in binade
+// key; a run that cannot apply becomes FAIL.
+__device__ __forceinline__ void op_reg(uint64_t *o, uint32_t key, Pair p, int64_t lo, int64_t hi,
+                                       uint32_t flags, uint64_t head, uint64_t range)
+{
+    if ((flags & (kFlagBad | kFlagNonFinite)) || !key_has_fast_path(key)) {
+        o[0] = kOpFail | head;
+        o[8] = range;
+        return;
+    }
+    const bool neg = (flags & kFlagNeg) != 0;
+    o[0] = kOpReg | ((uint64_t)(key & kKeyMask) << 2) | head;
+    o[1] = (uint64_t)(neg ? kCountLo + 1 - lo : (int64_t)0);
+    o[2] = (uint64_t)(neg ? kCountHi - 1 - hi : kCountHi - p.r0);
+    o[3] = (uint64_t)(neg ? kCountHi - 1 - hi : kCountHi - p.r1);
+    o[4] = (uint64_t)p.r0;
+    o[5] = (uint64_t)p.r1;
+    o[8] = range;
+}
+
+// The number of ops of a step record (word 0 of it).
+__device__ __forceinline__ int step_ops(uint64_t m0) { return (int)((m0 >> 12) & 1u) + 2 * (int)((m0 >> 13) & 3u); }
+
+// Writes the ops of a step record rw (run A, then per crossing CROSS and the
+// REG of the rest of its chunk and the chunks folded in after it).
+__device__ __forceinline__ void op_step(uint64_t (*o)[kOpWords], const uint64_t *rw, uint64_t range)
+{
+    const uint64_t m0 = rw[0];
+    const int nops = step_ops(m0);
+    int k = 0;
+    auto head = [&](int k) {
+        return (k == 0 ? (uint64_t)kOpFirst : 0u) | (k == nops - 1 ? (uint64_t)kOpLast : 0u) |
+               ((uint64_t)(nops - 1 - k) << kOpRestShift);
+    };
+    if ((m0 >> 12) & 1u) {
+        const int64_t r0 = dec_i64(rw[1]);
+        op_reg(o[k], (uint32_t)m0 & kKeyMask, Pair{r0, r0 + (int64_t)((m0 >> 17) & 3u) - 1},
+               dec_i64(rw[2]), dec_i64(rw[3]), (uint32_t)((m0 >> 15) & 3u) << 14, head(k), range);
+        k++;
+    }
+    const int nx = (int)((m0 >> 13) & 3u);
+    for (int j = 0; j < nx; j++) {
+        const uint64_t *x = rw + 4 + kXrecW * j;
+        const uint64_t xm = x[0];
+        const uint32_t key = (uint32_t)xm & kKeyMask;
+        const bool down = ((xm >> 12) & 1u) != 0;
+        const bool neg = ((xm >> 13) & 1u) != 0 || down;
+        const int len = (int)((xm >> 16) & 0x7FFu);
+        const int64_t jj = dec_i64(x[1 + kXj]);
+        const uint32_t key2 = down ? key - 1u : key + 1u;
+        uint64_t *c = o[k];
+        if (jj >= len || !key_has_fast_path(key) || !key_has_fast_path(key2)) {
+            c[0] = kOpFail | head(k);
+        } else {
+            const Pair pj1 = rec_unpack(dec_i64(x[1 + kXpj1]));
+            const Pair pj = rec_unpack(dec_i64(x[1 + kXpj]));
+            c[0] = kOpCross | ((uint64_t)key << 2) | head(k) | (down ? (uint64_t)kOpDown : 0u) |
+                   (jj == 0 ? (uint64_t)kOpJ0 : 0u);
+            c[1] = (uint64_t)(neg ? kCountLo + 1 - dec_i64(x[1 + kXpreLo]) : (int64_t)0);
+            c[2] = (uint64_t)pj1.r0;
+            c[3] = (uint64_t)pj1.r1;
+            c[4] = (uint64_t)pj.r0;
+            c[5] = (uint64_t)pj.r1;
+            c[6] = (uint64_t)(neg ? kCountHi - 1 - dec_i64(x[1 + kXpreHi]) : kCountHi);
+            c[7] = x[1 + kXterm] ^ kInclXor;
+        }
+        c[8] = range;
+        k++;
+        op_reg(o[k], key2, rec_unpack(dec_i64(x[1 + kXsuf])), dec_i64(x[1 + kXsufLo]),
+               dec_i64(x[1 + kXsufHi]), neg ? kFlagNeg : 0u, head(k), range);
+        k++;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The finisher of sum s
+// ---------------------------------------------------------------------------
+template <class Src>
+__device__ __forceinline__ void finisher_block(const PassArgs &pa, const Src &src, const PassWs &w,
+                                               int s, FinLds &F, WalkCore &sc, double *terms,
+                                               int *lds_src)
+{
+    const BatchArgs &a = pa.b;
+    const int t = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const size_t n = a.n[s];
+    const uint32_t nch = chunks_of_n(n);
+    const uint32_t nt = tiles_of(nch);
+    if (nt <= 1)
+        return;  // the head wrote the result
+    const SumView v{a.x[s], n, a.init[s], a.chunk_base[s], nch};
+    const uint32_t tb = pa.tile_base[s];
+    const uint64_t tag = pa.tag;
+    uint64_t n_fast = 0, n_fb = 0, fb_terms = 0;
+    int64_t first_fb = -1;
+    bool nonfinite = false;
+    if (t == 0) {
+        F.tally.fast = F.tally.fb = F.tally.terms = 0;
+        F.tally.first = -1;
+        F.tally.misses = F.tally.nonfinite = 0;
+    }
+    // a chunk range the finisher walks from its descriptors (fb_desc) or
+    // term by term: [fb_lo, fb_hi)
+    uint32_t fb_lo = 0, fb_hi = 0;
+    bool fb_desc = false;
+
+    // the head's exact sum after the first tile
+    double S = a.init[s];
+    {
+        uint64_t h0 = 0;
+        for (int spin = 0; spin <= kSpinLimit; spin++) {
+            h0 = uniform_u64(load_relaxed_u64(w.hrec + 2 * (size_t)s));
+            if ((h0 >> kTagShift) == tag)
+                break;
+            __builtin_amdgcn_s_sleep(2);
+        }
+        const uint32_t nk0 = nch < (uint32_t)kHeadCh ? nch : (uint32_t)kHeadCh;
+        if ((h0 >> kTagShift) == tag) {
+            S = bitsd(uniform_u64(load_relaxed_u64(w.hrec + 2 * (size_t)s + 1)));
+            const uint32_t res = (uint32_t)h0 & 0xFu;
+            nonfinite |= ((h0 >> 4) & 1u) != 0;
+            for (uint32_t k = 0; k < nk0; k++) {
+                if ((res >> k) & 1u) {
+                    n_fb++;
+                    fb_terms += (uint64_t)chunk_len(n, k);
+                    if (first_fb < 0)
+                        first_fb = (int64_t)k;
+                } else {
+                    n_fast++;
+                }
+            }
+        } else {
+            fb_hi = nk0;  // the head's sum never came: its chunks term by term
+        }
+    }
+
+    uint32_t base = 1;
+    while (base < nt) {
+        const uint32_t cnt = nt - base < (uint32_t)kFinTiles ? nt - base : (uint32_t)kFinTiles;
+        // ---- this lane's tiles (q = kFinLane t + j in the window): their
+        // records, polled until their tags show
+        const uint32_t q0 = (uint32_t)(kFinLane * t);
+        const size_t g0 = (size_t)(tb + base) + q0;
+        uint64_t w0[kFinLane];
+        bool got[kFinLane];
+#pragma unroll
+        for (int j = 0; j < kFinLane; j++) {
+            w0[j] = 0;
+            got[j] = q0 + (uint32_t)j >= cnt;
+        }
+        for (int spin = 0; spin <= kSpinLimit; spin++) {
+            bool all = true;
+#pragma unroll
+            for (int j = 0; j < kFinLane; j++) {
+                if (!got[j]) {
+                    w0[j] = load_relaxed_u64(w.trec + 4 * (g0 + j));
+                    got[j] = (w0[j] >> kTagShift) == tag;
+                    all &= got[j];
+                }
+            }
+            if (all)
+                break;
+            __builtin_amdgcn_s_sleep(2);
+        }
+        uint32_t kk[kFinLane];  // kind << 16 | key
+        Pair rp[kFinLane];
+        int64_t rlo[kFinLane], rtop[kFinLane];
+        uint32_t rfl[kFinLane];
+        bool lane_nf = false;
+#pragma unroll
+        for (int j = 0; j < kFinLane; j++) {
+            const bool in = q0 + (uint32_t)j < cnt;
+            const bool ok = in && (w0[j] >> kTagShift) == tag;
+            const uint32_t kind = !in ? 0u : ok ? (uint32_t)(w0[j] >> 17) & 3u : kKindLost;
+            kk[j] = kind << 16 | (ok ? (uint32_t)w0[j] & kKeyMask : 0u);
+            lane_nf |= ok && ((uint32_t)w0[j] & kFlagNonFinite);
+            rp[j] = pair_identity();
+            rlo[j] = rtop[j] = 0;
+            rfl[j] = 0u;
+            if (kind == kKindReg) {
+                const uint64_t *r = w.trec + 4 * (g0 + j);
+                const int64_t r0 = dec_i64(load_relaxed_u64(r + 1));
+                rp[j] = Pair{r0, r0 + (int64_t)((w0[j] >> kDrShift) & 3u) - 1};
+                rlo[j] = dec_i64(load_relaxed_u64(r + 2));
+                rtop[j] = dec_i64(load_relaxed_u64(r + 3));
+                rfl[j] = (uint32_t)w0[j] & (kFlagNeg | kFlagBad);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kFinLane; j++) {
+            if ((kk[j] >> 16) == kKindReg)
+                rtop[j] = run_top(Run{rp[j], rlo[j], rtop[j], rfl[j]});
+            if (q0 + (uint32_t)j < cnt)
+                F.kk[q0 + j] = kk[j];
+        }
+        __syncthreads();
+        // ---- segments: a regular tile starts one unless the tile before it
+        // is regular with the same key; one ends where the next tile starts
+        // one, or at the window's end; every other tile is an event of its own
+        uint32_t heads = 0u, evs = 0u;
+        {
+            const uint32_t prev0 = q0 == 0 ? 0u : F.kk[q0 - 1];
+            const uint32_t next3 = q0 + kFinLane < cnt ? F.kk[q0 + kFinLane] : 0u;
+#pragma unroll
+            for (int j = 0; j < kFinLane; j++) {
+                const uint32_t q = q0 + (uint32_t)j;
+                if (q >= cnt)
+                    continue;
+                const uint32_t me = kk[j];
+                const bool reg = (me >> 16) == kKindReg;
+                const uint32_t prev = j == 0 ? prev0 : kk[j - 1];
+                const uint32_t nx = j + 1 < kFinLane ? kk[j + 1] : next3;
+                const bool head = !reg || q == 0 || (prev >> 16) != kKindReg || ((prev ^ me) & kKeyMask) != 0u;
+                const bool end = !reg || q + 1 >= cnt || (nx >> 16) != kKindReg || ((nx ^ me) & kKeyMask) != 0u;
+                heads |= (head ? 1u : 0u) << j;
+                evs |= (end ? 1u : 0u) << j;
+            }
+        }
+        // the segments' pairs: this lane's, then across lanes
+        SegPair sp{pair_identity(), -1, 0};
+#pragma unroll
+        for (int j = 0; j < kFinLane; j++) {
+            const bool h = (heads >> j) & 1u;
+            if (q0 + (uint32_t)j < cnt)
+                sp = segp_op(sp, SegPair{rp[j], h ? (int32_t)(q0 + j) : -1, h ? 1 : 0});
+        }
+        const SegPair pexc = block_excl_segp(sp, F);
+        // the prefix bounds: each tile's, from the pair before it in its segment
+        SegBound sb{0, 0, 0u, 0};
+        {
+            SegPair run = pexc;
+#pragma unroll
+            for (int j = 0; j < kFinLane; j++) {
+                if (q0 + (uint32_t)j >= cnt)
+                    continue;
+                const bool h = (heads >> j) & 1u;
+                const Pair pex = h ? pair_identity() : run.p;
+                run = segp_op(run, SegPair{rp[j], h ? (int32_t)(q0 + j) : -1, h ? 1 : 0});
+                const int64_t pmin = pex.r0 < pex.r1 ? pex.r0 : pex.r1;
+                const int64_t pmax = pex.r0 < pex.r1 ? pex.r1 : pex.r0;
+                sb = segb_op(sb, SegBound{pmin + rlo[j], pmax + rtop[j], rfl[j], h ? 1 : 0});
+            }
+        }
+        const SegBound bexc = block_excl_segb(sb, F);
+        // ---- events in order: offsets by a workgroup count
+        int nev = 0, nstep = 0;
+#pragma unroll
+        for (int j = 0; j < kFinLane; j++) {
+            const bool e = (evs >> j) & 1u;
+            nev += e;
+            nstep += e && (kk[j] >> 16) == kKindStep;
+        }
+        const int64_t packed = (int64_t)nev | ((int64_t)nstep << 32);
+        const int64_t incp = wave_incl_scan_i64(packed);
+        if (lane == 63) {
+            F.cnt[wave] = (int32_t)(incp & 0xFFFFFFFF);
+            F.steps[wave] = (int32_t)(incp >> 32);
+        }
+        const uint32_t wnf = __ballot(lane_nf) != 0;
+        if (lane == 0)
+            F.nf[wave] = wnf;
+        __syncthreads();
+        int ev_off = 0, st_off = 0, ev_tot = 0, st_tot = 0;
+        for (int k = 0; k < kWaves; k++) {
+            if (k < wave) {
+                ev_off += F.cnt[k];
+                st_off += F.steps[k];
+            }
+            ev_tot += F.cnt[k];
+            st_tot += F.steps[k];
+            nonfinite |= F.nf[k] != 0;
+        }
+        {
+            const int64_t ex = incp - packed;
+            ev_off += (int)(ex & 0xFFFFFFFF);
+            st_off += (int)(ex >> 32);
+        }
+        {
+            SegPair run = pexc;
+            SegBound bnd = bexc;
+#pragma unroll
+            for (int j = 0; j < kFinLane; j++) {
+                const uint32_t q = q0 + (uint32_t)j;
+                if (q >= cnt)
+                    continue;
+                const bool h = (heads >> j) & 1u;
+                const Pair pex = h ? pair_identity() : run.p;
+                run = segp_op(run, SegPair{rp[j], h ? (int32_t)q : -1, h ? 1 : 0});
+                const int64_t pmin = pex.r0 < pex.r1 ? pex.r0 : pex.r1;
+                const int64_t pmax = pex.r0 < pex.r1 ? pex.r1 : pex.r0;
+                bnd = segb_op(bnd, SegBound{pmin + rlo[j], pmax + rtop[j], rfl[j], h ? 1 : 0});
+                if (!((evs >> j) & 1u))
+                    continue;
+                const uint32_t kind = kk[j] >> 16;
+                if (ev_off < kEvCap) {
+                    FinEv e;
+                    e.tile = (int32_t)q;
+                    e.slot = kind == kKindStep && st_off < kStepCap ? st_off : -1;
+                    if (kind == kKindReg) {
+                        // a segment whose numbers grew past any binade never applies
+                        const int64_t lim = (int64_t)1 << 56;
+                        const int64_t dr = run.p.r1 - run.p.r0;
+                        const bool ok = dr >= -1 && dr <= 1 && run.p.r0 < lim && run.p.r0 > -lim &&
+                                        bnd.lo > -lim && bnd.hi < lim;
+                        e.r0 = ok ? run.p.r0 : 0;
+                        e.lo = ok ? bnd.lo : 0;
+                        e.hi = ok ? bnd.hi : 0;
+                        e.start = run.start;
+                        e.meta = (kk[j] & kKeyMask) | ((uint32_t)(ok ? dr + 1 : 1) << kDrShift) |
+                                 (bnd.flags & (kFlagNeg | kFlagBad)) | (ok ? 0u : kFlagBad) |
+                                 (kKindReg << 20);
+                    } else {
+                        e.r0 = e.lo = e.hi = 0;
+                        e.start = (int32_t)q;
+                        e.meta = kind << 20;
+                    }
+                    F.ev[ev_off] = e;
+                }
+                ev_off++;
+                st_off += kind == kKindStep;
+            }
+        }
+        __syncthreads();
+        // this window takes up to kEvCap events, and up to the first step
+        // without a record slot
+        int ne = ev_tot < kEvCap ? ev_tot : kEvCap;
+        if (st_tot > kStepCap) {
+            for (int e = 0; e < ne; e++) {
+                if ((F.ev[e].meta >> 20) == kKindStep && F.ev[e].slot < 0) {
+                    ne = e;
+                    break;
+                }
+            }
+        }
+        // the step records of this window, all requested at once
+        for (int q = t; q < ne * kStepWords; q += kChunkThreads) {
+            const int e = q / kStepWords, k = q - e * kStepWords;
+            const FinEv &ev = F.ev[e];
+            if ((ev.meta >> 20) == kKindStep && ev.slot >= 0 && ev.slot < kStepCap)
+                F.rec[ev.slot][k] = load_relaxed_u64(
+                    w.xrec + kStepWords * ((size_t)tb + base + (uint32_t)ev.tile) + k);
+        }
+        if (t == 0)
+            F.ne_cut = ne;
+        __syncthreads();
+        // ---- the walk's ops, one lane per event; the window ends before the
+        // first event whose ops do not fit
+        {
+            int nop = 0;
+            FinEv ev;
+            uint64_t range = 0;
+            if (t < ne) {
+                ev = F.ev[t];
+                const uint32_t kd = ev.meta >> 20;
+                nop = kd == kKindStep ? step_ops(F.rec[ev.slot][0]) : 1;
+                const uint32_t c_lo = tile_c0(base + (uint32_t)ev.start);
+                const uint32_t c_end = tile_c0(base + (uint32_t)ev.tile + 1);
+                range = (uint64_t)c_lo | (uint64_t)(c_end < nch ? c_end : nch) << 32;
+            }
+            const int64_t inc = wave_incl_scan_i64(nop);
+            if (lane == 63)
+                F.cnt[wave] = (int32_t)inc;
+            __syncthreads();
+            int off = (int)(inc - nop);
+            for (int k = 0; k < kWaves; k++)
+                if (k < wave)
+                    off += F.cnt[k];
+            if (t < ne) {
+                if (off + nop > kOpCap) {
+                    atomicMin(&F.ne_cut, t);
+                } else {
+                    const uint32_t kd = ev.meta >> 20;
+                    const uint64_t one = (uint64_t)kOpFirst | kOpLast;
+                    if (kd == kKindStep) {
+                        op_step(F.ops + off, F.rec[ev.slot], range);
+                    } else if (kd == kKindReg) {
+                        const uint32_t m = ev.meta;
+                        op_reg(F.ops[off], m & kKeyMask,
+                               Pair{ev.r0, ev.r0 + (int64_t)((m >> kDrShift) & 3u) - 1}, ev.lo,
+                               ev.hi, m & (kFlagNeg | kFlagBad), one, range);
+                    } else {
+                        F.ops[off][0] = kOpFail | one | (kd == kKindLost ? (uint64_t)kOpNoDesc : 0u);
+                        F.ops[off][8] = range;
+                    }
+                }
+            }
+            __syncthreads();
+            const int cut = F.ne_cut;
+            if (t == cut - 1)
+                F.nops = off + nop;
+            if (cut == 0 && t == 0)
+                F.nops = 0;
+            __syncthreads();
+            ne = cut;
+        }
+        // ---- the ordered walk over the ops: lane k holds word k of the
+        // current op and of the next; S as its bit pattern.  (One call site
+        // of the fallback walk: the first window's walk also takes the
+        // head's chunks when its sum never came.)
+        uint32_t next = ne > 0 ? base + (uint32_t)F.ev[ne - 1].tile + 1 : base;
+        {
+            const int nops = F.nops;
+            auto op_word = [&](int i) { return lane < kOpWords && i < nops ? F.ops[i][lane] : (uint64_t)0; };
+            auto W = [&](uint64_t v, int k) { return (uint64_t)readlane_i64((int64_t)v, k); };
+            int i = 0;
+            for (;;) {
+                if (fb_hi > fb_lo) {
+                    S = walk_lean(src, v, w.d, fb_lo, fb_hi, S, sc, terms, lds_src, fb_desc, F.tally);
+                    S = bitsd(uniform_u64(dbits(S)));
+                    fb_lo = fb_hi = 0;
+                }
+                if (i >= nops)
+                    break;
+                // ops until one fails (which leaves fb_lo/fb_hi set), on wave 0
+                // alone: the waves of a workgroup share one scalar unit
+                if (wave == 0) {
+                uint64_t sbits = uniform_u64(dbits(S));
+                uint64_t sev = sbits;
+                uint64_t cur = op_word(i);
+                uint32_t fast = 0;
+                while (i < nops) {
+                    const uint64_t nxt = op_word(i + 1);
+                    const uint32_t meta = (uint32_t)W(cur, 0);
+                    sev = (meta & kOpFirst) ? sbits : sev;
+                    const int64_t m = (int64_t)((sbits & kFracMask) | (1ull << 52));
+                    const int par = (int)(m & 1);
+                    const int64_t a = (int64_t)W(cur, 1), b = (int64_t)W(cur, 2 + par),
+                                  c = (int64_t)W(cur, 4 + par);
+                    // REG: m in [a, b], then m + c.  CROSS: m in [a, word 6], the
+                    // counts before (cb) and through (cj) the crossing term on
+                    // either side of the binade's edge, then the one plain add
+                    // from the exact sum before the term.
+                    const bool reg = (meta & 3u) == kOpReg;
+                    const int64_t cb = (meta & kOpJ0) ? m : m + b;
+                    const int64_t cj = m + c;
+                    const bool edge = (meta & kOpDown) ? (cb >= kCountLo) & (cj < kCountLo)
+                                                       : (cb <= kCountHi - 1) & (cj >= kCountHi);
+                    const bool okc = (m <= (int64_t)W(cur, 6)) & edge;
+                    const bool ok = ((uint32_t)(sbits >> 52) == ((meta >> 2) & kKeyMask)) &
+                                    ((meta & 3u) != kOpFail) & (m >= a) & (reg ? m <= b : okc);
+                    const uint64_t crossed =
+                        uniform_u64(dbits(bitsd(sbits + (uint64_t)(cb - m)) + bitsd(W(cur, 7))));
+                    const uint64_t after = reg ? sbits + (uint64_t)c : crossed;
+                    const uint64_t range = W(cur, 8);
+                    if (!ok) {
+                        // the event's chunks, from the sum before it
+                        fb_lo = (uint32_t)range;
+                        fb_hi = (uint32_t)(range >> 32);
+                        fb_desc = !(meta & kOpNoDesc);
+                        sbits = sev;
+                        i += 1 + (int)(meta >> kOpRestShift);
+                        break;
+                    }
+                    sbits = after;
+                    if (meta & kOpLast)
+                        fast += (uint32_t)(range >> 32) - (uint32_t)range;
+                    i++;
+                    cur = nxt;
+                }
+                if (lane == 0) {
+                    F.wk.sbits = sbits;
+                    F.wk.i = i;
+                    F.wk.fast = fast;
+                    F.wk.fb_lo = fb_lo;
+                    F.wk.fb_hi = fb_hi;
+                    F.wk.fb_desc = fb_desc;
+                }
+                }
+                __syncthreads();
+                S = bitsd(F.wk.sbits);
+                i = F.wk.i;
+                n_fast += F.wk.fast;
+                fb_lo = F.wk.fb_lo;
+                fb_hi = F.wk.fb_hi;
+                fb_desc = F.wk.fb_desc != 0;
+                __syncthreads();
+            }
+        }
+        if (ne == ev_tot)
+            next = base + cnt;
+        __syncthreads();  // the window's LDS is reused by the next one
+        base = next;
+    }
+    if (t == 0) {
+        pa.outs[s] = S;
+        if (pa.stats) {
+            const FinTally &ft = F.tally;
+            exseq_stats st;
+            st.chunks = nch;
+            st.fast_chunks = n_fast + ft.fast;
+            st.fallback_chunks = n_fb + ft.fb;
+            st.fallback_terms = fb_terms + ft.terms;
+            st.first_fallback = first_fb >= 0 ? first_fb : ft.first;
+            st.flags = (nonfinite || ft.nonfinite) ? EXSEQ_STAT_NONFINITE : 0u;
+            st.plan_misses = ft.misses;
+            pa.stats[s] = st;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// A tile after a sum's first: eight chunks
+// ---------------------------------------------------------------------------
+template <class Src>
+__device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, const PassWs &w,
+                                           int s, uint32_t i, PassTileLds &L, WalkCore &sc,
+                                           CrossLds &xl, double *stage, int *lds_src)
+{
+    const BatchArgs &a = pa.b;
+    const int t = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const size_t n = a.n[s];
+    const uint32_t nch = chunks_of_n(n);
+    const uint32_t c0 = tile_c0(i);
+    const int nk = (int)(nch - c0 < (uint32_t)kTileCh ? nch - c0 : (uint32_t)kTileCh);
+    const uint32_t mode = a.flags & EXSEQ_PLAN_MASK;
+    const uint64_t tag = pa.tag;
+    const uint32_t g = pa.tile_base[s] + i;           // the tile in the launch
+    const size_t gc0 = (size_t)a.chunk_base[s] + c0;  // its first chunk in the launch
+    const SumView v{a.x[s], n, a.init[s], a.chunk_base[s], nch};
+
+    if (t == 0)
+        L.lb_stop = 0;
+    // ---- the terms: four chunks into registers, four into LDS
+    Four f[kHalf];
+#pragma unroll
+    for (int k = 0; k < kHalf; k++)
+        f[k] = src.chunk_v(v, c0 + k, lds_src);
+    if (nk > kHalf) {
+        const bool direct = ((reinterpret_cast<uintptr_t>(v.x) & 15u) == 0u) &&
+                            (size_t)(c0 + kTileCh) * kChunk <= n;
+#pragma unroll
+        for (int k = 0; k < kHalf; k++)
+            stage_chunk(stage, k, v, c0 + kHalf + k, direct);
+    }
+    // ---- the fixed-tree sum of every chunk
+    {
+        double ws[kHalf];
+#pragma unroll
+        for (int k = 0; k < kHalf; k++)
+            ws[k] = (f[k].v[0] + f[k].v[1]) + (f[k].v[2] + f[k].v[3]);
+        wave_sum_f64_n<kHalf>(ws);
+        if (lane == 0) {
+#pragma unroll
+            for (int k = 0; k < kHalf; k++)
+                L.wsum[k][wave] = ws[k];
+        }
+    }
+    if (nk > kHalf) {
+        // each wave reads back only what its own loads put in LDS
+        __builtin_amdgcn_s_waitcnt(0);
+        double ws[kHalf];
+#pragma unroll
+        for (int k = 0; k < kHalf; k++) {
+            const Four q = staged_chunk(stage, k, n, c0 + kHalf + k);
+            ws[k] = (q.v[0] + q.v[1]) + (q.v[2] + q.v[3]);
+        }
+        wave_sum_f64_n<kHalf>(ws);
+        if (lane == 0) {
+#pragma unroll
+            for (int k = 0; k < kHalf; k++)
+                L.wsum[kHalf + k][wave] = ws[k];
+        }
+    } else if (lane == 0) {
+#pragma unroll
+        for (int k = 0; k < kHalf; k++)
+            L.wsum[kHalf + k][wave] = 0.0;
+    }
+    __syncthreads();
+    double T[kTileCh];
+    double Ttile = 0.0;
+#pragma unroll
+    for (int k = 0; k < kTileCh; k++) {
+        T[k] = (L.wsum[k][0] + L.wsum[k][1]) + (L.wsum[k][2] + L.wsum[k][3]);
+        Ttile += T[k];
+    }
+
+    // ---- the plan
+    uint64_t *st0 = w.st + pa.tile_base[s];
+    uint64_t *gs0 = w.gst + pa.group_base[s];
+    const uint32_t lg = i / kGroup, pg = i % kGroup;
+    double P = a.init[s];
+    if (mode != EXSEQ_PLAN_FIXED) {
+        if (wave == 0) {
+            if (lane == 0)
+                store_relaxed_u64(st0 + i, st_pack(a.epoch, kStAgg, Ttile));
+            double v1;
+            bool ok1;
+            const bool found = lb_level1(st0 + kGroup * lg, (int)pg, a.epoch, v1, ok1);
+            if (lane == 0) {
+                L.lb1 = v1;
+                L.lb_found = found;
+                L.lb_ok1 = ok1;
+                if (found || lg == 0)
+                    L.lb_stop = 1;
+                // the group's sum (or its inclusive prefix) as soon as known
+                if (pg == kGroup - 1 && ok1)
+                    store_relaxed_u64(gs0 + lg, st_pack(a.epoch, found ? kStIncl : kStAgg, v1 + Ttile));
+            }
+        } else if (wave == 1) {
+            bool ok2 = true;
+            double v2 = 0.0;
+            if (lg > 0)
+                v2 = lb_level2(gs0, lg, a.epoch, &L.lb_stop, ok2);
+            if (lane == 0) {
+                L.lb2 = v2;
+                L.lb_ok2 = ok2;
+            }
+        }
+        __syncthreads();
+        const bool found = L.lb_found != 0;
+        const bool ok = L.lb_ok1 && (found || (lg > 0 && L.lb_ok2));
+        P = !ok ? __builtin_nan("") : (found ? L.lb1 : L.lb2 + L.lb1);
+        if (t == 0 && ok) {
+            store_relaxed_u64(st0 + i, st_pack(a.epoch, kStIncl, P + Ttile));
+            if (pg == kGroup - 1)
+                store_relaxed_u64(gs0 + lg, st_pack(a.epoch, kStIncl, P + Ttile));
+        }
+    }
+    if (wave == 0 && lane < kTileCh) {
+        double pk = P, tk = T[0];
+#pragma unroll
+        for (int k = 0; k < kTileCh - 1; k++) {
+            if (k < lane)
+                pk += T[k];
+            if (k + 1 == lane)
+                tk = T[k + 1];
+        }
+        L.pk[lane] = pk;
+        L.key[lane] = plan_key(pk, a.flags);
+        L.cross[lane] = key_of(pk + tk) != key_of(pk);
+        L.down[lane] = ((key_of(pk + tk) ^ key_of(pk)) & 0x800u) == 0u &&
+                       (key_of(pk + tk) & 0x7FFu) < (key_of(pk) & 0x7FFu);
+    }
+    __syncthreads();
+
+    // ---- every chunk's run under its planned binade, half a tile at a time,
+    // and the crossings of the chunks planned to cross
+    uint32_t found = 0u;
+    int buf = 0;
+#pragma unroll 1
+    for (int h = 0; h < 2; h++) {
+        const int kb = h * kHalf;
+        if (kb >= nk)
+            break;
+        if (h == 1) {
+#pragma unroll
+            for (int k = 0; k < kHalf; k++)
+                f[k] = staged_chunk(stage, k, n, c0 + kHalf + k);
+        }
+        uint32_t key[kHalf];
+        bool allfast = true;
+#pragma unroll
+        for (int k = 0; k < kHalf; k++) {
+            key[k] = L.key[kb + k];
+            allfast &= key_has_fast_path(key[k]);
+        }
+        if (allfast) {
+            wave_runs<kHalf>(f, key, L.wrun);
+        } else {
+#pragma unroll
+            for (int k = 0; k < kHalf; k++) {
+                WaveRun wr;
+                if (key_has_fast_path(key[k])) {
+                    wr = wave_run(f[k], key[k]);
+                } else {
+                    bool nf = false;
+#pragma unroll
+                    for (int q = 0; q < 4; q++)
+                        nf |= is_nonfinite(f[k].v[q]);
+                    wr.p = pair_identity();
+                    wr.lo = wr.hi = 0;
+                    wr.flags = __ballot(nf) ? kFlagNonFinite : 0u;
+                }
+                if (lane == 0)
+                    L.wrun[k][wave] = wr;
+            }
+        }
+        __syncthreads();
+        if (t < kHalf) {
+            const int c = kb + t;
+            const uint32_t kk = L.key[c];
+            const double pk = L.pk[c];
+            bool cc = L.cross[c] != 0;
+            bool plain = true, fall = true;
+            int64_t sum = 0;
+#pragma unroll
+            for (int wv = 0; wv < kWaves; wv++) {
+                const WaveRun &q = L.wrun[t][wv];
+                plain &= rising_run(q.p, q.flags);
+                fall &= falling_run(q.p, q.lo, q.hi, q.flags);
+                sum += q.p.r0;
+            }
+            const WaveRun r = clamp_run(plain  ? WaveRun{Pair{sum, sum}, 0, sum, 0u}
+                                        : fall ? WaveRun{Pair{sum, sum}, sum, 0, kFlagNeg}
+                                               : join_waves(L.wrun[t]));
+            if (key_has_fast_path(kk) && kk == key_of(pk)) {
+                const int64_t m = count_of(pk);
+                const int64_t mg = plan_margin(c0 + c + 1);
+                bool near = m < kCountLo + mg;
+                if (r.flags & kFlagNeg)
+                    near |= m + r.lo - mg < kCountLo + 1 || m + r.hi + mg > kCountHi - 1;
+                else
+                    near |= m + r.hi + mg > kCountHi;
+                cc |= near;
+            }
+            L.join[c] = r;
+            L.cross[c] = cc;
+            if (c < nk)
+                store_desc_coherent(w.d, gc0 + (size_t)c, kk, r, cc ? kFlagCross : 0u);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kHalf; k++) {
+            const int c = kb + k;
+            const uint32_t fl = L.join[c].flags;
+            if (!(c < nk && L.cross[c] && key_has_fast_path(L.key[c]) && L.key[c] == key_of(L.pk[c]) &&
+                  key_has_fast_path(L.down[c] ? L.key[c] - 1u : L.key[c] + 1u) &&
+                  !(fl & kFlagNonFinite)))
+                continue;
+            uint64_t xw[kCrossWords];
+            if (crossing_find(f[k], chunk_len(n, c0 + c), L.key[c], count_of(L.pk[c]),
+                              L.down[c] != 0u, sc, xl, buf, xw)) {
+                found |= 1u << c;
+                if (t == 0) {
+#pragma unroll
+                    for (int q = 0; q < kCrossWords; q++)
+                        L.xw[c][q] = xw[q];
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- the tile's record
+    bool regular = true;
+#pragma unroll
+    for (int k = 0; k < kTileCh; k++)
+        if (k < nk)
+            regular &= key_has_fast_path(L.key[k]) && L.key[k] == L.key[0] && !L.cross[k] &&
+                       !(L.join[k].flags & (kFlagBad | kFlagNonFinite));
+    uint64_t *trec = w.trec + 4 * (size_t)g;
+    if (regular) {
+        // the chunks' runs in order (plain ones add up), by lane 0
+        Run tr = run_identity();
+        if (t == 0) {
+            bool plain = true, fall = true;
+            int64_t sum = 0;
+            for (int k = 0; k < nk; k++) {
+                const WaveRun &q = L.join[k];
+                plain &= rising_run(q.p, q.flags);
+                fall &= falling_run(q.p, q.lo, q.hi, q.flags);
+                sum += q.p.r0;
+            }
+            if (plain) {
+                tr = Run{Pair{sum, sum}, 0, sum, 0u};
+            } else if (fall) {
+                tr = Run{Pair{sum, sum}, sum, 0, kFlagNeg};
+            } else {
+                for (int k = 0; k < nk; k++) {
+                    const WaveRun r = L.join[k];
+                    tr = run_compose_sat(tr, Run{r.p, r.lo, r.hi, r.flags});
+                }
+                if (!(tr.flags & kFlagNeg))
+                    tr.hi = run_top(tr);
+            }
+            // a run past the width of a binade never applies; bounded runs
+            // keep the finisher's sums over a window far from overflow
+            const int64_t lim = kCountLo + 1;
+            if (tr.p.r0 > lim || tr.p.r0 < -lim || tr.lo < -lim || tr.hi > lim) {
+                tr.flags |= kFlagBad;
+                tr.p = pair_identity();
+                tr.lo = tr.hi = 0;
+            }
+            store_relaxed_u64(trec + 1, enc_i64(tr.p.r0));
+            store_relaxed_u64(trec + 2, enc_i64(tr.lo));
+            store_relaxed_u64(trec + 3, enc_i64(tr.hi));
+        }
+        // the run's words and every lane's descriptor stores before the tag
+        stores_complete();
+        __syncthreads();
+        if (t == 0)
+            store_relaxed_u64(trec, rec_w0(tag, kKindReg, tr.flags, tr.p.r1 - tr.p.r0, L.key[0]));
+        return;
+    }
+    // An irregular tile: its O(1) step -- the chunks before the first located
+    // crossing as one run A, then up to kMaxCross crossings, each with the
+    // chunks after it (in the next binade) folded into its rest-of-chunk
+    // run.  Built in LDS by lane 0.  Any other shape is walked by the
+    // finisher chunk by chunk.
+    bool fast = true;
+    uint32_t nfl = 0u;
+    if (t == 0) {
+        Run A = run_identity();
+        uint32_t akey = 0u;
+        int nx = 0;
+        uint32_t next_key = 0u;  // the binade the chunks after the last crossing are in
+        Run suf = run_identity();
+        Pair whole = pair_identity();
+        uint64_t *xr = nullptr;  // the current crossing's words in L.rec
+        for (int k = 0; k < nk; k++)
+            nfl |= L.join[k].flags & kFlagNonFinite;
+        auto close_crossing = [&]() {
+            const int64_t lim = (int64_t)1 << 56;
+            fast = fast && !(suf.flags & kFlagBad) && whole.r0 < lim && whole.r1 < lim &&
+                   whole.r0 > -lim && whole.r1 > -lim;
+            xr[1 + kXsuf] = enc_i64(rec_pack(suf.p));
+            xr[1 + kXsufLo] = enc_i64(suf.lo);
+            xr[1 + kXsufHi] = enc_i64(suf.hi);
+            xr[1 + kXwhole] = enc_i64(rec_pack(whole));
+            xr[0] |= (uint64_t)((suf.flags & kFlagNeg) ? 1u : 0u) << 13;
+        };
+        for (int k = 0; fast && k < nk; k++) {
+            const WaveRun &q = L.join[k];
+            const uint32_t kk = L.key[k];
+            if ((found >> k) & 1u) {
+                if (nx == kMaxCross || (nx == 0 ? (akey != 0u && akey != kk) : kk != next_key)) {
+                    fast = false;
+                    break;
+                }
+                if (nx > 0)
+                    close_crossing();
+                xr = L.rec + 4 + kXrecW * nx;
+                const bool down = L.down[k] != 0u;
+#pragma unroll
+                for (int c = 0; c < kCrossWords; c++)
+                    xr[1 + c] = L.xw[k][c];
+                xr[0] = (uint64_t)(kk & kKeyMask) | ((uint64_t)down << 12) |
+                        ((uint64_t)chunk_len(n, c0 + k) << 16);
+                suf = Run{rec_unpack(dec_i64(xr[1 + kXsuf])), dec_i64(xr[1 + kXsufLo]),
+                          dec_i64(xr[1 + kXsufHi]), q.flags & kFlagNeg};
+                whole = rec_unpack(dec_i64(xr[1 + kXwhole]));
+                next_key = down ? kk - 1u : kk + 1u;
+                nx++;
+                continue;
+            }
+            fast = key_has_fast_path(kk) && !(q.flags & (kFlagBad | kFlagNonFinite));
+            if (nx == 0) {
+                fast = fast && (akey == 0u || akey == kk);
+                A = run_compose_sat(A, Run{q.p, q.lo, q.hi, q.flags});
+                akey = kk;
+            } else {
+                fast = fast && kk == next_key;
+                suf = run_compose_sat(suf, Run{q.p, q.lo, q.hi, q.flags & kFlagNeg});
+                whole = compose(whole, q.p);
+            }
+        }
+        if (fast && nx > 0)
+            close_crossing();
+        fast = fast && (akey != 0u || nx > 0) && !(A.flags & kFlagBad);
+        L.rec[0] = (uint64_t)(akey & kKeyMask) | ((uint64_t)(akey != 0u) << 12) |
+                   ((uint64_t)nx << 13) | ((uint64_t)((A.flags >> 14) & 3u) << 15) |
+                   ((uint64_t)(A.p.r1 - A.p.r0 + 1) << 17);
+        L.rec[1] = enc_i64(A.p.r0);
+        L.rec[2] = enc_i64(A.lo);
+        L.rec[3] = enc_i64(A.hi);
+        L.lb_found = fast ? 1 : 0;  // reused: tells the other lanes
+    }
+    __syncthreads();
+    fast = L.lb_found != 0;
+    if (fast && t < kStepWords)
+        store_relaxed_u64(w.xrec + kStepWords * (size_t)g + t, L.rec[t]);
+    stores_complete();
+    __syncthreads();
+    if (t == 0)
+        store_relaxed_u64(trec, rec_w0(tag, fast ? kKindStep : kKindSlow, nfl, 0, 0u));
+}
+
+// ---------------------------------------------------------------------------
+// The kernel: per sum, its head, its finisher, then its later tiles
+// ---------------------------------------------------------------------------
+template <class Src>
+__global__ __launch_bounds__(kChunkThreads, 4) void pass_kernel(PassArgs pa, Src src, PassWs w)
+{
+    __shared__ PassTileLds L;
+    __shared__ WalkCore sc;
+    __shared__ CrossLds xl;
+    __shared__ __align__(16) double U[kUnionDoubles];
+    __shared__ int lds_src[Src::kLdsInts];
+    const BatchArgs &a = pa.b;
+    // this block's sum: the last with block_base <= blockIdx.x
+    int lo = 0, hi = a.count - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pa.block_base[mid] <= blockIdx.x)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    const int s = lo;
+    const uint32_t b = blockIdx.x - pa.block_base[s];
+    // The head and the finisher are the sum's serial path; their waves go
+    // first in issue on the SIMDs they share with streaming tiles.
+    if (b <= 1)
+        __builtin_amdgcn_s_setprio(3);
+    if (b == 0)
+        head_block(pa, src, w, s, L, sc, U, lds_src);
+    else if (b == 1)
+        finisher_block(pa, src, w, s, *reinterpret_cast<FinLds *>(U), sc, U + kFinTermsOff, lds_src);
+    else
+        tile_block(pa, src, w, s, b - 1, L, sc, xl, U, lds_src);
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+namespace {
+
+// Launch tags: 45 bits, never zero, never repeated within a process; the
+// start is drawn from the clock and the process so that words a previous
+// process left in reused memory are unlikely to match.
+std::atomic<uint64_t> g_tag{0};
+
+uint64_t next_tag()
+{
+    uint64_t cur = g_tag.load(std::memory_order_relaxed);
+    if (cur == 0) {
+        uint64_t seed = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+        seed ^= (uint64_t)(uintptr_t)&g_tag * 0x9E3779B97F4A7C15ULL;
+        seed = (seed ^ (seed >> 31)) * 0xBF58476D1CE4E5B9ULL;
+        uint64_t expect = 0;
+        g_tag.compare_exchange_strong(expect, seed | 1u, std::memory_order_relaxed);
+    }
+    uint64_t tg;
+    do {
+        tg = g_tag.fetch_add(1, std::memory_order_relaxed) & ((1ULL << 45) - 1);
+    } while (tg == 0);
+    return tg;
+}
+
+size_t r256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Tiles and groups of a launch over total_chunks padded chunks and `sums`
+// sums: at most one tile per eight chunks plus two per sum.
+size_t max_tiles(size_t total_chunks, size_t sums) { return total_chunks / kTileCh + 2 * sums + 1; }
+size_t max_groups(size_t total_chunks, size_t sums)
+{
+    return max_tiles(total_chunks, sums) / kGroup + sums + 1;
+}
+
+PassWs pass_carve(void *ws, size_t total_chunks, size_t sums)
+{
+    char *p = static_cast<char *>(ws);
+    const size_t tiles = max_tiles(total_chunks, sums), groups = max_groups(total_chunks, sums);
+    PassWs w;
+    w.st = reinterpret_cast<uint64_t *>(p);
+    p += r256(tiles * 8);
+    w.gst = reinterpret_cast<uint64_t *>(p);
+    p += r256(groups * 8);
+    w.d.r0 = reinterpret_cast<int64_t *>(p);
+    p += r256(total_chunks * 8);
+    w.d.lo = reinterpret_cast<int64_t *>(p);
+    p += r256(total_chunks * 8);
+    w.d.hi = reinterpret_cast<int64_t *>(p);
+    p += r256(total_chunks * 8);
+    w.d.meta = reinterpret_cast<uint32_t *>(p);
+    p += r256(total_chunks * 4);
+    w.trec = reinterpret_cast<uint64_t *>(p);
+    p += r256(tiles * 4 * 8);
+    w.xrec = reinterpret_cast<uint64_t *>(p);
+    p += r256(tiles * kStepWords * 8);
+    w.hrec = reinterpret_cast<uint64_t *>(p);
+    return w;
+}
+
+}  // namespace
+
+size_t pass_ws_bytes(size_t total_chunks, size_t sums)
+{
+    const size_t tiles = max_tiles(total_chunks, sums), groups = max_groups(total_chunks, sums);
+    return r256(tiles * 8) + r256(groups * 8) + 3 * r256(total_chunks * 8) +
+           r256(total_chunks * 4) + r256(tiles * 32) + r256(tiles * kStepWords * 8) +
+           r256(sums * 16 + 16);
+}
+
+bool pass_eligible(const BatchArgs &a)
+{
+    const uint32_t mode = a.flags & EXSEQ_PLAN_MASK;
+    if (mode == EXSEQ_PLAN_ALL_FALLBACK)
+        return false;
+    if (a.flags & (EXSEQ_WALK_ONLY | EXSEQ_CHAIN_CUT | EXSEQ_PLAN_REUSE | EXSEQ_CHAIN_PATH))
+        return false;
+    if ((a.flags >> kTileShift) & 3u)
+        return false;
+    return !a.interleave;
+}
+
+template <class Src>
+static int launch_pass_src(const BatchArgs &a, const Src &src, void *ws, double *outs,
+                           hipStream_t stream, exseq_stats *stats, void *const *events,
+                           int n_events)
+{
+    PassArgs pa;
+    pa.b = a;
+    pa.outs = outs;
+    pa.stats = stats;
+    uint32_t blocks = 0, tiles = 0, groups = 0;
+    for (int s = 0; s < a.count; s++) {
+        const uint32_t nch = (uint32_t)((a.n[s] + kChunk - 1) / kChunk);
+        const uint32_t nt = tiles_of(nch);
+        pa.block_base[s] = blocks;
+        pa.tile_base[s] = tiles;
+        pa.group_base[s] = groups;
+        blocks += 2 + (nt > 1 ? nt - 1 : 0);
+        tiles += nt;
+        groups += (nt + kGroup - 1) / kGroup;
+    }
+    pa.block_base[a.count] = blocks;
+    pa.tile_base[a.count] = tiles;
+    pa.group_base[a.count] = groups;
+    pa.tag = next_tag();
+    pa.b.epoch = (uint32_t)(pa.tag & 0xFFFFu) ? (uint32_t)pa.tag : (uint32_t)pa.tag + 1u;
+    const PassWs w = pass_carve(ws, a.chunk_base[a.count], (size_t)a.count);
+    if (events && n_events > 0 && events[0])
+        hipEventRecord(static_cast<hipEvent_t>(events[0]), stream);
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(pass_kernel<Src>), dim3(blocks), dim3(kChunkThreads), 0,
+                       stream, pa, src, w);
+    if (events && n_events > 1 && events[1])
+        hipEventRecord(static_cast<hipEvent_t>(events[1]), stream);
+    return hipGetLastError() == hipSuccess ? EXSEQ_OK : EXSEQ_EHIP;
+}
+
+int launch_pass(const BatchArgs &a, void *ws, double *outs, hipStream_t stream,
+                exseq_stats *stats, void *const *events, int n_events)
+{
+    return launch_pass_src(a, PlainTerms{}, ws, outs, stream, stats, events, n_events);
+}
+
+}  // namespace exseq

@@ -79,6 +79,18 @@
 namespace exseq {
 
 
+// Fixed-tree sum of every chunk (the tree sum beside the exact one).
+__global__ __launch_bounds__(kChunkThreads) void chunk_tsum_kernel(
+    const double *__restrict__ x, size_t n, double *__restrict__ tsum)
+{
+    __shared__ double lds4[4];
+    const size_t c = blockIdx.x;
+    const Four f = load_four(x, n, c * kChunk + (size_t)threadIdx.x * 4, true);
+    const double t = chunk_tree(f, lds4);
+    if (threadIdx.x == 0)
+        tsum[c] = t;
+}
+
 // What the waves of a tile hand each other.
 template <int CPB>
 struct TileLds {
@@ -996,21 +1008,24 @@ WsParts carve(void *ws, size_t total)
 }
 }  // namespace
 
-const char *const kPathKernels[] = {"chain_clear_kernel", "tile_kernel", "walk_kernel"};
-const int kPathKernelCount = 3;
+// The kernels of the default path of a plain sum (the single pass).
+const char *const kPathKernels[] = {"pass_kernel"};
+const int kPathKernelCount = 1;
 
 // Per chunk (a tile is at least one chunk): the plan status word, the four
 // descriptor arrays, the chain words; per sum a head word and a kept-plan
 // tag; per tile of kTileMax chunks a kept planned prefix.
 size_t sum_ws_bytes(size_t total_chunks)
 {
-    return 4 * round256(total_chunks * sizeof(int64_t)) +
+    const size_t pass = pass_ws_bytes(total_chunks, kMaxBatch);
+    const size_t chain = 4 * round256(total_chunks * sizeof(int64_t)) +
            round256(total_chunks * sizeof(uint32_t)) +
            round256(4 * total_chunks * sizeof(uint64_t)) +
            round256(total_chunks * sizeof(uint64_t)) +
            2 * round256(kMaxBatch * sizeof(uint64_t)) +
            round256((total_chunks / kTileMax + 1) * sizeof(double)) +
            round256(kRecWords * total_chunks * sizeof(uint64_t));
+    return chain > pass ? chain : pass;
 }
 
 template <int CPB, class Src>
@@ -1094,6 +1109,14 @@ static int launch_batch_src(const BatchArgs &a, const Src &src, void *ws, double
 int launch_batch(const BatchArgs &a, void *ws, double *outs, hipStream_t stream,
                  exseq_stats *stats, void *const *events, int n_events)
 {
+    // the single pass for batches (and on request), except for launches of a
+    // few chunks (the walk alone)
+    const uint32_t total = a.chunk_base[a.count];
+    const bool tiny = total <= 2u * kTileMax && (a.flags & ~EXSEQ_PASS_PATH) == 0u &&
+                      !(events && n_events);
+    const bool want = a.count > 1 || (a.flags & EXSEQ_PASS_PATH);
+    if (want && !tiny && total > 0 && pass_eligible(a))
+        return launch_pass(a, ws, outs, stream, stats, events, n_events);
     return launch_batch_src(a, PlainTerms{}, ws, outs, stream, stats, events, n_events);
 }
 

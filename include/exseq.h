@@ -88,6 +88,17 @@ enum {
 #define EXSEQ_TILE_SHIFT 4
 #define EXSEQ_WALK_ONLY (1u << 6)
 #define EXSEQ_CHAIN_CUT (1u << 7)
+/* EXSEQ_CHAIN_PATH and EXSEQ_PASS_PATH choose between the two launch plans
+ * of a plain sum or batch (the same results): the tile chain and walk of
+ * three launches, and the single pass (one launch for all the sums of a
+ * batch: streaming tiles, a head block and a finisher block per sum).  By
+ * default a batch of two or more sums takes the single pass and one sum the
+ * chain.  Only the AUTO, PLUS_ONE, MINUS_ONE and FIXED plans with the
+ * default tile take the single pass; every other mode (ALL_FALLBACK,
+ * WALK_ONLY, CHAIN_CUT, PLAN_REUSE, a tile size) and the interleaved and
+ * fused SSIM sums take the chain. */
+#define EXSEQ_CHAIN_PATH (1u << 21)
+#define EXSEQ_PASS_PATH (1u << 22)
 
 /* EXSEQ_PLAN_REUSE (with EXSEQ_PLAN_AUTO and the default tile): the plan of
  * the previous call on the same workspace stands in for this call's where it

@@ -17,6 +17,9 @@ pytestmark = pytest.mark.gpu
 
 PLANS = [ex.PLAN_AUTO, ex.PLAN_ALL_FALLBACK, ex.PLAN_PLUS_ONE, ex.PLAN_MINUS_ONE,
          ex.plan_fixed(1023)]
+# both launch plans of a plain sum: the tile chain (default for one sum) and
+# the single pass
+PATHS = [0, ex.PASS_PATH]
 
 
 @pytest.fixture(autouse=True)
@@ -40,16 +43,18 @@ def test_edge_cases(case):
     name, x, init = case
     want = oracle.seq_sum(x, init)
     for plan in (ex.PLAN_AUTO, ex.PLAN_ALL_FALLBACK, ex.PLAN_PLUS_ONE):
-        got = gpu_sum(torch, x, init, plan)
-        assert same(got, want), (name, plan, got, want)
+        for path in PATHS:
+            got = gpu_sum(torch, x, init, plan | path)
+            assert same(got, want), (name, plan, path, got, want)
 
 
 @pytest.mark.parametrize("n", suites.ragged_sizes())
 def test_ragged_sizes(n):
     torch = torch_cuda()
     for x in (si.tie_heavy(n, n), si.signed_terms(n, n + 1)):
-        got = gpu_sum(torch, x)
-        assert same(got, oracle.seq_sum(x)), n
+        for path in PATHS:
+            got = gpu_sum(torch, x, 0.0, path)
+            assert same(got, oracle.seq_sum(x)), (n, path)
 
 
 @pytest.mark.parametrize("case", suites.workload_suite(small=True), ids=lambda c: c[0])
@@ -59,11 +64,12 @@ def test_workloads_every_plan(case):
     name, x, init = case
     want = oracle.seq_sum(x, init)
     for plan in PLANS:
-        got = gpu_sum(torch, x, init, plan)
-        assert same(got, want), (name, plan, got, want)
+        for path in PATHS:
+            got = gpu_sum(torch, x, init, plan | path)
+            assert same(got, want), (name, plan, path, got, want)
 
 
-CHAIN_VARIANTS = [0, ex.WALK_ONLY, ex.CHAIN_CUT, ex.tile_flag(1), ex.tile_flag(2),
+CHAIN_VARIANTS = [0, ex.PASS_PATH, ex.WALK_ONLY, ex.CHAIN_CUT, ex.tile_flag(1), ex.tile_flag(2),
                   ex.tile_flag(1) | ex.CHAIN_CUT, ex.tile_flag(2) | ex.CHAIN_CUT]
 
 
@@ -101,10 +107,11 @@ def test_full_size_workloads(seed):
     for name, x in (("uniform", si.uniform(4096, seed)),
                     ("tie_heavy", si.tie_heavy(si.FRAME_N, seed)),
                     ("signed", si.signed_terms(si.HALF_N, seed))):
-        got, st = gpu_sum(torch, x, stats=True)
         want = oracle.seq_sum(x)
-        say(name, seed, st)
-        assert same(got, want), (name, seed, got, want)
+        for path in PATHS:
+            got, st = gpu_sum(torch, x, 0.0, path, stats=True)
+            say(name, seed, path, st)
+            assert same(got, want), (name, seed, path, got, want)
 
 
 def test_full_size_stats_ranges():
