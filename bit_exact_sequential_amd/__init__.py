@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libexseq.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "exseq.h")
 
-EXSEQ_OK, EXSEQ_EINVAL, EXSEQ_EWORKSPACE, EXSEQ_EHIP = 0, -1, -2, -3
+EXSEQ_OK, EXSEQ_EINVAL, EXSEQ_EWORKSPACE, EXSEQ_EHIP, EXSEQ_ESCRATCH = 0, -1, -2, -3, -4
 
 PLAN_AUTO = 0
 PLAN_ALL_FALLBACK = 1
@@ -92,6 +92,10 @@ def lib():
     L.exact_seq_sum_f64_workspace_size.argtypes = [sz]
     L.exact_seq_sum_f64.restype = i32
     L.exact_seq_sum_f64.argtypes = [vp, sz, ctypes.c_double, vp, vp, sz, vp, u32, vp]
+    L.exact_seq_sum_f64_noalloc_max_terms.restype = sz
+    L.exact_seq_sum_f64_noalloc_max_terms.argtypes = []
+    L.exact_seq_sum_f64_noalloc.restype = i32
+    L.exact_seq_sum_f64_noalloc.argtypes = [vp, sz, ctypes.c_double, vp, vp, u32, vp]
     L.exact_seq_sum_f64_batch_workspace_size.restype = sz
     L.exact_seq_sum_f64_batch_workspace_size.argtypes = [ctypes.POINTER(sz), sz]
     L.exact_seq_sum_f64_batch.restype = i32
@@ -234,6 +238,33 @@ def exact_seq_sum(x, init: float = 0.0, *, flags: int = 0, out=None, ws=None,
                              int(flags), st.data_ptr() if st is not None else None)
     _check(rc, "exact_seq_sum_f64")
     _keep_for(stream, dev, out if new_out else None, ws if new_ws else None, st)
+    if stats:
+        _sync_for_stats(stream, dev)
+        return out, _read_stats(st)
+    return out
+
+
+def exact_seq_sum_noalloc(x, init: float = 0.0, *, flags: int = 0, out=None,
+                          stats: bool = False, stream=None):
+    """``exact_seq_sum`` through ``exact_seq_sum_f64_noalloc``: the library
+    takes no workspace from the caller (its static per-GPU array stands in).
+    Only ``out`` (and the stats buffer) are allocated here, by torch, when not
+    given."""
+    torch = _torch()
+    _check_device_f64(x)
+    L = lib()
+    n = x.numel()
+    dev = x.device
+    new_out = out is None
+    if out is None:
+        out = torch.empty(1, dtype=torch.float64, device=dev)
+    st = torch.empty(STATS_BYTES, dtype=torch.uint8, device=dev) if stats else None
+    with torch.cuda.device(dev):
+        rc = L.exact_seq_sum_f64_noalloc(x.data_ptr() if n else None, n, float(init),
+                                         out.data_ptr(), _stream_handle(stream, dev),
+                                         int(flags), st.data_ptr() if st is not None else None)
+    _check(rc, "exact_seq_sum_f64_noalloc")
+    _keep_for(stream, dev, out if new_out else None, st)
     if stats:
         _sync_for_stats(stream, dev)
         return out, _read_stats(st)

@@ -4,6 +4,9 @@
 
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "exseq.h"
 #include "exseq_internal.h"
 
@@ -14,6 +17,41 @@ namespace {
 bool aligned8(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0u; }
 
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+}  // namespace
+
+// The workspace of exact_seq_sum_f64_noalloc: a static device array, one copy
+// per GPU.  Host code never uses the name `scratch` as an address (on the
+// host it only names the symbol): the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[EXSEQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's array, or null (the runtime failed).
+void *scratch_for_current_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p)
+        return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        void *q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q)
+            return nullptr;
+        p = q;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
 
 }  // namespace
 
@@ -32,6 +70,8 @@ const char *exseq_strerror(int code)
         return "workspace too small";
     case EXSEQ_EHIP:
         return "HIP runtime error at launch";
+    case EXSEQ_ESCRATCH:
+        return "input too large for the static scratch array (exact_seq_sum_f64_noalloc)";
     default:
         return "unknown exseq error";
     }
@@ -53,6 +93,36 @@ int exact_seq_sum_f64(const double *x, size_t n, double init, double *out, void 
         return EXSEQ_EWORKSPACE;
     if (chunks_of(n) > 0xFFFFFFFFull)
         return EXSEQ_EINVAL;
+    return launch_exact_sum(x, n, init, out, ws, reinterpret_cast<hipStream_t>(stream), flags,
+                            stats);
+}
+
+size_t exact_seq_sum_f64_noalloc_max_terms(void)
+{
+    // the workspace grows with n: the largest n whose workspace fits
+    size_t lo = 0, hi = (size_t)1 << 40;
+    while (lo < hi) {
+        const size_t mid = lo + (hi - lo + 1) / 2;
+        if (exact_seq_sum_f64_workspace_size(mid) <= EXSEQ_NOALLOC_SCRATCH_BYTES)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+int exact_seq_sum_f64_noalloc(const double *x, size_t n, double init, double *out,
+                              exseq_stream_t stream, uint32_t flags, exseq_stats *stats)
+{
+    if (!out || !aligned8(out) || (n && (!x || !aligned8(x))))
+        return EXSEQ_EINVAL;
+    if (chunks_of(n) > 0xFFFFFFFFull)
+        return EXSEQ_EINVAL;
+    if (exact_seq_sum_f64_workspace_size(n) > EXSEQ_NOALLOC_SCRATCH_BYTES)
+        return EXSEQ_ESCRATCH;
+    void *ws = scratch_for_current_device();
+    if (!ws)
+        return EXSEQ_EHIP;
     return launch_exact_sum(x, n, init, out, ws, reinterpret_cast<hipStream_t>(stream), flags,
                             stats);
 }

@@ -53,7 +53,8 @@ enum {
     EXSEQ_OK = 0,
     EXSEQ_EINVAL = -1,     /* null pointer with work to do, misalignment, bad size */
     EXSEQ_EWORKSPACE = -2, /* ws_bytes below the required size */
-    EXSEQ_EHIP = -3        /* the HIP runtime rejected a launch */
+    EXSEQ_EHIP = -3,       /* the HIP runtime rejected a launch */
+    EXSEQ_ESCRATCH = -4    /* the input needs more than the static scratch array */
 };
 
 /* Plan modes (low 4 bits of `flags`).  The plan names the binade each chunk's
@@ -151,6 +152,30 @@ size_t exact_seq_sum_f64_workspace_size(size_t n);
 int exact_seq_sum_f64(const double *x, size_t n, double init, double *out,
                       void *ws, size_t ws_bytes, exseq_stream_t stream,
                       uint32_t flags, exseq_stats *stats);
+
+/* ---------------------------------------------------------------------------
+ * exact_seq_sum_f64_noalloc
+ *   For callers that cannot allocate device memory (code under HIP graph
+ *   capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ *   sum and launches as exact_seq_sum_f64, with its workspace in a static
+ *   device array of the library, EXSEQ_NOALLOC_SCRATCH_BYTES per GPU, held
+ *   until the process ends.  It calls no allocating routine.  The array of
+ *   the current device is used: `stream` must belong to it.  Sizes whose
+ *   workspace (exact_seq_sum_f64_workspace_size(n)) exceeds the array return
+ *   EXSEQ_ESCRATCH before anything is enqueued; that is n up to
+ *   exact_seq_sum_f64_noalloc_max_terms().  Every call on a GPU shares that
+ *   GPU's array: calls that overlap in time on one GPU (other streams, other
+ *   threads) race and give undefined results; calls in one stream are
+ *   ordered and safe.  The array needs no clearing (launch words are tagged
+ *   per launch; EXSEQ_PLAN_REUSE reuses the plan of the last call on that
+ *   GPU, which affects speed only).  Other arguments and errors as
+ *   exact_seq_sum_f64; EXSEQ_EHIP also when the array's address cannot be
+ *   obtained.
+ * ------------------------------------------------------------------------- */
+#define EXSEQ_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+size_t exact_seq_sum_f64_noalloc_max_terms(void);
+int exact_seq_sum_f64_noalloc(const double *x, size_t n, double init, double *out,
+                              exseq_stream_t stream, uint32_t flags, exseq_stats *stats);
 
 /* ---------------------------------------------------------------------------
  * exact_seq_sum_f64_batch

@@ -17,7 +17,7 @@ def test_library_exports_every_declared_function():
 
 def test_strerror_and_version():
     L = ex.lib()
-    for code in (0, -1, -2, -3, -99):
+    for code in (0, -1, -2, -3, -4, -99):
         assert L.exseq_strerror(code)
     assert b"gfx950" in L.exseq_version()
 
@@ -50,6 +50,19 @@ def test_argument_errors_return_before_any_launch():
     assert L.ssim_term_and_sum(64, 64, 5, 5, 4, 3, 1.0, 1.0, 8, None, None, 64, 1 << 20, None,
                                0, None) == ex.EXSEQ_EINVAL
     assert L.tree_sum_f64(None, 5, 8, 64, 1 << 20, None) == ex.EXSEQ_EINVAL
+
+
+def test_noalloc_limits_checked_before_any_launch():
+    L = ex.lib()
+    mx = L.exact_seq_sum_f64_noalloc_max_terms()
+    # the static array holds the workspace of the largest accepted input
+    assert L.exact_seq_sum_f64_workspace_size(mx) <= 8 << 20 < L.exact_seq_sum_f64_workspace_size(mx + 1)
+    assert mx >= 8294400
+    # beyond it: an error before anything touches the GPU
+    assert L.exact_seq_sum_f64_noalloc(64, mx + 1, 0.0, 8, None, 0, None) == ex.EXSEQ_ESCRATCH
+    assert L.exact_seq_sum_f64_noalloc(None, 10, 0.0, 8, None, 0, None) == ex.EXSEQ_EINVAL
+    assert L.exact_seq_sum_f64_noalloc(64, 10, 0.0, 9, None, 0, None) == ex.EXSEQ_EINVAL
+    assert b"scratch" in L.exseq_strerror(ex.EXSEQ_ESCRATCH)
 
 
 def test_built_for_gfx950():
