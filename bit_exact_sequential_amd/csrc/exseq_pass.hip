@@ -72,10 +72,12 @@ constexpr int kHeadCh = 4;           // chunks of a sum's first tile
 constexpr uint32_t kGroup = 64;      // tiles per look-back group
 constexpr int kFinLane = 4;          // tiles per lane in a finisher window
 constexpr int kFinTiles = kFinLane * kChunkThreads;  // tiles per finisher window
-constexpr int kEvCap = 128;          // events a finisher window holds
 constexpr int kStepCap = 16;         // step records a finisher window holds
 constexpr int kOpCap = 128;          // walk ops a finisher window holds
-constexpr int kTagShift = 19;
+// A finisher tile word: key | kind << kKkKind | step shape (A present, the
+// number of crossings) << kKkShape | (step record slot + 1) << kKkSlot.
+constexpr int kKkKind = 12, kKkShape = 15, kKkSlot = 18;
+constexpr int kTagShift = 22;       // record words: tag << 22 | ...; tags have 42 bits
 // An irregular tile's step (kStepWords words): word 0 holds A's key (12
 // bits), whether A is present (bit 12), the number of crossings (bits
 // 13..14), A's neg and bad flags (bits 15..16) and r1 - r0 + 1 (bits
@@ -85,6 +87,7 @@ constexpr int kTagShift = 19;
 constexpr int kMaxCross = 2;
 constexpr int kXrecW = 1 + kCrossWords;
 constexpr int kStepWords = 4 + kMaxCross * kXrecW;
+static_assert(kStepCap * kStepWords <= 2 * kChunkThreads, "a window's step records: two words per thread");
 constexpr uint32_t kKindReg = 1, kKindStep = 2, kKindSlow = 3;
 constexpr uint32_t kKindLost = 4;    // finisher only: the record never came
 
@@ -100,14 +103,38 @@ __host__ __device__ __forceinline__ uint32_t tile_c0(uint32_t i)
     return i == 0 ? 0u : (uint32_t)kHeadCh + (uint32_t)kTileCh * (i - 1);
 }
 
-// First word of a tile record: tag | kind | flags (neg, bad, non-finite at
-// their descriptor positions) | r1 - r0 + 1 | key.
+// First word of a tile record: tag | ext << 19 | kind << 17 | flags (neg,
+// bad, non-finite at their descriptor positions) | r1 - r0 + 1 | key.  For
+// an irregular tile, ext holds its step's shape (run A present: bit 0; the
+// number of crossings: bits 1..2) and key, dr and neg its last run's.
 __device__ __forceinline__ uint64_t rec_w0(uint64_t tag, uint32_t kind, uint32_t flags, int64_t dr,
-                                           uint32_t key)
+                                           uint32_t key, uint32_t ext = 0u)
 {
-    return (tag << kTagShift) | ((uint64_t)kind << 17) |
+    return (tag << kTagShift) | ((uint64_t)(ext & 7u) << 19) | ((uint64_t)kind << 17) |
            (uint64_t)(flags & (kFlagNeg | kFlagBad | kFlagNonFinite)) |
            ((uint64_t)(dr + 1) << kDrShift) | (uint64_t)(key & kKeyMask);
+}
+
+// Second word of a regular tile's record: r0 + 2^53 in the low 54 bits and
+// the launch tag's low 10 bits above (|r0| <= 2^52 + 1 for a record).  The
+// finisher reads the first two words with one 16-byte load; the tag bits
+// let it see that this word belongs to the same launch as the first.
+__device__ __forceinline__ uint64_t rec_w1(uint64_t tag, int64_t r0)
+{
+    return ((uint64_t)(r0 + ((int64_t)1 << 53)) & (((uint64_t)1 << 54) - 1)) | ((tag & 0x3FFu) << 54);
+}
+__device__ __forceinline__ bool rec_w1_ok(uint64_t tag, uint64_t w1) { return (w1 >> 54) == (tag & 0x3FFu); }
+__device__ __forceinline__ int64_t rec_w1_r0(uint64_t w1)
+{
+    return (int64_t)(w1 & (((uint64_t)1 << 54) - 1)) - ((int64_t)1 << 53);
+}
+
+// 16 bytes of device-coherent memory in one load.
+typedef uint64_t v2u64 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ v2u64 load_coherent_16(const uint64_t *p)
+{
+    typedef const volatile __attribute__((address_space(1))) v2u64 *gptr;
+    return *(gptr)(p);
 }
 
 // Workspace of a pass launch (see pass_carve).
@@ -115,7 +142,8 @@ struct PassWs {
     uint64_t *st;    // per tile: plan status word
     uint64_t *gst;   // per group: plan status word
     DescArrays d;    // per chunk: descriptor
-    uint64_t *trec;  // per tile: 4 words (w0, r0, lo, hi)
+    uint64_t *trec;  // per tile: 4 words (w0, r0 with tag bits, lo, hi; lo and hi
+                     // only for a run with a negative term)
     uint64_t *xrec;  // per tile: kStepWords words (an irregular tile's step)
     uint64_t *hrec;  // per sum: 2 words (w0, exact sum after the first tile)
 };
@@ -143,31 +171,18 @@ struct PassTileLds {
     uint32_t down[kTileCh];
     uint64_t xw[kTileCh][kCrossWords];
     uint64_t rec[kStepWords];
+    uint64_t xexit[4];  // an irregular tile's last run: key etc., r0, lo, hi
     double lb1, lb2;
     int lb_found, lb_ok1, lb_ok2;
     volatile int lb_stop;
 };
 
-// What a finisher window keeps per event.
-struct FinEv {
-    int64_t r0, lo, hi;
-    uint32_t meta;  // key | (r1 - r0 + 1) << 12 | flags | kind << 20
-    int32_t tile;   // the event's tile in the window (a segment's last tile)
-    int32_t start;  // a segment's first tile in the window
-    int32_t slot;   // a step's record slot
-};
-
-// The finisher composes the regular tiles of a segment with two segmented
-// scans (see segp_op and segb_op): their values carry whether they start a
-// segment (head) and that segment's first tile (start).
-struct SegPair {
-    Pair p;
+// The finisher composes the runs of a segment's tiles with an ordered
+// segmented scan: values carry whether they start a segment (head) and that
+// segment's first tile (start).
+struct SegRun {
+    Run r;
     int32_t start;
-    int32_t head;
-};
-struct SegBound {
-    int64_t lo, hi;
-    uint32_t flags;
     int32_t head;
 };
 
@@ -200,20 +215,20 @@ constexpr uint32_t kOpFirst = 1u << 14, kOpLast = 1u << 15, kOpDown = 1u << 16, 
 constexpr int kOpRestShift = 19;
 
 struct FinLds {
-    uint32_t kk[kFinTiles];  // per tile of the window: kind << 16 | key
-    FinEv ev[kEvCap];
+    uint32_t kk[kFinTiles];      // per tile of the window (see kKkKind)
+    uint16_t opoff[kFinTiles];   // a segment's first op, at its first tile
     uint64_t rec[kStepCap][kStepWords];
     uint64_t ops[kOpCap][kOpWords];
-    int32_t ne_cut, nops;
+    int32_t cut, nops_cut;
+    int32_t nslots;  // step record slots taken in this window
+    uint32_t stile[kStepCap];  // the tile (in the launch) of each slot
     struct {
         uint64_t sbits;
         int32_t i;
         uint32_t fast, fb_lo, fb_hi, fb_desc;
     } wk;  // where wave 0's walk stopped
-    SegPair wp[kWaves];
-    SegBound wb[kWaves];
+    SegRun wr[kWaves];
     int32_t cnt[kWaves];
-    int32_t steps[kWaves];
     uint32_t nf[kWaves];
     FinTally tally;
 };
@@ -431,77 +446,47 @@ __device__ __forceinline__ WaveRun block_run(const Four &f, uint32_t key, WaveRu
 // greatest of (the larger component + the tile's largest prefix), exactly as
 // run_compose folds them one at a time.
 
-__device__ __forceinline__ SegPair segp_op(const SegPair &l, const SegPair &r)
+
+// The ordered segmented composition of runs: r starts a segment, or the
+// segment continues with r (run_compose_sat: a composed run too wide for a
+// binade is only marked bad).
+__device__ __forceinline__ SegRun segr_op(const SegRun &l, const SegRun &r)
 {
     if (r.head)
         return r;
-    return SegPair{compose(l.p, r.p), l.start, l.head};
-}
-__device__ __forceinline__ SegBound segb_op(const SegBound &l, const SegBound &r)
-{
-    if (r.head)
-        return r;
-    return SegBound{l.lo < r.lo ? l.lo : r.lo, l.hi > r.hi ? l.hi : r.hi, l.flags | r.flags, l.head};
+    return SegRun{run_compose_sat(l.r, r.r), l.start, l.head};
 }
 
 template <int Ctrl, int RowMask = 0xF>
-__device__ __forceinline__ SegPair dpp_segp(const SegPair &v)
+__device__ __forceinline__ SegRun dpp_segr(const SegRun &v)
 {
-    return SegPair{dpp_pair<Ctrl, RowMask>(v.p),
-                   (int32_t)dpp_u32<Ctrl, RowMask>((uint32_t)v.start, 0xFFFFFFFFu),
-                   (int32_t)dpp_u32<Ctrl, RowMask>((uint32_t)v.head, 0u)};
-}
-template <int Ctrl, int RowMask = 0xF>
-__device__ __forceinline__ SegBound dpp_segb(const SegBound &v)
-{
-    // lanes without a source take the identity: no bound (0 is inside every
-    // segment's range already, since the empty prefix counts)
-    return SegBound{dpp_i64<Ctrl, RowMask>(v.lo, 0), dpp_i64<Ctrl, RowMask>(v.hi, 0),
-                    dpp_u32<Ctrl, RowMask>(v.flags, 0u),
-                    (int32_t)dpp_u32<Ctrl, RowMask>((uint32_t)v.head, 0u)};
+    // lanes without a source take the identity
+    return SegRun{dpp_run<Ctrl, RowMask>(v.r),
+                  (int32_t)dpp_u32<Ctrl, RowMask>((uint32_t)v.start, 0xFFFFFFFFu),
+                  (int32_t)dpp_u32<Ctrl, RowMask>((uint32_t)v.head, 0u)};
 }
 
-// Exclusive ordered segmented scans over the workgroup's lanes (one barrier
-// each): lane t gets the composition of lanes 0 .. t-1.
-__device__ __forceinline__ SegPair block_excl_segp(const SegPair &v, FinLds &F)
+// Exclusive ordered segmented scan over the workgroup's lanes (one
+// barrier): lane t gets the composition of lanes 0 .. t-1.
+__device__ __forceinline__ SegRun block_excl_segr(const SegRun &v, FinLds &F)
 {
     const int lane = lane_id(), wave = wave_id();
-    SegPair inc = v;
-    inc = segp_op(dpp_segp<kDppRowShr1>(inc), inc);
-    inc = segp_op(dpp_segp<kDppRowShr2>(inc), inc);
-    inc = segp_op(dpp_segp<kDppRowShr4>(inc), inc);
-    inc = segp_op(dpp_segp<kDppRowShr8>(inc), inc);
-    inc = segp_op(dpp_segp<kDppRowBcast15, 0xA>(inc), inc);
-    inc = segp_op(dpp_segp<kDppRowBcast31, 0xC>(inc), inc);
+    SegRun inc = v;
+    inc = segr_op(dpp_segr<kDppRowShr1>(inc), inc);
+    inc = segr_op(dpp_segr<kDppRowShr2>(inc), inc);
+    inc = segr_op(dpp_segr<kDppRowShr4>(inc), inc);
+    inc = segr_op(dpp_segr<kDppRowShr8>(inc), inc);
+    inc = segr_op(dpp_segr<kDppRowBcast15, 0xA>(inc), inc);
+    inc = segr_op(dpp_segr<kDppRowBcast31, 0xC>(inc), inc);
     if (lane == 63)
-        F.wp[wave] = inc;
-    const SegPair before = dpp_segp<kDppWaveShr1>(inc);  // lane 0: the identity
+        F.wr[wave] = inc;
+    const SegRun before = dpp_segr<kDppWaveShr1>(inc);  // lane 0: the identity
     __syncthreads();
-    SegPair carry{pair_identity(), -1, 0};
+    SegRun carry{run_identity(), -1, 0};
     for (int k = 0; k < kWaves; k++)
         if (k < wave)
-            carry = segp_op(carry, F.wp[k]);
-    return segp_op(carry, before);
-}
-__device__ __forceinline__ SegBound block_excl_segb(const SegBound &v, FinLds &F)
-{
-    const int lane = lane_id(), wave = wave_id();
-    SegBound inc = v;
-    inc = segb_op(dpp_segb<kDppRowShr1>(inc), inc);
-    inc = segb_op(dpp_segb<kDppRowShr2>(inc), inc);
-    inc = segb_op(dpp_segb<kDppRowShr4>(inc), inc);
-    inc = segb_op(dpp_segb<kDppRowShr8>(inc), inc);
-    inc = segb_op(dpp_segb<kDppRowBcast15, 0xA>(inc), inc);
-    inc = segb_op(dpp_segb<kDppRowBcast31, 0xC>(inc), inc);
-    if (lane == 63)
-        F.wb[wave] = inc;
-    const SegBound before = dpp_segb<kDppWaveShr1>(inc);
-    __syncthreads();
-    SegBound carry{0, 0, 0u, 0};
-    for (int k = 0; k < kWaves; k++)
-        if (k < wave)
-            carry = segb_op(carry, F.wb[k]);
-    return segb_op(carry, before);
+            carry = segr_op(carry, F.wr[k]);
+    return segr_op(carry, before);
 }
 
 // The finisher's fallback: the ordered walk over the descriptors of chunks
@@ -762,27 +747,46 @@ __device__ __forceinline__ void op_reg(uint64_t *o, uint32_t key, Pair p, int64_
     o[8] = range;
 }
 
-// The number of ops of a step record (word 0 of it).
-__device__ __forceinline__ int step_ops(uint64_t m0) { return (int)((m0 >> 12) & 1u) + 2 * (int)((m0 >> 13) & 3u); }
 
-// Writes the ops of a step record rw (run A, then per crossing CROSS and the
-// REG of the rest of its chunk and the chunks folded in after it).
-__device__ __forceinline__ void op_step(uint64_t (*o)[kOpWords], const uint64_t *rw, uint64_t range)
+// A finisher tile word's fields.
+__device__ __forceinline__ uint32_t kk_kind(uint32_t w) { return (w >> kKkKind) & 7u; }
+// The walk ops of the segment a tile starts: an irregular tile with a
+// record slot takes run A (when it has crossings), and per crossing CROSS
+// and the REG of the rest (the last one: the segment's run); any other
+// tile one op.
+__device__ __forceinline__ int kk_ops(uint32_t w)
+{
+    const uint32_t kind = kk_kind(w);
+    if (kind == 0u)
+        return 0;
+    if (kind != kKindStep || (w >> kKkSlot) == 0u)
+        return 1;
+    const uint32_t shape = (w >> kKkShape) & 7u;
+    const int nx = (int)(shape >> 1);
+    return nx == 0 ? 1 : (int)(shape & 1u) + 2 * nx;
+}
+
+// Writes the leading ops of an irregular tile's step (all but the last of
+// its n_op ops, which is the segment's run): run A, then per crossing CROSS
+// and, for all but the last crossing, the REG of its rest.
+__device__ __forceinline__ void op_step_lead(uint64_t (*o)[kOpWords], const uint64_t *rw, int n_op,
+                                             uint64_t range)
 {
     const uint64_t m0 = rw[0];
-    const int nops = step_ops(m0);
+    const int nx = (int)((m0 >> 13) & 3u);
     int k = 0;
     auto head = [&](int k) {
-        return (k == 0 ? (uint64_t)kOpFirst : 0u) | (k == nops - 1 ? (uint64_t)kOpLast : 0u) |
-               ((uint64_t)(nops - 1 - k) << kOpRestShift);
+        return (k == 0 ? (uint64_t)kOpFirst : 0u) | (k == n_op - 1 ? (uint64_t)kOpLast : 0u) |
+               ((uint64_t)(n_op - 1 - k) << kOpRestShift);
     };
+    if (nx == 0)
+        return;  // A alone: the segment's run starts with it
     if ((m0 >> 12) & 1u) {
         const int64_t r0 = dec_i64(rw[1]);
         op_reg(o[k], (uint32_t)m0 & kKeyMask, Pair{r0, r0 + (int64_t)((m0 >> 17) & 3u) - 1},
                dec_i64(rw[2]), dec_i64(rw[3]), (uint32_t)((m0 >> 15) & 3u) << 14, head(k), range);
         k++;
     }
-    const int nx = (int)((m0 >> 13) & 3u);
     for (int j = 0; j < nx; j++) {
         const uint64_t *x = rw + 4 + kXrecW * j;
         const uint64_t xm = x[0];
@@ -810,9 +814,11 @@ __device__ __forceinline__ void op_step(uint64_t (*o)[kOpWords], const uint64_t 
         }
         c[8] = range;
         k++;
-        op_reg(o[k], key2, rec_unpack(dec_i64(x[1 + kXsuf])), dec_i64(x[1 + kXsufLo]),
-               dec_i64(x[1 + kXsufHi]), neg ? kFlagNeg : 0u, head(k), range);
-        k++;
+        if (j < nx - 1) {
+            op_reg(o[k], key2, rec_unpack(dec_i64(x[1 + kXsuf])), dec_i64(x[1 + kXsufLo]),
+                   dec_i64(x[1 + kXsufHi]), neg ? kFlagNeg : 0u, head(k), range);
+            k++;
+        }
     }
 }
 
@@ -877,18 +883,21 @@ __device__ __forceinline__ void finisher_block(const PassArgs &pa, const Src &sr
         }
     }
 
+    if (t == 0)
+        F.nslots = 0;
+    __syncthreads();
     uint32_t base = 1;
     while (base < nt) {
-        const uint32_t cnt = nt - base < (uint32_t)kFinTiles ? nt - base : (uint32_t)kFinTiles;
+        uint32_t cnt = nt - base < (uint32_t)kFinTiles ? nt - base : (uint32_t)kFinTiles;
         // ---- this lane's tiles (q = kFinLane t + j in the window): their
         // records, polled until their tags show
         const uint32_t q0 = (uint32_t)(kFinLane * t);
         const size_t g0 = (size_t)(tb + base) + q0;
-        uint64_t w0[kFinLane];
+        uint64_t w0[kFinLane], w1[kFinLane];
         bool got[kFinLane];
 #pragma unroll
         for (int j = 0; j < kFinLane; j++) {
-            w0[j] = 0;
+            w0[j] = w1[j] = 0;
             got[j] = q0 + (uint32_t)j >= cnt;
         }
         for (int spin = 0; spin <= kSpinLimit; spin++) {
@@ -896,8 +905,12 @@ __device__ __forceinline__ void finisher_block(const PassArgs &pa, const Src &sr
 #pragma unroll
             for (int j = 0; j < kFinLane; j++) {
                 if (!got[j]) {
-                    w0[j] = load_relaxed_u64(w.trec + 4 * (g0 + j));
-                    got[j] = (w0[j] >> kTagShift) == tag;
+                    const v2u64 r = load_coherent_16(w.trec + 4 * (g0 + j));
+                    w0[j] = r.x;
+                    w1[j] = r.y;
+                    const uint32_t kd = (uint32_t)(r.x >> 17) & 3u;
+                    got[j] = (r.x >> kTagShift) == tag &&
+                             ((kd != kKindReg && kd != kKindStep) || rec_w1_ok(tag, r.y));
                     all &= got[j];
                 }
             }
@@ -905,42 +918,69 @@ __device__ __forceinline__ void finisher_block(const PassArgs &pa, const Src &sr
                 break;
             __builtin_amdgcn_s_sleep(2);
         }
-        uint32_t kk[kFinLane];  // kind << 16 | key
-        Pair rp[kFinLane];
-        int64_t rlo[kFinLane], rtop[kFinLane];
-        uint32_t rfl[kFinLane];
+        // per tile: kk = key | kind << 12 | step shape << 15 | (slot + 1) << 18,
+        // its run (a regular tile's, or the run an irregular one ends with),
+        // and its number of walk ops (counted at a segment's first tile)
+        uint32_t kk[kFinLane];
+        Run rr[kFinLane];
         bool lane_nf = false;
+        int nop_lane = 0;
 #pragma unroll
         for (int j = 0; j < kFinLane; j++) {
             const bool in = q0 + (uint32_t)j < cnt;
-            const bool ok = in && (w0[j] >> kTagShift) == tag;
-            const uint32_t kind = !in ? 0u : ok ? (uint32_t)(w0[j] >> 17) & 3u : kKindLost;
-            kk[j] = kind << 16 | (ok ? (uint32_t)w0[j] & kKeyMask : 0u);
-            lane_nf |= ok && ((uint32_t)w0[j] & kFlagNonFinite);
-            rp[j] = pair_identity();
-            rlo[j] = rtop[j] = 0;
-            rfl[j] = 0u;
-            if (kind == kKindReg) {
-                const uint64_t *r = w.trec + 4 * (g0 + j);
-                const int64_t r0 = dec_i64(load_relaxed_u64(r + 1));
-                rp[j] = Pair{r0, r0 + (int64_t)((w0[j] >> kDrShift) & 3u) - 1};
-                rlo[j] = dec_i64(load_relaxed_u64(r + 2));
-                rtop[j] = dec_i64(load_relaxed_u64(r + 3));
-                rfl[j] = (uint32_t)w0[j] & (kFlagNeg | kFlagBad);
+            const uint32_t kind = !in ? 0u : got[j] ? (uint32_t)(w0[j] >> 17) & 3u : kKindLost;
+            const uint32_t shape = (uint32_t)(w0[j] >> 19) & 7u;
+            kk[j] = (in && got[j] ? (uint32_t)w0[j] & kKeyMask : 0u) | kind << kKkKind;
+            lane_nf |= in && got[j] && ((uint32_t)w0[j] & kFlagNonFinite);
+            rr[j] = run_identity();
+            if (kind == kKindReg || kind == kKindStep) {
+                const int64_t r0 = rec_w1_r0(w1[j]);
+                rr[j].p = Pair{r0, r0 + (int64_t)((w0[j] >> kDrShift) & 3u) - 1};
+                rr[j].flags = (uint32_t)w0[j] & (kFlagNeg | kFlagBad);
+                if (rr[j].flags & kFlagNeg) {
+                    // a run with a negative term: its prefix bounds
+                    const uint64_t *r = w.trec + 4 * (g0 + j);
+                    rr[j].lo = dec_i64(load_relaxed_u64(r + 2));
+                    rr[j].hi = dec_i64(load_relaxed_u64(r + 3));
+                } else {
+                    // rising along either start parity: the largest prefix is
+                    // the total
+                    rr[j].hi = rr[j].p.r0 > rr[j].p.r1 ? rr[j].p.r0 : rr[j].p.r1;
+                }
+            }
+            if (kind == kKindStep) {
+                // a slot for its step record (the words are fetched below)
+                const int sl = atomicAdd(&F.nslots, 1);
+                if (sl < kStepCap) {
+                    F.stile[sl] = (uint32_t)(g0 + j);
+                    kk[j] |= shape << kKkShape | (uint32_t)(sl + 1) << kKkSlot;
+                }
             }
         }
+        // ---- walk ops per tile (at a segment's first tile), their offsets
+        // in the window by a workgroup count
+        int nop[kFinLane];
 #pragma unroll
         for (int j = 0; j < kFinLane; j++) {
-            if ((kk[j] >> 16) == kKindReg)
-                rtop[j] = run_top(Run{rp[j], rlo[j], rtop[j], rfl[j]});
             if (q0 + (uint32_t)j < cnt)
                 F.kk[q0 + j] = kk[j];
         }
         __syncthreads();
-        // ---- segments: a regular tile starts one unless the tile before it
-        // is regular with the same key; one ends where the next tile starts
-        // one, or at the window's end; every other tile is an event of its own
-        uint32_t heads = 0u, evs = 0u;
+        // the step records' words, one or two per thread, requested now and
+        // written to their slots after the scan
+        const int nsl = F.nslots < kStepCap ? F.nslots : kStepCap;
+        uint64_t recw[2] = {0, 0};
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int qq = t + h * kChunkThreads;
+            if (qq < nsl * kStepWords)
+                recw[h] = load_relaxed_u64(w.xrec + kStepWords * (size_t)F.stile[qq / kStepWords] +
+                                           (qq % kStepWords));
+        }
+        // segments: a regular tile continues the segment of a regular tile or
+        // of an irregular one's last run in its binade; every other tile is a
+        // segment of its own
+        uint32_t heads = 0u, ends = 0u;
         {
             const uint32_t prev0 = q0 == 0 ? 0u : F.kk[q0 - 1];
             const uint32_t next3 = q0 + kFinLane < cnt ? F.kk[q0 + kFinLane] : 0u;
@@ -950,199 +990,153 @@ __device__ __forceinline__ void finisher_block(const PassArgs &pa, const Src &sr
                 if (q >= cnt)
                     continue;
                 const uint32_t me = kk[j];
-                const bool reg = (me >> 16) == kKindReg;
+                const uint32_t kme = kk_kind(me);
+                const bool runs = kme == kKindReg || kme == kKindStep;
                 const uint32_t prev = j == 0 ? prev0 : kk[j - 1];
+                const uint32_t kpv = kk_kind(prev);
                 const uint32_t nx = j + 1 < kFinLane ? kk[j + 1] : next3;
-                const bool head = !reg || q == 0 || (prev >> 16) != kKindReg || ((prev ^ me) & kKeyMask) != 0u;
-                const bool end = !reg || q + 1 >= cnt || (nx >> 16) != kKindReg || ((nx ^ me) & kKeyMask) != 0u;
+                const bool head = kme != kKindReg || q == 0 || (kpv != kKindReg && kpv != kKindStep) ||
+                                  ((prev ^ me) & kKeyMask) != 0u;
+                const bool end = !runs || q + 1 >= cnt || kk_kind(nx) != kKindReg ||
+                                 ((nx ^ me) & kKeyMask) != 0u;
                 heads |= (head ? 1u : 0u) << j;
-                evs |= (end ? 1u : 0u) << j;
+                ends |= (end ? 1u : 0u) << j;
             }
         }
-        // the segments' pairs: this lane's, then across lanes
-        SegPair sp{pair_identity(), -1, 0};
 #pragma unroll
         for (int j = 0; j < kFinLane; j++) {
-            const bool h = (heads >> j) & 1u;
-            if (q0 + (uint32_t)j < cnt)
-                sp = segp_op(sp, SegPair{rp[j], h ? (int32_t)(q0 + j) : -1, h ? 1 : 0});
+            nop[j] = 0;
+            if (((heads >> j) & 1u) && q0 + (uint32_t)j < cnt)
+                nop[j] = kk_ops(kk[j]);
+            nop_lane += nop[j];
         }
-        const SegPair pexc = block_excl_segp(sp, F);
-        // the prefix bounds: each tile's, from the pair before it in its segment
-        SegBound sb{0, 0, 0u, 0};
-        {
-            SegPair run = pexc;
-#pragma unroll
-            for (int j = 0; j < kFinLane; j++) {
-                if (q0 + (uint32_t)j >= cnt)
-                    continue;
-                const bool h = (heads >> j) & 1u;
-                const Pair pex = h ? pair_identity() : run.p;
-                run = segp_op(run, SegPair{rp[j], h ? (int32_t)(q0 + j) : -1, h ? 1 : 0});
-                const int64_t pmin = pex.r0 < pex.r1 ? pex.r0 : pex.r1;
-                const int64_t pmax = pex.r0 < pex.r1 ? pex.r1 : pex.r0;
-                sb = segb_op(sb, SegBound{pmin + rlo[j], pmax + rtop[j], rfl[j], h ? 1 : 0});
-            }
-        }
-        const SegBound bexc = block_excl_segb(sb, F);
-        // ---- events in order: offsets by a workgroup count
-        int nev = 0, nstep = 0;
-#pragma unroll
-        for (int j = 0; j < kFinLane; j++) {
-            const bool e = (evs >> j) & 1u;
-            nev += e;
-            nstep += e && (kk[j] >> 16) == kKindStep;
-        }
-        const int64_t packed = (int64_t)nev | ((int64_t)nstep << 32);
-        const int64_t incp = wave_incl_scan_i64(packed);
-        if (lane == 63) {
-            F.cnt[wave] = (int32_t)(incp & 0xFFFFFFFF);
-            F.steps[wave] = (int32_t)(incp >> 32);
-        }
+        const int64_t incn = wave_incl_scan_i64(nop_lane);
+        if (lane == 63)
+            F.cnt[wave] = (int32_t)incn;
         const uint32_t wnf = __ballot(lane_nf) != 0;
         if (lane == 0)
             F.nf[wave] = wnf;
+        if (t == 0)
+            F.cut = (int32_t)cnt;
         __syncthreads();
-        int ev_off = 0, st_off = 0, ev_tot = 0, st_tot = 0;
+        int off_lane = (int)(incn - nop_lane), nops_tot = 0;
         for (int k = 0; k < kWaves; k++) {
-            if (k < wave) {
-                ev_off += F.cnt[k];
-                st_off += F.steps[k];
-            }
-            ev_tot += F.cnt[k];
-            st_tot += F.steps[k];
+            if (k < wave)
+                off_lane += F.cnt[k];
+            nops_tot += F.cnt[k];
             nonfinite |= F.nf[k] != 0;
         }
-        {
-            const int64_t ex = incp - packed;
-            ev_off += (int)(ex & 0xFFFFFFFF);
-            st_off += (int)(ex >> 32);
+        // the window ends before the first segment whose ops do not fit
+        if (nops_tot > kOpCap) {
+            int o = off_lane;
+#pragma unroll
+            for (int j = 0; j < kFinLane; j++) {
+                if (nop[j] && o + nop[j] > kOpCap) {
+                    atomicMin(&F.cut, (int32_t)(q0 + j));
+                    break;
+                }
+                o += nop[j];
+            }
+            __syncthreads();
+            const uint32_t cut = (uint32_t)F.cut;
+            if (cut < cnt) {
+                // the ops before the first segment left out
+                int oc = off_lane;
+#pragma unroll
+                for (int j = 0; j < kFinLane; j++) {
+                    if (q0 + (uint32_t)j == cut)
+                        F.nops_cut = oc;
+                    oc += nop[j];
+                }
+                cnt = cut;
+#pragma unroll
+                for (int j = 0; j < kFinLane; j++) {
+                    const uint32_t q = q0 + (uint32_t)j;
+                    if (q >= cnt) {
+                        heads &= ~(1u << j);
+                        ends &= ~(1u << j);
+                        nop[j] = 0;
+                    } else if (q + 1 == cnt) {
+                        ends |= 1u << j;
+                    }
+                }
+            }
         }
+        // ---- the segments' runs: this lane's fold, then an ordered segmented
+        // scan over the lanes
+        SegRun sr{run_identity(), -1, 0};
+#pragma unroll
+        for (int j = 0; j < kFinLane; j++) {
+            if (q0 + (uint32_t)j >= cnt)
+                continue;
+            const bool h = (heads >> j) & 1u;
+            sr = segr_op(sr, SegRun{rr[j], h ? (int32_t)(q0 + j) : -1, h ? 1 : 0});
+        }
+        const SegRun rexc = block_excl_segr(sr, F);
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int qq = t + h * kChunkThreads;
+            if (qq < nsl * kStepWords)
+                F.rec[qq / kStepWords][qq % kStepWords] = recw[h];
+        }
+        // each head's first op in the window, for the lane that ends its segment
         {
-            SegPair run = pexc;
-            SegBound bnd = bexc;
+            int o = off_lane;
+#pragma unroll
+            for (int j = 0; j < kFinLane; j++) {
+                if (nop[j])
+                    F.opoff[q0 + j] = (uint16_t)o;
+                o += nop[j];
+            }
+        }
+        __syncthreads();
+        const int nops = nops_tot <= kOpCap ? nops_tot : F.nops_cut;
+        // ---- the ops: a segment's last tile writes its final op (the run of
+        // the segment) and, for an irregular first tile, that tile's other ops
+        {
+            SegRun run = rexc;
 #pragma unroll
             for (int j = 0; j < kFinLane; j++) {
                 const uint32_t q = q0 + (uint32_t)j;
                 if (q >= cnt)
                     continue;
                 const bool h = (heads >> j) & 1u;
-                const Pair pex = h ? pair_identity() : run.p;
-                run = segp_op(run, SegPair{rp[j], h ? (int32_t)q : -1, h ? 1 : 0});
-                const int64_t pmin = pex.r0 < pex.r1 ? pex.r0 : pex.r1;
-                const int64_t pmax = pex.r0 < pex.r1 ? pex.r1 : pex.r0;
-                bnd = segb_op(bnd, SegBound{pmin + rlo[j], pmax + rtop[j], rfl[j], h ? 1 : 0});
-                if (!((evs >> j) & 1u))
+                run = segr_op(run, SegRun{rr[j], h ? (int32_t)q : -1, h ? 1 : 0});
+                if (!((ends >> j) & 1u))
                     continue;
-                const uint32_t kind = kk[j] >> 16;
-                if (ev_off < kEvCap) {
-                    FinEv e;
-                    e.tile = (int32_t)q;
-                    e.slot = kind == kKindStep && st_off < kStepCap ? st_off : -1;
-                    if (kind == kKindReg) {
-                        // a segment whose numbers grew past any binade never applies
-                        const int64_t lim = (int64_t)1 << 56;
-                        const int64_t dr = run.p.r1 - run.p.r0;
-                        const bool ok = dr >= -1 && dr <= 1 && run.p.r0 < lim && run.p.r0 > -lim &&
-                                        bnd.lo > -lim && bnd.hi < lim;
-                        e.r0 = ok ? run.p.r0 : 0;
-                        e.lo = ok ? bnd.lo : 0;
-                        e.hi = ok ? bnd.hi : 0;
-                        e.start = run.start;
-                        e.meta = (kk[j] & kKeyMask) | ((uint32_t)(ok ? dr + 1 : 1) << kDrShift) |
-                                 (bnd.flags & (kFlagNeg | kFlagBad)) | (ok ? 0u : kFlagBad) |
-                                 (kKindReg << 20);
-                    } else {
-                        e.r0 = e.lo = e.hi = 0;
-                        e.start = (int32_t)q;
-                        e.meta = kind << 20;
-                    }
-                    F.ev[ev_off] = e;
-                }
-                ev_off++;
-                st_off += kind == kKindStep;
-            }
-        }
-        __syncthreads();
-        // this window takes up to kEvCap events, and up to the first step
-        // without a record slot
-        int ne = ev_tot < kEvCap ? ev_tot : kEvCap;
-        if (st_tot > kStepCap) {
-            for (int e = 0; e < ne; e++) {
-                if ((F.ev[e].meta >> 20) == kKindStep && F.ev[e].slot < 0) {
-                    ne = e;
-                    break;
-                }
-            }
-        }
-        // the step records of this window, all requested at once
-        for (int q = t; q < ne * kStepWords; q += kChunkThreads) {
-            const int e = q / kStepWords, k = q - e * kStepWords;
-            const FinEv &ev = F.ev[e];
-            if ((ev.meta >> 20) == kKindStep && ev.slot >= 0 && ev.slot < kStepCap)
-                F.rec[ev.slot][k] = load_relaxed_u64(
-                    w.xrec + kStepWords * ((size_t)tb + base + (uint32_t)ev.tile) + k);
-        }
-        if (t == 0)
-            F.ne_cut = ne;
-        __syncthreads();
-        // ---- the walk's ops, one lane per event; the window ends before the
-        // first event whose ops do not fit
-        {
-            int nop = 0;
-            FinEv ev;
-            uint64_t range = 0;
-            if (t < ne) {
-                ev = F.ev[t];
-                const uint32_t kd = ev.meta >> 20;
-                nop = kd == kKindStep ? step_ops(F.rec[ev.slot][0]) : 1;
-                const uint32_t c_lo = tile_c0(base + (uint32_t)ev.start);
-                const uint32_t c_end = tile_c0(base + (uint32_t)ev.tile + 1);
-                range = (uint64_t)c_lo | (uint64_t)(c_end < nch ? c_end : nch) << 32;
-            }
-            const int64_t inc = wave_incl_scan_i64(nop);
-            if (lane == 63)
-                F.cnt[wave] = (int32_t)inc;
-            __syncthreads();
-            int off = (int)(inc - nop);
-            for (int k = 0; k < kWaves; k++)
-                if (k < wave)
-                    off += F.cnt[k];
-            if (t < ne) {
-                if (off + nop > kOpCap) {
-                    atomicMin(&F.ne_cut, t);
+                const uint32_t qs = (uint32_t)run.start;
+                const uint32_t hw = h ? kk[j] : F.kk[qs];
+                const uint32_t kind = kk_kind(hw);
+                const int o0 = F.opoff[qs];
+                const int n_op = kk_ops(hw);
+                const uint32_t c_lo = tile_c0(base + qs);
+                const uint32_t c_end = tile_c0(base + q + 1);
+                const uint64_t range = (uint64_t)c_lo | (uint64_t)(c_end < nch ? c_end : nch) << 32;
+                const int slot = (int)(hw >> kKkSlot) - 1;
+                if (kind == kKindReg || (kind == kKindStep && slot >= 0)) {
+                    auto head_of = [&](int k) {
+                        return (k == 0 ? (uint64_t)kOpFirst : 0u) | (k == n_op - 1 ? (uint64_t)kOpLast : 0u) |
+                               ((uint64_t)(n_op - 1 - k) << kOpRestShift);
+                    };
+                    // the segment's run, in the binade of its last tile
+                    op_reg(F.ops[o0 + n_op - 1], kk[j] & kKeyMask, run.r.p, run.r.lo, run.r.hi,
+                           run.r.flags, head_of(n_op - 1), range);
+                    if (kind == kKindStep)
+                        op_step_lead(F.ops + o0, F.rec[slot], n_op, range);
                 } else {
-                    const uint32_t kd = ev.meta >> 20;
-                    const uint64_t one = (uint64_t)kOpFirst | kOpLast;
-                    if (kd == kKindStep) {
-                        op_step(F.ops + off, F.rec[ev.slot], range);
-                    } else if (kd == kKindReg) {
-                        const uint32_t m = ev.meta;
-                        op_reg(F.ops[off], m & kKeyMask,
-                               Pair{ev.r0, ev.r0 + (int64_t)((m >> kDrShift) & 3u) - 1}, ev.lo,
-                               ev.hi, m & (kFlagNeg | kFlagBad), one, range);
-                    } else {
-                        F.ops[off][0] = kOpFail | one | (kd == kKindLost ? (uint64_t)kOpNoDesc : 0u);
-                        F.ops[off][8] = range;
-                    }
+                    // no O(1) step: the tile's chunks are walked
+                    F.ops[o0][0] = kOpFail | kOpFirst | kOpLast | (kind == kKindLost ? (uint64_t)kOpNoDesc : 0u);
+                    F.ops[o0][8] = range;
                 }
             }
-            __syncthreads();
-            const int cut = F.ne_cut;
-            if (t == cut - 1)
-                F.nops = off + nop;
-            if (cut == 0 && t == 0)
-                F.nops = 0;
-            __syncthreads();
-            ne = cut;
         }
+        __syncthreads();
         // ---- the ordered walk over the ops: lane k holds word k of the
         // current op and of the next; S as its bit pattern.  (One call site
         // of the fallback walk: the first window's walk also takes the
         // head's chunks when its sum never came.)
-        uint32_t next = ne > 0 ? base + (uint32_t)F.ev[ne - 1].tile + 1 : base;
+        const uint32_t next = base + cnt;
         {
-            const int nops = F.nops;
             auto op_word = [&](int i) { return lane < kOpWords && i < nops ? F.ops[i][lane] : (uint64_t)0; };
             auto W = [&](uint64_t v, int k) { return (uint64_t)readlane_i64((int64_t)v, k); };
             int i = 0;
@@ -1219,8 +1213,8 @@ __device__ __forceinline__ void finisher_block(const PassArgs &pa, const Src &sr
                 __syncthreads();
             }
         }
-        if (ne == ev_tot)
-            next = base + cnt;
+        if (t == 0)
+            F.nslots = 0;
         __syncthreads();  // the window's LDS is reused by the next one
         base = next;
     }
@@ -1514,9 +1508,11 @@ __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, c
                 tr.p = pair_identity();
                 tr.lo = tr.hi = 0;
             }
-            store_relaxed_u64(trec + 1, enc_i64(tr.p.r0));
-            store_relaxed_u64(trec + 2, enc_i64(tr.lo));
-            store_relaxed_u64(trec + 3, enc_i64(tr.hi));
+            store_relaxed_u64(trec + 1, rec_w1(tag, tr.p.r0));
+            if (tr.flags & kFlagNeg) {
+                store_relaxed_u64(trec + 2, enc_i64(tr.lo));
+                store_relaxed_u64(trec + 3, enc_i64(tr.hi));
+            }
         }
         // the run's words and every lane's descriptor stores before the tag
         stores_complete();
@@ -1590,6 +1586,22 @@ __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, c
         if (fast && nx > 0)
             close_crossing();
         fast = fast && (akey != 0u || nx > 0) && !(A.flags & kFlagBad);
+        // the run the tile ends with (the rest after its last crossing, or A
+        // without one) and its binade: published in the tile's record words
+        // so that the finisher composes the regular tiles after it with it
+        {
+            const bool lastdown = nx > 0 && ((L.rec[4 + kXrecW * (nx - 1)] >> 12) & 1u);
+            const Run ex = nx > 0 ? suf : A;
+            const bool neg = (ex.flags & kFlagNeg) || lastdown;
+            const int64_t lim = kCountLo + 1;
+            fast = fast && ex.p.r0 <= lim && ex.p.r0 >= -lim && ex.p.r1 <= lim && ex.p.r1 >= -lim &&
+                   (!neg || (ex.lo >= -lim && ex.hi <= lim));
+            L.xexit[0] = (uint64_t)(nx > 0 ? next_key : akey) | ((uint64_t)neg << 14) |
+                         ((uint64_t)(ex.p.r1 - ex.p.r0 + 1) << 32);
+            L.xexit[1] = rec_w1(tag, ex.p.r0);
+            L.xexit[2] = enc_i64(ex.lo);
+            L.xexit[3] = enc_i64(ex.hi);
+        }
         L.rec[0] = (uint64_t)(akey & kKeyMask) | ((uint64_t)(akey != 0u) << 12) |
                    ((uint64_t)nx << 13) | ((uint64_t)((A.flags >> 14) & 3u) << 15) |
                    ((uint64_t)(A.p.r1 - A.p.r0 + 1) << 17);
@@ -1600,12 +1612,20 @@ __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, c
     }
     __syncthreads();
     fast = L.lb_found != 0;
+    const bool xneg = ((L.xexit[0] >> 14) & 1u) != 0;
     if (fast && t < kStepWords)
         store_relaxed_u64(w.xrec + kStepWords * (size_t)g + t, L.rec[t]);
+    if (fast && t >= 64 && t < 64 + (xneg ? 3 : 1))
+        store_relaxed_u64(trec + (t - 63), L.xexit[t - 63]);
     stores_complete();
     __syncthreads();
-    if (t == 0)
-        store_relaxed_u64(trec, rec_w0(tag, fast ? kKindStep : kKindSlow, nfl, 0, 0u));
+    if (t == 0) {
+        const uint64_t x0 = L.xexit[0];
+        const uint32_t shape = (uint32_t)(L.rec[0] >> 12) & 7u;  // A present, crossings
+        store_relaxed_u64(trec, fast ? rec_w0(tag, kKindStep, nfl | (xneg ? kFlagNeg : 0u),
+                                              (int64_t)(x0 >> 32) - 1, (uint32_t)x0 & kKeyMask, shape)
+                                     : rec_w0(tag, kKindSlow, nfl, 0, 0u));
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1665,7 +1685,7 @@ uint64_t next_tag()
     }
     uint64_t tg;
     do {
-        tg = g_tag.fetch_add(1, std::memory_order_relaxed) & ((1ULL << 45) - 1);
+        tg = g_tag.fetch_add(1, std::memory_order_relaxed) & ((1ULL << 42) - 1);
     } while (tg == 0);
     return tg;
 }
