@@ -49,6 +49,7 @@ MUT_TIE_UP = 1
 MUT_NO_BINADE_CHECK = 2
 MUT_NO_UPPER_CHECK = 4
 MUT_IGNORE_PARITY = 8
+MUT_NO_RUN_TOP = 16
 
 CHUNK_TERMS = 1024
 STAT_NONFINITE = 1
@@ -128,6 +129,8 @@ def lib():
     L.exact_seq_sum_f64_profiled.restype = i32
     L.exact_seq_sum_f64_profiled.argtypes = [vp, sz, ctypes.c_double, vp, vp, sz, vp, u32, vp,
                                              ctypes.POINTER(vp), i32]
+    L.exseq_twin_seq_sum_f64.restype = ctypes.c_double
+    L.exseq_twin_seq_sum_f64.argtypes = [vp, sz, ctypes.c_double, u32, u32, vp]
     L.exseq_model_seq_sum_f64.restype = ctypes.c_double
     L.exseq_model_seq_sum_f64.argtypes = [vp, sz, ctypes.c_double, sz, u32, u32,
                                           ctypes.POINTER(Stats)]
@@ -418,6 +421,17 @@ def tree_sum(x, *, out=None, ws=None, stream=None):
 # ---------------------------------------------------------------------------
 # Host model of the method (CPU; test infrastructure for the rules)
 # ---------------------------------------------------------------------------
+
+def twin_seq_sum(x, init: float = 0.0, flags: int = 0, mutations: int = 0):
+    """The single pass replayed on the host in the kernels' grouping of the
+    terms (lanes, waves, tiles, finisher windows); returns (sum, stats)."""
+    import numpy as np
+    a = np.ascontiguousarray(x, dtype=np.float64)
+    st = Stats()
+    s = lib().exseq_twin_seq_sum_f64(a.ctypes.data if a.size else None, a.size, float(init),
+                                     int(flags), int(mutations), ctypes.byref(st))
+    return s, st.as_dict()
+
 
 def model_seq_sum(x, init: float = 0.0, chunk_terms: int = CHUNK_TERMS, flags: int = 0,
                   mutations: int = 0):

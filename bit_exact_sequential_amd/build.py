@@ -22,7 +22,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libexseq.so")
-SOURCES = ("exseq_api.cpp", "exseq_model.cpp", "exseq_sum.hip", "exseq_pass.hip", "exseq_ssim.hip")
+SOURCES = ("exseq_api.cpp", "exseq_model.cpp", "exseq_twin.cpp", "exseq_sum.hip", "exseq_pass.hip",
+           "exseq_ssim.hip")
 ARCH = "gfx950"
 
 COMMON = [

@@ -154,7 +154,7 @@ __device__ __forceinline__ double chunk_tree(const Four &f, double *lds4)
 // ---------------------------------------------------------------------------
 // The plan
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t plan_key(double p, uint32_t flags)
+EXSEQ_HD uint32_t plan_key(double p, uint32_t flags)
 {
     const uint32_t mode = flags & EXSEQ_PLAN_MASK;
     if (mode == EXSEQ_PLAN_ALL_FALLBACK)
@@ -258,7 +258,7 @@ __device__ double lookback(const uint64_t *st0, uint32_t c, double init, uint32_
 
 // A composed run over many tiles: the components stay bounded (a run that
 // large never applies, so it is only marked bad).
-__device__ __forceinline__ Run run_compose_sat(const Run &a, const Run &b)
+EXSEQ_HD Run run_compose_sat(const Run &a, const Run &b)
 {
     Run c = run_compose(a, b);
     const int64_t lim = (int64_t)1 << 56;
@@ -446,7 +446,7 @@ __device__ __forceinline__ void wave_runs(const Four *f, const uint32_t *key,
 }
 
 // The four waves' parts composed in order.
-__device__ __forceinline__ WaveRun join_waves(const WaveRun *w)
+EXSEQ_HD WaveRun join_waves(const WaveRun *w)
 {
     WaveRun r = w[0];
 #pragma unroll
@@ -465,7 +465,7 @@ __device__ __forceinline__ WaveRun join_waves(const WaveRun *w)
 
 // A run whose increment exceeds the width of a binade can never apply;
 // clearing it keeps every sum of runs far from int64 overflow.
-__device__ __forceinline__ WaveRun clamp_run(WaveRun r)
+EXSEQ_HD WaveRun clamp_run(WaveRun r)
 {
     const int64_t lim = kCountLo + 1;
     if (r.p.r0 > lim || r.p.r0 < -lim || r.p.r1 > lim || r.p.r1 < -lim || r.hi > lim ||
@@ -915,8 +915,8 @@ constexpr uint64_t kInclXor = 0xFFF8000000000001ULL;
 constexpr uint64_t kInclFailed = 1;
 constexpr uint64_t kQuietNaN = 0x7FF8000000000000ULL;
 
-__device__ __forceinline__ uint64_t enc_i64(int64_t v) { return (uint64_t)v ^ kIntTag; }
-__device__ __forceinline__ int64_t dec_i64(uint64_t w) { return (int64_t)(w ^ kIntTag); }
+EXSEQ_HD uint64_t enc_i64(int64_t v) { return (uint64_t)v ^ kIntTag; }
+EXSEQ_HD int64_t dec_i64(uint64_t w) { return (int64_t)(w ^ kIntTag); }
 __device__ __forceinline__ uint64_t enc_sum(double s)
 {
     return (s == s ? dbits(s) : kQuietNaN) ^ kInclXor;
@@ -939,11 +939,11 @@ __device__ __forceinline__ Run wave_reduce_run_rev(Run v)
 // Runs that compose by a plain sum of their increments: tie-free and
 // monotone, every one non-decreasing (no flag, the bounds unused) or every
 // one non-increasing (kFlagNeg, bounds (total, 0)).
-__device__ __forceinline__ bool rising_run(const Pair &p, uint32_t flags)
+EXSEQ_HD bool rising_run(const Pair &p, uint32_t flags)
 {
     return p.r0 == p.r1 && flags == 0u && p.r0 >= 0;
 }
-__device__ __forceinline__ bool falling_run(const Pair &p, int64_t lo, int64_t hi, uint32_t flags)
+EXSEQ_HD bool falling_run(const Pair &p, int64_t lo, int64_t hi, uint32_t flags)
 {
     return p.r0 == p.r1 && flags == kFlagNeg && p.r0 <= 0 && lo == p.r0 && hi == 0;
 }
@@ -1121,11 +1121,11 @@ __device__ __forceinline__ int chain_back(const ChainArea &ch, uint32_t tb, uint
 // alone shows that no second crossing happened).  Only chunks with no
 // negative scaled term and nothing bad under either binade get a crossing.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int64_t rec_pack(Pair p)
+EXSEQ_HD int64_t rec_pack(Pair p)
 {
     return p.r0 * 4 + (p.r1 - p.r0 + 1);
 }
-__device__ __forceinline__ Pair rec_unpack(int64_t v)
+EXSEQ_HD Pair rec_unpack(int64_t v)
 {
     const int64_t r0 = v >> 2;
     return Pair{r0, r0 + (v & 3) - 1};
@@ -1346,7 +1346,7 @@ __device__ __forceinline__ bool crossing_find(const Four &f, int len, uint32_t k
 // in, through the published bounds (Research-1424 Findings 3).  The pairs
 // w[kXsuf] and w[kXwhole] of a chunk without one may also take in runs that
 // follow the chunk in the next binade: every success applies one of them.
-__device__ __forceinline__ int crossing_apply(const uint64_t *w, int len, uint32_t key, uint32_t fl,
+EXSEQ_HD int crossing_apply(const uint64_t *w, int len, uint32_t key, uint32_t fl,
                                               bool down, double &S, int &pos)
 {
     // a downward crossing has falling counts: every bound is checked
@@ -1415,7 +1415,7 @@ __host__ __device__ __forceinline__ bool chain_on(uint32_t flags)
 // rounds by at most half a count, and rounding errors of either sum grow like
 // a random walk, so this is far beyond their usual distance.  The margin only
 // decides which chunks the chain adds term by term, never a result.
-__device__ __forceinline__ int64_t plan_margin(uint32_t chunks_to_end)
+EXSEQ_HD int64_t plan_margin(uint32_t chunks_to_end)
 {
     return 4096 + (int64_t)(64.0 * __builtin_sqrt((double)chunks_to_end * (double)kChunk));
 }

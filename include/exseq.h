@@ -286,6 +286,7 @@ const char *exseq_version(void);
 #define EXSEQ_MUT_NO_BINADE_CHECK 2u
 #define EXSEQ_MUT_NO_UPPER_CHECK 4u
 #define EXSEQ_MUT_IGNORE_PARITY 8u
+#define EXSEQ_MUT_NO_RUN_TOP 16u
 double exseq_model_seq_sum_f64(const double *x, size_t n, double init,
                                size_t chunk_terms, uint32_t flags,
                                uint32_t mutations, exseq_stats *stats);

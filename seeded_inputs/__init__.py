@@ -128,3 +128,97 @@ def lcs_records(windows: int = FRAME_N, seed: int = 0) -> np.ndarray:
     rec[:, 2] = c
     rec[:, 3] = s
     return rec.reshape(-1)
+
+
+# ---------------------------------------------------------------------------
+# Adversarial sums for the CPU twin of the kernels' composition: each a few
+# chunks of 1024 terms whose running sum, in units u = 2^(e - 52) of the
+# binade [2^e, 2^(e+1)) it starts in, comes close to or crosses a binade edge
+# in the ways the fast paths must refuse or take exactly.  Families:
+#
+# * ``rise_fall`` -- a negative term in the chunk's first 256 terms, a rise
+#   of ~50,000 units over the next 512 that passes 2^(e+1), a fall over the
+#   last 256 that comes back below it (the chunk's own sum stays inside).
+# * ``edge_counts`` -- whole-unit terms whose running count lands exactly on
+#   2^52, 2^52 + 1, 2^53 - 1 or 2^53 at a chunk's end, then odd terms.
+# * ``ties`` -- terms of k + 1/2 units (ties) among whole units, placed on
+#   lane, wave and chunk edges.
+# * ``falling`` -- a sum starting just above 2^e that falls through it.
+# * ``neg_cross`` -- a negative term early, an upward crossing late.
+# * ``neg_rise`` -- a negative term in the first 256 terms, a rise over the
+#   last 256 that passes 2^(e+1) at the chunk's end (the chunk among a sum's
+#   first four, or after them).
+# * ``mixed`` -- signed terms spanning a few binades.
+#
+# A sum's first chunks are zeros or not (the adversarial chunk in a sum's
+# first four chunks, or in the tiles after them); regular chunks may follow.
+# ---------------------------------------------------------------------------
+TWIN_FAMILIES = ("rise_fall", "edge_counts", "ties", "falling", "neg_cross", "neg_rise", "mixed")
+
+
+def twin_case(seed: int, family: str):
+    """(terms, init) of one adversarial sum."""
+    g = rng(seed)
+    C = 1024
+    e = int(g.integers(-60, 60))
+    u = 2.0 ** (e - 52)
+    lead = int(g.choice([0, 1, 2, 3, 4, 5]))    # zero chunks before (head or tiles)
+    tail = int(g.integers(0, 10))               # quiet chunks after
+    parts = [np.zeros(lead * C)]
+    if family == "rise_fall":
+        rise = g.uniform(50.0, 150.0, 2 * 256)
+        fall = -g.uniform(150.0, 250.0, 256)
+        w0 = g.uniform(0.0, 2.0, 256)
+        w0[int(g.integers(0, 256))] = -g.uniform(1.0, 3.0)
+        R = float(rise.sum())
+        m0 = 2.0 ** 53 - np.floor(R * g.uniform(0.2, 0.8))
+        init = m0 * u
+        parts.append(np.concatenate([w0, rise, fall]) * u)
+    elif family == "neg_rise":
+        w = g.uniform(0.0, 2.0, 768)
+        w[int(g.integers(0, 256))] = -g.uniform(1.0, 3.0)
+        rise = g.uniform(50.0, 150.0, 256)
+        m0 = 2.0 ** 53 - float(w.sum()) - np.floor(float(rise.sum()) * g.uniform(0.2, 0.9))
+        init = m0 * u
+        parts.append(np.concatenate([w, rise]) * u)
+    elif family == "edge_counts":
+        up = bool(g.integers(0, 2))
+        t = g.integers(1, 20, C).astype(np.float64)
+        T = float(t.sum())
+        d = float(g.integers(-1, 2))
+        if up:
+            m0 = 2.0 ** 53 - T - d
+            chunk = t
+        else:
+            m0 = 2.0 ** 52 + T + d
+            chunk = -t
+        init = m0 * u
+        odd = (2.0 * g.integers(0, 8, C) + 1.0) * (1 if up else -1)
+        parts += [chunk * u, odd * u]
+    elif family == "ties":
+        m0 = 2.0 ** 52 + float(g.integers(0, 2 ** 51))
+        init = m0 * u
+        k = g.integers(0, 6, 2 * C).astype(np.float64)
+        half = g.random(2 * C) < 0.3
+        for p in (0, 3, 4, 63, 64, 255, 256, 1023, 1024, 1279, 1280):
+            half[p] = True
+        parts.append((k + np.where(half, 0.5, 0.0)) * u)
+    elif family == "falling":
+        F = 40000.0
+        m0 = 2.0 ** 52 + np.floor(F * g.uniform(0.2, 0.8))
+        init = m0 * u
+        x = -g.uniform(50.0, 110.0, C)
+        x[g.random(C) < 0.05] *= -0.5
+        parts.append(x * u)
+    elif family == "neg_cross":
+        x = g.uniform(10.0, 60.0, C)
+        x[int(g.integers(0, 256))] = -g.uniform(1.0, 400.0)
+        m0 = 2.0 ** 53 - np.floor(float(x[:768].sum()) + g.uniform(0.0, float(x[768:].sum())))
+        init = m0 * u
+        parts.append(x * u)
+    else:  # mixed
+        init = float(g.uniform(-4.0, 4.0)) * 2.0 ** e
+        x = g.normal(0.0, 1.0, 2 * C) * 2.0 ** (e + g.integers(-12, 2, 2 * C).astype(np.float64))
+        parts.append(x)
+    parts.append(np.zeros(tail * C) if g.random() < 0.5 else g.uniform(0.0, 1.0, tail * C) * u)
+    return np.concatenate(parts).astype(np.float64), float(init)

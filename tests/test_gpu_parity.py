@@ -349,3 +349,20 @@ def test_rise_after_negative_term(flags):
     for n in (3072, 4096, 5000, 40960, 518400):
         x = f[:n]
         assert same(gpu_sum(torch, x, 0.0, flags=flags), oracle.seq_sum(x)), (n, flags)
+
+
+def test_twin_replays_the_single_pass():
+    """The CPU twin of the single pass takes the kernel's paths: the same
+    result and the same fast and term-by-term chunk counts on the GPU."""
+    torch = torch_cuda()
+    cases = (("tie_heavy 100003", si.tie_heavy(100_003, 41), 0.0),
+             ("signed 300001", si.signed_terms(300_001, 42), 0.0),
+             ("tie suite", si.tie_suite(1 << 20, 43), 1.0),
+             ("negated tie_heavy", -si.tie_heavy(200_000, 44), 0.0),
+             ("tie_heavy 3840x2160", si.tie_heavy(si.FRAME_N, 45), 0.0))
+    for name, x, init in cases:
+        got, st = gpu_sum(torch, x, init, ex.PASS_PATH, stats=True)
+        tw, tst = ex.twin_seq_sum(x, init)
+        say(name, st, tst)
+        assert same(got, tw), name
+        assert (st["fast_chunks"], st["fallback_chunks"]) == (tst["fast_chunks"], tst["fallback_chunks"]), name
