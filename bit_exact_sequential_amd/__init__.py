@@ -129,6 +129,8 @@ def lib():
     L.exact_seq_sum_f64_profiled.restype = i32
     L.exact_seq_sum_f64_profiled.argtypes = [vp, sz, ctypes.c_double, vp, vp, sz, vp, u32, vp,
                                              ctypes.POINTER(vp), i32]
+    L.exseq_div_f64.restype = i32
+    L.exseq_div_f64.argtypes = [vp, vp, vp, sz, vp]
     L.exseq_twin_seq_sum_f64.restype = ctypes.c_double
     L.exseq_twin_seq_sum_f64.argtypes = [vp, sz, ctypes.c_double, u32, u32, vp]
     L.exseq_model_seq_sum_f64.restype = ctypes.c_double
@@ -421,6 +423,22 @@ def tree_sum(x, *, out=None, ws=None, stream=None):
 # ---------------------------------------------------------------------------
 # Host model of the method (CPU; test infrastructure for the rules)
 # ---------------------------------------------------------------------------
+
+def device_div(a, b, *, stream=None):
+    """a / b elementwise (float64 device tensors) with the fused SSIM term's
+    device division."""
+    torch = _torch()
+    _check_device_f64(a)
+    _check_device_f64(b)
+    if a.numel() != b.numel():
+        raise ExseqError("a and b must have the same size")
+    q = torch.empty_like(a)
+    rc = lib().exseq_div_f64(a.data_ptr(), b.data_ptr(), q.data_ptr(), a.numel(),
+                             _stream_handle(stream, a.device))
+    _check(rc, "exseq_div_f64")
+    _keep_for(stream, a.device, q)
+    return q
+
 
 def twin_seq_sum(x, init: float = 0.0, flags: int = 0, mutations: int = 0):
     """The single pass replayed on the host in the kernels' grouping of the

@@ -252,6 +252,15 @@ int ssim_term_and_sum(const uint8_t *ref, const uint8_t *dis, int width, int hei
                            flags, stats);
 }
 
+int exseq_div_f64(const double *a, const double *b, double *q, size_t n, exseq_stream_t stream)
+{
+    if (n && (!a || !b || !q || !aligned8(a) || !aligned8(b) || !aligned8(q)))
+        return EXSEQ_EINVAL;
+    if ((n + 255) / 256 > 0x7FFFFFFFull)
+        return EXSEQ_EINVAL;
+    return launch_div(a, b, q, n, reinterpret_cast<hipStream_t>(stream));
+}
+
 size_t tree_sum_f64_workspace_size(size_t n) { return round256(chunks_of(n) * sizeof(double)) + 256; }
 
 int tree_sum_f64(const double *x, size_t n, double *out, void *ws, size_t ws_bytes,

@@ -134,6 +134,7 @@ int launch_tree_sum(const double *x, size_t n, double *out, void *ws, hipStream_
 
 // Workspace of the fused SSIM sum: the exact sum's, over width * height terms.
 size_t ssim_ws_bytes(int width, int height);
+int launch_div(const double *a, const double *b, double *q, size_t n, hipStream_t stream);
 int launch_ssim_sum(const uint8_t *ref, const uint8_t *dis, int width, int height,
                     ptrdiff_t stride, int radius, double c1, double c2, double *out_sum,
                     int64_t *out_weight_sum, double *out_terms, void *ws, hipStream_t stream,

@@ -10,6 +10,7 @@
 #include "exseq.h"
 #include "exseq_internal.h"
 #include "exseq_rules.h"
+#include "exseq_ssim_dev.h"
 
 namespace exseq {
 
@@ -23,6 +24,22 @@ static int64_t line_sum(int len, int radius)
         s += hi - lo + 1;
     }
     return s;
+}
+
+__global__ void div_kernel(const double *a, const double *b, double *q, size_t n)
+{
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        q[i] = ssim_div(a[i], b[i]);
+}
+
+int launch_div(const double *a, const double *b, double *q, size_t n, hipStream_t stream)
+{
+    if (n == 0)
+        return EXSEQ_OK;
+    const size_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(div_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a, b, q, n);
+    return hipGetLastError() == hipSuccess ? EXSEQ_OK : EXSEQ_EHIP;
 }
 
 size_t ssim_ws_bytes(int width, int height)

@@ -27,6 +27,10 @@
 
 namespace exseq {
 
+// The term's one division (also run alone by exseq_div_f64, so that tests
+// can compare it with the host's division on many operands).
+__device__ __forceinline__ double ssim_div(double num, double den) { return num / den; }
+
 __device__ __forceinline__ double ssim_term_dev(int64_t x, int64_t y, int64_t x2, int64_t y2,
                                                 int64_t xy, int64_t w, double c1, double c2)
 {
@@ -37,7 +41,7 @@ __device__ __forceinline__ double ssim_term_dev(int64_t x, int64_t y, int64_t x2
     const double num = w_d * (2.0 * mxy + c1) * (c2 + 2.0 * ((double)xy * w_d - mxy));
     const double den = (mx2 + my2 + c1) *
                        ((double)x2 * w_d - mx2 + (double)y2 * w_d - my2 + c2);
-    return num / den;
+    return ssim_div(num, den);
 }
 
 // Terms of a chunk (1024 consecutive pixels in raster order) for the 256

@@ -267,6 +267,16 @@ int exact_seq_sum_f64_profiled(const double *x, size_t n, double init, double *o
                                uint32_t flags, exseq_stats *stats,
                                void *const *events, int n_events);
 
+/* ---------------------------------------------------------------------------
+ * exseq_div_f64
+ *   q[i] = a[i] / b[i] for i < n: the device fp64 division that the fused
+ *   SSIM term performs (Research-1424 Findings 1: the term's one divide), run
+ *   alone so that tests can compare it with the host's correctly rounded
+ *   division on many operands.  a, b, q: device arrays of n doubles (8-byte
+ *   aligned); stream-ordered; EXSEQ_EINVAL for null or misaligned pointers.
+ * ------------------------------------------------------------------------- */
+int exseq_div_f64(const double *a, const double *b, double *q, size_t n, exseq_stream_t stream);
+
 /* Text for an EXSEQ_* return code (static storage). */
 const char *exseq_strerror(int code);
 
