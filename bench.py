@@ -37,8 +37,16 @@ if ROOT not in sys.path:
 
 METRIC = "fp64 terms/sec (GB/s, % HBM roofline) for bit-exact seq sum @3840x2160"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published peak
+# MI355X fp64 vector peak, published: 256 CUs x 4 SIMDs x 16 fp64 lanes x 2
+# (a fused multiply-add) x 2.4 GHz = 78.6 TFLOP/s
+FP64_VALU_PEAK_TFLOPS = 78.6
+# fp64 operations of one integer-SSIM term as the fused producer evaluates
+# it: the three moment products, eight in the numerator, nine in the
+# denominator, one division
+SSIM_TERM_FLOPS = 21
 TERM_BYTES = 8
 CHUNK = 1024
+L_STREAM_BLOCKS = 2048          # EXSEQ_STREAM_READ_BLOCKS
 PROFILE = os.path.join(ROOT, "profiles", "exact_sum_tie_heavy_3840x2160.md")
 TRAFFIC_TAG = "traffic record:"
 
@@ -181,9 +189,17 @@ def time_configs(ex, si, torch, dev, seed, reps=30):
     d4 = torch.from_numpy(dis).to(dev)
     w4 = ex.workspace(ex.lib().ssim_term_and_sum_workspace_size(si.FRAME_W, si.FRAME_H), dev)
     ms = timed(lambda: ex.ssim_term_and_sum(r4, d4, 3, ws=w4), reps)
+    tflops = SSIM_TERM_FLOPS * si.FRAME_N / (ms * 1e-3) / 1e12
     res["fused_ssim_3840x2160"] = {"us_per_frame": ms * 1e3,
                                    "pixels_per_s": si.FRAME_N / (ms * 1e-3),
-                                   "plane_gbs": 2 * si.FRAME_N / (ms * 1e-3) / 1e9}
+                                   "plane_gbs": 2 * si.FRAME_N / (ms * 1e-3) / 1e9,
+                                   "roofline": {"bound": "alu", "kernel": "tile_kernel<SsimTerms>",
+                                                "achieved": tflops, "peak": FP64_VALU_PEAK_TFLOPS,
+                                                "unit": "TFLOP/s", "frac": tflops / FP64_VALU_PEAK_TFLOPS,
+                                                "flops_per_pixel": SSIM_TERM_FLOPS,
+                                                "note": "fp64 operations of the terms only (the "
+                                                        "window moments are integer work); peak = "
+                                                        "256 CUs x 4 SIMDs x 16 lanes x 2 x 2.4 GHz"}}
 
     x6 = torch.from_numpy(si.lcs_records(si.FRAME_N, seed)).to(dev)
     o6 = torch.empty(4, dtype=torch.float64, device=dev)
@@ -202,9 +218,14 @@ def time_configs(ex, si, torch, dev, seed, reps=30):
     w5 = ex.workspace(ex.lib().exact_seq_sum_f64_batch_workspace_size(nsa, len(ns)), dev)
     o5 = torch.empty(len(xs), dtype=torch.float64, device=dev)
     ms = timed(lambda: ex.exact_seq_sum_batch(xs, out=o5, ws=w5), max(3, reps // 3))
+    gbs5 = total * 8 / (ms * 1e-3) / 1e9
     res["pyramid_batch_108"] = {"us_per_batch": ms * 1e3, "sums": len(xs), "terms": total,
-                                "terms_per_s": total / (ms * 1e-3),
-                                "gbs": total * 8 / (ms * 1e-3) / 1e9}
+                                "terms_per_s": total / (ms * 1e-3), "gbs": gbs5,
+                                "roofline": {"bound": "hbm", "kernel": "pass_kernel", "achieved": gbs5,
+                                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                             "frac": gbs5 / HBM_PEAK_GBS,
+                                             "note": "whole call (two launches of 64 and 44 sums); "
+                                                     "bytes = the terms read once"}}
     # the same batch as a video: two pyramids (frames) in turn, each call
     # keeping its plan for the next (EXSEQ_PLAN_REUSE); same bits required
     ref_bits = o5.cpu().numpy().view(np.uint64).copy()
@@ -227,6 +248,82 @@ def time_configs(ex, si, torch, dev, seed, reps=30):
                                            "note": "two pyramids in turn; each call keeps its plan for the next"}
     del xs, xs2
     return res
+
+
+def cpu_info():
+    """The host's CPU: processor count, the ones this process may use, model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    n = os.cpu_count() or 1
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = n
+    return {"nproc": n, "cores_available": avail,
+            "cpu_model": model or platform.processor() or platform.machine()}
+
+
+def cpu_configs(oracle, si, seed, threads, budget_s):
+    """The oracle on all host cores for the pyramid batch (one sum per task),
+    and staged for the fused SSIM frame (the terms on all cores by bands of
+    rows, then the raster-order sum on one core), each best of up to nine
+    runs within the budget (Research-1424 Findings 2 times the host loop as
+    the best of nine).  ctypes releases the GIL around the oracle's C calls,
+    so threads run them in parallel."""
+    from concurrent.futures import ThreadPoolExecutor
+    import numpy as np
+    out = {}
+    arrays = si.pyramid(seed)
+    total = sum(int(a.size) for a in arrays)
+    with ThreadPoolExecutor(threads) as pool:
+        times, t0 = [], time.perf_counter()
+        while True:
+            a = time.perf_counter()
+            vals = list(pool.map(oracle.seq_sum, arrays))
+            times.append(time.perf_counter() - a)
+            if time.perf_counter() - t0 > budget_s or len(times) >= 9:
+                break
+        best = min(times)
+        assert np.array_equal(np.array(vals).view(np.uint64), oracle.seq_sum_many(arrays).view(np.uint64))
+        out["pyramid_batch_108"] = {
+            "value": total / best, "unit": "terms/s", "cores": threads, "kind": "oracle",
+            "sample": "all 108 sums (%d terms), one in-order loop per sum, %d threads, best of %d "
+                      "(%.1f ms)" % (total, threads, len(times), best * 1e3)}
+        del arrays
+        H, W, r = si.FRAME_H, si.FRAME_W, 3
+        ref, dis = si.frame_pair(H, W, seed)
+        rows = np.linspace(0, H, threads + 1).astype(int)
+
+        def band(k):
+            r0, r1 = int(rows[k]), int(rows[k + 1])
+            a0, a1 = max(0, r0 - r), min(H, r1 + r)
+            _, _, t = oracle.ssim_frame_sum(ref[a0:a1], dis[a0:a1], r, want_terms=True)
+            return t[r0 - a0:r0 - a0 + (r1 - r0)]
+        times, t0 = [], time.perf_counter()
+        while True:
+            a = time.perf_counter()
+            terms = np.concatenate(list(pool.map(band, range(threads))))
+            b = time.perf_counter()
+            s = oracle.seq_sum(terms.ravel())
+            c = time.perf_counter()
+            times.append((c - a, b - a, c - b))
+            if time.perf_counter() - t0 > budget_s or len(times) >= 9:
+                break
+        best = min(times)
+        assert s == oracle.ssim_frame_sum(ref, dis, r)[0]
+        out["fused_ssim_3840x2160"] = {
+            "value": si.FRAME_N / best[0], "unit": "pixels/s", "cores": threads, "kind": "oracle (staged)",
+            "sample": "one 3840x2160 frame pair: window moments and terms on %d threads by bands of "
+                      "rows, then the raster-order sum on one core; best of %d (%.1f ms terms + "
+                      "%.1f ms sum)" % (threads, len(times), best[1] * 1e3, best[2] * 1e3)}
+    return out
 
 
 def main():
@@ -374,6 +471,23 @@ def main():
     tree0 = float(tout[0].cpu())
     exact0 = float(outs[0].cpu())
 
+    # ---- a plain streaming read of the same buffers: the achievable rate ---
+    sro = torch.empty(L_STREAM_BLOCKS, dtype=torch.int64, device=dev)
+    for i in range(args.warmup):
+        L.exseq_stream_read_f64(xp[i % args.buffers], n, sro.data_ptr(), sh)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        L.exseq_stream_read_f64(xp[i % args.buffers], n, sro.data_ptr(), sh)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    read_ms = t0.elapsed_time(t1) / args.steps
+    read_gbs = n * TERM_BYTES / (read_ms * 1e-3) / 1e9
+    stream_read = {"us": read_ms * 1e3, "gbs": read_gbs, "hbm_frac": read_gbs / HBM_PEAK_GBS,
+                   "exact_sum_frac_of_it": gbs / read_gbs,
+                   "note": "exseq_stream_read_f64 over the same rotated buffers: 16-byte loads, "
+                           "one xor per block; the achievable read rate beside the exact sum"}
+
     # ---- copy reference for the PMC byte counters ---------------------------
     if args.copy_ref:
         src = torch.empty(64 * 1024 * 1024, dtype=torch.float64, device=dev)  # 512 MiB
@@ -403,11 +517,16 @@ def main():
             if time.perf_counter() - tstart > args.cpu_seconds or len(times) >= 2000:
                 break
         med = statistics.median(times)
+        info = cpu_info()
         cpu = {"value": n / med, "unit": "terms/s", "cores": 1, "kind": "oracle",
                "sample": "the whole %d-term workload (buffer 0), %d repetitions in %.1f s; "
-                         "median %.3f ms, best %.3f ms; %s"
+                         "median %.3f ms, best %.3f ms"
                          % (n, len(times), time.perf_counter() - tstart, med * 1e3,
-                            min(times) * 1e3, platform.processor() or platform.machine())}
+                            min(times) * 1e3)}
+        cpu.update(info)
+        if not args.no_configs:
+            cpu["configs"] = cpu_configs(oracle, si, args.seed, info["cores_available"],
+                                         args.cpu_seconds)
         oracle_bits = np.array([s_cpu]).view(np.uint64)[0]
         parity = bool(oracle_bits == res[0])
         assert parity, "bench result differs from the oracle"
@@ -445,6 +564,7 @@ def main():
         "kernels_avg_us": {k: v * 1e3 for k, v in avg_ms.items()},
         "tree_sum": {"ms_per_step": tree_ms, "value": tree0, "exact": exact0,
                      "gap": tree0 - exact0},
+        "stream_read": stream_read,
         "host_wall_ms_per_step": wall * 1e3 / args.steps,
         "video_plan_reuse": video,
         "other_configs": others,

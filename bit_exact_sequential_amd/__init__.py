@@ -129,6 +129,8 @@ def lib():
     L.exact_seq_sum_f64_profiled.restype = i32
     L.exact_seq_sum_f64_profiled.argtypes = [vp, sz, ctypes.c_double, vp, vp, sz, vp, u32, vp,
                                              ctypes.POINTER(vp), i32]
+    L.exseq_stream_read_f64.restype = i32
+    L.exseq_stream_read_f64.argtypes = [vp, sz, vp, vp]
     L.exseq_div_f64.restype = i32
     L.exseq_div_f64.argtypes = [vp, vp, vp, sz, vp]
     L.exseq_twin_seq_sum_f64.restype = ctypes.c_double

@@ -252,6 +252,13 @@ int ssim_term_and_sum(const uint8_t *ref, const uint8_t *dis, int width, int hei
                            flags, stats);
 }
 
+int exseq_stream_read_f64(const double *x, size_t n, uint64_t *out, exseq_stream_t stream)
+{
+    if (!out || !aligned8(out) || (n && (!x || (reinterpret_cast<uintptr_t>(x) & 15u))))
+        return EXSEQ_EINVAL;
+    return launch_stream_read(x, n, out, reinterpret_cast<hipStream_t>(stream));
+}
+
 int exseq_div_f64(const double *a, const double *b, double *q, size_t n, exseq_stream_t stream)
 {
     if (n && (!a || !b || !q || !aligned8(a) || !aligned8(b) || !aligned8(q)))

@@ -131,6 +131,7 @@ int launch_pass(const BatchArgs &a, void *ws, double *outs, hipStream_t stream,
 extern const char *const kPathKernels[];
 extern const int kPathKernelCount;
 int launch_tree_sum(const double *x, size_t n, double *out, void *ws, hipStream_t stream);
+int launch_stream_read(const double *x, size_t n, uint64_t *out, hipStream_t stream);
 
 // Workspace of the fused SSIM sum: the exact sum's, over width * height terms.
 size_t ssim_ws_bytes(int width, int height);

@@ -1008,9 +1008,10 @@ WsParts carve(void *ws, size_t total)
 }
 }  // namespace
 
-// The kernels of the default path of a plain sum (the single pass).
-const char *const kPathKernels[] = {"pass_kernel"};
-const int kPathKernelCount = 1;
+// The kernels of the default path of one plain sum (the tile chain), in
+// launch order, for the profiled entry point.
+const char *const kPathKernels[] = {"chain_clear_kernel", "tile_kernel", "walk_kernel"};
+const int kPathKernelCount = 3;
 
 // Per chunk (a tile is at least one chunk): the plan status word, the four
 // descriptor arrays, the chain words; per sum a head word and a kept-plan
@@ -1168,6 +1169,39 @@ int launch_exact_sum(const double *x, size_t n, double init, double *out, void *
     a.chunk_base[0] = 0;
     a.chunk_base[1] = (uint32_t)padded_chunks(n);
     return launch_batch(a, ws, out, stream, stats, events, n_events);
+}
+
+// A plain streaming read of n doubles: 16-byte non-temporal loads over a
+// grid-stride loop, each block folding the bits it read with xor into one
+// word out[block] (so that no load can be dropped).  The achievable read
+// rate over a buffer, measured beside the exact sum.
+__global__ __launch_bounds__(256) void stream_read_kernel(const double *x, size_t n, uint64_t *out)
+{
+    typedef double v2d __attribute__((ext_vector_type(2)));
+    const size_t pairs = n / 2;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    uint64_t acc = 0;
+    const v2d *p = reinterpret_cast<const v2d *>(x);
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < pairs; i += stride) {
+        const v2d v = __builtin_nontemporal_load(p + i);
+        acc ^= dbits(v.x) ^ (dbits(v.y) * 3u);
+    }
+    if ((n & 1) && blockIdx.x == 0 && threadIdx.x == 0)
+        acc ^= dbits(x[n - 1]);
+    __shared__ uint64_t part[4];
+    for (int o = 32; o > 0; o >>= 1)
+        acc ^= (uint64_t)__shfl_xor((unsigned long long)acc, o);
+    if ((threadIdx.x & 63) == 0)
+        part[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        out[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+
+int launch_stream_read(const double *x, size_t n, uint64_t *out, hipStream_t stream)
+{
+    hipLaunchKernelGGL(stream_read_kernel, dim3(EXSEQ_STREAM_READ_BLOCKS), dim3(256), 0, stream, x, n, out);
+    return hipGetLastError() == hipSuccess ? EXSEQ_OK : EXSEQ_EHIP;
 }
 
 int launch_tree_sum(const double *x, size_t n, double *out, void *ws, hipStream_t stream)

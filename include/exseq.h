@@ -268,6 +268,19 @@ int exact_seq_sum_f64_profiled(const double *x, size_t n, double init, double *o
                                void *const *events, int n_events);
 
 /* ---------------------------------------------------------------------------
+ * exseq_stream_read_f64
+ *   A plain streaming read of x[0 .. n) (16-byte loads): the achievable HBM
+ *   read rate over the buffer the exact sum reads, measured beside it (a
+ *   measurement reference, not part of the method).  Each of the
+ *   EXSEQ_STREAM_READ_BLOCKS workgroups writes the xor of the bit patterns it
+ *   read to out[block].  x: device, 16-byte aligned; out: device array of
+ *   EXSEQ_STREAM_READ_BLOCKS words.  EXSEQ_EINVAL for null or misaligned
+ *   pointers.
+ * ------------------------------------------------------------------------- */
+#define EXSEQ_STREAM_READ_BLOCKS 2048
+int exseq_stream_read_f64(const double *x, size_t n, uint64_t *out, exseq_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * exseq_div_f64
  *   q[i] = a[i] / b[i] for i < n: the device fp64 division that the fused
  *   SSIM term performs (Research-1424 Findings 1: the term's one divide), run
