@@ -94,6 +94,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="bound on the oracle timing (cpu_baseline)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    ap.add_argument("--config", choices=CONFIG_NAMES, action="append",
+                    help="time only this workload (repeatable) and print its line; for profiling")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip timing the other configurations")
     ap.add_argument("--copy-ref", action="store_true",
@@ -133,7 +135,11 @@ class Hip:
         self.L.hipEventDestroy(e)
 
 
-def time_configs(ex, si, torch, dev, seed, reps=30):
+CONFIG_NAMES = ("uniform_4096", "signed_1920x1080", "negated_tie_heavy_3840x2160",
+                "fused_ssim_3840x2160", "lcs_interleaved_3840x2160", "pyramid_batch_108")
+
+
+def time_configs(ex, si, torch, dev, seed, reps=30, only=None):
     """Device time per call of the other workloads (torch events on the
     library's stream, after a warm-up call).  Sizes: the uniform 4096-term
     sum, the signed 1920x1080 sum, the fused SSIM sum of two 3840x2160
@@ -154,12 +160,33 @@ def time_configs(ex, si, torch, dev, seed, reps=30):
 
     import numpy as np
     res = {}
+
+    def want(name):
+        return only is None or name in only
+    if want("uniform_4096"):
+        _uniform(ex, si, torch, dev, seed, reps, timed, res)
+    if want("signed_1920x1080"):
+        _signed(ex, si, torch, dev, seed, reps, timed, res)
+    if want("negated_tie_heavy_3840x2160"):
+        _negated(ex, si, torch, dev, seed, reps, timed, res)
+    if want("fused_ssim_3840x2160"):
+        _ssim(ex, si, torch, dev, seed, reps, timed, res)
+    if want("lcs_interleaved_3840x2160"):
+        _lcs(ex, si, torch, dev, seed, reps, timed, res)
+    if want("pyramid_batch_108"):
+        _pyramid(ex, si, torch, dev, seed, reps, timed, res, video=only is None)
+    return res
+
+
+def _uniform(ex, si, torch, dev, seed, reps, timed, res):
     x1 = torch.from_numpy(si.uniform(4096, seed)).to(dev)
     o1 = torch.empty(1, dtype=torch.float64, device=dev)
     w1 = ex.workspace(ex.lib().exact_seq_sum_f64_workspace_size(4096), dev)
     ms = timed(lambda: ex.exact_seq_sum(x1, out=o1, ws=w1), reps)
     res["uniform_4096"] = {"us_per_sum": ms * 1e3, "terms_per_s": 4096 / (ms * 1e-3)}
 
+
+def _signed(ex, si, torch, dev, seed, reps, timed, res):
     n3 = si.HALF_N
     x3 = [torch.from_numpy(si.signed_terms(n3, seed + b)).to(dev) for b in range(4)]
     o3 = torch.empty(1, dtype=torch.float64, device=dev)
@@ -174,6 +201,8 @@ def time_configs(ex, si, torch, dev, seed, reps=30):
                                "gbs": n3 * 8 / (ms * 1e-3) / 1e9,
                                "buffers_rotated": 4}
 
+
+def _negated(ex, si, torch, dev, seed, reps, timed, res):
     x7 = torch.from_numpy(-si.tie_heavy(si.FRAME_N, seed)).to(dev)
     o7 = torch.empty(1, dtype=torch.float64, device=dev)
     w7 = ex.workspace(ex.lib().exact_seq_sum_f64_workspace_size(si.FRAME_N), dev)
@@ -184,6 +213,8 @@ def time_configs(ex, si, torch, dev, seed, reps=30):
                                                   "running sum crossing negative binades"}
     del x7
 
+
+def _ssim(ex, si, torch, dev, seed, reps, timed, res):
     ref, dis = si.frame_pair(si.FRAME_H, si.FRAME_W, seed)
     r4 = torch.from_numpy(ref).to(dev)
     d4 = torch.from_numpy(dis).to(dev)
@@ -201,6 +232,8 @@ def time_configs(ex, si, torch, dev, seed, reps=30):
                                                         "window moments are integer work); peak = "
                                                         "256 CUs x 4 SIMDs x 16 lanes x 2 x 2.4 GHz"}}
 
+
+def _lcs(ex, si, torch, dev, seed, reps, timed, res):
     x6 = torch.from_numpy(si.lcs_records(si.FRAME_N, seed)).to(dev)
     o6 = torch.empty(4, dtype=torch.float64, device=dev)
     w6 = ex.workspace(ex.lib().exact_seq_sum_f64_interleaved_workspace_size(si.FRAME_N, 4), dev)
@@ -210,6 +243,9 @@ def time_configs(ex, si, torch, dev, seed, reps=30):
                                         "gbs": 32 * si.FRAME_N / (ms * 1e-3) / 1e9}
     del x6
 
+
+def _pyramid(ex, si, torch, dev, seed, reps, timed, res, video=True):
+    import numpy as np
     xs = [torch.from_numpy(a).to(dev) for a in si.pyramid(seed)]
     total = sum(int(x.numel()) for x in xs)
     ns = [int(x.numel()) for x in xs]
@@ -226,6 +262,8 @@ def time_configs(ex, si, torch, dev, seed, reps=30):
                                              "frac": gbs5 / HBM_PEAK_GBS,
                                              "note": "whole call (two launches of 64 and 44 sums); "
                                                      "bytes = the terms read once"}}
+    if not video:
+        return
     # the same batch as a video: two pyramids (frames) in turn, each call
     # keeping its plan for the next (EXSEQ_PLAN_REUSE); same bits required
     ref_bits = o5.cpu().numpy().view(np.uint64).copy()
@@ -247,7 +285,6 @@ def time_configs(ex, si, torch, dev, seed, reps=30):
                                            "same_bits_as_plain_calls": same,
                                            "note": "two pyramids in turn; each call keeps its plan for the next"}
     del xs, xs2
-    return res
 
 
 def cpu_info():
@@ -341,6 +378,10 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
     dev = torch.device("cuda:0")
+    if args.config:
+        res = time_configs(ex, si, torch, dev, args.seed, reps=args.steps, only=set(args.config))
+        print(json.dumps({"configs": res}), flush=True)
+        return
     L = ex.lib()
     hip = Hip()
     n = si.FRAME_N
