@@ -1775,7 +1775,7 @@ __device__ double walk_descs(const Src &src, const BatchArgs &a, int s,
                 const int i = kPer * t + k;
                 if (i >= cur && i < cnt) {
                     const int64_t mt = m + ((p ? ex[k].r1 : ex[k].r0) - base_p);
-                    const bool ok = fs && dkey[k] == ks && mt >= kCountLo && mt < kCountHi &&
+                    const bool ok = fs && dkey[k] == ks && mt >= count_floor(ks) && mt < kCountHi &&
                                     run_applies(mt, mine[k], dlo[k], dhi[k], dfl[k]);
                     if (!ok) {
                         fk = k;

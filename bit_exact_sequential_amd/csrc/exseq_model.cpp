@@ -124,8 +124,8 @@ extern "C" double exseq_model_seq_sum_f64(const double *x, size_t n, double init
                 int64_t cnt = m + pair_at(run.p, m);
                 if (cnt > kCountHi)   // only reachable under a mutation
                     cnt = kCountHi;
-                if (cnt < kCountLo)
-                    cnt = kCountLo;
+                if (cnt < count_floor(ks))
+                    cnt = count_floor(ks);
                 s = assemble(ks, cnt);
                 fast = true;
             }

@@ -543,7 +543,7 @@ __device__ __forceinline__ double walk_lean(const Src &src, const SumView v, con
             const bool fs = key_has_fast_path(ks);
             const int64_t m = count_of(S);
             const int64_t mt = m + pair_at(X, m);
-            const bool ok = fs && dkey == ks && mt >= kCountLo && mt < kCountHi &&
+            const bool ok = fs && dkey == ks && mt >= count_floor(ks) && mt < kCountHi &&
                             run_applies(mt, mine, dlo, dhi, dfl);
             Cand mc = cand_none();
             if (in && !ok) {
@@ -1159,7 +1159,7 @@ __device__ __forceinline__ void finisher_block(const PassArgs &pa, const Src &sr
                     const uint64_t nxt = op_word(i + 1);
                     const uint32_t meta = (uint32_t)W(cur, 0);
                     sev = (meta & kOpFirst) ? sbits : sev;
-                    const int64_t m = (int64_t)((sbits & kFracMask) | (1ull << 52));
+                    const int64_t m = count_of(bitsd(sbits));
                     const int par = (int)(m & 1);
                     const int64_t a = (int64_t)W(cur, 1), b = (int64_t)W(cur, 2 + par),
                                   c = (int64_t)W(cur, 4 + par);
@@ -1173,7 +1173,7 @@ __device__ __forceinline__ void finisher_block(const PassArgs &pa, const Src &sr
                     const bool edge = (meta & kOpDown) ? (cb >= kCountLo) & (cj < kCountLo)
                                                        : (cb <= kCountHi - 1) & (cj >= kCountHi);
                     const bool okc = (m <= (int64_t)W(cur, 6)) & edge;
-                    const bool ok = ((uint32_t)(sbits >> 52) == ((meta >> 2) & kKeyMask)) &
+                    const bool ok = (key_of(bitsd(sbits)) == ((meta >> 2) & kKeyMask)) &
                                     ((meta & 3u) != kOpFail) & (m >= a) & (reg ? m <= b : okc);
                     const uint64_t crossed =
                         uniform_u64(dbits(bitsd(sbits + (uint64_t)(cb - m)) + bitsd(W(cur, 7))));
@@ -1433,7 +1433,7 @@ __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, c
             if (key_has_fast_path(kk) && kk == key_of(pk)) {
                 const int64_t m = count_of(pk);
                 const int64_t mg = plan_margin(c0 + c + 1);
-                bool near = m < kCountLo + mg;
+                bool near = m < count_floor(kk) + mg;
                 if (r.flags & kFlagNeg)
                     near |= m + r.lo - mg < kCountLo + 1 || m + r.hi + mg > kCountHi - 1;
                 else

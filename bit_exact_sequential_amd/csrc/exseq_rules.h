@@ -64,17 +64,43 @@ EXSEQ_HD uint64_t dbits(double x) { return __builtin_bit_cast(uint64_t, x); }
 EXSEQ_HD double bitsd(uint64_t b) { return __builtin_bit_cast(double, b); }
 
 // Plan key of a value: its sign and biased exponent (the top 12 bits).  A key
-// names a binade with a fast path only when the value is normal and finite.
-EXSEQ_HD uint32_t key_of(double v) { return (uint32_t)(dbits(v) >> 52); }
+// names a binade with a fast path only when the value is finite and not -0.
+//
+// The subnormal range: below 2^-1022 every double is a multiple of 2^-1074,
+// the unit of the lowest normal binade [2^-1022, 2^-1021) too.  So the two
+// form one range [0, 2^-1021) with one unit, where a sum is an integer count
+// in [0, 2^53) rounded to the nearest count (ties to even) exactly as in a
+// binade.  Subnormals and +0 take the key of that lowest binade (biased
+// exponent 1), and their count has no implicit bit; -0 keeps its own key
+// (no fast path), since adding +0 to it gives +0 and a count cannot say so.
+// Runs keep their usual lower bound (every prefix count at least 2^52 + 1
+// where a term is negative), so a run is applied below 2^-1022 only when it
+// rises (Research-1433 "Forming the CPU's sequential double sums on a GPU,
+// bit for bit" is silent on this range; this reading is the build's).
+EXSEQ_HD uint32_t key_of(double v)
+{
+    const uint64_t b = dbits(v);
+    const uint32_t k = (uint32_t)(b >> 52);
+    return ((k & 0x7FFu) == 0u && b != 0x8000000000000000ULL) ? k | 1u : k;
+}
 EXSEQ_HD bool key_has_fast_path(uint32_t key)
 {
     uint32_t e = key & 0x7FFu;
     return e != 0u && e != 0x7FFu;
 }
 
-// Count of a normal S in its own binade: the 52 fraction bits plus the
-// implicit bit, m in [2^52, 2^53).
-EXSEQ_HD int64_t count_of(double s) { return (int64_t)((dbits(s) & kFracMask) | (1ULL << 52)); }
+// Count of S in its binade: the 52 fraction bits plus the implicit bit, m in
+// [2^52, 2^53) for a normal S; the fraction bits alone, m in [0, 2^52), for a
+// subnormal S or +0 (in the lowest binade's range, see key_of).
+EXSEQ_HD int64_t count_of(double s)
+{
+    const uint64_t b = dbits(s);
+    return (int64_t)((b & kFracMask) | ((b & 0x7FF0000000000000ULL) ? (1ULL << 52) : 0ULL));
+}
+
+// The lowest count a binade's range holds: 0 for the lowest binade (which
+// takes in the subnormals), 2^52 for the others.
+EXSEQ_HD int64_t count_floor(uint32_t key) { return (key & 0x7FFu) == 1u ? 0 : kCountLo; }
 
 // S = sign * count * 2^(E - 1075) for count in [2^52, 2^53]; a count of 2^53
 // carries into the exponent (2^(e+1)), and past the largest binade it gives

@@ -313,7 +313,7 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
         if (key_has_fast_path(kk) && kk == key_of(pk)) {
             const int64_t m = count_of(pk);
             const int64_t mg = plan_margin(c0 + t + 1);
-            bool near = m < kCountLo + mg;
+            bool near = m < count_floor(kk) + mg;
             if (r.flags & kFlagNeg)
                 near |= m + r.lo - mg < kCountLo + 1 || m + r.hi + mg > kCountHi - 1;
             else

@@ -120,7 +120,7 @@ struct Rules {
     double advance(double S, int64_t m, Pair p) const
     {
         int64_t c = m + pair_at(p, m);
-        c = std::min(std::max(c, kCountLo), kCountHi);
+        c = std::min(std::max(c, count_floor(key_of(S))), kCountHi);
         return assemble(key_of(S), c);
     }
 };
@@ -634,7 +634,7 @@ struct Twin {
                 if (key_has_fast_path(key[c]) && key[c] == key_of(pk[c])) {
                     const int64_t m = count_of(pk[c]);
                     const int64_t mg = plan_margin(c0 + c + 1);
-                    bool near = m < kCountLo + mg;
+                    bool near = m < count_floor(key[c]) + mg;
                     if (join[c].flags & kFlagNeg)
                         near |= m + join[c].lo - mg < kCountLo + 1 || m + join[c].hi + mg > kCountHi - 1;
                     else

@@ -148,12 +148,16 @@ def lcs_records(windows: int = FRAME_N, seed: int = 0) -> np.ndarray:
 # * ``neg_rise`` -- a negative term in the first 256 terms, a rise over the
 #   last 256 that passes 2^(e+1) at the chunk's end (the chunk among a sum's
 #   first four, or after them).
+# * ``subnormal`` -- a sum from +0, -0 or a subnormal that grows through
+#   the subnormals (terms of up to 2^24 units of 2^-1074, a few of them
+#   negative) into the lowest normal binades.
 # * ``mixed`` -- signed terms spanning a few binades.
 #
 # A sum's first chunks are zeros or not (the adversarial chunk in a sum's
 # first four chunks, or in the tiles after them); regular chunks may follow.
 # ---------------------------------------------------------------------------
-TWIN_FAMILIES = ("rise_fall", "edge_counts", "ties", "falling", "neg_cross", "neg_rise", "mixed")
+TWIN_FAMILIES = ("rise_fall", "edge_counts", "ties", "falling", "neg_cross", "neg_rise", "subnormal",
+                 "mixed")
 
 
 def twin_case(seed: int, family: str):
@@ -216,6 +220,11 @@ def twin_case(seed: int, family: str):
         m0 = 2.0 ** 53 - np.floor(float(x[:768].sum()) + g.uniform(0.0, float(x[768:].sum())))
         init = m0 * u
         parts.append(x * u)
+    elif family == "subnormal":
+        init = float(g.choice([0.0, -0.0, float(g.integers(1, 2 ** 30)) * 2.0 ** -1074]))
+        k = g.integers(0, 2 ** int(g.integers(4, 25)), 2 * C).astype(np.float64)
+        k[g.random(2 * C) < 0.02] *= -1.0
+        parts = [np.zeros(lead * C), k * 2.0 ** -1074]
     else:  # mixed
         init = float(g.uniform(-4.0, 4.0)) * 2.0 ** e
         x = g.normal(0.0, 1.0, 2 * C) * 2.0 ** (e + g.integers(-12, 2, 2 * C).astype(np.float64))

@@ -3,9 +3,10 @@ size for the fused SSIM frame and the pyramid batch, every term of a full
 frame, the device divide on a million operand pairs, the non-finite flag,
 determinism over a thousand calls per launch plan, and the exhaustive
 tie-alphabet sequences placed where the tiles' lane and wave composition
-adds them (Research-1433 "Forming the CPU's sequential double sums on a
-GPU, bit for bit", Findings 5 and "Tests"; Research-1424 "integer_ssim_cuda
-and the CPU's frame sum", Findings 1)."""
+adds them, and sums that grow through the subnormal range (Research-1433
+"Forming the CPU's sequential double sums on a GPU, bit for bit", Findings 5
+and "Tests"; Research-1424 "integer_ssim_cuda and the CPU's frame sum",
+Findings 1)."""
 
 import math
 
@@ -17,6 +18,15 @@ import seeded_inputs as si
 import bit_exact_sequential_amd as ex
 from tests import suites
 from tests.gpu_util import same, say, to_dev, torch_cuda
+
+
+def gpu_sum(torch, x, init=0.0, flags=0, stats=False):
+    r = ex.exact_seq_sum(to_dev(torch, x), init, flags=flags, stats=stats)
+    if stats:
+        out, st = r
+        return float(out.cpu()[0]), st
+    return float(r.cpu()[0])
+
 
 pytestmark = pytest.mark.gpu
 
@@ -136,3 +146,24 @@ def test_exhaustive_sequences_through_tiles(offset):
             got = ex.exact_seq_sum_batch([to_dev(torch, a) for a in xs], inits, flags=path).cpu().tolist()
             for j, (a, init) in enumerate(zip(xs, inits)):
                 assert same(got[j], oracle.seq_sum(a, init)), (offset, path, k + j)
+
+
+@pytest.mark.parametrize("init", [0.0, -0.0, 3 * 2.0 ** -1074], ids=["zero", "minus_zero", "subnormal"])
+def test_subnormal_range_runs(init):
+    """Sums that start at zero or a subnormal and grow through the subnormals
+    into the normal binades: exact under every launch plan and tile size, and
+    the fast paths take them (the subnormal range is one count range with the
+    lowest binade's unit)."""
+    torch = torch_cuda()
+    g = np.random.Generator(np.random.PCG64(91))
+    n = 600_001
+    rising = g.integers(0, 2 ** 30, n).astype(np.float64) * 2.0 ** -1074
+    mixed = rising.copy()
+    mixed[g.random(n) < 0.01] *= -1.0
+    for name, x in (("rising", rising), ("some negative", mixed)):
+        want = oracle.seq_sum(x, init)
+        for fl in (0, ex.PASS_PATH, ex.tile_flag(1), ex.tile_flag(2), ex.tile_flag(4), ex.WALK_ONLY):
+            got, st = gpu_sum(torch, x, init, fl, stats=True)
+            assert same(got, want), (name, fl, got, want)
+            if name == "rising" and fl != ex.WALK_ONLY:
+                assert st["fast_chunks"] >= 0.9 * st["chunks"], (fl, st)
