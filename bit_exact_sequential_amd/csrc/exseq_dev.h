@@ -377,44 +377,57 @@ __device__ __forceinline__ WaveRun wave_run(const Four &f, uint32_t key)
 }
 
 // The runs of CPB chunks at once (one wave's part of each, as wave_run).
-// Where no term of the wave ties and every scaled term is in [0, 2^51) --
-// nearly always -- the CPB order-free integer sums are taken together so
-// that their reduction chains overlap; otherwise chunk by chunk.  Missing
-// terms are +0.0 (the sources pad with it), which changes no run.
+// Where no term of the wave ties and every increment of a chunk's part has
+// one sign -- nearly always -- the CPB order-free integer sums are taken
+// together so that their reduction chains overlap; otherwise chunk by chunk.
+// Missing terms are +0.0 (the sources pad with it), which changes no run.
+//
+// Per term: y = x * (+-2^scale) (one multiply while the factor is a normal
+// double, i.e. for sums from 2^-971 up; ldexp and a sign flip below), the
+// two magic adds, and three bit operations on the results: a0 = M0 + y lies
+// in [2^52, 2^53) exactly when y rounds to an integer there (high word
+// 0x433xxxxx: checked through the AND and the OR of the high words), its
+// mantissa bit 51 says whether the increment is >= 0, and a tie shows as a
+// difference other than one between the low words of a1 = M0 + 1 + y and a0.
 template <int CPB>
 __device__ __forceinline__ void wave_runs(const Four *f, const uint32_t *key,
                                           WaveRun (*lds)[kChunkThreads / 64])
 {
     uint64_t v[CPB];
     bool easy = true;
-    uint32_t negs = 0u;  // chunk k's increments are all <= 0 (bit k)
+    uint32_t negs = 0u;  // chunk k's increments are all < 0 (bit k)
 #pragma unroll
     for (int k = 0; k < CPB; k++) {
         const int scale = 1075 - (int)(key[k] & 0x7FFu);
-        const uint32_t flip = (key[k] & 0x800u) ? 0x80000000u : 0u;  // mirror a negative plan
-        bool tie = false, notpos = false, notneg = false;
+        const bool flip = (key[k] & 0x800u) != 0u;  // mirror a negative plan
+        uint32_t tacc = 0u, hand = ~0u, hor = 0u;
         uint64_t sum = 0;
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            double y = ldexp(f[k].v[i], scale);
-            y = bitsd(dbits(y) ^ ((uint64_t)flip << 32));
+        auto term = [&](double y) {
             const double a0 = kMagic0 + y;
             const double a1 = kMagic1 + y;
-            // 0 <= y < 2^51 as one unsigned compare of the bit patterns
-            // (a negative y, -0.0 and NaN have larger patterns), and the
-            // same for -y
-            notpos |= dbits(y) >= (uint64_t)dbits(kHugeY);
-            notneg |= dbits(-y) >= (uint64_t)dbits(kHugeY);
-            // a tie: the two starts round to counts that differ by other
-            // than one (both sums lie in [2^52, 2^53), so the low words do)
-            tie |= (uint32_t)dbits(a1) - (uint32_t)dbits(a0) != 1u;
+            const uint32_t h = (uint32_t)(dbits(a0) >> 32);
+            tacc |= ((uint32_t)dbits(a1) - (uint32_t)dbits(a0)) ^ 1u;
+            hand &= h;
+            hor |= h;
             sum += dbits(a0);
+        };
+        if (scale <= 1023) {
+            const double fac = flip ? -ldexp(1.0, scale) : ldexp(1.0, scale);
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                term(f[k].v[i] * fac);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const double y = ldexp(f[k].v[i], scale);
+                term(flip ? -y : y);
+            }
         }
         v[k] = sum - 4 * (uint64_t)kMagic0Bits;
-        // tie-free, and every increment of one sign: a monotone run, whose
-        // prefixes lie between 0 and its total (no scan for the bounds)
-        const bool pos = __ballot(notpos) == 0, neg = __ballot(notneg) == 0;
-        easy &= __ballot(tie) == 0 && (pos || neg);
+        const bool ok = tacc == 0u && (((hand ^ kMagic0Hi) | (hor ^ kMagic0Hi)) >> 20) == 0u;
+        const bool pos = __ballot(!((hand >> 19) & 1u)) == 0;  // every a0 >= M0
+        const bool neg = __ballot((hor >> 19) & 1u) == 0;      // every a0 < M0
+        easy &= __ballot(!ok) == 0 && (pos || neg);
         negs |= (!pos && neg) ? 1u << k : 0u;
     }
     if (easy) {

@@ -14,7 +14,7 @@
 //    further chunk by its run under the exact sum's binade where that run
 //    applies, else term by term, and publishes the exact sum after the tile.
 //  * the finisher: it takes the head's exact sum and then follows the tiles'
-//    records in order, a window of 256 tiles at a time as they appear: the
+//    records in order, a window of 1024 tiles at a time as they appear: the
 //    regular tiles between irregular ones are composed with one segmented
 //    scan (Research-1433 Open questions: compose runs that share a binade so
 //    that the walk steps over many chunks at once), and the segments and the
@@ -45,7 +45,7 @@
 //        crossing term, and the run after it in the next binade.  Nothing
 //        waits for an exact sum.
 //
-// Cross-workgroup words carry a tag of the launch (45 bits, never zero and
+// Cross-workgroup words carry a tag of the launch (42 bits, never zero and
 // never reused within a process), so no word needs clearing between launches
 // and stale words never match.  Plan words are self-contained.  Every word
 // another workgroup reads is written and read with device-coherent
@@ -142,8 +142,8 @@ struct PassWs {
     uint64_t *st;    // per tile: plan status word
     uint64_t *gst;   // per group: plan status word
     DescArrays d;    // per chunk: descriptor
-    uint64_t *trec;  // per tile: 4 words (w0, r0 with tag bits, lo, hi; lo and hi
-                     // only for a run with a negative term)
+    uint64_t *trec;  // per tile: 4 words (w0, then r0, lo, hi each with tag bits;
+                     // lo and hi only for a run with a negative term)
     uint64_t *xrec;  // per tile: kStepWords words (an irregular tile's step)
     uint64_t *hrec;  // per sum: 2 words (w0, exact sum after the first tile)
 };
@@ -163,7 +163,7 @@ struct PassArgs {
 // ---------------------------------------------------------------------------
 struct PassTileLds {
     double wsum[kTileCh][kWaves];
-    WaveRun wrun[kHalf][kWaves];
+    WaveRun wrun[kTileCh][kWaves];
     WaveRun join[kTileCh];
     double pk[kTileCh];
     uint32_t key[kTileCh];
@@ -172,6 +172,8 @@ struct PassTileLds {
     uint64_t xw[kTileCh][kCrossWords];
     uint64_t rec[kStepWords];
     uint64_t xexit[4];  // an irregular tile's last run: key etc., r0, lo, hi
+    uint32_t xmask;     // chunks whose crossing is to be located
+    uint32_t regular;   // the tile is regular
     double lb1, lb2;
     int lb_found, lb_ok1, lb_ok2;
     volatile int lb_stop;
@@ -938,10 +940,22 @@ __device__ __forceinline__ void finisher_block(const PassArgs &pa, const Src &sr
                 rr[j].p = Pair{r0, r0 + (int64_t)((w0[j] >> kDrShift) & 3u) - 1};
                 rr[j].flags = (uint32_t)w0[j] & (kFlagNeg | kFlagBad);
                 if (rr[j].flags & kFlagNeg) {
-                    // a run with a negative term: its prefix bounds
-                    const uint64_t *r = w.trec + 4 * (g0 + j);
-                    rr[j].lo = dec_i64(load_relaxed_u64(r + 2));
-                    rr[j].hi = dec_i64(load_relaxed_u64(r + 3));
+                    // a run with a negative term: its prefix bounds (tagged
+                    // words, written beside the first two)
+                    v2u64 b{0, 0};
+                    for (int spin = 0; spin <= kSpinLimit; spin++) {
+                        b = load_coherent_16(w.trec + 4 * (g0 + j) + 2);
+                        if (rec_w1_ok(tag, b.x) && rec_w1_ok(tag, b.y))
+                            break;
+                        __builtin_amdgcn_s_sleep(2);
+                    }
+                    if (rec_w1_ok(tag, b.x) && rec_w1_ok(tag, b.y)) {
+                        rr[j].lo = rec_w1_r0(b.x);
+                        rr[j].hi = rec_w1_r0(b.y);
+                    } else {
+                        // never arrived: a run that applies nowhere
+                        rr[j].flags |= kFlagBad;
+                    }
                 } else {
                     // rising along either start parity: the largest prefix is
                     // the total
@@ -1238,6 +1252,57 @@ __device__ __forceinline__ void finisher_block(const PassArgs &pa, const Src &sr
 // ---------------------------------------------------------------------------
 // A tile after a sum's first: eight chunks
 // ---------------------------------------------------------------------------
+// One wave's part of a chunk's run under `key`; a key with no fast path
+// (a non-finite plan, or the binade of the largest doubles) gives only the
+// non-finite flag, and the chunk is walked term by term.
+__device__ __forceinline__ WaveRun chunk_part(const Four &q, uint32_t key)
+{
+    if (key_has_fast_path(key))
+        return wave_run(q, key);
+    bool nf = false;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        nf |= is_nonfinite(q.v[i]);
+    WaveRun wr;
+    wr.p = pair_identity();
+    wr.lo = wr.hi = 0;
+    wr.flags = __ballot(nf) ? kFlagNonFinite : 0u;
+    return wr;
+}
+
+// The wave parts of N chunks' runs into wr[k][wave].
+template <int N>
+__device__ __forceinline__ void chunk_runs(const Four *q, const uint32_t *key, WaveRun (*wr)[kWaves])
+{
+    bool allfast = true;
+#pragma unroll
+    for (int k = 0; k < N; k++)
+        allfast &= key_has_fast_path(key[k]);
+    if (allfast) {
+        wave_runs<N>(q, key, wr);
+        return;
+    }
+#pragma unroll
+    for (int k = 0; k < N; k++) {
+        const WaveRun x = chunk_part(q[k], key[k]);
+        if (lane_id() == 0)
+            wr[k][wave_id()] = x;
+    }
+}
+
+// The runs of the four chunks staged in LDS, two at a time (the registers
+// still hold the first four chunks).
+__device__ __forceinline__ void staged_runs(double *stage, size_t n, uint32_t c_first, const uint32_t *key,
+                                            WaveRun (*wr)[kWaves])
+{
+#pragma unroll 1
+    for (int j = 0; j < kHalf; j += 2) {
+        const Four q[2] = {staged_chunk(stage, j, n, c_first + j), staged_chunk(stage, j + 1, n, c_first + j + 1)};
+        const uint32_t kq[2] = {j ? key[2] : key[0], j ? key[3] : key[1]};
+        chunk_runs<2>(q, kq, wr + j);
+    }
+}
+
 template <class Src>
 __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, const PassWs &w,
                                            int s, uint32_t i, PassTileLds &L, WalkCore &sc,
@@ -1311,15 +1376,36 @@ __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, c
         Ttile += T[k];
     }
 
-    // ---- the plan
+    // ---- the plan, and the runs formed while it is looked up
     uint64_t *st0 = w.st + pa.tile_base[s];
     uint64_t *gs0 = w.gst + pa.group_base[s];
     const uint32_t lg = i / kGroup, pg = i % kGroup;
+    const bool lookback = mode != EXSEQ_PLAN_FIXED;
+    if (lookback && t == 0)
+        store_relaxed_u64(st0 + i, st_pack(a.epoch, kStAgg, Ttile));
+    // A guess of every chunk's planned binade, from the prefix before the
+    // tile taken as its first chunk's index times the tile's mean chunk sum:
+    // the runs are formed under it while the look-back waits for the tiles
+    // before (the plan decides speed only; a chunk whose guess differs from
+    // its planned binade is formed again).  A group's last tile publishes
+    // the group's sum from its look-back, so it looks back first.
+    const bool spec = lookback && pg != kGroup - 1;
+    uint32_t gkey[kTileCh];
+    if (spec) {
+        const double mean = Ttile / (double)nk;
+        double pk = a.init[s] + (double)c0 * mean;
+#pragma unroll
+        for (int k = 0; k < kTileCh; k++) {
+            gkey[k] = (uint32_t)__builtin_amdgcn_readfirstlane((int)plan_key(pk, a.flags));
+            pk += T[k];
+        }
+        chunk_runs<kHalf>(f, gkey, L.wrun);
+        if (nk > kHalf)
+            staged_runs(stage, n, c0 + kHalf, gkey + kHalf, L.wrun + kHalf);
+    }
     double P = a.init[s];
-    if (mode != EXSEQ_PLAN_FIXED) {
+    if (lookback) {
         if (wave == 0) {
-            if (lane == 0)
-                store_relaxed_u64(st0 + i, st_pack(a.epoch, kStAgg, Ttile));
             double v1;
             bool ok1;
             const bool found = lb_level1(st0 + kGroup * lg, (int)pg, a.epoch, v1, ok1);
@@ -1354,13 +1440,17 @@ __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, c
         }
     }
     if (wave == 0 && lane < kTileCh) {
-        double pk = P, tk = T[0];
+        // the chunk sums again from LDS (the same tree: the same values), so
+        // that they need no registers through the runs and the look-back
+        auto tsum = [&](int k) { return (L.wsum[k][0] + L.wsum[k][1]) + (L.wsum[k][2] + L.wsum[k][3]); };
+        double pk = P, tk = tsum(0);
 #pragma unroll
         for (int k = 0; k < kTileCh - 1; k++) {
+            const double tn = tsum(k + 1);
             if (k < lane)
-                pk += T[k];
+                pk += tsum(k);
             if (k + 1 == lane)
-                tk = T[k + 1];
+                tk = tn;
         }
         L.pk[lane] = pk;
         L.key[lane] = plan_key(pk, a.flags);
@@ -1370,116 +1460,122 @@ __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, c
     }
     __syncthreads();
 
-    // ---- every chunk's run under its planned binade, half a tile at a time,
-    // and the crossings of the chunks planned to cross
-    uint32_t found = 0u;
-    int buf = 0;
-#pragma unroll 1
-    for (int h = 0; h < 2; h++) {
-        const int kb = h * kHalf;
-        if (kb >= nk)
-            break;
-        if (h == 1) {
+    bool miss_any = false;
+    // ---- the runs not formed under the guess: every chunk without one, else
+    // the chunks whose guess missed.  The registers' four chunks are dead
+    // after their runs; a chunk of theirs needed again (a missed guess, a
+    // crossing to locate) is read again from memory.
+    if (!spec) {
+        uint32_t key[kHalf];
+#pragma unroll
+        for (int k = 0; k < kHalf; k++)
+            key[k] = L.key[k];
+        chunk_runs<kHalf>(f, key, L.wrun);
+        if (nk > kHalf) {
 #pragma unroll
             for (int k = 0; k < kHalf; k++)
-                f[k] = staged_chunk(stage, k, n, c0 + kHalf + k);
+                key[k] = L.key[kHalf + k];
+            staged_runs(stage, n, c0 + kHalf, key, L.wrun + kHalf);
         }
-        uint32_t key[kHalf];
-        bool allfast = true;
+    } else {
+        uint32_t miss = 0u;
 #pragma unroll
-        for (int k = 0; k < kHalf; k++) {
-            key[k] = L.key[kb + k];
-            allfast &= key_has_fast_path(key[k]);
-        }
-        if (allfast) {
-            wave_runs<kHalf>(f, key, L.wrun);
-        } else {
-#pragma unroll
-            for (int k = 0; k < kHalf; k++) {
-                WaveRun wr;
-                if (key_has_fast_path(key[k])) {
-                    wr = wave_run(f[k], key[k]);
-                } else {
-                    bool nf = false;
-#pragma unroll
-                    for (int q = 0; q < 4; q++)
-                        nf |= is_nonfinite(f[k].v[q]);
-                    wr.p = pair_identity();
-                    wr.lo = wr.hi = 0;
-                    wr.flags = __ballot(nf) ? kFlagNonFinite : 0u;
-                }
-                if (lane == 0)
-                    L.wrun[k][wave] = wr;
-            }
-        }
-        __syncthreads();
-        if (t < kHalf) {
-            const int c = kb + t;
-            const uint32_t kk = L.key[c];
-            const double pk = L.pk[c];
-            bool cc = L.cross[c] != 0;
-            bool plain = true, fall = true;
-            int64_t sum = 0;
-#pragma unroll
-            for (int wv = 0; wv < kWaves; wv++) {
-                const WaveRun &q = L.wrun[t][wv];
-                plain &= rising_run(q.p, q.flags);
-                fall &= falling_run(q.p, q.lo, q.hi, q.flags);
-                sum += q.p.r0;
-            }
-            const WaveRun r = clamp_run(plain  ? WaveRun{Pair{sum, sum}, 0, sum, 0u}
-                                        : fall ? WaveRun{Pair{sum, sum}, sum, 0, kFlagNeg}
-                                               : join_waves(L.wrun[t]));
-            if (key_has_fast_path(kk) && kk == key_of(pk)) {
-                const int64_t m = count_of(pk);
-                const int64_t mg = plan_margin(c0 + c + 1);
-                bool near = m < count_floor(kk) + mg;
-                if (r.flags & kFlagNeg)
-                    near |= m + r.lo - mg < kCountLo + 1 || m + r.hi + mg > kCountHi - 1;
-                else
-                    near |= m + r.hi + mg > kCountHi;
-                cc |= near;
-            }
-            L.join[c] = r;
-            L.cross[c] = cc;
-            if (c < nk)
-                store_desc_coherent(w.d, gc0 + (size_t)c, kk, r, cc ? kFlagCross : 0u);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < kHalf; k++) {
-            const int c = kb + k;
-            const uint32_t fl = L.join[c].flags;
-            if (!(c < nk && L.cross[c] && key_has_fast_path(L.key[c]) && L.key[c] == key_of(L.pk[c]) &&
-                  key_has_fast_path(L.down[c] ? L.key[c] - 1u : L.key[c] + 1u) &&
-                  !(fl & kFlagNonFinite)))
+        for (int k = 0; k < kTileCh; k++)
+            miss |= (k < nk && L.key[k] != gkey[k]) ? 1u << k : 0u;
+        miss = (uint32_t)__builtin_amdgcn_readfirstlane((int)miss);
+        miss_any = miss != 0u;
+#pragma unroll 1
+        for (int c = 0; c < nk; c++) {
+            if (!((miss >> c) & 1u))
                 continue;
-            uint64_t xw[kCrossWords];
-            if (crossing_find(f[k], chunk_len(n, c0 + c), L.key[c], count_of(L.pk[c]),
-                              L.down[c] != 0u, sc, xl, buf, xw)) {
-                found |= 1u << c;
-                if (t == 0) {
+            const Four q = c < kHalf ? src.chunk_v(v, c0 + c, lds_src) : staged_chunk(stage, c - kHalf, n, c0 + c);
+            const WaveRun wr = chunk_part(q, L.key[c]);
+            if (lane == 0)
+                L.wrun[c][wave] = wr;
+        }
+    }
+    // (the guessed runs were written before the look-back's barrier)
+    if (!spec || miss_any)
+        __syncthreads();
+    // ---- each chunk's four parts joined (a lane per chunk), the binade
+    // edges checked, the descriptor stored
+    if (t < nk) {
+        const int c = t;
+        const uint32_t kk = L.key[c];
+        const double pk = L.pk[c];
+        bool cc = L.cross[c] != 0;
+        bool plain = true, fall = true;
+        int64_t sum = 0;
 #pragma unroll
-                    for (int q = 0; q < kCrossWords; q++)
-                        L.xw[c][q] = xw[q];
-                }
+        for (int wv = 0; wv < kWaves; wv++) {
+            const WaveRun &q = L.wrun[c][wv];
+            plain &= rising_run(q.p, q.flags);
+            fall &= falling_run(q.p, q.lo, q.hi, q.flags);
+            sum += q.p.r0;
+        }
+        const WaveRun r = clamp_run(plain  ? WaveRun{Pair{sum, sum}, 0, sum, 0u}
+                                    : fall ? WaveRun{Pair{sum, sum}, sum, 0, kFlagNeg}
+                                           : join_waves(L.wrun[c]));
+        if (key_has_fast_path(kk) && kk == key_of(pk)) {
+            const int64_t m = count_of(pk);
+            const int64_t mg = plan_margin(c0 + c + 1);
+            bool near = m < count_floor(kk) + mg;
+            if (r.flags & kFlagNeg)
+                near |= m + r.lo - mg < kCountLo + 1 || m + r.hi + mg > kCountHi - 1;
+            else
+                near |= m + r.hi + mg > kCountHi;
+            cc |= near;
+        }
+        L.join[c] = r;
+        L.cross[c] = cc;
+        store_desc_coherent(w.d, gc0 + (size_t)c, kk, r, cc ? kFlagCross : 0u);
+        // a crossing to locate; a chunk of a regular tile
+        const bool dn = L.down[c] != 0u;
+        const bool locate = cc && key_has_fast_path(kk) && kk == key_of(pk) &&
+                            key_has_fast_path(dn ? kk - 1u : kk + 1u) && !(r.flags & kFlagNonFinite);
+        const bool reg = key_has_fast_path(kk) && kk == L.key[0] && !cc &&
+                         !(r.flags & (kFlagBad | kFlagNonFinite));
+        const uint64_t xm = __ballot(locate), rm = __ballot(reg);
+        if (t == 0) {
+            L.xmask = (uint32_t)xm;
+            L.regular = rm == (1ull << nk) - 1u;
+        }
+    }
+    __syncthreads();
+    // ---- the crossing of every chunk planned to cross
+    uint32_t found = 0u;
+    int buf = 0;
+    const uint32_t xmask = (uint32_t)__builtin_amdgcn_readfirstlane((int)L.xmask);
+#pragma unroll 1
+    for (int c = 0; c < nk; c++) {
+        if (!((xmask >> c) & 1u))
+            continue;
+        const Four q = c < kHalf ? src.chunk_v(v, c0 + c, lds_src) : staged_chunk(stage, c - kHalf, n, c0 + c);
+        uint64_t xw[kCrossWords];
+        if (crossing_find(q, chunk_len(n, c0 + c), L.key[c], count_of(L.pk[c]), L.down[c] != 0u, sc, xl,
+                          buf, xw)) {
+            found |= 1u << c;
+            if (t == 0) {
+#pragma unroll
+                for (int q2 = 0; q2 < kCrossWords; q2++)
+                    L.xw[c][q2] = xw[q2];
             }
         }
-        __syncthreads();
     }
+    __syncthreads();
 
     // ---- the tile's record
-    bool regular = true;
-#pragma unroll
-    for (int k = 0; k < kTileCh; k++)
-        if (k < nk)
-            regular &= key_has_fast_path(L.key[k]) && L.key[k] == L.key[0] && !L.cross[k] &&
-                       !(L.join[k].flags & (kFlagBad | kFlagNonFinite));
+    const bool regular = L.regular != 0;
     uint64_t *trec = w.trec + 4 * (size_t)g;
     if (regular) {
-        // the chunks' runs in order (plain ones add up), by lane 0
-        Run tr = run_identity();
+        // The chunks' runs in order (plain ones add up), by lane 0.  Its
+        // wave stored every descriptor of the tile: once they are complete,
+        // the record's words go out together (each carries the launch tag).
+        if (wave != 0)
+            return;
+        stores_complete();
         if (t == 0) {
+            Run tr = run_identity();
             bool plain = true, fall = true;
             int64_t sum = 0;
             for (int k = 0; k < nk; k++) {
@@ -1510,15 +1606,11 @@ __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, c
             }
             store_relaxed_u64(trec + 1, rec_w1(tag, tr.p.r0));
             if (tr.flags & kFlagNeg) {
-                store_relaxed_u64(trec + 2, enc_i64(tr.lo));
-                store_relaxed_u64(trec + 3, enc_i64(tr.hi));
+                store_relaxed_u64(trec + 2, rec_w1(tag, tr.lo));
+                store_relaxed_u64(trec + 3, rec_w1(tag, tr.hi));
             }
-        }
-        // the run's words and every lane's descriptor stores before the tag
-        stores_complete();
-        __syncthreads();
-        if (t == 0)
             store_relaxed_u64(trec, rec_w0(tag, kKindReg, tr.flags, tr.p.r1 - tr.p.r0, L.key[0]));
+        }
         return;
     }
     // An irregular tile: its O(1) step -- the chunks before the first located
@@ -1599,8 +1691,8 @@ __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, c
             L.xexit[0] = (uint64_t)(nx > 0 ? next_key : akey) | ((uint64_t)neg << 14) |
                          ((uint64_t)(ex.p.r1 - ex.p.r0 + 1) << 32);
             L.xexit[1] = rec_w1(tag, ex.p.r0);
-            L.xexit[2] = enc_i64(ex.lo);
-            L.xexit[3] = enc_i64(ex.hi);
+            L.xexit[2] = rec_w1(tag, ex.lo);
+            L.xexit[3] = rec_w1(tag, ex.hi);
         }
         L.rec[0] = (uint64_t)(akey & kKeyMask) | ((uint64_t)(akey != 0u) << 12) |
                    ((uint64_t)nx << 13) | ((uint64_t)((A.flags >> 14) & 3u) << 15) |
@@ -1668,7 +1760,7 @@ __global__ __launch_bounds__(kChunkThreads, 4) void pass_kernel(PassArgs pa, Src
 // ---------------------------------------------------------------------------
 namespace {
 
-// Launch tags: 45 bits, never zero, never repeated within a process; the
+// Launch tags: 42 bits, never zero, never repeated within a process; the
 // start is drawn from the clock and the process so that words a previous
 // process left in reused memory are unlikely to match.
 std::atomic<uint64_t> g_tag{0};

@@ -45,6 +45,7 @@ constexpr double kMagic0 = 6755399441055744.0;          // 1.5 * 2^52, even
 constexpr double kMagic1 = 6755399441055745.0;          // 1.5 * 2^52 + 1, odd
 constexpr int64_t kMagic0Bits = 0x4338000000000000LL;
 constexpr int64_t kMagic1Bits = 0x4338000000000001LL;
+constexpr uint32_t kMagic0Hi = 0x43380000u;              // high word of M0: exponent field 0x433
 constexpr double kHugeY = 2251799813685248.0;           // 2^51
 constexpr int64_t kCountLo = 1LL << 52;                 // counts of one binade
 constexpr int64_t kCountHi = 1LL << 53;

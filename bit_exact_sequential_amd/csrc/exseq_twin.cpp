@@ -238,7 +238,8 @@ WaveRun twin_wave_run(const Rules &R, const Chunk &c, int wave, uint32_t key)
 }
 
 // wave_runs<4>: the four chunks of a half tile, per wave; the shortcut where
-// the wave has no tie in any of them and each is of one sign
+// the wave has no tie in any of them and the increments of each are all >= 0
+// or all < 0, with the kernel's tests on the magic sums' bit patterns
 void twin_wave_runs(const Rules &R, const Chunk *const *c, const uint32_t *key, WaveRun out[4][4])
 {
     for (int wave = 0; wave < 4; wave++) {
@@ -247,25 +248,37 @@ void twin_wave_runs(const Rules &R, const Chunk *const *c, const uint32_t *key, 
         int64_t v[4];
         for (int k = 0; k < 4; k++) {
             const int scale = 1075 - (int)(key[k] & 0x7FFu);
-            const uint64_t flip = (key[k] & 0x800u) ? 0x8000000000000000ull : 0ull;
-            bool tie = false, notpos = false, notneg = false;
+            const bool flip = (key[k] & 0x800u) != 0u;
+            const double fac = flip ? -std::ldexp(1.0, scale) : std::ldexp(1.0, scale);
+            bool bad = false, notpos = false, notneg = false;
             uint64_t sum = 0;
             for (int l = 0; l < kWaveLanes; l++) {
                 const int lane = kWaveLanes * wave + l;
+                uint32_t tacc = 0u, hand = ~0u, hor = 0u;
                 uint64_t lsum = 0;
                 for (int i = 0; i < 4; i++) {
                     const double x = c[k]->v[kPerLane * lane + i];  // +0.0 past the end
-                    const double y = bitsd(dbits(std::ldexp(x, scale)) ^ flip);
+                    double y;
+                    if (scale <= 1023) {
+                        y = x * fac;
+                    } else {
+                        y = std::ldexp(x, scale);
+                        y = flip ? -y : y;
+                    }
                     const double a0 = kMagic0 + y, a1 = kMagic1 + y;
-                    notpos |= dbits(y) >= dbits(kHugeY);
-                    notneg |= dbits(-y) >= dbits(kHugeY);
-                    tie |= (uint32_t)dbits(a1) - (uint32_t)dbits(a0) != 1u;
+                    const uint32_t h = (uint32_t)(dbits(a0) >> 32);
+                    tacc |= ((uint32_t)dbits(a1) - (uint32_t)dbits(a0)) ^ 1u;
+                    hand &= h;
+                    hor |= h;
                     lsum += dbits(a0);
                 }
                 sum += lsum - 4 * (uint64_t)kMagic0Bits;
+                bad |= tacc != 0u || (((hand ^ kMagic0Hi) | (hor ^ kMagic0Hi)) >> 20) != 0u;
+                notpos |= !((hand >> 19) & 1u);
+                notneg |= (hor >> 19) & 1u;
             }
             v[k] = (int64_t)sum;
-            easy &= !tie && (!notpos || !notneg);
+            easy &= !bad && (!notpos || !notneg);
             negs |= (notpos && !notneg) ? 1u << k : 0u;
         }
         // (a tie that the mutation rounds up is no tie: the shortcut then
