@@ -148,8 +148,54 @@ int exact_seq_sum_f64_profiled(const double *x, size_t n, double init, double *o
                             stats, events, n_events);
 }
 
-// Sums go to the kernels in groups of kMaxBatch; the groups run one after
-// the other on the stream and reuse one workspace region.
+// Sums go to the kernels in groups: up to kPassMax sums in one launch of
+// the single pass (the default for several sums), else groups of kMaxBatch
+// through the tile chain.  The groups run one after the other on the stream
+// and reuse one workspace region, sized for either grouping.
+namespace {
+
+bool batch_takes_pass(size_t count, uint32_t flags)
+{
+    return exseq::pass_flags_ok(flags) && (count > 1 || (flags & EXSEQ_PASS_PATH));
+}
+
+// A group of sums of at most a few chunks, with default flags: the walk
+// alone adds them in order (one launch).
+bool group_is_tiny(const size_t *ns, size_t count, uint32_t flags)
+{
+    size_t chunks = 0;
+    for (size_t k = 0; k < count; k++)
+        chunks += padded_chunks(ns[k]);
+    return chunks <= 2u * kTileMax && (flags & ~EXSEQ_PASS_PATH) == 0u;
+}
+
+int batch_chain(const double *const *xs, const size_t *ns, const double *inits, size_t count,
+                double *outs, void *ws, hipStream_t stream, uint32_t flags, exseq_stats *stats)
+{
+    for (size_t g = 0; g < count; g += kMaxBatch) {
+        BatchArgs a{};
+        a.count = (int)(count - g < (size_t)kMaxBatch ? count - g : (size_t)kMaxBatch);
+        a.flags = flags;
+        uint64_t chunks = 0;
+        for (int k = 0; k < a.count; k++) {
+            a.x[k] = xs[g + k];
+            a.n[k] = ns[g + k];
+            a.init[k] = inits ? inits[g + k] : 0.0;
+            a.chunk_base[k] = (uint32_t)chunks;
+            chunks += padded_chunks(ns[g + k]);
+        }
+        if (chunks > 0xFFFFFFFFull)
+            return EXSEQ_EINVAL;
+        a.chunk_base[a.count] = (uint32_t)chunks;
+        const int rc = launch_batch(a, ws, outs + g, stream, stats ? stats + g : nullptr);
+        if (rc != EXSEQ_OK)
+            return rc;
+    }
+    return EXSEQ_OK;
+}
+
+}  // namespace
+
 size_t exact_seq_sum_f64_batch_workspace_size(const size_t *ns, size_t count)
 {
     size_t mx = 0;
@@ -159,7 +205,13 @@ size_t exact_seq_sum_f64_batch_workspace_size(const size_t *ns, size_t count)
             chunks += padded_chunks(ns[k]);
         mx = chunks > mx ? chunks : mx;
     }
-    return round256(sum_ws_bytes(mx));
+    size_t bytes = sum_ws_bytes(mx);
+    for (size_t g = 0; ns && g < count; g += kPassMax) {
+        const size_t m = count - g < (size_t)kPassMax ? count - g : (size_t)kPassMax;
+        const size_t pb = exseq::pass_ws_bytes(exseq::pass_blocks(ns + g, m), m);
+        bytes = pb > bytes ? pb : bytes;
+    }
+    return round256(bytes);
 }
 
 int exact_seq_sum_f64_batch(const double *const *xs, const size_t *ns, const double *inits,
@@ -178,23 +230,21 @@ int exact_seq_sum_f64_batch(const double *const *xs, const size_t *ns, const dou
     }
     if (!ws || ws_bytes < exact_seq_sum_f64_batch_workspace_size(ns, count))
         return ws ? EXSEQ_EWORKSPACE : EXSEQ_EINVAL;
-    for (size_t g = 0; g < count; g += kMaxBatch) {
-        BatchArgs a{};
-        a.count = (int)(count - g < (size_t)kMaxBatch ? count - g : (size_t)kMaxBatch);
-        a.flags = flags;
-        uint64_t chunks = 0;
-        for (int k = 0; k < a.count; k++) {
-            a.x[k] = xs[g + k];
-            a.n[k] = ns[g + k];
-            a.init[k] = inits ? inits[g + k] : 0.0;
-            a.chunk_base[k] = (uint32_t)chunks;
-            chunks += padded_chunks(ns[g + k]);
-        }
-        if (chunks > 0xFFFFFFFFull)
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (!batch_takes_pass(count, flags))
+        return batch_chain(xs, ns, inits, count, outs, ws, st, flags, stats);
+    for (size_t g = 0; g < count; g += kPassMax) {
+        const size_t m = count - g < (size_t)kPassMax ? count - g : (size_t)kPassMax;
+        size_t chunks = 0;
+        for (size_t k = g; k < g + m; k++)
+            chunks += padded_chunks(ns[k]);
+        if (exseq::pass_blocks(ns + g, m) > 0xFFFFFFFFull / 8u)  // chunk indices: 8 per workgroup
             return EXSEQ_EINVAL;
-        a.chunk_base[a.count] = (uint32_t)chunks;
-        int rc = launch_batch(a, ws, outs + g, reinterpret_cast<hipStream_t>(stream),
-                              stats ? stats + g : nullptr);
+        const int rc = chunks == 0 || group_is_tiny(ns + g, m, flags)
+                           ? batch_chain(xs + g, ns + g, inits ? inits + g : nullptr, m, outs + g, ws, st,
+                                         flags, stats ? stats + g : nullptr)
+                           : exseq::launch_pass(xs + g, ns + g, inits ? inits + g : nullptr, (int)m, flags,
+                                                ws, outs + g, st, stats ? stats + g : nullptr, nullptr, 0);
         if (rc != EXSEQ_OK)
             return rc;
     }

@@ -15,6 +15,7 @@ constexpr int kChunkThreads = 256;         // 4 waves x 64 lanes x 4 terms
 constexpr int kPlanThreads = 1024;
 constexpr int kWalkThreads = 256;          // one walk workgroup: 4 waves x 4 items
 constexpr int kMaxBatch = 64;              // sums per launch (kernel arguments)
+constexpr int kPassMax = 128;              // sums per launch of the single pass
 
 static_assert(kChunk == kChunkThreads * 4, "a lane holds 4 consecutive terms");
 
@@ -124,10 +125,14 @@ int launch_exact_sum(const double *x, size_t n, double init, double *out, void *
                      void *const *events = nullptr, int n_events = 0);
 // The single pass (exseq_pass.hip): whether a launch can take it, its
 // workspace, and its launch (one kernel; events[0] and events[1] around it).
+bool pass_flags_ok(uint32_t flags);
 bool pass_eligible(const BatchArgs &a);
-size_t pass_ws_bytes(size_t total_chunks, size_t sums);
-int launch_pass(const BatchArgs &a, void *ws, double *outs, hipStream_t stream,
-                exseq_stats *stats, void *const *events, int n_events);
+size_t pass_blocks(const size_t *ns, size_t count);
+size_t pass_blocks_bound(size_t total_chunks, size_t sums);
+size_t pass_ws_bytes(size_t blocks, size_t sums);
+int launch_pass(const double *const *xs, const size_t *ns, const double *inits, int count,
+                uint32_t flags, void *ws, double *outs, hipStream_t stream, exseq_stats *stats,
+                void *const *events, int n_events);
 extern const char *const kPathKernels[];
 extern const int kPathKernelCount;
 int launch_tree_sum(const double *x, size_t n, double *out, void *ws, hipStream_t stream);

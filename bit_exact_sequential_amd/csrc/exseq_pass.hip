@@ -148,15 +148,28 @@ struct PassWs {
     uint64_t *hrec;  // per sum: 2 words (w0, exact sum after the first tile)
 };
 
+// Up to kPassMax sums, by value.  Sum s has the workgroups block_base[s] ..
+// block_base[s + 1] - 1 (its head, its finisher, its later tiles), and the
+// workspace is laid out by the same index: the tile words of sum s start at
+// block_base[s], its look-back group words at block_base[s] / 64 + s, its
+// chunk descriptors at 8 * block_base[s] (a sum of nt tiles has nt + 1
+// workgroups, at most 8 nt - 4 chunks and at most nt / 64 + 1 groups).
 struct PassArgs {
-    BatchArgs b;
-    uint32_t block_base[kMaxBatch + 1];  // first workgroup of each sum
-    uint32_t tile_base[kMaxBatch + 1];   // first tile of each sum
-    uint32_t group_base[kMaxBatch + 1];  // first look-back group of each sum
-    uint64_t tag;                        // this launch's record tag (45 bits, nonzero)
+    int count;
+    uint32_t flags;
+    uint32_t epoch;  // tags this launch's look-back status words
+    uint64_t tag;    // this launch's record tag (42 bits, nonzero)
     double *outs;
     exseq_stats *stats;
+    const double *x[kPassMax];
+    uint64_t n[kPassMax];
+    double init[kPassMax];
+    uint32_t block_base[kPassMax + 1];
+    __device__ __forceinline__ uint32_t tile_base(int s) const { return block_base[s]; }
+    __device__ __forceinline__ uint32_t group_base(int s) const { return (block_base[s] >> 6) + (uint32_t)s; }
+    __device__ __forceinline__ uint32_t chunk_base(int s) const { return (uint32_t)kTileCh * block_base[s]; }
 };
+static_assert(sizeof(PassArgs) <= 4096, "kernel arguments of the single pass");
 
 // ---------------------------------------------------------------------------
 // LDS
@@ -621,7 +634,7 @@ __device__ __forceinline__ void head_block(const PassArgs &pa, const Src &src, c
                                            int s, PassTileLds &L, WalkCore &sc, double *terms,
                                            int *lds_src)
 {
-    const BatchArgs &a = pa.b;
+    const PassArgs &a = pa;
     const int t = threadIdx.x, lane = lane_id(), wave = wave_id();
     const size_t n = a.n[s];
     exseq_stats *stats = pa.stats ? pa.stats + s : nullptr;
@@ -642,7 +655,7 @@ __device__ __forceinline__ void head_block(const PassArgs &pa, const Src &src, c
     const uint32_t nch = chunks_of_n(n);
     const uint32_t nt = tiles_of(nch);
     const int nk = (int)(nch < (uint32_t)kHeadCh ? nch : (uint32_t)kHeadCh);
-    const SumView v{a.x[s], n, a.init[s], a.chunk_base[s], nch};
+    const SumView v{a.x[s], n, a.init[s], a.chunk_base(s), nch};
     Four f[kHeadCh];
 #pragma unroll
     for (int k = 0; k < kHeadCh; k++)
@@ -671,7 +684,7 @@ __device__ __forceinline__ void head_block(const PassArgs &pa, const Src &src, c
 #pragma unroll
             for (int k = 0; k < kHeadCh; k++)
                 Ttile += (L.wsum[k][0] + L.wsum[k][1]) + (L.wsum[k][2] + L.wsum[k][3]);
-            store_relaxed_u64(w.st + pa.tile_base[s], st_pack(a.epoch, kStIncl, a.init[s] + Ttile));
+            store_relaxed_u64(w.st + pa.tile_base(s), st_pack(a.epoch, kStIncl, a.init[s] + Ttile));
         }
     }
     nf = __syncthreads_or(nf) != 0;
@@ -832,15 +845,15 @@ __device__ __forceinline__ void finisher_block(const PassArgs &pa, const Src &sr
                                                int s, FinLds &F, WalkCore &sc, double *terms,
                                                int *lds_src)
 {
-    const BatchArgs &a = pa.b;
+    const PassArgs &a = pa;
     const int t = threadIdx.x, lane = lane_id(), wave = wave_id();
     const size_t n = a.n[s];
     const uint32_t nch = chunks_of_n(n);
     const uint32_t nt = tiles_of(nch);
     if (nt <= 1)
         return;  // the head wrote the result
-    const SumView v{a.x[s], n, a.init[s], a.chunk_base[s], nch};
-    const uint32_t tb = pa.tile_base[s];
+    const SumView v{a.x[s], n, a.init[s], a.chunk_base(s), nch};
+    const uint32_t tb = pa.tile_base(s);
     const uint64_t tag = pa.tag;
     uint64_t n_fast = 0, n_fb = 0, fb_terms = 0;
     int64_t first_fb = -1;
@@ -1308,7 +1321,7 @@ __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, c
                                            int s, uint32_t i, PassTileLds &L, WalkCore &sc,
                                            CrossLds &xl, double *stage, int *lds_src)
 {
-    const BatchArgs &a = pa.b;
+    const PassArgs &a = pa;
     const int t = threadIdx.x, lane = lane_id(), wave = wave_id();
     const size_t n = a.n[s];
     const uint32_t nch = chunks_of_n(n);
@@ -1316,9 +1329,9 @@ __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, c
     const int nk = (int)(nch - c0 < (uint32_t)kTileCh ? nch - c0 : (uint32_t)kTileCh);
     const uint32_t mode = a.flags & EXSEQ_PLAN_MASK;
     const uint64_t tag = pa.tag;
-    const uint32_t g = pa.tile_base[s] + i;           // the tile in the launch
-    const size_t gc0 = (size_t)a.chunk_base[s] + c0;  // its first chunk in the launch
-    const SumView v{a.x[s], n, a.init[s], a.chunk_base[s], nch};
+    const uint32_t g = pa.tile_base(s) + i;           // the tile in the launch
+    const size_t gc0 = (size_t)a.chunk_base(s) + c0;  // its first chunk in the launch
+    const SumView v{a.x[s], n, a.init[s], a.chunk_base(s), nch};
 
     if (t == 0)
         L.lb_stop = 0;
@@ -1377,8 +1390,8 @@ __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, c
     }
 
     // ---- the plan, and the runs formed while it is looked up
-    uint64_t *st0 = w.st + pa.tile_base[s];
-    uint64_t *gs0 = w.gst + pa.group_base[s];
+    uint64_t *st0 = w.st + pa.tile_base(s);
+    uint64_t *gs0 = w.gst + pa.group_base(s);
     const uint32_t lg = i / kGroup, pg = i % kGroup;
     const bool lookback = mode != EXSEQ_PLAN_FIXED;
     if (lookback && t == 0)
@@ -1731,7 +1744,7 @@ __global__ __launch_bounds__(kChunkThreads, 4) void pass_kernel(PassArgs pa, Src
     __shared__ CrossLds xl;
     __shared__ __align__(16) double U[kUnionDoubles];
     __shared__ int lds_src[Src::kLdsInts];
-    const BatchArgs &a = pa.b;
+    const PassArgs &a = pa;
     // this block's sum: the last with block_base <= blockIdx.x
     int lo = 0, hi = a.count - 1;
     while (lo < hi) {
@@ -1784,100 +1797,95 @@ uint64_t next_tag()
 
 size_t r256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-// Tiles and groups of a launch over total_chunks padded chunks and `sums`
-// sums: at most one tile per eight chunks plus two per sum.
-size_t max_tiles(size_t total_chunks, size_t sums) { return total_chunks / kTileCh + 2 * sums + 1; }
-size_t max_groups(size_t total_chunks, size_t sums)
-{
-    return max_tiles(total_chunks, sums) / kGroup + sums + 1;
-}
-
-PassWs pass_carve(void *ws, size_t total_chunks, size_t sums)
+PassWs pass_carve(void *ws, size_t blocks, size_t sums)
 {
     char *p = static_cast<char *>(ws);
-    const size_t tiles = max_tiles(total_chunks, sums), groups = max_groups(total_chunks, sums);
+    const size_t groups = (blocks >> 6) + sums + 1, chunks = (size_t)kTileCh * blocks;
     PassWs w;
     w.st = reinterpret_cast<uint64_t *>(p);
-    p += r256(tiles * 8);
+    p += r256(blocks * 8);
     w.gst = reinterpret_cast<uint64_t *>(p);
     p += r256(groups * 8);
     w.d.r0 = reinterpret_cast<int64_t *>(p);
-    p += r256(total_chunks * 8);
+    p += r256(chunks * 8);
     w.d.lo = reinterpret_cast<int64_t *>(p);
-    p += r256(total_chunks * 8);
+    p += r256(chunks * 8);
     w.d.hi = reinterpret_cast<int64_t *>(p);
-    p += r256(total_chunks * 8);
+    p += r256(chunks * 8);
     w.d.meta = reinterpret_cast<uint32_t *>(p);
-    p += r256(total_chunks * 4);
+    p += r256(chunks * 4);
     w.trec = reinterpret_cast<uint64_t *>(p);
-    p += r256(tiles * 4 * 8);
+    p += r256(blocks * 4 * 8);
     w.xrec = reinterpret_cast<uint64_t *>(p);
-    p += r256(tiles * kStepWords * 8);
+    p += r256(blocks * kStepWords * 8);
     w.hrec = reinterpret_cast<uint64_t *>(p);
     return w;
 }
 
 }  // namespace
 
-size_t pass_ws_bytes(size_t total_chunks, size_t sums)
+// Workgroups of a launch over sums of ns[0 .. count - 1] terms.
+size_t pass_blocks(const size_t *ns, size_t count)
 {
-    const size_t tiles = max_tiles(total_chunks, sums), groups = max_groups(total_chunks, sums);
-    return r256(tiles * 8) + r256(groups * 8) + 3 * r256(total_chunks * 8) +
-           r256(total_chunks * 4) + r256(tiles * 32) + r256(tiles * kStepWords * 8) +
-           r256(sums * 16 + 16);
+    size_t blocks = 0;
+    for (size_t k = 0; k < count; k++)
+        blocks += 1 + tiles_of((uint32_t)((ns[k] + kChunk - 1) / kChunk));
+    return blocks;
 }
 
-bool pass_eligible(const BatchArgs &a)
+size_t pass_ws_bytes(size_t blocks, size_t sums)
 {
-    const uint32_t mode = a.flags & EXSEQ_PLAN_MASK;
+    const size_t groups = (blocks >> 6) + sums + 1, chunks = (size_t)kTileCh * blocks;
+    return r256(blocks * 8) + r256(groups * 8) + 3 * r256(chunks * 8) + r256(chunks * 4) +
+           r256(blocks * 32) + r256(blocks * kStepWords * 8) + r256(sums * 16 + 16);
+}
+
+// An upper bound of the workgroups of sums of `total_chunks` padded chunks:
+// per sum at most one tile per eight chunks plus three.
+size_t pass_blocks_bound(size_t total_chunks, size_t sums) { return total_chunks / kTileCh + 3 * sums + 1; }
+
+bool pass_flags_ok(uint32_t flags)
+{
+    const uint32_t mode = flags & EXSEQ_PLAN_MASK;
     if (mode == EXSEQ_PLAN_ALL_FALLBACK)
         return false;
-    if (a.flags & (EXSEQ_WALK_ONLY | EXSEQ_CHAIN_CUT | EXSEQ_PLAN_REUSE | EXSEQ_CHAIN_PATH))
+    if (flags & (EXSEQ_WALK_ONLY | EXSEQ_CHAIN_CUT | EXSEQ_PLAN_REUSE | EXSEQ_CHAIN_PATH))
         return false;
-    if ((a.flags >> kTileShift) & 3u)
-        return false;
-    return !a.interleave;
+    return ((flags >> kTileShift) & 3u) == 0u;
 }
 
-template <class Src>
-static int launch_pass_src(const BatchArgs &a, const Src &src, void *ws, double *outs,
-                           hipStream_t stream, exseq_stats *stats, void *const *events,
-                           int n_events)
+bool pass_eligible(const BatchArgs &a) { return pass_flags_ok(a.flags) && !a.interleave; }
+
+int launch_pass(const double *const *xs, const size_t *ns, const double *inits, int count,
+                uint32_t flags, void *ws, double *outs, hipStream_t stream, exseq_stats *stats,
+                void *const *events, int n_events)
 {
-    PassArgs pa;
-    pa.b = a;
+    if (count < 1 || count > kPassMax)
+        return EXSEQ_EINVAL;
+    PassArgs pa{};
+    pa.count = count;
+    pa.flags = flags;
     pa.outs = outs;
     pa.stats = stats;
-    uint32_t blocks = 0, tiles = 0, groups = 0;
-    for (int s = 0; s < a.count; s++) {
-        const uint32_t nch = (uint32_t)((a.n[s] + kChunk - 1) / kChunk);
-        const uint32_t nt = tiles_of(nch);
+    uint32_t blocks = 0;
+    for (int s = 0; s < count; s++) {
+        pa.x[s] = xs[s];
+        pa.n[s] = ns[s];
+        pa.init[s] = inits ? inits[s] : 0.0;
         pa.block_base[s] = blocks;
-        pa.tile_base[s] = tiles;
-        pa.group_base[s] = groups;
-        blocks += 2 + (nt > 1 ? nt - 1 : 0);
-        tiles += nt;
-        groups += (nt + kGroup - 1) / kGroup;
+        blocks += 1 + tiles_of((uint32_t)((ns[s] + kChunk - 1) / kChunk));
     }
-    pa.block_base[a.count] = blocks;
-    pa.tile_base[a.count] = tiles;
-    pa.group_base[a.count] = groups;
+    pa.block_base[count] = blocks;
     pa.tag = next_tag();
-    pa.b.epoch = (uint32_t)(pa.tag & 0xFFFFu) ? (uint32_t)pa.tag : (uint32_t)pa.tag + 1u;
-    const PassWs w = pass_carve(ws, a.chunk_base[a.count], (size_t)a.count);
+    pa.epoch = (uint32_t)(pa.tag & 0xFFFFu) ? (uint32_t)pa.tag : (uint32_t)pa.tag + 1u;
+    const PassWs w = pass_carve(ws, blocks, (size_t)count);
     if (events && n_events > 0 && events[0])
         hipEventRecord(static_cast<hipEvent_t>(events[0]), stream);
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(pass_kernel<Src>), dim3(blocks), dim3(kChunkThreads), 0,
-                       stream, pa, src, w);
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(pass_kernel<PlainTerms>), dim3(blocks), dim3(kChunkThreads), 0,
+                       stream, pa, PlainTerms{}, w);
     if (events && n_events > 1 && events[1])
         hipEventRecord(static_cast<hipEvent_t>(events[1]), stream);
     return hipGetLastError() == hipSuccess ? EXSEQ_OK : EXSEQ_EHIP;
-}
-
-int launch_pass(const BatchArgs &a, void *ws, double *outs, hipStream_t stream,
-                exseq_stats *stats, void *const *events, int n_events)
-{
-    return launch_pass_src(a, PlainTerms{}, ws, outs, stream, stats, events, n_events);
 }
 
 }  // namespace exseq

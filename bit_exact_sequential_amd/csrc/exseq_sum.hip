@@ -1018,7 +1018,7 @@ const int kPathKernelCount = 3;
 // tag; per tile of kTileMax chunks a kept planned prefix.
 size_t sum_ws_bytes(size_t total_chunks)
 {
-    const size_t pass = pass_ws_bytes(total_chunks, kMaxBatch);
+    const size_t pass = pass_ws_bytes(pass_blocks_bound(total_chunks, kMaxBatch), kMaxBatch);
     const size_t chain = 4 * round256(total_chunks * sizeof(int64_t)) +
            round256(total_chunks * sizeof(uint32_t)) +
            round256(4 * total_chunks * sizeof(uint64_t)) +
@@ -1116,8 +1116,12 @@ int launch_batch(const BatchArgs &a, void *ws, double *outs, hipStream_t stream,
     const bool tiny = total <= 2u * kTileMax && (a.flags & ~EXSEQ_PASS_PATH) == 0u &&
                       !(events && n_events);
     const bool want = a.count > 1 || (a.flags & EXSEQ_PASS_PATH);
-    if (want && !tiny && total > 0 && pass_eligible(a))
-        return launch_pass(a, ws, outs, stream, stats, events, n_events);
+    if (want && !tiny && total > 0 && pass_eligible(a)) {
+        size_t ns[kMaxBatch];
+        for (int k = 0; k < a.count; k++)
+            ns[k] = (size_t)a.n[k];
+        return launch_pass(a.x, ns, a.init, a.count, a.flags, ws, outs, stream, stats, events, n_events);
+    }
     return launch_batch_src(a, PlainTerms{}, ws, outs, stream, stats, events, n_events);
 }
 
