@@ -175,18 +175,18 @@ static_assert(sizeof(PassArgs) <= 4096, "kernel arguments of the single pass");
 // LDS
 // ---------------------------------------------------------------------------
 struct PassTileLds {
-    double wsum[kTileCh][kWaves];
-    WaveRun wrun[kTileCh][kWaves];
+    double tsum[kTileCh];
+    double wsum[kHeadCh][kWaves];  // the head's chunk sums per wave
+    WaveRun wrun[kWaves];          // the head's block_run scratch
     WaveRun join[kTileCh];
     double pk[kTileCh];
     uint32_t key[kTileCh];
     uint32_t cross[kTileCh];
     uint32_t down[kTileCh];
+    uint32_t locate[kTileCh];
     uint64_t xw[kTileCh][kCrossWords];
     uint64_t rec[kStepWords];
     uint64_t xexit[4];  // an irregular tile's last run: key etc., r0, lo, hi
-    uint32_t xmask;     // chunks whose crossing is to be located
-    uint32_t regular;   // the tile is regular
     double lb1, lb2;
     int lb_found, lb_ok1, lb_ok2;
     volatile int lb_stop;
@@ -666,7 +666,7 @@ __device__ __forceinline__ void head_block(const PassArgs &pa, const Src &src, c
 #pragma unroll
         for (int i = 0; i < 4; i++)
             nf |= i < f[k].cnt && is_nonfinite(f[k].v[i]);
-    // the tile's inclusive plan prefix (the same fixed tree as every tile's)
+    // the tile's inclusive plan prefix (fixed-tree chunk sums)
     if (nt > 1 && (a.flags & EXSEQ_PLAN_MASK) != EXSEQ_PLAN_FIXED) {
         double ws[kHeadCh];
 #pragma unroll
@@ -702,7 +702,7 @@ __device__ __forceinline__ void head_block(const PassArgs &pa, const Src &src, c
         const uint32_t ks = key_of(S);
         bool applied = false;
         if (k > 0 && key_has_fast_path(ks)) {
-            const WaveRun r = block_run(fk, ks, &L.wrun[0][0]);
+            const WaveRun r = block_run(fk, ks, L.wrun);
             const int64_t m = count_of(S);
             if (run_applies(m, r.p, r.lo, r.hi, r.flags)) {
                 S = assemble(ks, m + pair_at(r.p, m));
@@ -1265,55 +1265,141 @@ __device__ __forceinline__ void finisher_block(const PassArgs &pa, const Src &sr
 // ---------------------------------------------------------------------------
 // A tile after a sum's first: eight chunks
 // ---------------------------------------------------------------------------
-// One wave's part of a chunk's run under `key`; a key with no fast path
-// (a non-finite plan, or the binade of the largest doubles) gives only the
-// non-finite flag, and the chunk is walked term by term.
-__device__ __forceinline__ WaveRun chunk_part(const Four &q, uint32_t key)
+// Each wave forms two chunks of the tile on its own: chunk 2w from
+// registers, chunk 2w + 1 staged in LDS slot w.  Lane l holds terms
+// 256 j + 4 l .. 256 j + 4 l + 3 of its chunk for j = 0 .. 3 (group j is the
+// part a wave of the workgroup layout holds), so one reduction over the wave
+// forms a chunk and nothing is joined across waves.
+
+// Lane l's group-j terms of chunk c of a sum (+0.0 past its end).
+__device__ __forceinline__ Four wave_four(const SumView &v, size_t c, int j)
 {
-    if (key_has_fast_path(key))
-        return wave_run(q, key);
-    bool nf = false;
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-        nf |= is_nonfinite(q.v[i]);
-    WaveRun wr;
-    wr.p = pair_identity();
-    wr.lo = wr.hi = 0;
-    wr.flags = __ballot(nf) ? kFlagNonFinite : 0u;
-    return wr;
+    return load_four(v.x, v.n, c * kChunk + 256 * (size_t)j + 4 * (size_t)lane_id(), true);
 }
 
-// The wave parts of N chunks' runs into wr[k][wave].
-template <int N>
-__device__ __forceinline__ void chunk_runs(const Four *q, const uint32_t *key, WaveRun (*wr)[kWaves])
+// Chunk c into LDS slot k by this wave alone, in the workgroup layout's
+// arrangement (group j where wave j would put it), so that staged_chunk reads
+// lane t's four terms for a block-wide step and staged_four this lane's.
+__device__ __forceinline__ void stage_wave_chunk(double *stage, int k, const SumView &v, size_t c, bool direct)
 {
-    bool allfast = true;
+    const int lane = lane_id();
 #pragma unroll
-    for (int k = 0; k < N; k++)
-        allfast &= key_has_fast_path(key[k]);
-    if (allfast) {
-        wave_runs<N>(q, key, wr);
-        return;
-    }
-#pragma unroll
-    for (int k = 0; k < N; k++) {
-        const WaveRun x = chunk_part(q[k], key[k]);
-        if (lane_id() == 0)
-            wr[k][wave_id()] = x;
+    for (int j = 0; j < 4; j++) {
+        double *base = stage + k * kChunk + j * 256;
+        const size_t first = c * kChunk + 256 * (size_t)j + 4 * (size_t)lane;
+        if (direct) {
+            const double *p = v.x + first;
+            __builtin_amdgcn_global_load_lds((const void *)p, (__attribute__((address_space(3))) void *)base,
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(p + 2),
+                                             (__attribute__((address_space(3))) void *)(base + 128), 16, 0, 0);
+        } else {
+            const Four f = load_four(v.x, v.n, first, true);
+            base[2 * lane] = f.v[0];
+            base[2 * lane + 1] = f.v[1];
+            base[128 + 2 * lane] = f.v[2];
+            base[128 + 2 * lane + 1] = f.v[3];
+        }
     }
 }
 
-// The runs of the four chunks staged in LDS, two at a time (the registers
-// still hold the first four chunks).
-__device__ __forceinline__ void staged_runs(double *stage, size_t n, uint32_t c_first, const uint32_t *key,
-                                            WaveRun (*wr)[kWaves])
+__device__ __forceinline__ Four staged_four(const double *stage, int k, int j)
 {
-#pragma unroll 1
-    for (int j = 0; j < kHalf; j += 2) {
-        const Four q[2] = {staged_chunk(stage, j, n, c_first + j), staged_chunk(stage, j + 1, n, c_first + j + 1)};
-        const uint32_t kq[2] = {j ? key[2] : key[0], j ? key[3] : key[1]};
-        chunk_runs<2>(q, kq, wr + j);
+    const int lane = lane_id();
+    const double *base = stage + k * kChunk + j * 256;
+    Four f;
+    f.v[0] = base[2 * lane];
+    f.v[1] = base[2 * lane + 1];
+    f.v[2] = base[128 + 2 * lane];
+    f.v[3] = base[128 + 2 * lane + 1];
+    f.cnt = 4;
+    return f;
+}
+
+// The fixed-tree sum of a chunk held as four groups per lane.
+__device__ __forceinline__ double lane_tree(const Four *g)
+{
+    double q[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+        q[j] = (g[j].v[0] + g[j].v[1]) + (g[j].v[2] + g[j].v[3]);
+    return (q[0] + q[1]) + (q[2] + q[3]);
+}
+
+// A chunk's run under `key`, formed by one wave from its four groups, the
+// same in every lane.  Where no term ties and every increment has one sign
+// (the bit tests of wave_runs on all 1024 terms), one integer reduction;
+// otherwise each group's ordered run (wave_run) and the four composed in
+// order.  A key with no fast path gives only the non-finite flag.  Clamped.
+__device__ __forceinline__ WaveRun chunk_run(const Four *g, uint32_t key)
+{
+    if (!key_has_fast_path(key)) {
+        bool nf = false;
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                nf |= is_nonfinite(g[j].v[i]);
+        return WaveRun{pair_identity(), 0, 0, __ballot(nf) ? kFlagNonFinite : 0u};
     }
+    const int scale = 1075 - (int)(key & 0x7FFu);
+    const bool flip = (key & 0x800u) != 0u;
+    uint32_t tacc = 0u, hand = ~0u, hor = 0u;
+    uint64_t sum = 0;
+    auto term = [&](double y) {
+        const double a0 = kMagic0 + y;
+        const double a1 = kMagic1 + y;
+        const uint32_t h = (uint32_t)(dbits(a0) >> 32);
+        tacc |= ((uint32_t)dbits(a1) - (uint32_t)dbits(a0)) ^ 1u;
+        hand &= h;
+        hor |= h;
+        sum += dbits(a0);
+    };
+    if (scale <= 1023) {
+        const double fac = flip ? -ldexp(1.0, scale) : ldexp(1.0, scale);
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                term(g[j].v[i] * fac);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const double y = ldexp(g[j].v[i], scale);
+                term(flip ? -y : y);
+            }
+    }
+    const bool ok = tacc == 0u && (((hand ^ kMagic0Hi) | (hor ^ kMagic0Hi)) >> 20) == 0u;
+    const bool pos = __ballot(!((hand >> 19) & 1u)) == 0;  // every a0 >= M0
+    const bool neg = __ballot((hor >> 19) & 1u) == 0;      // every a0 < M0
+    if (__ballot(!ok) == 0 && (pos || neg)) {
+        const int64_t r = wave_sum_i64((int64_t)(sum - 16 * (uint64_t)kMagic0Bits));
+        return clamp_run(pos ? WaveRun{Pair{r, r}, 0, r, 0u} : WaveRun{Pair{r, r}, r, 0, kFlagNeg});
+    }
+    // the groups' runs composed in order as they come (join_waves)
+    WaveRun acc{};
+    bool plain = true, fall = true;
+    int64_t tot = 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const WaveRun q = wave_run(g[j], key);
+        plain &= rising_run(q.p, q.flags);
+        fall &= falling_run(q.p, q.lo, q.hi, q.flags);
+        tot += q.p.r0;
+        if (j == 0) {
+            acc = q;
+        } else {
+            const Run c = run_compose(Run{acc.p, acc.lo, acc.hi, acc.flags}, Run{q.p, q.lo, q.hi, q.flags});
+            acc = WaveRun{c.p, c.lo, c.hi, c.flags};
+        }
+    }
+    if (!(acc.flags & kFlagNeg))
+        acc.hi = acc.p.r0 > acc.p.r1 ? acc.p.r0 : acc.p.r1;
+    return clamp_run(plain  ? WaveRun{Pair{tot, tot}, 0, tot, 0u}
+                     : fall ? WaveRun{Pair{tot, tot}, tot, 0, kFlagNeg}
+                            : acc);
 }
 
 template <class Src>
@@ -1332,62 +1418,54 @@ __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, c
     const uint32_t g = pa.tile_base(s) + i;           // the tile in the launch
     const size_t gc0 = (size_t)a.chunk_base(s) + c0;  // its first chunk in the launch
     const SumView v{a.x[s], n, a.init[s], a.chunk_base(s), nch};
+    const int cr = 2 * wave, cs = 2 * wave + 1;       // this wave's chunks
 
     if (t == 0)
         L.lb_stop = 0;
-    // ---- the terms: four chunks into registers, four into LDS
-    Four f[kHalf];
+    // ---- the terms: chunk cr into registers, chunk cs into LDS slot `wave`
+    Four f[4];
 #pragma unroll
-    for (int k = 0; k < kHalf; k++)
-        f[k] = src.chunk_v(v, c0 + k, lds_src);
-    if (nk > kHalf) {
+    for (int j = 0; j < 4; j++) {
+        if (cr < nk) {
+            f[j] = wave_four(v, c0 + cr, j);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+                f[j].v[q] = 0.0;
+            f[j].cnt = 0;
+        }
+    }
+    if (cs < nk) {
         const bool direct = ((reinterpret_cast<uintptr_t>(v.x) & 15u) == 0u) &&
-                            (size_t)(c0 + kTileCh) * kChunk <= n;
-#pragma unroll
-        for (int k = 0; k < kHalf; k++)
-            stage_chunk(stage, k, v, c0 + kHalf + k, direct);
+                            (size_t)(c0 + cs + 1) * kChunk <= n;
+        stage_wave_chunk(stage, wave, v, c0 + cs, direct);
     }
-    // ---- the fixed-tree sum of every chunk
+    // ---- the fixed-tree sum of both chunks
     {
-        double ws[kHalf];
+        double ws[2];
+        ws[0] = lane_tree(f);
+        ws[1] = 0.0;
+        if (cs < nk) {
+            // the wave reads back only what its own loads put in LDS
+            __builtin_amdgcn_s_waitcnt(0);
+            Four q[4];
 #pragma unroll
-        for (int k = 0; k < kHalf; k++)
-            ws[k] = (f[k].v[0] + f[k].v[1]) + (f[k].v[2] + f[k].v[3]);
-        wave_sum_f64_n<kHalf>(ws);
+            for (int j = 0; j < 4; j++)
+                q[j] = staged_four(stage, wave, j);
+            ws[1] = lane_tree(q);
+        }
+        wave_sum_f64_n<2>(ws);
         if (lane == 0) {
-#pragma unroll
-            for (int k = 0; k < kHalf; k++)
-                L.wsum[k][wave] = ws[k];
+            L.tsum[cr] = ws[0];
+            L.tsum[cs] = ws[1];
         }
-    }
-    if (nk > kHalf) {
-        // each wave reads back only what its own loads put in LDS
-        __builtin_amdgcn_s_waitcnt(0);
-        double ws[kHalf];
-#pragma unroll
-        for (int k = 0; k < kHalf; k++) {
-            const Four q = staged_chunk(stage, k, n, c0 + kHalf + k);
-            ws[k] = (q.v[0] + q.v[1]) + (q.v[2] + q.v[3]);
-        }
-        wave_sum_f64_n<kHalf>(ws);
-        if (lane == 0) {
-#pragma unroll
-            for (int k = 0; k < kHalf; k++)
-                L.wsum[kHalf + k][wave] = ws[k];
-        }
-    } else if (lane == 0) {
-#pragma unroll
-        for (int k = 0; k < kHalf; k++)
-            L.wsum[kHalf + k][wave] = 0.0;
     }
     __syncthreads();
-    double T[kTileCh];
+    // (the chunk sums are read from LDS where needed, not held in registers)
     double Ttile = 0.0;
 #pragma unroll
-    for (int k = 0; k < kTileCh; k++) {
-        T[k] = (L.wsum[k][0] + L.wsum[k][1]) + (L.wsum[k][2] + L.wsum[k][3]);
-        Ttile += T[k];
-    }
+    for (int k = 0; k < kTileCh; k++)
+        Ttile += L.tsum[k];
 
     // ---- the plan, and the runs formed while it is looked up
     uint64_t *st0 = w.st + pa.tile_base(s);
@@ -1403,18 +1481,30 @@ __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, c
     // its planned binade is formed again).  A group's last tile publishes
     // the group's sum from its look-back, so it looks back first.
     const bool spec = lookback && pg != kGroup - 1;
-    uint32_t gkey[kTileCh];
+    uint32_t gk[2] = {0u, 0u};
+    WaveRun run[2];
     if (spec) {
         const double mean = Ttile / (double)nk;
         double pk = a.init[s] + (double)c0 * mean;
 #pragma unroll
         for (int k = 0; k < kTileCh; k++) {
-            gkey[k] = (uint32_t)__builtin_amdgcn_readfirstlane((int)plan_key(pk, a.flags));
-            pk += T[k];
+            const uint32_t kk = (uint32_t)__builtin_amdgcn_readfirstlane((int)plan_key(pk, a.flags));
+            if (k == cr)
+                gk[0] = kk;
+            if (k == cs)
+                gk[1] = kk;
+            pk += L.tsum[k];
         }
-        chunk_runs<kHalf>(f, gkey, L.wrun);
-        if (nk > kHalf)
-            staged_runs(stage, n, c0 + kHalf, gkey + kHalf, L.wrun + kHalf);
+        // the register chunk first: its registers are free after it
+        if (cr < nk)
+            run[0] = chunk_run(f, gk[0]);
+        if (cs < nk) {
+            Four q[4];
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                q[j] = staged_four(stage, wave, j);
+            run[1] = chunk_run(q, gk[1]);
+        }
     }
     double P = a.init[s];
     if (lookback) {
@@ -1452,83 +1542,58 @@ __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, c
                 store_relaxed_u64(gs0 + lg, st_pack(a.epoch, kStIncl, P + Ttile));
         }
     }
-    if (wave == 0 && lane < kTileCh) {
-        // the chunk sums again from LDS (the same tree: the same values), so
-        // that they need no registers through the runs and the look-back
-        auto tsum = [&](int k) { return (L.wsum[k][0] + L.wsum[k][1]) + (L.wsum[k][2] + L.wsum[k][3]); };
-        double pk = P, tk = tsum(0);
+    // ---- every chunk's planned prefix and binade (each wave its own two,
+    // from the same sums in the same order), kept in LDS by the wave
+    uint32_t kc[2];
+    {
+        double pk = P;
 #pragma unroll
-        for (int k = 0; k < kTileCh - 1; k++) {
-            const double tn = tsum(k + 1);
-            if (k < lane)
-                pk += tsum(k);
-            if (k + 1 == lane)
-                tk = tn;
+        for (int k = 0; k < kTileCh; k++) {
+            const double tk = L.tsum[k];
+            if ((k >> 1) == wave) {
+                const uint32_t ka = key_of(pk), kb = key_of(pk + tk);
+                const uint32_t kp = plan_key(pk, a.flags);
+                kc[k & 1] = kp;
+                if (lane == 0) {
+                    L.pk[k] = pk;
+                    L.key[k] = kp;
+                    L.cross[k] = kb != ka;
+                    L.down[k] = ((kb ^ ka) & 0x800u) == 0u && (kb & 0x7FFu) < (ka & 0x7FFu);
+                }
+            }
+            pk += tk;
         }
-        L.pk[lane] = pk;
-        L.key[lane] = plan_key(pk, a.flags);
-        L.cross[lane] = key_of(pk + tk) != key_of(pk);
-        L.down[lane] = ((key_of(pk + tk) ^ key_of(pk)) & 0x800u) == 0u &&
-                       (key_of(pk + tk) & 0x7FFu) < (key_of(pk) & 0x7FFu);
     }
-    __syncthreads();
-
-    bool miss_any = false;
     // ---- the runs not formed under the guess: every chunk without one, else
-    // the chunks whose guess missed.  The registers' four chunks are dead
-    // after their runs; a chunk of theirs needed again (a missed guess, a
-    // crossing to locate) is read again from memory.
-    if (!spec) {
-        uint32_t key[kHalf];
-#pragma unroll
-        for (int k = 0; k < kHalf; k++)
-            key[k] = L.key[k];
-        chunk_runs<kHalf>(f, key, L.wrun);
-        if (nk > kHalf) {
-#pragma unroll
-            for (int k = 0; k < kHalf; k++)
-                key[k] = L.key[kHalf + k];
-            staged_runs(stage, n, c0 + kHalf, key, L.wrun + kHalf);
-        }
-    } else {
-        uint32_t miss = 0u;
-#pragma unroll
-        for (int k = 0; k < kTileCh; k++)
-            miss |= (k < nk && L.key[k] != gkey[k]) ? 1u << k : 0u;
-        miss = (uint32_t)__builtin_amdgcn_readfirstlane((int)miss);
-        miss_any = miss != 0u;
+    // a chunk whose guess missed (its terms read again: the register chunk
+    // from memory, the other from its LDS slot)
 #pragma unroll 1
-        for (int c = 0; c < nk; c++) {
-            if (!((miss >> c) & 1u))
-                continue;
-            const Four q = c < kHalf ? src.chunk_v(v, c0 + c, lds_src) : staged_chunk(stage, c - kHalf, n, c0 + c);
-            const WaveRun wr = chunk_part(q, L.key[c]);
-            if (lane == 0)
-                L.wrun[c][wave] = wr;
-        }
+    for (int h = 0; h < 2; h++) {
+        const int c = cr + h;
+        const uint32_t kh = h ? kc[1] : kc[0];
+        if (c >= nk || (spec && (h ? gk[1] : gk[0]) == kh))
+            continue;
+        Four q[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            q[j] = h ? staged_four(stage, wave, j) : wave_four(v, c0 + cr, j);
+        const WaveRun r = chunk_run(q, kh);
+        if (h)
+            run[1] = r;
+        else
+            run[0] = r;
     }
-    // (the guessed runs were written before the look-back's barrier)
-    if (!spec || miss_any)
-        __syncthreads();
-    // ---- each chunk's four parts joined (a lane per chunk), the binade
-    // edges checked, the descriptor stored
-    if (t < nk) {
-        const int c = t;
+    // ---- the binade edges checked and the descriptors stored (lane h for
+    // the wave's chunk cr + h; lane 0 wrote their plan words above)
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (lane < 2 && cr + lane < nk) {
+        const int h = lane, c = cr + h;
+        const WaveRun r = h ? run[1] : run[0];
         const uint32_t kk = L.key[c];
         const double pk = L.pk[c];
-        bool cc = L.cross[c] != 0;
-        bool plain = true, fall = true;
-        int64_t sum = 0;
-#pragma unroll
-        for (int wv = 0; wv < kWaves; wv++) {
-            const WaveRun &q = L.wrun[c][wv];
-            plain &= rising_run(q.p, q.flags);
-            fall &= falling_run(q.p, q.lo, q.hi, q.flags);
-            sum += q.p.r0;
-        }
-        const WaveRun r = clamp_run(plain  ? WaveRun{Pair{sum, sum}, 0, sum, 0u}
-                                    : fall ? WaveRun{Pair{sum, sum}, sum, 0, kFlagNeg}
-                                           : join_waves(L.wrun[c]));
+        const bool dn = L.down[c] != 0u;
+        bool cc = L.cross[c] != 0u;
         if (key_has_fast_path(kk) && kk == key_of(pk)) {
             const int64_t m = count_of(pk);
             const int64_t mg = plan_margin(c0 + c + 1);
@@ -1542,28 +1607,31 @@ __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, c
         L.join[c] = r;
         L.cross[c] = cc;
         store_desc_coherent(w.d, gc0 + (size_t)c, kk, r, cc ? kFlagCross : 0u);
-        // a crossing to locate; a chunk of a regular tile
-        const bool dn = L.down[c] != 0u;
-        const bool locate = cc && key_has_fast_path(kk) && kk == key_of(pk) &&
-                            key_has_fast_path(dn ? kk - 1u : kk + 1u) && !(r.flags & kFlagNonFinite);
-        const bool reg = key_has_fast_path(kk) && kk == L.key[0] && !cc &&
-                         !(r.flags & (kFlagBad | kFlagNonFinite));
-        const uint64_t xm = __ballot(locate), rm = __ballot(reg);
-        if (t == 0) {
-            L.xmask = (uint32_t)xm;
-            L.regular = rm == (1ull << nk) - 1u;
-        }
+        // a crossing to locate
+        L.locate[c] = cc && key_has_fast_path(kk) && kk == key_of(pk) &&
+                      key_has_fast_path(dn ? kk - 1u : kk + 1u) && !(r.flags & kFlagNonFinite);
     }
     __syncthreads();
-    // ---- the crossing of every chunk planned to cross
+    uint32_t xmask = 0u;
+    bool regular = true;
+#pragma unroll
+    for (int k = 0; k < kTileCh; k++) {
+        if (k < nk) {
+            xmask |= L.locate[k] ? 1u << k : 0u;
+            regular &= key_has_fast_path(L.key[k]) && L.key[k] == L.key[0] && !L.cross[k] &&
+                       !(L.join[k].flags & (kFlagBad | kFlagNonFinite));
+        }
+    }
+    xmask = (uint32_t)__builtin_amdgcn_readfirstlane((int)xmask);
+    // ---- the crossing of every chunk planned to cross, located by the
+    // whole workgroup (a register chunk read again from memory)
     uint32_t found = 0u;
     int buf = 0;
-    const uint32_t xmask = (uint32_t)__builtin_amdgcn_readfirstlane((int)L.xmask);
 #pragma unroll 1
     for (int c = 0; c < nk; c++) {
         if (!((xmask >> c) & 1u))
             continue;
-        const Four q = c < kHalf ? src.chunk_v(v, c0 + c, lds_src) : staged_chunk(stage, c - kHalf, n, c0 + c);
+        const Four q = (c & 1) ? staged_chunk(stage, c >> 1, n, c0 + c) : src.chunk_v(v, c0 + c, lds_src);
         uint64_t xw[kCrossWords];
         if (crossing_find(q, chunk_len(n, c0 + c), L.key[c], count_of(L.pk[c]), L.down[c] != 0u, sc, xl,
                           buf, xw)) {
@@ -1575,18 +1643,19 @@ __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, c
             }
         }
     }
-    __syncthreads();
+    if (xmask)
+        __syncthreads();
 
     // ---- the tile's record
-    const bool regular = L.regular != 0;
     uint64_t *trec = w.trec + 4 * (size_t)g;
     if (regular) {
-        // The chunks' runs in order (plain ones add up), by lane 0.  Its
-        // wave stored every descriptor of the tile: once they are complete,
-        // the record's words go out together (each carries the launch tag).
+        // The chunks' runs in order (plain ones add up), by lane 0, once
+        // every wave's descriptor stores are complete; then the record's
+        // words go out together (each carries the launch tag).
+        stores_complete();
+        __syncthreads();
         if (wave != 0)
             return;
-        stores_complete();
         if (t == 0) {
             Run tr = run_identity();
             bool plain = true, fall = true;

@@ -237,64 +237,6 @@ WaveRun twin_wave_run(const Rules &R, const Chunk &c, int wave, uint32_t key)
     return w;
 }
 
-// wave_runs<4>: the four chunks of a half tile, per wave; the shortcut where
-// the wave has no tie in any of them and the increments of each are all >= 0
-// or all < 0, with the kernel's tests on the magic sums' bit patterns
-void twin_wave_runs(const Rules &R, const Chunk *const *c, const uint32_t *key, WaveRun out[4][4])
-{
-    for (int wave = 0; wave < 4; wave++) {
-        bool easy = true;
-        uint32_t negs = 0u;
-        int64_t v[4];
-        for (int k = 0; k < 4; k++) {
-            const int scale = 1075 - (int)(key[k] & 0x7FFu);
-            const bool flip = (key[k] & 0x800u) != 0u;
-            const double fac = flip ? -std::ldexp(1.0, scale) : std::ldexp(1.0, scale);
-            bool bad = false, notpos = false, notneg = false;
-            uint64_t sum = 0;
-            for (int l = 0; l < kWaveLanes; l++) {
-                const int lane = kWaveLanes * wave + l;
-                uint32_t tacc = 0u, hand = ~0u, hor = 0u;
-                uint64_t lsum = 0;
-                for (int i = 0; i < 4; i++) {
-                    const double x = c[k]->v[kPerLane * lane + i];  // +0.0 past the end
-                    double y;
-                    if (scale <= 1023) {
-                        y = x * fac;
-                    } else {
-                        y = std::ldexp(x, scale);
-                        y = flip ? -y : y;
-                    }
-                    const double a0 = kMagic0 + y, a1 = kMagic1 + y;
-                    const uint32_t h = (uint32_t)(dbits(a0) >> 32);
-                    tacc |= ((uint32_t)dbits(a1) - (uint32_t)dbits(a0)) ^ 1u;
-                    hand &= h;
-                    hor |= h;
-                    lsum += dbits(a0);
-                }
-                sum += lsum - 4 * (uint64_t)kMagic0Bits;
-                bad |= tacc != 0u || (((hand ^ kMagic0Hi) | (hor ^ kMagic0Hi)) >> 20) != 0u;
-                notpos |= !((hand >> 19) & 1u);
-                notneg |= (hor >> 19) & 1u;
-            }
-            v[k] = (int64_t)sum;
-            easy &= !bad && (!notpos || !notneg);
-            negs |= (notpos && !notneg) ? 1u << k : 0u;
-        }
-        // (a tie that the mutation rounds up is no tie: the shortcut then
-        // sees exactly what wave_run sees)
-        if (easy && !(R.mut & EXSEQ_MUT_TIE_UP)) {
-            for (int k = 0; k < 4; k++) {
-                const bool n = (negs >> k) & 1u;
-                out[k][wave] = WaveRun{Pair{v[k], v[k]}, n && v[k] < 0 ? v[k] : 0, 0, n ? kFlagNeg : 0u};
-            }
-        } else {
-            for (int k = 0; k < 4; k++)
-                out[k][wave] = twin_wave_run(R, *c[k], wave, key[k]);
-        }
-    }
-}
-
 // The tile's join of a chunk's four wave parts (the lane < 4 code of
 // tile_block), clamped
 WaveRun twin_join(const Rules &R, const WaveRun *w)
@@ -311,6 +253,55 @@ WaveRun twin_join(const Rules &R, const WaveRun *w)
                             : R.join(w));
 }
 
+// chunk_run: one wave forms a whole chunk of a tile (lane l holds terms
+// 256 j + 4 l .. + 3 of group j).  The shortcut where no term of the chunk
+// ties and its increments are all >= 0 or all < 0, with the kernel's tests on
+// the magic sums' bit patterns (AND and OR over the terms, in any grouping);
+// otherwise each group's run (wave_run over the 256 terms a wave of the
+// workgroup layout holds) and the four composed in order.  Clamped.
+WaveRun twin_chunk_run(const Rules &R, const Chunk &c, uint32_t key)
+{
+    if (!key_has_fast_path(key)) {
+        bool nf = false;
+        for (int q = 0; q < kLanes * kPerLane; q++)
+            nf |= is_nonfinite(c.v[q]);
+        return WaveRun{pair_identity(), 0, 0, nf ? kFlagNonFinite : 0u};
+    }
+    const int scale = 1075 - (int)(key & 0x7FFu);
+    const bool flip = (key & 0x800u) != 0u;
+    const double fac = flip ? -std::ldexp(1.0, scale) : std::ldexp(1.0, scale);
+    uint32_t tacc = 0u, hand = ~0u, hor = 0u;
+    uint64_t sum = 0;
+    for (int q = 0; q < kLanes * kPerLane; q++) {
+        const double x = c.v[q];  // +0.0 past the end
+        double y;
+        if (scale <= 1023) {
+            y = x * fac;
+        } else {
+            y = std::ldexp(x, scale);
+            y = flip ? -y : y;
+        }
+        const double a0 = kMagic0 + y, a1 = kMagic1 + y;
+        const uint32_t h = (uint32_t)(dbits(a0) >> 32);
+        tacc |= ((uint32_t)dbits(a1) - (uint32_t)dbits(a0)) ^ 1u;
+        hand &= h;
+        hor |= h;
+        sum += dbits(a0);
+    }
+    const bool ok = tacc == 0u && (((hand ^ kMagic0Hi) | (hor ^ kMagic0Hi)) >> 20) == 0u;
+    const bool pos = (hand >> 19) & 1u, neg = !((hor >> 19) & 1u);
+    // (a tie that the mutation rounds up is no tie: the shortcut then sees
+    // exactly what wave_run sees)
+    if (ok && (pos || neg) && !(R.mut & EXSEQ_MUT_TIE_UP)) {
+        const int64_t r = (int64_t)(sum - (uint64_t)(kLanes * kPerLane) * (uint64_t)kMagic0Bits);
+        return clamp_run(pos ? WaveRun{Pair{r, r}, 0, r, 0u} : WaveRun{Pair{r, r}, r, 0, kFlagNeg});
+    }
+    WaveRun w[4];
+    for (int j = 0; j < 4; j++)
+        w[j] = twin_wave_run(R, c, j, key);
+    return twin_join(R, w);
+}
+
 // block_run (the head): wave_run per wave, joined, clamped
 WaveRun twin_block_run(const Rules &R, const Chunk &c, uint32_t key)
 {
@@ -320,21 +311,22 @@ WaveRun twin_block_run(const Rules &R, const Chunk &c, uint32_t key)
     return clamp_run(R.join(w));
 }
 
-// The fixed-tree sum of a chunk: per lane (v0 + v1) + (v2 + v3), per wave the
-// row tree of wave_sum_f64, the four waves (w0 + w1) + (w2 + w3)
+// The fixed-tree sum of a tile's chunk (one wave): per lane and group j
+// (v0 + v1) + (v2 + v3), the lane's four groups (g0 + g1) + (g2 + g3), then
+// the row tree of wave_sum_f64 over the lanes
 double twin_tree_sum(const Chunk &c)
 {
-    double ws[4];
-    for (int wave = 0; wave < 4; wave++) {
-        double v[kWaveLanes];
-        for (int l = 0; l < kWaveLanes; l++) {
-            const double *q = c.v + kPerLane * (kWaveLanes * wave + l);
-            v[l] = (q[0] + q[1]) + (q[2] + q[3]);
+    double v[kWaveLanes];
+    for (int l = 0; l < kWaveLanes; l++) {
+        double g[4];
+        for (int j = 0; j < 4; j++) {
+            const double *q = c.v + 256 * j + kPerLane * l;
+            g[j] = (q[0] + q[1]) + (q[2] + q[3]);
         }
-        wave_scan_tree(v, [](double a, double b) { return a + b; }, 0.0);
-        ws[wave] = v[kWaveLanes - 1];
+        v[l] = (g[0] + g[1]) + (g[2] + g[3]);
     }
-    return (ws[0] + ws[1]) + (ws[2] + ws[3]);
+    wave_scan_tree(v, [](double a, double b) { return a + b; }, 0.0);
+    return v[kWaveLanes - 1];
 }
 
 // crossing_find: the crossing of a chunk from the planned count m_est under
@@ -616,47 +608,20 @@ struct Twin {
             p += tk[k];
         }
         WaveRun join[kTwinTile];
-        for (int h = 0; h < 2; h++) {
-            const Chunk *cs[4];
-            uint32_t ks[4];
-            bool allfast = true;
-            for (int k = 0; k < 4; k++) {
-                cs[k] = &ch[4 * h + k];
-                ks[k] = key[4 * h + k];
-                allfast &= key_has_fast_path(ks[k]);
+        for (uint32_t c = 0; c < kTwinTile; c++) {
+            join[c] = twin_chunk_run(R, ch[c], key[c]);
+            if (key_has_fast_path(key[c]) && key[c] == key_of(pk[c])) {
+                const int64_t m = count_of(pk[c]);
+                const int64_t mg = plan_margin(c0 + c + 1);
+                bool near = m < count_floor(key[c]) + mg;
+                if (join[c].flags & kFlagNeg)
+                    near |= m + join[c].lo - mg < kCountLo + 1 || m + join[c].hi + mg > kCountHi - 1;
+                else
+                    near |= m + join[c].hi + mg > kCountHi;
+                cross[c] |= near;
             }
-            WaveRun wr[4][4];
-            if (allfast) {
-                twin_wave_runs(R, cs, ks, wr);
-            } else {
-                for (int k = 0; k < 4; k++)
-                    for (int wv = 0; wv < 4; wv++) {
-                        if (key_has_fast_path(ks[k])) {
-                            wr[k][wv] = twin_wave_run(R, *cs[k], wv, ks[k]);
-                        } else {
-                            bool nf = false;
-                            for (int l = 0; l < kWaveLanes * 4; l++)
-                                nf |= is_nonfinite(cs[k]->v[kWaveLanes * 4 * wv + l]);
-                            wr[k][wv] = WaveRun{pair_identity(), 0, 0, nf ? kFlagNonFinite : 0u};
-                        }
-                    }
-            }
-            for (int k = 0; k < 4; k++) {
-                const int c = 4 * h + k;
-                join[c] = twin_join(R, wr[k]);
-                if (key_has_fast_path(key[c]) && key[c] == key_of(pk[c])) {
-                    const int64_t m = count_of(pk[c]);
-                    const int64_t mg = plan_margin(c0 + c + 1);
-                    bool near = m < count_floor(key[c]) + mg;
-                    if (join[c].flags & kFlagNeg)
-                        near |= m + join[c].lo - mg < kCountLo + 1 || m + join[c].hi + mg > kCountHi - 1;
-                    else
-                        near |= m + join[c].hi + mg > kCountHi;
-                    cross[c] |= near;
-                }
-                if ((uint32_t)c < nk)
-                    desc[c0 + c] = Desc{key[c], join[c]};
-            }
+            if (c < nk)
+                desc[c0 + c] = Desc{key[c], join[c]};
         }
         // the crossings it locates
         uint32_t found = 0u;
