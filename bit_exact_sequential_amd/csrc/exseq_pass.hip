@@ -69,7 +69,8 @@ namespace exseq {
 constexpr int kHalf = 4;             // chunks per half tile (one Four each in registers)
 constexpr int kTileCh = 8;           // chunks of every tile after a sum's first
 constexpr int kHeadCh = 4;           // chunks of a sum's first tile
-constexpr uint32_t kGroup = 64;      // tiles per look-back group
+constexpr int kGroupShift = 6;
+constexpr uint32_t kGroup = 1u << kGroupShift;  // tiles per look-back group
 constexpr int kFinLane = 4;          // tiles per lane in a finisher window
 constexpr int kFinTiles = kFinLane * kChunkThreads;  // tiles per finisher window
 constexpr int kStepCap = 16;         // step records a finisher window holds
@@ -151,9 +152,9 @@ struct PassWs {
 // Up to kPassMax sums, by value.  Sum s has the workgroups block_base[s] ..
 // block_base[s + 1] - 1 (its head, its finisher, its later tiles), and the
 // workspace is laid out by the same index: the tile words of sum s start at
-// block_base[s], its look-back group words at block_base[s] / 64 + s, its
+// block_base[s], its look-back group words at block_base[s] / kGroup + s, its
 // chunk descriptors at 8 * block_base[s] (a sum of nt tiles has nt + 1
-// workgroups, at most 8 nt - 4 chunks and at most nt / 64 + 1 groups).
+// workgroups, at most 8 nt - 4 chunks and at most nt / kGroup + 1 groups).
 struct PassArgs {
     int count;
     uint32_t flags;
@@ -166,7 +167,7 @@ struct PassArgs {
     double init[kPassMax];
     uint32_t block_base[kPassMax + 1];
     __device__ __forceinline__ uint32_t tile_base(int s) const { return block_base[s]; }
-    __device__ __forceinline__ uint32_t group_base(int s) const { return (block_base[s] >> 6) + (uint32_t)s; }
+    __device__ __forceinline__ uint32_t group_base(int s) const { return (block_base[s] >> kGroupShift) + (uint32_t)s; }
     __device__ __forceinline__ uint32_t chunk_base(int s) const { return (uint32_t)kTileCh * block_base[s]; }
 };
 static_assert(sizeof(PassArgs) <= 4096, "kernel arguments of the single pass");
@@ -1402,6 +1403,26 @@ __device__ __forceinline__ WaveRun chunk_run(const Four *g, uint32_t key)
                             : acc);
 }
 
+// The look-back's first level, by one wave: the plan prefix before the
+// tile from the tile words of its group (into L); the group's last tile
+// publishes the group's sum (or its inclusive prefix) as soon as known.
+__device__ __forceinline__ void level1(PassTileLds &L, const uint64_t *st, int pg, uint32_t lg, uint32_t epoch,
+                                       uint64_t *gs0, double Ttile)
+{
+    double v1;
+    bool ok1;
+    const bool found = lb_level1(st, pg, epoch, v1, ok1);
+    if (lane_id() == 0) {
+        L.lb1 = v1;
+        L.lb_found = found;
+        L.lb_ok1 = ok1;
+        if (found || lg == 0)
+            L.lb_stop = 1;
+        if (pg == (int)kGroup - 1 && ok1)
+            store_relaxed_u64(gs0 + lg, st_pack(epoch, found ? kStIncl : kStAgg, v1 + Ttile));
+    }
+}
+
 template <class Src>
 __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, const PassWs &w,
                                            int s, uint32_t i, PassTileLds &L, WalkCore &sc,
@@ -1474,13 +1495,17 @@ __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, c
     const bool lookback = mode != EXSEQ_PLAN_FIXED;
     if (lookback && t == 0)
         store_relaxed_u64(st0 + i, st_pack(a.epoch, kStAgg, Ttile));
+    // A group's last tile publishes the group's sum from its look-back over
+    // the group: its first wave does that first.
+    const bool last_in_group = lookback && pg == kGroup - 1;
+    if (last_in_group && wave == 0)
+        level1(L, st0 + kGroup * lg, (int)pg, lg, a.epoch, gs0, Ttile);
     // A guess of every chunk's planned binade, from the prefix before the
     // tile taken as its first chunk's index times the tile's mean chunk sum:
     // the runs are formed under it while the look-back waits for the tiles
     // before (the plan decides speed only; a chunk whose guess differs from
-    // its planned binade is formed again).  A group's last tile publishes
-    // the group's sum from its look-back, so it looks back first.
-    const bool spec = lookback && pg != kGroup - 1;
+    // its planned binade is formed again).
+    const bool spec = lookback;
     uint32_t gk[2] = {0u, 0u};
     WaveRun run[2];
     if (spec) {
@@ -1509,19 +1534,8 @@ __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, c
     double P = a.init[s];
     if (lookback) {
         if (wave == 0) {
-            double v1;
-            bool ok1;
-            const bool found = lb_level1(st0 + kGroup * lg, (int)pg, a.epoch, v1, ok1);
-            if (lane == 0) {
-                L.lb1 = v1;
-                L.lb_found = found;
-                L.lb_ok1 = ok1;
-                if (found || lg == 0)
-                    L.lb_stop = 1;
-                // the group's sum (or its inclusive prefix) as soon as known
-                if (pg == kGroup - 1 && ok1)
-                    store_relaxed_u64(gs0 + lg, st_pack(a.epoch, found ? kStIncl : kStAgg, v1 + Ttile));
-            }
+            if (!last_in_group)
+                level1(L, st0 + kGroup * lg, (int)pg, lg, a.epoch, gs0, Ttile);
         } else if (wave == 1) {
             bool ok2 = true;
             double v2 = 0.0;
@@ -1869,7 +1883,7 @@ size_t r256(size_t b) { return (b + 255) & ~(size_t)255; }
 PassWs pass_carve(void *ws, size_t blocks, size_t sums)
 {
     char *p = static_cast<char *>(ws);
-    const size_t groups = (blocks >> 6) + sums + 1, chunks = (size_t)kTileCh * blocks;
+    const size_t groups = (blocks >> kGroupShift) + sums + 1, chunks = (size_t)kTileCh * blocks;
     PassWs w;
     w.st = reinterpret_cast<uint64_t *>(p);
     p += r256(blocks * 8);
@@ -1904,7 +1918,7 @@ size_t pass_blocks(const size_t *ns, size_t count)
 
 size_t pass_ws_bytes(size_t blocks, size_t sums)
 {
-    const size_t groups = (blocks >> 6) + sums + 1, chunks = (size_t)kTileCh * blocks;
+    const size_t groups = (blocks >> kGroupShift) + sums + 1, chunks = (size_t)kTileCh * blocks;
     return r256(blocks * 8) + r256(groups * 8) + 3 * r256(chunks * 8) + r256(chunks * 4) +
            r256(blocks * 32) + r256(blocks * kStepWords * 8) + r256(sums * 16 + 16);
 }
