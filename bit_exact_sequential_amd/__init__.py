@@ -26,6 +26,7 @@ PLAN_ALL_FALLBACK = 1
 PLAN_PLUS_ONE = 2
 PLAN_MINUS_ONE = 3
 PLAN_FIXED = 4
+PLAN_ALL_ZERO = 5
 
 
 def plan_fixed(key: int) -> int:

@@ -161,6 +161,8 @@ EXSEQ_HD uint32_t plan_key(double p, uint32_t flags)
         return 0u;
     if (mode == EXSEQ_PLAN_FIXED)
         return (flags >> 8) & kKeyMask;
+    if (mode == EXSEQ_PLAN_ALL_ZERO)
+        return key_of(0.0);
     uint32_t k = key_of(p);
     if (!key_has_fast_path(k))
         return 0u;

@@ -66,12 +66,15 @@ enum {
  *   PLUS_ONE      one binade too high on every chunk
  *   MINUS_ONE     one binade too low on every chunk
  *   FIXED         every chunk planned for the key in bits 8..19 of `flags`
- *                 (sign bit << 11 | biased exponent; 1023 is [1, 2)) */
+ *                 (sign bit << 11 | biased exponent; 1023 is [1, 2))
+ *   ALL_ZERO      every chunk planned as if the sum before it were +0 (the
+ *                 binade of the subnormals) */
 #define EXSEQ_PLAN_AUTO 0u
 #define EXSEQ_PLAN_ALL_FALLBACK 1u
 #define EXSEQ_PLAN_PLUS_ONE 2u
 #define EXSEQ_PLAN_MINUS_ONE 3u
 #define EXSEQ_PLAN_FIXED 4u
+#define EXSEQ_PLAN_ALL_ZERO 5u
 #define EXSEQ_PLAN_MASK 0xFu
 #define EXSEQ_PLAN_FIXED_KEY(key) (EXSEQ_PLAN_FIXED | (((uint32_t)(key) & 0xFFFu) << 8))
 

@@ -15,7 +15,7 @@ from tests.gpu_util import same, say, to_dev, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
-PLANS = [ex.PLAN_AUTO, ex.PLAN_ALL_FALLBACK, ex.PLAN_PLUS_ONE, ex.PLAN_MINUS_ONE,
+PLANS = [ex.PLAN_AUTO, ex.PLAN_ALL_FALLBACK, ex.PLAN_PLUS_ONE, ex.PLAN_MINUS_ONE, ex.PLAN_ALL_ZERO,
          ex.plan_fixed(1023)]
 # both launch plans of a plain sum: the tile chain (default for one sum) and
 # the single pass

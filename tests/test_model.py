@@ -29,7 +29,7 @@ def same(a, b):
     return bits(a) == bits(b)
 
 
-PLANS = [ex.PLAN_AUTO, ex.PLAN_ALL_FALLBACK, ex.PLAN_PLUS_ONE, ex.PLAN_MINUS_ONE,
+PLANS = [ex.PLAN_AUTO, ex.PLAN_ALL_FALLBACK, ex.PLAN_PLUS_ONE, ex.PLAN_MINUS_ONE, ex.PLAN_ALL_ZERO,
          ex.plan_fixed(1023)]
 CHUNKS = [1, 2, 4, 1024]
 

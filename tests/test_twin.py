@@ -44,7 +44,7 @@ MUTATIONS = {"tie_up": ex.MUT_TIE_UP, "no_binade_check": ex.MUT_NO_BINADE_CHECK,
 @pytest.mark.parametrize("case", suites.edge_suite(), ids=lambda c: c[0])
 def test_edge_cases(case):
     name, x, init = case
-    for plan in (ex.PLAN_AUTO, ex.PLAN_PLUS_ONE, ex.PLAN_MINUS_ONE):
+    for plan in (ex.PLAN_AUTO, ex.PLAN_PLUS_ONE, ex.PLAN_MINUS_ONE, ex.PLAN_ALL_ZERO):
         got, _ = ex.twin_seq_sum(x, init, flags=plan)
         assert same(got, oracle.seq_sum(x, init)), (name, plan)
 
