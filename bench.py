@@ -260,8 +260,8 @@ def _pyramid(ex, si, torch, dev, seed, reps, timed, res, video=True):
                                 "roofline": {"bound": "hbm", "kernel": "pass_kernel", "achieved": gbs5,
                                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                              "frac": gbs5 / HBM_PEAK_GBS,
-                                             "note": "whole call (two launches of 64 and 44 sums); "
-                                                     "bytes = the terms read once"}}
+                                             "note": "whole call (one launch of the single pass for "
+                                                     "all 108 sums); bytes = the terms read once"}}
     if not video:
         return
     # the same batch as a video: two pyramids (frames) in turn, each call
