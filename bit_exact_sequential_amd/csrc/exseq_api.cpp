@@ -169,9 +169,30 @@ bool group_is_tiny(const size_t *ns, size_t count, uint32_t flags)
     return chunks <= 2u * kTileMax && (flags & ~EXSEQ_PASS_PATH) == 0u;
 }
 
+// A batch of more than kMaxBatch sums through the tile chain: the groups'
+// kept plans (EXSEQ_PLAN_REUSE) at the start of the workspace, each group at
+// a place of its own that does not depend on the group's size, and the
+// groups' working arrays after them.
+size_t batch_plan_bytes(const size_t *ns, size_t count)
+{
+    if (count <= (size_t)kMaxBatch)
+        return 0;
+    size_t tiles = 0;
+    for (size_t g = 0; g < count; g += kMaxBatch) {
+        size_t chunks = 0;
+        for (size_t k = g; k < count && k < g + kMaxBatch; k++)
+            chunks += padded_chunks(ns[k]);
+        tiles += chunks / kTileMax + 1;
+    }
+    return round256(count * sizeof(uint64_t)) + round256(tiles * sizeof(double));
+}
+
 int batch_chain(const double *const *xs, const size_t *ns, const double *inits, size_t count,
                 double *outs, void *ws, hipStream_t stream, uint32_t flags, exseq_stats *stats)
 {
+    const size_t plan_bytes = batch_plan_bytes(ns, count);
+    char *work = static_cast<char *>(ws) + plan_bytes;
+    size_t tile_off = 0;
     for (size_t g = 0; g < count; g += kMaxBatch) {
         BatchArgs a{};
         a.count = (int)(count - g < (size_t)kMaxBatch ? count - g : (size_t)kMaxBatch);
@@ -187,7 +208,13 @@ int batch_chain(const double *const *xs, const size_t *ns, const double *inits, 
         if (chunks > 0xFFFFFFFFull)
             return EXSEQ_EINVAL;
         a.chunk_base[a.count] = (uint32_t)chunks;
-        const int rc = launch_batch(a, ws, outs + g, stream, stats ? stats + g : nullptr);
+        if (plan_bytes) {
+            a.plan_hdr_ext = static_cast<uint64_t *>(ws) + g;
+            a.plan_ext = reinterpret_cast<double *>(static_cast<char *>(ws) + round256(count * sizeof(uint64_t))) +
+                         tile_off;
+            tile_off += chunks / kTileMax + 1;
+        }
+        const int rc = launch_batch(a, plan_bytes ? work : ws, outs + g, stream, stats ? stats + g : nullptr);
         if (rc != EXSEQ_OK)
             return rc;
     }
@@ -205,7 +232,7 @@ size_t exact_seq_sum_f64_batch_workspace_size(const size_t *ns, size_t count)
             chunks += padded_chunks(ns[k]);
         mx = chunks > mx ? chunks : mx;
     }
-    size_t bytes = sum_ws_bytes(mx);
+    size_t bytes = (ns ? batch_plan_bytes(ns, count) : 0) + sum_ws_bytes(mx);
     for (size_t g = 0; ns && g < count; g += kPassMax) {
         const size_t m = count - g < (size_t)kPassMax ? count - g : (size_t)kPassMax;
         const size_t pb = exseq::pass_ws_bytes(exseq::pass_blocks(ns + g, m), m);

@@ -80,6 +80,12 @@ struct BatchArgs {
     float *means;
     // A launch of at most a few chunks: the walk alone adds them in order.
     uint32_t tiny;
+    // Nullable: where this launch keeps its plan (EXSEQ_PLAN_REUSE) when it is
+    // one group of a larger batch: per sum a tag, per tile of kTileMax chunks
+    // a prefix, at places of the batch's own that do not depend on the
+    // group's size (else they follow the launch's other arrays).
+    uint64_t *plan_hdr_ext;
+    double *plan_ext;
 };
 
 // Descriptors live in four arrays (structure of arrays, so that the walk

@@ -1051,7 +1051,11 @@ static int launch_batch_src(const BatchArgs &a, const Src &src, void *ws, double
             hipEventRecord(static_cast<hipEvent_t>(events[i]), stream);
     };
     const uint32_t total = a.chunk_base[a.count];  // a multiple of kTileMax
-    const WsParts p = carve(ws, total);
+    WsParts p = carve(ws, total);
+    if (a.plan_hdr_ext) {
+        p.ch.plan_hdr = a.plan_hdr_ext;
+        p.ch.plan = a.plan_ext;
+    }
     BatchArgs args = a;
     args.epoch = next_epoch();
     // Chunks per tile.  By default as many as keep the launch's tiles within

@@ -143,3 +143,39 @@ def test_ssim_sequence():
                                          3, flags=REUSE, ws=ws)
         assert same(float(gs.cpu()[0]), s), f
         assert int(gw.cpu()[0]) == wsum
+
+
+def test_batch_of_two_groups_keeps_both_plans():
+    """A batch of more than 64 sums through the tile chain runs as groups of
+    64 that share the workspace.  Each group keeps its plan at a place of its
+    own, so both groups take it: the plan of x, reused for 4x (every binade
+    two too low), is exact and adds many more chunks term by term in both
+    groups than the same call without the flag; the next call (whose kept
+    plans are 4x's own) is back to normal."""
+    torch = torch_cuda()
+    sizes = [150_000 + 1024 * (k % 7) for k in range(100)]
+    xs = [si.tie_heavy(n, 700 + k) for k, n in enumerate(sizes)]
+    need = ex.lib().exact_seq_sum_f64_batch_workspace_size(
+        (ctypes.c_size_t * len(sizes))(*sizes), len(sizes))
+    ws = ex.workspace(need, torch.device("cuda"))
+    fl = REUSE | ex.CHAIN_PATH
+    out = ex.exact_seq_sum_batch([to_dev(torch, a) for a in xs], flags=fl, ws=ws).cpu().tolist()
+    for k, (a, o) in enumerate(zip(xs, out)):
+        assert same(o, oracle.seq_sum(a)), k
+    ys = [4.0 * a for a in xs]
+    yd = [to_dev(torch, a) for a in ys]
+    want = oracle.seq_sum_many(ys)
+    _, st0 = ex.exact_seq_sum_batch(yd, flags=ex.CHAIN_PATH, stats=True)
+    for rep in range(2):
+        out, st = ex.exact_seq_sum_batch(yd, flags=fl, ws=ws, stats=True)
+        out = out.cpu().tolist()
+        for k in range(len(ys)):
+            assert same(out[k], want[k]), (rep, k)
+        for lo, hi in ((0, 64), (64, 100)):
+            fb = sum(s["fallback_chunks"] for s in st[lo:hi])
+            fb0 = sum(s["fallback_chunks"] for s in st0[lo:hi])
+            say("group", lo, "call", rep, "fallback chunks reuse", fb, "plain", fb0)
+            if rep == 0:
+                assert fb > fb0 + 50, (lo, fb, fb0)
+            else:
+                assert fb <= fb0 + 2 * (hi - lo), (lo, fb, fb0)
