@@ -138,6 +138,16 @@ __device__ __forceinline__ v2u64 load_coherent_16(const uint64_t *p)
     return *(gptr)(p);
 }
 
+// 16 bytes to device-coherent memory in one store (written through).
+__device__ __forceinline__ void store_coherent_16(uint64_t *p, uint64_t a, uint64_t b)
+{
+    typedef volatile __attribute__((address_space(1))) v2u64 *gptr;
+    v2u64 v;
+    v.x = a;
+    v.y = b;
+    *(gptr)(p) = v;
+}
+
 // Workspace of a pass launch (see pass_carve).
 struct PassWs {
     uint64_t *st;    // per tile: plan status word
@@ -1423,6 +1433,169 @@ __device__ __forceinline__ void level1(PassTileLds &L, const uint64_t *st, int p
     }
 }
 
+// The record of one sum's tile, whose chunks c0 .. c0 + nk - 1 have their
+// runs, keys and crossings in L at q0 .. q0 + nk - 1 (g: the tile in the
+// launch).  Every thread of the workgroup calls it; the tile's descriptor
+// stores are complete before any tagged word of its record.
+__device__ __forceinline__ void publish_tile(const PassWs &w, uint64_t tag, uint32_t g, PassTileLds &L, int q0,
+                                             int nk, bool regular, uint32_t found, size_t n, uint32_t c0)
+{
+    const int t = threadIdx.x;
+    uint64_t *trec = w.trec + 4 * (size_t)g;
+    if (regular) {
+        // The chunks' runs in order (plain ones add up), by lane 0, once
+        // every wave's descriptor stores are complete; then the record:
+        // the bounds of a run with a negative term, and once they are
+        // complete its first two words in one 16-byte store (every word
+        // carries bits of the launch tag).
+        stores_complete();
+        __syncthreads();
+        if (t == 0) {
+            Run tr = run_identity();
+            bool plain = true, fall = true;
+            int64_t sum = 0;
+            for (int k = 0; k < nk; k++) {
+                const WaveRun &q = L.join[q0 + k];
+                plain &= rising_run(q.p, q.flags);
+                fall &= falling_run(q.p, q.lo, q.hi, q.flags);
+                sum += q.p.r0;
+            }
+            if (plain) {
+                tr = Run{Pair{sum, sum}, 0, sum, 0u};
+            } else if (fall) {
+                tr = Run{Pair{sum, sum}, sum, 0, kFlagNeg};
+            } else {
+                for (int k = 0; k < nk; k++) {
+                    const WaveRun r = L.join[q0 + k];
+                    tr = run_compose_sat(tr, Run{r.p, r.lo, r.hi, r.flags});
+                }
+                if (!(tr.flags & kFlagNeg))
+                    tr.hi = run_top(tr);
+            }
+            // a run past the width of a binade never applies; bounded runs
+            // keep the finisher's sums over a window far from overflow
+            const int64_t lim = kCountLo + 1;
+            if (tr.p.r0 > lim || tr.p.r0 < -lim || tr.lo < -lim || tr.hi > lim) {
+                tr.flags |= kFlagBad;
+                tr.p = pair_identity();
+                tr.lo = tr.hi = 0;
+            }
+            if (tr.flags & kFlagNeg) {
+                store_coherent_16(trec + 2, rec_w1(tag, tr.lo), rec_w1(tag, tr.hi));
+                stores_complete();
+            }
+            store_coherent_16(trec, rec_w0(tag, kKindReg, tr.flags, tr.p.r1 - tr.p.r0, L.key[q0]),
+                              rec_w1(tag, tr.p.r0));
+        }
+        return;
+    }
+    // An irregular tile: its O(1) step -- the chunks before the first located
+    // crossing as one run A, then up to kMaxCross crossings, each with the
+    // chunks after it (in the next binade) folded into its rest-of-chunk
+    // run.  Built in LDS by lane 0.  Any other shape is walked by the
+    // finisher chunk by chunk.
+    bool fast = true;
+    uint32_t nfl = 0u;
+    if (t == 0) {
+        Run A = run_identity();
+        uint32_t akey = 0u;
+        int nx = 0;
+        uint32_t next_key = 0u;  // the binade the chunks after the last crossing are in
+        Run suf = run_identity();
+        Pair whole = pair_identity();
+        uint64_t *xr = nullptr;  // the current crossing's words in L.rec
+        for (int k = 0; k < nk; k++)
+            nfl |= L.join[q0 + k].flags & kFlagNonFinite;
+        auto close_crossing = [&]() {
+            const int64_t lim = (int64_t)1 << 56;
+            fast = fast && !(suf.flags & kFlagBad) && whole.r0 < lim && whole.r1 < lim &&
+                   whole.r0 > -lim && whole.r1 > -lim;
+            xr[1 + kXsuf] = enc_i64(rec_pack(suf.p));
+            xr[1 + kXsufLo] = enc_i64(suf.lo);
+            xr[1 + kXsufHi] = enc_i64(suf.hi);
+            xr[1 + kXwhole] = enc_i64(rec_pack(whole));
+            xr[0] |= (uint64_t)((suf.flags & kFlagNeg) ? 1u : 0u) << 13;
+        };
+        for (int k = 0; fast && k < nk; k++) {
+            const WaveRun &q = L.join[q0 + k];
+            const uint32_t kk = L.key[q0 + k];
+            if ((found >> k) & 1u) {
+                if (nx == kMaxCross || (nx == 0 ? (akey != 0u && akey != kk) : kk != next_key)) {
+                    fast = false;
+                    break;
+                }
+                if (nx > 0)
+                    close_crossing();
+                xr = L.rec + 4 + kXrecW * nx;
+                const bool down = L.down[q0 + k] != 0u;
+#pragma unroll
+                for (int c = 0; c < kCrossWords; c++)
+                    xr[1 + c] = L.xw[q0 + k][c];
+                xr[0] = (uint64_t)(kk & kKeyMask) | ((uint64_t)down << 12) |
+                        ((uint64_t)chunk_len(n, c0 + k) << 16);
+                suf = Run{rec_unpack(dec_i64(xr[1 + kXsuf])), dec_i64(xr[1 + kXsufLo]),
+                          dec_i64(xr[1 + kXsufHi]), q.flags & kFlagNeg};
+                whole = rec_unpack(dec_i64(xr[1 + kXwhole]));
+                next_key = down ? kk - 1u : kk + 1u;
+                nx++;
+                continue;
+            }
+            fast = key_has_fast_path(kk) && !(q.flags & (kFlagBad | kFlagNonFinite));
+            if (nx == 0) {
+                fast = fast && (akey == 0u || akey == kk);
+                A = run_compose_sat(A, Run{q.p, q.lo, q.hi, q.flags});
+                akey = kk;
+            } else {
+                fast = fast && kk == next_key;
+                suf = run_compose_sat(suf, Run{q.p, q.lo, q.hi, q.flags & kFlagNeg});
+                whole = compose(whole, q.p);
+            }
+        }
+        if (fast && nx > 0)
+            close_crossing();
+        fast = fast && (akey != 0u || nx > 0) && !(A.flags & kFlagBad);
+        // the run the tile ends with (the rest after its last crossing, or A
+        // without one) and its binade: published in the tile's record words
+        // so that the finisher composes the regular tiles after it with it
+        {
+            const bool lastdown = nx > 0 && ((L.rec[4 + kXrecW * (nx - 1)] >> 12) & 1u);
+            const Run ex = nx > 0 ? suf : A;
+            const bool neg = (ex.flags & kFlagNeg) || lastdown;
+            const int64_t lim = kCountLo + 1;
+            fast = fast && ex.p.r0 <= lim && ex.p.r0 >= -lim && ex.p.r1 <= lim && ex.p.r1 >= -lim &&
+                   (!neg || (ex.lo >= -lim && ex.hi <= lim));
+            L.xexit[0] = (uint64_t)(nx > 0 ? next_key : akey) | ((uint64_t)neg << 14) |
+                         ((uint64_t)(ex.p.r1 - ex.p.r0 + 1) << 32);
+            L.xexit[1] = rec_w1(tag, ex.p.r0);
+            L.xexit[2] = rec_w1(tag, ex.lo);
+            L.xexit[3] = rec_w1(tag, ex.hi);
+        }
+        L.rec[0] = (uint64_t)(akey & kKeyMask) | ((uint64_t)(akey != 0u) << 12) |
+                   ((uint64_t)nx << 13) | ((uint64_t)((A.flags >> 14) & 3u) << 15) |
+                   ((uint64_t)(A.p.r1 - A.p.r0 + 1) << 17);
+        L.rec[1] = enc_i64(A.p.r0);
+        L.rec[2] = enc_i64(A.lo);
+        L.rec[3] = enc_i64(A.hi);
+        L.lb_found = fast ? 1 : 0;  // reused: tells the other lanes
+    }
+    __syncthreads();
+    fast = L.lb_found != 0;
+    const bool xneg = ((L.xexit[0] >> 14) & 1u) != 0;
+    if (fast && t < kStepWords)
+        store_relaxed_u64(w.xrec + kStepWords * (size_t)g + t, L.rec[t]);
+    if (fast && t >= 64 && t < 64 + (xneg ? 3 : 1))
+        store_relaxed_u64(trec + (t - 63), L.xexit[t - 63]);
+    stores_complete();
+    __syncthreads();
+    if (t == 0) {
+        const uint64_t x0 = L.xexit[0];
+        const uint32_t shape = (uint32_t)(L.rec[0] >> 12) & 7u;  // A present, crossings
+        store_relaxed_u64(trec, fast ? rec_w0(tag, kKindStep, nfl | (xneg ? kFlagNeg : 0u),
+                                              (int64_t)(x0 >> 32) - 1, (uint32_t)x0 & kKeyMask, shape)
+                                     : rec_w0(tag, kKindSlow, nfl, 0, 0u));
+    }
+}
+
 template <class Src>
 __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, const PassWs &w,
                                            int s, uint32_t i, PassTileLds &L, WalkCore &sc,
@@ -1661,159 +1834,7 @@ __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, c
         __syncthreads();
 
     // ---- the tile's record
-    uint64_t *trec = w.trec + 4 * (size_t)g;
-    if (regular) {
-        // The chunks' runs in order (plain ones add up), by lane 0, once
-        // every wave's descriptor stores are complete; then the record's
-        // words go out together (each carries the launch tag).
-        stores_complete();
-        __syncthreads();
-        if (wave != 0)
-            return;
-        if (t == 0) {
-            Run tr = run_identity();
-            bool plain = true, fall = true;
-            int64_t sum = 0;
-            for (int k = 0; k < nk; k++) {
-                const WaveRun &q = L.join[k];
-                plain &= rising_run(q.p, q.flags);
-                fall &= falling_run(q.p, q.lo, q.hi, q.flags);
-                sum += q.p.r0;
-            }
-            if (plain) {
-                tr = Run{Pair{sum, sum}, 0, sum, 0u};
-            } else if (fall) {
-                tr = Run{Pair{sum, sum}, sum, 0, kFlagNeg};
-            } else {
-                for (int k = 0; k < nk; k++) {
-                    const WaveRun r = L.join[k];
-                    tr = run_compose_sat(tr, Run{r.p, r.lo, r.hi, r.flags});
-                }
-                if (!(tr.flags & kFlagNeg))
-                    tr.hi = run_top(tr);
-            }
-            // a run past the width of a binade never applies; bounded runs
-            // keep the finisher's sums over a window far from overflow
-            const int64_t lim = kCountLo + 1;
-            if (tr.p.r0 > lim || tr.p.r0 < -lim || tr.lo < -lim || tr.hi > lim) {
-                tr.flags |= kFlagBad;
-                tr.p = pair_identity();
-                tr.lo = tr.hi = 0;
-            }
-            store_relaxed_u64(trec + 1, rec_w1(tag, tr.p.r0));
-            if (tr.flags & kFlagNeg) {
-                store_relaxed_u64(trec + 2, rec_w1(tag, tr.lo));
-                store_relaxed_u64(trec + 3, rec_w1(tag, tr.hi));
-            }
-            store_relaxed_u64(trec, rec_w0(tag, kKindReg, tr.flags, tr.p.r1 - tr.p.r0, L.key[0]));
-        }
-        return;
-    }
-    // An irregular tile: its O(1) step -- the chunks before the first located
-    // crossing as one run A, then up to kMaxCross crossings, each with the
-    // chunks after it (in the next binade) folded into its rest-of-chunk
-    // run.  Built in LDS by lane 0.  Any other shape is walked by the
-    // finisher chunk by chunk.
-    bool fast = true;
-    uint32_t nfl = 0u;
-    if (t == 0) {
-        Run A = run_identity();
-        uint32_t akey = 0u;
-        int nx = 0;
-        uint32_t next_key = 0u;  // the binade the chunks after the last crossing are in
-        Run suf = run_identity();
-        Pair whole = pair_identity();
-        uint64_t *xr = nullptr;  // the current crossing's words in L.rec
-        for (int k = 0; k < nk; k++)
-            nfl |= L.join[k].flags & kFlagNonFinite;
-        auto close_crossing = [&]() {
-            const int64_t lim = (int64_t)1 << 56;
-            fast = fast && !(suf.flags & kFlagBad) && whole.r0 < lim && whole.r1 < lim &&
-                   whole.r0 > -lim && whole.r1 > -lim;
-            xr[1 + kXsuf] = enc_i64(rec_pack(suf.p));
-            xr[1 + kXsufLo] = enc_i64(suf.lo);
-            xr[1 + kXsufHi] = enc_i64(suf.hi);
-            xr[1 + kXwhole] = enc_i64(rec_pack(whole));
-            xr[0] |= (uint64_t)((suf.flags & kFlagNeg) ? 1u : 0u) << 13;
-        };
-        for (int k = 0; fast && k < nk; k++) {
-            const WaveRun &q = L.join[k];
-            const uint32_t kk = L.key[k];
-            if ((found >> k) & 1u) {
-                if (nx == kMaxCross || (nx == 0 ? (akey != 0u && akey != kk) : kk != next_key)) {
-                    fast = false;
-                    break;
-                }
-                if (nx > 0)
-                    close_crossing();
-                xr = L.rec + 4 + kXrecW * nx;
-                const bool down = L.down[k] != 0u;
-#pragma unroll
-                for (int c = 0; c < kCrossWords; c++)
-                    xr[1 + c] = L.xw[k][c];
-                xr[0] = (uint64_t)(kk & kKeyMask) | ((uint64_t)down << 12) |
-                        ((uint64_t)chunk_len(n, c0 + k) << 16);
-                suf = Run{rec_unpack(dec_i64(xr[1 + kXsuf])), dec_i64(xr[1 + kXsufLo]),
-                          dec_i64(xr[1 + kXsufHi]), q.flags & kFlagNeg};
-                whole = rec_unpack(dec_i64(xr[1 + kXwhole]));
-                next_key = down ? kk - 1u : kk + 1u;
-                nx++;
-                continue;
-            }
-            fast = key_has_fast_path(kk) && !(q.flags & (kFlagBad | kFlagNonFinite));
-            if (nx == 0) {
-                fast = fast && (akey == 0u || akey == kk);
-                A = run_compose_sat(A, Run{q.p, q.lo, q.hi, q.flags});
-                akey = kk;
-            } else {
-                fast = fast && kk == next_key;
-                suf = run_compose_sat(suf, Run{q.p, q.lo, q.hi, q.flags & kFlagNeg});
-                whole = compose(whole, q.p);
-            }
-        }
-        if (fast && nx > 0)
-            close_crossing();
-        fast = fast && (akey != 0u || nx > 0) && !(A.flags & kFlagBad);
-        // the run the tile ends with (the rest after its last crossing, or A
-        // without one) and its binade: published in the tile's record words
-        // so that the finisher composes the regular tiles after it with it
-        {
-            const bool lastdown = nx > 0 && ((L.rec[4 + kXrecW * (nx - 1)] >> 12) & 1u);
-            const Run ex = nx > 0 ? suf : A;
-            const bool neg = (ex.flags & kFlagNeg) || lastdown;
-            const int64_t lim = kCountLo + 1;
-            fast = fast && ex.p.r0 <= lim && ex.p.r0 >= -lim && ex.p.r1 <= lim && ex.p.r1 >= -lim &&
-                   (!neg || (ex.lo >= -lim && ex.hi <= lim));
-            L.xexit[0] = (uint64_t)(nx > 0 ? next_key : akey) | ((uint64_t)neg << 14) |
-                         ((uint64_t)(ex.p.r1 - ex.p.r0 + 1) << 32);
-            L.xexit[1] = rec_w1(tag, ex.p.r0);
-            L.xexit[2] = rec_w1(tag, ex.lo);
-            L.xexit[3] = rec_w1(tag, ex.hi);
-        }
-        L.rec[0] = (uint64_t)(akey & kKeyMask) | ((uint64_t)(akey != 0u) << 12) |
-                   ((uint64_t)nx << 13) | ((uint64_t)((A.flags >> 14) & 3u) << 15) |
-                   ((uint64_t)(A.p.r1 - A.p.r0 + 1) << 17);
-        L.rec[1] = enc_i64(A.p.r0);
-        L.rec[2] = enc_i64(A.lo);
-        L.rec[3] = enc_i64(A.hi);
-        L.lb_found = fast ? 1 : 0;  // reused: tells the other lanes
-    }
-    __syncthreads();
-    fast = L.lb_found != 0;
-    const bool xneg = ((L.xexit[0] >> 14) & 1u) != 0;
-    if (fast && t < kStepWords)
-        store_relaxed_u64(w.xrec + kStepWords * (size_t)g + t, L.rec[t]);
-    if (fast && t >= 64 && t < 64 + (xneg ? 3 : 1))
-        store_relaxed_u64(trec + (t - 63), L.xexit[t - 63]);
-    stores_complete();
-    __syncthreads();
-    if (t == 0) {
-        const uint64_t x0 = L.xexit[0];
-        const uint32_t shape = (uint32_t)(L.rec[0] >> 12) & 7u;  // A present, crossings
-        store_relaxed_u64(trec, fast ? rec_w0(tag, kKindStep, nfl | (xneg ? kFlagNeg : 0u),
-                                              (int64_t)(x0 >> 32) - 1, (uint32_t)x0 & kKeyMask, shape)
-                                     : rec_w0(tag, kKindSlow, nfl, 0, 0u));
-    }
+    publish_tile(w, tag, g, L, 0, nk, regular, found, n, c0);
 }
 
 // ---------------------------------------------------------------------------
