@@ -282,7 +282,9 @@ size_t exact_seq_sum_f64_interleaved_workspace_size(size_t windows, int k)
 {
     if (k < 1 || k > EXSEQ_INTERLEAVE_MAX)
         return 256;
-    return sum_ws_bytes((size_t)k * padded_chunks(windows));
+    const size_t chain = sum_ws_bytes((size_t)k * padded_chunks(windows));
+    const size_t pass = (k == 2 || k == 4) ? exseq::pass_ws_bytes(exseq::pass_inter_blocks(windows, k), (size_t)k) : 0;
+    return round256(chain > pass ? chain : pass);
 }
 
 int exact_seq_sum_f64_interleaved(const double *x, size_t windows, int k, const double *inits,

@@ -139,6 +139,10 @@ size_t pass_ws_bytes(size_t blocks, size_t sums);
 int launch_pass(const double *const *xs, const size_t *ns, const double *inits, int count,
                 uint32_t flags, void *ws, double *outs, hipStream_t stream, exseq_stats *stats,
                 void *const *events, int n_events);
+size_t pass_inter_blocks(size_t windows, int k);
+bool pass_inter_ok(size_t windows, int k, uint32_t flags);
+int launch_pass_interleaved(const double *x, size_t windows, int k, const double *inits, double *outs,
+                            float *means, void *ws, hipStream_t stream, uint32_t flags, exseq_stats *stats);
 extern const char *const kPathKernels[];
 extern const int kPathKernelCount;
 int launch_tree_sum(const double *x, size_t n, double *out, void *ws, hipStream_t stream);

@@ -95,13 +95,15 @@ constexpr uint32_t kKindLost = 4;    // finisher only: the record never came
 static_assert(kHeadCh == kTileMax, "a sum's first tile is one padding unit of chunks");
 
 // Tiles of a sum of nch chunks, and the first chunk of tile i.
-__host__ __device__ __forceinline__ uint32_t tiles_of(uint32_t nch)
+// (tch: chunks of a later tile of the sum; kTileCh except in a launch of
+// interleaved sums, whose tiles take 8 / k chunks of each of k sums)
+__host__ __device__ __forceinline__ uint32_t tiles_of(uint32_t nch, uint32_t tch = kTileCh)
 {
-    return nch == 0 ? 0u : nch <= (uint32_t)kHeadCh ? 1u : 1u + (nch - kHeadCh + kTileCh - 1) / kTileCh;
+    return nch == 0 ? 0u : nch <= (uint32_t)kHeadCh ? 1u : 1u + (nch - kHeadCh + tch - 1) / tch;
 }
-__host__ __device__ __forceinline__ uint32_t tile_c0(uint32_t i)
+__host__ __device__ __forceinline__ uint32_t tile_c0(uint32_t i, uint32_t tch = kTileCh)
 {
-    return i == 0 ? 0u : (uint32_t)kHeadCh + (uint32_t)kTileCh * (i - 1);
+    return i == 0 ? 0u : (uint32_t)kHeadCh + tch * (i - 1);
 }
 
 // First word of a tile record: tag | ext << 19 | kind << 17 | flags (neg,
@@ -168,6 +170,9 @@ struct PassWs {
 struct PassArgs {
     int count;
     uint32_t flags;
+    uint32_t tch;    // chunks of a sum's later tiles (kTileCh, or 8 / inter)
+    uint32_t inter;  // interleaved sums: k fields per record (x[s] = x[0] + s), else 0
+    float *means;    // nullable: means[s] = (float)(sum / n[s])
     uint32_t epoch;  // tags this launch's look-back status words
     uint64_t tag;    // this launch's record tag (42 bits, nonzero)
     double *outs;
@@ -198,9 +203,11 @@ struct PassTileLds {
     uint64_t xw[kTileCh][kCrossWords];
     uint64_t rec[kStepWords];
     uint64_t xexit[4];  // an irregular tile's last run: key etc., r0, lo, hi
-    double lb1, lb2;
-    int lb_found, lb_ok1, lb_ok2;
-    volatile int lb_stop;
+    // the look-back's results, one slot per sum of the workgroup (the
+    // interleaved tiles take up to four sums)
+    double lb1[4], lb2[4];
+    int lb_found[4], lb_ok1[4], lb_ok2[4];
+    volatile int lb_stop[4];
 };
 
 // The finisher composes the runs of a segment's tiles with an ordered
@@ -261,7 +268,7 @@ struct FinLds {
 
 // The workgroup's 32 KB of role-dependent LDS: a tile's last four chunks, the
 // head's chunk terms, or the finisher's window and chunk terms.
-constexpr int kUnionDoubles = kHalf * kChunk;
+constexpr int kUnionDoubles = kHalf * kChunk + 16;
 constexpr int kFinTermsOff = (int)((sizeof(FinLds) + 15) / 16 * 2);  // in doubles
 static_assert(kFinTermsOff + kChunk <= kUnionDoubles, "the finisher's LDS fits the union");
 
@@ -664,7 +671,7 @@ __device__ __forceinline__ void head_block(const PassArgs &pa, const Src &src, c
         return;
     }
     const uint32_t nch = chunks_of_n(n);
-    const uint32_t nt = tiles_of(nch);
+    const uint32_t nt = tiles_of(nch, pa.tch);
     const int nk = (int)(nch < (uint32_t)kHeadCh ? nch : (uint32_t)kHeadCh);
     const SumView v{a.x[s], n, a.init[s], a.chunk_base(s), nch};
     Four f[kHeadCh];
@@ -860,7 +867,7 @@ __device__ __forceinline__ void finisher_block(const PassArgs &pa, const Src &sr
     const int t = threadIdx.x, lane = lane_id(), wave = wave_id();
     const size_t n = a.n[s];
     const uint32_t nch = chunks_of_n(n);
-    const uint32_t nt = tiles_of(nch);
+    const uint32_t nt = tiles_of(nch, pa.tch);
     if (nt <= 1)
         return;  // the head wrote the result
     const SumView v{a.x[s], n, a.init[s], a.chunk_base(s), nch};
@@ -919,11 +926,13 @@ __device__ __forceinline__ void finisher_block(const PassArgs &pa, const Src &sr
         // records, polled until their tags show
         const uint32_t q0 = (uint32_t)(kFinLane * t);
         const size_t g0 = (size_t)(tb + base) + q0;
-        uint64_t w0[kFinLane], w1[kFinLane];
+        // (the bounds words of a run with a negative term are polled with
+        // the first two: all four words of a record in one round trip)
+        uint64_t w0[kFinLane], w1[kFinLane], w2[kFinLane], w3[kFinLane];
         bool got[kFinLane];
 #pragma unroll
         for (int j = 0; j < kFinLane; j++) {
-            w0[j] = w1[j] = 0;
+            w0[j] = w1[j] = w2[j] = w3[j] = 0;
             got[j] = q0 + (uint32_t)j >= cnt;
         }
         for (int spin = 0; spin <= kSpinLimit; spin++) {
@@ -932,11 +941,15 @@ __device__ __forceinline__ void finisher_block(const PassArgs &pa, const Src &sr
             for (int j = 0; j < kFinLane; j++) {
                 if (!got[j]) {
                     const v2u64 r = load_coherent_16(w.trec + 4 * (g0 + j));
+                    const v2u64 b = load_coherent_16(w.trec + 4 * (g0 + j) + 2);
                     w0[j] = r.x;
                     w1[j] = r.y;
+                    w2[j] = b.x;
+                    w3[j] = b.y;
                     const uint32_t kd = (uint32_t)(r.x >> 17) & 3u;
-                    got[j] = (r.x >> kTagShift) == tag &&
-                             ((kd != kKindReg && kd != kKindStep) || rec_w1_ok(tag, r.y));
+                    const bool runs = kd == kKindReg || kd == kKindStep;
+                    got[j] = (r.x >> kTagShift) == tag && (!runs || rec_w1_ok(tag, r.y)) &&
+                             (!runs || !(r.x & kFlagNeg) || (rec_w1_ok(tag, b.x) && rec_w1_ok(tag, b.y)));
                     all &= got[j];
                 }
             }
@@ -964,22 +977,9 @@ __device__ __forceinline__ void finisher_block(const PassArgs &pa, const Src &sr
                 rr[j].p = Pair{r0, r0 + (int64_t)((w0[j] >> kDrShift) & 3u) - 1};
                 rr[j].flags = (uint32_t)w0[j] & (kFlagNeg | kFlagBad);
                 if (rr[j].flags & kFlagNeg) {
-                    // a run with a negative term: its prefix bounds (tagged
-                    // words, written beside the first two)
-                    v2u64 b{0, 0};
-                    for (int spin = 0; spin <= kSpinLimit; spin++) {
-                        b = load_coherent_16(w.trec + 4 * (g0 + j) + 2);
-                        if (rec_w1_ok(tag, b.x) && rec_w1_ok(tag, b.y))
-                            break;
-                        __builtin_amdgcn_s_sleep(2);
-                    }
-                    if (rec_w1_ok(tag, b.x) && rec_w1_ok(tag, b.y)) {
-                        rr[j].lo = rec_w1_r0(b.x);
-                        rr[j].hi = rec_w1_r0(b.y);
-                    } else {
-                        // never arrived: a run that applies nowhere
-                        rr[j].flags |= kFlagBad;
-                    }
+                    // a run with a negative term: its prefix bounds
+                    rr[j].lo = rec_w1_r0(w2[j]);
+                    rr[j].hi = rec_w1_r0(w3[j]);
                 } else {
                     // rising along either start parity: the largest prefix is
                     // the total
@@ -1147,8 +1147,8 @@ __device__ __forceinline__ void finisher_block(const PassArgs &pa, const Src &sr
                 const uint32_t kind = kk_kind(hw);
                 const int o0 = F.opoff[qs];
                 const int n_op = kk_ops(hw);
-                const uint32_t c_lo = tile_c0(base + qs);
-                const uint32_t c_end = tile_c0(base + q + 1);
+                const uint32_t c_lo = tile_c0(base + qs, pa.tch);
+                const uint32_t c_end = tile_c0(base + q + 1, pa.tch);
                 const uint64_t range = (uint64_t)c_lo | (uint64_t)(c_end < nch ? c_end : nch) << 32;
                 const int slot = (int)(hw >> kKkSlot) - 1;
                 if (kind == kKindReg || (kind == kKindStep && slot >= 0)) {
@@ -1258,6 +1258,8 @@ __device__ __forceinline__ void finisher_block(const PassArgs &pa, const Src &sr
     }
     if (t == 0) {
         pa.outs[s] = S;
+        if (pa.means)
+            pa.means[s] = (float)(S / (double)n);  // ADR-1464: (float)(sum / windows)
         if (pa.stats) {
             const FinTally &ft = F.tally;
             exseq_stats st;
@@ -1417,17 +1419,17 @@ __device__ __forceinline__ WaveRun chunk_run(const Four *g, uint32_t key)
 // tile from the tile words of its group (into L); the group's last tile
 // publishes the group's sum (or its inclusive prefix) as soon as known.
 __device__ __forceinline__ void level1(PassTileLds &L, const uint64_t *st, int pg, uint32_t lg, uint32_t epoch,
-                                       uint64_t *gs0, double Ttile)
+                                       uint64_t *gs0, double Ttile, int slot = 0)
 {
     double v1;
     bool ok1;
     const bool found = lb_level1(st, pg, epoch, v1, ok1);
     if (lane_id() == 0) {
-        L.lb1 = v1;
-        L.lb_found = found;
-        L.lb_ok1 = ok1;
+        L.lb1[slot] = v1;
+        L.lb_found[slot] = found;
+        L.lb_ok1[slot] = ok1;
         if (found || lg == 0)
-            L.lb_stop = 1;
+            L.lb_stop[slot] = 1;
         if (pg == (int)kGroup - 1 && ok1)
             store_relaxed_u64(gs0 + lg, st_pack(epoch, found ? kStIncl : kStAgg, v1 + Ttile));
     }
@@ -1437,56 +1439,63 @@ __device__ __forceinline__ void level1(PassTileLds &L, const uint64_t *st, int p
 // runs, keys and crossings in L at q0 .. q0 + nk - 1 (g: the tile in the
 // launch).  Every thread of the workgroup calls it; the tile's descriptor
 // stores are complete before any tagged word of its record.
+// A regular tile's record, by one lane, once the tile's descriptor stores
+// are complete: the chunks' runs in order (plain ones add up), then the
+// bounds of a run with a negative term, and once they are complete its
+// first two words in one 16-byte store (every word carries bits of the
+// launch tag).
+__device__ __forceinline__ void reg_record(const PassWs &w, uint64_t tag, uint32_t g, const PassTileLds &L,
+                                       int q0, int nk)
+{
+    uint64_t *trec = w.trec + 4 * (size_t)g;
+    Run tr = run_identity();
+    bool plain = true, fall = true;
+    int64_t sum = 0;
+    for (int k = 0; k < nk; k++) {
+        const WaveRun &q = L.join[q0 + k];
+        plain &= rising_run(q.p, q.flags);
+        fall &= falling_run(q.p, q.lo, q.hi, q.flags);
+        sum += q.p.r0;
+    }
+    if (plain) {
+        tr = Run{Pair{sum, sum}, 0, sum, 0u};
+    } else if (fall) {
+        tr = Run{Pair{sum, sum}, sum, 0, kFlagNeg};
+    } else {
+        for (int k = 0; k < nk; k++) {
+            const WaveRun r = L.join[q0 + k];
+            tr = run_compose_sat(tr, Run{r.p, r.lo, r.hi, r.flags});
+        }
+        if (!(tr.flags & kFlagNeg))
+            tr.hi = run_top(tr);
+    }
+    // a run past the width of a binade never applies; bounded runs
+    // keep the finisher's sums over a window far from overflow
+    const int64_t lim = kCountLo + 1;
+    if (tr.p.r0 > lim || tr.p.r0 < -lim || tr.lo < -lim || tr.hi > lim) {
+        tr.flags |= kFlagBad;
+        tr.p = pair_identity();
+        tr.lo = tr.hi = 0;
+    }
+    if (tr.flags & kFlagNeg) {
+        store_coherent_16(trec + 2, rec_w1(tag, tr.lo), rec_w1(tag, tr.hi));
+        stores_complete();
+    }
+    store_coherent_16(trec, rec_w0(tag, kKindReg, tr.flags, tr.p.r1 - tr.p.r0, L.key[q0]),
+                      rec_w1(tag, tr.p.r0));
+}
+
 __device__ __forceinline__ void publish_tile(const PassWs &w, uint64_t tag, uint32_t g, PassTileLds &L, int q0,
                                              int nk, bool regular, uint32_t found, size_t n, uint32_t c0)
 {
     const int t = threadIdx.x;
     uint64_t *trec = w.trec + 4 * (size_t)g;
     if (regular) {
-        // The chunks' runs in order (plain ones add up), by lane 0, once
-        // every wave's descriptor stores are complete; then the record:
-        // the bounds of a run with a negative term, and once they are
-        // complete its first two words in one 16-byte store (every word
-        // carries bits of the launch tag).
+        // once every wave's descriptor stores are complete
         stores_complete();
         __syncthreads();
-        if (t == 0) {
-            Run tr = run_identity();
-            bool plain = true, fall = true;
-            int64_t sum = 0;
-            for (int k = 0; k < nk; k++) {
-                const WaveRun &q = L.join[q0 + k];
-                plain &= rising_run(q.p, q.flags);
-                fall &= falling_run(q.p, q.lo, q.hi, q.flags);
-                sum += q.p.r0;
-            }
-            if (plain) {
-                tr = Run{Pair{sum, sum}, 0, sum, 0u};
-            } else if (fall) {
-                tr = Run{Pair{sum, sum}, sum, 0, kFlagNeg};
-            } else {
-                for (int k = 0; k < nk; k++) {
-                    const WaveRun r = L.join[q0 + k];
-                    tr = run_compose_sat(tr, Run{r.p, r.lo, r.hi, r.flags});
-                }
-                if (!(tr.flags & kFlagNeg))
-                    tr.hi = run_top(tr);
-            }
-            // a run past the width of a binade never applies; bounded runs
-            // keep the finisher's sums over a window far from overflow
-            const int64_t lim = kCountLo + 1;
-            if (tr.p.r0 > lim || tr.p.r0 < -lim || tr.lo < -lim || tr.hi > lim) {
-                tr.flags |= kFlagBad;
-                tr.p = pair_identity();
-                tr.lo = tr.hi = 0;
-            }
-            if (tr.flags & kFlagNeg) {
-                store_coherent_16(trec + 2, rec_w1(tag, tr.lo), rec_w1(tag, tr.hi));
-                stores_complete();
-            }
-            store_coherent_16(trec, rec_w0(tag, kKindReg, tr.flags, tr.p.r1 - tr.p.r0, L.key[q0]),
-                              rec_w1(tag, tr.p.r0));
-        }
+        if (t == 0)
+            reg_record(w, tag, g, L, q0, nk);
         return;
     }
     // An irregular tile: its O(1) step -- the chunks before the first located
@@ -1576,10 +1585,10 @@ __device__ __forceinline__ void publish_tile(const PassWs &w, uint64_t tag, uint
         L.rec[1] = enc_i64(A.p.r0);
         L.rec[2] = enc_i64(A.lo);
         L.rec[3] = enc_i64(A.hi);
-        L.lb_found = fast ? 1 : 0;  // reused: tells the other lanes
+        L.lb_found[0] = fast ? 1 : 0;  // reused: tells the other lanes
     }
     __syncthreads();
-    fast = L.lb_found != 0;
+    fast = L.lb_found[0] != 0;
     const bool xneg = ((L.xexit[0] >> 14) & 1u) != 0;
     if (fast && t < kStepWords)
         store_relaxed_u64(w.xrec + kStepWords * (size_t)g + t, L.rec[t]);
@@ -1596,6 +1605,337 @@ __device__ __forceinline__ void publish_tile(const PassWs &w, uint64_t tag, uint
     }
 }
 
+// ---------------------------------------------------------------------------
+// Interleaved sums: k fields per record, field s of record r at x[r k + s]
+// (ADR-1464 "float_ssim_cuda adds its frame sums in the CPU's raster order,
+// on the host", Decision: the l*c*s, l, c, s sums of a pass), k = 2 or 4.
+// One workgroup takes the same tile of all k sums, 8 / k chunks of each, so
+// that every cache line of the records is read once, with 16-byte loads:
+// the tile's records go through LDS in two halves, written field by field,
+// and each wave takes two chunks of one sum (the first from registers, the
+// second from the LDS image).
+// ---------------------------------------------------------------------------
+struct PassStrided {
+    static constexpr int kLdsInts = 1;
+    static constexpr bool kInter = true;
+    uint32_t k;
+    // lane t's terms 4t .. 4t + 3 of chunk c of the sum viewed by v (+0.0
+    // past its end), for the head, the walks and a located crossing
+    __device__ __forceinline__ Four chunk_v(const SumView &v, size_t c, int *) const
+    {
+        const size_t first = c * kChunk + 4 * (size_t)threadIdx.x;
+        Four f;
+        f.cnt = first < v.n ? (int)(v.n - first < 4 ? v.n - first : 4) : 0;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            f.v[i] = i < f.cnt ? v.x[(first + (size_t)i) * k] : 0.0;
+        return f;
+    }
+};
+
+// Lane l's group-g terms of chunk c of a sum of interleaved terms (x: its
+// first term; stride k), read again from memory.
+__device__ __forceinline__ Four strided_wave_four(const double *x, size_t n, uint32_t k, size_t c, int g)
+{
+    const size_t first = c * kChunk + 256 * (size_t)g + 4 * (size_t)lane_id();
+    Four f;
+    f.cnt = 4;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        f.v[i] = first + (size_t)i < n ? x[(first + (size_t)i) * k] : 0.0;
+    return f;
+}
+
+// Four consecutive terms of an LDS image in natural order: this lane's
+// group g of a chunk (wave layout), or lane t's four (workgroup layout).
+__device__ __forceinline__ Four image_four(const double *base, size_t at)
+{
+    const double *p = base + at;
+    Four f;
+    f.v[0] = p[0];
+    f.v[1] = p[1];
+    f.v[2] = p[2];
+    f.v[3] = p[3];
+    f.cnt = 4;
+    return f;
+}
+
+template <class Src>
+__device__ __forceinline__ void inter_tile_block(const PassArgs &pa, const Src &src, const PassWs &w, uint32_t i,
+                                                 PassTileLds &L, WalkCore &sc, CrossLds &xl, double *stage,
+                                                 int *lds_src)
+{
+    const int K = (int)pa.inter, tch = (int)pa.tch, half = tch / 2;
+    const int t = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const size_t n = pa.n[0];  // every sum's length
+    const uint32_t nch = chunks_of_n(n);
+    const uint32_t c0 = tile_c0(i, (uint32_t)tch);
+    const int nk = (int)(nch - c0 < (uint32_t)tch ? nch - c0 : (uint32_t)tch);
+    const uint32_t mode = pa.flags & EXSEQ_PLAN_MASK;
+    const uint64_t tag = pa.tag;
+    const double *xb = pa.x[0];  // record 0, field 0
+    const int sw = wave / half;                 // this wave's sum
+    const int jr = wave % half, js = half + jr; // its chunks in the sum's tile
+    const int qr = sw * tch + jr, qs = sw * tch + js;  // their places in L
+    const int Fs = half * kChunk + 2;           // doubles per field of an LDS image
+    const bool lead = jr == 0;                  // the sum's first wave
+
+    if (t < 4)
+        L.lb_stop[t] = 0;
+    // ---- the terms: the tile's records in two halves, each read once with
+    // 16-byte loads and written to LDS field by field
+    const bool vec = ((reinterpret_cast<uintptr_t>(xb) & 15u) == 0u);
+    // all sixteen 16-byte loads of the thread requested at once (both
+    // halves), then each half through LDS
+    v2f64 ld[16];
+#pragma unroll
+    for (int m = 0; m < 16; m++) {
+        const size_t r0 = ((size_t)c0 + (size_t)(m >> 3) * (size_t)half) * kChunk;
+        const size_t d = 2 * (256 * (size_t)(m & 7) + (size_t)t);  // double of the half
+        const size_t rec = r0 + d / (size_t)K;
+        ld[m].x = 0.0;
+        ld[m].y = 0.0;
+        if (rec < n) {
+            const double *p = xb + r0 * (size_t)K + d;
+            if (vec) {
+                ld[m] = __builtin_nontemporal_load(reinterpret_cast<const v2f64 *>(p));
+            } else {
+                ld[m].x = p[0];
+                ld[m].y = p[1];
+            }
+        }
+    }
+    Four f[4];
+#pragma unroll
+    for (int ph = 0; ph < 2; ph++) {
+        if (ph)
+            __syncthreads();  // the first half's image has been read
+#pragma unroll
+        for (int m = 0; m < 8; m++) {
+            const size_t d = 2 * (256 * (size_t)m + (size_t)t);
+            const int rr = (int)(d / (size_t)K), fld = (int)(d % (size_t)K);
+            stage[fld * Fs + rr] = ld[8 * ph + m].x;
+            stage[(fld + 1) * Fs + rr] = ld[8 * ph + m].y;
+        }
+        __syncthreads();
+        if (ph == 0) {
+#pragma unroll
+            for (int g = 0; g < 4; g++)
+                f[g] = image_four(stage + sw * Fs + jr * kChunk, 256 * (size_t)g + 4 * (size_t)lane);
+        }
+    }
+    const double *img = stage + sw * Fs + jr * kChunk;  // this wave's second chunk
+    // ---- the chunk sums (fixed tree)
+    {
+        double ws[2];
+        ws[0] = jr < nk ? lane_tree(f) : 0.0;
+        Four q[4];
+#pragma unroll
+        for (int g = 0; g < 4; g++)
+            q[g] = image_four(img, 256 * (size_t)g + 4 * (size_t)lane);
+        ws[1] = js < nk ? lane_tree(q) : 0.0;
+        wave_sum_f64_n<2>(ws);
+        if (lane == 0) {
+            L.tsum[qr] = ws[0];
+            L.tsum[qs] = ws[1];
+        }
+    }
+    __syncthreads();
+    double Ttile = 0.0;
+    for (int j = 0; j < nk; j++)
+        Ttile += L.tsum[sw * tch + j];
+
+    // ---- the plan of this wave's sum, and its runs formed meanwhile
+    uint64_t *st0 = w.st + pa.tile_base(sw);
+    uint64_t *gs0 = w.gst + pa.group_base(sw);
+    const uint32_t lg = i / kGroup, pg = i % kGroup;
+    const bool lookback = mode != EXSEQ_PLAN_FIXED;
+    if (lookback && lead && lane == 0)
+        store_relaxed_u64(st0 + i, st_pack(pa.epoch, kStAgg, Ttile));
+    const bool last_in_group = lookback && pg == kGroup - 1;
+    if (last_in_group && lead)
+        level1(L, st0 + kGroup * lg, (int)pg, lg, pa.epoch, gs0, Ttile, sw);
+    const bool spec = lookback;
+    uint32_t gk[2] = {0u, 0u};
+    WaveRun run[2];
+    if (spec) {
+        const double mean = Ttile / (double)nk;
+        double pk = pa.init[sw] + (double)c0 * mean;
+        for (int j = 0; j < tch; j++) {
+            const uint32_t kk = (uint32_t)__builtin_amdgcn_readfirstlane((int)plan_key(pk, pa.flags));
+            if (j == jr)
+                gk[0] = kk;
+            if (j == js)
+                gk[1] = kk;
+            pk += L.tsum[sw * tch + j];
+        }
+        if (jr < nk)
+            run[0] = chunk_run(f, gk[0]);
+        if (js < nk) {
+            Four q[4];
+#pragma unroll
+            for (int g = 0; g < 4; g++)
+                q[g] = image_four(img, 256 * (size_t)g + 4 * (size_t)lane);
+            run[1] = chunk_run(q, gk[1]);
+        }
+    }
+    double P = pa.init[sw];
+    if (lookback) {
+        // the first level by the sum's first wave, the second by its second
+        // (the same wave where a sum has one)
+        if (lead && !last_in_group)
+            level1(L, st0 + kGroup * lg, (int)pg, lg, pa.epoch, gs0, Ttile, sw);
+        if (jr == (half > 1 ? 1 : 0)) {
+            bool ok2 = true;
+            double v2 = 0.0;
+            if (lg > 0)
+                v2 = lb_level2(gs0, lg, pa.epoch, &L.lb_stop[sw], ok2);
+            if (lane == 0) {
+                L.lb2[sw] = v2;
+                L.lb_ok2[sw] = ok2;
+            }
+        }
+        __syncthreads();
+        const bool found = L.lb_found[sw] != 0;
+        const bool ok = L.lb_ok1[sw] && (found || (lg > 0 && L.lb_ok2[sw]));
+        P = !ok ? __builtin_nan("") : (found ? L.lb1[sw] : L.lb2[sw] + L.lb1[sw]);
+        if (lead && lane == 0 && ok) {
+            store_relaxed_u64(st0 + i, st_pack(pa.epoch, kStIncl, P + Ttile));
+            if (pg == kGroup - 1)
+                store_relaxed_u64(gs0 + lg, st_pack(pa.epoch, kStIncl, P + Ttile));
+        }
+    }
+    // ---- the planned prefix and binade of this wave's chunks
+    uint32_t kc[2] = {0u, 0u};
+    {
+        double pk = P;
+        for (int j = 0; j < tch; j++) {
+            const double tk = L.tsum[sw * tch + j];
+            if (j == jr || j == js) {
+                const int h = j == js ? 1 : 0;
+                const int q = sw * tch + j;
+                const uint32_t ka = key_of(pk), kb = key_of(pk + tk);
+                const uint32_t kp = plan_key(pk, pa.flags);
+                if (h)
+                    kc[1] = kp;
+                else
+                    kc[0] = kp;
+                if (lane == 0) {
+                    L.pk[q] = pk;
+                    L.key[q] = kp;
+                    L.cross[q] = kb != ka;
+                    L.down[q] = ((kb ^ ka) & 0x800u) == 0u && (kb & 0x7FFu) < (ka & 0x7FFu);
+                }
+            }
+            pk += tk;
+        }
+    }
+    // ---- the runs not formed under the guess (the register chunk read
+    // again from memory)
+#pragma unroll 1
+    for (int h = 0; h < 2; h++) {
+        const int j = h ? js : jr;
+        const uint32_t kh = h ? kc[1] : kc[0];
+        if (j >= nk || (spec && (h ? gk[1] : gk[0]) == kh))
+            continue;
+        Four q[4];
+#pragma unroll
+        for (int g = 0; g < 4; g++)
+            q[g] = h ? image_four(img, 256 * (size_t)g + 4 * (size_t)lane)
+                     : strided_wave_four(xb + sw, n, (uint32_t)K, c0 + (uint32_t)jr, g);
+        const WaveRun r = chunk_run(q, kh);
+        if (h)
+            run[1] = r;
+        else
+            run[0] = r;
+    }
+    // ---- the binade edges and the descriptors (lane h: this wave's chunk h)
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (lane < 2 && (lane ? js : jr) < nk) {
+        const int h = lane, j = h ? js : jr, q = sw * tch + j;
+        const WaveRun r = h ? run[1] : run[0];
+        const uint32_t kk = L.key[q];
+        const double pk = L.pk[q];
+        const bool dn = L.down[q] != 0u;
+        bool cc = L.cross[q] != 0u;
+        if (key_has_fast_path(kk) && kk == key_of(pk)) {
+            const int64_t m = count_of(pk);
+            const int64_t mg = plan_margin(c0 + (uint32_t)j + 1);
+            bool near = m < count_floor(kk) + mg;
+            if (r.flags & kFlagNeg)
+                near |= m + r.lo - mg < kCountLo + 1 || m + r.hi + mg > kCountHi - 1;
+            else
+                near |= m + r.hi + mg > kCountHi;
+            cc |= near;
+        }
+        L.join[q] = r;
+        L.cross[q] = cc;
+        store_desc_coherent(w.d, (size_t)pa.chunk_base(sw) + c0 + (size_t)j, kk, r, cc ? kFlagCross : 0u);
+        L.locate[q] = cc && key_has_fast_path(kk) && kk == key_of(pk) &&
+                      key_has_fast_path(dn ? kk - 1u : kk + 1u) && !(r.flags & kFlagNonFinite);
+    }
+    __syncthreads();
+    // ---- per sum: its crossings located by the whole workgroup, and an
+    // irregular sum's record
+    uint32_t regmask = 0u;
+#pragma unroll 1
+    for (int s = 0; s < K; s++) {
+        const int q0 = s * tch;
+        uint32_t xmask = 0u;
+        bool regular = true;
+        for (int j = 0; j < nk; j++) {
+            const int q = q0 + j;
+            xmask |= L.locate[q] ? 1u << j : 0u;
+            regular &= key_has_fast_path(L.key[q]) && L.key[q] == L.key[q0] && !L.cross[q] &&
+                       !(L.join[q].flags & (kFlagBad | kFlagNonFinite));
+        }
+        xmask = (uint32_t)__builtin_amdgcn_readfirstlane((int)xmask);
+        regular = __builtin_amdgcn_readfirstlane((int)regular) != 0;
+        const SumView vs{xb + s, n, pa.init[s], pa.chunk_base(s), nch};
+        uint32_t found = 0u;
+        int buf = 0;
+#pragma unroll 1
+        for (int j = 0; j < nk; j++) {
+            if (!((xmask >> j) & 1u))
+                continue;
+            // the chunk's terms in the workgroup layout: from the LDS image
+            // (the tile's second half), else read again from memory
+            const int len = chunk_len(n, c0 + (size_t)j);
+            Four q;
+            if (j >= half) {
+                q = image_four(stage + s * Fs + (j - half) * kChunk, 4 * (size_t)t);
+                q.cnt = len - 4 * t >= 4 ? 4 : (len - 4 * t > 0 ? len - 4 * t : 0);
+            } else {
+                q = src.chunk_v(vs, c0 + (size_t)j, lds_src);
+            }
+            uint64_t xw[kCrossWords];
+            if (crossing_find(q, len, L.key[q0 + j], count_of(L.pk[q0 + j]), L.down[q0 + j] != 0u, sc, xl,
+                              buf, xw)) {
+                found |= 1u << j;
+                if (t == 0) {
+#pragma unroll
+                    for (int q2 = 0; q2 < kCrossWords; q2++)
+                        L.xw[q0 + j][q2] = xw[q2];
+                }
+            }
+        }
+        if (xmask)
+            __syncthreads();
+        if (!regular) {
+            publish_tile(w, tag, pa.tile_base(s) + i, L, q0, nk, false, found, n, c0);
+            __syncthreads();  // the next sum's record reuses L.rec
+        }
+        regmask |= regular ? 1u << s : 0u;
+    }
+    // the regular sums' records together: lane 0 of wave s for sum s, once
+    // the tile's descriptor stores are complete
+    stores_complete();
+    __syncthreads();
+    if (lane == 0 && wave < K && ((regmask >> wave) & 1u))
+        reg_record(w, tag, pa.tile_base(wave) + i, L, wave * tch, nk);
+}
+
 template <class Src>
 __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, const PassWs &w,
                                            int s, uint32_t i, PassTileLds &L, WalkCore &sc,
@@ -1605,7 +1945,7 @@ __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, c
     const int t = threadIdx.x, lane = lane_id(), wave = wave_id();
     const size_t n = a.n[s];
     const uint32_t nch = chunks_of_n(n);
-    const uint32_t c0 = tile_c0(i);
+    const uint32_t c0 = tile_c0(i, pa.tch);
     const int nk = (int)(nch - c0 < (uint32_t)kTileCh ? nch - c0 : (uint32_t)kTileCh);
     const uint32_t mode = a.flags & EXSEQ_PLAN_MASK;
     const uint64_t tag = pa.tag;
@@ -1615,7 +1955,7 @@ __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, c
     const int cr = 2 * wave, cs = 2 * wave + 1;       // this wave's chunks
 
     if (t == 0)
-        L.lb_stop = 0;
+        L.lb_stop[0] = 0;
     // ---- the terms: chunk cr into registers, chunk cs into LDS slot `wave`
     Four f[4];
 #pragma unroll
@@ -1713,16 +2053,16 @@ __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, c
             bool ok2 = true;
             double v2 = 0.0;
             if (lg > 0)
-                v2 = lb_level2(gs0, lg, a.epoch, &L.lb_stop, ok2);
+                v2 = lb_level2(gs0, lg, a.epoch, &L.lb_stop[0], ok2);
             if (lane == 0) {
-                L.lb2 = v2;
-                L.lb_ok2 = ok2;
+                L.lb2[0] = v2;
+                L.lb_ok2[0] = ok2;
             }
         }
         __syncthreads();
-        const bool found = L.lb_found != 0;
-        const bool ok = L.lb_ok1 && (found || (lg > 0 && L.lb_ok2));
-        P = !ok ? __builtin_nan("") : (found ? L.lb1 : L.lb2 + L.lb1);
+        const bool found = L.lb_found[0] != 0;
+        const bool ok = L.lb_ok1[0] && (found || (lg > 0 && L.lb_ok2[0]));
+        P = !ok ? __builtin_nan("") : (found ? L.lb1[0] : L.lb2[0] + L.lb1[0]);
         if (t == 0 && ok) {
             store_relaxed_u64(st0 + i, st_pack(a.epoch, kStIncl, P + Ttile));
             if (pg == kGroup - 1)
@@ -1849,17 +2189,31 @@ __global__ __launch_bounds__(kChunkThreads, 4) void pass_kernel(PassArgs pa, Src
     __shared__ __align__(16) double U[kUnionDoubles];
     __shared__ int lds_src[Src::kLdsInts];
     const PassArgs &a = pa;
-    // this block's sum: the last with block_base <= blockIdx.x
-    int lo = 0, hi = a.count - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (pa.block_base[mid] <= blockIdx.x)
-            lo = mid;
-        else
-            hi = mid - 1;
+    int s;
+    uint32_t b;
+    if constexpr (Src::kInter) {
+        // interleaved sums: every sum's head and finisher, then the tiles,
+        // each the same tile of all sums
+        const uint32_t k2 = 2u * a.inter;
+        if (blockIdx.x >= k2) {
+            inter_tile_block(pa, src, w, blockIdx.x - k2 + 1u, L, sc, xl, U, lds_src);
+            return;
+        }
+        s = (int)(blockIdx.x >> 1);
+        b = blockIdx.x & 1u;
+    } else {
+        // this block's sum: the last with block_base <= blockIdx.x
+        int lo = 0, hi = a.count - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pa.block_base[mid] <= blockIdx.x)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        s = lo;
+        b = blockIdx.x - pa.block_base[s];
     }
-    const int s = lo;
-    const uint32_t b = blockIdx.x - pa.block_base[s];
     // The head and the finisher are the sum's serial path; their waves go
     // first in issue on the SIMDs they share with streaming tiles.
     if (b <= 1)
@@ -1868,7 +2222,7 @@ __global__ __launch_bounds__(kChunkThreads, 4) void pass_kernel(PassArgs pa, Src
         head_block(pa, src, w, s, L, sc, U, lds_src);
     else if (b == 1)
         finisher_block(pa, src, w, s, *reinterpret_cast<FinLds *>(U), sc, U + kFinTermsOff, lds_src);
-    else
+    else if constexpr (!Src::kInter)
         tile_block(pa, src, w, s, b - 1, L, sc, xl, U, lds_src);
 }
 
@@ -1969,6 +2323,7 @@ int launch_pass(const double *const *xs, const size_t *ns, const double *inits, 
     PassArgs pa{};
     pa.count = count;
     pa.flags = flags;
+    pa.tch = kTileCh;
     pa.outs = outs;
     pa.stats = stats;
     uint32_t blocks = 0;
@@ -1989,6 +2344,51 @@ int launch_pass(const double *const *xs, const size_t *ns, const double *inits, 
                        stream, pa, PlainTerms{}, w);
     if (events && n_events > 1 && events[1])
         hipEventRecord(static_cast<hipEvent_t>(events[1]), stream);
+    return hipGetLastError() == hipSuccess ? EXSEQ_OK : EXSEQ_EHIP;
+}
+
+// Interleaved sums (k = 2 or 4 fields per record) in one launch: the k
+// heads and finishers, then one workgroup per tile of all k sums.
+size_t pass_inter_blocks(size_t windows, int k)
+{
+    const uint32_t nch = (uint32_t)((windows + kChunk - 1) / kChunk);
+    return (size_t)k * (1 + tiles_of(nch, (uint32_t)(kTileCh / k)));
+}
+
+bool pass_inter_ok(size_t windows, int k, uint32_t flags)
+{
+    return (k == 2 || k == 4) && pass_flags_ok(flags) && windows > 0 &&
+           (uint64_t)windows * (uint64_t)k > (uint64_t)2 * kTileMax * kChunk;
+}
+
+int launch_pass_interleaved(const double *x, size_t windows, int k, const double *inits, double *outs,
+                            float *means, void *ws, hipStream_t stream, uint32_t flags, exseq_stats *stats)
+{
+    if (!(k == 2 || k == 4) || windows == 0)
+        return EXSEQ_EINVAL;
+    PassArgs pa{};
+    pa.count = k;
+    pa.flags = flags;
+    pa.tch = (uint32_t)(kTileCh / k);
+    pa.inter = (uint32_t)k;
+    pa.means = means;
+    pa.outs = outs;
+    pa.stats = stats;
+    const uint32_t nch = (uint32_t)((windows + kChunk - 1) / kChunk);
+    const uint32_t nt = tiles_of(nch, pa.tch);
+    for (int s = 0; s < k; s++) {
+        pa.x[s] = x + s;
+        pa.n[s] = windows;
+        pa.init[s] = inits ? inits[s] : 0.0;
+        pa.block_base[s] = (uint32_t)s * (nt + 1);  // the workspace layout of each sum
+    }
+    pa.block_base[k] = (uint32_t)k * (nt + 1);
+    pa.tag = next_tag();
+    pa.epoch = (uint32_t)(pa.tag & 0xFFFFu) ? (uint32_t)pa.tag : (uint32_t)pa.tag + 1u;
+    const PassWs w = pass_carve(ws, pa.block_base[k], (size_t)k);
+    const unsigned grid = 2u * (unsigned)k + (nt > 1 ? nt - 1 : 0u);
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(pass_kernel<PassStrided>), dim3(grid), dim3(kChunkThreads), 0, stream,
+                       pa, PassStrided{(uint32_t)k}, w);
     return hipGetLastError() == hipSuccess ? EXSEQ_OK : EXSEQ_EHIP;
 }
 

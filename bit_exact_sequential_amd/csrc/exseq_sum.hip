@@ -1148,6 +1148,9 @@ int launch_interleaved(const double *x, size_t windows, int k, const double *ini
                        float *means, void *ws, hipStream_t stream, uint32_t flags,
                        exseq_stats *stats)
 {
+    // k = 2 or 4 fields: the single pass, each line of the records read once
+    if (pass_inter_ok(windows, k, flags))
+        return launch_pass_interleaved(x, windows, k, inits, outs, means, ws, stream, flags, stats);
     BatchArgs a{};
     a.count = k;
     a.flags = flags;

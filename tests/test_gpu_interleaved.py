@@ -43,24 +43,57 @@ def check(torch, x, k, inits=None, flags=0, means=True):
         assert np.array_equal(mt.cpu().numpy().view(np.uint32), wmeans.view(np.uint32))
 
 
+# both launch plans: the default (the single pass for k = 2 and 4, whose
+# tiles read every record line once; the tile chain otherwise) and the tile
+# chain forced
+PATHS = [0, ex.CHAIN_PATH]
+
+
 @pytest.mark.parametrize("windows", [0, 1, 3, 1023, 1024, 1025, 4096 * 3 + 7, 200_001])
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 8])
-def test_sizes(windows, k):
+@pytest.mark.parametrize("path", PATHS)
+def test_sizes(windows, k, path):
     torch = torch_cuda()
     x = records(windows, k, windows + 10 * k)
     inits = [0.5 * j for j in range(k)] if windows % 2 else None
-    check(torch, x, k, inits)
+    check(torch, x, k, inits, flags=path)
 
 
-def test_lcs_full_size():
+@pytest.mark.parametrize("path", PATHS)
+def test_lcs_full_size(path):
     """The LCS layout of a 3840x2160 frame: (l*c*s, l, c, s) per window."""
     torch = torch_cuda()
     x = si.lcs_records(si.FRAME_N, 0)
-    check(torch, x, 4)
+    check(torch, x, 4, flags=path)
 
 
-@pytest.mark.parametrize("flags", [ex.PLAN_ALL_FALLBACK, ex.PLAN_PLUS_ONE, ex.PLAN_MINUS_ONE,
-                                   ex.WALK_ONLY, 1 << 4, 2 << 4, 3 << 4, ex.CHAIN_CUT])
+@pytest.mark.parametrize("k", [2, 4])
+def test_records_not_16_byte_aligned(k):
+    """Records that start 8 bytes past a 16-byte boundary (the tiles then
+    read them with 8-byte loads)."""
+    torch = torch_cuda()
+    windows = 300_001
+    x = records(windows, k, 77 + k)
+    buf = torch.empty(x.size + 1, dtype=torch.float64, device="cuda")
+    buf[1:] = torch.from_numpy(x).cuda()
+    xd = buf[1:]
+    assert xd.data_ptr() % 16 == 8
+    sums, mt = ex.exact_seq_sum_interleaved(xd, k, None, means=True)
+    want, wmeans = oracle.seq_sum_interleaved(x, k)
+    got = sums.cpu().numpy()
+    for j in range(k):
+        assert same(got[j], want[j]), (k, j)
+    assert np.array_equal(mt.cpu().numpy().view(np.uint32), wmeans.view(np.uint32))
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_lcs_full_size_more_seeds(seed):
+    torch = torch_cuda()
+    check(torch, si.lcs_records(si.FRAME_N, seed), 4, inits=[0.0, 1.0, -1.0, 0.25])
+
+
+@pytest.mark.parametrize("flags", [ex.PLAN_ALL_FALLBACK, ex.PLAN_PLUS_ONE, ex.PLAN_MINUS_ONE, ex.PLAN_ALL_ZERO,
+                                   ex.plan_fixed(1023), ex.WALK_ONLY, 1 << 4, 2 << 4, 3 << 4, ex.CHAIN_CUT])
 def test_plan_and_chain_variants(flags):
     torch = torch_cuda()
     x = records(300_000, 4, 5)
