@@ -1679,6 +1679,19 @@ __device__ __forceinline__ void inter_tile_block(const PassArgs &pa, const Src &
     const int qr = sw * tch + jr, qs = sw * tch + js;  // their places in L
     const int Fs = half * kChunk + 2;           // doubles per field of an LDS image
     const bool lead = jr == 0;                  // the sum's first wave
+    // With four sums each wave holds all of its sum's chunks in the tile, and
+    // everything up to the records is the wave's own: its barriers are
+    // wave barriers.  With two, two waves share a sum and meet at the
+    // workgroup's.
+    const bool solo = half == 1;
+    auto sync = [&]() {
+        if (solo) {
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+        } else {
+            __syncthreads();
+        }
+    };
 
     if (t < 4)
         L.lb_stop[t] = 0;
@@ -1740,7 +1753,7 @@ __device__ __forceinline__ void inter_tile_block(const PassArgs &pa, const Src &
             L.tsum[qs] = ws[1];
         }
     }
-    __syncthreads();
+    sync();
     double Ttile = 0.0;
     for (int j = 0; j < nk; j++)
         Ttile += L.tsum[sw * tch + j];
@@ -1795,7 +1808,7 @@ __device__ __forceinline__ void inter_tile_block(const PassArgs &pa, const Src &
                 L.lb_ok2[sw] = ok2;
             }
         }
-        __syncthreads();
+        sync();
         const bool found = L.lb_found[sw] != 0;
         const bool ok = L.lb_ok1[sw] && (found || (lg > 0 && L.lb_ok2[sw]));
         P = !ok ? __builtin_nan("") : (found ? L.lb1[sw] : L.lb2[sw] + L.lb1[sw]);
@@ -1875,10 +1888,32 @@ __device__ __forceinline__ void inter_tile_block(const PassArgs &pa, const Src &
         L.locate[q] = cc && key_has_fast_path(kk) && kk == key_of(pk) &&
                       key_has_fast_path(dn ? kk - 1u : kk + 1u) && !(r.flags & kFlagNonFinite);
     }
-    __syncthreads();
+    // ---- a sum alone in its wave: its record at once when it is regular
+    // (its descriptors are this wave's stores)
+    uint32_t regmask = 0u;
+    bool done = false;
+    if (solo) {
+        sync();
+        bool reg = true;
+        for (int j = 0; j < nk; j++) {
+            const int q = sw * tch + j;
+            reg &= key_has_fast_path(L.key[q]) && L.key[q] == L.key[sw * tch] && !L.cross[q] &&
+                   !(L.join[q].flags & (kFlagBad | kFlagNonFinite));
+        }
+        if (reg) {
+            stores_complete();
+            if (lane == 0)
+                reg_record(w, tag, pa.tile_base(sw) + i, L, sw * tch, nk);
+        }
+        // the irregular sums, if any, by the whole workgroup
+        done = __syncthreads_or(reg ? 0 : 1) == 0;
+    } else {
+        __syncthreads();
+    }
+    if (done)
+        return;
     // ---- per sum: its crossings located by the whole workgroup, and an
     // irregular sum's record
-    uint32_t regmask = 0u;
 #pragma unroll 1
     for (int s = 0; s < K; s++) {
         const int q0 = s * tch;
@@ -1928,6 +1963,8 @@ __device__ __forceinline__ void inter_tile_block(const PassArgs &pa, const Src &
         }
         regmask |= regular ? 1u << s : 0u;
     }
+    if (solo)
+        return;  // (the regular sums' records are out)
     // the regular sums' records together: lane 0 of wave s for sum s, once
     // the tile's descriptor stores are complete
     stores_complete();
