@@ -237,10 +237,15 @@ def _lcs(ex, si, torch, dev, seed, reps, timed, res):
     x6 = torch.from_numpy(si.lcs_records(si.FRAME_N, seed)).to(dev)
     o6 = torch.empty(4, dtype=torch.float64, device=dev)
     w6 = ex.workspace(ex.lib().exact_seq_sum_f64_interleaved_workspace_size(si.FRAME_N, 4), dev)
-    ms = timed(lambda: ex.exact_seq_sum_interleaved(x6, 4, out=o6, ws=w6), reps)
+    ms = timed(lambda: ex.exact_seq_sum_interleaved(x6, 4, out=o6, ws=w6, means=True), reps)
+    gbs6 = 32 * si.FRAME_N / (ms * 1e-3) / 1e9
     res["lcs_interleaved_3840x2160"] = {"us_per_frame": ms * 1e3, "sums": 4,
-                                        "terms_per_s": 4 * si.FRAME_N / (ms * 1e-3),
-                                        "gbs": 32 * si.FRAME_N / (ms * 1e-3) / 1e9}
+                                        "terms_per_s": 4 * si.FRAME_N / (ms * 1e-3), "gbs": gbs6,
+                                        "roofline": {"bound": "hbm", "kernel": "pass_kernel<PassStrided>",
+                                                     "achieved": gbs6, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                                     "frac": gbs6 / HBM_PEAK_GBS,
+                                                     "note": "whole call (one launch: the four sums and their "
+                                                             "float means); bytes = the records read once"}}
     del x6
 
 
