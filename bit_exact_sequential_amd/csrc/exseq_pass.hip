@@ -2224,7 +2224,7 @@ __global__ __launch_bounds__(kChunkThreads, 4) void pass_kernel(PassArgs pa, Src
     __shared__ WalkCore sc;
     __shared__ CrossLds xl;
     __shared__ __align__(16) double U[kUnionDoubles];
-    __shared__ int lds_src[Src::kLdsInts];
+    __shared__ __attribute__((aligned(16))) int lds_src[Src::kLdsInts];
     const PassArgs &a = pa;
     int s;
     uint32_t b;

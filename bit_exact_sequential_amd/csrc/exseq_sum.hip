@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
     __shared__ WalkLds sh;
     __shared__ ChainLds cl;
     __shared__ CrossLds xl;
-    __shared__ int lds_src[Src::kLdsInts];
+    __shared__ __attribute__((aligned(16))) int lds_src[Src::kLdsInts];
     const bool chain = chain_on(a.flags);
     uint32_t gt = blockIdx.x;  // this block's tile
     if (chain) {
@@ -747,7 +747,7 @@ __global__ __launch_bounds__(kWalkThreads) void walk_kernel(BatchArgs a, Src src
                                                             exseq_stats *__restrict__ stats)
 {
     __shared__ WalkLds sh;
-    __shared__ int lds_src[Src::kLdsInts];
+    __shared__ __attribute__((aligned(16))) int lds_src[Src::kLdsInts];
     __shared__ unsigned long long st_fb, st_terms;
     __shared__ long long st_first;
     __shared__ unsigned st_nf;

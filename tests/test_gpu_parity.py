@@ -246,7 +246,8 @@ def test_ssim_small_frames(hw):
 
 
 @pytest.mark.parametrize("hwsr", [(40, 1088, 1088, 3), (33, 1100, 1100, 5), (21, 1057, 1057, 3),
-                                  (19, 1088, 1096, 15), (9, 2048, 2052, 0), (64, 1280, 1280, 1)],
+                                  (19, 1088, 1096, 15), (9, 2048, 2052, 0), (64, 1280, 1280, 1),
+                                  (24, 1280, 1284, 2), (17, 1104, 1104, 4), (12, 1536, 1540, 6)],
                          ids=lambda v: "%dx%d_s%d_r%d" % v)
 def test_ssim_wide_rows(hwsr):
     """Rows at least as wide as a chunk's span (the producer's one-division
@@ -263,6 +264,24 @@ def test_ssim_wide_rows(hwsr):
     r = torch.from_numpy(big_r).cuda()[:, :w]
     d = torch.from_numpy(big_d).cuda()[:, :w]
     gs, gw, gt = ex.ssim_term_and_sum(r, d, radius, want_terms=True)
+    assert np.array_equal(gt.cpu().numpy().view(np.uint64), terms.view(np.uint64))
+    assert same(float(gs.cpu()[0]), s)
+    assert int(gw.cpu()[0]) == wsum
+
+
+@pytest.mark.parametrize("radius", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("hw", [(37, 203), (16, 64), (9, 13)], ids=lambda s: "%dx%d" % s)
+def test_ssim_radius_small_frames(hw, radius):
+    """Narrow frames at every window radius up to five (the producer's
+    register windows take radii up to four, on pixels away from the row
+    ends; the rest add up their windows from LDS): every term and the sum
+    equal the oracle's."""
+    torch = torch_cuda()
+    h, w = hw
+    ref, dis = si.frame_pair(h, w, 31 * h + w + radius)
+    s, wsum, terms = oracle.ssim_frame_sum(ref, dis, radius, want_terms=True)
+    gs, gw, gt = ex.ssim_term_and_sum(torch.from_numpy(ref).cuda(), torch.from_numpy(dis).cuda(),
+                                      radius, want_terms=True)
     assert np.array_equal(gt.cpu().numpy().view(np.uint64), terms.view(np.uint64))
     assert same(float(gs.cpu()[0]), s)
     assert int(gw.cpu()[0]) == wsum
