@@ -102,6 +102,7 @@ struct SumView {
 struct PlainTerms {
     static constexpr int kLdsInts = 1;
     static constexpr bool kInter = false;  // the single pass: one sum per tile
+    static constexpr int kPassWaves = 4;   // the single pass: waves per SIMD it is built for
     __device__ __forceinline__ Four chunk_v(const SumView &v, size_t c, int *) const
     {
         return load_four(v.x, v.n, c * kChunk + 4 * (size_t)threadIdx.x, true);

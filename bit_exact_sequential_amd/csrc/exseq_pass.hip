@@ -1618,6 +1618,10 @@ __device__ __forceinline__ void publish_tile(const PassWs &w, uint64_t tag, uint
 struct PassStrided {
     static constexpr int kLdsInts = 1;
     static constexpr bool kInter = true;
+    // Three waves per SIMD: the interleaved tile's 16-byte record loads and
+    // field images need more registers than four waves leave, and spilling
+    // them costs more than the fourth wave gains.
+    static constexpr int kPassWaves = 3;
     uint32_t k;
     // lane t's terms 4t .. 4t + 3 of chunk c of the sum viewed by v (+0.0
     // past its end), for the head, the walks and a located crossing
@@ -2218,7 +2222,7 @@ __device__ __forceinline__ void tile_block(const PassArgs &pa, const Src &src, c
 // The kernel: per sum, its head, its finisher, then its later tiles
 // ---------------------------------------------------------------------------
 template <class Src>
-__global__ __launch_bounds__(kChunkThreads, 4) void pass_kernel(PassArgs pa, Src src, PassWs w)
+__global__ __launch_bounds__(kChunkThreads, Src::kPassWaves) void pass_kernel(PassArgs pa, Src src, PassWs w)
 {
     __shared__ PassTileLds L;
     __shared__ WalkCore sc;
