@@ -1,6 +1,11 @@
 """Build libexseq.so in-tree with hipcc for gfx950.
 
-    python -m bit_exact_sequential_amd.build
+    python -m bit_exact_sequential_amd.build              # the library
+    python -m bit_exact_sequential_amd.build --timeline   # its diagnostic twin
+
+The diagnostic twin, libexseq_timeline.so, is the same sources with
+EXSEQ_TIMELINE defined: the exact chain's tiles record the GPU's real-time
+counter at their steps (read by ``python -m bit_exact_sequential_amd.timeline``).
 
 Every HIP translation unit is compiled with -ffp-contract=off (no multiply
 is ever fused into an add: the SSIM term is defined with one rounding per
@@ -44,30 +49,37 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+TIMELINE_BUILD = os.path.join(HERE, "_build_timeline")
+TIMELINE_LIB = os.path.join(HERE, "libexseq_timeline.so")
+
+
+def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *COMMON, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed on %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, timeline: bool = False) -> str:
+    build_dir, lib, extra = BUILD, LIB, ()
+    if timeline:
+        build_dir, lib, extra = TIMELINE_BUILD, TIMELINE_LIB, ("-DEXSEQ_TIMELINE",)
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda src: _compile(src, build_dir, extra), SOURCES))
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", lib)
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, timeline="--timeline" in sys.argv[1:])
     sys.exit(0)

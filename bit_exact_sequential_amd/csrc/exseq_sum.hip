@@ -76,6 +76,42 @@
 #include "exseq_wave.h"
 #include "exseq_dev.h"
 
+// The diagnostic build (-DEXSEQ_TIMELINE, libexseq_timeline.so) records the
+// 100 MHz real-time counter at the steps of the exact chain's tiles, for the
+// host to read back (exseq_timeline_read): per tile, words 0-9 of its 12 are
+// its start, its plan, its runs, its record (regular) or its look-back
+// (irregular), 1 for an irregular tile, the look-back's end, the exact sum's
+// arrival, its own exact sum, and its last crossing search's start and end;
+// then two words per sum for its head.  Tiles past the array are not
+// recorded.  The product build compiles every stamp away.
+#ifdef EXSEQ_TIMELINE
+namespace exseq {
+constexpr uint32_t kTlTiles = 16384;
+constexpr uint32_t kTlPer = 12;
+constexpr uint32_t kTlWords = kTlPer * kTlTiles + 2 * kMaxBatch;
+__device__ uint64_t exseq_timeline[kTlWords];
+}  // namespace exseq
+#define EXSEQ_TL(tile, slot, v)                                                   \
+    do {                                                                           \
+        if (threadIdx.x == 0 && (uint32_t)(tile) < kTlTiles)                       \
+            exseq_timeline[kTlPer * (uint32_t)(tile) + (slot)] = (v);              \
+    } while (0)
+#define EXSEQ_TL_HEAD(s, slot)                                                    \
+    do {                                                                           \
+        if (threadIdx.x == 0 && (uint32_t)(s) < (uint32_t)kMaxBatch)               \
+            exseq_timeline[kTlPer * kTlTiles + 2 * (uint32_t)(s) + (slot)] =       \
+                __builtin_amdgcn_s_memrealtime();                                  \
+    } while (0)
+#define EXSEQ_TL_NOW() __builtin_amdgcn_s_memrealtime()
+#else
+#define EXSEQ_TL(tile, slot, v) \
+    do {                        \
+    } while (0)
+#define EXSEQ_TL_HEAD(s, slot) \
+    do {                       \
+    } while (0)
+#endif
+
 namespace exseq {
 
 
@@ -132,7 +168,9 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
             if (gt == ~0u)
                 return;
         } else if (gt < 2u * (uint32_t)a.count) {
+            EXSEQ_TL_HEAD(gt - (uint32_t)a.count, 0);
             chain_head(src, a, (int)(gt - (uint32_t)a.count), ch, d, sh, lds_src);
+            EXSEQ_TL_HEAD(gt - (uint32_t)a.count, 1);
             return;
         } else {
             const uint32_t r = gt - 2u * (uint32_t)a.count;
@@ -173,6 +211,7 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
     const uint32_t mode = a.flags & EXSEQ_PLAN_MASK;
     const int t = threadIdx.x, lane = lane_id(), wave = wave_id();
     const uint32_t tl = c0 / CPB;               // tile index within the sum
+    EXSEQ_TL(gt, 0, EXSEQ_TL_NOW());
     const uint32_t tb = a.chunk_base[s] / CPB;  // the sum's first tile in the launch
     // A sum's first tile heads the exact chain: its waves go first in the
     // instruction arbitration of their SIMDs, ahead of streaming tiles.
@@ -258,6 +297,7 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
     }
     __syncthreads();
 
+    EXSEQ_TL(gt, 1, EXSEQ_TL_NOW());
     // ---- every chunk's run under its planned binade
     uint32_t key[CPB];
     bool allfast = true;
@@ -344,6 +384,7 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
         return;
     }
 
+    EXSEQ_TL(gt, 2, EXSEQ_TL_NOW());
     // ---- the exact chain ----------------------------------------------------
     uint64_t *agg = ch.agg + 4 * (size_t)(tb + tl);
     bool regular = c0 != 0 && c0 + CPB < nch;
@@ -383,8 +424,10 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
                                            ((uint64_t)(dr + 1) << kDrShift) |
                                            (uint64_t)(tr.flags & kFlagNeg));
         }
+        EXSEQ_TL(gt, 3, EXSEQ_TL_NOW());
         return;
     }
+    EXSEQ_TL(gt, 4, 1);
     // An irregular tile: located crossings, the composed run of the regular
     // tiles back to the nearest irregular one, that tile's exact sum, then
     // this tile's chunks in order from it.
@@ -422,12 +465,14 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
         // the terms again (from cache, most likely): irregular tiles are few,
         // and not keeping every chunk's terms in registers this far keeps
         // the register count of all tiles down
+        EXSEQ_TL(gt, 8, EXSEQ_TL_NOW());
         const Four fr = src.chunk(a, s, c0 + k, lds_src);
         const size_t b = (size_t)(c0 + k) * kChunk;
         const int len = (int)(n - b < (size_t)kChunk ? n - b : (size_t)kChunk);
         uint64_t w[kCrossWords];
         if (crossing_find(fr, len, L.key[k], count_of(L.pk[k]), L.down[k] != 0u, sh, xl, buf, w)) {
             found |= 1u << k;
+            EXSEQ_TL(gt, 9, EXSEQ_TL_NOW());
             if (t == 0) {
 #pragma unroll
                 for (int i = 0; i < kCrossWords; i++)
@@ -477,7 +522,9 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
         int64_t xp = -1;
         int st = kBackOk;
         if (c0 != 0) {
+            EXSEQ_TL(gt, 3, EXSEQ_TL_NOW());
             st = chain_back(ch, tb, tl, sh, cl, buf, acc, key0, xp);
+            EXSEQ_TL(gt, 5, EXSEQ_TL_NOW());
             if ((a.flags & EXSEQ_CHAIN_CUT) && tl >= ((nch + CPB - 1) / CPB) / 2 && st == kBackOk)
                 st = kBackBad;  // a test hook: the chain stops here
         }
@@ -588,6 +635,7 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
                 w = uniform_u64(catch_up(ch, tb, xp, wave == 0));
             }
             ok = w > kInclFailed;  // 0: the wait timed out
+            EXSEQ_TL(gt, 6, EXSEQ_TL_NOW());
             if (ok)
                 S = bitsd(w ^ kInclXor);
             if (ok && fast && tile_step(akey, A, kx < nk, xw, xlen, xkey, xfl, xdown, S))
@@ -647,6 +695,7 @@ __global__ __launch_bounds__(kChunkThreads) void tile_kernel(BatchArgs a, Src sr
     }
     if (t == 0) {
         store_relaxed_u64(ch.incl + tb + tl, ok ? enc_sum(S) : kInclFailed);
+        EXSEQ_TL(gt, 7, EXSEQ_TL_NOW());
 #pragma unroll
         for (int k = 0; k < CPB; k++)
             if ((resolved >> k) & 1u)
@@ -1230,3 +1279,26 @@ int launch_tree_sum(const double *x, size_t n, double *out, void *ws, hipStream_
 }
 
 }  // namespace exseq
+
+#ifdef EXSEQ_TIMELINE
+// The diagnostic build's read-back of the stamps (words: how many to copy,
+// at most the array's size) and their reset; both synchronous.
+extern "C" int exseq_timeline_read(uint64_t *host, size_t words)
+{
+    if (!host || words > exseq::kTlWords)
+        return EXSEQ_EINVAL;
+    return hipMemcpyFromSymbol(host, HIP_SYMBOL(exseq::exseq_timeline), words * 8, 0,
+                               hipMemcpyDeviceToHost) == hipSuccess
+               ? EXSEQ_OK
+               : EXSEQ_EHIP;
+}
+extern "C" int exseq_timeline_clear(void)
+{
+    static uint64_t zeros[exseq::kTlWords];
+    return hipMemcpyToSymbol(HIP_SYMBOL(exseq::exseq_timeline), zeros, sizeof zeros, 0,
+                             hipMemcpyHostToDevice) == hipSuccess
+               ? EXSEQ_OK
+               : EXSEQ_EHIP;
+}
+extern "C" size_t exseq_timeline_words(void) { return exseq::kTlWords; }
+#endif
