@@ -220,17 +220,25 @@ def _ssim(ex, si, torch, dev, seed, reps, timed, res):
     d4 = torch.from_numpy(dis).to(dev)
     w4 = ex.workspace(ex.lib().ssim_term_and_sum_workspace_size(si.FRAME_W, si.FRAME_H), dev)
     ms = timed(lambda: ex.ssim_term_and_sum(r4, d4, 3, ws=w4), reps)
+    ms_tiles = timed(lambda: ex.ssim_term_and_sum(r4, d4, 3, ws=w4, flags=ex.SSIM_IN_TILES), reps)
     tflops = SSIM_TERM_FLOPS * si.FRAME_N / (ms * 1e-3) / 1e12
     res["fused_ssim_3840x2160"] = {"us_per_frame": ms * 1e3,
                                    "pixels_per_s": si.FRAME_N / (ms * 1e-3),
                                    "plane_gbs": 2 * si.FRAME_N / (ms * 1e-3) / 1e9,
-                                   "roofline": {"bound": "alu", "kernel": "tile_kernel<SsimTerms>",
+                                   "terms_in_tiles_us_per_frame": ms_tiles * 1e3,
+                                   "note": "default: the term producer (windows sliding down the rows) "
+                                           "into the workspace, then the exact sum; "
+                                           "terms_in_tiles: EXSEQ_SSIM_IN_TILES, the sum's tiles form "
+                                           "the terms",
+                                   "roofline": {"bound": "alu",
+                                                "kernel": "ssim_terms_rows_kernel + tile_kernel<PlainTerms>",
                                                 "achieved": tflops, "peak": FP64_VALU_PEAK_TFLOPS,
                                                 "unit": "TFLOP/s", "frac": tflops / FP64_VALU_PEAK_TFLOPS,
                                                 "flops_per_pixel": SSIM_TERM_FLOPS,
                                                 "note": "fp64 operations of the terms only (the "
-                                                        "window moments are integer work); peak = "
-                                                        "256 CUs x 4 SIMDs x 16 lanes x 2 x 2.4 GHz"}}
+                                                        "window moments are integer work) over the "
+                                                        "whole call; peak = 256 CUs x 4 SIMDs x 16 "
+                                                        "lanes x 2 x 2.4 GHz"}}
 
 
 def _lcs(ex, si, torch, dev, seed, reps, timed, res):

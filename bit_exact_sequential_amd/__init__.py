@@ -39,6 +39,7 @@ CHAIN_CUT = 1 << 7
 PLAN_REUSE = 1 << 20
 CHAIN_PATH = 1 << 21
 PASS_PATH = 1 << 22
+SSIM_IN_TILES = 1 << 23
 
 
 def tile_flag(chunks_per_tile: int) -> int:

@@ -101,7 +101,7 @@ __device__ __forceinline__ void window_sums4(const int *lds, int plane, int kb, 
     static_assert(R >= 0 && R <= 4, "the lane's twelve positions hold windows of radius 4 at most");
 #pragma unroll
     for (int m = 0; m < 5; m++) {
-        const int4 *q = reinterpret_cast<const int4 *>(lds + m * plane + kb);
+        const int4 *q = reinterpret_cast<const int4 *>(__builtin_assume_aligned(lds + m * plane + kb, 16));
         const int4 a = q[0], b = q[1], c = q[2];
         const int v[12] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w, c.x, c.y, c.z, c.w};
         int acc = v[4];
@@ -134,6 +134,14 @@ struct SsimTerms {
     static_assert(kPlane % 4 == 0 && kLead % 4 == 0 && kLead >= kMaxRadius, "aligned planes");
 
     __device__ __forceinline__ Four chunk(const BatchArgs &, int, size_t c, int *lds_in) const
+    {
+        return chunk_at(c, lds_in);
+    }
+
+    // The terms of chunk c (pixels 1024 c .. 1024 c + 1023 in raster order),
+    // lane t holding pixels 4t .. 4t + 3.  Block-level: every lane calls it
+    // with the same chunk (two barriers).
+    __device__ __forceinline__ Four chunk_at(size_t c, int *lds_in) const
     {
         int *lds = static_cast<int *>(__builtin_assume_aligned(lds_in, 16));
         const int t = threadIdx.x;

@@ -128,6 +128,15 @@ enum {
  * than the default. */
 #define EXSEQ_PLAN_REUSE (1u << 20)
 
+/* EXSEQ_SSIM_IN_TILES (ssim_term_and_sum only): the exact sum's tiles form
+ * the terms as they need them (no term is stored unless asked for).  Without
+ * it the terms are formed by a producer launch into device memory (the
+ * caller's out_terms plane, else the workspace: 8 bytes per pixel), then
+ * added by the exact sum of exact_seq_sum_f64 (every other flag applies to
+ * that sum).  Both give the same bits; the producer's windows slide down the
+ * rows, which the tiles' raster chunks cannot. */
+#define EXSEQ_SSIM_IN_TILES (1u << 23)
+
 /* Device-side statistics of one sum (written when the walk finishes). */
 typedef struct exseq_stats {
     uint64_t chunks;          /* chunks walked */
@@ -220,7 +229,8 @@ int exact_seq_sum_f64_interleaved(const double *x, size_t windows, int k,
 
 /* ---------------------------------------------------------------------------
  * ssim_term_and_sum
- *   Fused integer-SSIM frame sum.  For every pixel (i, j) of two 8-bit planes
+ *   Integer-SSIM frame sum, terms formed on the device from the planes
+ *   (EXSEQ_SSIM_IN_TILES: inside the sum's tiles).  For every pixel (i, j) of two 8-bit planes
  *   (row-major, `stride` bytes between rows) the edge-truncated
  *   (2r+1) x (2r+1) window gives int64 sums x, y, x2, y2, xy and the pixel
  *   count w; the fp64 term

@@ -54,17 +54,20 @@ def test_ssim_full_frame_more_seeds(seed):
     torch = torch_cuda()
     ref, dis = si.frame_pair(si.FRAME_H, si.FRAME_W, seed)
     s, wsum, _ = oracle.ssim_frame_sum(ref, dis, 3)
-    gs, gw, _ = ex.ssim_term_and_sum(torch.from_numpy(ref).cuda(), torch.from_numpy(dis).cuda(), 3)
-    assert same(float(gs.cpu()[0]), s), seed
-    assert int(gw.cpu()[0]) == wsum
+    r, d = torch.from_numpy(ref).cuda(), torch.from_numpy(dis).cuda()
+    for mode in (0, ex.SSIM_IN_TILES):
+        gs, gw, _ = ex.ssim_term_and_sum(r, d, 3, flags=mode)
+        assert same(float(gs.cpu()[0]), s), (seed, mode)
+        assert int(gw.cpu()[0]) == wsum
 
 
-def test_ssim_full_frame_every_term():
+@pytest.mark.parametrize("mode", [0, ex.SSIM_IN_TILES], ids=["producer", "in_tiles"])
+def test_ssim_full_frame_every_term(mode):
     torch = torch_cuda()
     ref, dis = si.frame_pair(si.FRAME_H, si.FRAME_W, 0)
     s, wsum, terms = oracle.ssim_frame_sum(ref, dis, 3, want_terms=True)
     gs, gw, gt = ex.ssim_term_and_sum(torch.from_numpy(ref).cuda(), torch.from_numpy(dis).cuda(), 3,
-                                      want_terms=True)
+                                      want_terms=True, flags=mode)
     g = gt.cpu().numpy()
     assert g.size == si.FRAME_N
     diff = np.nonzero(g.view(np.uint64) != terms.view(np.uint64))[0]

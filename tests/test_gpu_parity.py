@@ -229,27 +229,37 @@ SIZES = [(1, 1), (2, 2), (3, 4), (5, 7), (9, 9), (16, 16), (33, 17), (65, 63), (
          (8, 8), (17, 9), (31, 33), (323, 577), (48, 64), (47, 65)]
 
 
+SSIM_MODES = [0, ex.SSIM_IN_TILES]
+
+
+@pytest.mark.parametrize("mode", SSIM_MODES, ids=["producer", "in_tiles"])
 @pytest.mark.parametrize("hw", SIZES, ids=lambda s: "%dx%d" % s)
-def test_ssim_small_frames(hw):
+def test_ssim_small_frames(hw, mode):
     """Frame sizes from the pages' random-size lists; every term and the sum
-    equal the oracle's."""
+    equal the oracle's, with the terms formed by the producer or in the sum's
+    tiles."""
     torch = torch_cuda()
     h, w = hw
     ref, dis = si.frame_pair(h, w, h * 1000 + w)
     s, wsum, terms = oracle.ssim_frame_sum(ref, dis, 3, want_terms=True)
     r = torch.from_numpy(ref).cuda()
     d = torch.from_numpy(dis).cuda()
-    gs, gw, gt = ex.ssim_term_and_sum(r, d, 3, want_terms=True)
+    gs, gw, gt = ex.ssim_term_and_sum(r, d, 3, want_terms=True, flags=mode)
     assert np.array_equal(gt.cpu().numpy().view(np.uint64), terms.view(np.uint64))
     assert same(float(gs.cpu()[0]), s)
     assert int(gw.cpu()[0]) == wsum
+    # without the terms asked for (the producer: the workspace holds them)
+    gs2, gw2, _ = ex.ssim_term_and_sum(r, d, 3, flags=mode)
+    assert same(float(gs2.cpu()[0]), s)
+    assert int(gw2.cpu()[0]) == wsum
 
 
 @pytest.mark.parametrize("hwsr", [(40, 1088, 1088, 3), (33, 1100, 1100, 5), (21, 1057, 1057, 3),
                                   (19, 1088, 1096, 15), (9, 2048, 2052, 0), (64, 1280, 1280, 1),
                                   (24, 1280, 1284, 2), (17, 1104, 1104, 4), (12, 1536, 1540, 6)],
                          ids=lambda v: "%dx%d_s%d_r%d" % v)
-def test_ssim_wide_rows(hwsr):
+@pytest.mark.parametrize("mode", SSIM_MODES, ids=["producer", "in_tiles"])
+def test_ssim_wide_rows(hwsr, mode):
     """Rows at least as wide as a chunk's span (the producer's one-division
     row tracking; 4-byte plane loads where rows and strides are multiples of
     four): every term and the sum equal the oracle's, padded strides too."""
@@ -263,15 +273,16 @@ def test_ssim_wide_rows(hwsr):
     big_d[:, :w] = dis
     r = torch.from_numpy(big_r).cuda()[:, :w]
     d = torch.from_numpy(big_d).cuda()[:, :w]
-    gs, gw, gt = ex.ssim_term_and_sum(r, d, radius, want_terms=True)
+    gs, gw, gt = ex.ssim_term_and_sum(r, d, radius, want_terms=True, flags=mode)
     assert np.array_equal(gt.cpu().numpy().view(np.uint64), terms.view(np.uint64))
     assert same(float(gs.cpu()[0]), s)
     assert int(gw.cpu()[0]) == wsum
 
 
+@pytest.mark.parametrize("mode", SSIM_MODES, ids=["producer", "in_tiles"])
 @pytest.mark.parametrize("radius", [0, 1, 2, 3, 4, 5])
 @pytest.mark.parametrize("hw", [(37, 203), (16, 64), (9, 13)], ids=lambda s: "%dx%d" % s)
-def test_ssim_radius_small_frames(hw, radius):
+def test_ssim_radius_small_frames(hw, radius, mode):
     """Narrow frames at every window radius up to five (the producer's
     register windows take radii up to four, on pixels away from the row
     ends; the rest add up their windows from LDS): every term and the sum
@@ -281,31 +292,35 @@ def test_ssim_radius_small_frames(hw, radius):
     ref, dis = si.frame_pair(h, w, 31 * h + w + radius)
     s, wsum, terms = oracle.ssim_frame_sum(ref, dis, radius, want_terms=True)
     gs, gw, gt = ex.ssim_term_and_sum(torch.from_numpy(ref).cuda(), torch.from_numpy(dis).cuda(),
-                                      radius, want_terms=True)
+                                      radius, want_terms=True, flags=mode)
     assert np.array_equal(gt.cpu().numpy().view(np.uint64), terms.view(np.uint64))
     assert same(float(gs.cpu()[0]), s)
     assert int(gw.cpu()[0]) == wsum
 
 
-def test_ssim_full_frame():
+@pytest.mark.parametrize("mode", SSIM_MODES, ids=["producer", "in_tiles"])
+def test_ssim_full_frame(mode):
     torch = torch_cuda()
     ref, dis = si.frame_pair(si.FRAME_H, si.FRAME_W, 0)
     s, wsum, _ = oracle.ssim_frame_sum(ref, dis, 3)
     r = torch.from_numpy(ref).cuda()
     d = torch.from_numpy(dis).cuda()
-    gs, gw, _, st = ex.ssim_term_and_sum(r, d, 3, stats=True)
-    say("ssim full", st)
+    gs, gw, _, st = ex.ssim_term_and_sum(r, d, 3, stats=True, flags=mode)
+    say("ssim full", mode, st)
     assert same(float(gs.cpu()[0]), s)
     assert int(gw.cpu()[0]) == wsum
 
 
-@pytest.mark.parametrize("flags", [ex.WALK_ONLY, ex.CHAIN_CUT, ex.PLAN_ALL_FALLBACK,
-                                   ex.tile_flag(1), ex.tile_flag(2) | ex.CHAIN_CUT])
+@pytest.mark.parametrize("flags", [ex.SSIM_IN_TILES | ex.WALK_ONLY, ex.SSIM_IN_TILES | ex.CHAIN_CUT,
+                                   ex.SSIM_IN_TILES | ex.PLAN_ALL_FALLBACK, ex.SSIM_IN_TILES | ex.tile_flag(1),
+                                   ex.SSIM_IN_TILES | ex.tile_flag(2) | ex.CHAIN_CUT,
+                                   ex.CHAIN_CUT, ex.PASS_PATH, ex.PLAN_ALL_FALLBACK, ex.WALK_ONLY])
 def test_ssim_fused_paths(flags):
-    """The fused term source under every walk: the terms the tiles form and
-    the ones the walk forms again for chunks it adds term by term give the
-    oracle's sum (radius 5, a frame whose rows are not a multiple of a
-    chunk, plane rows padded)."""
+    """The terms formed in the tiles under every walk (the terms the tiles
+    form and the ones the walk forms again for chunks it adds term by term),
+    and the producer's terms under the sum's launch plans, give the oracle's
+    sum (radius 5, a frame whose rows are not a multiple of a chunk, plane
+    rows padded)."""
     torch = torch_cuda()
     h, w = 211, 373
     ref, dis = si.frame_pair(h, w, 77)

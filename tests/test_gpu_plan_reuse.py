@@ -130,8 +130,9 @@ def test_full_size_frames():
         assert same(got, want), f
 
 
-def test_ssim_sequence():
-    """The fused SSIM sum of consecutive frame pairs with the kept plan."""
+@pytest.mark.parametrize("mode", [0, ex.SSIM_IN_TILES], ids=["producer", "in_tiles"])
+def test_ssim_sequence(mode):
+    """The SSIM sum of consecutive frame pairs with the kept plan."""
     torch = torch_cuda()
     h, w = 270, 480
     need = ex.lib().ssim_term_and_sum_workspace_size(w, h)
@@ -140,7 +141,7 @@ def test_ssim_sequence():
         ref, dis = si.frame_pair(h, w, 500 + f)
         s, wsum, _ = oracle.ssim_frame_sum(ref, dis, 3)
         gs, gw, _ = ex.ssim_term_and_sum(torch.from_numpy(ref).cuda(), torch.from_numpy(dis).cuda(),
-                                         3, flags=REUSE, ws=ws)
+                                         3, flags=REUSE | mode, ws=ws)
         assert same(float(gs.cpu()[0]), s), f
         assert int(gw.cpu()[0]) == wsum
 
