@@ -39,7 +39,7 @@ CHAIN_CUT = 1 << 7
 PLAN_REUSE = 1 << 20
 CHAIN_PATH = 1 << 21
 PASS_PATH = 1 << 22
-SSIM_IN_TILES = 1 << 23
+SSIM_IN_TILES = 1 << 23  # ssim_term_and_sum: the sum's tiles form the terms
 
 
 def tile_flag(chunks_per_tile: int) -> int:
@@ -366,7 +366,11 @@ def exact_seq_sum_batch(xs, inits=None, *, flags: int = 0, out=None, ws=None,
 def ssim_term_and_sum(ref, dis, radius: int = 3, c1: float = None, c2: float = None, *,
                       flags: int = 0, want_terms: bool = False, ws=None, stats: bool = False,
                       stream=None):
-    """Fused integer-SSIM frame sum of two uint8 planes (H x W, row-major).
+    """Integer-SSIM frame sum of two uint8 planes (H x W, row-major): every
+    pixel's term formed on the device, then added in raster order.  By default
+    a producer launch writes the terms (into ``terms`` with ``want_terms``,
+    else into the workspace) and the exact sum adds them; with
+    ``flags | SSIM_IN_TILES`` the sum's tiles form the terms themselves.
 
     Returns (sum tensor[1] f64, weight-sum tensor[1] i64, terms or None[, stats])."""
     torch = _torch()

@@ -59,8 +59,17 @@ def run(ssim: bool = False, seed: int = 0, out=sys.stdout) -> dict:
         call = lambda: ex.exact_seq_sum(x)  # noqa: E731
         n = si.FRAME_N
     want = call().cpu().numpy().view(np.uint64)[0]
+    saved = (ex._lib, ex.LIB_PATH)
     ex._lib = None
     ex.LIB_PATH = _build.TIMELINE_LIB
+    try:
+        return _timed(ex, torch, call, want, n, ssim, seed, out)
+    finally:
+        # the process goes on with the product library
+        ex._lib, ex.LIB_PATH = saved
+
+
+def _timed(ex, torch, call, want, n, ssim, seed, out):
     L = ex.lib()
     L.exseq_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
     L.exseq_timeline_words.restype = ctypes.c_size_t

@@ -31,7 +31,10 @@ def test_workspace_sizes():
     assert 8100 * 32 <= w <= 8100 * 444 + 8192
     assert w < 8294400 * 8 * 6 // 100
     assert L.tree_sum_f64_workspace_size(1000) > 0
-    assert L.ssim_term_and_sum_workspace_size(3840, 2160) > 0
+    # the SSIM sum's workspace holds the producer's terms (8 bytes a pixel)
+    # beside the exact sum's
+    assert L.ssim_term_and_sum_workspace_size(3840, 2160) >= (
+        3840 * 2160 * 8 + L.exact_seq_sum_f64_workspace_size(3840 * 2160))
     ns = (ctypes.c_size_t * 3)(10, 100000, 0)
     assert L.exact_seq_sum_f64_batch_workspace_size(ns, 3) >= L.exact_seq_sum_f64_workspace_size(100000)
 
