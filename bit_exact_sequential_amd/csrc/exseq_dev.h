@@ -953,6 +953,30 @@ __device__ __forceinline__ Run wave_reduce_run_rev(Run v)
     return v;
 }
 
+// Pairs of runs without a negative term composed in order, each result held
+// within +-2^57 (such pairs only grow, so a total past 2^56 shows at the end).
+__device__ __forceinline__ Pair compose_clamped(Pair a, Pair b)
+{
+    const int64_t lim = (int64_t)1 << 57;
+    Pair c = compose(a, b);
+    c.r0 = c.r0 > lim ? lim : c.r0;
+    c.r1 = c.r1 > lim ? lim : c.r1;
+    return c;
+}
+
+// The same order as wave_reduce_run_rev (the higher lanes first, complete in
+// lane 63) for such pairs.
+__device__ __forceinline__ Pair wave_reduce_pair_rev(Pair v)
+{
+    v = compose_clamped(v, dpp_pair<kDppRowShr1>(v));
+    v = compose_clamped(v, dpp_pair<kDppRowShr2>(v));
+    v = compose_clamped(v, dpp_pair<kDppRowShr4>(v));
+    v = compose_clamped(v, dpp_pair<kDppRowShr8>(v));
+    v = compose_clamped(v, dpp_pair<kDppRowBcast15, 0xA>(v));
+    v = compose_clamped(v, dpp_pair<kDppRowBcast31, 0xC>(v));
+    return v;
+}
+
 // Runs that compose by a plain sum of their increments: tie-free and
 // monotone, every one non-decreasing (no flag, the bounds unused) or every
 // one non-increasing (kFlagNeg, bounds (total, 0)).
@@ -1064,9 +1088,11 @@ __device__ __forceinline__ int chain_back(const ChainArea &ch, uint32_t tb, uint
             return kBackLost;
         // the regular tiles after it, the earlier ones first; a wave whose
         // tiles all have a tie-free run without a negative term (nearly
-        // always) composes them as one integer sum
-        Run r = run_identity();
-        bool bad = false, plain = true, fall = true;
+        // always) composes them as one integer sum, and one whose tiles have
+        // no negative term (ties allowed) composes their pairs alone: such a
+        // run's prefixes are bounded by its total (run_top), so its bounds
+        // need no composing
+        bool bad = false, plain = true, fall = true, nonneg = true;
         int64_t tot = 0;
 #pragma unroll
         for (int i = kBackPer - 1; i >= 0; i--) {
@@ -1077,11 +1103,12 @@ __device__ __forceinline__ int chain_back(const ChainArea &ch, uint32_t tb, uint
                              (uint32_t)w[i][0] & (kFlagNeg | kFlagBad | kFlagNonFinite)};
                 plain &= rising_run(ti.p, ti.flags);
                 fall &= falling_run(ti.p, ti.lo, ti.hi, ti.flags);
+                nonneg &= ti.flags == 0u && ti.p.r0 >= 0 && ti.p.r1 >= 0;
                 tot += r0;
-                r = run_compose_sat(r, ti);
                 bad |= ((uint32_t)w[i][0] & kKeyMask) != key0;
             }
         }
+        Run r;
         if (__ballot(!plain) == 0) {
             tot = wave_sum_i64(tot);
             r = Run{Pair{tot, tot}, 0, tot, 0u};
@@ -1092,7 +1119,32 @@ __device__ __forceinline__ int chain_back(const ChainArea &ch, uint32_t tb, uint
             r = Run{Pair{tot, tot}, tot, 0, kFlagNeg};
             if (tot < -((int64_t)1 << 56))
                 r = Run{Pair{0, 0}, 0, 0, kFlagBad};
+        } else if (__ballot(!nonneg) == 0) {
+            Pair pp = pair_identity();
+#pragma unroll
+            for (int i = kBackPer - 1; i >= 0; i--) {
+                if (j0 - kBackPer * t - i >= 0 && kBackPer * t + i < first) {
+                    const int64_t r0 = dec_i64(w[i][1]);
+                    pp = compose_clamped(pp, Pair{r0, r0 + (int64_t)((w[i][0] >> kDrShift) & 3u) - 1});
+                }
+            }
+            pp = wave_reduce_pair_rev(pp);
+            const int64_t lim = (int64_t)1 << 56;
+            r = Run{pp, 0, 0, 0u};
+            if (pp.r0 > lim || pp.r1 > lim)
+                r = Run{Pair{0, 0}, 0, 0, kFlagBad};
         } else {
+            r = run_identity();
+#pragma unroll
+            for (int i = kBackPer - 1; i >= 0; i--) {
+                if (j0 - kBackPer * t - i >= 0 && kBackPer * t + i < first) {
+                    const int64_t r0 = dec_i64(w[i][1]);
+                    const Run ti{Pair{r0, r0 + (int64_t)((w[i][0] >> kDrShift) & 3u) - 1},
+                                 dec_i64(w[i][2]), dec_i64(w[i][3]),
+                                 (uint32_t)w[i][0] & (kFlagNeg | kFlagBad | kFlagNonFinite)};
+                    r = run_compose_sat(r, ti);
+                }
+            }
             r = wave_reduce_run_rev(r);
         }
         const uint64_t bb = __ballot(bad);
