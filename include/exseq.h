@@ -229,8 +229,9 @@ int exact_seq_sum_f64_interleaved(const double *x, size_t windows, int k,
 
 /* ---------------------------------------------------------------------------
  * ssim_term_and_sum
- *   Integer-SSIM frame sum, terms formed on the device from the planes
- *   (EXSEQ_SSIM_IN_TILES: inside the sum's tiles).  For every pixel (i, j) of two 8-bit planes
+ *   Integer-SSIM frame sum, the terms formed on the device from the planes
+ *   (by a producer launch, or with EXSEQ_SSIM_IN_TILES inside the sum's
+ *   tiles).  For every pixel (i, j) of two 8-bit planes
  *   (row-major, `stride` bytes between rows) the edge-truncated
  *   (2r+1) x (2r+1) window gives int64 sums x, y, x2, y2, xy and the pixel
  *   count w; the fp64 term
@@ -242,8 +243,14 @@ int exact_seq_sum_f64_interleaved(const double *x, size_t windows, int k,
  *   order", Context and Decision), is added into one double in raster order
  *   starting from +0.0.  out_sum: one device double.  out_weight_sum:
  *   nullable device int64, the sum of w over the frame.  out_terms: nullable
- *   device plane of width*height doubles receiving every term (debugging).
- *   width, height >= 1; stride >= width; 0 <= radius <= 15.
+ *   device plane of width*height doubles receiving every term (debugging);
+ *   without it the producer writes the terms into the workspace, whose size
+ *   (ssim_term_and_sum_workspace_size) includes 8 bytes per pixel for them.
+ *   ws must not overlap the planes or out_terms.  width, height >= 1;
+ *   stride >= width; 0 <= radius <= 15.  Errors: EXSEQ_EINVAL for a null
+ *   plane or out_sum, misaligned outputs, a bad geometry or width*height
+ *   >= 2^31; EXSEQ_EWORKSPACE for a workspace below the size; EXSEQ_EHIP for
+ *   a launch that failed.
  * ------------------------------------------------------------------------- */
 size_t ssim_term_and_sum_workspace_size(int width, int height);
 int ssim_term_and_sum(const uint8_t *ref, const uint8_t *dis, int width,
