@@ -1563,6 +1563,27 @@ constexpr int kRecWords = 16;
 constexpr uint64_t kRecPresent = 1ULL << 63;
 constexpr int kCatch = 4;  // records a wave holds while it waits (16 lanes each)
 
+// Zeroes the chain words of a launch of `tiles` tiles (none if 0): every
+// tile's agg, incl and record words and the heads (a published chain word is
+// never zero, so zero means "not yet").  Called by every thread of a grid of
+// any shape, each taking words by its linear index.
+__device__ __forceinline__ void zero_chain_words(const ChainArea &ch, uint32_t tiles)
+{
+    if (tiles == 0)
+        return;
+    const size_t blocks = (size_t)gridDim.x * gridDim.y;
+    const size_t i = ((size_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
+    const size_t stride = blocks * blockDim.x;
+    for (size_t k = i; k < 4 * (size_t)tiles; k += stride)
+        ch.agg[k] = 0;
+    for (size_t k = i; k < (size_t)kRecWords * tiles; k += stride)
+        ch.rec[k] = 0;
+    for (size_t k = i; k < (size_t)tiles; k += stride)
+        ch.incl[k] = 0;
+    if (i < (size_t)kMaxBatch)
+        ch.head[i] = 0;
+}
+
 // The word of the record a lane i < kRecWords of the publishing wave writes.
 __device__ __forceinline__ uint64_t rec_word(int i, uint32_t akey, const Run &A, bool hasx,
                                              const uint64_t *w, int len, uint32_t xkey,

@@ -86,6 +86,9 @@ struct BatchArgs {
     // group's size (else they follow the launch's other arrays).
     uint64_t *plan_hdr_ext;
     double *plan_ext;
+    // Nonzero: a launch before this one on the stream zeroed the chain words
+    // (the SSIM term producer), so the launch sequence skips its clear.
+    uint32_t chain_cleared;
 };
 
 // Descriptors live in four arrays (structure of arrays, so that the walk
@@ -129,6 +132,14 @@ int launch_interleaved(const double *x, size_t windows, int k, const double *ini
 int launch_exact_sum(const double *x, size_t n, double init, double *out, void *ws,
                      hipStream_t stream, uint32_t flags, exseq_stats *stats,
                      void *const *events = nullptr, int n_events = 0);
+// The chain words a launch of launch_exact_sum(n, flags) on workspace ws
+// zeroes before its tiles: false if it takes no tile chain (a few chunks, the
+// single pass, a mode without the chain).  A launch earlier on the same
+// stream may zero them instead (zero_chain_words), and launch_exact_sum with
+// chain_cleared then skips its clear.
+bool chain_words_of(size_t n, uint32_t flags, void *ws, ChainArea *ch, uint32_t *tiles);
+int launch_exact_sum_cleared(const double *x, size_t n, double init, double *out, void *ws,
+                             hipStream_t stream, uint32_t flags, exseq_stats *stats);
 // The single pass (exseq_pass.hip): whether a launch can take it, its
 // workspace, and its launch (one kernel; events[0] and events[1] around it).
 bool pass_flags_ok(uint32_t flags);

@@ -11,6 +11,7 @@
 #include "exseq_internal.h"
 #include "exseq_rules.h"
 #include "exseq_ssim_dev.h"
+#include "exseq_dev.h"
 
 namespace exseq {
 
@@ -45,8 +46,10 @@ int launch_div(const double *a, const double *b, double *q, size_t n, hipStream_
 // The producer for any frame: every pixel's term in raster order into
 // `terms`, one workgroup per chunk of 1024 pixels (the column sums, windows
 // and term of the tiles' own source), and the frame's weight sum.
-__global__ __launch_bounds__(256) void ssim_terms_kernel(SsimParams sp, double *terms)
+__global__ __launch_bounds__(256) void ssim_terms_kernel(SsimParams sp, double *terms, ChainArea ch,
+                                                         uint32_t tiles)
 {
+    zero_chain_words(ch, tiles);
     __shared__ __attribute__((aligned(16))) int lds[SsimTerms::kLdsInts];
     const SsimTerms src{sp};
     const size_t c = blockIdx.x;
@@ -76,7 +79,6 @@ __global__ __launch_bounds__(256) void ssim_terms_kernel(SsimParams sp, double *
 // says how many.
 constexpr int kRowBlock = 4;
 constexpr int kWaveCols = 4 * 62;
-constexpr int kDppWaveShr1 = 0x138;  // lane l takes lane l - 1's value (lane 0: 0)
 constexpr int kDppWaveShl1 = 0x130;  // lane l takes lane l + 1's value (lane 63: 0)
 
 __device__ __forceinline__ uint32_t plane_word(const __amdgpu_buffer_rsrc_t &rs, int vo, int so)
@@ -201,8 +203,10 @@ __device__ __forceinline__ void wave_strip(const SsimParams &sp, double *terms)
     }
 }
 
-__global__ __launch_bounds__(256) void ssim_terms_rows_kernel(SsimParams sp, double *terms)
+__global__ __launch_bounds__(256) void ssim_terms_rows_kernel(SsimParams sp, double *terms, ChainArea ch,
+                                                              uint32_t tiles)
 {
+    zero_chain_words(ch, tiles);
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0 && sp.out_weight_sum)
         *sp.out_weight_sum = sp.weight_sum;
     switch (sp.radius) {
@@ -257,16 +261,24 @@ int launch_ssim_sum(const uint8_t *ref, const uint8_t *dis, int width, int heigh
     double *terms = out_terms ? out_terms
                               : reinterpret_cast<double *>(static_cast<char *>(ws) + ssim_sum_ws(n));
     sp.out_terms = nullptr;
+    // the producer also zeroes the exact sum's chain words, one launch fewer
+    ChainArea ch{};
+    uint32_t tiles = 0;
+    const bool fold = chain_words_of(n, flags, ws, &ch, &tiles);
+    if (!fold)
+        tiles = 0;
     if (rows_producer_ok(sp))
         hipLaunchKernelGGL(ssim_terms_rows_kernel,
                            dim3((unsigned)((width + 4 * kWaveCols - 1) / (4 * kWaveCols)),
                                 (unsigned)((height + kRowBlock - 1) / kRowBlock)),
-                           dim3(256), 0, stream, sp, terms);
+                           dim3(256), 0, stream, sp, terms, ch, tiles);
     else
         hipLaunchKernelGGL(ssim_terms_kernel, dim3((unsigned)((n + 1023) / 1024)), dim3(256), 0, stream,
-                           sp, terms);
+                           sp, terms, ch, tiles);
     if (hipGetLastError() != hipSuccess)
         return EXSEQ_EHIP;
+    if (fold)
+        return launch_exact_sum_cleared(terms, n, 0.0, out_sum, ws, stream, flags, stats);
     return launch_exact_sum(terms, n, 0.0, out_sum, ws, stream, flags, stats, nullptr, 0);
 }
 

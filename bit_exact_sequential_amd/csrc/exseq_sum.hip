@@ -969,17 +969,7 @@ __global__ void write_value_kernel(double *out, double v) { out[0] = v; }
 // Zeroes the chain words of `tiles` tiles before a launch's tiles run.
 __global__ __launch_bounds__(256) void chain_clear_kernel(ChainArea ch, uint32_t tiles)
 {
-    // consecutive lanes on consecutive words
-    const size_t i = (size_t)blockIdx.x * 256u + threadIdx.x;
-    const size_t stride = (size_t)gridDim.x * 256u;
-    for (size_t k = i; k < 4 * (size_t)tiles; k += stride)
-        ch.agg[k] = 0;
-    for (size_t k = i; k < (size_t)kRecWords * tiles; k += stride)
-        ch.rec[k] = 0;
-    if (i < tiles)
-        ch.incl[i] = 0;
-    if (i < (size_t)kMaxBatch)
-        ch.head[i] = 0;
+    zero_chain_words(ch, tiles);  // consecutive lanes on consecutive words
 }
 
 // ---------------------------------------------------------------------------
@@ -1027,6 +1017,15 @@ uint64_t plan_tag(const BatchArgs &a)
 
 
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Chunks per tile of a launch over `total` chunks.
+uint32_t tile_chunks(uint32_t total, uint32_t flags)
+{
+    const uint32_t sel = (flags >> kTileShift) & 3u;  // 0: by size
+    if (sel == 0 && !(flags & EXSEQ_PLAN_REUSE))
+        return total <= 2u * kTileMax ? 4u : total <= 2048u ? 1u : total <= 4096u ? 2u : 4u;
+    return sel == 1 ? 1u : (sel == 2 ? 2u : 4u);
+}
 
 WsParts carve(void *ws, size_t total)
 {
@@ -1114,11 +1113,7 @@ static int launch_batch_src(const BatchArgs &a, const Src &src, void *ws, double
     // that saves.  A sum of at most two tiles of kTileMax chunks keeps them
     // (more tiles would only add links to its chain), and a kept plan is
     // kept per tile of kTileMax chunks.
-    const uint32_t sel = (a.flags >> kTileShift) & 3u;  // 0: by size
-    if (sel == 0 && !(a.flags & EXSEQ_PLAN_REUSE))
-        args.tile = total <= 2u * kTileMax ? 4u : total <= 2048u ? 1u : total <= 4096u ? 2u : 4u;
-    else
-        args.tile = sel == 1 ? 1u : (sel == 2 ? 2u : 4u);
+    args.tile = tile_chunks(total, a.flags);
     const uint32_t tiles = total / args.tile;
     args.plan_sig = (a.flags & EXSEQ_PLAN_REUSE) && (a.flags & EXSEQ_PLAN_MASK) == EXSEQ_PLAN_AUTO &&
                             chain_on(a.flags) && args.tile == (uint32_t)kTileMax && tiles
@@ -1140,7 +1135,7 @@ static int launch_batch_src(const BatchArgs &a, const Src &src, void *ws, double
         return hipGetLastError() == hipSuccess ? EXSEQ_OK : EXSEQ_EHIP;
     }
     mark(0);
-    if (chain_on(a.flags) && tiles)
+    if (chain_on(a.flags) && tiles && !a.chain_cleared)
         hipLaunchKernelGGL(chain_clear_kernel,
                            dim3((unsigned)((4 * tiles > (uint32_t)kMaxBatch ? 4 * tiles : (uint32_t)kMaxBatch) + 255) / 256),
                            dim3(256), 0, stream, p.ch, tiles);
@@ -1214,6 +1209,33 @@ int launch_interleaved(const double *x, size_t windows, int k, const double *ini
     }
     a.chunk_base[k] = (uint32_t)k * per;
     return launch_batch_src(a, StridedTerms{(uint32_t)k}, ws, outs, stream, stats, nullptr, 0);
+}
+
+bool chain_words_of(size_t n, uint32_t flags, void *ws, ChainArea *ch, uint32_t *tiles)
+{
+    const uint32_t total = (uint32_t)padded_chunks(n);
+    // the decisions of launch_batch and launch_batch_src for one sum
+    const bool tiny = total <= 2u * kTileMax && (flags & ~EXSEQ_PASS_PATH) == 0u;
+    if (total == 0 || tiny || (flags & EXSEQ_PASS_PATH) || !chain_on(flags))
+        return false;
+    *tiles = total / tile_chunks(total, flags);
+    *ch = carve(ws, total).ch;
+    return *tiles > 0;
+}
+
+int launch_exact_sum_cleared(const double *x, size_t n, double init, double *out, void *ws,
+                             hipStream_t stream, uint32_t flags, exseq_stats *stats)
+{
+    BatchArgs a{};
+    a.count = 1;
+    a.flags = flags;
+    a.x[0] = x;
+    a.n[0] = n;
+    a.init[0] = init;
+    a.chunk_base[0] = 0;
+    a.chunk_base[1] = (uint32_t)padded_chunks(n);
+    a.chain_cleared = 1;
+    return launch_batch_src(a, PlainTerms{}, ws, out, stream, stats, nullptr, 0);
 }
 
 int launch_exact_sum(const double *x, size_t n, double init, double *out, void *ws,
