@@ -379,8 +379,9 @@ def cpu_configs(oracle, si, seed, threads, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
-              "(the multi-GPU design is described, not built)" % args.gpus, file=sys.stderr)
+        print("bench.py: the library runs on one GPU; --gpus %d is not supported "
+              "(how the sums would shard over several GPUs is a design only)" % args.gpus,
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

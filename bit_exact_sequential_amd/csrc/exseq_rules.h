@@ -22,7 +22,7 @@
 //    binade (the smallest/largest prefix check).  Otherwise its terms are
 //    added one by one.
 //
-// How an increment pair is formed here (this build's own construction, not
+// How an increment pair is formed here (this library's own construction, not
 // the pages' bit-shift form): y = x * 2^(52 - e) is exact (a power-of-two
 // scaling).  For |y| < 2^51 the fp64 add t = fl(M + y) with M = 1.5 * 2^52
 // lands in [2^52, 2^53], where doubles are exactly the integers; so t - M is

@@ -14,7 +14,8 @@
  *    the moments are int64 sums; mx2, my2, mxy are the three products of two
  *    moments (x*x, y*y, x*y) formed in fp64 from the converted moments.
  *  - The window is the edge-truncated (2r+1)x(2r+1) box (r = 3 gives 7x7)
- *    and w is the number of pixels it covers (reading stated in the design doc).
+ *    and w is the number of pixels it covers: the pages name the box and w
+ *    but not its edges, and a window cut by the frame keeps the pixels inside.
  *
  * Build: gcc -O2 -ffp-contract=off -fno-fast-math (no FMA may form).
  */
