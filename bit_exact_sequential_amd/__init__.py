@@ -137,6 +137,8 @@ def lib():
     L.exseq_div_f64.argtypes = [vp, vp, vp, sz, vp]
     L.exseq_twin_seq_sum_f64.restype = ctypes.c_double
     L.exseq_twin_seq_sum_f64.argtypes = [vp, sz, ctypes.c_double, u32, u32, vp]
+    L.exseq_twin_chain_sum_f64.restype = ctypes.c_double
+    L.exseq_twin_chain_sum_f64.argtypes = [vp, sz, ctypes.c_double, u32, u32, ctypes.c_int64, vp, vp]
     L.exseq_model_seq_sum_f64.restype = ctypes.c_double
     L.exseq_model_seq_sum_f64.argtypes = [vp, sz, ctypes.c_double, sz, u32, u32,
                                           ctypes.POINTER(Stats)]
@@ -457,6 +459,25 @@ def twin_seq_sum(x, init: float = 0.0, flags: int = 0, mutations: int = 0):
     s = lib().exseq_twin_seq_sum_f64(a.ctypes.data if a.size else None, a.size, float(init),
                                      int(flags), int(mutations), ctypes.byref(st))
     return s, st.as_dict()
+
+
+def twin_chain_sum(x, init: float = 0.0, flags: int = 0, mutations: int = 0, skew: int = 0):
+    """The tile chain (four chunks per tile) replayed on the host in the
+    kernels' grouping: the tiles' runs, the chain look-back's composition of
+    the regular tiles, the irregular tiles' chunks from the exact sum and the
+    walk's resume.  skew moves every planned prefix by skew * 2^-30 of itself.
+    Returns (sum, stats, paths): paths counts the look-back's waves composed
+    as integer sums, falling sums, pairs alone and full runs, the composed
+    runs applied, and the stops of the chain."""
+    import numpy as np
+    a = np.ascontiguousarray(x, dtype=np.float64)
+    st = Stats()
+    paths = (ctypes.c_uint64 * 6)()
+    s = lib().exseq_twin_chain_sum_f64(a.ctypes.data if a.size else None, a.size, float(init),
+                                       int(flags), int(mutations), int(skew), ctypes.byref(st),
+                                       paths)
+    return s, st.as_dict(), dict(zip(("plain", "falling", "pairs", "runs", "applied", "stops"),
+                                     (int(v) for v in paths)))
 
 
 def model_seq_sum(x, init: float = 0.0, chunk_terms: int = CHUNK_TERMS, flags: int = 0,

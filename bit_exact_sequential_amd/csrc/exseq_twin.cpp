@@ -12,6 +12,11 @@
 // wave scan tree of row shifts and row broadcasts, then the carry over the
 // waves -- before it walks the ops.  A check that fails sends the event's
 // chunks through the descriptor walk and term-by-term adds, as on the GPU.
+// A second replay, of the tile chain (tile_kernel with four chunks per tile
+// and the chain after it), forms the tiles' runs in the same way, composes
+// the regular tiles before each irregular one in chain_back's grouping, adds
+// the irregular tiles' chunks from the exact sum and resumes with the walk
+// where a composed run does not apply.
 //
 // The rule helpers (term_inc, compose, run_compose, run_top, run_applies,
 // run_compose_sat, join_waves, clamp_run, crossing_apply, plan_key,
@@ -886,6 +891,347 @@ struct Twin {
         }
         return S;
     }
+
+    // -----------------------------------------------------------------------
+    // The tile chain (tile_kernel with four chunks per tile, then the chain):
+    // each chunk's four wave parts in the workgroup layout, joined; a regular
+    // tile's one run as its look-back words hold it; chain_back's grouping
+    // of the regular tiles before an irregular one (four per lane, earlier
+    // tiles first; per wave the integer sum, the falling sum, the pairs alone
+    // or the full runs, then the reversed wave tree; the waves in reverse;
+    // the rounds of 1024 tiles); the irregular tiles' chunk loop from the
+    // exact sum (a chunk's run where it applies, else its located crossing,
+    // else its terms in order); and walk_kernel's resume from the last exact
+    // sum where the chain stops.  The plan prefix before a tile is init plus
+    // the earlier tiles' sums in order, moved by skew * 2^-30 of itself: the
+    // plan never decides the bits, so no skew may change them.
+    // -----------------------------------------------------------------------
+    static constexpr int kCT = 4;
+    struct CTile {
+        bool regular;
+        uint64_t w[4];  // a regular tile's look-back words
+        uint32_t key[kCT];
+        WaveRun join[kCT];
+        bool hasx[kCT];
+        Cross x[kCT];
+    };
+    int64_t skew = 0;
+    uint64_t paths[6] = {0, 0, 0, 0, 0, 0};  // waves composed: plain, falling, pairs, runs; applied; stops
+
+    CTile chain_tile(uint32_t c0, double P)
+    {
+        CTile T;
+        std::memset(&T, 0, sizeof(T));
+        const uint32_t nk = std::min<uint32_t>(kCT, nch - c0);
+        std::vector<Chunk> ch(kCT);
+        double pk[kCT], tk[kCT];
+        bool cross[kCT], down[kCT];
+        for (uint32_t k = 0; k < kCT; k++) {
+            if (k < nk) {
+                ch[k] = chunk(c0 + k);
+            } else {
+                ch[k].len = 0;
+                std::fill(ch[k].v, ch[k].v + kLanes * kPerLane, 0.0);
+            }
+            tk[k] = k < nk ? tsum[c0 + k] : 0.0;
+        }
+        double p = P;
+        for (uint32_t k = 0; k < kCT; k++) {
+            pk[k] = p;
+            T.key[k] = plan_key(p, flags);
+            cross[k] = key_of(p + tk[k]) != key_of(p);
+            down[k] = ((key_of(p + tk[k]) ^ key_of(p)) & 0x800u) == 0u &&
+                      (key_of(p + tk[k]) & 0x7FFu) < (key_of(p) & 0x7FFu);
+            p += tk[k];
+        }
+        for (uint32_t k = 0; k < kCT; k++) {
+            const uint32_t kk = T.key[k];
+            WaveRun w[4];
+            for (int wv = 0; wv < 4; wv++) {
+                if (key_has_fast_path(kk)) {
+                    w[wv] = twin_wave_run(R, ch[k], wv, kk);
+                } else {
+                    bool nf = false;
+                    for (int q = kWaveLanes * kPerLane * wv; q < kWaveLanes * kPerLane * (wv + 1); q++)
+                        nf |= is_nonfinite(ch[k].v[q]);
+                    w[wv] = WaveRun{pair_identity(), 0, 0, nf ? kFlagNonFinite : 0u};
+                }
+            }
+            const WaveRun r = twin_join(R, w);
+            bool cc = cross[k];
+            if (key_has_fast_path(kk) && kk == key_of(pk[k])) {
+                const int64_t m = count_of(pk[k]);
+                const int64_t mg = plan_margin(c0 + k + 1);
+                bool near = m < count_floor(kk) + mg;
+                if (r.flags & kFlagNeg)
+                    near |= m + r.lo - mg < kCountLo + 1 || m + r.hi + mg > kCountHi - 1;
+                else
+                    near |= m + r.hi + mg > kCountHi;
+                cc |= near;
+            }
+            T.join[k] = r;
+            cross[k] = cc;
+            if (k < nk)
+                desc[c0 + k] = Desc{kk, r};
+        }
+        bool regular = c0 != 0 && c0 + kCT < nch;
+        for (uint32_t k = 0; k < kCT; k++)
+            regular &= key_has_fast_path(T.key[k]) && T.key[k] == T.key[0] && !cross[k] &&
+                       !(T.join[k].flags & (kFlagBad | kFlagNonFinite));
+        if (regular) {
+            bool plain = true, fall = true;
+            int64_t sum = 0;
+            for (uint32_t k = 0; k < kCT; k++) {
+                const WaveRun &q = T.join[k];
+                plain &= rising_run(q.p, q.flags);
+                fall &= falling_run(q.p, q.lo, q.hi, q.flags);
+                sum += q.p.r0;
+            }
+            Run tr = run_identity();
+            if (plain) {
+                tr = Run{Pair{sum, sum}, 0, sum, 0u};
+            } else if (fall) {
+                tr = Run{Pair{sum, sum}, sum, 0, kFlagNeg};
+            } else {
+                for (uint32_t k = 0; k < kCT; k++)
+                    tr = R.rcomp_sat(tr, Run{T.join[k].p, T.join[k].lo, T.join[k].hi, T.join[k].flags});
+            }
+            const int64_t dr = tr.p.r1 - tr.p.r0;
+            T.regular = true;
+            T.w[0] = kAggPresent | kAggRegular | (uint64_t)(T.key[0] & kKeyMask) |
+                     ((uint64_t)(dr + 1) << kDrShift) | (uint64_t)(tr.flags & kFlagNeg);
+            T.w[1] = enc_i64(tr.p.r0);
+            T.w[2] = enc_i64(tr.lo);
+            T.w[3] = enc_i64(tr.hi);
+            return T;
+        }
+        for (uint32_t k = 0; k < nk; k++) {
+            const uint32_t kk = T.key[k];
+            if (!(c0 != 0 && cross[k] && key_has_fast_path(kk) && kk == key_of(pk[k]) &&
+                  key_has_fast_path(down[k] ? kk - 1u : kk + 1u) &&
+                  !(T.join[k].flags & kFlagNonFinite)))
+                continue;
+            if (twin_crossing_find(R, ch[k], kk, count_of(pk[k]), down[k], T.x[k].w)) {
+                T.hasx[k] = true;
+                T.x[k].key = kk;
+                T.x[k].down = down[k];
+                T.x[k].len = ch[k].len;
+            }
+        }
+        return T;
+    }
+
+    // A regular tile's run as chain_back decodes its words
+    static Run agg_run(const uint64_t *w)
+    {
+        const int64_t r0 = dec_i64(w[1]);
+        return Run{Pair{r0, r0 + (int64_t)((w[0] >> kDrShift) & 3u) - 1}, dec_i64(w[2]), dec_i64(w[3]),
+                   (uint32_t)w[0] & (kFlagNeg | kFlagBad | kFlagNonFinite)};
+    }
+
+    Pair pair_clamped(Pair a, Pair b) const
+    {
+        const int64_t lim = (int64_t)1 << 57;
+        Pair c = R.comp(a, b);
+        c.r0 = c.r0 > lim ? lim : c.r0;
+        c.r1 = c.r1 > lim ? lim : c.r1;
+        return c;
+    }
+
+    // chain_back from irregular tile tl: 0 ok, 1 the keys differ, 2 lost
+    int chain_back_twin(const std::vector<CTile> &tiles, uint32_t tl, Run &acc, uint32_t &key0,
+                        int64_t &xp)
+    {
+        constexpr int kPer = 4, kRound = kPer * kLanes;
+        const int64_t big = (int64_t)1 << 56;
+        acc = run_identity();
+        key0 = 0u;
+        xp = -1;
+        bool keys_ok = true;
+        for (int64_t j0 = (int64_t)tl - 1; j0 >= 0; j0 -= kRound) {
+            if (j0 == (int64_t)tl - 1)
+                key0 = tiles[j0].regular ? (uint32_t)(tiles[j0].w[0] & kKeyMask) : 0u;
+            int first = kRound;
+            for (int q = 0; q < kRound; q++)
+                if (j0 - q >= 0 && !tiles[j0 - q].regular) {
+                    first = q;
+                    break;
+                }
+            auto in = [&](int t, int i) { return j0 - kPer * t - i >= 0 && kPer * t + i < first; };
+            Run wr[4];
+            bool anybad = false;
+            for (int wv = 0; wv < 4; wv++) {
+                bool plain = true, fall = true, nonneg = true, any = false;
+                int64_t tot = 0;
+                for (int l = 0; l < kWaveLanes; l++) {
+                    const int t = kWaveLanes * wv + l;
+                    for (int i = kPer - 1; i >= 0; i--) {
+                        if (!in(t, i))
+                            continue;
+                        const uint64_t *w = tiles[j0 - kPer * t - i].w;
+                        const Run ti = agg_run(w);
+                        plain &= rising_run(ti.p, ti.flags);
+                        fall &= falling_run(ti.p, ti.lo, ti.hi, ti.flags);
+                        nonneg &= ti.flags == 0u && ti.p.r0 >= 0 && ti.p.r1 >= 0;
+                        tot += ti.p.r0;
+                        anybad |= ((uint32_t)w[0] & kKeyMask) != key0;
+                        any = true;
+                    }
+                }
+                Run r;
+                if (plain) {
+                    r = Run{Pair{tot, tot}, 0, tot, 0u};
+                    if (tot > big)
+                        r = Run{Pair{0, 0}, 0, 0, kFlagBad};
+                    paths[0] += any;
+                } else if (fall) {
+                    r = Run{Pair{tot, tot}, tot, 0, kFlagNeg};
+                    if (tot < -big)
+                        r = Run{Pair{0, 0}, 0, 0, kFlagBad};
+                    paths[1] += any;
+                } else if (nonneg) {
+                    Pair pp[kWaveLanes];
+                    for (int l = 0; l < kWaveLanes; l++) {
+                        const int t = kWaveLanes * wv + l;
+                        pp[l] = pair_identity();
+                        for (int i = kPer - 1; i >= 0; i--)
+                            if (in(t, i))
+                                pp[l] = pair_clamped(pp[l], agg_run(tiles[j0 - kPer * t - i].w).p);
+                    }
+                    wave_scan_tree(pp, [&](Pair s, Pair v) { return pair_clamped(v, s); }, pair_identity());
+                    const Pair q = pp[kWaveLanes - 1];
+                    r = Run{q, 0, 0, 0u};
+                    if (q.r0 > big || q.r1 > big)
+                        r = Run{Pair{0, 0}, 0, 0, kFlagBad};
+                    paths[2] += any;
+                } else {
+                    Run rr[kWaveLanes];
+                    for (int l = 0; l < kWaveLanes; l++) {
+                        const int t = kWaveLanes * wv + l;
+                        rr[l] = run_identity();
+                        for (int i = kPer - 1; i >= 0; i--)
+                            if (in(t, i))
+                                rr[l] = R.rcomp_sat(rr[l], agg_run(tiles[j0 - kPer * t - i].w));
+                    }
+                    wave_scan_tree(rr, [&](Run s, Run v) { return R.rcomp_sat(v, s); }, run_identity());
+                    r = rr[kWaveLanes - 1];
+                    paths[3] += any;
+                }
+                wr[wv] = r;
+            }
+            Run Rr = wr[3];
+            for (int k = 2; k >= 0; k--)
+                Rr = R.rcomp_sat(Rr, wr[k]);
+            keys_ok &= !anybad;
+            acc = R.rcomp_sat(Rr, acc);
+            if (first < kRound) {
+                xp = j0 - first;
+                break;
+            }
+        }
+        if (xp < 0)
+            return 2;
+        return keys_ok ? 0 : 1;
+    }
+
+    // chunk c's terms from position pos on, in order
+    double add_terms_from(double S, uint32_t c, int pos)
+    {
+        const size_t b = (size_t)c * kLanes * kPerLane;
+        const size_t e = std::min(n, b + kLanes * kPerLane);
+        for (size_t i = b + (size_t)pos; i < e; i++)
+            S = S + x[i];
+        note_fallback(c);
+        return S;
+    }
+
+    // an irregular tile's chunks [kfirst, nk) from the exact sum S
+    double chain_chunks(double S, const CTile &T, uint32_t c0, uint32_t kfirst, uint32_t nk)
+    {
+        for (uint32_t k = kfirst; k < nk; k++) {
+            const WaveRun &r = T.join[k];
+            const uint32_t fl = r.flags & (kFlagNeg | kFlagBad | kFlagNonFinite);
+            const int64_t m = count_of(S);
+            if (R.key_ok(key_of(S), T.key[k]) && R.applies(m, r.p, r.lo, r.hi, fl)) {
+                S = R.advance(S, m, r.p);
+                st.fast_chunks++;
+                continue;
+            }
+            int pos = 0, xr = 0;
+            if (T.hasx[k])
+                xr = crossing_apply(T.x[k].w, T.x[k].len, T.key[k], fl, T.x[k].down, S, pos);
+            if (xr == 1) {
+                st.fast_chunks++;
+                continue;
+            }
+            if (xr == 0)
+                pos = 0;
+            S = add_terms_from(S, c0 + k, pos);
+        }
+        return S;
+    }
+
+    double run_chain()
+    {
+        std::memset(&st, 0, sizeof(st));
+        st.first_fallback = -1;
+        nch = (uint32_t)((n + kLanes * kPerLane - 1) / (kLanes * kPerLane));
+        st.chunks = nch;
+        if (n == 0)
+            return init;
+        for (size_t i = 0; i < n; i++)
+            if (is_nonfinite(x[i]))
+                st.flags |= EXSEQ_STAT_NONFINITE;
+        desc.assign(nch, Desc{0u, WaveRun{pair_identity(), 0, 0, kFlagBad}});
+        tsum.resize(nch);
+        for (uint32_t c = 0; c < nch; c++)
+            tsum[c] = twin_tree_sum(chunk(c));
+        const uint32_t mode = flags & EXSEQ_PLAN_MASK;
+        const bool looks = mode != EXSEQ_PLAN_ALL_FALLBACK && mode != EXSEQ_PLAN_FIXED;
+        const uint32_t ntl = (nch + kCT - 1) / kCT;
+        std::vector<CTile> tiles;
+        tiles.reserve(ntl);
+        double P = init;
+        for (uint32_t tl = 0; tl < ntl; tl++) {
+            const double Pk = P + std::ldexp((double)skew, -30) * P;
+            tiles.push_back(chain_tile(tl * kCT, looks ? Pk : 0.0));
+            for (uint32_t c = tl * kCT; c < std::min<uint32_t>(tl * kCT + kCT, nch); c++)
+                P += tsum[c];
+        }
+        if (!chain_on(flags))
+            return walk_chunks(init, 0, nch, true);
+        // the head, then the first tile's other chunks
+        double S = add_terms(init, 0);
+        S = chain_chunks(S, tiles[0], 0, 1, std::min<uint32_t>(kCT, nch));
+        for (uint32_t tl = 1; tl < ntl; tl++) {
+            if (tiles[tl].regular)
+                continue;
+            Run acc;
+            uint32_t key0;
+            int64_t xp;
+            bool ok = chain_back_twin(tiles, tl, acc, key0, xp) == 0;
+            if (ok && xp != (int64_t)tl - 1) {
+                const int64_t m = count_of(S);
+                ok = R.key_ok(key_of(S), key0) &&
+                     R.applies(m, acc.p, acc.lo, acc.hi, acc.flags & (kFlagNeg | kFlagBad | kFlagNonFinite));
+                if (ok) {
+                    S = R.advance(S, m, acc.p);
+                    st.fast_chunks += (uint64_t)kCT * (tl - 1 - (uint32_t)xp);
+                    paths[4]++;
+                }
+            }
+            if (!ok) {
+                // the walk resumes after the last tile that published its sum
+                paths[5]++;
+                uint32_t j = tl - 1;
+                while (tiles[j].regular)
+                    j--;
+                return walk_chunks(S, (j + 1) * kCT, nch, true);
+            }
+            S = chain_chunks(S, tiles[tl], tl * kCT, 0, std::min<uint32_t>(kCT, nch - tl * kCT));
+        }
+        return S;
+    }
 };
 
 }  // namespace
@@ -904,5 +1250,30 @@ extern "C" double exseq_twin_seq_sum_f64(const double *x, size_t n, double init,
     const double S = tw.run_sum();
     if (stats)
         *stats = tw.st;
+    return S;
+}
+
+// The twin of the tile chain (four chunks per tile): the sum of x[0 .. n)
+// from init, its plan prefixes moved by skew * 2^-30 of themselves (flags: a
+// plan mode; mut: planted mutations).  paths: nullable host array of 6 counts
+// (waves of regular tiles composed as integer sums, falling sums, pairs
+// alone, full runs; composed runs applied; stops of the chain).
+extern "C" double exseq_twin_chain_sum_f64(const double *x, size_t n, double init, uint32_t flags,
+                                           uint32_t mut, int64_t skew, exseq_stats *stats,
+                                           uint64_t *paths)
+{
+    Twin tw;
+    tw.R = Rules{mut};
+    tw.x = x;
+    tw.n = n;
+    tw.init = init;
+    tw.flags = flags;
+    tw.skew = skew;
+    const double S = tw.run_chain();
+    if (stats)
+        *stats = tw.st;
+    if (paths)
+        for (int k = 0; k < 6; k++)
+            paths[k] = tw.paths[k];
     return S;
 }

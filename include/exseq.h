@@ -334,6 +334,29 @@ double exseq_model_seq_sum_f64(const double *x, size_t n, double init,
                                size_t chunk_terms, uint32_t flags,
                                uint32_t mutations, exseq_stats *stats);
 
+/* ---------------------------------------------------------------------------
+ * CPU twins of the kernels' composition (test infrastructure; no GPU).
+ *   The same rule helpers as the kernels, replayed in the kernels' grouping
+ *   of the terms -- four per lane, 64-lane waves with their shortcuts and
+ *   scan trees, four waves per chunk -- so that the grouping's shortcuts are
+ *   checked against the sequential loop on the host (Research-1433 "Forming
+ *   the CPU's sequential double sums on a GPU, bit for bit", Findings
+ *   "Tests").  x: HOST array of n doubles; flags: a plan mode; mutations:
+ *   EXSEQ_MUT_* planted in the replay; stats: nullable HOST pointer.
+ *   exseq_twin_seq_sum_f64: the single pass (tiles of eight chunks, the
+ *   finisher's windows).  exseq_twin_chain_sum_f64: the tile chain (tiles of
+ *   four chunks, the chain look-back, the irregular tiles, the walk's
+ *   resume), every planned prefix moved by skew * 2^-30 of itself; paths:
+ *   nullable HOST array of 6 counts (look-back waves composed as integer
+ *   sums, falling sums, pairs alone, full runs; composed runs applied; chain
+ *   stops).  Both return the sum.
+ * ------------------------------------------------------------------------- */
+double exseq_twin_seq_sum_f64(const double *x, size_t n, double init, uint32_t flags,
+                              uint32_t mutations, exseq_stats *stats);
+double exseq_twin_chain_sum_f64(const double *x, size_t n, double init, uint32_t flags,
+                                uint32_t mutations, int64_t skew, exseq_stats *stats,
+                                uint64_t *paths);
+
 #ifdef __cplusplus
 }
 #endif

@@ -160,6 +160,61 @@ TWIN_FAMILIES = ("rise_fall", "edge_counts", "ties", "falling", "neg_cross", "ne
                  "mixed")
 
 
+TWIN_CHAIN_FAMILIES = ("chain_mix", "chain_wave_rise")
+
+
+def twin_chain_case(seed: int, family: str):
+    """(terms, init) of one sum of whole tiles of 4096 terms, for the tile
+    chain's twin.  chain_mix: 3-40 tiles in blocks of one kind (tie-free
+    rising, rising with half-unit ties, tie-free falling, rising with a few
+    negative terms and ties), placed so that the running count meets an edge
+    of its binade along the sum (up or down; sometimes the whole sum
+    negated).  chain_wave_rise: about 60 tiles with negative terms, then 258
+    rising tiles with ties, the count passing the binade's top among the
+    latter: one look-back wave of full runs before one of pairs alone."""
+    g = rng(seed)
+    C = 4096
+    e = int(g.integers(-40, 40))
+    u = 2.0 ** (e - 52)
+
+    def tile(kind):
+        if kind == 0:
+            return g.integers(0, 9, C).astype(np.float64)
+        if kind == 1:
+            k = g.integers(0, 4, C).astype(np.float64)
+            return k + np.where(g.random(C) < 0.3, 0.5, 0.0)
+        if kind == 2:
+            return -g.integers(0, 9, C).astype(np.float64)
+        k = g.integers(0, 6, C).astype(np.float64)
+        k[g.random(C) < 0.01] = -3.0
+        return k + np.where(g.random(C) < 0.1, 0.5, 0.0)
+
+    if family == "chain_wave_rise":
+        kinds = [3] * int(g.integers(58, 66)) + [1] * 258
+        x = np.concatenate([tile(k) for k in kinds])
+        cum = np.cumsum(x)
+        m0 = 2.0 ** 53 - float(cum[-1]) * float(g.uniform(0.3, 0.9))
+        return x * u, m0 * u
+    T = int(g.integers(3, 40))
+    kinds = []
+    while len(kinds) < T:
+        kinds += [int(g.integers(0, 4))] * int(g.integers(1, 12))
+    x = np.concatenate([tile(k) for k in kinds[:T]])
+    cum = np.cumsum(x)
+    top, bot = float(cum.max()), float(cum.min())
+    if g.random() < 0.5:
+        m0 = 2.0 ** 53 - max(top, 1.0) * float(g.uniform(0.3, 1.3))
+        m0 = max(m0, 2.0 ** 52 - bot + 8.0)
+    else:
+        m0 = 2.0 ** 52 - min(bot, -1.0) * float(g.uniform(0.3, 1.3))
+        m0 = min(m0, 2.0 ** 53 - top - 8.0)
+    init = float(np.floor(m0)) * u
+    x = x * u
+    if g.random() < 0.25:
+        return -x, -init
+    return x, init
+
+
 def twin_case(seed: int, family: str):
     """(terms, init) of one adversarial sum."""
     g = rng(seed)
