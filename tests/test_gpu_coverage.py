@@ -170,3 +170,27 @@ def test_subnormal_range_runs(init):
             assert same(got, want), (name, fl, got, want)
             if name == "rising" and fl != ex.WALK_ONLY:
                 assert st["fast_chunks"] >= 0.9 * st["chunks"], (fl, st)
+
+
+TILE4 = 3 << 4  # bits 4..5 of flags: four chunks per tile
+
+
+@pytest.mark.parametrize("family", si.TWIN_CHAIN_FAMILIES)
+def test_chain_families(family):
+    """The adversarial sums of whole tiles that the tile chain's CPU twin is
+    checked on (blocks of tie-free rising, tied rising, falling and mixed
+    tiles meeting a binade edge; a wave of tiles with negative terms before
+    a wave of tied rising tiles that passes the binade's top), through the
+    GPU's tile chain at four chunks per tile under every plan, with the
+    chain cut half way, and through the single pass: the oracle's bits."""
+    torch = torch_cuda()
+    seeds = range(60) if family == "chain_mix" else range(6)
+    flag_sets = (0, TILE4, TILE4 | ex.PLAN_PLUS_ONE, TILE4 | ex.PLAN_MINUS_ONE,
+                 TILE4 | ex.PLAN_ALL_ZERO, TILE4 | ex.CHAIN_CUT, ex.PASS_PATH)
+    for sd in seeds:
+        x, init = si.twin_chain_case(sd, family)
+        want = oracle.seq_sum(x, init)
+        xd = to_dev(torch, x)
+        for fl in flag_sets:
+            got = float(ex.exact_seq_sum(xd, init, flags=fl).cpu()[0])
+            assert same(got, want), (family, sd, fl)
